@@ -1,0 +1,220 @@
+/*
+ * attn_fp4.h -- C ABI of the MI355X (gfx950) Direct-P FP4 attention forward.
+ *
+ * The method is the one described on the pages "Hardware-Aware FP4
+ * FlashAttention-4" (summary page, section "What the paper found"; arXiv
+ * listing 2609.04105v1, abstract): Q and K stay in NVFP4, the row-max-shifted
+ * log2 scores are mapped directly to MXFP4 E2M1 probability codes with one
+ * E8M0 scale per 32 keys, the softmax denominator is summed from the same
+ * rounded probabilities that the P.V product consumes, and a causal path
+ * keeps FP8 E4M3 probabilities and values.  The forward saves the
+ * log-sum-exp (LSE) per query row.
+ *
+ * Conventions shared by every entry point:
+ *  - All pointers except `args` structs and `cu_seqlens_*_host` are DEVICE
+ *    pointers on the current HIP device.  The caller owns every buffer; the
+ *    library never allocates, frees or synchronizes, and keeps no state.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work; they return before the work finishes.
+ *  - Arguments are validated on the host before any work is enqueued.  On
+ *    any status other than ATTN_OK nothing has been enqueued and no output
+ *    has been written.  Data-dependent conditions (NaN/Inf inputs, a
+ *    cu_seqlens array that is not non-decreasing, lengths that disagree with
+ *    the totals) are not detected and give unspecified outputs.
+ *  - bf16 inputs are contiguous and row-major.  A "row" is the D values of
+ *    one (token, head): dense tensors are [B, N, H, D], packed variable-length
+ *    ("varlen") tensors are [T, H, D] with sequence s occupying tokens
+ *    cu_seqlens[s] .. cu_seqlens[s+1]-1.
+ *  - Minimum alignments: 16 bytes for every tensor pointer, 4 bytes for
+ *    scalars.
+ */
+#ifndef ATTN_FP4_H
+#define ATTN_FP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, bad layout */
+  ATTN_ERR_UNSUPPORTED = 2,      /* valid request this library does not implement */
+  ATTN_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required */
+  ATTN_ERR_HIP = 4               /* a HIP launch failed; see attn_last_hip_error() */
+} attn_status;
+
+typedef enum attn_v_format {
+  ATTN_V_FP8_E4M3 = 0, /* E4M3 codes and one FP32 scale per tensor */
+  ATTN_V_MXFP4 = 1     /* E2M1 codes and one E8M0 scale per (channel, 32 keys) */
+} attn_v_format;
+
+typedef enum attn_out_dtype {
+  ATTN_OUT_BF16 = 0, /* O rounded to nearest-even bfloat16 */
+  ATTN_OUT_F32 = 1   /* O in float32 */
+} attn_out_dtype;
+
+/* Human-readable name of a status code (static storage). */
+const char* attn_status_str(attn_status s);
+/* The hipError_t (as int) of the last ATTN_ERR_HIP in this thread, else 0. */
+int attn_last_hip_error(void);
+/* Library version string. */
+const char* attn_version(void);
+
+/* ------------------------------------------------------------------------
+ * Quantization
+ * --------------------------------------------------------------------- */
+
+/* Bytes of device workspace every quantizer needs (a fixed, small size). */
+size_t attn_quant_ws_bytes(void);
+
+/*
+ * NVFP4 quantization of Q or K (the pages keep "NVFP4 for Q and K": summary
+ * page, "What the paper found").  x_bf16 is a [rows, D] bf16 matrix, D a
+ * multiple of 16 (64 and 128 are what the forward accepts).
+ *
+ * Rule (one FP32 scale per tensor, one E4M3 scale per 16 consecutive
+ * elements along D, every step an IEEE float32 operation rounded to nearest
+ * even):
+ *   amax_t = max |x| over the tensor
+ *   S_enc  = 2688 / amax_t  (1 if amax_t == 0; FLT_MAX if the quotient overflows)
+ *   g      = 1 / S_enc                                -> *tensor_scale
+ *   per block: s = E4M3_sat((amax_b / 6) * S_enc)     -> scales
+ *              code_i = E2M1_sat(x_i * (S_enc / s)), all 0 when s == 0
+ * E2M1/E4M3 encoders round to nearest even, keep the sign (so -0 and values
+ * that round to zero from below are code 8 / 0x80) and saturate.
+ *
+ * Outputs: codes [rows, D/2] (element 2k in the low nibble of byte k),
+ * scales [rows, D/16] (E4M3 bytes), tensor_scale (one float).
+ * ws: at least attn_quant_ws_bytes() bytes, no alignment beyond 16.
+ * rows == 0 is valid and writes only *tensor_scale (= 1).
+ */
+attn_status attn_quant_nvfp4(const void* x_bf16, int64_t rows, int32_t D,
+                             uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Number of key columns of the transposed V layout used by attn_quant_v and
+ * the forward.  Sequence s starts at column
+ *     dense : s * roundup(Nk, 128)
+ *     varlen: 128 * (cu_seqlens_k[s] / 128 + s)
+ * and the columns past its end up to the next 128-multiple hold zeros.
+ * dense (varlen == 0): B * roundup(Nk, 128); varlen: 128 * (ceil(total_k/128) + B).
+ */
+int64_t attn_v_cols(int32_t B, int32_t Nk, int64_t total_k, int32_t varlen);
+
+/*
+ * Quantize V (FP8 E4M3 or MXFP4; the pages pair FP4 or FP8 P with FP4 or FP8
+ * V: summary page, "What the paper found") and transpose it so that keys are
+ * contiguous, which is the operand order the P.V product reads.
+ *   v_bf16 : [B, Nk, Hkv, D] (dense) or [total_k, Hkv, D] (varlen)
+ *   cu_seqlens_k : device int32 [B+1] for varlen, NULL for dense
+ *   FP8  : enc = 448 / amax_v (1 if amax_v == 0), *tensor_scale = 1 / enc,
+ *          code = E4M3_sat(v * enc)
+ *   MXFP4: per (head, channel, 32 keys from the start of the sequence):
+ *          e = clamp(floor(log2 amax) - 2, -127, 127) (-127 if all zero),
+ *          code = E2M1_sat(v * 2^-e), scale byte = e + 127
+ * Outputs (cols = attn_v_cols(...)):
+ *   codes : FP8 [Hkv, D, cols] bytes; MXFP4 [Hkv, D, cols/2] (key 2k in the
+ *           low nibble of byte k)
+ *   scales: MXFP4 only, [Hkv, D, cols/32] E8M0 bytes (may be NULL for FP8)
+ *   tensor_scale: FP8 only (may be NULL for MXFP4)
+ * Padding columns receive code 0 and (MXFP4) scale byte 0.
+ */
+attn_status attn_quant_v(const void* v_bf16, int32_t B, int32_t Nk, int32_t Hkv, int32_t D,
+                         const int32_t* cu_seqlens_k, int64_t total_k, int32_t format,
+                         uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Forward
+ * --------------------------------------------------------------------- */
+
+typedef struct attn_nvfp4_tensor {
+  const uint8_t* codes;       /* [rows, D/2] as written by attn_quant_nvfp4 */
+  const uint8_t* scales;      /* [rows, D/16] */
+  const float* tensor_scale;  /* one float */
+} attn_nvfp4_tensor;
+
+typedef struct attn_v_tensor {
+  int32_t format;             /* attn_v_format */
+  const uint8_t* codes;       /* as written by attn_quant_v */
+  const uint8_t* scales;      /* MXFP4 only */
+  const float* tensor_scale;  /* FP8 only */
+} attn_v_tensor;
+
+typedef struct attn_fwd_args {
+  /* Shapes.  Dense: B batches of Nq queries and Nk keys.  Varlen: B
+   * sequences, Nq/Nk are the longest query/key lengths, total_q/total_k the
+   * packed token counts, and cu_seqlens_q/k (device int32 [B+1]) the
+   * offsets; the forward requires identical query and key lengths per
+   * sequence only when causal. */
+  int32_t B, Hq, Hkv, Nq, Nk, D;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  int64_t total_q, total_k;
+  float softmax_scale;        /* sigma; scores are sigma * Q.K */
+  int32_t causal;             /* key j visible to query i iff j <= i (needs Nq == Nk) */
+  attn_nvfp4_tensor q;        /* rows ordered like the bf16 Q: [B, Nq, Hq] / [total_q, Hq] */
+  attn_nvfp4_tensor k;        /* [B, Nk, Hkv] / [total_k, Hkv] */
+  attn_v_tensor v;
+  void* o;                    /* [B, Nq, Hq, D] / [total_q, Hq, D] */
+  int32_t o_dtype;            /* attn_out_dtype */
+  float* lse;                 /* nullable; [B, Hq, Nq] / [Hq, total_q], natural log */
+  void* ws;                   /* at least attn_fwd_ws_bytes(args) bytes */
+  size_t ws_bytes;
+  /* Optional probability dump for one (batch or sequence dbg_b, head dbg_h):
+   * P codes [Nq, roundup(Nk,128)/2] (MXFP4, key 2k in the low nibble) or
+   * [Nq, roundup(Nk,128)] (FP8), and E8M0 bytes [Nq, roundup(Nk,128)/32]
+   * (MXFP4).  Codes of masked keys are 0.  NULL disables the dump. */
+  uint8_t* dbg_p_codes;
+  uint8_t* dbg_p_scales;
+  int32_t dbg_b, dbg_h;
+} attn_fwd_args;
+
+/* Bytes of device workspace the forward needs for these shapes: the exact
+ * float16 expansion of the NVFP4 Q and K payloads (E2M1 * E4M3, 6
+ * significant bits, exact in float16), arranged in 32-query and 128-key
+ * tiles.  Returns 0 for invalid shapes. */
+size_t attn_fwd_ws_bytes(const attn_fwd_args* a);
+
+/*
+ * Direct-P forward (noncausal inference path of the pages; summary page,
+ * "What the paper found"): S = Q.K^T on the exact NVFP4 values, per tile of
+ * 128 keys the running max m' of t = sigma*log2(e)*S is updated, each
+ * 32-key block gets the E8M0 exponent e = max(floor(max(t) - m') - 2, -127)
+ * and codes E2M1(2^(t - m' - e)), the denominator l and O accumulate the
+ * dequantized codes times V, and finally O = o / l (times the FP8 V tensor
+ * scale) and LSE = ln2 * (m + log2 l).  V may be FP8 or MXFP4.
+ * D in {64, 128}; Hq % Hkv == 0; causal must be 0 (ATTN_ERR_UNSUPPORTED).
+ */
+attn_status attn_fwd_directp(const attn_fwd_args* a, void* stream);
+
+/*
+ * FP8-P/V forward (the variant the pages keep for stable causal training;
+ * summary page, "What the paper found"): identical to attn_fwd_directp
+ * except that each probability is E4M3(2^(t - m')) with unit scale and V is
+ * FP8 E4M3.  Causal or not.  D in {64, 128}; Hq % Hkv == 0.
+ */
+attn_status attn_fwd_fp8pv(const attn_fwd_args* a, void* stream);
+
+/*
+ * BF16 fused attention forward, the baseline the pages compare against
+ * (BF16 FlashAttention-4 on the summary page, "Key results"): O =
+ * softmax(sigma Q K^T) V with bf16 operands, float32 accumulation and
+ * probabilities rounded to bf16 for the P.V product.
+ *   q: [B, Nq, Hq, D] bf16, k/v: [B, Nk, Hkv, D] bf16 (dense only),
+ *   o: [B, Nq, Hq, D] bf16, lse: nullable [B, Hq, Nq].
+ * D in {64, 128}.  No workspace.
+ */
+attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int32_t B, int32_t Hq, int32_t Hkv, int32_t Nq, int32_t Nk, int32_t D,
+                          float softmax_scale, int32_t causal, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FP4_H */

@@ -30,7 +30,7 @@ def _enc_scale(amax, top):
     return F32(FLT_MAX) if not np.isfinite(s) else s
 
 
-def quant_nvfp4(x):
+def quant_nvfp4(x, amax=None):
     """NVFP4 quantization of a tensor whose last axis is D (multiple of 16).
 
     Reading (the pages give the format name only):
@@ -45,13 +45,18 @@ def quant_nvfp4(x):
 
     Returns (codes_packed uint8 [..., D/2], scales uint8 [..., D/16], g float32).
     Element 2k of a row sits in the low nibble of byte k.
+
+    ``amax`` lets a caller quantize a slice of a larger tensor: pass the max
+    |x| of the whole tensor (step 1) and the rows of interest.
     """
     x = np.asarray(x, dtype=F32)
     D = x.shape[-1]
     assert D % NVFP4_BLOCK == 0
     lead = x.shape[:-1]
     xb = x.reshape(-1, D // NVFP4_BLOCK, NVFP4_BLOCK)
-    amax_t = F32(np.max(np.abs(xb))) if xb.size else F32(0)
+    if amax is None:
+        amax = np.max(np.abs(xb)) if xb.size else 0.0
+    amax_t = F32(amax)
     s_enc = _enc_scale(amax_t, 2688.0)
     g = F32(F32(1.0) / s_enc)
     amax_b = np.max(np.abs(xb), axis=-1) if xb.size else np.zeros(xb.shape[:-1], F32)
@@ -83,15 +88,18 @@ def dequant_nvfp4(codes_packed, scales, g):
     return dequant_nvfp4_raw(codes_packed, scales) * np.float64(g)
 
 
-def quant_v_fp8(v):
+def quant_v_fp8(v, amax=None):
     """FP8 E4M3 V with one FP32 scale per tensor.
 
     Reading: enc = fl(448 / amax_v) (1 when amax_v = 0), stored scale
     s_v = fl(1 / enc), code = E4M3(fl(v * enc)); dequantized value
     E4M3(code) * s_v.  Returns (codes uint8 same shape as v, s_v float32).
+    ``amax`` (max |v| of the whole tensor) allows quantizing a slice.
     """
     v = np.asarray(v, dtype=F32)
-    amax = F32(np.max(np.abs(v))) if v.size else F32(0)
+    if amax is None:
+        amax = np.max(np.abs(v)) if v.size else 0.0
+    amax = F32(amax)
     enc = _enc_scale(amax, 448.0)
     s_v = F32(F32(1.0) / enc)
     codes = e4m3_encode((v * enc).astype(F32))

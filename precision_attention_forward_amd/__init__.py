@@ -1,0 +1,11 @@
+"""MI355X (gfx950) Direct-P FP4 attention forward.
+
+The computation lives in the HIP library ``libattnfp4.so`` (C ABI in
+``include/attn_fp4.h``); this package is its thin ctypes binding plus the
+seeded synthetic-input generators (``synth``).
+"""
+
+from ._binding import (  # noqa: F401
+    AttnError, LIB_PATH, OUT_BF16, OUT_F32, V_FP8, V_MXFP4, EXPORTS, Workspace,
+    fwd_bf16, fwd_directp, fwd_fp8pv, load_library, make_fwd_args, quant_nvfp4, quant_v, v_cols,
+)

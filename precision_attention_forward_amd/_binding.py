@@ -1,0 +1,271 @@
+"""ctypes binding of libattnfp4.so (the C ABI in include/attn_fp4.h).
+
+Argument marshalling only: torch provides device memory and the current
+stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback: if the shared library is missing or fails to load,
+every entry point raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattnfp4.so")
+
+ATTN_OK = 0
+V_FP8 = 0
+V_MXFP4 = 1
+OUT_BF16 = 0
+OUT_F32 = 1
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    pass
+
+
+class _NvTensor(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("tensor_scale", ctypes.c_void_p)]
+
+
+class _VTensor(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("tensor_scale", ctypes.c_void_p)]
+
+
+class FwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("Nq", ctypes.c_int32), ("Nk", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
+        ("total_q", ctypes.c_int64), ("total_k", ctypes.c_int64),
+        ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32),
+        ("q", _NvTensor), ("k", _NvTensor), ("v", _VTensor),
+        ("o", ctypes.c_void_p), ("o_dtype", ctypes.c_int32), ("lse", ctypes.c_void_p),
+        ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
+        ("dbg_p_codes", ctypes.c_void_p), ("dbg_p_scales", ctypes.c_void_p),
+        ("dbg_b", ctypes.c_int32), ("dbg_h", ctypes.c_int32),
+    ]
+
+
+EXPORTS = {
+    "attn_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "attn_last_hip_error": (ctypes.c_int, []),
+    "attn_version": (ctypes.c_char_p, []),
+    "attn_quant_ws_bytes": (ctypes.c_size_t, []),
+    "attn_quant_nvfp4": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_void_p]),
+    "attn_v_cols": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]),
+    "attn_quant_v": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "attn_fwd_ws_bytes": (ctypes.c_size_t, [ctypes.POINTER(FwdArgs)]),
+    "attn_fwd_directp": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
+    "attn_fwd_fp8pv": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
+    "attn_fwd_bf16": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+                                     ctypes.c_void_p]),
+}
+
+
+def load_library(path=None):
+    """Load libattnfp4.so (raises if it is missing) and declare signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise AttnError(f"{path} is missing: build it with `python -m precision_attention_forward_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in EXPORTS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != ATTN_OK:
+        lib = load_library()
+        msg = lib.attn_status_str(status).decode()
+        if status == 4:
+            msg += f" (hipError {lib.attn_last_hip_error()})"
+        raise AttnError(f"attn library returned {status}: {msg}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise AttnError("tensors must be contiguous and on the GPU")
+
+
+def quant_nvfp4(x):
+    """NVFP4-quantize a bf16 tensor along its last axis (D).  Returns
+    (codes uint8 [..., D/2], scales uint8 [..., D/16], tensor_scale float32 [1])."""
+    lib = load_library()
+    _need_cuda(x)
+    if x.dtype != torch.bfloat16:
+        raise AttnError("quant_nvfp4 expects bfloat16")
+    D = x.shape[-1]
+    rows = x.numel() // D if D else 0
+    codes = torch.empty(x.shape[:-1] + (D // 2,), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(x.shape[:-1] + (D // 16,), dtype=torch.uint8, device=x.device)
+    ts = torch.empty(1, dtype=torch.float32, device=x.device)
+    ws = torch.empty(lib.attn_quant_ws_bytes(), dtype=torch.uint8, device=x.device)
+    _check(lib.attn_quant_nvfp4(_ptr(x), rows, D, _ptr(codes), _ptr(scales), _ptr(ts), _ptr(ws), ws.numel(),
+                                _stream()))
+    return codes, scales, ts
+
+
+def v_cols(B, Nk, total_k=0, varlen=False):
+    return load_library().attn_v_cols(B, Nk, total_k, 1 if varlen else 0)
+
+
+def quant_v(v, fmt, cu_seqlens=None, max_seqlen=None):
+    """Quantize V (bf16 [B, Nk, Hkv, D] or packed [T, Hkv, D] with device
+    cu_seqlens) to FP8 E4M3 (fmt=V_FP8) or MXFP4 (fmt=V_MXFP4), transposed to
+    [Hkv, D, cols] with keys contiguous.  Returns (codes, scales|None, tensor_scale|None, cols)."""
+    lib = load_library()
+    _need_cuda(v, cu_seqlens)
+    if v.dtype != torch.bfloat16:
+        raise AttnError("quant_v expects bfloat16")
+    if cu_seqlens is None:
+        B, Nk, Hkv, D = v.shape
+        total = B * Nk
+    else:
+        total, Hkv, D = v.shape
+        B = cu_seqlens.numel() - 1
+        Nk = int(max_seqlen)
+    cols = lib.attn_v_cols(B, Nk, total, 0 if cu_seqlens is None else 1)
+    if fmt == V_FP8:
+        codes = torch.zeros((Hkv, D, cols), dtype=torch.uint8, device=v.device)
+        scales = None
+        ts = torch.empty(1, dtype=torch.float32, device=v.device)
+    else:
+        codes = torch.zeros((Hkv, D, cols // 2), dtype=torch.uint8, device=v.device)
+        scales = torch.zeros((Hkv, D, cols // 32), dtype=torch.uint8, device=v.device)
+        ts = None
+    ws = torch.empty(lib.attn_quant_ws_bytes(), dtype=torch.uint8, device=v.device)
+    _check(lib.attn_quant_v(_ptr(v), B, Nk, Hkv, D, _ptr(cu_seqlens), total, fmt, _ptr(codes), _ptr(scales),
+                            _ptr(ts), _ptr(ws), ws.numel(), _stream()))
+    return codes, scales, ts, cols
+
+
+class Workspace:
+    """A reusable device byte buffer that grows on demand."""
+
+    def __init__(self):
+        self.buf = None
+
+    def get(self, nbytes, device):
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != torch.device(device):
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        return self.buf
+
+
+_default_ws = Workspace()
+
+
+def make_fwd_args(q, k, v, *, B, Hq, Hkv, Nq, Nk, D, softmax_scale, causal=False, cu_seqlens_q=None,
+                  cu_seqlens_k=None, total_q=0, total_k=0, o=None, o_dtype=OUT_F32, lse=None, ws=None,
+                  dbg_codes=None, dbg_scales=None, dbg_b=0, dbg_h=0):
+    """q/k: (codes, scales, tensor_scale); v: (format, codes, scales|None, tensor_scale|None)."""
+    a = FwdArgs()
+    a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.D = B, Hq, Hkv, Nq, Nk, D
+    a.cu_seqlens_q = None if cu_seqlens_q is None else cu_seqlens_q.data_ptr()
+    a.cu_seqlens_k = None if cu_seqlens_k is None else cu_seqlens_k.data_ptr()
+    a.total_q, a.total_k = total_q, total_k
+    a.softmax_scale = softmax_scale
+    a.causal = 1 if causal else 0
+    a.q = _NvTensor(q[0].data_ptr(), q[1].data_ptr(), q[2].data_ptr())
+    a.k = _NvTensor(k[0].data_ptr(), k[1].data_ptr(), k[2].data_ptr())
+    a.v = _VTensor(v[0], v[1].data_ptr(), None if v[2] is None else v[2].data_ptr(),
+                   None if v[3] is None else v[3].data_ptr())
+    a.o = None if o is None else o.data_ptr()
+    a.o_dtype = o_dtype
+    a.lse = None if lse is None else lse.data_ptr()
+    a.ws = None if ws is None else ws.data_ptr()
+    a.ws_bytes = 0 if ws is None else ws.numel()
+    a.dbg_p_codes = None if dbg_codes is None else dbg_codes.data_ptr()
+    a.dbg_p_scales = None if dbg_scales is None else dbg_scales.data_ptr()
+    a.dbg_b, a.dbg_h = dbg_b, dbg_h
+    return a
+
+
+def _fwd_lowp(entry, q, k, v, *, Hq, Hkv, D, softmax_scale, causal=False, B=None, Nq=None, Nk=None,
+              cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
+              out_dtype=torch.float32, want_lse=True, workspace=None, debug=None):
+    """Shared driver of attn_fwd_directp / attn_fwd_fp8pv.  Returns (O, LSE, dbg)."""
+    lib = load_library()
+    dev = q[0].device
+    varlen = cu_seqlens_q is not None
+    if varlen:
+        B = cu_seqlens_q.numel() - 1
+        total_q = q[0].shape[0]
+        total_k = k[0].shape[0]
+        Nq, Nk = int(max_seqlen_q), int(max_seqlen_k)
+        oshape = (total_q, Hq, D)
+        lshape = (Hq, total_q)
+    else:
+        total_q, total_k = B * Nq, B * Nk
+        oshape = (B, Nq, Hq, D)
+        lshape = (B, Hq, Nq)
+    o = torch.empty(oshape, dtype=out_dtype, device=dev)
+    lse = torch.empty(lshape, dtype=torch.float32, device=dev) if want_lse else None
+    dbg_codes = dbg_scales = None
+    dbg_b = dbg_h = 0
+    if debug is not None:
+        dbg_b, dbg_h = debug
+        nq_dbg = Nq
+        nk_pad = (Nk + 127) // 128 * 128
+        if entry == "attn_fwd_directp":
+            dbg_codes = torch.zeros((nq_dbg, nk_pad // 2), dtype=torch.uint8, device=dev)
+            dbg_scales = torch.zeros((nq_dbg, nk_pad // 32), dtype=torch.uint8, device=dev)
+        else:
+            dbg_codes = torch.zeros((nq_dbg, nk_pad), dtype=torch.uint8, device=dev)
+    a = make_fwd_args(q, k, v, B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nk=Nk, D=D, softmax_scale=softmax_scale, causal=causal,
+                      cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k, total_q=total_q, total_k=total_k, o=o,
+                      o_dtype=OUT_F32 if out_dtype == torch.float32 else OUT_BF16, lse=lse,
+                      dbg_codes=dbg_codes, dbg_scales=dbg_scales, dbg_b=dbg_b, dbg_h=dbg_h)
+    need = lib.attn_fwd_ws_bytes(ctypes.byref(a))
+    ws = (workspace or _default_ws).get(need, dev)
+    a.ws, a.ws_bytes = ws.data_ptr(), ws.numel()
+    _check(getattr(lib, entry)(ctypes.byref(a), _stream()))
+    return o, lse, (dbg_codes, dbg_scales)
+
+
+def fwd_directp(q, k, v, **kw):
+    """Direct-P forward: MXFP4 P, V FP8 or MXFP4 (noncausal)."""
+    return _fwd_lowp("attn_fwd_directp", q, k, v, **kw)
+
+
+def fwd_fp8pv(q, k, v, **kw):
+    """FP8-P/V forward (causal allowed)."""
+    return _fwd_lowp("attn_fwd_fp8pv", q, k, v, **kw)
+
+
+def fwd_bf16(q, k, v, softmax_scale, causal=False, want_lse=True):
+    """BF16 baseline forward on dense [B, N, H, D] bf16 tensors."""
+    lib = load_library()
+    _need_cuda(q, k, v)
+    B, Nq, Hq, D = q.shape
+    _, Nk, Hkv, _ = k.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if want_lse else None
+    _check(lib.attn_fwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, D, softmax_scale,
+                             1 if causal else 0, _stream()))
+    return o, lse

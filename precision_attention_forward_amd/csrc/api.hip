@@ -1,0 +1,238 @@
+// C ABI of the Direct-P FP4 attention library (declared in include/attn_fp4.h).
+// Host-side argument validation and launch sequencing only; every step of the
+// computation runs in the HIP kernels of quant.hip, fwd_lowp.hip and fwd_bf16.hip.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/attn_fp4.h"
+#include "common.h"
+
+namespace attn {
+hipError_t launch_amax(const void* x, int64_t n, float* partials, int* np_out, hipStream_t st);
+hipError_t launch_quant_nvfp4(const void* x, int64_t rows, int D, const float* partials, int np, uint8_t* codes,
+                              uint8_t* scales, float* tensor_scale, hipStream_t st);
+hipError_t launch_quant_v(const void* v, int B, int Nk, int Hkv, int D, const int32_t* cu_k, int max_len, int64_t cols,
+                          int fmt, const float* partials, int np, uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                          hipStream_t st);
+hipError_t launch_expand(bool is_q, const uint8_t* codes, const uint8_t* scales, int H, int B, int N, int max_len,
+                         const int32_t* cu, int64_t n_pad, int64_t cols, int D, int pf, _Float16* out, hipStream_t st);
+struct FwdParams;
+hipError_t launch_fwd_lowp(const FwdParams& p, int D, int pf, int vf, bool causal, bool debug, hipStream_t st);
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                           int Nq, int Nk, int D, float sigma, bool causal, hipStream_t st);
+}  // namespace attn
+
+#include "fwd_params.h"
+
+using namespace attn;
+
+static thread_local int g_last_hip_error = 0;
+static const size_t QUANT_WS = 4096;   // >= 512 partial maxima
+
+static attn_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return ATTN_OK;
+  g_last_hip_error = (int)e;
+  return ATTN_ERR_HIP;
+}
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+extern "C" {
+
+const char* attn_status_str(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int attn_last_hip_error(void) { return g_last_hip_error; }
+const char* attn_version(void) { return "attn_fp4 0.1 gfx950"; }
+size_t attn_quant_ws_bytes(void) { return QUANT_WS; }
+
+attn_status attn_quant_nvfp4(const void* x_bf16, int64_t rows, int32_t D, uint8_t* codes, uint8_t* scales,
+                             float* tensor_scale, void* ws, size_t ws_bytes, void* stream) {
+  if (rows < 0 || D <= 0 || D % 16 != 0 || tensor_scale == nullptr || !aligned(tensor_scale, 4))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (rows > 0 && (x_bf16 == nullptr || codes == nullptr || scales == nullptr || !aligned(x_bf16, 16) ||
+                   !aligned(codes, 8)))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (ws == nullptr || ws_bytes < QUANT_WS || !aligned(ws, 16)) return ATTN_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  int np = 0;
+  float* partials = (float*)ws;
+  hipError_t e = launch_amax(x_bf16, rows * (int64_t)D, partials, &np, st);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(launch_quant_nvfp4(x_bf16, rows, D, partials, np, codes, scales, tensor_scale, st));
+}
+
+int64_t attn_v_cols(int32_t B, int32_t Nk, int64_t total_k, int32_t varlen) {
+  if (B < 0 || Nk < 0 || total_k < 0) return -1;
+  if (varlen) return 128 * ((total_k + 127) / 128 + B);
+  return (int64_t)B * roundup(Nk, 128);
+}
+
+attn_status attn_quant_v(const void* v_bf16, int32_t B, int32_t Nk, int32_t Hkv, int32_t D,
+                         const int32_t* cu_seqlens_k, int64_t total_k, int32_t format, uint8_t* codes,
+                         uint8_t* scales, float* tensor_scale, void* ws, size_t ws_bytes, void* stream) {
+  if (B < 0 || Nk < 0 || Hkv <= 0 || (D != 64 && D != 128)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (format != ATTN_V_FP8_E4M3 && format != ATTN_V_MXFP4) return ATTN_ERR_INVALID_ARGUMENT;
+  const bool varlen = cu_seqlens_k != nullptr;
+  if (varlen && total_k < 0) return ATTN_ERR_INVALID_ARGUMENT;
+  const int64_t tokens = varlen ? total_k : (int64_t)B * Nk;
+  if (format == ATTN_V_FP8_E4M3 && (tensor_scale == nullptr || !aligned(tensor_scale, 4)))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (tokens > 0 && (v_bf16 == nullptr || codes == nullptr || !aligned(v_bf16, 16) || !aligned(codes, 16)))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (tokens > 0 && format == ATTN_V_MXFP4 && (scales == nullptr || !aligned(scales, 4)))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (ws == nullptr || ws_bytes < QUANT_WS || !aligned(ws, 16)) return ATTN_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t cols = attn_v_cols(B, Nk, total_k, varlen);
+  float* partials = (float*)ws;
+  int np = 0;
+  hipError_t e;
+  if (format == ATTN_V_FP8_E4M3) {
+    e = launch_amax(v_bf16, tokens * Hkv * (int64_t)D, partials, &np, st);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (B == 0) return ATTN_OK;
+  return hip_status(launch_quant_v(v_bf16, B, Nk, Hkv, D, cu_seqlens_k, Nk, cols, format, partials, np, codes, scales,
+                                   tensor_scale, st));
+}
+
+// Workspace layout of the forward: [Q fp16 tiles | K fp16 tiles].
+static bool fwd_geometry(const attn_fwd_args* a, int64_t* qcols, int64_t* kcols) {
+  const bool varlen = a->cu_seqlens_q != nullptr;
+  if (varlen) {
+    *qcols = 32 * ((a->total_q + 31) / 32 + a->B);
+    *kcols = 128 * ((a->total_k + 127) / 128 + a->B);
+  } else {
+    *qcols = (int64_t)a->B * roundup(a->Nq, 32);
+    *kcols = (int64_t)a->B * roundup(a->Nk, 128);
+  }
+  return true;
+}
+
+size_t attn_fwd_ws_bytes(const attn_fwd_args* a) {
+  if (a == nullptr || a->B < 0 || a->Hq <= 0 || a->Hkv <= 0 || (a->D != 64 && a->D != 128)) return 0;
+  int64_t qc, kc;
+  fwd_geometry(a, &qc, &kc);
+  return (size_t)(2 * a->D) * (size_t)(a->Hq * qc + a->Hkv * kc) + 256;
+}
+
+static attn_status validate_fwd(const attn_fwd_args* a, bool allow_causal, int pf) {
+  if (a == nullptr) return ATTN_ERR_INVALID_ARGUMENT;
+  if (a->B < 0 || a->Hq <= 0 || a->Hkv <= 0 || a->Nq < 0 || a->Nk < 0) return ATTN_ERR_INVALID_ARGUMENT;
+  if (a->D != 64 && a->D != 128) return ATTN_ERR_INVALID_ARGUMENT;
+  if (a->Hq % a->Hkv != 0) return ATTN_ERR_INVALID_ARGUMENT;
+  if ((a->cu_seqlens_q == nullptr) != (a->cu_seqlens_k == nullptr)) return ATTN_ERR_INVALID_ARGUMENT;
+  const bool varlen = a->cu_seqlens_q != nullptr;
+  if (varlen && (a->total_q < 0 || a->total_k < 0 || !aligned(a->cu_seqlens_q, 4) || !aligned(a->cu_seqlens_k, 4)))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (!(a->softmax_scale > 0.0f) || a->softmax_scale != a->softmax_scale) return ATTN_ERR_INVALID_ARGUMENT;
+  if (a->causal && !allow_causal) return ATTN_ERR_UNSUPPORTED;
+  if (a->causal && a->Nq != a->Nk) return ATTN_ERR_INVALID_ARGUMENT;
+  if (a->v.format != ATTN_V_FP8_E4M3 && a->v.format != ATTN_V_MXFP4) return ATTN_ERR_INVALID_ARGUMENT;
+  if (pf == 1 && a->v.format != ATTN_V_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
+  if (a->o_dtype != ATTN_OUT_BF16 && a->o_dtype != ATTN_OUT_F32) return ATTN_ERR_INVALID_ARGUMENT;
+  const int64_t nq = varlen ? a->total_q : (int64_t)a->B * a->Nq;
+  const int64_t nk = varlen ? a->total_k : (int64_t)a->B * a->Nk;
+  const attn_nvfp4_tensor* t[2] = {&a->q, &a->k};
+  const int64_t n[2] = {nq, nk};
+  for (int i = 0; i < 2; ++i) {
+    if (t[i]->tensor_scale == nullptr || !aligned(t[i]->tensor_scale, 4)) return ATTN_ERR_INVALID_ARGUMENT;
+    if (n[i] > 0 && (t[i]->codes == nullptr || t[i]->scales == nullptr || !aligned(t[i]->codes, 8)))
+      return ATTN_ERR_INVALID_ARGUMENT;
+  }
+  if (nk > 0 && (a->v.codes == nullptr || !aligned(a->v.codes, 16))) return ATTN_ERR_INVALID_ARGUMENT;
+  if (nk > 0 && a->v.format == ATTN_V_MXFP4 && (a->v.scales == nullptr || !aligned(a->v.scales, 4)))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (a->v.format == ATTN_V_FP8_E4M3 && (a->v.tensor_scale == nullptr || !aligned(a->v.tensor_scale, 4)))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (nq > 0 && (a->o == nullptr || !aligned(a->o, 16))) return ATTN_ERR_INVALID_ARGUMENT;
+  if (a->lse != nullptr && !aligned(a->lse, 4)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (a->dbg_p_codes != nullptr) {
+    if (a->dbg_b < 0 || a->dbg_b >= a->B || a->dbg_h < 0 || a->dbg_h >= a->Hq || !aligned(a->dbg_p_codes, 16))
+      return ATTN_ERR_INVALID_ARGUMENT;
+    if (pf == 0 && a->dbg_p_scales == nullptr) return ATTN_ERR_INVALID_ARGUMENT;
+  }
+  const size_t need = attn_fwd_ws_bytes(a);
+  if (a->ws == nullptr || a->ws_bytes < need || !aligned(a->ws, 256)) return ATTN_ERR_WORKSPACE;
+  return ATTN_OK;
+}
+
+static attn_status run_fwd_lowp(const attn_fwd_args* a, void* stream, int pf) {
+  attn_status s = validate_fwd(a, pf == 1, pf);
+  if (s != ATTN_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const bool varlen = a->cu_seqlens_q != nullptr;
+  int64_t qcols, kcols;
+  fwd_geometry(a, &qcols, &kcols);
+  _Float16* qhat = (_Float16*)a->ws;
+  _Float16* khat = qhat + (int64_t)a->Hq * qcols * a->D;
+  const int64_t nq_pad = roundup(a->Nq, 32), nk_pad = roundup(a->Nk, 128);
+  hipError_t e = launch_expand(true, a->q.codes, a->q.scales, a->Hq, a->B, a->Nq, a->Nq, a->cu_seqlens_q, nq_pad,
+                               qcols, a->D, pf, qhat, st);
+  if (e != hipSuccess) return hip_status(e);
+  e = launch_expand(false, a->k.codes, a->k.scales, a->Hkv, a->B, a->Nk, a->Nk, a->cu_seqlens_k, nk_pad, kcols,
+                    a->D, pf, khat, st);
+  if (e != hipSuccess) return hip_status(e);
+  FwdParams p;
+  memset(&p, 0, sizeof(p));
+  p.qhat = qhat;
+  p.khat = khat;
+  p.qcols = qcols;
+  p.kcols = kcols;
+  p.v_codes = a->v.codes;
+  p.v_scales = a->v.scales;
+  p.gq = a->q.tensor_scale;
+  p.gk = a->k.tensor_scale;
+  p.sv = a->v.tensor_scale;
+  p.o = a->o;
+  p.o_f32 = a->o_dtype == ATTN_OUT_F32;
+  p.lse = a->lse;
+  p.cu_q = a->cu_seqlens_q;
+  p.cu_k = a->cu_seqlens_k;
+  p.B = a->B;
+  p.Hq = a->Hq;
+  p.Hkv = a->Hkv;
+  p.Nq = a->Nq;
+  p.Nk = a->Nk;
+  p.QB = (a->Nq + WG_Q - 1) / WG_Q;
+  p.nq_pad = nq_pad;
+  p.nk_pad = nk_pad;
+  p.sigma = a->softmax_scale;
+  p.dbg_codes = a->dbg_p_codes;
+  p.dbg_scales = a->dbg_p_scales;
+  p.dbg_b = a->dbg_b;
+  p.dbg_h = a->dbg_h;
+  p.dbg_ld = nk_pad;
+  (void)varlen;
+  return hip_status(launch_fwd_lowp(p, a->D, pf, a->v.format == ATTN_V_MXFP4 ? 1 : 0, a->causal != 0,
+                                    a->dbg_p_codes != nullptr, st));
+}
+
+attn_status attn_fwd_directp(const attn_fwd_args* a, void* stream) { return run_fwd_lowp(a, stream, 0); }
+attn_status attn_fwd_fp8pv(const attn_fwd_args* a, void* stream) { return run_fwd_lowp(a, stream, 1); }
+
+attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Hq,
+                          int32_t Hkv, int32_t Nq, int32_t Nk, int32_t D, float softmax_scale, int32_t causal,
+                          void* stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Nq < 0 || Nk < 0 || (D != 64 && D != 128) || Hq % Hkv != 0)
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (!(softmax_scale > 0.0f)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (causal && Nq != Nk) return ATTN_ERR_INVALID_ARGUMENT;
+  const int64_t nq = (int64_t)B * Nq, nk = (int64_t)B * Nk;
+  if (nq > 0 && (q == nullptr || o == nullptr || !aligned(q, 16) || !aligned(o, 16))) return ATTN_ERR_INVALID_ARGUMENT;
+  if (nk > 0 && (k == nullptr || v == nullptr || !aligned(k, 16) || !aligned(v, 16))) return ATTN_ERR_INVALID_ARGUMENT;
+  if (lse != nullptr && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_fwd_bf16(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, D, softmax_scale, causal != 0,
+                                    (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,462 @@
+// Direct-P FP4 attention forward and its FP8-P/V variant for gfx950.
+//
+// Method: "Hardware-Aware FP4 FlashAttention-4" (summary page, "What the paper
+// found"; arXiv listing 2609.04105v1, abstract).  NVFP4 Q and K; per tile of
+// 128 keys the running row max m' of the log2-domain scores is updated, the
+// shifted scores are mapped straight to E2M1 probability codes with one E8M0
+// exponent per 32 keys (Direct-P) or to E4M3 codes with a unit scale (FP8 P);
+// the denominator is summed from the same rounded probabilities the P.V
+// product consumes; O = o / l and LSE = ln2 * (m + log2 l).
+//
+// gfx950 mapping (the pages' Blackwell pipeline is prior art, not copied):
+//  * NVFP4 blocks carry an E4M3 scale per 16 elements; the scaled MFMA takes
+//    one E8M0 scale per 32, so Q.K^T is run as an FP16 MFMA on the exact
+//    dequantized values (E2M1 x E4M3 has at most 6 significant bits).  A
+//    pre-pass expands Q and K once into 32-query / 128-key FP16 tiles laid
+//    out in the order the MFMA operands are read.
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_f16 puts one query per lane; the key
+//    rows of K are permuted so that each lane ends up holding exactly the 32
+//    keys of one P block (MXFP4) or the 32 keys the FP8 operand layout wants.
+//    Block max, E8M0 exponent and E2M1/E4M3 encoding are then lane-local; the
+//    row max needs one exchange with lane l^32.
+//  * O^T += V^T P^T on v_mfma_scale_f32_32x32x64_f8f6f4 (P as the B operand,
+//    its E8M0 block exponent as scale_b; MXFP4 V brings its own scale_a).
+//  * l = sum of the dequantized P is computed by one 16x16x128 scaled MFMA
+//    per 64 keys against a constant 0/1 operand, so it sums exactly the
+//    rounded probabilities without any VALU work.
+#include "common.h"
+#include "fwd_params.h"
+
+namespace attn {
+
+
+// Key (0..127) of S^T sub-tile st (0..3), accumulator register v (0..15), lane half hh.
+// MXFP4 P: lane half hh of chunk c = st/2 owns keys 64c + 32hh + [0, 32).
+// FP8 P  : lane half hh owns keys 64c + 16hh + [0,16) and 64c + 32 + 16hh + [0,16)
+//          (the k order of the FP8 operand of the 32x32x64 MFMA).
+template <int PF>
+__host__ __device__ inline int s_key(int st, int v, int hh) {
+  const int c = st >> 1, s2 = st & 1;
+  return PF == PF_MXFP4 ? 64 * c + 32 * hh + 16 * s2 + v : 64 * c + 32 * s2 + 16 * hh + v;
+}
+// Accumulator row r (0..31) of a 32x32 MFMA output held by lane half hh, register v.
+__host__ __device__ inline int out_row(int v, int hh) { return 8 * (v >> 2) + 4 * hh + (v & 3); }
+
+// ---------------------------------------------------------------------------
+// Pre-pass: exact FP16 expansion of NVFP4 Q / K into the operand tile order.
+//   K tile (128 keys, D): element (st, kh, ks, r, j) at (((st*2+kh)*KS+ks)*32+r)*8+j,
+//     holding K[key = s_key(st, v(r), hh(r))][d = kh*D/2 + 8*ks + j], KS = D/16.
+//   Q group (32 queries, D): element (lane = 32*kh + q, o) at lane*(D/2) + o,
+//     holding Q[q][kh*D/2 + o].
+// Padding rows are written as zeros.
+template <bool IS_Q, int D, int PF>
+__global__ void __launch_bounds__(256) expand_nvfp4_kernel(const uint8_t* __restrict__ codes,
+                                                           const uint8_t* __restrict__ scales, int H, int N,
+                                                           const int32_t* __restrict__ cu, int64_t n_pad,
+                                                           int64_t cols, _Float16* __restrict__ out) {
+  const int tile = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const bool varlen = cu != nullptr;
+  const int64_t tok0 = varlen ? cu[s] : (int64_t)s * N;
+  const int len = varlen ? cu[s + 1] - cu[s] : N;
+  const int lim = IS_Q ? (int)roundup(len, 32) : (int)roundup(len, KEY_TILE);
+  if (tile * 128 >= lim) return;
+  const int64_t col0 = IS_Q ? qcol_offset(varlen, s, tok0, n_pad) : kcol_offset(varlen, s, tok0, n_pad);
+  constexpr int NB = D / 16, KS = D / 16, HALF = D / 2;
+  for (int p = threadIdx.x; p < 128 * NB; p += 256) {
+    const int row = p / NB, b16 = p % NB;        // row within this 128-row block
+    const int idx = tile * 128 + row;            // token index within the sequence
+    if (idx >= lim) continue;
+    f16x8 lo = {}, hi = {};
+    if (idx < len) {
+      const int64_t r = (tok0 + idx) * H + h;
+      const uint2 cw = *reinterpret_cast<const uint2*>(codes + r * (D / 2) + 8 * b16);
+      const float sv = e4m3_decode(scales[r * NB + b16]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        lo[j] = (_Float16)(e2m1_decode((cw.x >> (4 * j)) & 0xFu) * sv);
+        hi[j] = (_Float16)(e2m1_decode((cw.y >> (4 * j)) & 0xFu) * sv);
+      }
+    }
+    const int d0 = 16 * b16, kh = d0 / HALF, o = d0 % HALF;
+    _Float16* base = out + ((int64_t)h * cols + col0) * D;
+    if (IS_Q) {
+      const int g = idx / 32, q = idx % 32;
+      _Float16* dst = base + (int64_t)g * 32 * D + (int64_t)(32 * kh + q) * HALF + o;
+      *reinterpret_cast<f16x8*>(dst) = lo;
+      *reinterpret_cast<f16x8*>(dst + 8) = hi;
+    } else {
+      const int t = idx / 128, key = idx % 128;
+      int st, v, hh;
+      const int c = key >> 6;
+      if (PF == PF_MXFP4) { hh = (key >> 5) & 1; st = 2 * c + ((key >> 4) & 1); }
+      else                { st = 2 * c + ((key >> 5) & 1); hh = (key >> 4) & 1; }
+      v = key & 15;
+      const int r = out_row(v, hh), ks = o / 8;
+      _Float16* tb = base + (int64_t)t * 128 * D;
+      *reinterpret_cast<f16x8*>(tb + ((((st * 2 + kh) * KS + ks) * 32 + r) * 8)) = lo;
+      *reinterpret_cast<f16x8*>(tb + ((((st * 2 + kh) * KS + ks + 1) * 32 + r) * 8)) = hi;
+    }
+  }
+}
+
+
+template <int D, int VF>
+struct LdsLayout {
+  static constexpr int K_BYTES = KEY_TILE * D * 2;
+  static constexpr int V_BYTES = VF == VF_MXFP4 ? KEY_TILE * D / 2 : KEY_TILE * D;
+  static constexpr int VS_BYTES = VF == VF_MXFP4 ? D * 4 : 0;
+  static constexpr int STAGE = K_BYTES + V_BYTES + VS_BYTES;
+  static constexpr int TOTAL = 2 * STAGE;
+};
+
+template <int D, int PF, int VF, bool CAUSAL, bool DEBUG>
+__global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
+  constexpr int KS = D / 16;           // k-steps of the S MFMA
+  constexpr int DT = D / 32;           // 32-row tiles of O^T
+  constexpr int HALF = D / 2;
+  using L = LdsLayout<D, VF>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  // ---- workgroup -> (batch, head, query block); XCD-grouped so that the
+  // query blocks of one head share an L2.
+  const int nwg = gridDim.x;
+  int lin = blockIdx.x;
+  if ((nwg & 7) == 0) lin = (lin & 7) * (nwg >> 3) + (lin >> 3);
+  int qb = lin % p.QB;
+  const int h = (lin / p.QB) % p.Hq;
+  const int b = lin / (p.QB * p.Hq);
+  if (CAUSAL) qb = p.QB - 1 - qb;      // longest rows first
+  const bool varlen = p.cu_q != nullptr;
+  const int64_t tq0 = varlen ? p.cu_q[b] : (int64_t)b * p.Nq;
+  const int64_t tk0 = varlen ? p.cu_k[b] : (int64_t)b * p.Nk;
+  const int len_q = varlen ? p.cu_q[b + 1] - p.cu_q[b] : p.Nq;
+  const int len_k = varlen ? p.cu_k[b + 1] - p.cu_k[b] : p.Nk;
+  if (qb * WG_Q >= len_q) return;
+  const int hk = h / (p.Hq / p.Hkv);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hh = lane >> 5, ql = lane & 31;
+  const int q0 = qb * WG_Q + wave * WAVE_Q;     // first query of this wave
+  const int my_q = q0 + ql;
+  const bool wave_active = q0 < len_q;
+
+  int n_tiles = (len_k + KEY_TILE - 1) / KEY_TILE;
+  if (CAUSAL) {
+    const int last_q = min(qb * WG_Q + WG_Q, len_q) - 1;
+    n_tiles = min(n_tiles, last_q / KEY_TILE + 1);
+  }
+
+  // ---- scalars: c = sigma * log2(e) * gq * gk
+  const float cc = (float)((double)p.sigma * 1.4426950408889634 * (double)(*p.gq) * (double)(*p.gk));
+  const float vscale = VF == VF_FP8 ? *p.sv : 1.0f;
+
+  // ---- Q operand (B of S^T): lane holds query ql, d in [hh*D/2, hh*D/2 + D/2)
+  f16x8 qf[KS];
+  {
+    const int64_t qcol = qcol_offset(varlen, b, tq0, p.nq_pad) + q0;
+    const _Float16* src = p.qhat + ((int64_t)h * p.qcols + qcol) * D + lane * HALF;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (wave_active) qf[ks] = *reinterpret_cast<const f16x8*>(src + 8 * ks);
+      else qf[ks] = f16x8{};
+    }
+  }
+
+  // ---- global -> LDS staging of one key tile (K fp16 tile, V codes, V scales)
+  const int64_t kcol0 = kcol_offset(varlen, b, tk0, p.nk_pad);
+  const uint8_t* ksrc = reinterpret_cast<const uint8_t*>(p.khat + ((int64_t)hk * p.kcols + kcol0) * D);
+  constexpr int K_CHUNKS = L::K_BYTES / 16 / 512;    // 16-byte chunks per thread
+  constexpr int V_UNITS = L::V_BYTES / 16;
+  constexpr int V_CHUNKS = (V_UNITS + 511) / 512;
+  static_assert(L::K_BYTES % (16 * 512) == 0, "K tile must split evenly over the workgroup");
+  u32x4 kreg[K_CHUNKS], vreg[V_CHUNKS];
+  uint32_t sreg = 0;
+  auto load_tile = [&](int t) {
+    const uint8_t* kt = ksrc + (int64_t)t * L::K_BYTES;
+#pragma unroll
+    for (int i = 0; i < K_CHUNKS; ++i) kreg[i] = *reinterpret_cast<const u32x4*>(kt + (i * 512 + tid) * 16);
+#pragma unroll
+    for (int i = 0; i < V_CHUNKS; ++i) {
+      const int u = i * 512 + tid;           // destination 16-byte unit in the V tile
+      if (u >= V_UNITS) break;
+      int c, dt, kh, r, part = 0;
+      if (VF == VF_MXFP4) { r = u & 31; kh = (u >> 5) & 1; dt = (u >> 6) % DT; c = (u >> 6) / DT; }
+      else { r = u & 31; kh = (u >> 5) & 1; part = (u >> 6) & 1; dt = (u >> 7) % DT; c = (u >> 7) / DT; }
+      const int d = 32 * dt + r;
+      const int64_t col = kcol0 + (int64_t)t * KEY_TILE;
+      const uint8_t* src;
+      if (VF == VF_MXFP4) src = p.v_codes + (((int64_t)hk * D + d) * p.kcols + col + 64 * c + 32 * kh) / 2;
+      else src = p.v_codes + ((int64_t)hk * D + d) * p.kcols + col + 64 * c + 16 * kh + 32 * part;
+      vreg[i] = *reinterpret_cast<const u32x4*>(src);
+    }
+    if (VF == VF_MXFP4 && tid < D) {
+      const int64_t col = kcol0 + (int64_t)t * KEY_TILE;
+      sreg = *reinterpret_cast<const uint32_t*>(p.v_scales + ((int64_t)hk * D + tid) * (p.kcols / 32) + col / 32);
+    }
+  };
+  auto store_tile = [&](int stage) {
+    uint8_t* base = smem + stage * L::STAGE;
+#pragma unroll
+    for (int i = 0; i < K_CHUNKS; ++i) *reinterpret_cast<u32x4*>(base + (i * 512 + tid) * 16) = kreg[i];
+#pragma unroll
+    for (int i = 0; i < V_CHUNKS; ++i)
+      if (i * 512 + tid < V_UNITS) *reinterpret_cast<u32x4*>(base + L::K_BYTES + (i * 512 + tid) * 16) = vreg[i];
+    if (VF == VF_MXFP4 && tid < D) *reinterpret_cast<uint32_t*>(base + L::K_BYTES + L::V_BYTES + tid * 4) = sreg;
+  };
+
+  // ---- accumulators
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) oacc[i] = f32x16{};
+  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
+  float m_run = -__builtin_inff();
+
+  // constant 0/1 operand of the row-sum MFMA (16x16x128, FP4 1.0 = code 2)
+  i32x8 ones = {0, 0, 0, 0, 0, 0, 0, 0};
+  {
+    const int row = lane & 15, g = lane >> 4;
+    const bool r0 = (row == 0 || row == 8), r1 = (row == 4 || row == 12);
+    if (PF == PF_MXFP4) {
+      // rows 0/8 sum k-blocks {0,2}, rows 4/12 k-blocks {1,3}; lane holds k = 32g + [0,32)
+      const bool on = (r0 && (g == 0 || g == 2)) || (r1 && (g == 1 || g == 3));
+      if (on) { ones[0] = ones[1] = ones[2] = ones[3] = 0x22222222; }
+    } else {
+      // FP8 P: rows 0/8 sum k with k%32 < 16, rows 4/12 k%32 >= 16
+      if (r0) { ones[0] = ones[1] = 0x22222222; }
+      if (r1) { ones[2] = ones[3] = 0x22222222; }
+    }
+  }
+
+  if (n_tiles > 0) { load_tile(0); store_tile(0); }
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int stage = t & 1;
+    if (t + 1 < n_tiles) load_tile(t + 1);
+    const uint8_t* sK = smem + stage * L::STAGE;
+    const uint8_t* sV = sK + L::K_BYTES;
+    const uint32_t* sVS = reinterpret_cast<const uint32_t*>(sV + L::V_BYTES);
+    const int key0 = t * KEY_TILE;
+    bool wave_work = wave_active;
+    if (CAUSAL) wave_work = wave_work && (key0 <= q0 + WAVE_Q - 1);
+    if (wave_work) {
+      // ---- S^T = K Q^T for 4 sub-tiles of 32 keys
+      f32x16 s[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        s[st] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const f16x8 a = *reinterpret_cast<const f16x8*>(sK + ((((st * 2 + hh) * KS + ks) * 32 + ql) * 16));
+          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ks], s[st], 0, 0, 0);
+        }
+      }
+      // ---- masking (tail of the sequence, causal diagonal)
+      const bool need_mask = (key0 + KEY_TILE > len_k) || (CAUSAL && key0 + KEY_TILE - 1 > q0);
+      if (need_mask) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int key = key0 + s_key<PF>(st, v, hh);
+            const bool dead = key >= len_k || (CAUSAL && key > my_q);
+            if (dead) s[st][v] = -__builtin_inff();
+          }
+      }
+      // ---- block maxima (per lane: chunk c = sub-tiles 2c, 2c+1) and row max
+      float bm[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        float m0 = s[2 * c][0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) m0 = __builtin_fmaxf(m0, s[2 * c][v]);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) m0 = __builtin_fmaxf(m0, s[2 * c + 1][v]);
+        bm[c] = m0;
+      }
+      float rmax = __builtin_fmaxf(bm[0], bm[1]);
+      rmax = __builtin_fmaxf(rmax, __shfl_xor(rmax, 32, 64));
+      const float tmax = rmax * cc;                       // max of fl(S*c) (c > 0)
+      const float m_new = __builtin_fmaxf(m_run, tmax);
+      const bool row_dead = m_new == -__builtin_inff();
+      const float alpha = row_dead ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      // ---- encode P, lane-local
+      i32x8 pk[2];
+      int psc[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        pk[c] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        float me;
+        if (PF == PF_MXFP4) {
+          const float xmax = bm[c] * cc - m_new;          // fl(fl(S*c) - m'), no contraction
+          const float fl = __builtin_floorf(xmax);
+          const int e = fl < -125.0f ? -127 : (int)fl - 2; // also -inf (no live key)
+          psc[c] = e + 127;
+          me = row_dead ? 0.0f : m_new + (float)e;
+        } else {
+          psc[c] = 127;
+          me = row_dead ? 0.0f : m_new;
+        }
+        if (PF == PF_MXFP4) {
+          uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int v = 0; v < 16; v += 2) {
+              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v], cc, -me));
+              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v + 1], cc, -me));
+              const int j = 16 * s2 + v;                  // key index within the lane's block
+              const int word = j >> 3, byte = (j >> 1) & 3;
+              if (byte == 0) w[word] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[word], p0, p1, 1.0f, 0);
+              else if (byte == 1) w[word] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[word], p0, p1, 1.0f, 1);
+              else if (byte == 2) w[word] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[word], p0, p1, 1.0f, 2);
+              else w[word] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[word], p0, p1, 1.0f, 3);
+            }
+          pk[c][0] = (int)w[0]; pk[c][1] = (int)w[1]; pk[c][2] = (int)w[2]; pk[c][3] = (int)w[3];
+        } else {
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int v = 0; v < 16; v += 4) {
+              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v], cc, -me));
+              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v + 1], cc, -me));
+              const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v + 2], cc, -me));
+              const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v + 3], cc, -me));
+              int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+              wv = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wv, true);
+              pk[c][4 * s2 + v / 4] = wv;
+            }
+        }
+      }
+      // ---- rescale running state (skipped when no row of the wave changed max)
+      if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
+        lacc[0] *= alpha;
+      }
+      m_run = m_new;
+      // ---- O^T += V^T P^T and l += sum(P)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          i32x8 a;
+          int sa = 127;
+          if (VF == VF_MXFP4) {
+            const u32x4 av = *reinterpret_cast<const u32x4*>(sV + ((((c * DT + dt) * 2 + hh) * 32 + ql) * 16));
+            a = i32x8{(int)av[0], (int)av[1], (int)av[2], (int)av[3], 0, 0, 0, 0};
+            sa = (int)((sVS[32 * dt + ql] >> (8 * (2 * c + hh))) & 0xFFu);
+            oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pk[c], oacc[dt], 4, PF == PF_MXFP4 ? 4 : 0,
+                                                                       0, sa, 0, psc[c]);
+          } else {
+            const int u0 = ((((c * DT + dt) * 2 + 0) * 2 + hh) * 32 + ql) * 16;
+            const int u1 = ((((c * DT + dt) * 2 + 1) * 2 + hh) * 32 + ql) * 16;
+            const u32x4 a0 = *reinterpret_cast<const u32x4*>(sV + u0);
+            const u32x4 a1 = *reinterpret_cast<const u32x4*>(sV + u1);
+            a = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+            oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pk[c], oacc[dt], 0, PF == PF_MXFP4 ? 4 : 0,
+                                                                       0, 127, 0, psc[c]);
+          }
+        }
+        lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pk[c], lacc, 4, PF == PF_MXFP4 ? 4 : 0, 0, 127, 0,
+                                                               psc[c]);
+      }
+      if (DEBUG && b == p.dbg_b && h == p.dbg_h && my_q < len_q) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int64_t row = (int64_t)my_q * p.dbg_ld;
+          if (PF == PF_MXFP4) {
+            const int key = key0 + 64 * c + 32 * hh;
+            *reinterpret_cast<u32x4*>(p.dbg_codes + (row + key) / 2) =
+                u32x4{(uint32_t)pk[c][0], (uint32_t)pk[c][1], (uint32_t)pk[c][2], (uint32_t)pk[c][3]};
+            p.dbg_scales[(row + key) / 32] = (uint8_t)psc[c];
+          } else {
+            const int key = key0 + 64 * c + 16 * hh;
+            *reinterpret_cast<u32x4*>(p.dbg_codes + row + key) =
+                u32x4{(uint32_t)pk[c][0], (uint32_t)pk[c][1], (uint32_t)pk[c][2], (uint32_t)pk[c][3]};
+            *reinterpret_cast<u32x4*>(p.dbg_codes + row + key + 32) =
+                u32x4{(uint32_t)pk[c][4], (uint32_t)pk[c][5], (uint32_t)pk[c][6], (uint32_t)pk[c][7]};
+          }
+        }
+      }
+    }
+    if (t + 1 < n_tiles) store_tile(stage ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = o / l (x FP8 V tensor scale), LSE = ln2 * (m + log2 l)
+  if (!wave_active || my_q >= len_q) return;
+  const float l = lacc[0];
+  const bool empty = !(l > 0.0f);
+  const float inv = empty ? 0.0f : vscale / l;
+  const int64_t orow = ((tq0 + my_q) * p.Hq + h) * (int64_t)D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d = 32 * dt + 8 * j + 4 * hh;
+      f32x4 v = {oacc[dt][4 * j] * inv, oacc[dt][4 * j + 1] * inv, oacc[dt][4 * j + 2] * inv, oacc[dt][4 * j + 3] * inv};
+      if (p.o_f32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o) + orow + d) = v;
+      } else {
+        uint32_t u[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          uint32_t x = __float_as_uint(v[k]);
+          u[k] = (x + 0x7FFFu + ((x >> 16) & 1u)) >> 16;   // round to nearest even
+        }
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.o) + orow + d) = u32x2{u[0] | (u[1] << 16), u[2] | (u[3] << 16)};
+      }
+    }
+  if (p.lse != nullptr && hh == 0) {
+    const float lse = empty ? -__builtin_inff() : 0.6931471805599453f * (m_run + __builtin_log2f(l));
+    if (varlen) p.lse[(int64_t)h * (p.cu_q[p.B]) + tq0 + my_q] = lse;
+    else p.lse[((int64_t)b * p.Hq + h) * p.Nq + my_q] = lse;
+  }
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_expand(bool is_q, const uint8_t* codes, const uint8_t* scales, int H, int B, int N, int max_len,
+                         const int32_t* cu, int64_t n_pad, int64_t cols, int D, int pf, _Float16* out, hipStream_t st) {
+  dim3 grid((unsigned)((max_len + 127) / 128), (unsigned)H, (unsigned)B);
+  if (grid.x == 0) return hipSuccess;
+#define EX(Q, DD, P) \
+  hipLaunchKernelGGL((expand_nvfp4_kernel<Q, DD, P>), grid, dim3(256), 0, st, codes, scales, H, N, cu, n_pad, cols, out)
+  if (is_q) {
+    if (D == 64) EX(true, 64, 0); else EX(true, 128, 0);
+  } else if (pf == PF_MXFP4) {
+    if (D == 64) EX(false, 64, 0); else EX(false, 128, 0);
+  } else {
+    if (D == 64) EX(false, 64, 1); else EX(false, 128, 1);
+  }
+#undef EX
+  return hipGetLastError();
+}
+
+template <int D, int PF, int VF, bool CAUSAL, bool DEBUG>
+static hipError_t launch_fwd_t(const FwdParams& p, int nwg, hipStream_t st) {
+  auto kern = fwd_lowp_kernel<D, PF, VF, CAUSAL, DEBUG>;
+  const int lds = LdsLayout<D, VF>::TOTAL;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(512), lds, st, p);
+  return hipGetLastError();
+}
+
+template <int D, int PF, int VF, bool CAUSAL>
+static hipError_t launch_fwd_d(const FwdParams& p, int nwg, bool debug, hipStream_t st) {
+  return debug ? launch_fwd_t<D, PF, VF, CAUSAL, true>(p, nwg, st) : launch_fwd_t<D, PF, VF, CAUSAL, false>(p, nwg, st);
+}
+
+hipError_t launch_fwd_lowp(const FwdParams& p, int D, int pf, int vf, bool causal, bool debug, hipStream_t st) {
+  const int nwg = p.B * p.Hq * p.QB;
+  if (nwg == 0) return hipSuccess;
+  if (pf == PF_MXFP4) {
+    if (vf == VF_MXFP4) return D == 64 ? launch_fwd_d<64, 0, 1, false>(p, nwg, debug, st) : launch_fwd_d<128, 0, 1, false>(p, nwg, debug, st);
+    return D == 64 ? launch_fwd_d<64, 0, 0, false>(p, nwg, debug, st) : launch_fwd_d<128, 0, 0, false>(p, nwg, debug, st);
+  }
+  if (causal) return D == 64 ? launch_fwd_d<64, 1, 0, true>(p, nwg, debug, st) : launch_fwd_d<128, 1, 0, true>(p, nwg, debug, st);
+  return D == 64 ? launch_fwd_d<64, 1, 0, false>(p, nwg, debug, st) : launch_fwd_d<128, 1, 0, false>(p, nwg, debug, st);
+}
+
+}  // namespace attn

@@ -1,0 +1,204 @@
+// Quantizers of the Direct-P attention forward (gfx950).
+//
+// NVFP4 for Q and K and FP8 E4M3 / MXFP4 for V, following "Hardware-Aware FP4
+// FlashAttention-4" (summary page, "What the paper found": NVFP4 Q/K, FP4 or
+// FP8 P/V).  The page gives only the format names; the rules implemented here
+// are the NVFP4 and OCP MX conventions stated in include/attn_fp4.h, with
+// every step an IEEE float32 operation so the codes are reproducible bit for
+// bit.  All kernels are HBM-bound: each reads its bf16 input once for the
+// per-tensor amax and once for the encode.
+#include "common.h"
+
+namespace attn {
+
+constexpr int AMAX_THREADS = 256;
+constexpr int AMAX_MAX_PARTIALS = 512;
+
+// Pass 1: per-workgroup max |x| over a bf16 array of n elements (n % 8 == 0).
+__global__ void __launch_bounds__(AMAX_THREADS) amax_partials_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                                     float* __restrict__ partials) {
+  float m = 0.0f;
+  const int64_t n8 = n / 8;
+  const u32x4* x8 = reinterpret_cast<const u32x4*>(x);
+  for (int64_t i = blockIdx.x * (int64_t)AMAX_THREADS + threadIdx.x; i < n8; i += (int64_t)gridDim.x * AMAX_THREADS) {
+    u32x4 v = __builtin_nontemporal_load(&x8[i]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m = __builtin_fmaxf(m, __builtin_fabsf(bf16_bits_to_f32(v[j] & 0xFFFFu)));
+      m = __builtin_fmaxf(m, __builtin_fabsf(bf16_bits_to_f32(v[j] >> 16)));
+    }
+  }
+  m = wave_max(m);
+  __shared__ float red[AMAX_THREADS / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+    for (int w = 1; w < AMAX_THREADS / 64; ++w) r = __builtin_fmaxf(r, red[w]);
+    partials[blockIdx.x] = r;
+  }
+}
+
+// Reduce the pass-1 partials (every workgroup of pass 2 does this itself; at
+// most AMAX_MAX_PARTIALS floats, read from L2).
+__device__ inline float reduce_partials(const float* partials, int np) {
+  __shared__ float red[8];
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < np; i += blockDim.x) m = __builtin_fmaxf(m, partials[i]);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float r = red[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) r = __builtin_fmaxf(r, red[w]);
+  __syncthreads();
+  return r;
+}
+
+// top / amax, 1 for amax == 0, FLT_MAX when the quotient overflows.
+__device__ inline float encode_scale(float amax, float top) {
+  if (amax == 0.0f) return 1.0f;
+  float s = top / amax;
+  return __builtin_isinf(s) ? 3.40282347e+38f : s;
+}
+
+// Pass 2 (NVFP4): one thread per 16-element block along D.
+__global__ void __launch_bounds__(256) quant_nvfp4_kernel(const uint16_t* __restrict__ x, int64_t nblocks,
+                                                          const float* __restrict__ partials, int np,
+                                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                          float* __restrict__ tensor_scale) {
+  const float amax_t = reduce_partials(partials, np);
+  const float s_enc = encode_scale(amax_t, 2688.0f);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = 1.0f / s_enc;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nblocks; i += (int64_t)gridDim.x * blockDim.x) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(x + 16 * i);
+    u32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = bf16_bits_to_f32(a[j] & 0xFFFFu);
+      v[2 * j + 1] = bf16_bits_to_f32(a[j] >> 16);
+      v[8 + 2 * j] = bf16_bits_to_f32(b[j] & 0xFFFFu);
+      v[8 + 2 * j + 1] = bf16_bits_to_f32(b[j] >> 16);
+    }
+    float amax_b = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) amax_b = __builtin_fmaxf(amax_b, __builtin_fabsf(v[j]));
+    const float sf = (amax_b / 6.0f) * s_enc;
+    const uint32_t sc = e4m3_encode(sf);
+    const float sv = e4m3_decode(sc);
+    u32x2 out = {0u, 0u};
+    if (sv > 0.0f) {
+      const float enc = s_enc / sv;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        uint32_t c = e2m1_encode(v[j] * enc);
+        out[j >> 3] |= c << (4 * (j & 7));
+      }
+    }
+    *reinterpret_cast<u32x2*>(codes + 8 * i) = out;
+    scales[i] = (uint8_t)sc;
+  }
+}
+
+// Pass 2 (V): one workgroup per (128-key tile, kv head, sequence).  The tile
+// is staged in LDS, then each thread encodes one (channel, 32-key block) and
+// writes it key-contiguous.  FMT 0 = FP8 E4M3 (per-tensor scale), 1 = MXFP4.
+template <int FMT, int D>
+__global__ void __launch_bounds__(256) quant_v_kernel(const uint16_t* __restrict__ v, int Nk, int Hkv,
+                                                      const int32_t* __restrict__ cu_k, int64_t nk_pad, int64_t cols,
+                                                      const float* __restrict__ partials, int np,
+                                                      uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                      float* __restrict__ tensor_scale) {
+  const int tile = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const bool varlen = cu_k != nullptr;
+  const int64_t tok0 = varlen ? cu_k[s] : (int64_t)s * Nk;
+  const int len = varlen ? cu_k[s + 1] - cu_k[s] : Nk;
+  float enc = 1.0f;
+  if (FMT == 0) {
+    const float amax = reduce_partials(partials, np);
+    enc = encode_scale(amax, 448.0f);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *tensor_scale = 1.0f / enc;
+  }
+  if (tile * KEY_TILE >= len) return;
+  __shared__ uint16_t tileb[KEY_TILE * D];
+  // stage: 128 keys x D bf16, zero beyond the end of the sequence
+  constexpr int CH = KEY_TILE * D / 8;  // 16-byte chunks
+  for (int c = threadIdx.x; c < CH; c += 256) {
+    const int key = c / (D / 8), part = c % (D / 8);
+    u32x4 val = {0u, 0u, 0u, 0u};
+    const int kg = tile * KEY_TILE + key;
+    if (kg < len) val = *reinterpret_cast<const u32x4*>(v + ((tok0 + kg) * Hkv + h) * (int64_t)D + part * 8);
+    *reinterpret_cast<u32x4*>(&tileb[key * D + part * 8]) = val;
+  }
+  __syncthreads();
+  const int64_t col0 = kcol_offset(varlen, s, tok0, nk_pad) + (int64_t)tile * KEY_TILE;
+  for (int p = threadIdx.x; p < D * 4; p += 256) {
+    const int d = p >> 2, blk = p & 3;
+    float x[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) x[j] = bf16_bits_to_f32(tileb[(blk * 32 + j) * D + d]);
+    const int64_t row = (int64_t)h * D + d;
+    if (FMT == 0) {
+      u32x4 o0 = {0u, 0u, 0u, 0u}, o1 = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 16; ++j) o0[j >> 2] |= e4m3_encode(x[j] * enc) << (8 * (j & 3));
+#pragma unroll
+      for (int j = 0; j < 16; ++j) o1[j >> 2] |= e4m3_encode(x[16 + j] * enc) << (8 * (j & 3));
+      u32x4* dst = reinterpret_cast<u32x4*>(codes + row * cols + col0 + blk * 32);
+      dst[0] = o0;
+      dst[1] = o1;
+    } else {
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[j]));
+      const uint32_t ab = __float_as_uint(amax);
+      const int E = (int)(ab >> 23) - 127;              // floor(log2 amax) for normal amax
+      int e = (ab >> 23) == 0 ? -127 : E - 2;           // zero/subnormal block max -> -127
+      e = e < -127 ? -127 : e;
+      const float inv = __builtin_amdgcn_ldexpf(1.0f, -e);
+      u32x4 o = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 32; ++j) o[j >> 3] |= e2m1_encode(x[j] * inv) << (4 * (j & 7));
+      *reinterpret_cast<u32x4*>(codes + (row * cols + col0 + blk * 32) / 2) = o;
+      scales[row * (cols / 32) + (col0 + blk * 32) / 32] = (uint8_t)(e + 127);
+    }
+  }
+}
+
+// ---- host launchers (called from api.cpp) ----
+hipError_t launch_amax(const void* x, int64_t n, float* partials, int* np_out, hipStream_t st) {
+  int64_t want = (n / 8 + AMAX_THREADS * 8 - 1) / (AMAX_THREADS * 8);
+  int np = (int)(want < 1 ? 1 : (want > AMAX_MAX_PARTIALS ? AMAX_MAX_PARTIALS : want));
+  *np_out = np;
+  hipLaunchKernelGGL(amax_partials_kernel, dim3(np), dim3(AMAX_THREADS), 0, st, (const uint16_t*)x, n, partials);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_nvfp4(const void* x, int64_t rows, int D, const float* partials, int np, uint8_t* codes,
+                              uint8_t* scales, float* tensor_scale, hipStream_t st) {
+  int64_t nblocks = rows * (D / 16);
+  int64_t want = (nblocks + 255) / 256;
+  int grid = (int)(want < 1 ? 1 : (want > 8192 ? 8192 : want));
+  hipLaunchKernelGGL(quant_nvfp4_kernel, dim3(grid), dim3(256), 0, st, (const uint16_t*)x, nblocks, partials, np, codes,
+                     scales, tensor_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_v(const void* v, int B, int Nk, int Hkv, int D, const int32_t* cu_k, int max_len, int64_t cols,
+                          int fmt, const float* partials, int np, uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                          hipStream_t st) {
+  const int64_t nk_pad = roundup(Nk, KEY_TILE);
+  dim3 grid((unsigned)((max_len + KEY_TILE - 1) / KEY_TILE), (unsigned)Hkv, (unsigned)B);
+  if (grid.x == 0) grid.x = 1;
+#define QV(F, DD)                                                                                           \
+  hipLaunchKernelGGL((quant_v_kernel<F, DD>), grid, dim3(256), 0, st, (const uint16_t*)v, Nk, Hkv, cu_k, nk_pad, \
+                     cols, partials, np, codes, scales, tensor_scale)
+  if (fmt == 0 && D == 64) QV(0, 64);
+  else if (fmt == 0 && D == 128) QV(0, 128);
+  else if (fmt == 1 && D == 64) QV(1, 64);
+  else QV(1, 128);
+#undef QV
+  return hipGetLastError();
+}
+
+}  // namespace attn

@@ -1,0 +1,118 @@
+"""The C ABI library loads, exports every function include/attn_fp4.h declares,
+and rejects bad arguments on the host (no GPU work is launched by these calls)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import precision_attention_forward_amd as paf
+from precision_attention_forward_amd import _binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "attn_fp4.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", src)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(paf.LIB_PATH):
+        pytest.fail("libattnfp4.so is not built (run __graft_entry__.build())")
+    return paf.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert "attn_fwd_directp" in names and "attn_quant_nvfp4" in names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in attn_fp4.h but not exported"
+    assert set(names) == set(B.EXPORTS), "binding and header disagree"
+
+
+def test_struct_layout_matches_header():
+    # attn_fwd_args as laid out by the compiler for the C declaration
+    assert ctypes.sizeof(B.FwdArgs) == 4 * 6 + 8 * 2 + 8 * 2 + 4 + 4 + 24 * 2 + 32 + 8 + 4 + 4 + 8 + 8 + 8 + 8 + 8 + 4 + 4
+
+
+def test_status_strings_and_constants(lib):
+    assert lib.attn_status_str(0) == b"ok"
+    assert lib.attn_status_str(1) == b"invalid argument"
+    assert lib.attn_status_str(3) == b"workspace missing or too small"
+    assert lib.attn_quant_ws_bytes() >= 2048
+    assert lib.attn_version().startswith(b"attn_fp4")
+
+
+def test_v_cols(lib):
+    assert lib.attn_v_cols(2, 300, 0, 0) == 2 * 384
+    assert lib.attn_v_cols(1, 32760, 0, 0) == 32768
+    assert lib.attn_v_cols(3, 100, 1000, 1) == 128 * (8 + 3)
+    # every varlen sequence fits: start 128*(cu//128 + s), length roundup(len, 128)
+    import numpy as np
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        lens = rng.integers(0, 700, size=rng.integers(1, 9))
+        cu = np.concatenate([[0], np.cumsum(lens)])
+        cols = lib.attn_v_cols(len(lens), int(lens.max()), int(cu[-1]), 1)
+        ends = [128 * (cu[s] // 128 + s) + (lens[s] + 127) // 128 * 128 for s in range(len(lens))]
+        starts = [128 * (cu[s] // 128 + s) for s in range(len(lens))]
+        assert max(ends) <= cols
+        assert all(ends[s] <= starts[s + 1] for s in range(len(lens) - 1))
+
+
+def test_quant_rejects_bad_arguments_without_launching(lib):
+    ws = ctypes.create_string_buffer(4096)
+    ts = ctypes.c_float()
+    # D not a multiple of 16
+    assert lib.attn_quant_nvfp4(None, 4, 24, None, None, ctypes.byref(ts), ws, 4096, None) == 1
+    # missing input pointer for a non-empty tensor
+    assert lib.attn_quant_nvfp4(None, 4, 64, None, None, ctypes.byref(ts), ws, 4096, None) == 1
+    # workspace too small
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.attn_quant_nvfp4(fake, 4, 64, fake, fake, ctypes.byref(ts), ws, 16, None) == 3
+    # V: unsupported head dim, bad format
+    assert lib.attn_quant_v(fake, 1, 8, 1, 96, None, 0, 0, fake, None, ctypes.byref(ts), ws, 4096, None) == 1
+    assert lib.attn_quant_v(fake, 1, 8, 1, 64, None, 0, 7, fake, None, ctypes.byref(ts), ws, 4096, None) == 1
+
+
+def _args(**kw):
+    a = B.FwdArgs()
+    a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.D = 1, 4, 2, 256, 256, 128
+    a.softmax_scale = 0.125
+    p = 1 << 24
+    a.q = B._NvTensor(p, p, p)
+    a.k = B._NvTensor(p, p, p)
+    a.v = B._VTensor(0, p, p, p)
+    a.o = p
+    a.o_dtype = 1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_fwd_validation(lib):
+    a = _args()
+    need = lib.attn_fwd_ws_bytes(ctypes.byref(a))
+    # Q fp16 tiles (4 heads x 256 rows x 128) + K tiles (2 heads x 256 x 128), 2 bytes each
+    assert need == 2 * 128 * (4 * 256 + 2 * 256) + 256
+    a.ws, a.ws_bytes = 1 << 24, need
+    assert lib.attn_fwd_directp(ctypes.byref(_args(D=96, ws=1 << 24, ws_bytes=need)), None) == 1
+    assert lib.attn_fwd_directp(ctypes.byref(_args(Hkv=3, ws=1 << 24, ws_bytes=need)), None) == 1
+    assert lib.attn_fwd_directp(ctypes.byref(_args(causal=1, ws=1 << 24, ws_bytes=need)), None) == 2
+    assert lib.attn_fwd_fp8pv(ctypes.byref(_args(causal=1, Nk=128, ws=1 << 24, ws_bytes=need)), None) == 1
+    assert lib.attn_fwd_fp8pv(ctypes.byref(_args(v=B._VTensor(1, 1 << 24, 1 << 24, 1 << 24), ws=1 << 24,
+                                                 ws_bytes=need)), None) == 2
+    assert lib.attn_fwd_directp(ctypes.byref(_args(ws=1 << 24, ws_bytes=need - 1)), None) == 3
+    assert lib.attn_fwd_directp(ctypes.byref(_args(softmax_scale=0.0, ws=1 << 24, ws_bytes=need)), None) == 1
+    assert lib.attn_fwd_directp(ctypes.byref(_args(o=None, ws=1 << 24, ws_bytes=need)), None) == 1
+    assert lib.attn_fwd_directp(None, None) == 1
+    # varlen needs both cu_seqlens
+    assert lib.attn_fwd_directp(ctypes.byref(_args(cu_seqlens_q=1 << 24, ws=1 << 24, ws_bytes=need)), None) == 1
+    # bf16 baseline argument checks
+    assert lib.attn_fwd_bf16(None, None, None, None, None, 1, 4, 3, 16, 16, 128, 0.1, 0, None) == 1
+    assert lib.attn_fwd_bf16(None, None, None, None, None, 1, 4, 4, 16, 16, 80, 0.1, 0, None) == 1
