@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Throughput of the Direct-P FP4 attention forward on one MI355X.
+
+One step is the whole hot path over one batch of synthetic inputs already
+resident in HBM: NVFP4 quantization of Q and K, quantization of V, and the
+forward (Q/K expansion pre-pass + attention kernel).  Default workload: the
+Wan2.1-14B-shaped video self-attention (B=1, H=40, N=32760, D=128,
+noncausal, MXFP4 P and V).  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload 1..5]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MXFP4_PEAK_TFLOPS = 10066.3        # MI355X dense MXFP4/MXFP6 MFMA peak
+FP8_PEAK_TFLOPS = 5033.2
+BF16_PEAK_TFLOPS = 2516.6
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2, help="1..5 (default 2: Wan2.1-14B shape)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows of the oracle sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(inp, rows):
+    """Time the CPU oracle (as it stands) on a bounded sample: one (batch,
+    head), `rows` query rows against all keys, including the sample's
+    quantization.  Returns a dict for the JSON line."""
+    import numpy as np
+    from oracle import attention as OA, quant as OQ
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = os.cpu_count() or 1
+    wl = inp.wl
+    if inp.cu_seqlens is None:
+        Nk = wl.N
+        qh, kh, vh = inp.q[0, :, 0], inp.k[0, :, 0], inp.v[0, :, 0]
+    else:
+        s = int(np.argmax(inp.seqlens))
+        t0, Nk = int(inp.cu_seqlens[s]), int(inp.seqlens[s])
+        qh, kh, vh = inp.q[t0:t0 + Nk, 0], inp.k[t0:t0 + Nk, 0], inp.v[t0:t0 + Nk, 0]
+    R = min(rows, qh.shape[0])
+    idx = np.linspace(0, qh.shape[0] - 1, R).astype(np.int64)
+    qf = qh.float().cpu().numpy()[idx]
+    kf = kh.float().cpu().numpy()
+    vf = vh.float().cpu().numpy()
+    t = time.perf_counter()
+    qc, qs, gq = OQ.quant_nvfp4(qf)
+    kc, ks, gk = OQ.quant_nvfp4(kf)
+    if wl.v_format == "fp8":
+        vcodes, s_v = OQ.quant_v_fp8(vf)
+        vhat = OQ.dequant_v_fp8(vcodes, s_v)
+    else:
+        vcodes, ve = OQ.quant_v_mxfp4(vf[:, None, :])
+        vhat = OQ.dequant_v_mxfp4(vcodes, ve)[:, 0, :]
+    OA.attn_lowp_head(OQ.dequant_nvfp4_raw(qc, qs), OQ.dequant_nvfp4_raw(kc, ks), gq, gk, vhat, inp.sigma,
+                      wl.p_format, wl.causal, q_index=idx)
+    dt = time.perf_counter() - t
+    live = sum(min(int(i) + 1, Nk) for i in idx) if wl.causal else R * Nk
+    flops = 4.0 * live * wl.D
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"1 head, {R} query rows x {Nk} keys of workload {wl.name} (NVFP4/V quantization of the "
+                      f"sample included), {dt:.1f} s; numpy float64, BLAS threads = cores"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import precision_attention_forward_amd as paf
+    from precision_attention_forward_amd import synth
+
+    paf.load_library()
+    wl = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = synth.generate(wl, dev)
+    varlen = inp.cu_seqlens is not None
+    vfmt = paf.V_FP8 if wl.v_format == "fp8" else paf.V_MXFP4
+    fwd = paf.fwd_directp if wl.p_format == "mxfp4" else paf.fwd_fp8pv
+    kw = dict(Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D, softmax_scale=inp.sigma, causal=wl.causal, out_dtype=torch.bfloat16)
+    if varlen:
+        cu = inp.cu_seqlens.to(dev)
+        mx = int(inp.seqlens.max())
+        kw.update(cu_seqlens_q=cu, cu_seqlens_k=cu, max_seqlen_q=mx, max_seqlen_k=mx)
+    else:
+        kw.update(B=wl.B, Nq=wl.N, Nk=wl.N)
+    flops = synth.flops(wl, inp.seqlens)
+    ws = paf.Workspace()
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+
+    def quantize():
+        q = paf.quant_nvfp4(inp.q)
+        k = paf.quant_nvfp4(inp.k)
+        if varlen:
+            vc, vs, vt, _ = paf.quant_v(inp.v, vfmt, cu_seqlens=kw["cu_seqlens_k"], max_seqlen=kw["max_seqlen_k"])
+        else:
+            vc, vs, vt, _ = paf.quant_v(inp.v, vfmt)
+        return q, k, (vfmt, vc, vs, vt)
+
+    def step():
+        q, k, v = quantize()
+        return fwd(q, k, v, workspace=ws, **kw)
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(n):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    for _ in range(args.warmup):
+        step()
+    # (1) the whole step: quantize Q, K, V + forward
+    wall0 = time.perf_counter()
+    ms_step = timed(lambda i: step(), args.steps)
+    wall = time.perf_counter() - wall0
+    value = flops / (ms_step * 1e-3) / 1e12
+    # (2) the forward call alone on stored quantized operands, with HIP events
+    #     around the attention kernel inside it (same stream)
+    qkv = quantize()
+    fwd_ms = timed(lambda i: fwd(*qkv, workspace=ws, events=kev[i], **kw), args.steps)
+    kern_ms = sum(a.elapsed_time(b) for a, b in kev) / args.steps
+    fwd_tflops = flops / (fwd_ms * 1e-3) / 1e12
+    kern_tflops = flops / (kern_ms * 1e-3) / 1e12
+
+    # the in-library BF16 forward on the same bf16 inputs (dense layouts only)
+    bf16 = None
+    if not args.no_bf16 and not varlen:
+        for _ in range(2):
+            paf.fwd_bf16(inp.q, inp.k, inp.v, inp.sigma, causal=wl.causal, want_lse=True)
+        torch.cuda.synchronize()
+        b0 = torch.cuda.Event(enable_timing=True)
+        b1 = torch.cuda.Event(enable_timing=True)
+        b0.record()
+        nb = max(3, args.steps // 2)
+        for _ in range(nb):
+            paf.fwd_bf16(inp.q, inp.k, inp.v, inp.sigma, causal=wl.causal, want_lse=True)
+        b1.record()
+        torch.cuda.synchronize()
+        bf_ms = b0.elapsed_time(b1) / nb
+        bf16 = {"ms": bf_ms, "tflops": flops / (bf_ms * 1e-3) / 1e12}
+
+    # dominant kernel roofline: the attention kernel is MFMA bound
+    pv_peak = MXFP4_PEAK_TFLOPS if wl.v_format == "mxfp4" else FP8_PEAK_TFLOPS
+    # mixed ceiling: QK^T runs on the FP16 MFMA (exact NVFP4), P.V at the P/V format rate
+    qk_rate, pv_rate = BF16_PEAK_TFLOPS, (pv_peak if wl.p_format == "mxfp4" else FP8_PEAK_TFLOPS)
+    ceiling = 1.0 / (0.5 / qk_rate + 0.5 / pv_rate)
+    roofline = {"bound": "mfma", "achieved": round(kern_tflops, 2), "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(kern_tflops / MXFP4_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "fwd_lowp_kernel", "kernel_ms": round(kern_ms, 4),
+                "mixed_ceiling_tflops": round(ceiling, 1), "frac_of_mixed_ceiling": round(kern_tflops / ceiling, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, args.cpu_rows)
+
+    cfg = {"workload": f"{wl.name}: " + (f"{wl.varlen[0]} packed sequences" if varlen else
+                                         f"B={wl.B} N={wl.N}") +
+           f" Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D} {'causal' if wl.causal else 'noncausal'}, "
+           f"P={wl.p_format.upper()} V={wl.v_format.upper()}",
+           "B": wl.B if not varlen else int(len(inp.seqlens)), "Hq": wl.Hq, "Hkv": wl.Hkv,
+           "N": wl.N if not varlen else int(inp.seqlens.max()), "D": wl.D, "causal": wl.causal,
+           "flops_per_step": flops, "parallelism": "single GPU"}
+    out = {
+        "metric": "Direct-P attn fwd TFLOP/s on 1 MI355X; % of MXFP4 MFMA peak; x BF16 attn",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp4", "data": "synthetic (seeded Gaussian, the workload's outlier recipe)", "config": cfg,
+        "fwd_call_tflops": round(fwd_tflops, 2),
+        "fwd_kernel_tflops": round(kern_tflops, 2),
+        "quantize_ms": round(ms_step - fwd_ms, 4),
+        "pct_mxfp4_peak": round(100 * value / MXFP4_PEAK_TFLOPS, 2),
+        "pct_mxfp4_peak_fwd_call": round(100 * fwd_tflops / MXFP4_PEAK_TFLOPS, 2),
+        "pct_mxfp4_peak_fwd_kernel": round(100 * kern_tflops / MXFP4_PEAK_TFLOPS, 2),
+        "x_bf16": None if bf16 is None else round(fwd_tflops / bf16["tflops"], 3),
+        "x_bf16_incl_quantize": None if bf16 is None else round(value / bf16["tflops"], 3),
+        "bf16_tflops": None if bf16 is None else round(bf16["tflops"], 2),
+        "precision": "NVFP4 Q/K (exact, contracted on the FP16 MFMA), " +
+                     ("MXFP4 E2M1 P (Direct-P)" if wl.p_format == "mxfp4" else "FP8 E4M3 P") +
+                     f", {wl.v_format.upper()} V, FP32 accumulation",
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -172,6 +172,11 @@ typedef struct attn_fwd_args {
   uint8_t* dbg_p_codes;
   uint8_t* dbg_p_scales;
   int32_t dbg_b, dbg_h;
+  /* Optional profiling: hipEvent_t handles (NULL to skip) recorded on
+   * `stream` immediately before and after the attention kernel itself (after
+   * the Q/K expansion pre-pass), so callers can time the dominant kernel. */
+  void* prof_event_begin;
+  void* prof_event_end;
 } attn_fwd_args;
 
 /* Bytes of device workspace the forward needs for these shapes: the exact

@@ -48,6 +48,7 @@ class FwdArgs(ctypes.Structure):
         ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
         ("dbg_p_codes", ctypes.c_void_p), ("dbg_p_scales", ctypes.c_void_p),
         ("dbg_b", ctypes.c_int32), ("dbg_h", ctypes.c_int32),
+        ("prof_event_begin", ctypes.c_void_p), ("prof_event_end", ctypes.c_void_p),
     ]
 
 
@@ -208,7 +209,7 @@ def make_fwd_args(q, k, v, *, B, Hq, Hkv, Nq, Nk, D, softmax_scale, causal=False
 
 def _fwd_lowp(entry, q, k, v, *, Hq, Hkv, D, softmax_scale, causal=False, B=None, Nq=None, Nk=None,
               cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
-              out_dtype=torch.float32, want_lse=True, workspace=None, debug=None):
+              out_dtype=torch.float32, want_lse=True, workspace=None, debug=None, events=None, out=None):
     """Shared driver of attn_fwd_directp / attn_fwd_fp8pv.  Returns (O, LSE, dbg)."""
     lib = load_library()
     dev = q[0].device
@@ -224,8 +225,11 @@ def _fwd_lowp(entry, q, k, v, *, Hq, Hkv, D, softmax_scale, causal=False, B=None
         total_q, total_k = B * Nq, B * Nk
         oshape = (B, Nq, Hq, D)
         lshape = (B, Hq, Nq)
-    o = torch.empty(oshape, dtype=out_dtype, device=dev)
-    lse = torch.empty(lshape, dtype=torch.float32, device=dev) if want_lse else None
+    if out is not None:
+        o, lse = out
+    else:
+        o = torch.empty(oshape, dtype=out_dtype, device=dev)
+        lse = torch.empty(lshape, dtype=torch.float32, device=dev) if want_lse else None
     dbg_codes = dbg_scales = None
     dbg_b = dbg_h = 0
     if debug is not None:
@@ -244,6 +248,9 @@ def _fwd_lowp(entry, q, k, v, *, Hq, Hkv, D, softmax_scale, causal=False, B=None
     need = lib.attn_fwd_ws_bytes(ctypes.byref(a))
     ws = (workspace or _default_ws).get(need, dev)
     a.ws, a.ws_bytes = ws.data_ptr(), ws.numel()
+    if events is not None:
+        a.prof_event_begin = events[0].cuda_event
+        a.prof_event_end = events[1].cuda_event
     _check(getattr(lib, entry)(ctypes.byref(a), _stream()))
     return o, lse, (dbg_codes, dbg_scales)
 

@@ -213,8 +213,15 @@ static attn_status run_fwd_lowp(const attn_fwd_args* a, void* stream, int pf) {
   p.dbg_h = a->dbg_h;
   p.dbg_ld = nk_pad;
   (void)varlen;
-  return hip_status(launch_fwd_lowp(p, a->D, pf, a->v.format == ATTN_V_MXFP4 ? 1 : 0, a->causal != 0,
-                                    a->dbg_p_codes != nullptr, st));
+  if (a->prof_event_begin != nullptr) {
+    e = hipEventRecord((hipEvent_t)a->prof_event_begin, st);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  e = launch_fwd_lowp(p, a->D, pf, a->v.format == ATTN_V_MXFP4 ? 1 : 0, a->causal != 0, a->dbg_p_codes != nullptr,
+                      st);
+  if (e != hipSuccess) return hip_status(e);
+  if (a->prof_event_end != nullptr) e = hipEventRecord((hipEvent_t)a->prof_event_end, st);
+  return hip_status(e);
 }
 
 attn_status attn_fwd_directp(const attn_fwd_args* a, void* stream) { return run_fwd_lowp(a, stream, 0); }

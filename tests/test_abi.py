@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_struct_layout_matches_header():
     # attn_fwd_args as laid out by the compiler for the C declaration
-    assert ctypes.sizeof(B.FwdArgs) == 4 * 6 + 8 * 2 + 8 * 2 + 4 + 4 + 24 * 2 + 32 + 8 + 4 + 4 + 8 + 8 + 8 + 8 + 8 + 4 + 4
+    assert ctypes.sizeof(B.FwdArgs) == 4 * 6 + 8 * 2 + 8 * 2 + 4 + 4 + 24 * 2 + 32 + 8 + 4 + 4 + 8 + 8 + 8 + 8 + 8 + 4 + 4 + 8 + 8
 
 
 def test_status_strings_and_constants(lib):
