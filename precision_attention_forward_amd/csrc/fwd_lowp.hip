@@ -26,6 +26,7 @@
 //    rounded probabilities without any VALU work.
 #include "common.h"
 #include "fwd_params.h"
+#include "pipeline.h"
 
 namespace attn {
 
@@ -136,6 +137,7 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, ql = lane & 31;
+  const int grp = wave >> 2;                    // ping-pong group (1 lags by a phase)
   const int q0 = qb * WG_Q + wave * WAVE_Q;     // first query of this wave
   const int my_q = q0 + ql;
   const bool wave_active = q0 < len_q;
@@ -160,56 +162,71 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
       if (wave_active) qf[ks] = *reinterpret_cast<const f16x8*>(src + 8 * ks);
       else qf[ks] = f16x8{};
     }
+    // make the Q loads complete here, so no vector-memory wait is left for the
+    // pipeline below (it would also wait for the in-flight LDS copies)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[ks]));
   }
 
-  // ---- global -> LDS staging of one key tile (K fp16 tile, V codes, V scales)
+  // ---- LDS stages.  Stage j (slot j % 2) holds the K tile j (read by the
+  // Q.K^T of MFMA phase j) and the V tile j-1 with its scales (read by the
+  // P.V of the same phase).  Copies go global -> LDS directly.
   const int64_t kcol0 = kcol_offset(varlen, b, tk0, p.nk_pad);
   const uint8_t* ksrc = reinterpret_cast<const uint8_t*>(p.khat + ((int64_t)hk * p.kcols + kcol0) * D);
-  constexpr int K_CHUNKS = L::K_BYTES / 16 / 512;    // 16-byte chunks per thread
+  const uint32_t lds0 = lds_address(smem);
+  // per-head bases (per-lane offsets below stay under 4 GiB)
+  const uint8_t* vhead = p.v_codes + (VF == VF_MXFP4 ? (int64_t)hk * D * p.kcols / 2 : (int64_t)hk * D * p.kcols);
+  const uint8_t* shead = VF == VF_MXFP4 ? p.v_scales + (int64_t)hk * D * (p.kcols / 32) : nullptr;
+  constexpr int K_UNITS = L::K_BYTES / 16;
   constexpr int V_UNITS = L::V_BYTES / 16;
-  constexpr int V_CHUNKS = (V_UNITS + 511) / 512;
-  static_assert(L::K_BYTES % (16 * 512) == 0, "K tile must split evenly over the workgroup");
-  u32x4 kreg[K_CHUNKS], vreg[V_CHUNKS];
-  uint32_t sreg = 0;
-  auto load_tile = [&](int t) {
-    const uint8_t* kt = ksrc + (int64_t)t * L::K_BYTES;
+  static_assert(K_UNITS % 512 == 0, "K tile must split evenly over the workgroup");
+  auto issue_stage = [&](int j) {
+    const uint32_t slot = lds0 + (uint32_t)((j & 1) * L::STAGE);
+    if (j < n_tiles) {
 #pragma unroll
-    for (int i = 0; i < K_CHUNKS; ++i) kreg[i] = *reinterpret_cast<const u32x4*>(kt + (i * 512 + tid) * 16);
-#pragma unroll
-    for (int i = 0; i < V_CHUNKS; ++i) {
-      const int u = i * 512 + tid;           // destination 16-byte unit in the V tile
-      if (u >= V_UNITS) break;
-      int c, dt, kh, r, part = 0;
-      if (VF == VF_MXFP4) { r = u & 31; kh = (u >> 5) & 1; dt = (u >> 6) % DT; c = (u >> 6) / DT; }
-      else { r = u & 31; kh = (u >> 5) & 1; part = (u >> 6) & 1; dt = (u >> 7) % DT; c = (u >> 7) / DT; }
-      const int d = 32 * dt + r;
-      const int64_t col = kcol0 + (int64_t)t * KEY_TILE;
-      const uint8_t* src;
-      if (VF == VF_MXFP4) src = p.v_codes + (((int64_t)hk * D + d) * p.kcols + col + 64 * c + 32 * kh) / 2;
-      else src = p.v_codes + ((int64_t)hk * D + d) * p.kcols + col + 64 * c + 16 * kh + 32 * part;
-      vreg[i] = *reinterpret_cast<const u32x4*>(src);
+      for (int i = 0; i < K_UNITS / 512; ++i) {
+        const int u0 = i * 512 + wave * 64;
+        dma16(ksrc, (uint32_t)(j * L::K_BYTES + (u0 + lane) * 16), slot + u0 * 16);
+      }
     }
-    if (VF == VF_MXFP4 && tid < D) {
+    if (j >= 1) {
+      const int t = j - 1;
       const int64_t col = kcol0 + (int64_t)t * KEY_TILE;
-      sreg = *reinterpret_cast<const uint32_t*>(p.v_scales + ((int64_t)hk * D + tid) * (p.kcols / 32) + col / 32);
+#pragma unroll
+      for (int i = 0; i < (V_UNITS + 511) / 512; ++i) {
+        const int u0 = i * 512 + wave * 64;
+        if (u0 < V_UNITS) {
+          const int u = u0 + lane;
+          int c, dt, kh, r, part = 0;
+          if (VF == VF_MXFP4) { r = u & 31; kh = (u >> 5) & 1; dt = (u >> 6) % DT; c = (u >> 6) / DT; }
+          else { r = u & 31; kh = (u >> 5) & 1; part = (u >> 6) & 1; dt = (u >> 7) % DT; c = (u >> 7) / DT; }
+          const int d = 32 * dt + r;
+          uint32_t off;
+          if (VF == VF_MXFP4) off = (uint32_t)((d * p.kcols + col + 64 * c + 32 * kh) / 2);
+          else off = (uint32_t)(d * p.kcols + col + 64 * c + 16 * kh + 32 * part);
+          dma16(vhead, off, slot + L::K_BYTES + u0 * 16);
+        }
+      }
+      if (VF == VF_MXFP4 && wave * 64 < D) {
+        const int d = wave * 64 + lane;
+        dma4(shead, (uint32_t)(d * (p.kcols / 32) + col / 32), slot + L::K_BYTES + L::V_BYTES + wave * 256);
+      }
     }
-  };
-  auto store_tile = [&](int stage) {
-    uint8_t* base = smem + stage * L::STAGE;
-#pragma unroll
-    for (int i = 0; i < K_CHUNKS; ++i) *reinterpret_cast<u32x4*>(base + (i * 512 + tid) * 16) = kreg[i];
-#pragma unroll
-    for (int i = 0; i < V_CHUNKS; ++i)
-      if (i * 512 + tid < V_UNITS) *reinterpret_cast<u32x4*>(base + L::K_BYTES + (i * 512 + tid) * 16) = vreg[i];
-    if (VF == VF_MXFP4 && tid < D) *reinterpret_cast<uint32_t*>(base + L::K_BYTES + L::V_BYTES + tid * 4) = sreg;
   };
 
-  // ---- accumulators
+  // ---- accumulators and per-wave state
   f32x16 oacc[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) oacc[i] = f32x16{};
   f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
   float m_run = -__builtin_inff();
+  f32x16 s[4];
+  i32x8 pk[2];
+  int psc[2] = {127, 127};
+  bool have_s = false, have_p = false;
+#pragma unroll
+  for (int st = 0; st < 4; ++st) s[st] = f32x16{};
+  pk[0] = pk[1] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
 
   // constant 0/1 operand of the row-sum MFMA (16x16x128, FP4 1.0 = code 2)
   i32x8 ones = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -227,133 +244,26 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
     }
   }
 
-  if (n_tiles > 0) { load_tile(0); store_tile(0); }
-  __syncthreads();
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int stage = t & 1;
-    if (t + 1 < n_tiles) load_tile(t + 1);
-    const uint8_t* sK = smem + stage * L::STAGE;
+  // ---- MFMA phase j: P(j-1).V(j-1) then S(j) = K(j) Q^T
+  auto mfma_phase = [&](int j) {
+    const uint8_t* sK = smem + (j & 1) * L::STAGE;
     const uint8_t* sV = sK + L::K_BYTES;
     const uint32_t* sVS = reinterpret_cast<const uint32_t*>(sV + L::V_BYTES);
-    const int key0 = t * KEY_TILE;
-    bool wave_work = wave_active;
-    if (CAUSAL) wave_work = wave_work && (key0 <= q0 + WAVE_Q - 1);
-    if (wave_work) {
-      // ---- S^T = K Q^T for 4 sub-tiles of 32 keys
-      f32x16 s[4];
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        s[st] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const f16x8 a = *reinterpret_cast<const f16x8*>(sK + ((((st * 2 + hh) * KS + ks) * 32 + ql) * 16));
-          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ks], s[st], 0, 0, 0);
-        }
-      }
-      // ---- masking (tail of the sequence, causal diagonal)
-      const bool need_mask = (key0 + KEY_TILE > len_k) || (CAUSAL && key0 + KEY_TILE - 1 > q0);
-      if (need_mask) {
-#pragma unroll
-        for (int st = 0; st < 4; ++st)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = key0 + s_key<PF>(st, v, hh);
-            const bool dead = key >= len_k || (CAUSAL && key > my_q);
-            if (dead) s[st][v] = -__builtin_inff();
-          }
-      }
-      // ---- block maxima (per lane: chunk c = sub-tiles 2c, 2c+1) and row max
-      float bm[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        float m0 = s[2 * c][0];
-#pragma unroll
-        for (int v = 1; v < 16; ++v) m0 = __builtin_fmaxf(m0, s[2 * c][v]);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) m0 = __builtin_fmaxf(m0, s[2 * c + 1][v]);
-        bm[c] = m0;
-      }
-      float rmax = __builtin_fmaxf(bm[0], bm[1]);
-      rmax = __builtin_fmaxf(rmax, __shfl_xor(rmax, 32, 64));
-      const float tmax = rmax * cc;                       // max of fl(S*c) (c > 0)
-      const float m_new = __builtin_fmaxf(m_run, tmax);
-      const bool row_dead = m_new == -__builtin_inff();
-      const float alpha = row_dead ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-      // ---- encode P, lane-local
-      i32x8 pk[2];
-      int psc[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        pk[c] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-        float me;
-        if (PF == PF_MXFP4) {
-          const float xmax = bm[c] * cc - m_new;          // fl(fl(S*c) - m'), no contraction
-          const float fl = __builtin_floorf(xmax);
-          const int e = fl < -125.0f ? -127 : (int)fl - 2; // also -inf (no live key)
-          psc[c] = e + 127;
-          me = row_dead ? 0.0f : m_new + (float)e;
-        } else {
-          psc[c] = 127;
-          me = row_dead ? 0.0f : m_new;
-        }
-        if (PF == PF_MXFP4) {
-          uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-            for (int v = 0; v < 16; v += 2) {
-              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v], cc, -me));
-              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v + 1], cc, -me));
-              const int j = 16 * s2 + v;                  // key index within the lane's block
-              const int word = j >> 3, byte = (j >> 1) & 3;
-              if (byte == 0) w[word] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[word], p0, p1, 1.0f, 0);
-              else if (byte == 1) w[word] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[word], p0, p1, 1.0f, 1);
-              else if (byte == 2) w[word] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[word], p0, p1, 1.0f, 2);
-              else w[word] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[word], p0, p1, 1.0f, 3);
-            }
-          pk[c][0] = (int)w[0]; pk[c][1] = (int)w[1]; pk[c][2] = (int)w[2]; pk[c][3] = (int)w[3];
-        } else {
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-            for (int v = 0; v < 16; v += 4) {
-              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v], cc, -me));
-              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v + 1], cc, -me));
-              const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v + 2], cc, -me));
-              const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v + 3], cc, -me));
-              int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-              wv = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wv, true);
-              pk[c][4 * s2 + v / 4] = wv;
-            }
-        }
-      }
-      // ---- rescale running state (skipped when no row of the wave changed max)
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
-        lacc[0] *= alpha;
-      }
-      m_run = m_new;
-      // ---- O^T += V^T P^T and l += sum(P)
+    if (have_p) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          i32x8 a;
-          int sa = 127;
           if (VF == VF_MXFP4) {
             const u32x4 av = *reinterpret_cast<const u32x4*>(sV + ((((c * DT + dt) * 2 + hh) * 32 + ql) * 16));
-            a = i32x8{(int)av[0], (int)av[1], (int)av[2], (int)av[3], 0, 0, 0, 0};
-            sa = (int)((sVS[32 * dt + ql] >> (8 * (2 * c + hh))) & 0xFFu);
+            const i32x8 a = {(int)av[0], (int)av[1], (int)av[2], (int)av[3], 0, 0, 0, 0};
+            const int sa = (int)((sVS[32 * dt + ql] >> (8 * (2 * c + hh))) & 0xFFu);
             oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pk[c], oacc[dt], 4, PF == PF_MXFP4 ? 4 : 0,
                                                                        0, sa, 0, psc[c]);
           } else {
-            const int u0 = ((((c * DT + dt) * 2 + 0) * 2 + hh) * 32 + ql) * 16;
-            const int u1 = ((((c * DT + dt) * 2 + 1) * 2 + hh) * 32 + ql) * 16;
-            const u32x4 a0 = *reinterpret_cast<const u32x4*>(sV + u0);
-            const u32x4 a1 = *reinterpret_cast<const u32x4*>(sV + u1);
-            a = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+            const u32x4 a0 = *reinterpret_cast<const u32x4*>(sV + ((((c * DT + dt) * 2 + 0) * 2 + hh) * 32 + ql) * 16);
+            const u32x4 a1 = *reinterpret_cast<const u32x4*>(sV + ((((c * DT + dt) * 2 + 1) * 2 + hh) * 32 + ql) * 16);
+            const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
             oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pk[c], oacc[dt], 0, PF == PF_MXFP4 ? 4 : 0,
                                                                        0, 127, 0, psc[c]);
           }
@@ -361,27 +271,159 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
         lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pk[c], lacc, 4, PF == PF_MXFP4 ? 4 : 0, 0, 127, 0,
                                                                psc[c]);
       }
-      if (DEBUG && b == p.dbg_b && h == p.dbg_h && my_q < len_q) {
+      have_p = false;
+    }
+    have_s = false;
+    if (j < n_tiles) {
+      bool work = wave_active;
+      if (CAUSAL) work = work && (j * KEY_TILE <= q0 + WAVE_Q - 1);
+      if (work) {
+        // k-step outer, sub-tile inner: four independent accumulation chains
+        // keep the matrix pipe busy; operands of step ks+1 are read ahead.
+        const uint8_t* kb = sK + (hh * KS * 32 + ql) * 16;
+        f16x8 a[4], an[4];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int64_t row = (int64_t)my_q * p.dbg_ld;
-          if (PF == PF_MXFP4) {
-            const int key = key0 + 64 * c + 32 * hh;
-            *reinterpret_cast<u32x4*>(p.dbg_codes + (row + key) / 2) =
-                u32x4{(uint32_t)pk[c][0], (uint32_t)pk[c][1], (uint32_t)pk[c][2], (uint32_t)pk[c][3]};
-            p.dbg_scales[(row + key) / 32] = (uint8_t)psc[c];
-          } else {
-            const int key = key0 + 64 * c + 16 * hh;
-            *reinterpret_cast<u32x4*>(p.dbg_codes + row + key) =
-                u32x4{(uint32_t)pk[c][0], (uint32_t)pk[c][1], (uint32_t)pk[c][2], (uint32_t)pk[c][3]};
-            *reinterpret_cast<u32x4*>(p.dbg_codes + row + key + 32) =
-                u32x4{(uint32_t)pk[c][4], (uint32_t)pk[c][5], (uint32_t)pk[c][6], (uint32_t)pk[c][7]};
+        for (int st = 0; st < 4; ++st) {
+          s[st] = f32x16{};
+          a[st] = *reinterpret_cast<const f16x8*>(kb + st * 2 * KS * 32 * 16);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks + 1 < KS) {
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+              an[st] = *reinterpret_cast<const f16x8*>(kb + (st * 2 * KS + ks + 1) * 32 * 16);
           }
+#pragma unroll
+          for (int st = 0; st < 4; ++st) s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[st], qf[ks], s[st], 0, 0, 0);
+          if (ks + 1 < KS) {
+#pragma unroll
+            for (int st = 0; st < 4; ++st) a[st] = an[st];
+          }
+        }
+        have_s = true;
+      }
+    }
+  };
+
+  // ---- vector phase j: running max, rescale, Direct-P / FP8 encode of S(j)
+  auto valu_phase = [&](int j) {
+    if (!have_s) return;
+    const int key0 = j * KEY_TILE;
+    const bool need_mask = (key0 + KEY_TILE > len_k) || (CAUSAL && key0 + KEY_TILE - 1 > q0);
+    if (need_mask) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = key0 + s_key<PF>(st, v, hh);
+          const bool dead = key >= len_k || (CAUSAL && key > my_q);
+          if (dead) s[st][v] = -__builtin_inff();
+        }
+    }
+    // block maxima (per lane: chunk c = sub-tiles 2c, 2c+1) and row max
+    float bm[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float m0 = s[2 * c][0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) m0 = __builtin_fmaxf(m0, s[2 * c][v]);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) m0 = __builtin_fmaxf(m0, s[2 * c + 1][v]);
+      bm[c] = m0;
+    }
+    float rmax = __builtin_fmaxf(bm[0], bm[1]);
+    rmax = __builtin_fmaxf(rmax, __shfl_xor(rmax, 32, 64));
+    const float tmax = rmax * cc;                       // max of fl(S*c) (c > 0)
+    const float m_new = __builtin_fmaxf(m_run, tmax);
+    const bool row_dead = m_new == -__builtin_inff();
+    const float alpha = row_dead ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
+      lacc[0] *= alpha;
+    }
+    m_run = m_new;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      pk[c] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      float me;
+      if (PF == PF_MXFP4) {
+        const float xmax = bm[c] * cc - m_new;          // fl(fl(S*c) - m'), no contraction
+        const float fl = __builtin_floorf(xmax);
+        const int e = fl < -125.0f ? -127 : (int)fl - 2; // also -inf (no live key)
+        psc[c] = e + 127;
+        me = row_dead ? 0.0f : m_new + (float)e;
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int v = 0; v < 16; v += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v], cc, -me));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v + 1], cc, -me));
+            const int jj = 16 * s2 + v;                 // key index within the lane's block
+            const int word = jj >> 3, byte = (jj >> 1) & 3;
+            if (byte == 0) w[word] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[word], p0, p1, 1.0f, 0);
+            else if (byte == 1) w[word] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[word], p0, p1, 1.0f, 1);
+            else if (byte == 2) w[word] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[word], p0, p1, 1.0f, 2);
+            else w[word] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[word], p0, p1, 1.0f, 3);
+          }
+        pk[c][0] = (int)w[0]; pk[c][1] = (int)w[1]; pk[c][2] = (int)w[2]; pk[c][3] = (int)w[3];
+      } else {
+        psc[c] = 127;
+        me = row_dead ? 0.0f : m_new;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int v = 0; v < 16; v += 4) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v], cc, -me));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v + 1], cc, -me));
+            const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v + 2], cc, -me));
+            const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v + 3], cc, -me));
+            int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+            wv = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wv, true);
+            pk[c][4 * s2 + v / 4] = wv;
+          }
+      }
+    }
+    have_p = true;
+    if (DEBUG && b == p.dbg_b && h == p.dbg_h && my_q < len_q) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int64_t row = (int64_t)my_q * p.dbg_ld;
+        if (PF == PF_MXFP4) {
+          const int key = key0 + 64 * c + 32 * hh;
+          *reinterpret_cast<u32x4*>(p.dbg_codes + (row + key) / 2) =
+              u32x4{(uint32_t)pk[c][0], (uint32_t)pk[c][1], (uint32_t)pk[c][2], (uint32_t)pk[c][3]};
+          p.dbg_scales[(row + key) / 32] = (uint8_t)psc[c];
+        } else {
+          const int key = key0 + 64 * c + 16 * hh;
+          *reinterpret_cast<u32x4*>(p.dbg_codes + row + key) =
+              u32x4{(uint32_t)pk[c][0], (uint32_t)pk[c][1], (uint32_t)pk[c][2], (uint32_t)pk[c][3]};
+          *reinterpret_cast<u32x4*>(p.dbg_codes + row + key + 32) =
+              u32x4{(uint32_t)pk[c][4], (uint32_t)pk[c][5], (uint32_t)pk[c][6], (uint32_t)pk[c][7]};
         }
       }
     }
-    if (t + 1 < n_tiles) store_tile(stage ^ 1);
-    __syncthreads();
+  };
+
+  // ---- the phase pipeline.  Global phase ph: group 0 runs MFMA phase ph/2
+  // on even ph and vector phase ph/2 on odd ph; group 1 one phase later.
+  // Stage m+1 is copied during phases 2m and 2m+1 (waited for at the end of
+  // 2m+1); its slot was last read in phase 2m-1.
+  issue_stage(0);
+  dma_wait();
+  phase_barrier();
+  const int nph = 2 * n_tiles + 2;
+  for (int ph = 0; ph < nph; ++ph) {
+    if ((ph & 1) == 0 && (ph >> 1) + 1 <= n_tiles) issue_stage((ph >> 1) + 1);
+    const int my = ph - grp;
+    if (my >= 0 && my <= 2 * n_tiles) {
+      if ((my & 1) == 0) mfma_phase(my >> 1);
+      else valu_phase(my >> 1);
+    }
+    if (ph & 1) dma_wait();
+    phase_barrier();
   }
 
   // ---- epilogue: O = o / l (x FP8 V tensor scale), LSE = ln2 * (m + log2 l)
