@@ -103,13 +103,26 @@ __global__ void __launch_bounds__(256) expand_nvfp4_kernel(const uint8_t* __rest
 
 template <int D, int VF>
 struct LdsLayout {
-  static constexpr int K_BYTES = KEY_TILE * D * 2;
+  static constexpr int K_BYTES = KEY_TILE * D * 2;                         // fp16 K tile
   static constexpr int V_BYTES = VF == VF_MXFP4 ? KEY_TILE * D / 2 : KEY_TILE * D;
-  static constexpr int VS_BYTES = VF == VF_MXFP4 ? D * 4 : 0;
-  static constexpr int STAGE = K_BYTES + V_BYTES + VS_BYTES;
-  static constexpr int TOTAL = 2 * STAGE;
+  static constexpr int VS_BYTES = VF == VF_MXFP4 ? D * 4 : 0;              // E8M0 V scales
+  static constexpr int V_SLOT = V_BYTES + VS_BYTES;
+  static constexpr int TOTAL = 2 * K_BYTES + 2 * V_SLOT;
 };
 
+// Software pipeline of one wave (32 queries).  Iteration t of the key loop:
+//   A: O^T += V(t-2)^T P(t-2)^T and l += sum P(t-2)      (matrix)
+//      row max of S(t-1), m', alpha, block exponents,
+//      encode keys 0..63 of S(t-1) -> P(t-1)            (vector)
+//   B: S(t) sub-tiles 0,1 = K(t) Q^T                      (matrix)
+//      encode keys 64..127 of S(t-1) -> P(t-1)           (vector)
+//   C: S(t) sub-tiles 2,3                                 (matrix)
+//      O *= alpha(t-1), l *= alpha(t-1)                   (vector)
+// so every matrix step has independent vector work beside it in the same
+// wave.  S sub-tiles are overwritten only after they have been encoded;
+// P is double-buffered (P(t-2) is read while P(t-1) is written).  The
+// 8 waves share K(t) / V(t-2) tiles in LDS; tiles for iteration t+1 are
+// copied during iteration t and one barrier per iteration separates them.
 template <int D, int PF, int VF, bool CAUSAL, bool DEBUG>
 __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   constexpr int KS = D / 16;           // k-steps of the S MFMA
@@ -137,7 +150,6 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, ql = lane & 31;
-  const int grp = wave >> 2;                    // ping-pong group (1 lags by a phase)
   const int q0 = qb * WG_Q + wave * WAVE_Q;     // first query of this wave
   const int my_q = q0 + ql;
   const bool wave_active = q0 < len_q;
@@ -168,9 +180,8 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
     for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[ks]));
   }
 
-  // ---- LDS stages.  Stage j (slot j % 2) holds the K tile j (read by the
-  // Q.K^T of MFMA phase j) and the V tile j-1 with its scales (read by the
-  // P.V of the same phase).  Copies go global -> LDS directly.
+  // ---- LDS: K slots 0/1 then V slots 0/1 (codes + scales).  Iteration t reads
+  // K(t) from K slot t%2 and V(t-2) from V slot t%2.
   const int64_t kcol0 = kcol_offset(varlen, b, tk0, p.nk_pad);
   const uint8_t* ksrc = reinterpret_cast<const uint8_t*>(p.khat + ((int64_t)hk * p.kcols + kcol0) * D);
   const uint32_t lds0 = lds_address(smem);
@@ -180,37 +191,35 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   constexpr int K_UNITS = L::K_BYTES / 16;
   constexpr int V_UNITS = L::V_BYTES / 16;
   static_assert(K_UNITS % 512 == 0, "K tile must split evenly over the workgroup");
-  auto issue_stage = [&](int j) {
-    const uint32_t slot = lds0 + (uint32_t)((j & 1) * L::STAGE);
-    if (j < n_tiles) {
+  auto copy_k = [&](int t) {           // K(t) -> K slot t%2
+    const uint32_t slot = lds0 + (uint32_t)((t & 1) * L::K_BYTES);
 #pragma unroll
-      for (int i = 0; i < K_UNITS / 512; ++i) {
-        const int u0 = i * 512 + wave * 64;
-        dma16(ksrc, (uint32_t)(j * L::K_BYTES + (u0 + lane) * 16), slot + u0 * 16);
+    for (int i = 0; i < K_UNITS / 512; ++i) {
+      const int u0 = i * 512 + wave * 64;
+      dma16(ksrc, (uint32_t)(t * L::K_BYTES + (u0 + lane) * 16), slot + u0 * 16);
+    }
+  };
+  auto copy_v = [&](int t) {           // V(t) -> V slot t%2
+    const uint32_t slot = lds0 + (uint32_t)(2 * L::K_BYTES + (t & 1) * L::V_SLOT);
+    const int64_t col = kcol0 + (int64_t)t * KEY_TILE;
+#pragma unroll
+    for (int i = 0; i < (V_UNITS + 511) / 512; ++i) {
+      const int u0 = i * 512 + wave * 64;
+      if (u0 < V_UNITS) {
+        const int u = u0 + lane;
+        int c, dt, kh, r, part = 0;
+        if (VF == VF_MXFP4) { r = u & 31; kh = (u >> 5) & 1; dt = (u >> 6) % DT; c = (u >> 6) / DT; }
+        else { r = u & 31; kh = (u >> 5) & 1; part = (u >> 6) & 1; dt = (u >> 7) % DT; c = (u >> 7) / DT; }
+        const int d = 32 * dt + r;
+        uint32_t off;
+        if (VF == VF_MXFP4) off = (uint32_t)((d * p.kcols + col + 64 * c + 32 * kh) / 2);
+        else off = (uint32_t)(d * p.kcols + col + 64 * c + 16 * kh + 32 * part);
+        dma16(vhead, off, slot + u0 * 16);
       }
     }
-    if (j >= 1) {
-      const int t = j - 1;
-      const int64_t col = kcol0 + (int64_t)t * KEY_TILE;
-#pragma unroll
-      for (int i = 0; i < (V_UNITS + 511) / 512; ++i) {
-        const int u0 = i * 512 + wave * 64;
-        if (u0 < V_UNITS) {
-          const int u = u0 + lane;
-          int c, dt, kh, r, part = 0;
-          if (VF == VF_MXFP4) { r = u & 31; kh = (u >> 5) & 1; dt = (u >> 6) % DT; c = (u >> 6) / DT; }
-          else { r = u & 31; kh = (u >> 5) & 1; part = (u >> 6) & 1; dt = (u >> 7) % DT; c = (u >> 7) / DT; }
-          const int d = 32 * dt + r;
-          uint32_t off;
-          if (VF == VF_MXFP4) off = (uint32_t)((d * p.kcols + col + 64 * c + 32 * kh) / 2);
-          else off = (uint32_t)(d * p.kcols + col + 64 * c + 16 * kh + 32 * part);
-          dma16(vhead, off, slot + L::K_BYTES + u0 * 16);
-        }
-      }
-      if (VF == VF_MXFP4 && wave * 64 < D) {
-        const int d = wave * 64 + lane;
-        dma4(shead, (uint32_t)(d * (p.kcols / 32) + col / 32), slot + L::K_BYTES + L::V_BYTES + wave * 256);
-      }
+    if (VF == VF_MXFP4 && wave * 64 < D) {
+      const int d = wave * 64 + lane;
+      dma4(shead, (uint32_t)(d * (p.kcols / 32) + col / 32), slot + L::V_BYTES + wave * 256);
     }
   };
 
@@ -220,13 +229,15 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   for (int i = 0; i < DT; ++i) oacc[i] = f32x16{};
   f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
   float m_run = -__builtin_inff();
+  float alpha_pend = 1.0f;
   f32x16 s[4];
-  i32x8 pk[2];
-  int psc[2] = {127, 127};
-  bool have_s = false, have_p = false;
 #pragma unroll
   for (int st = 0; st < 4; ++st) s[st] = f32x16{};
-  pk[0] = pk[1] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+  i32x8 pw[2], pr[2];                  // probabilities being written / read by P.V
+  int psw[2] = {127, 127}, psr[2] = {127, 127};
+  float bm[2] = {0.f, 0.f};
+  float me[2] = {0.f, 0.f};
+  pw[0] = pw[1] = pr[0] = pr[1] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
 
   // constant 0/1 operand of the row-sum MFMA (16x16x128, FP4 1.0 = code 2)
   i32x8 ones = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -244,90 +255,69 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
     }
   }
 
-  // ---- MFMA phase j: P(j-1).V(j-1) then S(j) = K(j) Q^T
-  auto mfma_phase = [&](int j) {
-    const uint8_t* sK = smem + (j & 1) * L::STAGE;
-    const uint8_t* sV = sK + L::K_BYTES;
+  // ---- pipeline pieces --------------------------------------------------
+  // O^T += V^T P^T and l += sum(P) for the tile whose V is in V slot `vs`
+  auto pv = [&](int vs, const i32x8 (&pk)[2], const int (&psc)[2]) {
+    const uint8_t* sV = smem + 2 * L::K_BYTES + vs * L::V_SLOT;
     const uint32_t* sVS = reinterpret_cast<const uint32_t*>(sV + L::V_BYTES);
-    if (have_p) {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          if (VF == VF_MXFP4) {
-            const u32x4 av = *reinterpret_cast<const u32x4*>(sV + ((((c * DT + dt) * 2 + hh) * 32 + ql) * 16));
-            const i32x8 a = {(int)av[0], (int)av[1], (int)av[2], (int)av[3], 0, 0, 0, 0};
-            const int sa = (int)((sVS[32 * dt + ql] >> (8 * (2 * c + hh))) & 0xFFu);
-            oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pk[c], oacc[dt], 4, PF == PF_MXFP4 ? 4 : 0,
-                                                                       0, sa, 0, psc[c]);
-          } else {
-            const u32x4 a0 = *reinterpret_cast<const u32x4*>(sV + ((((c * DT + dt) * 2 + 0) * 2 + hh) * 32 + ql) * 16);
-            const u32x4 a1 = *reinterpret_cast<const u32x4*>(sV + ((((c * DT + dt) * 2 + 1) * 2 + hh) * 32 + ql) * 16);
-            const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-            oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pk[c], oacc[dt], 0, PF == PF_MXFP4 ? 4 : 0,
-                                                                       0, 127, 0, psc[c]);
-          }
-        }
-        lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pk[c], lacc, 4, PF == PF_MXFP4 ? 4 : 0, 0, 127, 0,
-                                                               psc[c]);
-      }
-      have_p = false;
-    }
-    have_s = false;
-    if (j < n_tiles) {
-      bool work = wave_active;
-      if (CAUSAL) work = work && (j * KEY_TILE <= q0 + WAVE_Q - 1);
-      if (work) {
-        // k-step outer, sub-tile inner: four independent accumulation chains
-        // keep the matrix pipe busy; operands of step ks+1 are read ahead.
-        const uint8_t* kb = sK + (hh * KS * 32 + ql) * 16;
-        f16x8 a[4], an[4];
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          s[st] = f32x16{};
-          a[st] = *reinterpret_cast<const f16x8*>(kb + st * 2 * KS * 32 * 16);
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          if (ks + 1 < KS) {
-#pragma unroll
-            for (int st = 0; st < 4; ++st)
-              an[st] = *reinterpret_cast<const f16x8*>(kb + (st * 2 * KS + ks + 1) * 32 * 16);
-          }
-#pragma unroll
-          for (int st = 0; st < 4; ++st) s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[st], qf[ks], s[st], 0, 0, 0);
-          if (ks + 1 < KS) {
-#pragma unroll
-            for (int st = 0; st < 4; ++st) a[st] = an[st];
-          }
-        }
-        have_s = true;
-      }
-    }
-  };
-
-  // ---- vector phase j: running max, rescale, Direct-P / FP8 encode of S(j)
-  auto valu_phase = [&](int j) {
-    if (!have_s) return;
-    const int key0 = j * KEY_TILE;
-    const bool need_mask = (key0 + KEY_TILE > len_k) || (CAUSAL && key0 + KEY_TILE - 1 > q0);
-    if (need_mask) {
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = key0 + s_key<PF>(st, v, hh);
-          const bool dead = key >= len_k || (CAUSAL && key > my_q);
-          if (dead) s[st][v] = -__builtin_inff();
-        }
-    }
-    // block maxima (per lane: chunk c = sub-tiles 2c, 2c+1) and row max
-    float bm[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      float m0 = s[2 * c][0];
 #pragma unroll
-      for (int v = 1; v < 16; ++v) m0 = __builtin_fmaxf(m0, s[2 * c][v]);
+      for (int dt = 0; dt < DT; ++dt) {
+        if (VF == VF_MXFP4) {
+          const u32x4 av = *reinterpret_cast<const u32x4*>(sV + ((((c * DT + dt) * 2 + hh) * 32 + ql) * 16));
+          const i32x8 a = {(int)av[0], (int)av[1], (int)av[2], (int)av[3], 0, 0, 0, 0};
+          const int sa = (int)((sVS[32 * dt + ql] >> (8 * (2 * c + hh))) & 0xFFu);
+          oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pk[c], oacc[dt], 4, PF == PF_MXFP4 ? 4 : 0,
+                                                                     0, sa, 0, psc[c]);
+        } else {
+          const u32x4 a0 = *reinterpret_cast<const u32x4*>(sV + ((((c * DT + dt) * 2 + 0) * 2 + hh) * 32 + ql) * 16);
+          const u32x4 a1 = *reinterpret_cast<const u32x4*>(sV + ((((c * DT + dt) * 2 + 1) * 2 + hh) * 32 + ql) * 16);
+          const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+          oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pk[c], oacc[dt], 0, PF == PF_MXFP4 ? 4 : 0,
+                                                                     0, 127, 0, psc[c]);
+        }
+      }
+      lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pk[c], lacc, 4, PF == PF_MXFP4 ? 4 : 0, 0, 127, 0,
+                                                             psc[c]);
+    }
+  };
+  // S^T sub-tiles st0, st0+1 of K(t) Q^T (K in slot ks_)
+  auto qk2 = [&](int kslot, int st0) {
+    const uint8_t* kb = smem + kslot * L::K_BYTES + (hh * KS * 32 + ql) * 16;
+    f16x8 a0 = *reinterpret_cast<const f16x8*>(kb + (st0 * 2 * KS) * 32 * 16);
+    f16x8 a1 = *reinterpret_cast<const f16x8*>(kb + ((st0 + 1) * 2 * KS) * 32 * 16);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      f16x8 n0, n1;
+      if (ks + 1 < KS) {
+        n0 = *reinterpret_cast<const f16x8*>(kb + (st0 * 2 * KS + ks + 1) * 32 * 16);
+        n1 = *reinterpret_cast<const f16x8*>(kb + ((st0 + 1) * 2 * KS + ks + 1) * 32 * 16);
+      }
+      s[st0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, qf[ks], ks == 0 ? f32x16{} : s[st0], 0, 0, 0);
+      s[st0 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, qf[ks], ks == 0 ? f32x16{} : s[st0 + 1], 0, 0, 0);
+      if (ks + 1 < KS) { a0 = n0; a1 = n1; }
+    }
+  };
+  // masking of S (tail of the sequence, causal diagonal) for tile j
+  auto mask = [&](int j) {
+    const int key0 = j * KEY_TILE;
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = key0 + s_key<PF>(st, v, hh);
+        const bool dead = key >= len_k || (CAUSAL && key > my_q);
+        if (dead) s[st][v] = -__builtin_inff();
+      }
+  };
+  // running max, alpha, block exponents of S (tile j)
+  auto stats = [&](int (&psc)[2]) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float m0 = __builtin_fmaxf(s[2 * c][0], s[2 * c][1]);
+#pragma unroll
+      for (int v = 2; v < 16; ++v) m0 = __builtin_fmaxf(m0, s[2 * c][v]);
 #pragma unroll
       for (int v = 0; v < 16; ++v) m0 = __builtin_fmaxf(m0, s[2 * c + 1][v]);
       bm[c] = m0;
@@ -337,57 +327,65 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
     const float tmax = rmax * cc;                       // max of fl(S*c) (c > 0)
     const float m_new = __builtin_fmaxf(m_run, tmax);
     const bool row_dead = m_new == -__builtin_inff();
-    const float alpha = row_dead ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-    if (__any(alpha != 1.0f)) {
-#pragma unroll
-      for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
-      lacc[0] *= alpha;
-    }
+    alpha_pend = row_dead ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      pk[c] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-      float me;
       if (PF == PF_MXFP4) {
         const float xmax = bm[c] * cc - m_new;          // fl(fl(S*c) - m'), no contraction
         const float fl = __builtin_floorf(xmax);
         const int e = fl < -125.0f ? -127 : (int)fl - 2; // also -inf (no live key)
         psc[c] = e + 127;
-        me = row_dead ? 0.0f : m_new + (float)e;
-        uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int v = 0; v < 16; v += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v], cc, -me));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v + 1], cc, -me));
-            const int jj = 16 * s2 + v;                 // key index within the lane's block
-            const int word = jj >> 3, byte = (jj >> 1) & 3;
-            if (byte == 0) w[word] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[word], p0, p1, 1.0f, 0);
-            else if (byte == 1) w[word] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[word], p0, p1, 1.0f, 1);
-            else if (byte == 2) w[word] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[word], p0, p1, 1.0f, 2);
-            else w[word] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[word], p0, p1, 1.0f, 3);
-          }
-        pk[c][0] = (int)w[0]; pk[c][1] = (int)w[1]; pk[c][2] = (int)w[2]; pk[c][3] = (int)w[3];
+        me[c] = row_dead ? 0.0f : m_new + (float)e;
       } else {
         psc[c] = 127;
-        me = row_dead ? 0.0f : m_new;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int v = 0; v < 16; v += 4) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v], cc, -me));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v + 1], cc, -me));
-            const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v + 2], cc, -me));
-            const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v + 3], cc, -me));
-            int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-            wv = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wv, true);
-            pk[c][4 * s2 + v / 4] = wv;
-          }
+        me[c] = row_dead ? 0.0f : m_new;
       }
     }
-    have_p = true;
+  };
+  // Direct-P / FP8 encode of chunk c (keys 64c..64c+63 of the tile) of S
+  auto encode = [&](int c, i32x8 (&pk)[2]) {
+    if (PF == PF_MXFP4) {
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v], cc, -me[c]));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v + 1], cc, -me[c]));
+          const int jj = 16 * s2 + v;                   // key index within the lane's block
+          const int word = jj >> 3, byte = (jj >> 1) & 3;
+          if (byte == 0) w[word] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[word], p0, p1, 1.0f, 0);
+          else if (byte == 1) w[word] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[word], p0, p1, 1.0f, 1);
+          else if (byte == 2) w[word] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[word], p0, p1, 1.0f, 2);
+          else w[word] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[word], p0, p1, 1.0f, 3);
+        }
+      pk[c] = i32x8{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+    } else {
+      int w[8];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int v = 0; v < 16; v += 4) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v], cc, -me[c]));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v + 1], cc, -me[c]));
+          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v + 2], cc, -me[c]));
+          const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v + 3], cc, -me[c]));
+          int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+          wv = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wv, true);
+          w[4 * s2 + v / 4] = wv;
+        }
+      pk[c] = i32x8{w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7]};
+    }
+  };
+  auto rescale = [&]() {
+#pragma unroll
+    for (int i = 0; i < DT; ++i) oacc[i] *= alpha_pend;
+    lacc[0] *= alpha_pend;
+  };
+  auto dump = [&](int j, const i32x8 (&pk)[2], const int (&psc)[2]) {
     if (DEBUG && b == p.dbg_b && h == p.dbg_h && my_q < len_q) {
+      const int key0 = j * KEY_TILE;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int64_t row = (int64_t)my_q * p.dbg_ld;
@@ -406,23 +404,46 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
       }
     }
   };
-
-  // ---- the phase pipeline.  Global phase ph: group 0 runs MFMA phase ph/2
-  // on even ph and vector phase ph/2 on odd ph; group 1 one phase later.
-  // Stage m+1 is copied during phases 2m and 2m+1 (waited for at the end of
-  // 2m+1); its slot was last read in phase 2m-1.
-  issue_stage(0);
+  // ---- the key loop.  Prologue: K(0) and S(0).  Iteration t = 1..n+1 runs
+  // P.V of tile t-2, the softmax/encode of tile t-1 and Q.K^T of tile t.
+  // Out-of-range pieces run on harmless data instead of branching: P of the
+  // tile before 0 is all-zero codes against a zeroed V slot, and the tile
+  // after the last is masked completely (all its probabilities are 0), so the
+  // steady body has no branches between its matrix and vector work.
+  {
+    // zero the V slots once (P(-1) = 0 meets V slot 1 in iteration 1)
+    for (int i = tid; i < 2 * L::V_SLOT / 16; i += 512)
+      *reinterpret_cast<u32x4*>(smem + 2 * L::K_BYTES + i * 16) = u32x4{0u, 0u, 0u, 0u};
+  }
+  copy_k(0);
+  dma_wait();
+  __syncthreads();
+  if (n_tiles > 1) copy_k(1);
+  qk2(0, 0);
+  qk2(0, 2);
   dma_wait();
   phase_barrier();
-  const int nph = 2 * n_tiles + 2;
-  for (int ph = 0; ph < nph; ++ph) {
-    if ((ph & 1) == 0 && (ph >> 1) + 1 <= n_tiles) issue_stage((ph >> 1) + 1);
-    const int my = ph - grp;
-    if (my >= 0 && my <= 2 * n_tiles) {
-      if ((my & 1) == 0) mfma_phase(my >> 1);
-      else valu_phase(my >> 1);
-    }
-    if (ph & 1) dma_wait();
+  for (int t = 1; t <= n_tiles + 1; ++t) {
+    if (t + 1 < n_tiles) copy_k(t + 1);
+    if (t - 1 < n_tiles) copy_v(t - 1);
+    const int j = t - 1;                       // tile being encoded
+    if (j * KEY_TILE + KEY_TILE > len_k || (CAUSAL && j * KEY_TILE + KEY_TILE - 1 > q0)) mask(j);
+    // region A: P(t-2).V(t-2) beside the row statistics and chunk-0 encode of S(t-1)
+    pv(t & 1, pr, psr);
+    stats(psw);
+    encode(0, pw);
+    __builtin_amdgcn_sched_barrier(0);
+    // region B: S(t) sub-tiles 0,1 beside the chunk-1 encode
+    qk2(t & 1, 0);
+    encode(1, pw);
+    __builtin_amdgcn_sched_barrier(0);
+    // region C: S(t) sub-tiles 2,3 beside the O / l rescale
+    qk2(t & 1, 2);
+    rescale();
+    __builtin_amdgcn_sched_barrier(0);
+    if (j < n_tiles) dump(j, pw, psw);
+    pr[0] = pw[0]; pr[1] = pw[1]; psr[0] = psw[0]; psr[1] = psw[1];
+    dma_wait();
     phase_barrier();
   }
 
