@@ -13,6 +13,7 @@ noncausal, MXFP4 P and V).  Prints one JSON line.
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -32,8 +33,53 @@ def parse():
     ap.add_argument("--workload", type=int, default=2, help="1..5 (default 2: Wan2.1-14B shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows of the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=16384, help="query rows of the oracle sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (HBM counter calibration) and exit")
     return ap.parse_args()
+
+
+# Sources the forward attention kernel is compiled from; a traffic figure
+# measured by hardware counters is reported only while they are unchanged.
+KERNEL_SOURCES = ["fwd_lowp.hip", "common.h", "pipeline.h", "fwd_params.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_lowp_kernel_hbm_traffic.md")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "precision_attention_forward_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the attention kernel for `workload`, from the
+    counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by the factor a plain
+    copy of known size reads for the same counter), or None when there is no
+    figure for this workload or the kernel sources changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    src = kernel_source_hash()
+    for line in open(TRAFFIC_FILE):
+        m = re.match(r"\s*traffic:\s+workload=(\d+)\s+source=([0-9a-f]+)\s+bytes_per_launch=([0-9.eE+]+)", line)
+        if m and int(m.group(1)) == workload and m.group(2) == src:
+            return float(m.group(3))
+    return None
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                      "launches": 3}), flush=True)
 
 
 def cpu_baseline(inp, rows):
@@ -114,6 +160,9 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import torch
     import precision_attention_forward_amd as paf
     from precision_attention_forward_amd import synth
@@ -199,7 +248,7 @@ def main():
     qk_rate, pv_rate = BF16_PEAK_TFLOPS, (pv_peak if wl.p_format == "mxfp4" else FP8_PEAK_TFLOPS)
     ceiling = 1.0 / (0.5 / qk_rate + 0.5 / pv_rate)
     roofline = {"bound": "mfma", "achieved": round(kern_tflops, 2), "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(kern_tflops / MXFP4_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(kern_tflops / MXFP4_PEAK_TFLOPS, 4), "traffic": measured_traffic(args.workload),
                 "kernel": "fwd_lowp_kernel", "kernel_ms": round(kern_ms, 4),
                 "mixed_ceiling_tflops": round(ceiling, 1), "frac_of_mixed_ceiling": round(kern_tflops / ceiling, 4)}
 
