@@ -101,6 +101,14 @@ __global__ void __launch_bounds__(256) expand_nvfp4_kernel(const uint8_t* __rest
 }
 
 
+// First vector unit of slot i of the key loop: slots [0, NPV) carry units
+// [0, 13) (statistics and the encode of sub-tile 0); then each group of KS
+// slots carries 8 units (encode of the next sub-tile, finally the rescale).
+template <int NPV, int KS>
+__host__ __device__ constexpr int slot_unit_begin(int i) {
+  return i < NPV ? (i * 13) / NPV : 13 + 8 * ((i - NPV) / KS) + (((i - NPV) % KS) * 8) / KS;
+}
+
 template <int D, int VF>
 struct LdsLayout {
   static constexpr int K_BYTES = KEY_TILE * D * 2;                         // fp16 K tile
@@ -191,36 +199,44 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   constexpr int K_UNITS = L::K_BYTES / 16;
   constexpr int V_UNITS = L::V_BYTES / 16;
   static_assert(K_UNITS % 512 == 0, "K tile must split evenly over the workgroup");
-  auto copy_k = [&](int t) {           // K(t) -> K slot t%2
+  // Copies are split into parts of one instruction per wave (1 KB of K or V,
+  // or the V block exponents) so that the key loop can spread them over its
+  // slots: a burst of copies at one point would fill the address queue and
+  // stall the issuing waves' matrix work behind it.
+  constexpr int NK_DMA = K_UNITS / 512;
+  constexpr int NV_DMA = (V_UNITS + 511) / 512 + (VF == VF_MXFP4 ? 1 : 0);
+  // part i of K(src) -> K slot t%2
+  auto copy_k_part = [&](int t, int src, int i) {
     const uint32_t slot = lds0 + (uint32_t)((t & 1) * L::K_BYTES);
-#pragma unroll
-    for (int i = 0; i < K_UNITS / 512; ++i) {
-      const int u0 = i * 512 + wave * 64;
-      dma16(ksrc, (uint32_t)(t * L::K_BYTES + (u0 + lane) * 16), slot + u0 * 16);
-    }
+    const int u0 = i * 512 + wave * 64;
+    dma16(ksrc, (uint32_t)(src * L::K_BYTES + (u0 + lane) * 16), slot + u0 * 16);
   };
-  auto copy_v = [&](int t) {           // V(t) -> V slot t%2
+  // part i of V(src) -> V slot t%2
+  auto copy_v_part = [&](int t, int src, int i) {
     const uint32_t slot = lds0 + (uint32_t)(2 * L::K_BYTES + (t & 1) * L::V_SLOT);
-    const int64_t col = kcol0 + (int64_t)t * KEY_TILE;
+    const int64_t col = kcol0 + (int64_t)src * KEY_TILE;
+    // No branches here (these copies sit inside the key loop's slots): waves
+    // beyond the ones a part needs copy the same bytes to the same place again.
+    if (VF == VF_MXFP4 && i == NV_DMA - 1) {         // E8M0 exponents, one dword per d
+      const int w = wave % (D / 64);
+      const int d = w * 64 + lane;
+      dma4(shead, (uint32_t)(d * (p.kcols / 32) + col / 32), slot + L::V_BYTES + w * 256);
+      return;
+    }
+    const int u0 = (i * 512 + wave * 64) % V_UNITS;
+    const int u = u0 + lane;
+    int c, dt, kh, r, part = 0;
+    if (VF == VF_MXFP4) { r = u & 31; kh = (u >> 5) & 1; dt = (u >> 6) % DT; c = (u >> 6) / DT; }
+    else { r = u & 31; kh = (u >> 5) & 1; part = (u >> 6) & 1; dt = (u >> 7) % DT; c = (u >> 7) / DT; }
+    const int d = 32 * dt + r;
+    uint32_t off;
+    if (VF == VF_MXFP4) off = (uint32_t)((d * p.kcols + col + 64 * c + 32 * kh) / 2);
+    else off = (uint32_t)(d * p.kcols + col + 64 * c + 16 * kh + 32 * part);
+    dma16(vhead, off, slot + u0 * 16);
+  };
+  auto copy_k = [&](int t) {
 #pragma unroll
-    for (int i = 0; i < (V_UNITS + 511) / 512; ++i) {
-      const int u0 = i * 512 + wave * 64;
-      if (u0 < V_UNITS) {
-        const int u = u0 + lane;
-        int c, dt, kh, r, part = 0;
-        if (VF == VF_MXFP4) { r = u & 31; kh = (u >> 5) & 1; dt = (u >> 6) % DT; c = (u >> 6) / DT; }
-        else { r = u & 31; kh = (u >> 5) & 1; part = (u >> 6) & 1; dt = (u >> 7) % DT; c = (u >> 7) / DT; }
-        const int d = 32 * dt + r;
-        uint32_t off;
-        if (VF == VF_MXFP4) off = (uint32_t)((d * p.kcols + col + 64 * c + 32 * kh) / 2);
-        else off = (uint32_t)(d * p.kcols + col + 64 * c + 16 * kh + 32 * part);
-        dma16(vhead, off, slot + u0 * 16);
-      }
-    }
-    if (VF == VF_MXFP4 && wave * 64 < D) {
-      const int d = wave * 64 + lane;
-      dma4(shead, (uint32_t)(d * (p.kcols / 32) + col / 32), slot + L::V_BYTES + wave * 256);
-    }
+    for (int i = 0; i < NK_DMA; ++i) copy_k_part(t, t, i);
   };
 
   // ---- accumulators and per-wave state
@@ -404,6 +420,116 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
       }
     }
   };
+  // ---- one iteration as NS slots ----------------------------------------
+  // Slot i issues one matrix instruction -- P.V / row-sum of tile t-2 for
+  // i < NPV, then S(t) = K(t) Q^T sub-tile by sub-tile -- and a fixed share of
+  // the vector units of tile t-1, with a scheduling fence after each slot so
+  // that matrix and vector work stay interleaved in the instruction stream
+  // (one wave issues in order: a run of matrix instructions would otherwise
+  // stall its vector work).  LDS operands are read two slots ahead.
+  //   units [0, 4)  : block maxima of S(t-1)
+  //   unit  4       : row max, m', alpha, block exponents
+  //   units [5, 37) : encode two scores (sub-tile (u-5)/8, registers 2k, 2k+1)
+  //   units [37, 45): O / l rescale, one eighth each
+  // Sub-tile st of S(t-1) is fully encoded before the slot that overwrites it.
+  constexpr int NPV = 2 * (DT + 1);
+  constexpr int NS = NPV + 4 * KS;
+  u32x4 opa[3], opb[3];
+  uint32_t vsc[DT];
+  auto load_op = [&](int i, const uint8_t* sV, const uint8_t* kb) {
+    const int bs = i % 3;
+    if (i < NPV) {
+      const int c = i / (DT + 1), dt = i % (DT + 1);
+      if (dt == DT) return;                      // row-sum: constant operand
+      if (VF == VF_MXFP4) {
+        opa[bs] = *reinterpret_cast<const u32x4*>(sV + ((((c * DT + dt) * 2 + hh) * 32 + ql) * 16));
+      } else {
+        opa[bs] = *reinterpret_cast<const u32x4*>(sV + ((((c * DT + dt) * 2 + 0) * 2 + hh) * 32 + ql) * 16);
+        opb[bs] = *reinterpret_cast<const u32x4*>(sV + ((((c * DT + dt) * 2 + 1) * 2 + hh) * 32 + ql) * 16);
+      }
+    } else {
+      const int q = i - NPV, st = q / KS, ks = q % KS;
+      opa[bs] = *reinterpret_cast<const u32x4*>(kb + (st * 2 * KS + ks) * 32 * 16);
+    }
+  };
+  auto mfma_slot = [&](int i) {
+    const int bs = i % 3;
+    if (i < NPV) {
+      const int c = i / (DT + 1), dt = i % (DT + 1);
+      if (dt == DT) {
+        lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pr[c], lacc, 4, PF == PF_MXFP4 ? 4 : 0, 0, 127,
+                                                               0, psr[c]);
+      } else if (VF == VF_MXFP4) {
+        const i32x8 a = {(int)opa[bs][0], (int)opa[bs][1], (int)opa[bs][2], (int)opa[bs][3], 0, 0, 0, 0};
+        const int sa = (int)((vsc[dt] >> (8 * (2 * c + hh))) & 0xFFu);
+        oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pr[c], oacc[dt], 4, PF == PF_MXFP4 ? 4 : 0, 0,
+                                                                   sa, 0, psr[c]);
+      } else {
+        const i32x8 a = {(int)opa[bs][0], (int)opa[bs][1], (int)opa[bs][2], (int)opa[bs][3],
+                         (int)opb[bs][0], (int)opb[bs][1], (int)opb[bs][2], (int)opb[bs][3]};
+        oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pr[c], oacc[dt], 0, PF == PF_MXFP4 ? 4 : 0, 0,
+                                                                   127, 0, psr[c]);
+      }
+    } else {
+      const int q = i - NPV, st = q / KS, ks = q % KS;
+      const f16x8 a = __builtin_bit_cast(f16x8, opa[bs]);
+      s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ks], ks == 0 ? f32x16{} : s[st], 0, 0, 0);
+    }
+  };
+  auto vunit = [&](int u) {
+    if (u < 4) {                                 // block max of chunk u/2, half u%2
+      const int c = u >> 1, st = 2 * c + (u & 1);
+      float m0 = (u & 1) ? bm[c] : s[st][0];
+#pragma unroll
+      for (int v = (u & 1) ? 0 : 1; v < 16; ++v) m0 = __builtin_fmaxf(m0, s[st][v]);
+      bm[c] = m0;
+    } else if (u == 4) {                         // row statistics
+      float rmax = __builtin_fmaxf(bm[0], bm[1]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax), __float_as_uint(rmax), false, false);
+      rmax = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));   // max with lane ^ 32
+      const float tmax = rmax * cc;              // max of fl(S*c) (c > 0)
+      const float m_new = __builtin_fmaxf(m_run, tmax);
+      const bool row_dead = m_new == -__builtin_inff();
+      alpha_pend = row_dead ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        if (PF == PF_MXFP4) {
+          const float xmax = bm[c] * cc - m_new;   // fl(fl(S*c) - m'), no contraction
+          const float fl = __builtin_floorf(xmax);
+          const int e = fl < -125.0f ? -127 : (int)fl - 2;   // also -inf (no live key)
+          psw[c] = e + 127;
+          me[c] = row_dead ? 0.0f : m_new + (float)e;
+        } else {
+          psw[c] = 127;
+          me[c] = row_dead ? 0.0f : m_new;
+        }
+      }
+    } else if (u < 37) {                         // encode scores 2k, 2k+1 of sub-tile st
+      const int st = (u - 5) >> 3, k = (u - 5) & 7, c = st >> 1, s2 = st & 1, v = 2 * k;
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][v], cc, -me[c]));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][v + 1], cc, -me[c]));
+      if (PF == PF_MXFP4) {
+        const int word = 2 * s2 + (k >> 2), byte = k & 3;   // key 16*s2 + v of the lane's block
+        uint32_t w = (uint32_t)pw[c][word];
+        if (byte == 0) w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p0, p1, 1.0f, 0);
+        else if (byte == 1) w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p0, p1, 1.0f, 1);
+        else if (byte == 2) w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p0, p1, 1.0f, 2);
+        else w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p0, p1, 1.0f, 3);
+        pw[c][word] = (int)w;
+      } else {
+        const int word = 4 * s2 + (k >> 1);
+        if (k & 1) pw[c][word] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pw[c][word], true);
+        else pw[c][word] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pw[c][word], false);
+      }
+    } else {                                     // rescale slice
+      const int r = u - 37;
+#pragma unroll
+      for (int e = r * 2 * DT; e < (r + 1) * 2 * DT; ++e) oacc[e >> 4][e & 15] *= alpha_pend;
+      if (r == 7) lacc[0] *= alpha_pend;
+    }
+  };
+
   // ---- the key loop.  Prologue: K(0) and S(0).  Iteration t = 1..n+1 runs
   // P.V of tile t-2, the softmax/encode of tile t-1 and Q.K^T of tile t.
   // Out-of-range pieces run on harmless data instead of branching: P of the
@@ -424,23 +550,39 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   dma_wait();
   phase_barrier();
   for (int t = 1; t <= n_tiles + 1; ++t) {
-    if (t + 1 < n_tiles) copy_k(t + 1);
-    if (t - 1 < n_tiles) copy_v(t - 1);
+    // sources of the copies of this iteration, K(t+1) and V(t-1); past the
+    // last tile the last tile is copied again (into a slot whose contents
+    // only meet all-zero probabilities), which keeps the loop free of branches
+    const int last = n_tiles > 0 ? n_tiles - 1 : 0;
+    const int src_k = min(t + 1, last), src_v = min(t - 1, last);
     const int j = t - 1;                       // tile being encoded
     if (j * KEY_TILE + KEY_TILE > len_k || (CAUSAL && j * KEY_TILE + KEY_TILE - 1 > q0)) mask(j);
-    // region A: P(t-2).V(t-2) beside the row statistics and chunk-0 encode of S(t-1)
-    pv(t & 1, pr, psr);
-    stats(psw);
-    encode(0, pw);
+    const uint8_t* sV = smem + 2 * L::K_BYTES + (t & 1) * L::V_SLOT;
+    const uint8_t* kb = smem + (t & 1) * L::K_BYTES + (hh * KS * 32 + ql) * 16;
+    if (VF == VF_MXFP4) {
+      const uint32_t* sVS = reinterpret_cast<const uint32_t*>(sV + L::V_BYTES);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) vsc[dt] = sVS[32 * dt + ql];
+    }
+    load_op(0, sV, kb);
+    load_op(1, sV, kb);
     __builtin_amdgcn_sched_barrier(0);
-    // region B: S(t) sub-tiles 0,1 beside the chunk-1 encode
-    qk2(t & 1, 0);
-    encode(1, pw);
-    __builtin_amdgcn_sched_barrier(0);
-    // region C: S(t) sub-tiles 2,3 beside the O / l rescale
-    qk2(t & 1, 2);
-    rescale();
-    __builtin_amdgcn_sched_barrier(0);
+#pragma clang loop unroll(full)
+    for (int i = 0; i < NS; ++i) {
+      // copies for the next iterations: K(t+1) and V(t-1), one part every
+      // NS / (NK_DMA + NV_DMA) slots
+#pragma unroll
+      for (int q = 0; q < NK_DMA + NV_DMA; ++q)
+        if (i == (q * NS) / (NK_DMA + NV_DMA)) {
+          if (q < NK_DMA) copy_k_part(t + 1, src_k, q);
+          else copy_v_part(t - 1, src_v, q - NK_DMA);
+        }
+      if (i + 2 < NS) load_op(i + 2, sV, kb);
+      mfma_slot(i);
+#pragma unroll
+      for (int u = slot_unit_begin<NPV, KS>(i); u < slot_unit_begin<NPV, KS>(i + 1); ++u) vunit(u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (j < n_tiles) dump(j, pw, psw);
     pr[0] = pw[0]; pr[1] = pw[1]; psr[0] = psw[0]; psr[1] = psw[1];
     dma_wait();
