@@ -156,7 +156,8 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   if (qb * WG_Q >= len_q) return;
   const int hk = h / (p.Hq / p.Hkv);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: kept in a scalar register
   const int hh = lane >> 5, ql = lane & 31;
   const int q0 = qb * WG_Q + wave * WAVE_Q;     // first query of this wave
   const int my_q = q0 + ql;
@@ -206,10 +207,12 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   constexpr int NK_DMA = K_UNITS / 512;
   constexpr int NV_DMA = (V_UNITS + 511) / 512 + (VF == VF_MXFP4 ? 1 : 0);
   // part i of K(src) -> K slot t%2
+  // (tile and part offsets go into the scalar base, so that the per-lane
+  // offsets are loop invariant)
   auto copy_k_part = [&](int t, int src, int i) {
     const uint32_t slot = lds0 + (uint32_t)((t & 1) * L::K_BYTES);
     const int u0 = i * 512 + wave * 64;
-    dma16(ksrc, (uint32_t)(src * L::K_BYTES + (u0 + lane) * 16), slot + u0 * 16);
+    dma16(ksrc + (int64_t)src * L::K_BYTES + u0 * 16, (uint32_t)(lane * 16), slot + u0 * 16);
   };
   // part i of V(src) -> V slot t%2
   auto copy_v_part = [&](int t, int src, int i) {
@@ -220,7 +223,7 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
     if (VF == VF_MXFP4 && i == NV_DMA - 1) {         // E8M0 exponents, one dword per d
       const int w = wave % (D / 64);
       const int d = w * 64 + lane;
-      dma4(shead, (uint32_t)(d * (p.kcols / 32) + col / 32), slot + L::V_BYTES + w * 256);
+      dma4(shead + col / 32, (uint32_t)(d * (p.kcols / 32)), slot + L::V_BYTES + w * 256);
       return;
     }
     const int u0 = (i * 512 + wave * 64) % V_UNITS;
@@ -229,10 +232,10 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
     if (VF == VF_MXFP4) { r = u & 31; kh = (u >> 5) & 1; dt = (u >> 6) % DT; c = (u >> 6) / DT; }
     else { r = u & 31; kh = (u >> 5) & 1; part = (u >> 6) & 1; dt = (u >> 7) % DT; c = (u >> 7) / DT; }
     const int d = 32 * dt + r;
-    uint32_t off;
-    if (VF == VF_MXFP4) off = (uint32_t)((d * p.kcols + col + 64 * c + 32 * kh) / 2);
-    else off = (uint32_t)(d * p.kcols + col + 64 * c + 16 * kh + 32 * part);
-    dma16(vhead, off, slot + u0 * 16);
+    if (VF == VF_MXFP4)   // col and the per-lane key offset are even
+      dma16(vhead + col / 2, (uint32_t)((d * p.kcols + 64 * c + 32 * kh) / 2), slot + u0 * 16);
+    else
+      dma16(vhead + col, (uint32_t)(d * p.kcols + 64 * c + 16 * kh + 32 * part), slot + u0 * 16);
   };
   auto copy_k = [&](int t) {
 #pragma unroll
@@ -246,6 +249,7 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
   float m_run = -__builtin_inff();
   float alpha_pend = 1.0f;
+  bool rescale_any = false;
   f32x16 s[4];
 #pragma unroll
   for (int st = 0; st < 4; ++st) s[st] = f32x16{};
@@ -272,32 +276,6 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   }
 
   // ---- pipeline pieces --------------------------------------------------
-  // O^T += V^T P^T and l += sum(P) for the tile whose V is in V slot `vs`
-  auto pv = [&](int vs, const i32x8 (&pk)[2], const int (&psc)[2]) {
-    const uint8_t* sV = smem + 2 * L::K_BYTES + vs * L::V_SLOT;
-    const uint32_t* sVS = reinterpret_cast<const uint32_t*>(sV + L::V_BYTES);
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        if (VF == VF_MXFP4) {
-          const u32x4 av = *reinterpret_cast<const u32x4*>(sV + ((((c * DT + dt) * 2 + hh) * 32 + ql) * 16));
-          const i32x8 a = {(int)av[0], (int)av[1], (int)av[2], (int)av[3], 0, 0, 0, 0};
-          const int sa = (int)((sVS[32 * dt + ql] >> (8 * (2 * c + hh))) & 0xFFu);
-          oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pk[c], oacc[dt], 4, PF == PF_MXFP4 ? 4 : 0,
-                                                                     0, sa, 0, psc[c]);
-        } else {
-          const u32x4 a0 = *reinterpret_cast<const u32x4*>(sV + ((((c * DT + dt) * 2 + 0) * 2 + hh) * 32 + ql) * 16);
-          const u32x4 a1 = *reinterpret_cast<const u32x4*>(sV + ((((c * DT + dt) * 2 + 1) * 2 + hh) * 32 + ql) * 16);
-          const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-          oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pk[c], oacc[dt], 0, PF == PF_MXFP4 ? 4 : 0,
-                                                                     0, 127, 0, psc[c]);
-        }
-      }
-      lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pk[c], lacc, 4, PF == PF_MXFP4 ? 4 : 0, 0, 127, 0,
-                                                             psc[c]);
-    }
-  };
   // S^T sub-tiles st0, st0+1 of K(t) Q^T (K in slot ks_)
   auto qk2 = [&](int kslot, int st0) {
     const uint8_t* kb = smem + kslot * L::K_BYTES + (hh * KS * 32 + ql) * 16;
@@ -326,78 +304,6 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
         const bool dead = key >= len_k || (CAUSAL && key > my_q);
         if (dead) s[st][v] = -__builtin_inff();
       }
-  };
-  // running max, alpha, block exponents of S (tile j)
-  auto stats = [&](int (&psc)[2]) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      float m0 = __builtin_fmaxf(s[2 * c][0], s[2 * c][1]);
-#pragma unroll
-      for (int v = 2; v < 16; ++v) m0 = __builtin_fmaxf(m0, s[2 * c][v]);
-#pragma unroll
-      for (int v = 0; v < 16; ++v) m0 = __builtin_fmaxf(m0, s[2 * c + 1][v]);
-      bm[c] = m0;
-    }
-    float rmax = __builtin_fmaxf(bm[0], bm[1]);
-    rmax = __builtin_fmaxf(rmax, __shfl_xor(rmax, 32, 64));
-    const float tmax = rmax * cc;                       // max of fl(S*c) (c > 0)
-    const float m_new = __builtin_fmaxf(m_run, tmax);
-    const bool row_dead = m_new == -__builtin_inff();
-    alpha_pend = row_dead ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      if (PF == PF_MXFP4) {
-        const float xmax = bm[c] * cc - m_new;          // fl(fl(S*c) - m'), no contraction
-        const float fl = __builtin_floorf(xmax);
-        const int e = fl < -125.0f ? -127 : (int)fl - 2; // also -inf (no live key)
-        psc[c] = e + 127;
-        me[c] = row_dead ? 0.0f : m_new + (float)e;
-      } else {
-        psc[c] = 127;
-        me[c] = row_dead ? 0.0f : m_new;
-      }
-    }
-  };
-  // Direct-P / FP8 encode of chunk c (keys 64c..64c+63 of the tile) of S
-  auto encode = [&](int c, i32x8 (&pk)[2]) {
-    if (PF == PF_MXFP4) {
-      uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int v = 0; v < 16; v += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v], cc, -me[c]));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v + 1], cc, -me[c]));
-          const int jj = 16 * s2 + v;                   // key index within the lane's block
-          const int word = jj >> 3, byte = (jj >> 1) & 3;
-          if (byte == 0) w[word] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[word], p0, p1, 1.0f, 0);
-          else if (byte == 1) w[word] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[word], p0, p1, 1.0f, 1);
-          else if (byte == 2) w[word] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[word], p0, p1, 1.0f, 2);
-          else w[word] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[word], p0, p1, 1.0f, 3);
-        }
-      pk[c] = i32x8{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
-    } else {
-      int w[8];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int v = 0; v < 16; v += 4) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v], cc, -me[c]));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v + 1], cc, -me[c]));
-          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v + 2], cc, -me[c]));
-          const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + s2][v + 3], cc, -me[c]));
-          int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-          wv = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wv, true);
-          w[4 * s2 + v / 4] = wv;
-        }
-      pk[c] = i32x8{w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7]};
-    }
-  };
-  auto rescale = [&]() {
-#pragma unroll
-    for (int i = 0; i < DT; ++i) oacc[i] *= alpha_pend;
-    lacc[0] *= alpha_pend;
   };
   auto dump = [&](int j, const i32x8 (&pk)[2], const int (&psc)[2]) {
     if (DEBUG && b == p.dbg_b && h == p.dbg_h && my_q < len_q) {
@@ -430,7 +336,8 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   //   units [0, 4)  : block maxima of S(t-1)
   //   unit  4       : row max, m', alpha, block exponents
   //   units [5, 37) : encode two scores (sub-tile (u-5)/8, registers 2k, 2k+1)
-  //   units [37, 45): O / l rescale, one eighth each
+  //   units [37, 45): O / l rescale, one eighth each (run after the slots,
+  //                   and only when some row max of the wave moved)
   // Sub-tile st of S(t-1) is fully encoded before the slot that overwrites it.
   constexpr int NPV = 2 * (DT + 1);
   constexpr int NS = NPV + 4 * KS;
@@ -461,9 +368,13 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
                                                                0, psr[c]);
       } else if (VF == VF_MXFP4) {
         const i32x8 a = {(int)opa[bs][0], (int)opa[bs][1], (int)opa[bs][2], (int)opa[bs][3], 0, 0, 0, 0};
-        const int sa = (int)((vsc[dt] >> (8 * (2 * c + hh))) & 0xFFu);
-        oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pr[c], oacc[dt], 4, PF == PF_MXFP4 ? 4 : 0, 0,
-                                                                   sa, 0, psr[c]);
+        // byte 2c of the lane's shifted scale word is its block (c, hh)
+        if (c == 0)
+          oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pr[c], oacc[dt], 4, PF == PF_MXFP4 ? 4 : 0,
+                                                                     0, (int)vsc[dt], 0, psr[c]);
+        else
+          oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pr[c], oacc[dt], 4, PF == PF_MXFP4 ? 4 : 0,
+                                                                     2, (int)vsc[dt], 0, psr[c]);
       } else {
         const i32x8 a = {(int)opa[bs][0], (int)opa[bs][1], (int)opa[bs][2], (int)opa[bs][3],
                          (int)opb[bs][0], (int)opb[bs][1], (int)opb[bs][2], (int)opb[bs][3]};
@@ -491,6 +402,9 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
       const float m_new = __builtin_fmaxf(m_run, tmax);
       const bool row_dead = m_new == -__builtin_inff();
       alpha_pend = row_dead ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      // alpha is exactly 1 wherever the running max did not move; the rescale
+      // is skipped when that holds for the whole wave
+      rescale_any = __builtin_amdgcn_ballot_w64(alpha_pend != 1.0f) != 0;
       m_run = m_new;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -555,6 +469,10 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
     // only meet all-zero probabilities), which keeps the loop free of branches
     const int last = n_tiles > 0 ? n_tiles - 1 : 0;
     const int src_k = min(t + 1, last), src_v = min(t - 1, last);
+    if (rescale_any) {
+#pragma unroll
+      for (int u = 37; u < 45; ++u) vunit(u);
+    }
     const int j = t - 1;                       // tile being encoded
     if (j * KEY_TILE + KEY_TILE > len_k || (CAUSAL && j * KEY_TILE + KEY_TILE - 1 > q0)) mask(j);
     const uint8_t* sV = smem + 2 * L::K_BYTES + (t & 1) * L::V_SLOT;
@@ -562,27 +480,29 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
     if (VF == VF_MXFP4) {
       const uint32_t* sVS = reinterpret_cast<const uint32_t*>(sV + L::V_BYTES);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) vsc[dt] = sVS[32 * dt + ql];
+      for (int dt = 0; dt < DT; ++dt) vsc[dt] = sVS[32 * dt + ql] >> (8 * hh);   // blocks (c, hh) at bytes 2c
     }
     load_op(0, sV, kb);
     load_op(1, sV, kb);
     __builtin_amdgcn_sched_barrier(0);
 #pragma clang loop unroll(full)
     for (int i = 0; i < NS; ++i) {
-      // copies for the next iterations: K(t+1) and V(t-1), one part every
-      // NS / (NK_DMA + NV_DMA) slots
+      // copies for the next iterations, K(t+1) and V(t-1), spread over the
+      // first half of the slots (so that they have landed by the iteration's end)
 #pragma unroll
       for (int q = 0; q < NK_DMA + NV_DMA; ++q)
-        if (i == (q * NS) / (NK_DMA + NV_DMA)) {
+        if (i == (q * (NS / 2)) / (NK_DMA + NV_DMA)) {
           if (q < NK_DMA) copy_k_part(t + 1, src_k, q);
           else copy_v_part(t - 1, src_v, q - NK_DMA);
         }
       if (i + 2 < NS) load_op(i + 2, sV, kb);
       mfma_slot(i);
 #pragma unroll
-      for (int u = slot_unit_begin<NPV, KS>(i); u < slot_unit_begin<NPV, KS>(i + 1); ++u) vunit(u);
+      for (int u = slot_unit_begin<NPV, KS>(i); u < slot_unit_begin<NPV, KS>(i + 1); ++u)
+        if (u < 37) vunit(u);
       __builtin_amdgcn_sched_barrier(0);
     }
+
     if (j < n_tiles) dump(j, pw, psw);
     pr[0] = pw[0]; pr[1] = pw[1]; psr[0] = psw[0]; psr[1] = psw[1];
     dma_wait();
