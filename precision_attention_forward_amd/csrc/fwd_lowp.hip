@@ -109,13 +109,27 @@ __host__ __device__ constexpr int slot_unit_begin(int i) {
   return i < NPV ? (i * 13) / NPV : 13 + 8 * ((i - NPV) / KS) + (((i - NPV) % KS) * 8) / KS;
 }
 
+// Slot after which the second wave group of a workgroup takes its barrier
+// (the first group takes it after the last slot); see the key loop.
+#ifndef ATTN_G1_BARRIER
+#define ATTN_G1_BARRIER (NS - KS)
+#endif
+#ifndef ATTN_PRIO_MODE
+#define ATTN_PRIO_MODE 1
+#endif
+#ifndef ATTN_PRIO_END
+#define ATTN_PRIO_END (NPV - 1)
+#endif
+
 template <int D, int VF>
 struct LdsLayout {
   static constexpr int K_BYTES = KEY_TILE * D * 2;                         // fp16 K tile
   static constexpr int V_BYTES = VF == VF_MXFP4 ? KEY_TILE * D / 2 : KEY_TILE * D;
   static constexpr int VS_BYTES = VF == VF_MXFP4 ? D * 4 : 0;              // E8M0 V scales
   static constexpr int V_SLOT = V_BYTES + VS_BYTES;
-  static constexpr int TOTAL = 2 * K_BYTES + 2 * V_SLOT;
+  static constexpr int RING = 3;                                            // tiles in flight
+  static constexpr int V_BASE = RING * K_BYTES;
+  static constexpr int TOTAL = RING * K_BYTES + RING * V_SLOT;
 };
 
 // Software pipeline of one wave (32 queries).  Iteration t of the key loop:
@@ -139,15 +153,33 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   using L = LdsLayout<D, VF>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
-  // ---- workgroup -> (batch, head, query block); XCD-grouped so that the
-  // query blocks of one head share an L2.
+  // ---- workgroup -> (batch, head, query block).
+  // Dense batches: XCD-grouped, so that the query blocks of one head run on
+  // one XCD and share its L2 copy of the head's K / V tiles (workgroups are
+  // dispatched round-robin over the 8 XCDs).
+  // Packed variable-length batches: sequences differ in length, so grouping
+  // them by XCD would leave XCDs unevenly loaded; there the order is query
+  // block major, from the last block down (only long sequences have high
+  // blocks, and their workgroups are the longest-running), and consecutive
+  // workgroups spread over all XCDs.
   const int nwg = gridDim.x;
   int lin = blockIdx.x;
-  if ((nwg & 7) == 0) lin = (lin & 7) * (nwg >> 3) + (lin >> 3);
-  int qb = lin % p.QB;
-  const int h = (lin / p.QB) % p.Hq;
-  const int b = lin / (p.QB * p.Hq);
-  if (CAUSAL) qb = p.QB - 1 - qb;      // longest rows first
+  int qb, h, b;
+  if (p.cu_q != nullptr) {
+    qb = p.QB - 1 - lin / (p.B * p.Hq);
+    h = lin % p.Hq;
+    b = (lin / p.Hq) % p.B;
+  } else {
+    if ((nwg & 7) == 0) lin = (lin & 7) * (nwg >> 3) + (lin >> 3);
+    qb = lin % p.QB;
+    h = (lin / p.QB) % p.Hq;
+    b = lin / (p.QB * p.Hq);
+    if (CAUSAL) qb = p.QB - 1 - qb;    // longest rows first
+  }
+  // (uniform: keep them, and everything derived, in scalar registers)
+  qb = __builtin_amdgcn_readfirstlane(qb);
+  h = __builtin_amdgcn_readfirstlane(h);
+  b = __builtin_amdgcn_readfirstlane(b);
   const bool varlen = p.cu_q != nullptr;
   const int64_t tq0 = varlen ? p.cu_q[b] : (int64_t)b * p.Nq;
   const int64_t tk0 = varlen ? p.cu_k[b] : (int64_t)b * p.Nk;
@@ -206,17 +238,17 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   // stall the issuing waves' matrix work behind it.
   constexpr int NK_DMA = K_UNITS / 512;
   constexpr int NV_DMA = (V_UNITS + 511) / 512 + (VF == VF_MXFP4 ? 1 : 0);
-  // part i of K(src) -> K slot t%2
+  // part i of K(src) -> K ring slot rs
   // (tile and part offsets go into the scalar base, so that the per-lane
   // offsets are loop invariant)
-  auto copy_k_part = [&](int t, int src, int i) {
-    const uint32_t slot = lds0 + (uint32_t)((t & 1) * L::K_BYTES);
+  auto copy_k_part = [&](int rs, int src, int i) {
+    const uint32_t slot = lds0 + (uint32_t)(rs * L::K_BYTES);
     const int u0 = i * 512 + wave * 64;
     dma16(ksrc + (int64_t)src * L::K_BYTES + u0 * 16, (uint32_t)(lane * 16), slot + u0 * 16);
   };
-  // part i of V(src) -> V slot t%2
-  auto copy_v_part = [&](int t, int src, int i) {
-    const uint32_t slot = lds0 + (uint32_t)(2 * L::K_BYTES + (t & 1) * L::V_SLOT);
+  // part i of V(src) -> V ring slot rs
+  auto copy_v_part = [&](int rs, int src, int i) {
+    const uint32_t slot = lds0 + (uint32_t)(L::V_BASE + rs * L::V_SLOT);
     const int64_t col = kcol0 + (int64_t)src * KEY_TILE;
     // No branches here (these copies sit inside the key loop's slots): waves
     // beyond the ones a part needs copy the same bytes to the same place again.
@@ -237,7 +269,7 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
     else
       dma16(vhead + col, (uint32_t)(d * p.kcols + 64 * c + 16 * kh + 32 * part), slot + u0 * 16);
   };
-  auto copy_k = [&](int t) {
+  auto copy_k = [&](int t) {                 // K(t) -> ring slot t (prologue, t < 3)
 #pragma unroll
     for (int i = 0; i < NK_DMA; ++i) copy_k_part(t, t, i);
   };
@@ -450,10 +482,23 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   // tile before 0 is all-zero codes against a zeroed V slot, and the tile
   // after the last is masked completely (all its probabilities are 0), so the
   // steady body has no branches between its matrix and vector work.
+  //
+  // K and V tiles sit in rings of three LDS slots (tile x in slot x mod 3).
+  // Iteration t copies K(t+1) and V(t-1) in its first NS/2 slots; every wave
+  // waits for its own copies and then joins one workgroup barrier per
+  // iteration.  Waves 0-3 take it after their last slot, waves 4-7 after
+  // slot G1B: the two waves of a SIMD (one of each group) then run G1B slots
+  // apart instead of in step, so the vector-heavy first slots of one meet
+  // the matrix-only last slots of the other.  With three slots a tile is
+  // overwritten only two barriers after the last iteration that reads it,
+  // which covers the lag of the second group.
+  constexpr int G1B = ATTN_G1_BARRIER;
+  static_assert(G1B >= NS / 2, "the second group's barrier must follow its copies");
+  const int group = wave >> 2;
   {
-    // zero the V slots once (P(-1) = 0 meets V slot 1 in iteration 1)
-    for (int i = tid; i < 2 * L::V_SLOT / 16; i += 512)
-      *reinterpret_cast<u32x4*>(smem + 2 * L::K_BYTES + i * 16) = u32x4{0u, 0u, 0u, 0u};
+    // zero the V slots once (P(-1) = 0 meets V(-1) = slot 2 in iteration 1)
+    for (int i = tid; i < L::RING * L::V_SLOT / 16; i += 512)
+      *reinterpret_cast<u32x4*>(smem + L::V_BASE + i * 16) = u32x4{0u, 0u, 0u, 0u};
   }
   copy_k(0);
   dma_wait();
@@ -463,20 +508,26 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   qk2(0, 2);
   dma_wait();
   phase_barrier();
+  int rk = 1;                                  // ring slot of K(t) = t mod 3
   for (int t = 1; t <= n_tiles + 1; ++t) {
+    const int rk1 = rk == 2 ? 0 : rk + 1, rk2 = rk1 == 2 ? 0 : rk1 + 1;   // (t+1), (t+2) = (t-1) mod 3
     // sources of the copies of this iteration, K(t+1) and V(t-1); past the
     // last tile the last tile is copied again (into a slot whose contents
     // only meet all-zero probabilities), which keeps the loop free of branches
     const int last = n_tiles > 0 ? n_tiles - 1 : 0;
     const int src_k = min(t + 1, last), src_v = min(t - 1, last);
+    // O / l rescale by alpha(t-2), set while S(t-2) was encoded in the
+    // previous iteration: after P(t-3).V, before P(t-2).V.  Only waves where
+    // some row max moved do it (alpha is exactly 1 elsewhere); as a branch
+    // inside the slots it would split them, so it runs before them.
     if (rescale_any) {
 #pragma unroll
       for (int u = 37; u < 45; ++u) vunit(u);
     }
     const int j = t - 1;                       // tile being encoded
     if (j * KEY_TILE + KEY_TILE > len_k || (CAUSAL && j * KEY_TILE + KEY_TILE - 1 > q0)) mask(j);
-    const uint8_t* sV = smem + 2 * L::K_BYTES + (t & 1) * L::V_SLOT;
-    const uint8_t* kb = smem + (t & 1) * L::K_BYTES + (hh * KS * 32 + ql) * 16;
+    const uint8_t* sV = smem + L::V_BASE + rk1 * L::V_SLOT;                   // V(t-2): (t-2) mod 3 = (t+1) mod 3
+    const uint8_t* kb = smem + rk * L::K_BYTES + (hh * KS * 32 + ql) * 16;   // K(t)
     if (VF == VF_MXFP4) {
       const uint32_t* sVS = reinterpret_cast<const uint32_t*>(sV + L::V_BYTES);
 #pragma unroll
@@ -484,16 +535,19 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
     }
     load_op(0, sV, kb);
     load_op(1, sV, kb);
+#if ATTN_PRIO_MODE == 1 || ATTN_PRIO_MODE == 2
+    setprio_if<2>(group);
+#endif
     __builtin_amdgcn_sched_barrier(0);
 #pragma clang loop unroll(full)
     for (int i = 0; i < NS; ++i) {
       // copies for the next iterations, K(t+1) and V(t-1), spread over the
-      // first half of the slots (so that they have landed by the iteration's end)
+      // first half of the slots
 #pragma unroll
       for (int q = 0; q < NK_DMA + NV_DMA; ++q)
         if (i == (q * (NS / 2)) / (NK_DMA + NV_DMA)) {
-          if (q < NK_DMA) copy_k_part(t + 1, src_k, q);
-          else copy_v_part(t - 1, src_v, q - NK_DMA);
+          if (q < NK_DMA) copy_k_part(rk1, src_k, q);
+          else copy_v_part(rk2, src_v, q - NK_DMA);
         }
       if (i + 2 < NS) load_op(i + 2, sV, kb);
       mfma_slot(i);
@@ -501,12 +555,16 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
       for (int u = slot_unit_begin<NPV, KS>(i); u < slot_unit_begin<NPV, KS>(i + 1); ++u)
         if (u < 37) vunit(u);
       __builtin_amdgcn_sched_barrier(0);
+#if ATTN_PRIO_MODE == 1
+      if (i == ATTN_PRIO_END) setprio_if<0>(group);
+#endif
+      if (i == G1B - 1 && G1B < NS) dma_wait_barrier_if(group);
     }
 
     if (j < n_tiles) dump(j, pw, psw);
     pr[0] = pw[0]; pr[1] = pw[1]; psr[0] = psw[0]; psr[1] = psw[1];
-    dma_wait();
-    phase_barrier();
+    dma_wait_barrier_if(G1B >= NS ? 1 : group ^ 1);
+    rk = rk1;
   }
 
   // ---- epilogue: O = o / l (x FP8 V tensor scale), LSE = ln2 * (m + log2 l)

@@ -49,4 +49,34 @@ __device__ inline void phase_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Wait for this wave's copies and join the workgroup barrier, but only when
+// `take` (wave-uniform, in a scalar register) is nonzero.  The test and the
+// branch around the barrier sit inside one asm statement, so that the code
+// around it stays a single basic block for the compiler's scheduler and
+// register allocator.  Each wave must still join the same number of barriers.
+__device__ inline void dma_wait_barrier_if(int take) {
+  asm volatile(
+      "s_cmp_eq_u32 %0, 0\n\t"
+      "s_cbranch_scc1 1f\n\t"
+      "s_waitcnt vmcnt(0)\n\t"
+      "s_barrier\n"
+      "1:"
+      :
+      : "s"(take)
+      : "memory", "scc");
+}
+
+// Set this wave's issue priority to PRIO when `take` (wave-uniform) is nonzero.
+template <int PRIO>
+__device__ inline void setprio_if(int take) {
+  asm volatile(
+      "s_cmp_eq_u32 %0, 0\n\t"
+      "s_cbranch_scc1 1f\n\t"
+      "s_setprio %1\n"
+      "1:"
+      :
+      : "s"(take), "n"(PRIO)
+      : "scc");
+}
+
 }  // namespace attn
