@@ -69,7 +69,7 @@ def _check(gpu, inp, heads=None, seqs=None, rows=None, debug=None, max_rows=None
     stats = []
     worst = [0.0, 0.0, 0.0]
     for (s, t0, L) in _seq_slices(inp):
-        if seqs is not None and s not in seqs:
+        if (seqs is not None and s not in seqs) or L == 0:
             continue
         for h in (range(wl.Hq) if heads is None else heads):
             hk = h // group
@@ -116,6 +116,7 @@ SMALL = [
     ("directp_fp8v_d128_gqa", synth.WORKLOADS[2].with_(Hq=4, Hkv=1, N=384, v_format="fp8", seed=22), None),
     ("varlen_small", synth.WORKLOADS[5].with_(Hq=2, Hkv=2, varlen=(5, 1, 700), seed=51), None),
     ("varlen_causal_fp8", synth.WORKLOADS[4].with_(B=0, Hq=2, Hkv=1, varlen=(4, 1, 400), seed=52), None),
+    ("llama_causal_d64", synth.WORKLOADS[4].with_(B=1, Hq=2, Hkv=1, N=450, D=64, seed=43), None),
 ]
 
 
@@ -138,6 +139,23 @@ def test_edge_single_key_and_short(gpu):
         if N == 1:
             # one key: every query's O is the same dequantized V row
             assert torch.equal(o[0, :1].expand_as(o[0]), o[0])
+
+
+def test_varlen_with_empty_sequences(gpu):
+    # packed batch whose second and fourth sequences are empty: their
+    # workgroups must write nothing and the neighbours must be unaffected
+    wl = synth.WORKLOADS[5].with_(Hq=2, Hkv=1, varlen=(4, 0, 300), seed=53)
+    lens = torch.tensor([257, 0, 130, 0], dtype=torch.int32)
+    T = int(lens.sum())
+    g = torch.Generator().manual_seed(53)
+    q = torch.randn(T, 2, 128, generator=g).to(torch.bfloat16).cuda()
+    k = torch.randn(T, 1, 128, generator=g).to(torch.bfloat16).cuda()
+    v = torch.randn(T, 1, 128, generator=g).to(torch.bfloat16).cuda()
+    cu = torch.zeros(5, dtype=torch.int32)
+    cu[1:] = torch.cumsum(lens, 0)
+    inp = synth.Inputs(wl, q, k, v, lens, cu, None)
+    _say("varlen lengths [257, 0, 130, 0]")
+    _check(gpu, inp, debug=(0, 1))
 
 
 def test_edge_zero_queries_closed_form(gpu):
