@@ -102,11 +102,12 @@ __global__ void __launch_bounds__(256) expand_nvfp4_kernel(const uint8_t* __rest
 
 
 // First vector unit of slot i of the key loop: slots [0, NPV) carry units
-// [0, 13) (statistics and the encode of sub-tile 0); then each group of KS
-// slots carries 8 units (encode of the next sub-tile, finally the rescale).
+// [3, 13) (statistics and the encode of sub-tile 0); then each group of KS
+// slots carries 8 units (encode of the next sub-tile; in the last group the
+// rescale units, which run elsewhere).
 template <int NPV, int KS>
 __host__ __device__ constexpr int slot_unit_begin(int i) {
-  return i < NPV ? (i * 13) / NPV : 13 + 8 * ((i - NPV) / KS) + (((i - NPV) % KS) * 8) / KS;
+  return i < NPV ? 3 + (i * 10) / NPV : 13 + 8 * ((i - NPV) / KS) + (((i - NPV) % KS) * 8) / KS;
 }
 
 // Slot after which the second wave group of a workgroup takes its barrier
@@ -287,7 +288,9 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   for (int st = 0; st < 4; ++st) s[st] = f32x16{};
   i32x8 pw[2], pr[2];                  // probabilities being written / read by P.V
   int psw[2] = {127, 127}, psr[2] = {127, 127};
-  float bm[2] = {0.f, 0.f};
+  float bm[2] = {0.f, 0.f};            // block maxima of S(t-1) (raw scores)
+  float bmp[2] = {0.f, 0.f};           // S(t-1): max of sub-tiles 0,1 / of sub-tile 2 (set a tile ahead)
+  float bmn[2] = {0.f, 0.f};           // the same for S(t), built during iteration t
   float me[2] = {0.f, 0.f};
   pw[0] = pw[1] = pr[0] = pr[1] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
 
@@ -324,6 +327,15 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
       s[st0 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, qf[ks], ks == 0 ? f32x16{} : s[st0 + 1], 0, 0, 0);
       if (ks + 1 < KS) { a0 = n0; a1 = n1; }
     }
+  };
+  // max of the 16 scores of S sub-tile st, as a shallow tree (short dependency chains)
+  auto tile_max = [&](int st) {
+    const float a = __builtin_fmaxf(__builtin_fmaxf(s[st][0], s[st][1]), s[st][2]);
+    const float b = __builtin_fmaxf(__builtin_fmaxf(s[st][3], s[st][4]), s[st][5]);
+    const float c = __builtin_fmaxf(__builtin_fmaxf(s[st][6], s[st][7]), s[st][8]);
+    const float d = __builtin_fmaxf(__builtin_fmaxf(s[st][9], s[st][10]), s[st][11]);
+    const float e = __builtin_fmaxf(__builtin_fmaxf(s[st][12], s[st][13]), s[st][14]);
+    return __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(a, b), c), __builtin_fmaxf(__builtin_fmaxf(d, e), s[st][15]));
   };
   // masking of S (tail of the sequence, causal diagonal) for tile j
   auto mask = [&](int j) {
@@ -365,11 +377,13 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   // that matrix and vector work stay interleaved in the instruction stream
   // (one wave issues in order: a run of matrix instructions would otherwise
   // stall its vector work).  LDS operands are read two slots ahead.
-  //   units [0, 4)  : block maxima of S(t-1)
+  //   unit  3       : block maxima of S(t-1): sub-tile 3 joins the maxima of
+  //                   sub-tiles 0..2, taken beside the previous iteration's
+  //                   later slots (units 45..47, one phase after each sub-tile)
   //   unit  4       : row max, m', alpha, block exponents
   //   units [5, 37) : encode two scores (sub-tile (u-5)/8, registers 2k, 2k+1)
-  //   units [37, 45): O / l rescale, one eighth each (run after the slots,
-  //                   and only when some row max of the wave moved)
+  //   units [37, 45): O / l rescale, one eighth each (run at the head of the
+  //                   next iteration, and only when some row max of the wave moved)
   // Sub-tile st of S(t-1) is fully encoded before the slot that overwrites it.
   constexpr int NPV = 2 * (DT + 1);
   constexpr int NS = NPV + 4 * KS;
@@ -420,12 +434,11 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
     }
   };
   auto vunit = [&](int u) {
-    if (u < 4) {                                 // block max of chunk u/2, half u%2
-      const int c = u >> 1, st = 2 * c + (u & 1);
-      float m0 = (u & 1) ? bm[c] : s[st][0];
-#pragma unroll
-      for (int v = (u & 1) ? 0 : 1; v < 16; ++v) m0 = __builtin_fmaxf(m0, s[st][v]);
-      bm[c] = m0;
+    if (u < 4) {                                 // block maxima of S(t-1): sub-tile 3 joins the
+      if (u == 3) {                              // maxima of sub-tiles 0..2 taken a tile earlier
+        bm[0] = bmp[0];
+        bm[1] = __builtin_fmaxf(bmp[1], tile_max(3));
+      }
     } else if (u == 4) {                         // row statistics
       float rmax = __builtin_fmaxf(bm[0], bm[1]);
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax), __float_as_uint(rmax), false, false);
@@ -468,6 +481,10 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
         if (k & 1) pw[c][word] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pw[c][word], true);
         else pw[c][word] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pw[c][word], false);
       }
+    } else if (u >= 45) {                        // maxima of S(t) sub-tiles 0..2 for the next tile
+      if (u == 45) bmn[0] = tile_max(0);
+      else if (u == 46) bmn[0] = __builtin_fmaxf(bmn[0], tile_max(1));
+      else bmn[1] = tile_max(2);
     } else {                                     // rescale slice
       const int r = u - 37;
 #pragma unroll
@@ -506,6 +523,8 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   if (n_tiles > 1) copy_k(1);
   qk2(0, 0);
   qk2(0, 2);
+  bmp[0] = __builtin_fmaxf(tile_max(0), tile_max(1));
+  bmp[1] = tile_max(2);
   dma_wait();
   phase_barrier();
   int rk = 1;                                  // ring slot of K(t) = t mod 3
@@ -525,7 +544,11 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
       for (int u = 37; u < 45; ++u) vunit(u);
     }
     const int j = t - 1;                       // tile being encoded
-    if (j * KEY_TILE + KEY_TILE > len_k || (CAUSAL && j * KEY_TILE + KEY_TILE - 1 > q0)) mask(j);
+    if (j * KEY_TILE + KEY_TILE > len_k || (CAUSAL && j * KEY_TILE + KEY_TILE - 1 > q0)) {
+      mask(j);
+      bmp[0] = __builtin_fmaxf(tile_max(0), tile_max(1));   // maxima taken before the mask
+      bmp[1] = tile_max(2);
+    }
     const uint8_t* sV = smem + L::V_BASE + rk1 * L::V_SLOT;                   // V(t-2): (t-2) mod 3 = (t+1) mod 3
     const uint8_t* kb = smem + rk * L::K_BYTES + (hh * KS * 32 + ql) * 16;   // K(t)
     if (VF == VF_MXFP4) {
@@ -554,6 +577,9 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
 #pragma unroll
       for (int u = slot_unit_begin<NPV, KS>(i); u < slot_unit_begin<NPV, KS>(i + 1); ++u)
         if (u < 37) vunit(u);
+      if (i == NPV + 2 * KS - 1) vunit(45);      // S(t) sub-tile 0, finished one phase ago
+      if (i == NPV + 3 * KS - 1) vunit(46);      // sub-tile 1
+      if (i == NS - 1) vunit(47);                // sub-tile 2
       __builtin_amdgcn_sched_barrier(0);
 #if ATTN_PRIO_MODE == 1
       if (i == ATTN_PRIO_END) setprio_if<0>(group);
@@ -563,6 +589,7 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
 
     if (j < n_tiles) dump(j, pw, psw);
     pr[0] = pw[0]; pr[1] = pw[1]; psr[0] = psw[0]; psr[1] = psw[1];
+    bmp[0] = bmn[0]; bmp[1] = bmn[1];
     dma_wait_barrier_if(G1B >= NS ? 1 : group ^ 1);
     rk = rk1;
   }
