@@ -174,15 +174,18 @@ typedef struct attn_fwd_args {
   int32_t dbg_b, dbg_h;
   /* Optional profiling: hipEvent_t handles (NULL to skip) recorded on
    * `stream` immediately before and after the attention kernel itself (after
-   * the Q/K expansion pre-pass), so callers can time the dominant kernel. */
+   * the K expansion pre-pass), so callers can time the dominant kernel. */
   void* prof_event_begin;
   void* prof_event_end;
 } attn_fwd_args;
 
 /* Bytes of device workspace the forward needs for these shapes: the exact
- * float16 expansion of the NVFP4 Q and K payloads (E2M1 * E4M3, 6
- * significant bits, exact in float16), arranged in 32-query and 128-key
- * tiles.  Returns 0 for invalid shapes. */
+ * float16 expansion of the NVFP4 K payload (E2M1 * E4M3, 6 significant
+ * bits, exact in float16), arranged in 128-key operand tiles, i.e.
+ * 2 * D * Hkv * kcols + 256 with kcols = B * roundup(Nk, 128), or
+ * 128 * (ceil(total_k / 128) + B) for packed batches.  (Q is decoded from
+ * its NVFP4 codes inside the attention kernel.)  Returns 0 for invalid
+ * shapes. */
 size_t attn_fwd_ws_bytes(const attn_fwd_args* a);
 
 /*

@@ -15,8 +15,9 @@ hipError_t launch_quant_nvfp4(const void* x, int64_t rows, int D, const float* p
 hipError_t launch_quant_v(const void* v, int B, int Nk, int Hkv, int D, const int32_t* cu_k, int max_len, int64_t cols,
                           int fmt, const float* partials, int np, uint8_t* codes, uint8_t* scales, float* tensor_scale,
                           hipStream_t st);
-hipError_t launch_expand(bool is_q, const uint8_t* codes, const uint8_t* scales, int H, int B, int N, int max_len,
-                         const int32_t* cu, int64_t n_pad, int64_t cols, int D, int pf, _Float16* out, hipStream_t st);
+hipError_t launch_expand_k(const uint8_t* codes, const uint8_t* scales, int H, int B, int N, int max_len,
+                           const int32_t* cu, int64_t n_pad, int64_t cols, int D, int pf, _Float16* out,
+                           hipStream_t st);
 struct FwdParams;
 hipError_t launch_fwd_lowp(const FwdParams& p, int D, int pf, int vf, bool causal, bool debug, hipStream_t st);
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
@@ -105,24 +106,15 @@ attn_status attn_quant_v(const void* v_bf16, int32_t B, int32_t Nk, int32_t Hkv,
                                    tensor_scale, st));
 }
 
-// Workspace layout of the forward: [Q fp16 tiles | K fp16 tiles].
-static bool fwd_geometry(const attn_fwd_args* a, int64_t* qcols, int64_t* kcols) {
-  const bool varlen = a->cu_seqlens_q != nullptr;
-  if (varlen) {
-    *qcols = 32 * ((a->total_q + 31) / 32 + a->B);
-    *kcols = 128 * ((a->total_k + 127) / 128 + a->B);
-  } else {
-    *qcols = (int64_t)a->B * roundup(a->Nq, 32);
-    *kcols = (int64_t)a->B * roundup(a->Nk, 128);
-  }
-  return true;
+// Workspace of the forward: the K fp16 operand tiles, kcols columns per KV head.
+static int64_t fwd_kcols(const attn_fwd_args* a) {
+  if (a->cu_seqlens_q != nullptr) return 128 * ((a->total_k + 127) / 128 + a->B);
+  return (int64_t)a->B * roundup(a->Nk, 128);
 }
 
 size_t attn_fwd_ws_bytes(const attn_fwd_args* a) {
   if (a == nullptr || a->B < 0 || a->Hq <= 0 || a->Hkv <= 0 || (a->D != 64 && a->D != 128)) return 0;
-  int64_t qc, kc;
-  fwd_geometry(a, &qc, &kc);
-  return (size_t)(2 * a->D) * (size_t)(a->Hq * qc + a->Hkv * kc) + 256;
+  return (size_t)(2 * a->D) * (size_t)(a->Hkv * fwd_kcols(a)) + 256;
 }
 
 static attn_status validate_fwd(const attn_fwd_args* a, bool allow_causal, int pf) {
@@ -171,22 +163,17 @@ static attn_status run_fwd_lowp(const attn_fwd_args* a, void* stream, int pf) {
   if (s != ATTN_OK) return s;
   hipStream_t st = (hipStream_t)stream;
   const bool varlen = a->cu_seqlens_q != nullptr;
-  int64_t qcols, kcols;
-  fwd_geometry(a, &qcols, &kcols);
-  _Float16* qhat = (_Float16*)a->ws;
-  _Float16* khat = qhat + (int64_t)a->Hq * qcols * a->D;
-  const int64_t nq_pad = roundup(a->Nq, 32), nk_pad = roundup(a->Nk, 128);
-  hipError_t e = launch_expand(true, a->q.codes, a->q.scales, a->Hq, a->B, a->Nq, a->Nq, a->cu_seqlens_q, nq_pad,
-                               qcols, a->D, pf, qhat, st);
-  if (e != hipSuccess) return hip_status(e);
-  e = launch_expand(false, a->k.codes, a->k.scales, a->Hkv, a->B, a->Nk, a->Nk, a->cu_seqlens_k, nk_pad, kcols,
-                    a->D, pf, khat, st);
+  const int64_t kcols = fwd_kcols(a);
+  _Float16* khat = (_Float16*)a->ws;
+  const int64_t nk_pad = roundup(a->Nk, 128);
+  hipError_t e = launch_expand_k(a->k.codes, a->k.scales, a->Hkv, a->B, a->Nk, a->Nk, a->cu_seqlens_k, nk_pad, kcols,
+                                 a->D, pf, khat, st);
   if (e != hipSuccess) return hip_status(e);
   FwdParams p;
   memset(&p, 0, sizeof(p));
-  p.qhat = qhat;
+  p.q_codes = a->q.codes;
+  p.q_scales = a->q.scales;
   p.khat = khat;
-  p.qcols = qcols;
   p.kcols = kcols;
   p.v_codes = a->v.codes;
   p.v_scales = a->v.scales;
@@ -204,7 +191,6 @@ static attn_status run_fwd_lowp(const attn_fwd_args* a, void* stream, int pf) {
   p.Nq = a->Nq;
   p.Nk = a->Nk;
   p.QB = (a->Nq + WG_Q - 1) / WG_Q;
-  p.nq_pad = nq_pad;
   p.nk_pad = nk_pad;
   p.sigma = a->softmax_scale;
   p.dbg_codes = a->dbg_p_codes;

@@ -30,10 +30,6 @@ __host__ __device__ inline int64_t roundup(int64_t x, int64_t m) { return (x + m
 __host__ __device__ inline int64_t kcol_offset(bool varlen, int s, int64_t cu_k_s, int64_t nk_pad) {
   return varlen ? 128 * (cu_k_s / 128 + s) : (int64_t)s * nk_pad;
 }
-// Start column of sequence s in the tiled Q layout (32-query groups).
-__host__ __device__ inline int64_t qcol_offset(bool varlen, int s, int64_t cu_q_s, int64_t nq_pad) {
-  return varlen ? 32 * (cu_q_s / 32 + s) : (int64_t)s * nq_pad;
-}
 
 // bf16 bits -> float (exact).
 __device__ inline float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }

@@ -44,62 +44,40 @@ __host__ __device__ inline int s_key(int st, int v, int hh) {
 __host__ __device__ inline int out_row(int v, int hh) { return 8 * (v >> 2) + 4 * hh + (v & 3); }
 
 // ---------------------------------------------------------------------------
-// Pre-pass: exact FP16 expansion of NVFP4 Q / K into the operand tile order.
+// Pre-pass: exact FP16 expansion of NVFP4 K into the operand tile order.
 //   K tile (128 keys, D): element (st, kh, ks, r, j) at (((st*2+kh)*KS+ks)*32+r)*8+j,
 //     holding K[key = s_key(st, v(r), hh(r))][d = kh*D/2 + 8*ks + j], KS = D/16.
-//   Q group (32 queries, D): element (lane = 32*kh + q, o) at lane*(D/2) + o,
-//     holding Q[q][kh*D/2 + o].
-// Padding rows are written as zeros.
-template <bool IS_Q, int D, int PF>
-__global__ void __launch_bounds__(256) expand_nvfp4_kernel(const uint8_t* __restrict__ codes,
-                                                           const uint8_t* __restrict__ scales, int H, int N,
-                                                           const int32_t* __restrict__ cu, int64_t n_pad,
-                                                           int64_t cols, _Float16* __restrict__ out) {
+// Each thread writes whole 16-byte chunks in output order (coalesced) and
+// gathers the 4 code bytes and the scale of its 8 elements.  Keys past the
+// end of the sequence are written as zeros.
+template <int D, int PF>
+__global__ void __launch_bounds__(256) expand_k_kernel(const uint8_t* __restrict__ codes,
+                                                       const uint8_t* __restrict__ scales, int H, int N,
+                                                       const int32_t* __restrict__ cu, int64_t n_pad, int64_t cols,
+                                                       _Float16* __restrict__ out) {
   const int tile = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const bool varlen = cu != nullptr;
   const int64_t tok0 = varlen ? cu[s] : (int64_t)s * N;
   const int len = varlen ? cu[s + 1] - cu[s] : N;
-  const int lim = IS_Q ? (int)roundup(len, 32) : (int)roundup(len, KEY_TILE);
-  if (tile * 128 >= lim) return;
-  const int64_t col0 = IS_Q ? qcol_offset(varlen, s, tok0, n_pad) : kcol_offset(varlen, s, tok0, n_pad);
-  constexpr int NB = D / 16, KS = D / 16, HALF = D / 2;
-  for (int p = threadIdx.x; p < 128 * NB; p += 256) {
-    const int row = p / NB, b16 = p % NB;        // row within this 128-row block
-    const int idx = tile * 128 + row;            // token index within the sequence
-    if (idx >= lim) continue;
-    f16x8 lo = {}, hi = {};
+  if (tile * KEY_TILE >= len) return;
+  constexpr int KS = D / 16, HALF = D / 2, CHUNKS = KEY_TILE * D / 8;
+  _Float16* tb = out + ((int64_t)h * cols + kcol_offset(varlen, s, tok0, n_pad) + (int64_t)tile * KEY_TILE) * D;
+  for (int u = threadIdx.x; u < CHUNKS; u += 256) {
+    const int r = u & 31, ks = (u >> 5) % KS, kh = ((u >> 5) / KS) & 1, st = (u >> 5) / (2 * KS);
+    const int hh = (r >> 2) & 1, v = 4 * (r >> 3) + (r & 3);   // inverse of out_row
+    const int idx = tile * KEY_TILE + s_key<PF>(st, v, hh);
+    const int d0 = kh * HALF + 8 * ks;
+    f16x8 val = {};
     if (idx < len) {
-      const int64_t r = (tok0 + idx) * H + h;
-      const uint2 cw = *reinterpret_cast<const uint2*>(codes + r * (D / 2) + 8 * b16);
-      const float sv = e4m3_decode(scales[r * NB + b16]);
+      const int64_t row = (tok0 + idx) * H + h;
+      const uint32_t cw = *reinterpret_cast<const uint32_t*>(codes + row * HALF + d0 / 2);
+      const float sv = e4m3_decode(scales[row * (D / 16) + d0 / 16]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        lo[j] = (_Float16)(e2m1_decode((cw.x >> (4 * j)) & 0xFu) * sv);
-        hi[j] = (_Float16)(e2m1_decode((cw.y >> (4 * j)) & 0xFu) * sv);
-      }
+      for (int j = 0; j < 8; ++j) val[j] = (_Float16)(e2m1_decode((cw >> (4 * j)) & 0xFu) * sv);
     }
-    const int d0 = 16 * b16, kh = d0 / HALF, o = d0 % HALF;
-    _Float16* base = out + ((int64_t)h * cols + col0) * D;
-    if (IS_Q) {
-      const int g = idx / 32, q = idx % 32;
-      _Float16* dst = base + (int64_t)g * 32 * D + (int64_t)(32 * kh + q) * HALF + o;
-      *reinterpret_cast<f16x8*>(dst) = lo;
-      *reinterpret_cast<f16x8*>(dst + 8) = hi;
-    } else {
-      const int t = idx / 128, key = idx % 128;
-      int st, v, hh;
-      const int c = key >> 6;
-      if (PF == PF_MXFP4) { hh = (key >> 5) & 1; st = 2 * c + ((key >> 4) & 1); }
-      else                { st = 2 * c + ((key >> 5) & 1); hh = (key >> 4) & 1; }
-      v = key & 15;
-      const int r = out_row(v, hh), ks = o / 8;
-      _Float16* tb = base + (int64_t)t * 128 * D;
-      *reinterpret_cast<f16x8*>(tb + ((((st * 2 + kh) * KS + ks) * 32 + r) * 8)) = lo;
-      *reinterpret_cast<f16x8*>(tb + ((((st * 2 + kh) * KS + ks + 1) * 32 + r) * 8)) = hi;
-    }
+    *reinterpret_cast<f16x8*>(tb + u * 8) = val;
   }
 }
-
 
 // First vector unit of slot i of the key loop: slots [0, NPV) carry units
 // [3, 13) (statistics and the encode of sub-tile 0); then each group of KS
@@ -206,15 +184,21 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   const float cc = (float)((double)p.sigma * 1.4426950408889634 * (double)(*p.gq) * (double)(*p.gk));
   const float vscale = VF == VF_FP8 ? *p.sv : 1.0f;
 
-  // ---- Q operand (B of S^T): lane holds query ql, d in [hh*D/2, hh*D/2 + D/2)
+  // ---- Q operand (B of S^T): lane holds query ql, d in [hh*D/2, hh*D/2 + D/2),
+  // decoded here from the NVFP4 codes (E2M1 * E4M3 is exact in FP16); once per
+  // workgroup, so a separate expansion pass for Q is not needed
   f16x8 qf[KS];
   {
-    const int64_t qcol = qcol_offset(varlen, b, tq0, p.nq_pad) + q0;
-    const _Float16* src = p.qhat + ((int64_t)h * p.qcols + qcol) * D + lane * HALF;
+    const bool live = wave_active && my_q < len_q;
+    const int64_t row = live ? (tq0 + my_q) * p.Hq + h : 0;
+    const uint8_t* qc = p.q_codes + row * HALF + hh * (HALF / 2);
+    const uint8_t* qs = p.q_scales + row * (D / 16) + hh * (HALF / 16);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (wave_active) qf[ks] = *reinterpret_cast<const f16x8*>(src + 8 * ks);
-      else qf[ks] = f16x8{};
+      const uint32_t cw = live ? *reinterpret_cast<const uint32_t*>(qc + 4 * ks) : 0u;
+      const float sv = e4m3_decode(live ? qs[ks >> 1] : 0u);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qf[ks][j] = (_Float16)(e2m1_decode((cw >> (4 * j)) & 0xFu) * sv);
     }
     // make the Q loads complete here, so no vector-memory wait is left for the
     // pipeline below (it would also wait for the in-flight LDS copies)
@@ -626,18 +610,17 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-hipError_t launch_expand(bool is_q, const uint8_t* codes, const uint8_t* scales, int H, int B, int N, int max_len,
-                         const int32_t* cu, int64_t n_pad, int64_t cols, int D, int pf, _Float16* out, hipStream_t st) {
-  dim3 grid((unsigned)((max_len + 127) / 128), (unsigned)H, (unsigned)B);
-  if (grid.x == 0) return hipSuccess;
-#define EX(Q, DD, P) \
-  hipLaunchKernelGGL((expand_nvfp4_kernel<Q, DD, P>), grid, dim3(256), 0, st, codes, scales, H, N, cu, n_pad, cols, out)
-  if (is_q) {
-    if (D == 64) EX(true, 64, 0); else EX(true, 128, 0);
-  } else if (pf == PF_MXFP4) {
-    if (D == 64) EX(false, 64, 0); else EX(false, 128, 0);
+hipError_t launch_expand_k(const uint8_t* codes, const uint8_t* scales, int H, int B, int N, int max_len,
+                           const int32_t* cu, int64_t n_pad, int64_t cols, int D, int pf, _Float16* out,
+                           hipStream_t st) {
+  dim3 grid((unsigned)((max_len + KEY_TILE - 1) / KEY_TILE), (unsigned)H, (unsigned)B);
+  if (grid.x == 0 || B == 0) return hipSuccess;
+#define EX(DD, P) \
+  hipLaunchKernelGGL((expand_k_kernel<DD, P>), grid, dim3(256), 0, st, codes, scales, H, N, cu, n_pad, cols, out)
+  if (pf == PF_MXFP4) {
+    if (D == 64) EX(64, 0); else EX(128, 0);
   } else {
-    if (D == 64) EX(false, 64, 1); else EX(false, 128, 1);
+    if (D == 64) EX(64, 1); else EX(128, 1);
   }
 #undef EX
   return hipGetLastError();

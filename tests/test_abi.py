@@ -98,8 +98,8 @@ def _args(**kw):
 def test_fwd_validation(lib):
     a = _args()
     need = lib.attn_fwd_ws_bytes(ctypes.byref(a))
-    # Q fp16 tiles (4 heads x 256 rows x 128) + K tiles (2 heads x 256 x 128), 2 bytes each
-    assert need == 2 * 128 * (4 * 256 + 2 * 256) + 256
+    # K fp16 operand tiles (2 KV heads x 256 keys x 128), 2 bytes each; Q is decoded in the kernel
+    assert need == 2 * 128 * (2 * 256) + 256
     a.ws, a.ws_bytes = 1 << 24, need
     assert lib.attn_fwd_directp(ctypes.byref(_args(D=96, ws=1 << 24, ws_bytes=need)), None) == 1
     assert lib.attn_fwd_directp(ctypes.byref(_args(Hkv=3, ws=1 << 24, ws_bytes=need)), None) == 1
