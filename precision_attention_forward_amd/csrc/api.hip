@@ -29,7 +29,7 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
 using namespace attn;
 
 static thread_local int g_last_hip_error = 0;
-static const size_t QUANT_WS = 4096;   // >= 512 partial maxima
+static const size_t QUANT_WS = 8192;   // >= 2048 partial maxima
 
 static attn_status hip_status(hipError_t e) {
   if (e == hipSuccess) return ATTN_OK;

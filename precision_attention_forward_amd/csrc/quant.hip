@@ -6,13 +6,18 @@
 // are the NVFP4 and OCP MX conventions stated in include/attn_fp4.h, with
 // every step an IEEE float32 operation so the codes are reproducible bit for
 // bit.  All kernels are HBM-bound: each reads its bf16 input once for the
-// per-tensor amax and once for the encode.
+// per-tensor amax and once for the encode.  Element codes come from gfx950's
+// conversions (v_cvt_scalef32_pk_fp4_f32: round to nearest even, saturating,
+// sign kept; v_cvt_pk_fp8_f32: round to nearest even) applied to the same
+// float32 products fl(x * enc) the rules define; block scales use the
+// integer E4M3 encoder of common.h.
 #include "common.h"
 
 namespace attn {
 
 constexpr int AMAX_THREADS = 256;
-constexpr int AMAX_MAX_PARTIALS = 512;
+constexpr int AMAX_MAX_PARTIALS = 2048;
+constexpr int AMAX_UNROLL = 4;      // 16-byte loads in flight per thread
 
 // Pass 1: per-workgroup max |x| over a bf16 array of n elements (n % 8 == 0).
 __global__ void __launch_bounds__(AMAX_THREADS) amax_partials_kernel(const uint16_t* __restrict__ x, int64_t n,
@@ -20,8 +25,22 @@ __global__ void __launch_bounds__(AMAX_THREADS) amax_partials_kernel(const uint1
   float m = 0.0f;
   const int64_t n8 = n / 8;
   const u32x4* x8 = reinterpret_cast<const u32x4*>(x);
-  for (int64_t i = blockIdx.x * (int64_t)AMAX_THREADS + threadIdx.x; i < n8; i += (int64_t)gridDim.x * AMAX_THREADS) {
-    u32x4 v = __builtin_nontemporal_load(&x8[i]);
+  const int64_t stride = (int64_t)gridDim.x * AMAX_THREADS;
+  int64_t i = blockIdx.x * (int64_t)AMAX_THREADS + threadIdx.x;
+  for (; i + (AMAX_UNROLL - 1) * stride < n8; i += AMAX_UNROLL * stride) {
+    u32x4 v[AMAX_UNROLL];
+#pragma unroll
+    for (int u = 0; u < AMAX_UNROLL; ++u) v[u] = __builtin_nontemporal_load(&x8[i + u * stride]);
+#pragma unroll
+    for (int u = 0; u < AMAX_UNROLL; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        m = __builtin_fmaxf(m, __builtin_fabsf(bf16_bits_to_f32(v[u][j] & 0xFFFFu)));
+        m = __builtin_fmaxf(m, __builtin_fabsf(bf16_bits_to_f32(v[u][j] >> 16)));
+      }
+  }
+  for (; i < n8; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(&x8[i]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       m = __builtin_fmaxf(m, __builtin_fabsf(bf16_bits_to_f32(v[j] & 0xFFFFu)));
@@ -89,10 +108,17 @@ __global__ void __launch_bounds__(256) quant_nvfp4_kernel(const uint16_t* __rest
     u32x2 out = {0u, 0u};
     if (sv > 0.0f) {
       const float enc = s_enc / sv;
+      float y[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        uint32_t c = e2m1_encode(v[j] * enc);
-        out[j >> 3] |= c << (4 * (j & 7));
+      for (int j = 0; j < 16; ++j) y[j] = v[j] * enc;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        uint32_t w = 0u;   // element 2k in the low nibble of byte k
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[8 * h2 + 0], y[8 * h2 + 1], 1.0f, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[8 * h2 + 2], y[8 * h2 + 3], 1.0f, 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[8 * h2 + 4], y[8 * h2 + 5], 1.0f, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[8 * h2 + 6], y[8 * h2 + 7], 1.0f, 3);
+        out[h2] = w;
       }
     }
     *reinterpret_cast<u32x2*>(codes + 8 * i) = out;
@@ -132,22 +158,16 @@ __global__ void __launch_bounds__(256) quant_v_kernel(const uint16_t* __restrict
   }
   __syncthreads();
   const int64_t col0 = kcol_offset(varlen, s, tok0, nk_pad) + (int64_t)tile * KEY_TILE;
+  // one thread per (channel d, 32-key block); consecutive lanes take
+  // consecutive channels, so each LDS read of a wave covers 128 contiguous bytes
   for (int p = threadIdx.x; p < D * 4; p += 256) {
-    const int d = p >> 2, blk = p & 3;
+    const int d = p % D, blk = p / D;
     float x[32];
 #pragma unroll
     for (int j = 0; j < 32; ++j) x[j] = bf16_bits_to_f32(tileb[(blk * 32 + j) * D + d]);
     const int64_t row = (int64_t)h * D + d;
-    if (FMT == 0) {
-      u32x4 o0 = {0u, 0u, 0u, 0u}, o1 = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int j = 0; j < 16; ++j) o0[j >> 2] |= e4m3_encode(x[j] * enc) << (8 * (j & 3));
-#pragma unroll
-      for (int j = 0; j < 16; ++j) o1[j >> 2] |= e4m3_encode(x[16 + j] * enc) << (8 * (j & 3));
-      u32x4* dst = reinterpret_cast<u32x4*>(codes + row * cols + col0 + blk * 32);
-      dst[0] = o0;
-      dst[1] = o1;
-    } else {
+    float mul = enc;
+    if (FMT == 1) {
       float amax = 0.0f;
 #pragma unroll
       for (int j = 0; j < 32; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[j]));
@@ -155,19 +175,40 @@ __global__ void __launch_bounds__(256) quant_v_kernel(const uint16_t* __restrict
       const int E = (int)(ab >> 23) - 127;              // floor(log2 amax) for normal amax
       int e = (ab >> 23) == 0 ? -127 : E - 2;           // zero/subnormal block max -> -127
       e = e < -127 ? -127 : e;
-      const float inv = __builtin_amdgcn_ldexpf(1.0f, -e);
-      u32x4 o = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int j = 0; j < 32; ++j) o[j >> 3] |= e2m1_encode(x[j] * inv) << (4 * (j & 7));
-      *reinterpret_cast<u32x4*>(codes + (row * cols + col0 + blk * 32) / 2) = o;
+      mul = __builtin_amdgcn_ldexpf(1.0f, -e);          // exact: x * 2^-e
       scales[row * (cols / 32) + (col0 + blk * 32) / 32] = (uint8_t)(e + 127);
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) x[j] *= mul;
+    if (FMT == 0) {
+      u32x4 o[2];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {   // value 4k + i in byte i of word k
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * k], x[4 * k + 1], 0, false);
+        o[k >> 2][k & 3] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x[4 * k + 2], x[4 * k + 3], lo, true);
+      }
+      u32x4* dst = reinterpret_cast<u32x4*>(codes + row * cols + col0 + blk * 32);
+      dst[0] = o[0];
+      dst[1] = o[1];
+    } else {
+      u32x4 o;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {   // value 8k + 2i (+1) in byte i of word k, low nibble first
+        uint32_t w = 0u;
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[8 * k + 0], x[8 * k + 1], 1.0f, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[8 * k + 2], x[8 * k + 3], 1.0f, 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[8 * k + 4], x[8 * k + 5], 1.0f, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[8 * k + 6], x[8 * k + 7], 1.0f, 3);
+        o[k] = w;
+      }
+      *reinterpret_cast<u32x4*>(codes + (row * cols + col0 + blk * 32) / 2) = o;
     }
   }
 }
 
 // ---- host launchers (called from api.cpp) ----
 hipError_t launch_amax(const void* x, int64_t n, float* partials, int* np_out, hipStream_t st) {
-  int64_t want = (n / 8 + AMAX_THREADS * 8 - 1) / (AMAX_THREADS * 8);
+  int64_t want = (n / 8 + AMAX_THREADS * 16 - 1) / (AMAX_THREADS * 16);
   int np = (int)(want < 1 ? 1 : (want > AMAX_MAX_PARTIALS ? AMAX_MAX_PARTIALS : want));
   *np_out = np;
   hipLaunchKernelGGL(amax_partials_kernel, dim3(np), dim3(AMAX_THREADS), 0, st, (const uint16_t*)x, n, partials);
@@ -178,7 +219,7 @@ hipError_t launch_quant_nvfp4(const void* x, int64_t rows, int D, const float* p
                               uint8_t* scales, float* tensor_scale, hipStream_t st) {
   int64_t nblocks = rows * (D / 16);
   int64_t want = (nblocks + 255) / 256;
-  int grid = (int)(want < 1 ? 1 : (want > 8192 ? 8192 : want));
+  int grid = (int)(want < 1 ? 1 : (want > 4096 ? 4096 : want));
   hipLaunchKernelGGL(quant_nvfp4_kernel, dim3(grid), dim3(256), 0, st, (const uint16_t*)x, nblocks, partials, np, codes,
                      scales, tensor_scale);
   return hipGetLastError();
