@@ -21,10 +21,12 @@ Modules:
   formats    -- E2M1, E4M3 (fn) and E8M0 codecs
   quant      -- NVFP4 (Q, K), FP8 E4M3 per-tensor and MXFP4 (V) quantizers
   attention  -- Direct-P and FP8-P/V tiled forward, exact softmax attention
+  loglin     -- exp-free log-linear probability casts (E4M3, E2M1) of the
+                related methods listed beside the arXiv entry
 
 Parity status: every function is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_*.py`` (closed forms, exhaustive codec checks against
 torch's float8 dtypes, invariants, and an exact-attention special case).
 """
 
-from . import formats, quant, attention  # noqa: F401
+from . import formats, quant, attention, loglin  # noqa: F401

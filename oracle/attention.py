@@ -15,6 +15,10 @@ taken for each:
   e = max(floor(xmax) - 2, -127) with xmax the block max of t - m'; a block
   with no live key gets e = -127 and zero codes.
 * FP8 P uses a unit scale: code = E4M3(2**(t - m')).
+* ``encoder="loglin"`` swaps the element map for the exp-free log-linear
+  cast of the related pages (VC-Attention for E4M3, EFQ-Softmax for block
+  E2M1; see ``oracle.loglin``): same running max, same block exponent e,
+  code = loglin(t - m' - e) instead of RNE(2**(t - m' - e)).
 * Masked (causal: key > query; or past the end) keys contribute nothing.
 * LSE is the natural log built from the quantized denominator:
   LSE = ln2 * (m + log2 l).  A row with no live key gives O = 0, LSE = -inf.
@@ -30,6 +34,7 @@ import math
 import numpy as np
 
 from .formats import e2m1_encode, e2m1_decode, e4m3_encode, e4m3_decode
+from .loglin import loglin_encode
 
 TILE = 128
 PBLOCK = 32
@@ -38,7 +43,7 @@ LN2 = math.log(2.0)
 
 
 def attn_lowp_head(q_raw, k_raw, gq, gk, v_hat, sigma, p_format="mxfp4",
-                   causal=False, q_index=None, return_p=False):
+                   causal=False, q_index=None, return_p=False, encoder="exact"):
     """One (batch, head): tiled Direct-P (``p_format="mxfp4"``) or FP8-P
     (``p_format="fp8"``) forward.
 
@@ -49,10 +54,13 @@ def attn_lowp_head(q_raw, k_raw, gq, gk, v_hat, sigma, p_format="mxfp4",
     sigma                   softmax scale
     q_index int [nq]        absolute query positions (for the causal mask);
                             defaults to 0..nq-1
+    encoder                 "exact" (RNE of 2**y) or "loglin" (exp-free cast)
     Returns (O [nq, Dv], LSE [nq]) and, with ``return_p``, the probability
     codes [nq, Nk] (uint8, 0 where masked) and, for MXFP4, the E8M0 bytes
     [nq, ceil(Nk/32)].
     """
+    if encoder not in ("exact", "loglin"):
+        raise ValueError(encoder)
     q_raw = np.asarray(q_raw, np.float64)
     k_raw = np.asarray(k_raw, np.float64)
     v_hat = np.asarray(v_hat, np.float64)
@@ -91,13 +99,16 @@ def attn_lowp_head(q_raw, k_raw, gq, gk, v_hat, sigma, p_format="mxfp4",
                 xmax = xb.max(axis=1)
                 has = lb.any(axis=1)
                 e = np.where(has, np.maximum(np.floor(np.where(has, xmax, 0.0)) - 2, -127), -127)
-                codes = e2m1_encode(np.exp2(xb - e[:, None]))
+                if encoder == "exact":
+                    codes = e2m1_encode(np.exp2(xb - e[:, None]))
+                else:
+                    codes = loglin_encode(xb - e[:, None], "e2m1")
                 codes = np.where(lb, codes, 0).astype(np.uint8)
                 p_hat[:, b0:b1] = e2m1_decode(codes) * np.exp2(e)[:, None]
                 if return_p:
                     p_e8m0[:, (t0 + b0) // PBLOCK] = (e + 127).astype(np.uint8)
             elif p_format == "fp8":
-                codes = e4m3_encode(np.exp2(xb))
+                codes = e4m3_encode(np.exp2(xb)) if encoder == "exact" else loglin_encode(xb, "e4m3")
                 codes = np.where(lb, codes, 0).astype(np.uint8)
                 p_hat[:, b0:b1] = e4m3_decode(codes)
             else:
