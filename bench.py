@@ -31,6 +31,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=2, help="1..5 (default 2: Wan2.1-14B shape)")
+    ap.add_argument("--encoder", choices=("exact", "loglin"), default="exact",
+                    help="probability encoder: exact (RNE of 2^y) or the exp-free log-linear cast")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=16384, help="query rows of the oracle sample")
@@ -82,7 +84,7 @@ def copy_calibration(mib):
                       "launches": 3}), flush=True)
 
 
-def cpu_baseline(inp, rows):
+def cpu_baseline(inp, rows, encoder="exact"):
     """Time the CPU oracle (as it stands) on a bounded sample: one (batch,
     head), `rows` query rows against all keys, including the sample's
     quantization.  Returns a dict for the JSON line."""
@@ -116,13 +118,50 @@ def cpu_baseline(inp, rows):
         vcodes, ve = OQ.quant_v_mxfp4(vf[:, None, :])
         vhat = OQ.dequant_v_mxfp4(vcodes, ve)[:, 0, :]
     OA.attn_lowp_head(OQ.dequant_nvfp4_raw(qc, qs), OQ.dequant_nvfp4_raw(kc, ks), gq, gk, vhat, inp.sigma,
-                      wl.p_format, wl.causal, q_index=idx)
+                      wl.p_format, wl.causal, q_index=idx, encoder=encoder)
     dt = time.perf_counter() - t
     live = sum(min(int(i) + 1, Nk) for i in idx) if wl.causal else R * Nk
     flops = 4.0 * live * wl.D
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
             "sample": f"1 head, {R} query rows x {Nk} keys of workload {wl.name} (NVFP4/V quantization of the "
                       f"sample included), {dt:.1f} s; numpy float64, BLAS threads = cores"}
+
+
+def accuracy_sample(inp, o, lse, rows=64):
+    """Error of the low-precision forward against softmax attention computed
+    in float64 on the unquantized (bf16) inputs, for `rows` evenly spaced
+    query rows of head 0 of the first batch entry (the longest sequence of a
+    packed batch), all keys.  Not the parity check (that compares with the
+    oracle); this measures what the quantized path costs in accuracy."""
+    import numpy as np
+    wl = inp.wl
+    if inp.cu_seqlens is None:
+        t0, L = 0, wl.N
+        qh, kh, vh = inp.q[0, :, 0], inp.k[0, :, 0], inp.v[0, :, 0]
+        og, lg = o[0, :, 0], lse[0, 0]
+    else:
+        s = int(np.argmax(inp.seqlens))
+        t0, L = int(inp.cu_seqlens[s]), int(inp.seqlens[s])
+        qh, kh, vh = inp.q[t0:t0 + L, 0], inp.k[t0:t0 + L, 0], inp.v[t0:t0 + L, 0]
+        og, lg = o[t0:t0 + L, 0], lse[0, t0:t0 + L]
+    idx = np.linspace(0, L - 1, min(rows, L)).astype(np.int64)
+    q = qh.float().cpu().numpy().astype(np.float64)[idx]
+    k = kh.float().cpu().numpy().astype(np.float64)
+    v = vh.float().cpu().numpy().astype(np.float64)
+    sc = inp.sigma * (q @ k.T)
+    if wl.causal:
+        sc = np.where(np.arange(L)[None, :] <= idx[:, None], sc, -np.inf)
+    mx = sc.max(axis=1, keepdims=True)
+    p = np.exp(sc - mx)
+    den = p.sum(axis=1, keepdims=True)
+    o_ref = (p @ v) / den
+    lse_ref = (mx + np.log(den))[:, 0]
+    got = og.float().cpu().numpy()[idx].astype(np.float64)
+    lse_got = lg.float().cpu().numpy()[idx].astype(np.float64)
+    return {"o_rel_l2_vs_softmax": float(np.linalg.norm(got - o_ref) / np.linalg.norm(o_ref)),
+            "lse_max_abs_vs_softmax": float(np.abs(lse_got - lse_ref).max()),
+            "sample": f"{len(idx)} evenly spaced query rows of head 0, all {L} keys; float64 softmax attention "
+                      "on the bf16 inputs"}
 
 
 class HipEvents:
@@ -174,7 +213,9 @@ def main():
     inp = synth.generate(wl, dev)
     varlen = inp.cu_seqlens is not None
     vfmt = paf.V_FP8 if wl.v_format == "fp8" else paf.V_MXFP4
-    fwd = paf.fwd_directp if wl.p_format == "mxfp4" else paf.fwd_fp8pv
+    fwd = {("mxfp4", "exact"): paf.fwd_directp, ("fp8", "exact"): paf.fwd_fp8pv,
+           ("mxfp4", "loglin"): paf.fwd_directp_efq, ("fp8", "loglin"): paf.fwd_fp8pv_cast}[(wl.p_format,
+                                                                                          args.encoder)]
     kw = dict(Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D, softmax_scale=inp.sigma, causal=wl.causal, out_dtype=torch.bfloat16)
     if varlen:
         cu = inp.cu_seqlens.to(dev)
@@ -224,6 +265,8 @@ def main():
     kern_ms = kev.mean_ms()
     fwd_tflops = flops / (fwd_ms * 1e-3) / 1e12
     kern_tflops = flops / (kern_ms * 1e-3) / 1e12
+    o_out, lse_out, _ = fwd(*qkv, workspace=ws, **kw)
+    acc = accuracy_sample(inp, o_out, lse_out)
 
     # the in-library BF16 forward on the same bf16 inputs (dense layouts only)
     bf16 = None
@@ -248,18 +291,21 @@ def main():
     qk_rate, pv_rate = BF16_PEAK_TFLOPS, (pv_peak if wl.p_format == "mxfp4" else FP8_PEAK_TFLOPS)
     ceiling = 1.0 / (0.5 / qk_rate + 0.5 / pv_rate)
     roofline = {"bound": "mfma", "achieved": round(kern_tflops, 2), "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(kern_tflops / MXFP4_PEAK_TFLOPS, 4), "traffic": measured_traffic(args.workload),
+                "frac": round(kern_tflops / MXFP4_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(args.workload) if args.encoder == "exact" else None,
                 "kernel": "fwd_lowp_kernel", "kernel_ms": round(kern_ms, 4),
                 "mixed_ceiling_tflops": round(ceiling, 1), "frac_of_mixed_ceiling": round(kern_tflops / ceiling, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, args.cpu_rows)
+        cpu = cpu_baseline(inp, args.cpu_rows, args.encoder)
 
     cfg = {"workload": f"{wl.name}: " + (f"{wl.varlen[0]} packed sequences" if varlen else
                                          f"B={wl.B} N={wl.N}") +
            f" Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D} {'causal' if wl.causal else 'noncausal'}, "
-           f"P={wl.p_format.upper()} V={wl.v_format.upper()}",
+           f"P={wl.p_format.upper()} V={wl.v_format.upper()}" +
+           ("" if args.encoder == "exact" else ", exp-free log-linear P encoder"),
+           "encoder": args.encoder,
            "B": wl.B if not varlen else int(len(inp.seqlens)), "Hq": wl.Hq, "Hkv": wl.Hkv,
            "N": wl.N if not varlen else int(inp.seqlens.max()), "D": wl.D, "causal": wl.causal,
            "flops_per_step": flops, "parallelism": "single GPU"}
@@ -279,8 +325,10 @@ def main():
         "bf16_tflops": None if bf16 is None else round(bf16["tflops"], 2),
         "precision": "NVFP4 Q/K (exact, contracted on the FP16 MFMA), " +
                      ("MXFP4 E2M1 P (Direct-P)" if wl.p_format == "mxfp4" else "FP8 E4M3 P") +
+                     ("" if args.encoder == "exact" else " by the exp-free log-linear cast") +
                      f", {wl.v_format.upper()} V, FP32 accumulation",
         "roofline": roofline,
+        "accuracy": acc,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }

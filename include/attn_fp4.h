@@ -209,6 +209,32 @@ attn_status attn_fwd_directp(const attn_fwd_args* a, void* stream);
 attn_status attn_fwd_fp8pv(const attn_fwd_args* a, void* stream);
 
 /*
+ * Exp-free variants.  Two related methods listed beside the arXiv entry of
+ * the pages' paper (2609.04105v1, "Related papers") map log2-domain scores
+ * to probability codes without an exponential: "VC-Attention: Value
+ * Smoothing and Softmax Casting for Low-bit Attention" (E4M3 codes from one
+ * fused multiply-add) and "EFQ-Softmax: Exp-Free Quantization for Softmax"
+ * (block-scaled E2M1).  Only their abstracts are available; the reading
+ * implemented is the log-linear cast: a minifloat code read as an integer is
+ * a fixed-point log2 of its value, so with y the log2 of the probability the
+ * code is clamp(RNE(2^M (y + b)), 0, top) -- M mantissa bits and exponent
+ * bias b of the code format, top its largest finite code.  The decoded value
+ * is Mitchell's piecewise-linear 2^y (to M fraction bits) in the normal range.
+ * Running max, block exponents, denominator (from the same decoded codes),
+ * P.V, O and LSE are those of the exact entry points; only the element map
+ * changes, so the results are approximations of the exact ones, not equal to
+ * them.  Arguments, workspace, errors and the debug dump are as for the exact
+ * entry point named.
+ *
+ * attn_fwd_directp_efq: as attn_fwd_directp, code = min(RNE(2 (t - m' - e) + 2), 7)
+ *                       (E2M1: M = 1, b = 1), same E8M0 exponent e per 32 keys.
+ * attn_fwd_fp8pv_cast:  as attn_fwd_fp8pv, code = max(RNE(8 (t - m') + 56), 0)
+ *                       (E4M3: M = 3, b = 7), unit scale.  Causal or not.
+ */
+attn_status attn_fwd_directp_efq(const attn_fwd_args* a, void* stream);
+attn_status attn_fwd_fp8pv_cast(const attn_fwd_args* a, void* stream);
+
+/*
  * BF16 fused attention forward, the baseline the pages compare against
  * (BF16 FlashAttention-4 on the summary page, "Key results"): O =
  * softmax(sigma Q K^T) V with bf16 operands, float32 accumulation and

@@ -34,7 +34,7 @@ import math
 import numpy as np
 
 from .formats import e2m1_encode, e2m1_decode, e4m3_encode, e4m3_decode
-from .loglin import loglin_encode
+from .loglin import loglin_encode, loglin_position
 
 TILE = 128
 PBLOCK = 32
@@ -43,7 +43,8 @@ LN2 = math.log(2.0)
 
 
 def attn_lowp_head(q_raw, k_raw, gq, gk, v_hat, sigma, p_format="mxfp4",
-                   causal=False, q_index=None, return_p=False, encoder="exact"):
+                   causal=False, q_index=None, return_p=False, encoder="exact",
+                   p_given=None, return_pre=False):
     """One (batch, head): tiled Direct-P (``p_format="mxfp4"``) or FP8-P
     (``p_format="fp8"``) forward.
 
@@ -58,6 +59,16 @@ def attn_lowp_head(q_raw, k_raw, gq, gk, v_hat, sigma, p_format="mxfp4",
     Returns (O [nq, Dv], LSE [nq]) and, with ``return_p``, the probability
     codes [nq, Nk] (uint8, 0 where masked) and, for MXFP4, the E8M0 bytes
     [nq, ceil(Nk/32)].
+
+    Two hooks for checking an implementation whose float32 arithmetic may
+    round a value that lies on a code boundary the other way:
+    p_given     (codes [nq, Nk], E8M0 bytes [nq, ceil(Nk/32)] or None): use
+                these codes (and, for MXFP4, block exponents of blocks with a
+                live key) instead of rounding; every other step is unchanged
+    return_pre  also return the value each code rounds, [nq, Nk] (2**y for
+                the exact encoders, the position 2**M (y + b) for the cast,
+                -inf where masked), and the block maxima xmax of t - m',
+                [nq, ceil(Nk/32)] (-inf for blocks with no live key)
     """
     if encoder not in ("exact", "loglin"):
         raise ValueError(encoder)
@@ -74,8 +85,11 @@ def attn_lowp_head(q_raw, k_raw, gq, gk, v_hat, sigma, p_format="mxfp4",
     l = np.zeros(nq)
     o = np.zeros((nq, v_hat.shape[1]))
     nblk = (Nk + PBLOCK - 1) // PBLOCK
+    return_p = return_p or return_pre
     p_codes = np.zeros((nq, Nk), np.uint8) if return_p else None
     p_e8m0 = np.zeros((nq, nblk), np.uint8) if (return_p and p_format == "mxfp4") else None
+    pre_all = np.full((nq, Nk), -np.inf) if return_pre else None
+    xmax_all = np.full((nq, nblk), -np.inf) if return_pre else None
     for t0 in range(0, Nk, TILE):
         t1 = min(t0 + TILE, Nk)
         keys = np.arange(t0, t1)
@@ -95,32 +109,52 @@ def attn_lowp_head(q_raw, k_raw, gq, gk, v_hat, sigma, p_format="mxfp4",
             b1 = min(b0 + PBLOCK, t1 - t0)
             xb = x[:, b0:b1]
             lb = live[:, b0:b1]
+            blk = (t0 + b0) // PBLOCK
+            xmax = xb.max(axis=1)
+            if return_pre:
+                xmax_all[:, blk] = xmax
             if p_format == "mxfp4":
-                xmax = xb.max(axis=1)
                 has = lb.any(axis=1)
                 e = np.where(has, np.maximum(np.floor(np.where(has, xmax, 0.0)) - 2, -127), -127)
+                if p_given is not None:
+                    e = np.where(has, p_given[1][:, blk].astype(np.int64) - 127, e)
                 if encoder == "exact":
-                    codes = e2m1_encode(np.exp2(xb - e[:, None]))
+                    pre = np.exp2(xb - e[:, None])
+                    codes = e2m1_encode(pre)
                 else:
+                    pre = loglin_position(xb - e[:, None], "e2m1")
                     codes = loglin_encode(xb - e[:, None], "e2m1")
+                if p_given is not None:
+                    codes = p_given[0][:, t0 + b0:t0 + b1]
                 codes = np.where(lb, codes, 0).astype(np.uint8)
                 p_hat[:, b0:b1] = e2m1_decode(codes) * np.exp2(e)[:, None]
                 if return_p:
-                    p_e8m0[:, (t0 + b0) // PBLOCK] = (e + 127).astype(np.uint8)
+                    p_e8m0[:, blk] = (e + 127).astype(np.uint8)
             elif p_format == "fp8":
-                codes = e4m3_encode(np.exp2(xb)) if encoder == "exact" else loglin_encode(xb, "e4m3")
+                if encoder == "exact":
+                    pre = np.exp2(xb)
+                    codes = e4m3_encode(pre)
+                else:
+                    pre = loglin_position(xb, "e4m3")
+                    codes = loglin_encode(xb, "e4m3")
+                if p_given is not None:
+                    codes = p_given[0][:, t0 + b0:t0 + b1]
                 codes = np.where(lb, codes, 0).astype(np.uint8)
                 p_hat[:, b0:b1] = e4m3_decode(codes)
             else:
                 raise ValueError(p_format)
             if return_p:
                 p_codes[:, t0 + b0:t0 + b1] = codes
+            if return_pre:
+                pre_all[:, t0 + b0:t0 + b1] = np.where(lb, pre, -np.inf)
         l = alpha * l + p_hat.sum(axis=1)
         o = alpha[:, None] * o + p_hat @ v_hat[t0:t1]
         m = m_new
     with np.errstate(divide="ignore", invalid="ignore"):
         O = np.where(l[:, None] > 0, o / np.where(l > 0, l, 1.0)[:, None], 0.0)
         lse = np.where(l > 0, LN2 * (m + np.log2(np.where(l > 0, l, 1.0))), -np.inf)
+    if return_pre:
+        return O, lse, p_codes, p_e8m0, pre_all, xmax_all
     if return_p:
         return O, lse, p_codes, p_e8m0
     return O, lse

@@ -38,11 +38,22 @@ LOGLIN_FORMATS = {
 }
 
 
+def loglin_position(y, fmt):
+    """The unrounded code position 2**M * (y + b) of log2-domain values ``y``
+    (float64; -inf stays -inf)."""
+    mbits, bias, _ = LOGLIN_FORMATS[fmt]
+    return np.ldexp(np.asarray(y, dtype=np.float64) + bias, mbits)
+
+
+def loglin_round(z, fmt):
+    """Code of an unrounded position z: clamp(RNE(z), 0, top); -inf -> 0."""
+    top = LOGLIN_FORMATS[fmt][2]
+    z = np.asarray(z, dtype=np.float64)
+    z = np.where(np.isfinite(z), z, -1.0)      # -inf (masked key) -> code 0
+    return np.clip(np.rint(z), 0, top).astype(np.uint8)
+
+
 def loglin_encode(y, fmt):
     """Log-linear cast of log2-domain values ``y`` (float64, -inf allowed) to
     unsigned minifloat codes (uint8): clamp(RNE(2**M * (y + b)), 0, top)."""
-    mbits, bias, top = LOGLIN_FORMATS[fmt]
-    y = np.asarray(y, dtype=np.float64)
-    z = np.ldexp(y + bias, mbits)
-    z = np.where(np.isfinite(z), z, -1.0)      # -inf (masked key) -> code 0
-    return np.clip(np.rint(z), 0, top).astype(np.uint8)
+    return loglin_round(loglin_position(y, fmt), fmt)

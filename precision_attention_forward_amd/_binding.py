@@ -67,6 +67,8 @@ EXPORTS = {
     "attn_fwd_ws_bytes": (ctypes.c_size_t, [ctypes.POINTER(FwdArgs)]),
     "attn_fwd_directp": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "attn_fwd_fp8pv": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
+    "attn_fwd_directp_efq": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
+    "attn_fwd_fp8pv_cast": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "attn_fwd_bf16": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
@@ -210,7 +212,7 @@ def make_fwd_args(q, k, v, *, B, Hq, Hkv, Nq, Nk, D, softmax_scale, causal=False
 def _fwd_lowp(entry, q, k, v, *, Hq, Hkv, D, softmax_scale, causal=False, B=None, Nq=None, Nk=None,
               cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
               out_dtype=torch.float32, want_lse=True, workspace=None, debug=None, events=None, out=None):
-    """Shared driver of attn_fwd_directp / attn_fwd_fp8pv.  Returns (O, LSE, dbg)."""
+    """Shared driver of the low-precision forward entry points.  Returns (O, LSE, dbg)."""
     lib = load_library()
     dev = q[0].device
     varlen = cu_seqlens_q is not None
@@ -236,7 +238,7 @@ def _fwd_lowp(entry, q, k, v, *, Hq, Hkv, D, softmax_scale, causal=False, B=None
         dbg_b, dbg_h = debug
         nq_dbg = Nq
         nk_pad = (Nk + 127) // 128 * 128
-        if entry == "attn_fwd_directp":
+        if entry in ("attn_fwd_directp", "attn_fwd_directp_efq"):
             dbg_codes = torch.zeros((nq_dbg, nk_pad // 2), dtype=torch.uint8, device=dev)
             dbg_scales = torch.zeros((nq_dbg, nk_pad // 32), dtype=torch.uint8, device=dev)
         else:
@@ -263,6 +265,16 @@ def fwd_directp(q, k, v, **kw):
 def fwd_fp8pv(q, k, v, **kw):
     """FP8-P/V forward (causal allowed)."""
     return _fwd_lowp("attn_fwd_fp8pv", q, k, v, **kw)
+
+
+def fwd_directp_efq(q, k, v, **kw):
+    """Exp-free Direct-P: E2M1 codes by the log-linear cast (noncausal)."""
+    return _fwd_lowp("attn_fwd_directp_efq", q, k, v, **kw)
+
+
+def fwd_fp8pv_cast(q, k, v, **kw):
+    """Exp-free FP8-P/V: E4M3 codes by the one-FMA log-linear cast (causal allowed)."""
+    return _fwd_lowp("attn_fwd_fp8pv_cast", q, k, v, **kw)
 
 
 def fwd_bf16(q, k, v, softmax_scale, causal=False, want_lse=True):

@@ -19,7 +19,8 @@ hipError_t launch_expand_k(const uint8_t* codes, const uint8_t* scales, int H, i
                            const int32_t* cu, int64_t n_pad, int64_t cols, int D, int pf, _Float16* out,
                            hipStream_t st);
 struct FwdParams;
-hipError_t launch_fwd_lowp(const FwdParams& p, int D, int pf, int vf, bool causal, bool debug, hipStream_t st);
+hipError_t launch_fwd_lowp(const FwdParams& p, int D, int pf, int vf, bool causal, bool debug, int enc,
+                           hipStream_t st);
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                            int Nq, int Nk, int D, float sigma, bool causal, hipStream_t st);
 }  // namespace attn
@@ -158,7 +159,7 @@ static attn_status validate_fwd(const attn_fwd_args* a, bool allow_causal, int p
   return ATTN_OK;
 }
 
-static attn_status run_fwd_lowp(const attn_fwd_args* a, void* stream, int pf) {
+static attn_status run_fwd_lowp(const attn_fwd_args* a, void* stream, int pf, int enc) {
   attn_status s = validate_fwd(a, pf == 1, pf);
   if (s != ATTN_OK) return s;
   hipStream_t st = (hipStream_t)stream;
@@ -204,14 +205,16 @@ static attn_status run_fwd_lowp(const attn_fwd_args* a, void* stream, int pf) {
     if (e != hipSuccess) return hip_status(e);
   }
   e = launch_fwd_lowp(p, a->D, pf, a->v.format == ATTN_V_MXFP4 ? 1 : 0, a->causal != 0, a->dbg_p_codes != nullptr,
-                      st);
+                      enc, st);
   if (e != hipSuccess) return hip_status(e);
   if (a->prof_event_end != nullptr) e = hipEventRecord((hipEvent_t)a->prof_event_end, st);
   return hip_status(e);
 }
 
-attn_status attn_fwd_directp(const attn_fwd_args* a, void* stream) { return run_fwd_lowp(a, stream, 0); }
-attn_status attn_fwd_fp8pv(const attn_fwd_args* a, void* stream) { return run_fwd_lowp(a, stream, 1); }
+attn_status attn_fwd_directp(const attn_fwd_args* a, void* stream) { return run_fwd_lowp(a, stream, 0, 0); }
+attn_status attn_fwd_fp8pv(const attn_fwd_args* a, void* stream) { return run_fwd_lowp(a, stream, 1, 0); }
+attn_status attn_fwd_directp_efq(const attn_fwd_args* a, void* stream) { return run_fwd_lowp(a, stream, 0, 1); }
+attn_status attn_fwd_fp8pv_cast(const attn_fwd_args* a, void* stream) { return run_fwd_lowp(a, stream, 1, 1); }
 
 attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Hq,
                           int32_t Hkv, int32_t Nq, int32_t Nk, int32_t D, float softmax_scale, int32_t causal,

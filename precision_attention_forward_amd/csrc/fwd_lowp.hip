@@ -8,12 +8,23 @@
 // the denominator is summed from the same rounded probabilities the P.V
 // product consumes; O = o / l and LSE = ln2 * (m + log2 l).
 //
+// Exp-free variants (ENC = 1), from two related methods listed beside the
+// arXiv entry ("VC-Attention: Value Smoothing and Softmax Casting for Low-bit
+// Attention" for E4M3, "EFQ-Softmax: Exp-Free Quantization for Softmax" for
+// block-scaled E2M1; abstracts only): a minifloat code read as an integer is
+// a fixed-point log2 of its value (M mantissa bits, exponent bias b), so the
+// code of 2^y is taken as clamp(RNE(2^M (y + b)), 0, top) -- one FMA of the
+// raw score with per-row constants, then v_cvt_pk_u8_f32 (round to nearest
+// even, clamped to [0, 255]) -- instead of exp2 and a format conversion.
+// Same running max, block exponents, denominator and P.V as ENC = 0.
+//
 // gfx950 mapping (the pages' Blackwell pipeline is prior art, not copied):
 //  * NVFP4 blocks carry an E4M3 scale per 16 elements; the scaled MFMA takes
 //    one E8M0 scale per 32, so Q.K^T is run as an FP16 MFMA on the exact
 //    dequantized values (E2M1 x E4M3 has at most 6 significant bits).  A
-//    pre-pass expands Q and K once into 32-query / 128-key FP16 tiles laid
-//    out in the order the MFMA operands are read.
+//    pre-pass expands K once into 128-key FP16 tiles laid out in the order
+//    the MFMA operand is read; Q is decoded into FP16 operand registers at
+//    the start of each workgroup.
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_f16 puts one query per lane; the key
 //    rows of K are permuted so that each lane ends up holding exactly the 32
 //    keys of one P block (MXFP4) or the 32 keys the FP8 operand layout wants.
@@ -124,7 +135,7 @@ struct LdsLayout {
 // P is double-buffered (P(t-2) is read while P(t-1) is written).  The
 // 8 waves share K(t) / V(t-2) tiles in LDS; tiles for iteration t+1 are
 // copied during iteration t and one barrier per iteration separates them.
-template <int D, int PF, int VF, bool CAUSAL, bool DEBUG>
+template <int D, int PF, int VF, bool CAUSAL, bool DEBUG, int ENC>
 __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   constexpr int KS = D / 16;           // k-steps of the S MFMA
   constexpr int DT = D / 32;           // 32-row tiles of O^T
@@ -183,6 +194,11 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   // ---- scalars: c = sigma * log2(e) * gq * gk
   const float cc = (float)((double)p.sigma * 1.4426950408889634 * (double)(*p.gq) * (double)(*p.gk));
   const float vscale = VF == VF_FP8 ? *p.sv : 1.0f;
+  // exp-free cast: 2^M, and 2^M * b, of the code format (E2M1: M = 1, b = 1;
+  // E4M3: M = 3, b = 7); ccl = 2^M c is exact
+  constexpr float CAST_MUL = PF == PF_MXFP4 ? 2.0f : 8.0f;
+  constexpr float CAST_BIAS = PF == PF_MXFP4 ? 2.0f : 56.0f;
+  const float ccl = cc * CAST_MUL;
 
   // ---- Q operand (B of S^T): lane holds query ql, d in [hh*D/2, hh*D/2 + D/2),
   // decoded here from the NVFP4 codes (E2M1 * E4M3 is exact in FP16); once per
@@ -275,7 +291,9 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   float bm[2] = {0.f, 0.f};            // block maxima of S(t-1) (raw scores)
   float bmp[2] = {0.f, 0.f};           // S(t-1): max of sub-tiles 0,1 / of sub-tile 2 (set a tile ahead)
   float bmn[2] = {0.f, 0.f};           // the same for S(t), built during iteration t
-  float me[2] = {0.f, 0.f};
+  float me[2] = {0.f, 0.f};            // exact encode: m' + e per block
+  float mb[2] = {0.f, 0.f};            // exp-free cast: 2^M (b - m' - e) per block
+  uint32_t cev = 0, cod = 0;           // exp-free E2M1: even / odd key codes, one byte each
   pw[0] = pw[1] = pr[0] = pr[1] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
 
   // constant 0/1 operand of the row-sum MFMA (16x16x128, FP4 1.0 = code 2)
@@ -447,6 +465,34 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
           psw[c] = 127;
           me[c] = row_dead ? 0.0f : m_new;
         }
+        if (ENC) mb[c] = CAST_BIAS - CAST_MUL * me[c];   // 2^M me is exact
+      }
+    } else if (u < 37 && ENC) {                  // exp-free cast of scores 2k, 2k+1 of sub-tile st
+      const int st = (u - 5) >> 3, k = (u - 5) & 7, c = st >> 1, s2 = st & 1, v = 2 * k;
+      const float y0 = __builtin_fmaf(s[st][v], ccl, mb[c]);       // -inf on masked keys -> code 0
+      const float y1 = __builtin_fmaf(s[st][v + 1], ccl, mb[c]);
+      if (PF == PF_MXFP4) {
+        // E2M1 codes of keys 16*s2 + v, v+1 go to the low / high nibble of
+        // byte k&3 of word 2*s2 + k/4; even and odd keys are gathered one
+        // byte each, then merged once per word
+        const float a0 = __builtin_fminf(y0, 7.0f), a1 = __builtin_fminf(y1, 7.0f);
+        const int byte = k & 3;
+        if (byte == 0) { cev = __builtin_amdgcn_cvt_pk_u8_f32(a0, 0, cev); cod = __builtin_amdgcn_cvt_pk_u8_f32(a1, 0, cod); }
+        else if (byte == 1) { cev = __builtin_amdgcn_cvt_pk_u8_f32(a0, 1, cev); cod = __builtin_amdgcn_cvt_pk_u8_f32(a1, 1, cod); }
+        else if (byte == 2) { cev = __builtin_amdgcn_cvt_pk_u8_f32(a0, 2, cev); cod = __builtin_amdgcn_cvt_pk_u8_f32(a1, 2, cod); }
+        else {
+          cev = __builtin_amdgcn_cvt_pk_u8_f32(a0, 3, cev);
+          cod = __builtin_amdgcn_cvt_pk_u8_f32(a1, 3, cod);
+          pw[c][2 * s2 + (k >> 2)] = (int)((cod << 4) | cev);
+        }
+      } else {
+        // E4M3 codes (at most 56 here: y <= 56 up to rounding) of keys v, v+1
+        // go to bytes 2(k&1), 2(k&1)+1 of word 4*s2 + k/2
+        const int word = 4 * s2 + (k >> 1);
+        uint32_t w = (uint32_t)pw[c][word];
+        if (k & 1) { w = __builtin_amdgcn_cvt_pk_u8_f32(y0, 2, w); w = __builtin_amdgcn_cvt_pk_u8_f32(y1, 3, w); }
+        else { w = __builtin_amdgcn_cvt_pk_u8_f32(y0, 0, w); w = __builtin_amdgcn_cvt_pk_u8_f32(y1, 1, w); }
+        pw[c][word] = (int)w;
       }
     } else if (u < 37) {                         // encode scores 2k, 2k+1 of sub-tile st
       const int st = (u - 5) >> 3, k = (u - 5) & 7, c = st >> 1, s2 = st & 1, v = 2 * k;
@@ -626,9 +672,9 @@ hipError_t launch_expand_k(const uint8_t* codes, const uint8_t* scales, int H, i
   return hipGetLastError();
 }
 
-template <int D, int PF, int VF, bool CAUSAL, bool DEBUG>
+template <int D, int PF, int VF, bool CAUSAL, bool DEBUG, int ENC>
 static hipError_t launch_fwd_t(const FwdParams& p, int nwg, hipStream_t st) {
-  auto kern = fwd_lowp_kernel<D, PF, VF, CAUSAL, DEBUG>;
+  auto kern = fwd_lowp_kernel<D, PF, VF, CAUSAL, DEBUG, ENC>;
   const int lds = LdsLayout<D, VF>::TOTAL;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
@@ -636,20 +682,35 @@ static hipError_t launch_fwd_t(const FwdParams& p, int nwg, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int D, int PF, int VF, bool CAUSAL>
+template <int D, int PF, int VF, bool CAUSAL, int ENC>
 static hipError_t launch_fwd_d(const FwdParams& p, int nwg, bool debug, hipStream_t st) {
-  return debug ? launch_fwd_t<D, PF, VF, CAUSAL, true>(p, nwg, st) : launch_fwd_t<D, PF, VF, CAUSAL, false>(p, nwg, st);
+  return debug ? launch_fwd_t<D, PF, VF, CAUSAL, true, ENC>(p, nwg, st)
+               : launch_fwd_t<D, PF, VF, CAUSAL, false, ENC>(p, nwg, st);
 }
 
-hipError_t launch_fwd_lowp(const FwdParams& p, int D, int pf, int vf, bool causal, bool debug, hipStream_t st) {
+template <int ENC>
+static hipError_t launch_fwd_e(const FwdParams& p, int nwg, int D, int pf, int vf, bool causal, bool debug,
+                               hipStream_t st) {
+  if (pf == PF_MXFP4) {
+    if (vf == VF_MXFP4)
+      return D == 64 ? launch_fwd_d<64, 0, 1, false, ENC>(p, nwg, debug, st)
+                     : launch_fwd_d<128, 0, 1, false, ENC>(p, nwg, debug, st);
+    return D == 64 ? launch_fwd_d<64, 0, 0, false, ENC>(p, nwg, debug, st)
+                   : launch_fwd_d<128, 0, 0, false, ENC>(p, nwg, debug, st);
+  }
+  if (causal)
+    return D == 64 ? launch_fwd_d<64, 1, 0, true, ENC>(p, nwg, debug, st)
+                   : launch_fwd_d<128, 1, 0, true, ENC>(p, nwg, debug, st);
+  return D == 64 ? launch_fwd_d<64, 1, 0, false, ENC>(p, nwg, debug, st)
+                 : launch_fwd_d<128, 1, 0, false, ENC>(p, nwg, debug, st);
+}
+
+hipError_t launch_fwd_lowp(const FwdParams& p, int D, int pf, int vf, bool causal, bool debug, int enc,
+                           hipStream_t st) {
   const int nwg = p.B * p.Hq * p.QB;
   if (nwg == 0) return hipSuccess;
-  if (pf == PF_MXFP4) {
-    if (vf == VF_MXFP4) return D == 64 ? launch_fwd_d<64, 0, 1, false>(p, nwg, debug, st) : launch_fwd_d<128, 0, 1, false>(p, nwg, debug, st);
-    return D == 64 ? launch_fwd_d<64, 0, 0, false>(p, nwg, debug, st) : launch_fwd_d<128, 0, 0, false>(p, nwg, debug, st);
-  }
-  if (causal) return D == 64 ? launch_fwd_d<64, 1, 0, true>(p, nwg, debug, st) : launch_fwd_d<128, 1, 0, true>(p, nwg, debug, st);
-  return D == 64 ? launch_fwd_d<64, 1, 0, false>(p, nwg, debug, st) : launch_fwd_d<128, 1, 0, false>(p, nwg, debug, st);
+  return enc ? launch_fwd_e<1>(p, nwg, D, pf, vf, causal, debug, st)
+             : launch_fwd_e<0>(p, nwg, D, pf, vf, causal, debug, st);
 }
 
 }  // namespace attn

@@ -9,12 +9,20 @@ import torch
 from oracle import attention as OA
 from oracle import formats as OF
 from oracle import quant as OQ
+from oracle import loglin as OL
 
 # Tolerances of the parity bar (float results); codes and scales are bit-exact.
 P_MISMATCH_MAX = 1e-4        # fraction of live probability codes
 O_REL_L2_MAX = 1e-3
 O_MAX_ABS = 5e-3
 LSE_REL_MAX = 1e-4           # |dLSE| <= 1e-4 * max(1, |LSE|)
+# Where float32 arithmetic decides a probability code, a value on a code
+# boundary may round either way.  A code that differs from the oracle's is
+# accepted only when it is the neighbouring code and the oracle's unrounded
+# value lies this close to the boundary between the two:
+NEAR_TIE_REL = 1e-4          # exact encoders: |2^y - midpoint| / midpoint
+NEAR_TIE_POS = 1e-3          # log-linear cast: |position - (c + 1/2)|, code units
+NEAR_INT = 1e-4              # E8M0 block exponent: |xmax - nearest integer|
 
 
 def f32(t):
@@ -44,14 +52,15 @@ def oracle_v_head(v_head_f32, v_format, amax_all=None):
 
 
 def oracle_head(q_rows, k_rows, v_rows, *, amax_q, amax_k, amax_v, sigma, p_format, v_format, causal,
-                q_index=None, return_p=False):
+                q_index=None, return_p=False, encoder="exact", p_given=None, return_pre=False):
     """Oracle forward for a set of query rows of one head, given the bf16
     inputs (as float32 numpy) and the whole-tensor amax values."""
     qc, qs, gq = OQ.quant_nvfp4(q_rows, amax=amax_q)
     kc, ks, gk = OQ.quant_nvfp4(k_rows, amax=amax_k)
     vh = oracle_v_head(v_rows, v_format, amax_v)
     return OA.attn_lowp_head(OQ.dequant_nvfp4_raw(qc, qs), OQ.dequant_nvfp4_raw(kc, ks), gq, gk, vh, sigma,
-                             p_format, causal, q_index=q_index, return_p=return_p)
+                             p_format, causal, q_index=q_index, return_p=return_p, encoder=encoder,
+                             p_given=p_given, return_pre=return_pre)
 
 
 def p_mismatch(gpu_codes, gpu_scales, ora_codes, ora_e8, p_format, nk, live):
@@ -77,3 +86,61 @@ def assert_close_outputs(o_gpu, lse_gpu, o_ref, lse_ref, what=""):
     assert ma <= O_MAX_ABS, f"{what}: O max abs {ma:.3e}"
     assert le <= LSE_REL_MAX, f"{what}: LSE rel {le:.3e}"
     return r, ma, le
+
+
+def gpu_codes(dump_codes, dump_scales, p_format, nk):
+    """Debug dump rows -> (codes [R, nk] in key order, E8M0 bytes [R, ceil(nk/32)] or None)."""
+    if p_format == "mxfp4":
+        return OF.unpack_nibbles(dump_codes)[:, :nk], dump_scales[:, :(nk + 31) // 32]
+    return dump_codes[:, :nk], None
+
+
+def check_code_choices(gc, ge, oc, oe, pre, xmax, p_format, encoder, live):
+    """Every probability code and E8M0 block exponent in which the kernel
+    differs from the oracle must be a rounding near-tie (the neighbouring
+    code, the oracle's unrounded value within NEAR_* of the boundary).
+    gc/ge: kernel codes and exponents; oc/oe/pre/xmax: the oracle's, from
+    return_pre.  Returns (differing exponents, differing element codes)."""
+    fmt = "e2m1" if p_format == "mxfp4" else "e4m3"
+    R, nk = gc.shape
+    pre = pre.copy()
+    n_e = 0
+    if p_format == "mxfp4":
+        nblk = (nk + 31) // 32
+        has = np.zeros((R, nblk), bool)
+        for b in range(nblk):
+            has[:, b] = live[:, 32 * b:32 * b + 32].any(axis=1)
+        de = (ge.astype(np.int64) != oe.astype(np.int64)) & has
+        n_e = int(de.sum())
+        if n_e:
+            bad = de & ~((np.abs(xmax - np.rint(xmax)) <= NEAR_INT)
+                         & (np.abs(ge.astype(np.int64) - oe.astype(np.int64)) == 1))
+            assert not bad.any(), f"E8M0 exponents differ away from a boundary at {np.argwhere(bad)[:5].tolist()}"
+        # the oracle's unrounded values under the kernel's exponents
+        shift = np.repeat(oe.astype(np.int64) - ge.astype(np.int64), 32, axis=1)[:, :nk]
+        fin = np.isfinite(pre)
+        if encoder == "exact":
+            pre[fin] = pre[fin] * np.exp2(shift[fin])
+        else:
+            pre[fin] = pre[fin] + 2.0 * shift[fin]
+        if encoder == "exact":
+            oc = np.where(live, OF.e2m1_encode(np.where(fin, pre, 0.0)), 0).astype(np.uint8)
+        else:
+            oc = np.where(live, OL.loglin_round(pre, fmt), 0).astype(np.uint8)
+    dm = (gc.astype(np.int64) != oc.astype(np.int64)) & live
+    n_c = int(dm.sum())
+    if n_c:
+        g, o, v = gc[dm].astype(np.int64), oc[dm].astype(np.int64), pre[dm]
+        adjacent = np.abs(g - o) == 1
+        lo = np.minimum(g, o)
+        if encoder == "exact":
+            dec = OF.e2m1_decode if fmt == "e2m1" else OF.e4m3_decode
+            mid = 0.5 * (dec(lo) + dec(lo + 1))
+            near = np.abs(v - mid) <= NEAR_TIE_REL * mid
+        else:
+            near = np.abs(v - (lo + 0.5)) <= NEAR_TIE_POS
+        bad = ~(adjacent & near)
+        where = np.argwhere(dm)[bad][:5].tolist()
+        assert not bad.any(), (f"{int(bad.sum())} codes differ away from a rounding boundary, e.g. at {where}: "
+                               f"kernel {g[bad][:5].tolist()} oracle {o[bad][:5].tolist()} value {v[bad][:5].tolist()}")
+    return n_e, n_c

@@ -111,6 +111,14 @@ def test_fwd_validation(lib):
     assert lib.attn_fwd_directp(ctypes.byref(_args(softmax_scale=0.0, ws=1 << 24, ws_bytes=need)), None) == 1
     assert lib.attn_fwd_directp(ctypes.byref(_args(o=None, ws=1 << 24, ws_bytes=need)), None) == 1
     assert lib.attn_fwd_directp(None, None) == 1
+    # the exp-free entry points share the checks of the exact ones
+    assert lib.attn_fwd_directp_efq(ctypes.byref(_args(causal=1, ws=1 << 24, ws_bytes=need)), None) == 2
+    assert lib.attn_fwd_directp_efq(ctypes.byref(_args(D=96, ws=1 << 24, ws_bytes=need)), None) == 1
+    assert lib.attn_fwd_directp_efq(ctypes.byref(_args(ws=1 << 24, ws_bytes=need - 1)), None) == 3
+    assert lib.attn_fwd_fp8pv_cast(ctypes.byref(_args(v=B._VTensor(1, 1 << 24, 1 << 24, 1 << 24), ws=1 << 24,
+                                                      ws_bytes=need)), None) == 2
+    assert lib.attn_fwd_fp8pv_cast(ctypes.byref(_args(causal=1, Nk=128, ws=1 << 24, ws_bytes=need)), None) == 1
+    assert lib.attn_fwd_fp8pv_cast(None, None) == 1
     # varlen needs both cu_seqlens
     assert lib.attn_fwd_directp(ctypes.byref(_args(cu_seqlens_q=1 << 24, ws=1 << 24, ws_bytes=need)), None) == 1
     # bf16 baseline argument checks
