@@ -72,6 +72,69 @@ def quant_nvfp4(x, amax=None):
     return pack_nibbles(codes), s_code.reshape(lead + (D // NVFP4_BLOCK,)), g
 
 
+def quant_nvfp4_46(x, amax=None, return_choice=False, candidates=(6.0, 4.0)):
+    """NVFP4 quantization with the Four Over Six adaptive block scale.
+
+    The method is listed beside the arXiv entry of the pages' paper (arXiv
+    listing 2609.04105v1, "Related papers": "Four Over Six: More Accurate
+    NVFP4 Quantization with Adaptive Block Scaling"), abstract only: each
+    block evaluates two scale factors, and for some blocks scaling the block
+    maximum to the smaller FP4 value 4 instead of 6 represents the block
+    better.  Reading taken (same float32 operation order as quant_nvfp4):
+      1. amax_t as in quant_nvfp4; S_enc = fl(1792 / amax_t) (1792 = 448 * 4,
+         so that a block scale that maps the block max to 4 still fits E4M3),
+         or 1 when amax_t = 0; g = fl(1 / S_enc).
+      2. For M in (6, 4): s_M = E4M3(fl(fl(amax_b / M) * S_enc)) and codes_M
+         as step 5 of quant_nvfp4 with s_M.
+      3. err_M = sum over the block's 16 elements, in element order, of
+         fl(d * d) with d = fl(fl(x_i * S_enc) - E2M1(code_i) * s_M), summed
+         in float32 from 0 (the squared error in units of g).
+      4. The block keeps M = 4 when err_4 < err_6, else M = 6.
+    Dequantized value: E2M1(code) * E4M3(s) * g, as for quant_nvfp4.
+
+    Returns (codes_packed, scales, g) like quant_nvfp4 and, with
+    ``return_choice``, a bool array [..., D/16] that is True where M = 4.
+    ``candidates`` restricts the block maxima tried (one value forces it).
+    """
+    x = np.asarray(x, dtype=F32)
+    D = x.shape[-1]
+    assert D % NVFP4_BLOCK == 0
+    lead = x.shape[:-1]
+    xb = x.reshape(-1, D // NVFP4_BLOCK, NVFP4_BLOCK)
+    if amax is None:
+        amax = np.max(np.abs(xb)) if xb.size else 0.0
+    s_enc = _enc_scale(F32(amax), 1792.0)
+    g = F32(F32(1.0) / s_enc)
+    amax_b = np.max(np.abs(xb), axis=-1) if xb.size else np.zeros(xb.shape[:-1], F32)
+    xs = (xb * s_enc).astype(F32)
+    cand = []
+    for M in candidates:
+        s_code = e4m3_encode(((amax_b / F32(M)).astype(F32) * s_enc).astype(F32))
+        s_val = e4m3_decode(s_code).astype(F32)
+        with np.errstate(divide="ignore"):
+            enc = np.where(s_val > 0, s_enc / np.where(s_val > 0, s_val, F32(1)), F32(0)).astype(F32)
+        codes = e2m1_encode((xb * enc[..., None]).astype(F32))
+        codes = np.where((s_val > 0)[..., None], codes, np.uint8(0)).astype(np.uint8)
+        q = (e2m1_decode(codes).astype(F32) * s_val[..., None]).astype(F32)
+        d = (xs - q).astype(F32)
+        sq = (d * d).astype(F32)
+        err = np.zeros(xb.shape[:-1], F32)
+        for i in range(NVFP4_BLOCK):
+            err = (err + sq[..., i]).astype(F32)
+        cand.append((s_code, codes, err))
+    if len(cand) == 1:
+        four = np.full(xb.shape[:-1], candidates[0] == 4.0)
+        s_code, codes = cand[0][0], cand[0][1].reshape(lead + (D,))
+    else:
+        four = cand[1][2] < cand[0][2]
+        s_code = np.where(four, cand[1][0], cand[0][0]).astype(np.uint8)
+        codes = np.where(four[..., None], cand[1][1], cand[0][1]).astype(np.uint8).reshape(lead + (D,))
+    out = (pack_nibbles(codes), s_code.reshape(lead + (D // NVFP4_BLOCK,)), g)
+    if return_choice:
+        return out + (four.reshape(lead + (D // NVFP4_BLOCK,)),)
+    return out
+
+
 def dequant_nvfp4_raw(codes_packed, scales):
     """E2M1(code) * E4M3(scale) without the tensor scale, float64 [..., D].
 
