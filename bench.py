@@ -33,6 +33,8 @@ def parse():
     ap.add_argument("--workload", type=int, default=2, help="1..5 (default 2: Wan2.1-14B shape)")
     ap.add_argument("--encoder", choices=("exact", "loglin"), default="exact",
                     help="probability encoder: exact (RNE of 2^y) or the exp-free log-linear cast")
+    ap.add_argument("--four-six", action="store_true",
+                    help="quantize Q and K with the Four Over Six adaptive block scale (attn_quant_nvfp4_46)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=16384, help="query rows of the oracle sample")
@@ -84,7 +86,7 @@ def copy_calibration(mib):
                       "launches": 3}), flush=True)
 
 
-def cpu_baseline(inp, rows, encoder="exact"):
+def cpu_baseline(inp, rows, encoder="exact", four_six=False):
     """Time the CPU oracle (as it stands) on a bounded sample: one (batch,
     head), `rows` query rows against all keys, including the sample's
     quantization.  Returns a dict for the JSON line."""
@@ -109,8 +111,9 @@ def cpu_baseline(inp, rows, encoder="exact"):
     kf = kh.float().cpu().numpy()
     vf = vh.float().cpu().numpy()
     t = time.perf_counter()
-    qc, qs, gq = OQ.quant_nvfp4(qf)
-    kc, ks, gk = OQ.quant_nvfp4(kf)
+    qfn = OQ.quant_nvfp4_46 if four_six else OQ.quant_nvfp4
+    qc, qs, gq = qfn(qf)
+    kc, ks, gk = qfn(kf)
     if wl.v_format == "fp8":
         vcodes, s_v = OQ.quant_v_fp8(vf)
         vhat = OQ.dequant_v_fp8(vcodes, s_v)
@@ -228,8 +231,8 @@ def main():
     kev = HipEvents(args.steps)
 
     def quantize():
-        q = paf.quant_nvfp4(inp.q)
-        k = paf.quant_nvfp4(inp.k)
+        q = paf.quant_nvfp4(inp.q, four_six=args.four_six)
+        k = paf.quant_nvfp4(inp.k, four_six=args.four_six)
         if varlen:
             vc, vs, vt, _ = paf.quant_v(inp.v, vfmt, cu_seqlens=kw["cu_seqlens_k"], max_seqlen=kw["max_seqlen_k"])
         else:
@@ -298,14 +301,15 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, args.cpu_rows, args.encoder)
+        cpu = cpu_baseline(inp, args.cpu_rows, args.encoder, args.four_six)
 
     cfg = {"workload": f"{wl.name}: " + (f"{wl.varlen[0]} packed sequences" if varlen else
                                          f"B={wl.B} N={wl.N}") +
            f" Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D} {'causal' if wl.causal else 'noncausal'}, "
            f"P={wl.p_format.upper()} V={wl.v_format.upper()}" +
-           ("" if args.encoder == "exact" else ", exp-free log-linear P encoder"),
-           "encoder": args.encoder,
+           ("" if args.encoder == "exact" else ", exp-free log-linear P encoder") +
+           (", Four Over Six Q/K block scales" if args.four_six else ""),
+           "encoder": args.encoder, "four_six": args.four_six,
            "B": wl.B if not varlen else int(len(inp.seqlens)), "Hq": wl.Hq, "Hkv": wl.Hkv,
            "N": wl.N if not varlen else int(inp.seqlens.max()), "D": wl.D, "causal": wl.causal,
            "flops_per_step": flops, "parallelism": "single GPU"}

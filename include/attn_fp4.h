@@ -96,6 +96,26 @@ attn_status attn_quant_nvfp4(const void* x_bf16, int64_t rows, int32_t D,
                              void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * NVFP4 quantization with the Four Over Six adaptive block scale, a related
+ * method listed beside the arXiv entry of the pages' paper (2609.04105v1,
+ * "Related papers": "Four Over Six: More Accurate NVFP4 Quantization with
+ * Adaptive Block Scaling"; abstract only): each block evaluates two scale
+ * factors, one mapping the block maximum to 6 and one mapping it to 4.
+ * Reading implemented (float32, RNE, same order as attn_quant_nvfp4):
+ *   S_enc = 1792 / amax_t   (448 * 4, so that both candidate scales fit E4M3)
+ *   g     = 1 / S_enc                                -> *tensor_scale
+ *   per block, for M in {6, 4}: s_M = E4M3_sat((amax_b / M) * S_enc),
+ *     codes_M = E2M1_sat(x_i * (S_enc / s_M)) (all 0 when s_M == 0),
+ *     err_M = sum over i = 0..15 in order of (x_i * S_enc - E2M1(code_i) * s_M)^2
+ *   the block keeps M = 4 when err_4 < err_6, else M = 6.
+ * The output format, arguments, workspace and errors are those of
+ * attn_quant_nvfp4, so the forward entry points take its output unchanged.
+ */
+attn_status attn_quant_nvfp4_46(const void* x_bf16, int64_t rows, int32_t D,
+                                uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Number of key columns of the transposed V layout used by attn_quant_v and
  * the forward.  Sequence s starts at column
  *     dense : s * roundup(Nk, 128)

@@ -60,6 +60,9 @@ EXPORTS = {
     "attn_quant_nvfp4": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                         ctypes.c_void_p]),
+    "attn_quant_nvfp4_46": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_void_p]),
     "attn_v_cols": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]),
     "attn_quant_v": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
@@ -116,9 +119,11 @@ def _need_cuda(*ts):
             raise AttnError("tensors must be contiguous and on the GPU")
 
 
-def quant_nvfp4(x):
+def quant_nvfp4(x, four_six=False):
     """NVFP4-quantize a bf16 tensor along its last axis (D).  Returns
-    (codes uint8 [..., D/2], scales uint8 [..., D/16], tensor_scale float32 [1])."""
+    (codes uint8 [..., D/2], scales uint8 [..., D/16], tensor_scale float32 [1]).
+    ``four_six`` selects the Four Over Six adaptive block scale
+    (attn_quant_nvfp4_46); the output format is the same."""
     lib = load_library()
     _need_cuda(x)
     if x.dtype != torch.bfloat16:
@@ -129,8 +134,8 @@ def quant_nvfp4(x):
     scales = torch.empty(x.shape[:-1] + (D // 16,), dtype=torch.uint8, device=x.device)
     ts = torch.empty(1, dtype=torch.float32, device=x.device)
     ws = torch.empty(lib.attn_quant_ws_bytes(), dtype=torch.uint8, device=x.device)
-    _check(lib.attn_quant_nvfp4(_ptr(x), rows, D, _ptr(codes), _ptr(scales), _ptr(ts), _ptr(ws), ws.numel(),
-                                _stream()))
+    fn = lib.attn_quant_nvfp4_46 if four_six else lib.attn_quant_nvfp4
+    _check(fn(_ptr(x), rows, D, _ptr(codes), _ptr(scales), _ptr(ts), _ptr(ws), ws.numel(), _stream()))
     return codes, scales, ts
 
 

@@ -11,7 +11,7 @@
 namespace attn {
 hipError_t launch_amax(const void* x, int64_t n, float* partials, int* np_out, hipStream_t st);
 hipError_t launch_quant_nvfp4(const void* x, int64_t rows, int D, const float* partials, int np, uint8_t* codes,
-                              uint8_t* scales, float* tensor_scale, hipStream_t st);
+                              uint8_t* scales, float* tensor_scale, bool four_six, hipStream_t st);
 hipError_t launch_quant_v(const void* v, int B, int Nk, int Hkv, int D, const int32_t* cu_k, int max_len, int64_t cols,
                           int fmt, const float* partials, int np, uint8_t* codes, uint8_t* scales, float* tensor_scale,
                           hipStream_t st);
@@ -56,8 +56,8 @@ int attn_last_hip_error(void) { return g_last_hip_error; }
 const char* attn_version(void) { return "attn_fp4 0.1 gfx950"; }
 size_t attn_quant_ws_bytes(void) { return QUANT_WS; }
 
-attn_status attn_quant_nvfp4(const void* x_bf16, int64_t rows, int32_t D, uint8_t* codes, uint8_t* scales,
-                             float* tensor_scale, void* ws, size_t ws_bytes, void* stream) {
+static attn_status run_quant_nvfp4(const void* x_bf16, int64_t rows, int32_t D, uint8_t* codes, uint8_t* scales,
+                                   float* tensor_scale, void* ws, size_t ws_bytes, void* stream, bool four_six) {
   if (rows < 0 || D <= 0 || D % 16 != 0 || tensor_scale == nullptr || !aligned(tensor_scale, 4))
     return ATTN_ERR_INVALID_ARGUMENT;
   if (rows > 0 && (x_bf16 == nullptr || codes == nullptr || scales == nullptr || !aligned(x_bf16, 16) ||
@@ -69,7 +69,17 @@ attn_status attn_quant_nvfp4(const void* x_bf16, int64_t rows, int32_t D, uint8_
   float* partials = (float*)ws;
   hipError_t e = launch_amax(x_bf16, rows * (int64_t)D, partials, &np, st);
   if (e != hipSuccess) return hip_status(e);
-  return hip_status(launch_quant_nvfp4(x_bf16, rows, D, partials, np, codes, scales, tensor_scale, st));
+  return hip_status(launch_quant_nvfp4(x_bf16, rows, D, partials, np, codes, scales, tensor_scale, four_six, st));
+}
+
+attn_status attn_quant_nvfp4(const void* x_bf16, int64_t rows, int32_t D, uint8_t* codes, uint8_t* scales,
+                             float* tensor_scale, void* ws, size_t ws_bytes, void* stream) {
+  return run_quant_nvfp4(x_bf16, rows, D, codes, scales, tensor_scale, ws, ws_bytes, stream, false);
+}
+
+attn_status attn_quant_nvfp4_46(const void* x_bf16, int64_t rows, int32_t D, uint8_t* codes, uint8_t* scales,
+                                float* tensor_scale, void* ws, size_t ws_bytes, void* stream) {
+  return run_quant_nvfp4(x_bf16, rows, D, codes, scales, tensor_scale, ws, ws_bytes, stream, true);
 }
 
 int64_t attn_v_cols(int32_t B, int32_t Nk, int64_t total_k, int32_t varlen) {

@@ -80,13 +80,74 @@ __device__ inline float encode_scale(float amax, float top) {
   return __builtin_isinf(s) ? 3.40282347e+38f : s;
 }
 
-// Pass 2 (NVFP4): one thread per 16-element block along D.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// One NVFP4 block for a block maximum mapped to M (6 in the standard recipe):
+// s = E4M3((amax_b / M) * S_enc), codes E2M1(x * (S_enc / s)) (element 2k in
+// the low nibble of byte k), all 0 when s decodes to 0.  Returns the scale code.
+__device__ inline uint32_t nvfp4_block(const float (&v)[16], float amax_b, float s_enc, float M, u32x2& out,
+                                       float& sv) {
+  const float sf = (amax_b / M) * s_enc;
+  const uint32_t sc = e4m3_encode(sf);
+  sv = e4m3_decode(sc);
+  out = u32x2{0u, 0u};
+  if (sv > 0.0f) {
+    const float enc = s_enc / sv;
+    float y[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) y[j] = v[j] * enc;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      uint32_t w = 0u;
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[8 * h2 + 0], y[8 * h2 + 1], 1.0f, 0);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[8 * h2 + 2], y[8 * h2 + 3], 1.0f, 1);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[8 * h2 + 4], y[8 * h2 + 5], 1.0f, 2);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[8 * h2 + 6], y[8 * h2 + 7], 1.0f, 3);
+      out[h2] = w;
+    }
+  }
+  return sc;
+}
+
+// Squared error of a block candidate in units of the tensor scale:
+// sum over j in order of (x_j S_enc - E2M1(code_j) s)^2, float32, no contraction.
+// The codes are decoded two at a time by the hardware FP4 -> F32 conversion
+// (unit scale; element 2k from the low nibble of byte k), then multiplied by s
+// (exact: at most 2 x 4 significant bits).
+__device__ inline float nvfp4_block_err(const float (&xs)[16], const u32x2& w, float sv) {
+  float q[16];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[h2], 1.0f, 0);
+    const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[h2], 1.0f, 1);
+    const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[h2], 1.0f, 2);
+    const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[h2], 1.0f, 3);
+    q[8 * h2 + 0] = p0[0]; q[8 * h2 + 1] = p0[1];
+    q[8 * h2 + 2] = p1[0]; q[8 * h2 + 3] = p1[1];
+    q[8 * h2 + 4] = p2[0]; q[8 * h2 + 5] = p2[1];
+    q[8 * h2 + 6] = p3[0]; q[8 * h2 + 7] = p3[1];
+  }
+  float err = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float d = xs[j] - q[j] * sv;
+    err = err + d * d;
+  }
+  return err;
+}
+
+// Pass 2 (NVFP4): one thread per 16-element block along D.  FOUR_SIX: the
+// Four Over Six variant (related method listed beside the arXiv entry of the
+// pages' paper, "Four Over Six: More Accurate NVFP4 Quantization with Adaptive
+// Block Scaling"): S_enc = 1792 / amax_t, and each block keeps the block
+// maximum mapped to 4 instead of 6 when that gives the smaller squared error.
+template <bool FOUR_SIX>
 __global__ void __launch_bounds__(256) quant_nvfp4_kernel(const uint16_t* __restrict__ x, int64_t nblocks,
                                                           const float* __restrict__ partials, int np,
                                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                           float* __restrict__ tensor_scale) {
   const float amax_t = reduce_partials(partials, np);
-  const float s_enc = encode_scale(amax_t, 2688.0f);
+  const float s_enc = encode_scale(amax_t, FOUR_SIX ? 1792.0f : 2688.0f);
   if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = 1.0f / s_enc;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nblocks; i += (int64_t)gridDim.x * blockDim.x) {
     const u32x4* p = reinterpret_cast<const u32x4*>(x + 16 * i);
@@ -102,23 +163,19 @@ __global__ void __launch_bounds__(256) quant_nvfp4_kernel(const uint16_t* __rest
     float amax_b = 0.0f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) amax_b = __builtin_fmaxf(amax_b, __builtin_fabsf(v[j]));
-    const float sf = (amax_b / 6.0f) * s_enc;
-    const uint32_t sc = e4m3_encode(sf);
-    const float sv = e4m3_decode(sc);
-    u32x2 out = {0u, 0u};
-    if (sv > 0.0f) {
-      const float enc = s_enc / sv;
-      float y[16];
+    u32x2 out;
+    float sv;
+    uint32_t sc = nvfp4_block(v, amax_b, s_enc, 6.0f, out, sv);
+    if (FOUR_SIX) {
+      float xs[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) y[j] = v[j] * enc;
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        uint32_t w = 0u;   // element 2k in the low nibble of byte k
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[8 * h2 + 0], y[8 * h2 + 1], 1.0f, 0);
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[8 * h2 + 2], y[8 * h2 + 3], 1.0f, 1);
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[8 * h2 + 4], y[8 * h2 + 5], 1.0f, 2);
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[8 * h2 + 6], y[8 * h2 + 7], 1.0f, 3);
-        out[h2] = w;
+      for (int j = 0; j < 16; ++j) xs[j] = v[j] * s_enc;
+      u32x2 out4;
+      float sv4;
+      const uint32_t sc4 = nvfp4_block(v, amax_b, s_enc, 4.0f, out4, sv4);
+      if (nvfp4_block_err(xs, out4, sv4) < nvfp4_block_err(xs, out, sv)) {
+        out = out4;
+        sc = sc4;
       }
     }
     *reinterpret_cast<u32x2*>(codes + 8 * i) = out;
@@ -216,12 +273,16 @@ hipError_t launch_amax(const void* x, int64_t n, float* partials, int* np_out, h
 }
 
 hipError_t launch_quant_nvfp4(const void* x, int64_t rows, int D, const float* partials, int np, uint8_t* codes,
-                              uint8_t* scales, float* tensor_scale, hipStream_t st) {
+                              uint8_t* scales, float* tensor_scale, bool four_six, hipStream_t st) {
   int64_t nblocks = rows * (D / 16);
   int64_t want = (nblocks + 255) / 256;
   int grid = (int)(want < 1 ? 1 : (want > 4096 ? 4096 : want));
-  hipLaunchKernelGGL(quant_nvfp4_kernel, dim3(grid), dim3(256), 0, st, (const uint16_t*)x, nblocks, partials, np, codes,
-                     scales, tensor_scale);
+  if (four_six)
+    hipLaunchKernelGGL(quant_nvfp4_kernel<true>, dim3(grid), dim3(256), 0, st, (const uint16_t*)x, nblocks, partials,
+                       np, codes, scales, tensor_scale);
+  else
+    hipLaunchKernelGGL(quant_nvfp4_kernel<false>, dim3(grid), dim3(256), 0, st, (const uint16_t*)x, nblocks, partials,
+                       np, codes, scales, tensor_scale);
   return hipGetLastError();
 }
 

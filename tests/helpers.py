@@ -52,11 +52,12 @@ def oracle_v_head(v_head_f32, v_format, amax_all=None):
 
 
 def oracle_head(q_rows, k_rows, v_rows, *, amax_q, amax_k, amax_v, sigma, p_format, v_format, causal,
-                q_index=None, return_p=False, encoder="exact", p_given=None, return_pre=False):
+                q_index=None, return_p=False, encoder="exact", p_given=None, return_pre=False, four_six=False):
     """Oracle forward for a set of query rows of one head, given the bf16
     inputs (as float32 numpy) and the whole-tensor amax values."""
-    qc, qs, gq = OQ.quant_nvfp4(q_rows, amax=amax_q)
-    kc, ks, gk = OQ.quant_nvfp4(k_rows, amax=amax_k)
+    qfn = OQ.quant_nvfp4_46 if four_six else OQ.quant_nvfp4
+    qc, qs, gq = qfn(q_rows, amax=amax_q)
+    kc, ks, gk = qfn(k_rows, amax=amax_k)
     vh = oracle_v_head(v_rows, v_format, amax_v)
     return OA.attn_lowp_head(OQ.dequant_nvfp4_raw(qc, qs), OQ.dequant_nvfp4_raw(kc, ks), gq, gk, vh, sigma,
                              p_format, causal, q_index=q_index, return_p=return_p, encoder=encoder,

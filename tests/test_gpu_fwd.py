@@ -29,10 +29,10 @@ ENTRY = {("mxfp4", "exact"): "fwd_directp", ("fp8", "exact"): "fwd_fp8pv",
          ("mxfp4", "loglin"): "fwd_directp_efq", ("fp8", "loglin"): "fwd_fp8pv_cast"}
 
 
-def _gpu_run(gpu, inp, debug=None, out_dtype=torch.float32, encoder="exact"):
+def _gpu_run(gpu, inp, debug=None, out_dtype=torch.float32, encoder="exact", four_six=False):
     wl = inp.wl
-    q = gpu.quant_nvfp4(inp.q)
-    k = gpu.quant_nvfp4(inp.k)
+    q = gpu.quant_nvfp4(inp.q, four_six=four_six)
+    k = gpu.quant_nvfp4(inp.k, four_six=four_six)
     vf = gpu.V_FP8 if wl.v_format == "fp8" else gpu.V_MXFP4
     kw = dict(Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D, softmax_scale=inp.sigma, causal=wl.causal, out_dtype=out_dtype,
               debug=debug)
@@ -64,7 +64,7 @@ def _seq_slices(inp):
     return [(s, int(cu[s]), int(cu[s + 1] - cu[s])) for s in range(len(cu) - 1)]
 
 
-def _check(gpu, inp, heads=None, seqs=None, rows=None, dumps=True, max_rows=None, encoder="exact"):
+def _check(gpu, inp, heads=None, seqs=None, rows=None, dumps=True, max_rows=None, encoder="exact", four_six=False):
     """Run the production kernel once and compare the selected (sequence,
     head, rows) with the oracle.
 
@@ -76,7 +76,7 @@ def _check(gpu, inp, heads=None, seqs=None, rows=None, dumps=True, max_rows=None
     are then compared with the oracle run on the kernel's codes, so that a
     tie decided the other way is not counted as an output error."""
     wl = inp.wl
-    o, lse, _ = _gpu_run(gpu, inp, encoder=encoder)
+    o, lse, _ = _gpu_run(gpu, inp, encoder=encoder, four_six=four_six)
     amax_q, amax_k, amax_v = _amax(inp.q), _amax(inp.k), _amax(inp.v)
     varlen = inp.cu_seqlens is not None
     group = wl.Hq // wl.Hkv
@@ -104,12 +104,12 @@ def _check(gpu, inp, heads=None, seqs=None, rows=None, dumps=True, max_rows=None
                 r = r[np.linspace(0, len(r) - 1, max_rows).astype(int)]
             ridx = torch.as_tensor(r, device=o.device)
             kw = dict(amax_q=amax_q, amax_k=amax_k, amax_v=amax_v, sigma=inp.sigma, p_format=wl.p_format,
-                      v_format=wl.v_format, causal=wl.causal, q_index=r, encoder=encoder)
+                      v_format=wl.v_format, causal=wl.causal, q_index=r, encoder=encoder, four_six=four_six)
             q_rows, k_all, v_all = f32(qh[torch.as_tensor(r, device=qh.device)]), f32(kh), f32(vh)
             if not dumps:
                 res = oracle_head(q_rows, k_all, v_all, **kw)
             else:
-                od, ld, (dc, ds) = _gpu_run(gpu, inp, debug=(s, h), encoder=encoder)
+                od, ld, (dc, ds) = _gpu_run(gpu, inp, debug=(s, h), encoder=encoder, four_six=four_six)
                 assert torch.equal(od, o) and torch.equal(ld, lse), "the dump build computes other outputs"
                 res = oracle_head(q_rows, k_all, v_all, return_pre=True, **kw)
                 gc, ge = gpu_codes(dc[ridx].cpu().numpy(), None if ds is None else ds[ridx].cpu().numpy(),
@@ -289,3 +289,18 @@ def test_expfree_full_size_sampled(gpu, k, heads, nrows):
     assert stats
     del inp
     torch.cuda.empty_cache()
+
+
+# ---- Q and K quantized with the Four Over Six block scale: the forward
+# consumes the same format; parity against the oracle on the same quantizer
+
+FOUR_SIX = [SMALL[1], SMALL[3], SMALL[7]]
+
+
+@pytest.mark.parametrize("name,wl,_", FOUR_SIX, ids=[s[0] for s in FOUR_SIX])
+def test_four_six_quantized_forward(gpu, name, wl, _):
+    _say(f"fwd 4/6-quantized Q/K {name}")
+    inp = synth.generate(wl, "cpu")
+    inp.q, inp.k, inp.v = inp.q.cuda(), inp.k.cuda(), inp.v.cuda()
+    o, lse, stats = _check(gpu, inp, four_six=True)
+    assert stats

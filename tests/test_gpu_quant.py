@@ -30,16 +30,16 @@ def _amax_cpu(x_gpu, chunk=1 << 26):
     return m
 
 
-def _check_nvfp4(gpu, x_gpu, rows=None, amax=None):
+def _check_nvfp4(gpu, x_gpu, rows=None, amax=None, four_six=False):
     D = x_gpu.shape[-1]
-    codes, scales, ts = gpu.quant_nvfp4(x_gpu)
+    codes, scales, ts = gpu.quant_nvfp4(x_gpu, four_six=four_six)
     torch.cuda.synchronize()
     x2 = x_gpu.reshape(-1, D)
     c2, s2 = codes.reshape(-1, D // 2), scales.reshape(-1, D // 16)
     if rows is not None:
         x2, c2, s2 = x2[rows], c2[rows], s2[rows]
     xc = _bf16_cpu(x2).float().numpy()
-    oc, os_, og = OQ.quant_nvfp4(xc, amax=amax)
+    oc, os_, og = (OQ.quant_nvfp4_46 if four_six else OQ.quant_nvfp4)(xc, amax=amax)
     np.testing.assert_array_equal(c2.cpu().numpy(), oc)
     np.testing.assert_array_equal(s2.cpu().numpy(), os_)
     assert ts.item() == float(og)
@@ -81,6 +81,50 @@ def test_nvfp4_full_size_sampled(gpu, k):
         rng = np.random.default_rng(k)
         rows = torch.from_numpy(np.unique(np.concatenate([rng.integers(0, nrows, 2000), [0, nrows - 1]]))).cuda()
         _check_nvfp4(gpu, x, rows=rows, amax=_amax_cpu(x))
+    del inp
+    torch.cuda.empty_cache()
+
+
+# ---- Four Over Six (adaptive block scale): the same bar
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("rows", [1, 37, 1000])
+def test_nvfp4_46_small_bitexact(gpu, D, rows):
+    _say(f"nvfp4 4/6 D={D} rows={rows}")
+    g = torch.Generator().manual_seed(rows * 11 + D)
+    x = torch.randn((rows, D), generator=g) * torch.exp2(torch.randint(-8, 8, (rows, 1), generator=g).float())
+    x[:, 5] *= 16
+    _check_nvfp4(gpu, x.to(torch.bfloat16).cuda(), four_six=True)
+
+
+def test_nvfp4_46_degenerate_and_hand_derived(gpu):
+    _say("nvfp4 4/6 zeros / tiny / hand-derived blocks / tie")
+    _check_nvfp4(gpu, torch.zeros((5, 64), dtype=torch.bfloat16, device="cuda"), four_six=True)
+    tiny = torch.full((3, 64), 1e-37) * torch.randn((3, 64), generator=torch.Generator().manual_seed(1))
+    _check_nvfp4(gpu, tiny.to(torch.bfloat16).cuda(), four_six=True)
+    # amax_t = 7 (S_enc 256): block [7, 5.25] takes max 4; block [6] ties and keeps max 6;
+    # block [6, 1] with max 6 wins over max 4; then a block of rounding ties
+    x = torch.zeros((1, 64))
+    x[0, 0], x[0, 1] = 7.0, 5.25
+    x[0, 16] = 6.0
+    x[0, 32], x[0, 33] = 6.0, 1.0
+    x[0, 48:64] = torch.tensor([5.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, -5.0, 4.5, 5.5, 1.0, 2.0, -0.0, 0.0, 3.0, -3.0])
+    _check_nvfp4(gpu, x.to(torch.bfloat16).cuda(), four_six=True)
+    codes, scales, ts = gpu.quant_nvfp4(x.to(torch.bfloat16).cuda(), four_six=True)
+    assert scales[0, 0].item() == 0x7E and scales[0, 1].item() == 0x78 and ts.item() == 1.0 / 256.0
+
+
+@pytest.mark.parametrize("k", [2, 4])
+def test_nvfp4_46_full_size_sampled(gpu, k):
+    wl = synth.WORKLOADS[k]
+    _say(f"nvfp4 4/6 full-size workload {wl.name}")
+    inp = synth.generate(wl, "cuda")
+    for name, x in (("q", inp.q), ("k", inp.k)):
+        D = x.shape[-1]
+        nrows = x.numel() // D
+        rng = np.random.default_rng(100 + k)
+        rows = torch.from_numpy(np.unique(np.concatenate([rng.integers(0, nrows, 2000), [0, nrows - 1]]))).cuda()
+        _check_nvfp4(gpu, x, rows=rows, amax=_amax_cpu(x), four_six=True)
     del inp
     torch.cuda.empty_cache()
 
