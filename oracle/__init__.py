@@ -23,10 +23,12 @@ Modules:
   attention  -- Direct-P and FP8-P/V tiled forward, exact softmax attention
   loglin     -- exp-free log-linear probability casts (E4M3, E2M1) of the
                 related methods listed beside the arXiv entry
+  backward   -- causal-training backward: probabilities rebuilt from the
+                saved quantized Q/K and LSE, FP8 gradient operands (E5M2 dO)
 
 Parity status: every function is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_*.py`` (closed forms, exhaustive codec checks against
 torch's float8 dtypes, invariants, and an exact-attention special case).
 """
 
-from . import formats, quant, attention, loglin  # noqa: F401
+from . import formats, quant, attention, loglin, backward  # noqa: F401

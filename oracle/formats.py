@@ -10,6 +10,10 @@ point and OCP Microscaling (MX) v1.0 definitions):
 * E4M3 (the "fn" variant): 1 sign, 4 exponent bits (bias 7), 3 mantissa bits,
   no infinities, 0x7F/0xFF are NaN, largest finite 448, subnormals down to
   2**-9.  Used for the NVFP4 block scales, FP8 V and FP8 P.
+* E5M2: 1 sign, 5 exponent bits (bias 15), 2 mantissa bits, largest finite
+  57344, subnormals down to 2**-16; 0x7C is infinity and 0x7D..0x7F NaN.  Used
+  for the output gradient dO of the backward (summary page, "What the paper
+  found": FP8 gradient operands, with E5M2 output gradients).
 * E8M0: an unsigned biased exponent, value 2**(k-127) for k in 0..254, 255 is
   NaN.  Used for the per-32-element MX scales.
 
@@ -24,6 +28,7 @@ import numpy as np
 E2M1_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
 E2M1_MAX = 6.0
 E4M3_MAX = 448.0
+E5M2_MAX = 57344.0
 
 
 def _round_to_minifloat(a, mbits, emin):
@@ -75,6 +80,31 @@ def e4m3_encode(x):
     sub = r < 2.0 ** -6
     mant = np.where(sub, 0, np.rint((r / np.ldexp(1.0, np.where(sub, 0, e)) - 1.0) * 8.0))
     code = np.where(sub, np.rint(r * 2.0 ** 9), ((e + 7) << 3) + mant).astype(np.int64)
+    code = np.where(np.signbit(x), code | 0x80, code)
+    return code.astype(np.uint8)
+
+
+def e5m2_decode(codes):
+    """E5M2 codes -> float64 values (0x7C/0xFC are +-inf, 0x7D..0x7F NaN)."""
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    s = c >> 7
+    e = (c >> 2) & 0x1F
+    m = c & 3
+    mag = np.where(e == 0, m * 2.0 ** -16, (1.0 + m / 4.0) * np.ldexp(1.0, e - 15))
+    mag = np.where(e == 31, np.where(m == 0, np.inf, np.nan), mag)
+    return np.where(s == 1, -mag, mag)
+
+
+def e5m2_encode(x):
+    """Real values -> E5M2 codes, round-to-nearest-even, saturating to 57344."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    r = np.minimum(_round_to_minifloat(a, 2, -14), E5M2_MAX)
+    _, k = np.frexp(r)
+    e = k.astype(np.int64) - 1
+    sub = r < 2.0 ** -14
+    mant = np.where(sub, 0, np.rint((r / np.ldexp(1.0, np.where(sub, 0, e)) - 1.0) * 4.0))
+    code = np.where(sub, np.rint(r * 2.0 ** 16), ((e + 15) << 2) + mant).astype(np.int64)
     code = np.where(np.signbit(x), code | 0x80, code)
     return code.astype(np.uint8)
 

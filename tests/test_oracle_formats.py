@@ -115,3 +115,34 @@ def test_e8m0_exponent_range():
     assert F.e8m0_encode_exponent([-127, 0, 127]).tolist() == [0, 127, 254]
     with pytest.raises(ValueError):
         F.e8m0_encode_exponent([128])
+
+
+def test_e5m2_decode_matches_torch():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e5m2).to(torch.float64).numpy()
+    got = F.e5m2_decode(codes.numpy())
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+
+
+def test_e5m2_encode_matches_torch_on_all_bf16():
+    # torch's cast rounds to nearest even; past 61440 it gives infinity, where
+    # the oracle saturates to 57344
+    x = _all_finite_bf16()
+    ref = x.to(torch.float8_e5m2)
+    finite = torch.isfinite(ref.to(torch.float32))
+    got = F.e5m2_encode(x.to(torch.float32).numpy())
+    np.testing.assert_array_equal(got[finite.numpy()], ref.view(torch.uint8).numpy()[finite.numpy()])
+    big = (~finite).numpy()
+    xs = x.to(torch.float32).numpy()[big]
+    assert np.all(np.abs(xs) >= 61440)
+    np.testing.assert_array_equal(got[big], np.where(xs < 0, 0xFB, 0x7B).astype(np.uint8))
+
+
+def test_e5m2_encode_matches_torch_random_f32():
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal(200000) * np.exp2(rng.uniform(-20, 15, 200000))).astype(np.float32)
+    x = x[np.abs(x) < 61440]
+    ref = torch.from_numpy(x).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(F.e5m2_encode(x), ref)
