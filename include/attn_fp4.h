@@ -267,6 +267,77 @@ attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, 
                           int32_t B, int32_t Hq, int32_t Hkv, int32_t Nq, int32_t Nk, int32_t D,
                           float softmax_scale, int32_t causal, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Backward (causal training path)
+ * --------------------------------------------------------------------- */
+
+/*
+ * Backward of the FP8-P/V forward, the path the pages train with (summary
+ * page, "What the paper found": the forward keeps its quantized Q/K payloads,
+ * scales and LSE; the backward rebuilds the probabilities from them and uses
+ * FP8 gradient operands, with E5M2 output gradients).  The pages give no
+ * formulas; the operation implemented, per (batch, head), is:
+ *   dO^ = E5M2_sat(dO * S) * s with S = 57344 / amax(dO) (one scale per tensor), s = 1 / S
+ *   D_i = sum_d dO^_id O_id
+ *   P   = 2^(t - LSE log2 e), t = sigma log2(e) g_q g_k Q_raw . K_raw (as in the forward)
+ *   dP  = dO^ V^T,  dS = P (dP - D)
+ *   dV  = P~^T dO^, dK = sigma dS~^T Q^, dQ = sigma dS~ K^
+ * with Q^ = Q_raw g_q, K^ = K_raw g_k the exact NVFP4 values, V^ the FP8
+ * values, and P~, dS~ rounded to E4M3 with one E8M0 exponent per 32 elements
+ * along the contraction axis of their product (OCP MX rule, e = floor(log2
+ * amax) - 8): along queries for dV and dK, along keys for dQ.  GQA sums the
+ * query heads of a group into dK and dV.  Causal: key j is visible to query
+ * i iff j <= i.
+ *
+ * Dense batches only (Nq == Nk == N).  D in {64, 128}; Hq % Hkv == 0.
+ *   q, k   : the forward's NVFP4 operands (attn_quant_nvfp4 output)
+ *   v      : the forward's FP8 V (attn_quant_v, ATTN_V_FP8_E4M3; MXFP4 V is
+ *            ATTN_ERR_UNSUPPORTED)
+ *   o      : bf16 [B, N, Hq, D], the forward output
+ *   lse    : float [B, Hq, N], the forward LSE (natural log)
+ *   dout   : bf16 [B, N, Hq, D]
+ *   dq     : float [B, N, Hq, D];  dk, dv : float [B, N, Hkv, D] (written)
+ *   ws     : attn_bwd_ws_bytes(args) bytes, 256-byte aligned: the prepared
+ *            operands (bf16 Q^/K^ row-major and transposed, E5M2 dO^ both
+ *            ways, key-major V codes, D and LSE log2 e per row)
+ * Argument errors are found before any launch.  prof_event_begin/end
+ * (hipEvent_t, nullable) are recorded around the dK/dV and dQ kernels.
+ */
+typedef struct attn_bwd_args {
+  int32_t B, Hq, Hkv, N, D;
+  float softmax_scale;
+  int32_t causal;
+  attn_nvfp4_tensor q;
+  attn_nvfp4_tensor k;
+  attn_v_tensor v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  float* dq;
+  float* dk;
+  float* dv;
+  void* ws;
+  size_t ws_bytes;
+  /* Optional dump of the E4M3 operands of one (batch dbg_b, query head
+   * dbg_h), each buffer caller-allocated and zero-filled, NPAD = roundup(N,
+   * 128): P~ and dS~K codes [NPAD, NPAD] (query row, key column) with their
+   * E8M0 bytes [NPAD/32, NPAD] (32-query block, key); dS~Q codes [NPAD, NPAD]
+   * with E8M0 bytes [NPAD, NPAD/32] (query, 32-key block).  All six NULL
+   * disables the dump; otherwise all six must be given. */
+  uint8_t* dbg_p_codes;
+  uint8_t* dbg_p_exps;
+  uint8_t* dbg_dsk_codes;
+  uint8_t* dbg_dsk_exps;
+  uint8_t* dbg_dsq_codes;
+  uint8_t* dbg_dsq_exps;
+  int32_t dbg_b, dbg_h;
+  void* prof_event_begin;
+  void* prof_event_end;
+} attn_bwd_args;
+
+size_t attn_bwd_ws_bytes(const attn_bwd_args* a);
+attn_status attn_bwd_fp8(const attn_bwd_args* a, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -84,8 +84,16 @@ def mx_e4m3(x, axis):
     return np.moveaxis(deq, -1, axis), np.moveaxis(codes, -1, axis), np.moveaxis(e, -1, axis)
 
 
+def _given_values(codes, exps, axis):
+    """E4M3 codes times 2^e with the E8M0 bytes ``exps`` (e + 127) repeated
+    over the 32-element blocks of ``axis``."""
+    e = np.repeat(np.asarray(exps, np.int64) - 127, MX_BLOCK, axis=axis)
+    e = e[:, :codes.shape[1]] if axis == 1 else e[:codes.shape[0], :]
+    return e4m3_decode(codes) * np.exp2(e)
+
+
 def attn_bwd_head(q_raw, k_raw, gq, gk, v_hat, o, do_hat, lse, sigma, causal=False,
-                  q_rows=None, k_rows=None, quantize=True):
+                  q_rows=None, k_rows=None, quantize=True, given=None, return_pre=False):
     """Backward of one (batch, head) for a sequence of Nq queries and Nk keys.
 
     q_raw [Nq, D], k_raw [Nk, D]: exact NVFP4 values without tensor scales;
@@ -94,6 +102,17 @@ def attn_bwd_head(q_raw, k_raw, gq, gk, v_hat, o, do_hat, lse, sigma, causal=Fal
     q_rows / k_rows select the query rows of dQ and the key rows of dK, dV
     (default all); each needs every key / query, which the function computes.
     Returns (dQ [len(q_rows), D], dK [len(k_rows), D], dV [len(k_rows), D]).
+
+    Hooks for checking an implementation whose float32 arithmetic may round a
+    value lying on an E4M3 boundary the other way:
+    given       dict with any of "ds_q" (codes [len(q_rows), Nk], E8M0 bytes
+                [len(q_rows), ceil(Nk/32)]), "p_t" and "ds_k" (codes [Nq,
+                len(k_rows)], E8M0 bytes [ceil(Nq/32), len(k_rows)]): use
+                these instead of rounding; every other step is unchanged
+    return_pre  also return a dict of intermediates: for "q" (the dQ rows)
+                and "k" (the dK/dV columns) the exact P, dS, the codes and
+                exponents, and the magnitude sums |Q_raw|.|K_raw|, |dO^|.|V^|
+                and |dO^|.|O| (for error bounds of float32 sums)
     """
     q_raw = np.asarray(q_raw, np.float64)
     k_raw = np.asarray(k_raw, np.float64)
@@ -117,19 +136,42 @@ def attn_bwd_head(q_raw, k_raw, gq, gk, v_hat, o, do_hat, lse, sigma, causal=Fal
             p = np.where(kj[None, :] <= qi[:, None], p, 0.0)
         return p
 
+    given = given or {}
+    pre = {}
     # dQ rows: all keys, MX blocks along keys (per query row)
     kall = np.arange(Nk)
     p = probs(q_rows, kall)
     ds = p * (do_hat[q_rows] @ v_hat.T - D_[q_rows][:, None])
-    ds_q = mx_e4m3(ds, axis=1)[0] if quantize else ds
+    ds_q = ds
+    if quantize:
+        ds_q, cq, eq = mx_e4m3(ds, axis=1)
+        if "ds_q" in given:
+            ds_q = _given_values(*given["ds_q"], axis=1)
+        if return_pre:
+            pre["q"] = dict(p=p, ds=ds, codes=cq, exps=eq + 127, D=D_[q_rows], abs_D=np.abs(do_hat * o).sum(1)[q_rows],
+                            abs_qk=c * (np.abs(q_raw[q_rows]) @ np.abs(k_raw).T),
+                            abs_dpv=np.abs(do_hat[q_rows]) @ np.abs(v_hat).T, lse2=L[q_rows])
     dq = sigma * (ds_q @ k_hat)
 
     # dK, dV rows: all queries, MX blocks along queries (per key column)
     qall = np.arange(Nq)
     p = probs(qall, k_rows)
     ds = p * (do_hat @ v_hat[k_rows].T - D_[:, None])
-    p_t = mx_e4m3(p, axis=0)[0] if quantize else p
-    ds_k = mx_e4m3(ds, axis=0)[0] if quantize else ds
+    p_t, ds_k = p, ds
+    if quantize:
+        p_t, cp, ep = mx_e4m3(p, axis=0)
+        ds_k, ck, ek = mx_e4m3(ds, axis=0)
+        if "p_t" in given:
+            p_t = _given_values(*given["p_t"], axis=0)
+        if "ds_k" in given:
+            ds_k = _given_values(*given["ds_k"], axis=0)
+        if return_pre:
+            pre["k"] = dict(p=p, ds=ds, codes_p=cp, exps_p=ep + 127, codes_ds=ck, exps_ds=ek + 127, D=D_,
+                            abs_D=np.abs(do_hat * o).sum(1),
+                            abs_qk=c * (np.abs(q_raw) @ np.abs(k_raw[k_rows]).T),
+                            abs_dpv=np.abs(do_hat) @ np.abs(v_hat[k_rows]).T, lse2=L)
     dv = p_t.T @ do_hat
     dk = sigma * (ds_k.T @ q_hat)
+    if return_pre:
+        return dq, dk, dv, pre
     return dq, dk, dv

@@ -52,6 +52,23 @@ class FwdArgs(ctypes.Structure):
     ]
 
 
+class BwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("N", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32),
+        ("q", _NvTensor), ("k", _NvTensor), ("v", _VTensor),
+        ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("dout", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
+        ("dbg_p_codes", ctypes.c_void_p), ("dbg_p_exps", ctypes.c_void_p),
+        ("dbg_dsk_codes", ctypes.c_void_p), ("dbg_dsk_exps", ctypes.c_void_p),
+        ("dbg_dsq_codes", ctypes.c_void_p), ("dbg_dsq_exps", ctypes.c_void_p),
+        ("dbg_b", ctypes.c_int32), ("dbg_h", ctypes.c_int32),
+        ("prof_event_begin", ctypes.c_void_p), ("prof_event_end", ctypes.c_void_p),
+    ]
+
+
 EXPORTS = {
     "attn_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "attn_last_hip_error": (ctypes.c_int, []),
@@ -72,6 +89,8 @@ EXPORTS = {
     "attn_fwd_fp8pv": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "attn_fwd_directp_efq": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "attn_fwd_fp8pv_cast": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
+    "attn_bwd_ws_bytes": (ctypes.c_size_t, [ctypes.POINTER(BwdArgs)]),
+    "attn_bwd_fp8": (ctypes.c_int, [ctypes.POINTER(BwdArgs), ctypes.c_void_p]),
     "attn_fwd_bf16": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
@@ -280,6 +299,59 @@ def fwd_directp_efq(q, k, v, **kw):
 def fwd_fp8pv_cast(q, k, v, **kw):
     """Exp-free FP8-P/V: E4M3 codes by the one-FMA log-linear cast (causal allowed)."""
     return _fwd_lowp("attn_fwd_fp8pv_cast", q, k, v, **kw)
+
+
+def bwd_fp8(q, k, v, o, lse, dout, *, softmax_scale, causal=True, workspace=None, events=None, debug=None):
+    """Backward of the FP8-P/V forward on its saved quantized operands.
+    q, k: (codes, scales, tensor_scale) from quant_nvfp4; v: (V_FP8, codes,
+    None, tensor_scale) from quant_v; o: bf16 [B, N, Hq, D] forward output;
+    lse: float32 [B, Hq, N]; dout: bf16 [B, N, Hq, D].  Returns float32
+    (dq [B, N, Hq, D], dk [B, N, Hkv, D], dv [B, N, Hkv, D]) and, with
+    ``debug=(b, h)``, a dict of the E4M3 operand dumps of that (batch, query
+    head) as a fourth element."""
+    lib = load_library()
+    _need_cuda(o, lse, dout, q[0], k[0], v[1])
+    if o.dtype != torch.bfloat16 or dout.dtype != torch.bfloat16 or lse.dtype != torch.float32:
+        raise AttnError("bwd_fp8 expects bf16 o/dout and float32 lse")
+    B, N, Hq, D = dout.shape
+    Hkv = k[0].shape[-2]
+    dev = dout.device
+    dq = torch.empty((B, N, Hq, D), dtype=torch.float32, device=dev)
+    dk = torch.empty((B, N, Hkv, D), dtype=torch.float32, device=dev)
+    dv = torch.empty((B, N, Hkv, D), dtype=torch.float32, device=dev)
+    a = BwdArgs()
+    a.B, a.Hq, a.Hkv, a.N, a.D = B, Hq, Hkv, N, D
+    a.softmax_scale = softmax_scale
+    a.causal = 1 if causal else 0
+    a.q = _NvTensor(q[0].data_ptr(), q[1].data_ptr(), q[2].data_ptr())
+    a.k = _NvTensor(k[0].data_ptr(), k[1].data_ptr(), k[2].data_ptr())
+    a.v = _VTensor(v[0], v[1].data_ptr(), None if v[2] is None else v[2].data_ptr(),
+                   None if v[3] is None else v[3].data_ptr())
+    a.o, a.lse, a.dout = o.data_ptr(), lse.data_ptr(), dout.data_ptr()
+    a.dq, a.dk, a.dv = dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    dumps = None
+    if debug is not None:
+        npad = (N + 127) // 128 * 128
+        dumps = {"p_codes": torch.zeros((npad, npad), dtype=torch.uint8, device=dev),
+                 "p_exps": torch.zeros((npad // 32, npad), dtype=torch.uint8, device=dev),
+                 "dsk_codes": torch.zeros((npad, npad), dtype=torch.uint8, device=dev),
+                 "dsk_exps": torch.zeros((npad // 32, npad), dtype=torch.uint8, device=dev),
+                 "dsq_codes": torch.zeros((npad, npad), dtype=torch.uint8, device=dev),
+                 "dsq_exps": torch.zeros((npad, npad // 32), dtype=torch.uint8, device=dev)}
+        a.dbg_p_codes, a.dbg_p_exps = dumps["p_codes"].data_ptr(), dumps["p_exps"].data_ptr()
+        a.dbg_dsk_codes, a.dbg_dsk_exps = dumps["dsk_codes"].data_ptr(), dumps["dsk_exps"].data_ptr()
+        a.dbg_dsq_codes, a.dbg_dsq_exps = dumps["dsq_codes"].data_ptr(), dumps["dsq_exps"].data_ptr()
+        a.dbg_b, a.dbg_h = debug
+    need = lib.attn_bwd_ws_bytes(ctypes.byref(a))
+    ws = (workspace or _default_ws).get(need, dev)
+    a.ws, a.ws_bytes = ws.data_ptr(), ws.numel()
+    if events is not None:
+        a.prof_event_begin = events[0].cuda_event
+        a.prof_event_end = events[1].cuda_event
+    _check(lib.attn_bwd_fp8(ctypes.byref(a), _stream()))
+    if debug is not None:
+        return dq, dk, dv, dumps
+    return dq, dk, dv
 
 
 def fwd_bf16(q, k, v, softmax_scale, causal=False, want_lse=True):

@@ -1,6 +1,7 @@
 // C ABI of the Direct-P FP4 attention library (declared in include/attn_fp4.h).
 // Host-side argument validation and launch sequencing only; every step of the
-// computation runs in the HIP kernels of quant.hip, fwd_lowp.hip and fwd_bf16.hip.
+// computation runs in the HIP kernels of quant.hip, fwd_lowp.hip, fwd_bf16.hip
+// and bwd.hip.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -23,9 +24,18 @@ hipError_t launch_fwd_lowp(const FwdParams& p, int D, int pf, int vf, bool causa
                            hipStream_t st);
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                            int Nq, int Nk, int D, float sigma, bool causal, hipStream_t st);
+hipError_t launch_bwd_prep(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
+                           const uint8_t* k_scales, const uint8_t* v_codes, int64_t v_cols, const void* dout,
+                           const void* o, const float* lse, const float* partials, int np, int B, int Hq, int Hkv,
+                           int N, int D, int64_t npad, __bf16* qrm, __bf16* qt, __bf16* krm, __bf16* kt,
+                           uint8_t* vrm, uint8_t* drm, uint8_t* dtr, float* dvec, float* lvec, float* sdo,
+                           hipStream_t st);
+struct BwdParams;
+hipError_t launch_bwd_main(const BwdParams& p, int D, bool causal, bool debug, hipStream_t st);
 }  // namespace attn
 
 #include "fwd_params.h"
+#include "bwd_params.h"
 
 using namespace attn;
 
@@ -241,4 +251,117 @@ attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, 
                                     (hipStream_t)stream));
 }
 
+
+// ---- backward -------------------------------------------------------------
+struct BwdLayout {
+  int64_t npad, qrm, qt, krm, kt, vrm, drm, dtr, dvec, lvec, sdo, partials, total;
+};
+
+static bool bwd_shapes_ok(const attn_bwd_args* a) {
+  return a != nullptr && a->B >= 0 && a->N >= 0 && a->Hq > 0 && a->Hkv > 0 && a->Hq % a->Hkv == 0 &&
+         (a->D == 64 || a->D == 128);
+}
+
+static BwdLayout bwd_layout(const attn_bwd_args* a) {
+  BwdLayout L;
+  auto al = [](int64_t x) { return (x + 255) / 256 * 256; };
+  L.npad = roundup(a->N, 128);
+  const int64_t nq = (int64_t)a->B * a->Hq * L.npad * a->D, nk = (int64_t)a->B * a->Hkv * L.npad * a->D;
+  int64_t off = 0;
+  L.qrm = off; off += al(2 * nq);
+  L.qt = off; off += al(2 * nq);
+  L.krm = off; off += al(2 * nk);
+  L.kt = off; off += al(2 * nk);
+  L.vrm = off; off += al(nk);
+  L.drm = off; off += al(nq);
+  L.dtr = off; off += al(nq);
+  L.dvec = off; off += al(4 * (int64_t)a->B * a->Hq * L.npad);
+  L.lvec = off; off += al(4 * (int64_t)a->B * a->Hq * L.npad);
+  L.sdo = off; off += 256;
+  L.partials = off; off += (int64_t)QUANT_WS;
+  L.total = off;
+  return L;
+}
+
+size_t attn_bwd_ws_bytes(const attn_bwd_args* a) {
+  if (!bwd_shapes_ok(a)) return 0;
+  return (size_t)bwd_layout(a).total + 256;
+}
+
+attn_status attn_bwd_fp8(const attn_bwd_args* a, void* stream) {
+  if (!bwd_shapes_ok(a) || !(a->softmax_scale > 0.0f)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (a->v.format != ATTN_V_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
+  if (a->N > 0) {
+    const void* need[] = {a->q.codes, a->q.scales, a->q.tensor_scale, a->k.codes, a->k.scales, a->k.tensor_scale,
+                          a->v.codes, a->v.tensor_scale, a->o, a->lse, a->dout, a->dq, a->dk, a->dv};
+    for (const void* x : need)
+      if (x == nullptr) return ATTN_ERR_INVALID_ARGUMENT;
+    if (!aligned(a->o, 16) || !aligned(a->dout, 16) || !aligned(a->q.codes, 4) || !aligned(a->k.codes, 4) ||
+        !aligned(a->v.codes, 16) || !aligned(a->lse, 4) || !aligned(a->dq, 4) || !aligned(a->dk, 4) ||
+        !aligned(a->dv, 4))
+      return ATTN_ERR_INVALID_ARGUMENT;
+  }
+  const uint8_t* dumps[] = {a->dbg_p_codes, a->dbg_p_exps, a->dbg_dsk_codes, a->dbg_dsk_exps, a->dbg_dsq_codes,
+                           a->dbg_dsq_exps};
+  int ndump = 0;
+  for (const uint8_t* x : dumps) ndump += x != nullptr;
+  const bool debug = ndump == 6;
+  if (ndump != 0 && (!debug || a->dbg_b < 0 || a->dbg_b >= a->B || a->dbg_h < 0 || a->dbg_h >= a->Hq))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  const BwdLayout L = bwd_layout(a);
+  if (a->ws == nullptr || a->ws_bytes < (size_t)L.total || !aligned(a->ws, 256)) return ATTN_ERR_WORKSPACE;
+  if (a->N == 0 || a->B == 0) return ATTN_OK;
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* w = (uint8_t*)a->ws;
+  int np = 0;
+  float* partials = (float*)(w + L.partials);
+  hipError_t e = launch_amax(a->dout, (int64_t)a->B * a->N * a->Hq * a->D, partials, &np, st);
+  if (e != hipSuccess) return hip_status(e);
+  float* sdo = (float*)(w + L.sdo);
+  e = launch_bwd_prep(a->q.codes, a->q.scales, a->k.codes, a->k.scales, a->v.codes, (int64_t)a->B * L.npad, a->dout,
+                      a->o, a->lse, partials, np, a->B, a->Hq, a->Hkv, a->N, a->D, L.npad, (__bf16*)(w + L.qrm),
+                      (__bf16*)(w + L.qt), (__bf16*)(w + L.krm), (__bf16*)(w + L.kt), w + L.vrm, w + L.drm,
+                      w + L.dtr, (float*)(w + L.dvec), (float*)(w + L.lvec), sdo, st);
+  if (e != hipSuccess) return hip_status(e);
+  BwdParams p;
+  memset(&p, 0, sizeof(p));
+  p.qrm = (const __bf16*)(w + L.qrm);
+  p.qt = (const __bf16*)(w + L.qt);
+  p.krm = (const __bf16*)(w + L.krm);
+  p.kt = (const __bf16*)(w + L.kt);
+  p.vrm = w + L.vrm;
+  p.dorm = w + L.drm;
+  p.dot = w + L.dtr;
+  p.lv = (const float*)(w + L.lvec);
+  p.dv = (const float*)(w + L.dvec);
+  p.gq = a->q.tensor_scale;
+  p.gk = a->k.tensor_scale;
+  p.sv = a->v.tensor_scale;
+  p.sdo = sdo;
+  p.dq_out = a->dq;
+  p.dk_out = a->dk;
+  p.dv_out = a->dv;
+  p.B = a->B;
+  p.Hq = a->Hq;
+  p.Hkv = a->Hkv;
+  p.N = a->N;
+  p.npad = L.npad;
+  p.sigma = a->softmax_scale;
+  p.dbg_pt = a->dbg_p_codes;
+  p.dbg_pt_e = a->dbg_p_exps;
+  p.dbg_dsk = a->dbg_dsk_codes;
+  p.dbg_dsk_e = a->dbg_dsk_exps;
+  p.dbg_dsq = a->dbg_dsq_codes;
+  p.dbg_dsq_e = a->dbg_dsq_exps;
+  p.dbg_b = a->dbg_b;
+  p.dbg_h = a->dbg_h;
+  if (a->prof_event_begin != nullptr) {
+    e = hipEventRecord((hipEvent_t)a->prof_event_begin, st);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  e = launch_bwd_main(p, a->D, a->causal != 0, debug, st);
+  if (e != hipSuccess) return hip_status(e);
+  if (a->prof_event_end != nullptr) e = hipEventRecord((hipEvent_t)a->prof_event_end, st);
+  return hip_status(e);
+}
 }  // extern "C"

@@ -145,3 +145,76 @@ def check_code_choices(gc, ge, oc, oe, pre, xmax, p_format, encoder, live):
         assert not bad.any(), (f"{int(bad.sum())} codes differ away from a rounding boundary, e.g. at {where}: "
                                f"kernel {g[bad][:5].tolist()} oracle {o[bad][:5].tolist()} value {v[bad][:5].tolist()}")
     return n_e, n_c
+
+
+# ---- backward: E4M3 operands decided in float32 --------------------------
+# The kernel computes P = 2^(t - L) and dS = P (dP - D) in float32.  Error
+# sources, each bounded by a multiple of the sum of the magnitudes of its
+# terms (measured on gfx950):
+#  * t = c Q.K on the bf16 MFMA: products exact, sums keep 24 bits below the
+#    largest product -> 2^-20 of |c| sum |Q||K|;
+#  * dP = dO^.V^ on the FP8 MFMA: each group of 8 products is aligned to its
+#    largest product and truncated 15 bits below it -> 2^-11 of sum |dO^||V^|;
+#  * D: a float32 sum over D terms -> 2^-20 of sum |dO^ O|;
+# and dP - D cancels, which divides by |dP - D|.  A code that differs from
+# the oracle's is accepted when it is the E4M3 rounding of some value within
+# BWD_TIE_FACTOR times that bound of the exact value.
+BWD_TIE_FACTOR = 4.0
+BWD_MISMATCH_MAX = 1e-2      # fraction of live codes that may differ (plus 2)
+
+
+def _bwd_rel_err(abs_t, lse2, ds=None, p=None, abs_dpv=None, abs_D=None):
+    """Relative float32 error bound of P (and of dS when ds is given)."""
+    eps = math.log(2.0) * 2.0 ** -20 * (abs_t + np.abs(lse2)) + 2.0 ** -20
+    if ds is not None:
+        with np.errstate(divide="ignore", invalid="ignore"):
+            diff = np.where(p > 0, np.abs(ds) / np.where(p > 0, p, 1.0), np.inf)
+            eps = eps + (2.0 ** -11 * abs_dpv + 2.0 ** -20 * abs_D) / diff + 2.0 ** -20
+    return eps
+
+
+def check_bwd_codes(gc, ge, x, oc, oe, eps, axis, live, what=""):
+    """Kernel E4M3 codes gc with E8M0 bytes ge (blocks of 32 along ``axis``)
+    against the oracle's (oc, oe) for exact values x with relative error
+    bounds eps.  Exponents may differ only where the block max is within its
+    error of a power of two; codes only at rounding near-ties.  Returns the
+    number of differing live codes."""
+    gc = np.asarray(gc); oc = np.asarray(oc)
+    rep = lambda e: np.repeat(np.asarray(e, np.int64), 32, axis=axis)[:x.shape[0], :x.shape[1]]
+    eg, eo = rep(ge) - 127, rep(oe) - 127
+    de = (eg != eo) & live
+    if de.any():
+        # the block's largest magnitude must sit on the power of two that separates the exponents
+        amax = np.abs(x)
+        lim = np.ldexp(1.0, np.maximum(eg, eo) + 8)
+        ok = (np.abs(eg - eo) == 1) & (np.abs(amax - lim) <= BWD_TIE_FACTOR * eps * lim)
+        blk_ok = np.zeros_like(de)
+        # a block passes if some live element of it is that near-boundary maximum
+        n = x.shape[axis]
+        for b0 in range(0, n, 32):
+            sl = (slice(b0, b0 + 32), slice(None)) if axis == 0 else (slice(None), slice(b0, b0 + 32))
+            any_ok = (ok[sl] & live[sl]).any(axis=axis, keepdims=True)
+            blk_ok[sl] = np.broadcast_to(any_ok, blk_ok[sl].shape)
+        bad = de & ~blk_ok
+        assert not bad.any(), f"{what}: E8M0 exponents differ away from a boundary at {np.argwhere(bad)[:4].tolist()}"
+    y = x * np.exp2(-eg.astype(np.float64))
+    ref = np.where(live, OF.e4m3_encode(np.clip(np.where(live, y, 0.0), -448, 448)), 0)
+    gval, rval = OF.e4m3_decode(gc), OF.e4m3_decode(ref)
+    diff = (gval != rval) & live
+    n_diff = int(diff.sum())
+    if n_diff:
+        # the kernel's code must be the rounding of some value within the error
+        # bound of the exact one: rounding is monotone, so its value must lie
+        # between the roundings of the interval's ends
+        half = BWD_TIE_FACTOR * np.where(np.isfinite(eps), eps, 1e30) * np.abs(y)
+        ends = [OF.e4m3_decode(OF.e4m3_encode(np.clip(np.where(live, y + sgn * half, 0.0), -448, 448)))
+                for sgn in (-1.0, 1.0)]
+        near = (gval >= np.minimum(*ends)) & (gval <= np.maximum(*ends))
+        bad = diff & ~near
+        where = np.argwhere(bad)[:4].tolist()
+        assert not bad.any(), (f"{what}: {int(bad.sum())} E4M3 codes lie outside the rounding of the float32 error "
+                               f"interval, e.g. at {where}: kernel {gc[bad][:4].tolist()} oracle "
+                               f"{ref[bad][:4].tolist()} scaled value {y[bad][:4].tolist()} relative error bound "
+                               f"{eps[bad][:4].tolist()}")
+    assert n_diff <= BWD_MISMATCH_MAX * int(live.sum()) + 2, f"{what}: {n_diff} of {int(live.sum())} codes differ"
+    return n_diff

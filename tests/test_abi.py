@@ -40,6 +40,34 @@ def test_struct_layout_matches_header():
     assert ctypes.sizeof(B.FwdArgs) == 4 * 6 + 8 * 2 + 8 * 2 + 4 + 4 + 24 * 2 + 32 + 8 + 4 + 4 + 8 + 8 + 8 + 8 + 8 + 4 + 4 + 8 + 8
 
 
+def _c_offsets(struct, fields):
+    """sizeof and offsetof of a header struct, from a C program compiled with gcc."""
+    import shutil
+    import subprocess
+    import tempfile
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    lines = [f'printf("%zu\\n", sizeof({struct}));']
+    lines += [f'printf("%zu\\n", offsetof({struct}, {f}));' for f in fields]
+    src = "#include <stddef.h>\n#include <stdio.h>\n#include \"attn_fp4.h\"\nint main(void) {\n" + "\n".join(lines) + "\nreturn 0; }\n"
+    with tempfile.TemporaryDirectory() as d:
+        c, exe = os.path.join(d, "t.c"), os.path.join(d, "t")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-I", inc, c, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()
+    return [int(x) for x in out]
+
+
+@pytest.mark.parametrize("cls,cname", [(B.FwdArgs, "attn_fwd_args"), (B.BwdArgs, "attn_bwd_args")])
+def test_ctypes_struct_matches_c_layout(cls, cname):
+    fields = [f for f, _ in cls._fields_]
+    got = _c_offsets(cname, fields)
+    assert got[0] == ctypes.sizeof(cls)
+    for f, off in zip(fields, got[1:]):
+        assert getattr(cls, f).offset == off, f
+
+
 def test_status_strings_and_constants(lib):
     assert lib.attn_status_str(0) == b"ok"
     assert lib.attn_status_str(1) == b"invalid argument"
@@ -119,6 +147,21 @@ def test_fwd_validation(lib):
                                                       ws_bytes=need)), None) == 2
     assert lib.attn_fwd_fp8pv_cast(ctypes.byref(_args(causal=1, Nk=128, ws=1 << 24, ws_bytes=need)), None) == 1
     assert lib.attn_fwd_fp8pv_cast(None, None) == 1
+    # backward: shapes, V format, workspace
+    bw = B.BwdArgs()
+    bw.B, bw.Hq, bw.Hkv, bw.N, bw.D, bw.softmax_scale, bw.causal = 2, 4, 2, 256, 128, 0.1, 1
+    need_b = lib.attn_bwd_ws_bytes(ctypes.byref(bw))
+    assert need_b > 2 * (2 * 4 * 256 * 128 * 2) + 2 * (2 * 2 * 256 * 128 * 2)
+    bw.D = 96
+    assert lib.attn_bwd_ws_bytes(ctypes.byref(bw)) == 0 and lib.attn_bwd_fp8(ctypes.byref(bw), None) == 1
+    bw.D, bw.Hkv = 128, 3
+    assert lib.attn_bwd_fp8(ctypes.byref(bw), None) == 1
+    bw.Hkv = 2
+    bw.v = B._VTensor(1, 1 << 24, 1 << 24, 1 << 24)
+    assert lib.attn_bwd_fp8(ctypes.byref(bw), None) == 2
+    bw.v = B._VTensor(0, 1 << 24, None, 1 << 24)
+    assert lib.attn_bwd_fp8(ctypes.byref(bw), None) == 1          # null operand pointers
+    assert lib.attn_bwd_fp8(None, None) == 1
     # varlen needs both cu_seqlens
     assert lib.attn_fwd_directp(ctypes.byref(_args(cu_seqlens_q=1 << 24, ws=1 << 24, ws_bytes=need)), None) == 1
     # bf16 baseline argument checks

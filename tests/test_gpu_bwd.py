@@ -1,0 +1,175 @@
+"""GPU backward (attn_bwd_fp8) vs the oracle on the same seeded inputs.
+
+The backward takes the forward's quantized Q/K/V, its output O and LSE, and
+dO.  O and LSE are inputs here: they are computed as textbook float32
+attention on the bf16 inputs with torch operations (never with this
+library's kernels), and both sides receive the same values.
+
+Bar: every E4M3 code of P~ / dS~ equals the oracle's except at float32
+near-ties (checked element by element on the dump of the kernel's codes);
+then, against the oracle run on the kernel's codes, each of dQ, dK, dV per
+(batch, head) within relative L2 1e-3 and max abs 1e-3 of the reference's
+largest magnitude (the rest is float32 against float64 arithmetic).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import _bwd_rel_err, check_bwd_codes, f32
+from oracle import backward as OB
+from oracle import quant as OQ
+from precision_attention_forward_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 1e-3
+MAX_ABS_REL = 1e-3
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _attention_o_lse(q, k, v, sigma, causal, device):
+    """Textbook attention in float32 per (batch, head) with torch: O (bf16
+    [B, N, Hq, D]) and LSE (float32 [B, Hq, N])."""
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    o = torch.empty((B, N, Hq, D), dtype=torch.bfloat16, device=device)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=device)
+    mask = torch.ones((N, N), dtype=torch.bool, device=device).tril() if causal else None
+    for b in range(B):
+        for h in range(Hq):
+            qh = q[b, :, h].to(device, torch.float32).contiguous()
+            kh = k[b, :, h // G].to(device, torch.float32).contiguous()
+            vh = v[b, :, h // G].to(device, torch.float32).contiguous()
+            s = sigma * (qh @ kh.T.contiguous())
+            if causal:
+                s = s.masked_fill(~mask, float("-inf"))
+            l = torch.logsumexp(s, dim=1)
+            o[b, :, h] = (torch.exp(s - l[:, None]) @ vh).to(torch.bfloat16)
+            lse[b, h] = l
+    return o, lse
+
+
+def _amax(x, chunk=1 << 26):
+    flat = x.reshape(-1)
+    return max(float(flat[i:i + chunk].to("cpu").abs().max()) for i in range(0, flat.numel(), chunk))
+
+
+def _check_close(got, ref, what):
+    den = np.linalg.norm(ref)
+    rel = float(np.linalg.norm(got - ref) / den) if den > 0 else float(np.abs(got).max())
+    mx = float(np.abs(got - ref).max()) if ref.size else 0.0
+    top = float(np.abs(ref).max()) if ref.size else 0.0
+    assert rel <= REL_L2, f"{what}: rel L2 {rel:.3e}"
+    assert mx <= MAX_ABS_REL * max(top, 1e-30), f"{what}: max abs {mx:.3e} (ref max {top:.3e})"
+    return rel
+
+
+def _run(gpu, wl, q_rows=None, k_rows=None, heads=None, batches=None, seed_do=0):
+    """Generate inputs, run the production backward once, then per compared
+    (batch, query head) the build with the E4M3 operand dump, which must
+    reproduce the production outputs bit for bit.  Every dumped code that
+    differs from the oracle's must be a float32 near-tie
+    (helpers.check_bwd_codes); dQ / dK / dV are then compared with the oracle
+    run on the kernel's codes."""
+    inp = synth.generate(wl, "cuda")
+    B, N, Hq, D = inp.q.shape
+    Hkv = inp.k.shape[2]
+    G = Hq // Hkv
+    gen = torch.Generator().manual_seed(seed_do + wl.seed)
+    dout = torch.randn((B, N, Hq, D), generator=gen).to(torch.bfloat16).cuda()
+    o, lse = _attention_o_lse(inp.q, inp.k, inp.v, inp.sigma, wl.causal, "cuda")
+    qq = gpu.quant_nvfp4(inp.q)
+    kq = gpu.quant_nvfp4(inp.k)
+    vc, vs, vt, _ = gpu.quant_v(inp.v, gpu.V_FP8)
+    args = (qq, kq, (gpu.V_FP8, vc, None, vt), o, lse, dout)
+    kw = dict(softmax_scale=inp.sigma, causal=wl.causal)
+    dq, dk, dv = gpu.bwd_fp8(*args, **kw)
+    torch.cuda.synchronize()
+    amax_q, amax_k, amax_v, amax_do = _amax(inp.q), _amax(inp.k), _amax(inp.v), _amax(dout)
+    worst, n_ties, n_live = 0.0, 0, 0
+    qr = np.arange(N) if q_rows is None else np.asarray(sorted(set(int(x) for x in q_rows if x < N)))
+    kr = np.arange(N) if k_rows is None else np.asarray(sorted(set(int(x) for x in k_rows if x < N)))
+    nb = (N + 31) // 32
+    for b in (range(B) if batches is None else batches):
+        for hk in (range(Hkv) if heads is None else sorted({h // G for h in heads})):
+            kc, ks, gk = OQ.quant_nvfp4(f32(inp.k[b, :, hk]), amax=amax_k)
+            k_raw = OQ.dequant_nvfp4_raw(kc, ks)
+            vcod, s_v = OQ.quant_v_fp8(f32(inp.v[b, :, hk]), amax=amax_v)
+            v_hat = OQ.dequant_v_fp8(vcod, s_v)
+            dk_ref = np.zeros((len(kr), D))
+            dv_ref = np.zeros((len(kr), D))
+            for h in range(hk * G, hk * G + G):
+                d2q, d2k, d2v, dump = gpu.bwd_fp8(*args, debug=(b, h), **kw)
+                assert torch.equal(d2q, dq) and torch.equal(d2k, dk) and torch.equal(d2v, dv), \
+                    "the dump build computes other gradients"
+                qc, qs, gq = OQ.quant_nvfp4(f32(inp.q[b, :, h]), amax=amax_q)
+                q_raw = OQ.dequant_nvfp4_raw(qc, qs)
+                dcodes, s_do = OB.quant_do_e5m2(f32(dout[b, :, h]), amax=amax_do)
+                do_hat = OB.dequant_do_e5m2(dcodes, s_do)
+                bargs = (q_raw, k_raw, gq, gk, v_hat, f32(o[b, :, h]), do_hat, f32(lse[b, h]), inp.sigma, wl.causal)
+                *_, pre = OB.attn_bwd_head(*bargs, q_rows=qr, k_rows=kr, return_pre=True)
+                pq, pk = pre["q"], pre["k"]
+                gsel = torch.as_tensor(qr, device="cuda")
+                ksel = torch.as_tensor(kr, device="cuda")
+                g_dsq = (dump["dsq_codes"][gsel][:, :N].cpu().numpy(), dump["dsq_exps"][gsel][:, :nb].cpu().numpy())
+                g_pt = (dump["p_codes"][:N][:, ksel].cpu().numpy(), dump["p_exps"][:nb][:, ksel].cpu().numpy())
+                g_dsk = (dump["dsk_codes"][:N][:, ksel].cpu().numpy(), dump["dsk_exps"][:nb][:, ksel].cpu().numpy())
+                live_q, live_k = pq["p"] > 0, pk["p"] > 0
+                eps_q = _bwd_rel_err(pq["abs_qk"], pq["lse2"][:, None], pq["ds"], pq["p"], pq["abs_dpv"],
+                                     pq["abs_D"][:, None])
+                eps_kp = _bwd_rel_err(pk["abs_qk"], pk["lse2"][:, None])
+                eps_kd = _bwd_rel_err(pk["abs_qk"], pk["lse2"][:, None], pk["ds"], pk["p"], pk["abs_dpv"],
+                                      pk["abs_D"][:, None])
+                n_ties += check_bwd_codes(*g_dsq, pq["ds"], pq["codes"], pq["exps"], eps_q, 1, live_q, f"dS~Q {b},{h}")
+                n_ties += check_bwd_codes(*g_pt, pk["p"], pk["codes_p"], pk["exps_p"], eps_kp, 0, live_k, f"P~ {b},{h}")
+                n_ties += check_bwd_codes(*g_dsk, pk["ds"], pk["codes_ds"], pk["exps_ds"], eps_kd, 0, live_k,
+                                          f"dS~K {b},{h}")
+                n_live += int(live_q.sum()) + 2 * int(live_k.sum())
+                rq, rk, rv = OB.attn_bwd_head(*bargs, q_rows=qr, k_rows=kr,
+                                              given={"ds_q": g_dsq, "p_t": g_pt, "ds_k": g_dsk})
+                dk_ref += rk
+                dv_ref += rv
+                if heads is None or h in heads:
+                    worst = max(worst, _check_close(f32(dq[b, gsel, h]), rq, f"dQ batch {b} head {h}"))
+            worst = max(worst, _check_close(f32(dk[b, ksel, hk]), dk_ref, f"dK batch {b} kv head {hk}"))
+            worst = max(worst, _check_close(f32(dv[b, ksel, hk]), dv_ref, f"dV batch {b} kv head {hk}"))
+    print(f"  worst rel L2 {worst:.2e}; E4M3 near-ties decided the other way: {n_ties} of {n_live} live codes",
+          flush=True)
+    return dq, dk, dv
+
+
+SMALL = [
+    ("causal_d128_gqa", synth.WORKLOADS[4].with_(B=1, Hq=2, Hkv=1, N=200, seed=81)),
+    ("causal_d64_b2", synth.WORKLOADS[4].with_(B=2, Hq=2, Hkv=2, N=130, D=64, seed=82)),
+    ("noncausal_d128", synth.WORKLOADS[4].with_(B=1, Hq=2, Hkv=2, N=300, causal=False, seed=83)),
+    ("causal_tile_edges", synth.WORKLOADS[4].with_(B=1, Hq=1, Hkv=1, N=257, seed=84)),
+]
+
+
+@pytest.mark.parametrize("name,wl", SMALL, ids=[s[0] for s in SMALL])
+def test_bwd_small_all_rows(gpu, name, wl):
+    _say(f"bwd small {name}")
+    _run(gpu, wl)
+
+
+def test_bwd_edges(gpu):
+    for N in (1, 2, 64, 65):
+        _say(f"bwd edge N={N}")
+        _run(gpu, synth.WORKLOADS[4].with_(B=1, Hq=2, Hkv=1, N=N, seed=90 + N))
+
+
+def test_bwd_full_size_sampled(gpu):
+    wl = synth.WORKLOADS[4]
+    _say(f"bwd full-size {wl.name}")
+    N = wl.N
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([rng.integers(0, N, 24), [0, 1, 127, 128, N - 1]]))
+    _run(gpu, wl, q_rows=rows, k_rows=rows, heads=[0, 31], batches=[0, wl.B - 1])
+    torch.cuda.empty_cache()
