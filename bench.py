@@ -30,14 +30,18 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=2, help="1..5 (default 2: Wan2.1-14B shape)")
+    ap.add_argument("--workload", type=int, default=None,
+                    help="1..5 (default 2: Wan2.1-14B shape; 4: Llama-3.1-8B shape with --backward)")
     ap.add_argument("--encoder", choices=("exact", "loglin"), default="exact",
                     help="probability encoder: exact (RNE of 2^y) or the exp-free log-linear cast")
     ap.add_argument("--four-six", action="store_true",
                     help="quantize Q and K with the Four Over Six adaptive block scale (attn_quant_nvfp4_46)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the causal-training backward (attn_bwd_fp8) instead of the forward; its own JSON line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=16384, help="query rows of the oracle sample")
+    ap.add_argument("--cpu-rows-bwd", type=int, default=1024, help="rows of the backward oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (HBM counter calibration) and exit")
     return ap.parse_args()
@@ -197,6 +201,116 @@ class HipEvents:
         return tot / len(self.pairs)
 
 
+def cpu_baseline_bwd(inp, dout, o, lse, rows):
+    """The oracle backward (as it stands) on a bounded sample: one (batch,
+    head), ``rows`` query rows of dQ and ``rows`` key rows of dK/dV, including
+    the quantization of the head.  Returns a dict for the JSON line."""
+    import numpy as np
+    from oracle import backward as OB, quant as OQ
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = os.cpu_count() or 1
+    wl = inp.wl
+    N = wl.N
+    qf = inp.q[0, :, 0].float().cpu().numpy()
+    kf = inp.k[0, :, 0].float().cpu().numpy()
+    vf = inp.v[0, :, 0].float().cpu().numpy()
+    df = dout[0, :, 0].float().cpu().numpy()
+    of = o[0, :, 0].float().cpu().numpy()
+    lf = lse[0, 0].float().cpu().numpy()
+    R = min(rows, N)
+    idx = np.linspace(0, N - 1, R).astype(np.int64)
+    t = time.perf_counter()
+    qc, qs, gq = OQ.quant_nvfp4(qf)
+    kc, ks, gk = OQ.quant_nvfp4(kf)
+    vcodes, s_v = OQ.quant_v_fp8(vf)
+    dcodes, s_do = OB.quant_do_e5m2(df)
+    OB.attn_bwd_head(OQ.dequant_nvfp4_raw(qc, qs), OQ.dequant_nvfp4_raw(kc, ks), gq, gk, OQ.dequant_v_fp8(vcodes, s_v),
+                     of, OB.dequant_do_e5m2(dcodes, s_do), lf, inp.sigma, wl.causal, q_rows=idx, k_rows=idx)
+    dt = time.perf_counter() - t
+    # algorithmic work of the sample: dQ rows see their visible keys, dK/dV rows their visible queries
+    vis_q = sum(min(int(i) + 1, N) for i in idx) if wl.causal else R * N
+    vis_k = sum(N - int(j) for j in idx) if wl.causal else R * N
+    flops = 2.0 * wl.D * (3 * vis_q + 4 * vis_k)   # dQ rows: S, dP, dQ; dK/dV rows: S, dP, dV, dK
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"1 head, {R} dQ rows and {R} dK/dV rows of workload {wl.name} (quantization of the head "
+                      f"included), {dt:.1f} s; numpy float64, BLAS threads = cores"}
+
+
+def backward_main(args, torch, paf, synth):
+    """One step = attn_bwd_fp8 on resident forward outputs (quantized Q/K/V,
+    O, LSE) and dO.  Flops: 5 matrix products of 2 N^2 D per (batch, head),
+    halved for causal (the usual backward count, 2.5x the forward's)."""
+    wl = synth.WORKLOADS[args.workload]
+    if wl.varlen is not None:
+        print("the backward takes dense batches only", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = synth.generate(wl, dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed + 7)
+    dout = torch.randn(inp.q.shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    q = paf.quant_nvfp4(inp.q)
+    k = paf.quant_nvfp4(inp.k)
+    vc, vs, vt, _ = paf.quant_v(inp.v, paf.V_FP8)
+    v = (paf.V_FP8, vc, None, vt)
+    B, N, Hq, D = inp.q.shape
+    Hkv = inp.k.shape[2]
+    o, lse, _ = paf.fwd_fp8pv(q, k, v, Hq=Hq, Hkv=Hkv, D=D, softmax_scale=inp.sigma, causal=wl.causal, B=B, Nq=N,
+                              Nk=N, out_dtype=torch.bfloat16)
+    ws = paf.Workspace()
+    kev = HipEvents(args.steps)
+    flops = 2.5 * synth.flops(wl)
+
+    def step(i=None):
+        return paf.bwd_fp8(q, k, v, o, lse, dout, softmax_scale=inp.sigma, causal=wl.causal, workspace=ws,
+                           events=None if i is None else kev.handles(i))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    a.record()
+    for i in range(args.steps):
+        step(i)
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = a.elapsed_time(b) / args.steps
+    kern_ms = kev.mean_ms()
+    value = flops / (ms * 1e-3) / 1e12
+    kern_tflops = flops / (kern_ms * 1e-3) / 1e12
+    # three of the five products run on the bf16 MFMA (S, dK, dQ: NVFP4 values need 6 bits), two on FP8 (dP, dV)
+    ceiling = 1.0 / (0.6 / BF16_PEAK_TFLOPS + 0.4 / FP8_PEAK_TFLOPS)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_bwd(inp, dout, o, lse, args.cpu_rows_bwd)
+    out = {
+        "metric": "attn bwd (causal training path, FP8 gradient operands) TFLOP/s on 1 MI355X",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8+bf16", "data": "synthetic (seeded Gaussian, the workload's recipe)",
+        "config": {"workload": f"{wl.name}: B={B} N={N} Hq={Hq} Hkv={Hkv} D={D} "
+                               f"{'causal' if wl.causal else 'noncausal'}, backward of the FP8-P/V forward",
+                   "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "D": D, "causal": wl.causal, "flops_per_step": flops,
+                   "parallelism": "single GPU"},
+        "bwd_kernels_tflops": round(kern_tflops, 2),
+        "prep_ms": round(ms - kern_ms, 4),
+        "precision": "NVFP4 Q/K (exact values on the bf16 MFMA), E5M2 dO, FP8 E4M3 V, MX E4M3 P~ and dS~, "
+                     "FP32 accumulation",
+        "roofline": {"bound": "mfma", "achieved": round(kern_tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(kern_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "bwd_dkdv_kernel + bwd_dq_kernel", "kernel_ms": round(kern_ms, 4),
+                     "mixed_ceiling_tflops": round(ceiling, 1), "frac_of_mixed_ceiling": round(kern_tflops / ceiling, 4)},
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -210,6 +324,11 @@ def main():
     from precision_attention_forward_amd import synth
 
     paf.load_library()
+    if args.workload is None:
+        args.workload = 4 if args.backward else 2
+    if args.backward:
+        backward_main(args, torch, paf, synth)
+        return
     wl = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -220,11 +220,15 @@ __global__ void __launch_bounds__(256) bwd_v_kernel(const uint8_t* __restrict__ 
 template <int D, bool CAUSAL, bool DEBUG>
 __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
   constexpr int KS = D / 16, DT = D / 32, KK = D / 64;
-  __shared__ __attribute__((aligned(16))) __bf16 sQ[BWD_CHUNK * D];
-  __shared__ __attribute__((aligned(16))) __bf16 sQT[D * BWD_CHUNK];
-  __shared__ __attribute__((aligned(16))) uint8_t sDO[BWD_CHUNK * D];
-  __shared__ __attribute__((aligned(16))) uint8_t sDOT[D * BWD_CHUNK];
-  __shared__ float sL[BWD_CHUNK], sD[BWD_CHUNK];
+  // LDS rows padded by 16 bytes (row strides of 256k + 16 bytes spread the
+  // permuted-row operand reads over all banks)
+  constexpr int QS = D + 8, QTS = BWD_CHUNK + 8;          // bf16 elements
+  constexpr int DS = D + 16, DTS = BWD_CHUNK + 16;        // bytes
+  __shared__ __attribute__((aligned(16))) __bf16 sQ[2][BWD_CHUNK * QS];
+  __shared__ __attribute__((aligned(16))) __bf16 sQT[2][D * QTS];
+  __shared__ __attribute__((aligned(16))) uint8_t sDO[2][BWD_CHUNK * DS];
+  __shared__ __attribute__((aligned(16))) uint8_t sDOT[2][D * DTS];
+  __shared__ float sL[2][BWD_CHUNK], sD[2][BWD_CHUNK];
   const int kb = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, ln = lane & 31;
   const int key = kb * BWD_ROWS + wave * 32 + ln;
@@ -249,37 +253,79 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
   const float sdv = sdo * *p.sv;
   const int nchunks = (int)(npad / BWD_CHUNK);
   const int c0 = CAUSAL ? (kb * BWD_ROWS) / BWD_CHUNK : 0;
+  const int nch = nchunks - c0;                 // >= 2: the key block's own chunks
+  const int total = G * nch;                    // (query head, query chunk) steps
   const int m = ln;
-  for (int g = 0; g < G; ++g) {
+  // Chunk copies are double-buffered through registers: the global loads of
+  // step it + 1 are issued before the matrix work of step it and stored to
+  // the other LDS buffer after it (one barrier per step).
+  constexpr int NQ = BWD_CHUNK * D / 8 / 256, NQT = D * (BWD_CHUNK / 8) / 256;
+  constexpr int NDO = BWD_CHUNK * D / 16 / 256, NDOT = D * (BWD_CHUNK / 16) / 256;
+  u32x4 pq[NQ], pqt[NQT], pdo[NDO], pdot[NDOT];
+  float pl = 0.0f, pd = 0.0f;
+  auto fetch = [&](int step) {
+    const int g = step / nch, c = c0 + step % nch;
+    const int64_t qhead = (int64_t)b * p.Hq + hk * G + g;
+    const int64_t q0 = qhead * npad + (int64_t)c * BWD_CHUNK;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int it = tid + 256 * i, row = it / (D / 8), g8 = it % (D / 8);
+      pq[i] = *reinterpret_cast<const u32x4*>(p.qrm + (q0 + row) * D + 8 * g8);
+    }
+#pragma unroll
+    for (int i = 0; i < NQT; ++i) {
+      const int it = tid + 256 * i, d = it / (BWD_CHUNK / 8), r8 = it % (BWD_CHUNK / 8);
+      pqt[i] = *reinterpret_cast<const u32x4*>(p.qt + (qhead * D + d) * npad + (int64_t)c * BWD_CHUNK + 8 * r8);
+    }
+#pragma unroll
+    for (int i = 0; i < NDO; ++i) {
+      const int it = tid + 256 * i, row = it / (D / 16), g16 = it % (D / 16);
+      pdo[i] = *reinterpret_cast<const u32x4*>(p.dorm + (q0 + row) * D + 16 * g16);
+    }
+#pragma unroll
+    for (int i = 0; i < NDOT; ++i) {
+      const int it = tid + 256 * i, d = it / (BWD_CHUNK / 16), r16 = it % (BWD_CHUNK / 16);
+      pdot[i] = *reinterpret_cast<const u32x4*>(p.dot + (qhead * D + d) * npad + (int64_t)c * BWD_CHUNK + 16 * r16);
+    }
+    if (tid < BWD_CHUNK) {
+      pl = p.lv[q0 + tid];
+      pd = p.dv[q0 + tid];
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int it = tid + 256 * i, row = it / (D / 8), g8 = it % (D / 8);
+      *reinterpret_cast<u32x4*>(&sQ[buf][row * QS + 8 * g8]) = pq[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NQT; ++i) {
+      const int it = tid + 256 * i, d = it / (BWD_CHUNK / 8), r8 = it % (BWD_CHUNK / 8);
+      *reinterpret_cast<u32x4*>(&sQT[buf][d * QTS + 8 * r8]) = pqt[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NDO; ++i) {
+      const int it = tid + 256 * i, row = it / (D / 16), g16 = it % (D / 16);
+      *reinterpret_cast<u32x4*>(&sDO[buf][row * DS + 16 * g16]) = pdo[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NDOT; ++i) {
+      const int it = tid + 256 * i, d = it / (BWD_CHUNK / 16), r16 = it % (BWD_CHUNK / 16);
+      *reinterpret_cast<u32x4*>(&sDOT[buf][d * DTS + 16 * r16]) = pdot[i];
+    }
+    if (tid < BWD_CHUNK) {
+      sL[buf][tid] = pl;
+      sD[buf][tid] = pd;
+    }
+  };
+  fetch(0);
+  store(0);
+  __syncthreads();
+  for (int step = 0; step < total; ++step) {
+    const int g = step / nch, c = c0 + step % nch, buf = step & 1;
     const int h = hk * G + g;
-    const int64_t qhead = (int64_t)b * p.Hq + h;
-    for (int c = c0; c < nchunks; ++c) {
-      const int64_t q0 = qhead * npad + (int64_t)c * BWD_CHUNK;
-      __syncthreads();
-      for (int it = tid; it < BWD_CHUNK * D / 8; it += 256) {
-        const int row = it / (D / 8), g8 = it % (D / 8);
-        *reinterpret_cast<u32x4*>(&sQ[row * D + 8 * g8]) = *reinterpret_cast<const u32x4*>(p.qrm + (q0 + row) * D + 8 * g8);
-      }
-      for (int it = tid; it < D * (BWD_CHUNK / 8); it += 256) {
-        const int d = it / (BWD_CHUNK / 8), r8 = it % (BWD_CHUNK / 8);
-        *reinterpret_cast<u32x4*>(&sQT[d * BWD_CHUNK + 8 * r8]) =
-            *reinterpret_cast<const u32x4*>(p.qt + (qhead * D + d) * npad + (int64_t)c * BWD_CHUNK + 8 * r8);
-      }
-      for (int it = tid; it < BWD_CHUNK * D / 16; it += 256) {
-        const int row = it / (D / 16), g16 = it % (D / 16);
-        *reinterpret_cast<u32x4*>(&sDO[row * D + 16 * g16]) = *reinterpret_cast<const u32x4*>(p.dorm + (q0 + row) * D + 16 * g16);
-      }
-      for (int it = tid; it < D * (BWD_CHUNK / 16); it += 256) {
-        const int d = it / (BWD_CHUNK / 16), r16 = it % (BWD_CHUNK / 16);
-        *reinterpret_cast<u32x4*>(&sDOT[d * BWD_CHUNK + 16 * r16]) =
-            *reinterpret_cast<const u32x4*>(p.dot + (qhead * D + d) * npad + (int64_t)c * BWD_CHUNK + 16 * r16);
-      }
-      if (tid < BWD_CHUNK) {
-        sL[tid] = p.lv[q0 + tid];
-        sD[tid] = p.dv[q0 + tid];
-      }
-      __syncthreads();
-
+    fetch(step + 1 < total ? step + 1 : step);
+    {
       f32x16 s[2], dp[2];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
@@ -287,14 +333,14 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
         s[s2] = f32x16{};
 #pragma unroll
         for (int st = 0; st < KS; ++st) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sQ[qrow * D + 16 * st + 8 * hh]);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sQ[buf][qrow * QS + 16 * st + 8 * hh]);
           s[s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kreg[st], s[s2], 0, 0, 0);
         }
         dp[s2] = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          const u32x4 lo = *reinterpret_cast<const u32x4*>(&sDO[qrow * D + 64 * kk + 16 * hh]);
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(&sDO[qrow * D + 64 * kk + 32 + 16 * hh]);
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(&sDO[buf][qrow * DS + 64 * kk + 16 * hh]);
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(&sDO[buf][qrow * DS + 64 * kk + 32 + 16 * hh]);
           const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
           // A: dO^ codes (E5M2, format 1), B: V codes (E4M3, format 0), unit scales
           dp[s2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, vreg[kk], dp[s2], 1, 0, 0, 127, 0, 127);
@@ -312,8 +358,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
           const int ql = 32 * s2 + 16 * hh + r, qi = c * BWD_CHUNK + ql;
           const bool live = key < p.N && (!CAUSAL || key <= qi);
           const float t = s[s2][r] * cc;
-          const float pr = live ? __builtin_amdgcn_exp2f(t - sL[ql]) : 0.0f;
-          const float ds = pr * (dp[s2][r] * sdv - sD[ql]);
+          const float pr = live ? __builtin_amdgcn_exp2f(t - sL[buf][ql]) : 0.0f;
+          const float ds = pr * (dp[s2][r] * sdv - sD[buf][ql]);
           pv[s2][r] = pr;
           dsv[s2][r] = ds;
           amp[s2] = __builtin_fmaxf(amp[s2], pr);
@@ -360,8 +406,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int d = 32 * dt + ln;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(&sDOT[d * BWD_CHUNK + 16 * hh]);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(&sDOT[d * BWD_CHUNK + 32 + 16 * hh]);
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(&sDOT[buf][d * DTS + 16 * hh]);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(&sDOT[buf][d * DTS + 32 + 16 * hh]);
         const i32x8 bb = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         // A: P~ (E4M3, format 0) with its block exponents, B: dO^ codes (E5M2, format 1)
         dv[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pa, bb, dv[dt], 0, 1, 0, scale_p, 0, 127);
@@ -392,11 +438,13 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const int d = 32 * dt + ln;
-          const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&sQT[d * BWD_CHUNK + 32 * s2 + 16 * hh + r0]);
+          const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&sQT[buf][d * QTS + 32 * s2 + 16 * hh + r0]);
           dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, dk[dt], 0, 0, 0);
         }
       }
     }
+    store(buf ^ 1);
+    __syncthreads();
   }
   // C[key row][d]: lane holds d = 32 dt + ln, register r holds key row out_row(r, hh)
   const float fk = p.sigma * *p.gq;
@@ -421,9 +469,11 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
 template <int D, bool CAUSAL, bool DEBUG>
 __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdParams p) {
   constexpr int KS = D / 16, DT = D / 32, KK = D / 64;
-  __shared__ __attribute__((aligned(16))) __bf16 sK[BWD_CHUNK * D];
-  __shared__ __attribute__((aligned(16))) __bf16 sKT[D * BWD_CHUNK];
-  __shared__ __attribute__((aligned(16))) uint8_t sV[BWD_CHUNK * D];
+  constexpr int KSR = D + 8, KTS = BWD_CHUNK + 8;         // padded row strides (bf16 elements)
+  constexpr int VS = D + 16;                              // bytes
+  __shared__ __attribute__((aligned(16))) __bf16 sK[2][BWD_CHUNK * KSR];
+  __shared__ __attribute__((aligned(16))) __bf16 sKT[2][D * KTS];
+  __shared__ __attribute__((aligned(16))) uint8_t sV[2][BWD_CHUNK * VS];
   const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, ln = lane & 31;
   const int q = qb * BWD_ROWS + wave * 32 + ln;
@@ -450,23 +500,50 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdParams p) {
   int nchunks = (int)(npad / BWD_CHUNK);
   if (CAUSAL) nchunks = min(nchunks, (qb * BWD_ROWS + BWD_ROWS) / BWD_CHUNK);
   const int m = ln;
-  for (int c = 0; c < nchunks; ++c) {
+  // chunk copies double-buffered through registers, as in the dK/dV kernel
+  constexpr int NK = BWD_CHUNK * D / 8 / 256, NKT = D * (BWD_CHUNK / 8) / 256, NV = BWD_CHUNK * D / 16 / 256;
+  u32x4 pk[NK], pkt[NKT], pv4[NV];
+  auto fetch = [&](int c) {
     const int64_t k0 = khead * npad + (int64_t)c * BWD_CHUNK;
-    __syncthreads();
-    for (int it = tid; it < BWD_CHUNK * D / 8; it += 256) {
-      const int row = it / (D / 8), g8 = it % (D / 8);
-      *reinterpret_cast<u32x4*>(&sK[row * D + 8 * g8]) = *reinterpret_cast<const u32x4*>(p.krm + (k0 + row) * D + 8 * g8);
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int it = tid + 256 * i, row = it / (D / 8), g8 = it % (D / 8);
+      pk[i] = *reinterpret_cast<const u32x4*>(p.krm + (k0 + row) * D + 8 * g8);
     }
-    for (int it = tid; it < D * (BWD_CHUNK / 8); it += 256) {
-      const int d = it / (BWD_CHUNK / 8), r8 = it % (BWD_CHUNK / 8);
-      *reinterpret_cast<u32x4*>(&sKT[d * BWD_CHUNK + 8 * r8]) =
-          *reinterpret_cast<const u32x4*>(p.kt + (khead * D + d) * npad + (int64_t)c * BWD_CHUNK + 8 * r8);
+#pragma unroll
+    for (int i = 0; i < NKT; ++i) {
+      const int it = tid + 256 * i, d = it / (BWD_CHUNK / 8), r8 = it % (BWD_CHUNK / 8);
+      pkt[i] = *reinterpret_cast<const u32x4*>(p.kt + (khead * D + d) * npad + (int64_t)c * BWD_CHUNK + 8 * r8);
     }
-    for (int it = tid; it < BWD_CHUNK * D / 16; it += 256) {
-      const int row = it / (D / 16), g16 = it % (D / 16);
-      *reinterpret_cast<u32x4*>(&sV[row * D + 16 * g16]) = *reinterpret_cast<const u32x4*>(p.vrm + (k0 + row) * D + 16 * g16);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int it = tid + 256 * i, row = it / (D / 16), g16 = it % (D / 16);
+      pv4[i] = *reinterpret_cast<const u32x4*>(p.vrm + (k0 + row) * D + 16 * g16);
     }
-    __syncthreads();
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int it = tid + 256 * i, row = it / (D / 8), g8 = it % (D / 8);
+      *reinterpret_cast<u32x4*>(&sK[buf][row * KSR + 8 * g8]) = pk[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NKT; ++i) {
+      const int it = tid + 256 * i, d = it / (BWD_CHUNK / 8), r8 = it % (BWD_CHUNK / 8);
+      *reinterpret_cast<u32x4*>(&sKT[buf][d * KTS + 8 * r8]) = pkt[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int it = tid + 256 * i, row = it / (D / 16), g16 = it % (D / 16);
+      *reinterpret_cast<u32x4*>(&sV[buf][row * VS + 16 * g16]) = pv4[i];
+    }
+  };
+  fetch(0);
+  store(0);
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    const int buf = c & 1;
+    fetch(c + 1 < nchunks ? c + 1 : c);
 
     f32x16 s[2], dp[2];
 #pragma unroll
@@ -475,14 +552,14 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdParams p) {
       s[s2] = f32x16{};
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sK[krow * D + 16 * st + 8 * hh]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sK[buf][krow * KSR + 16 * st + 8 * hh]);
         s[s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[st], s[s2], 0, 0, 0);
       }
       dp[s2] = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(&sV[krow * D + 64 * kk + 16 * hh]);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(&sV[krow * D + 64 * kk + 32 + 16 * hh]);
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(&sV[buf][krow * VS + 64 * kk + 16 * hh]);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(&sV[buf][krow * VS + 64 * kk + 32 + 16 * hh]);
         const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         // A: V codes (E4M3, format 0), B: dO^ codes (E5M2, format 1), unit scales
         dp[s2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, doreg[kk], dp[s2], 0, 1, 0, 127, 0, 127);
@@ -530,10 +607,12 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int d = 32 * dt + ln;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sKT[d * BWD_CHUNK + 32 * hh + 16 * s2 + r0]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sKT[buf][d * KTS + 32 * hh + 16 * s2 + r0]);
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv, acc[dt], 0, 0, 0);
       }
     }
+    store(buf ^ 1);
+    __syncthreads();
   }
   // C[d row][query]: lane holds the query, register r holds d = 32 dt + out_row(r, hh)
   if (q < p.N) {
