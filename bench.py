@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=16384, help="query rows of the oracle sample")
-    ap.add_argument("--cpu-rows-bwd", type=int, default=1024, help="rows of the backward oracle sample")
+    ap.add_argument("--cpu-rows-bwd", type=int, default=8192, help="rows of the backward oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (HBM counter calibration) and exit")
     return ap.parse_args()
