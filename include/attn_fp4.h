@@ -268,6 +268,65 @@ attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, 
                           float softmax_scale, int32_t causal, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Decode-shaped forward
+ * --------------------------------------------------------------------- */
+
+/*
+ * Forward of a decode step: nq new query tokens per sequence attend to a KV
+ * cache of up to Nk keys (the workload of the Colfax Research feed's post on
+ * FlashAttention-4 decode, which generates one or a few tokens per step from
+ * the cached keys and values).  The arithmetic is exactly that of
+ * attn_fwd_directp / attn_fwd_fp8pv (128-key tiles of the running max from
+ * key 0, E8M0 per 32 keys, l from the rounded probabilities), so a decode
+ * call and a prefill call over the same quantized operands give the same
+ * probability codes up to float32 rounding near-ties.  The kernel reads the
+ * compact cache directly; it needs no workspace.
+ *
+ *   q     : NVFP4 Q of the new tokens, rows ordered [B, nq, Hq]
+ *           (attn_quant_nvfp4 of a bf16 [B, nq, Hq, D] tensor)
+ *   k     : NVFP4 K cache, head-major: rows ordered [B, Hkv, Nk]
+ *           (attn_quant_nvfp4 of a bf16 [B, Hkv, Nk, D] tensor)
+ *   v     : V cache as attn_quant_v writes it for a dense bf16
+ *           [B, Nk, Hkv, D] tensor (cols = B * roundup(Nk, 128))
+ *   seqlens_k : nullable device int32 [B], the number of valid cache
+ *           entries of each sequence (values are clamped to [0, Nk]); NULL
+ *           means Nk for every sequence
+ *   causal: new token i (0-based) of a sequence with L valid keys sits at
+ *           position L - nq + i and sees keys 0 .. L - nq + i (the new
+ *           tokens are the last nq entries of the cache); otherwise every
+ *           new token sees all L keys.  With nq == 1 both are the same.
+ *   o     : [B, nq, Hq, D] (o_dtype); lse: nullable float [B, Hq, nq]
+ * A row with no visible key gets O = 0 and LSE = -inf.
+ * Limits: D in {64, 128}; Hq % Hkv == 0; 1 <= nq; D * B * roundup(Nk, 128)
+ * below 2^31.  attn_decode_fp8pv requires FP8 V.  Optional probability dump
+ * of (dbg_b, dbg_h): codes [nq, roundup(Nk,128)/2] (MXFP4 P) or
+ * [nq, roundup(Nk,128)] (FP8 P), E8M0 bytes [nq, roundup(Nk,128)/32].
+ * prof_event_begin/end (hipEvent_t, nullable) are recorded around the kernel.
+ */
+typedef struct attn_decode_args {
+  int32_t B, Hq, Hkv, nq, Nk, D;
+  const int32_t* seqlens_k;
+  float softmax_scale;
+  int32_t causal;
+  attn_nvfp4_tensor q;
+  attn_nvfp4_tensor k;
+  attn_v_tensor v;
+  void* o;
+  int32_t o_dtype;
+  float* lse;
+  uint8_t* dbg_p_codes;
+  uint8_t* dbg_p_scales;
+  int32_t dbg_b, dbg_h;
+  void* prof_event_begin;
+  void* prof_event_end;
+} attn_decode_args;
+
+/* Direct-P decode: MXFP4 P (E8M0 per 32 keys), V FP8 or MXFP4. */
+attn_status attn_decode_directp(const attn_decode_args* a, void* stream);
+/* FP8-P/V decode: E4M3 P with unit scale, FP8 V. */
+attn_status attn_decode_fp8pv(const attn_decode_args* a, void* stream);
+
+/* ------------------------------------------------------------------------
  * Backward (causal training path)
  * --------------------------------------------------------------------- */
 

@@ -69,6 +69,20 @@ class BwdArgs(ctypes.Structure):
     ]
 
 
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("nq", ctypes.c_int32), ("Nk", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("seqlens_k", ctypes.c_void_p),
+        ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32),
+        ("q", _NvTensor), ("k", _NvTensor), ("v", _VTensor),
+        ("o", ctypes.c_void_p), ("o_dtype", ctypes.c_int32), ("lse", ctypes.c_void_p),
+        ("dbg_p_codes", ctypes.c_void_p), ("dbg_p_scales", ctypes.c_void_p),
+        ("dbg_b", ctypes.c_int32), ("dbg_h", ctypes.c_int32),
+        ("prof_event_begin", ctypes.c_void_p), ("prof_event_end", ctypes.c_void_p),
+    ]
+
+
 EXPORTS = {
     "attn_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "attn_last_hip_error": (ctypes.c_int, []),
@@ -89,6 +103,8 @@ EXPORTS = {
     "attn_fwd_fp8pv": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "attn_fwd_directp_efq": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "attn_fwd_fp8pv_cast": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
+    "attn_decode_directp": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]),
+    "attn_decode_fp8pv": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]),
     "attn_bwd_ws_bytes": (ctypes.c_size_t, [ctypes.POINTER(BwdArgs)]),
     "attn_bwd_fp8": (ctypes.c_int, [ctypes.POINTER(BwdArgs), ctypes.c_void_p]),
     "attn_fwd_bf16": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -299,6 +315,62 @@ def fwd_directp_efq(q, k, v, **kw):
 def fwd_fp8pv_cast(q, k, v, **kw):
     """Exp-free FP8-P/V: E4M3 codes by the one-FMA log-linear cast (causal allowed)."""
     return _fwd_lowp("attn_fwd_fp8pv_cast", q, k, v, **kw)
+
+
+def _decode(entry, q, k, v, *, B, Hq, Hkv, nq, Nk, D, softmax_scale, causal=False, seqlens_k=None,
+            out_dtype=torch.float32, want_lse=True, debug=None, events=None, out=None):
+    """Shared driver of the decode entry points.  q: NVFP4 (codes, scales,
+    tensor_scale) of a [B, nq, Hq, D] tensor; k: the same of the head-major
+    K cache [B, Hkv, Nk, D]; v: (format, codes, scales|None,
+    tensor_scale|None) from quant_v of the [B, Nk, Hkv, D] V cache;
+    seqlens_k: optional device int32 [B].  Returns (O [B, nq, Hq, D],
+    LSE [B, Hq, nq], (dump codes, dump scales))."""
+    lib = load_library()
+    _need_cuda(q[0], k[0], v[1], seqlens_k)
+    dev = q[0].device
+    if out is not None:
+        o, lse = out
+    else:
+        o = torch.empty((B, nq, Hq, D), dtype=out_dtype, device=dev)
+        lse = torch.empty((B, Hq, nq), dtype=torch.float32, device=dev) if want_lse else None
+    a = DecodeArgs()
+    a.B, a.Hq, a.Hkv, a.nq, a.Nk, a.D = B, Hq, Hkv, nq, Nk, D
+    a.seqlens_k = None if seqlens_k is None else seqlens_k.data_ptr()
+    a.softmax_scale = softmax_scale
+    a.causal = 1 if causal else 0
+    a.q = _NvTensor(q[0].data_ptr(), q[1].data_ptr(), q[2].data_ptr())
+    a.k = _NvTensor(k[0].data_ptr(), k[1].data_ptr(), k[2].data_ptr())
+    a.v = _VTensor(v[0], v[1].data_ptr(), None if v[2] is None else v[2].data_ptr(),
+                   None if v[3] is None else v[3].data_ptr())
+    a.o = o.data_ptr()
+    a.o_dtype = OUT_F32 if o.dtype == torch.float32 else OUT_BF16
+    a.lse = None if lse is None else lse.data_ptr()
+    dbg_codes = dbg_scales = None
+    if debug is not None:
+        a.dbg_b, a.dbg_h = debug
+        nk_pad = (Nk + 127) // 128 * 128
+        if entry == "attn_decode_directp":
+            dbg_codes = torch.zeros((nq, nk_pad // 2), dtype=torch.uint8, device=dev)
+            dbg_scales = torch.zeros((nq, nk_pad // 32), dtype=torch.uint8, device=dev)
+            a.dbg_p_scales = dbg_scales.data_ptr()
+        else:
+            dbg_codes = torch.zeros((nq, nk_pad), dtype=torch.uint8, device=dev)
+        a.dbg_p_codes = dbg_codes.data_ptr()
+    if events is not None:
+        a.prof_event_begin = events[0].cuda_event
+        a.prof_event_end = events[1].cuda_event
+    _check(getattr(lib, entry)(ctypes.byref(a), _stream()))
+    return o, lse, (dbg_codes, dbg_scales)
+
+
+def decode_directp(q, k, v, **kw):
+    """Decode-shaped Direct-P forward (MXFP4 P, V FP8 or MXFP4)."""
+    return _decode("attn_decode_directp", q, k, v, **kw)
+
+
+def decode_fp8pv(q, k, v, **kw):
+    """Decode-shaped FP8-P/V forward."""
+    return _decode("attn_decode_fp8pv", q, k, v, **kw)
 
 
 def bwd_fp8(q, k, v, o, lse, dout, *, softmax_scale, causal=True, workspace=None, events=None, debug=None):

@@ -1,7 +1,7 @@
 // C ABI of the Direct-P FP4 attention library (declared in include/attn_fp4.h).
 // Host-side argument validation and launch sequencing only; every step of the
-// computation runs in the HIP kernels of quant.hip, fwd_lowp.hip, fwd_bf16.hip
-// and bwd.hip.
+// computation runs in the HIP kernels of quant.hip, fwd_lowp.hip, fwd_bf16.hip,
+// decode.hip and bwd.hip.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -32,10 +32,13 @@ hipError_t launch_bwd_prep(const uint8_t* q_codes, const uint8_t* q_scales, cons
                            hipStream_t st);
 struct BwdParams;
 hipError_t launch_bwd_main(const BwdParams& p, int D, bool causal, bool debug, hipStream_t st);
+struct DecParams;
+hipError_t launch_decode(const DecParams& p, int D, int pf, int vf, bool causal, bool debug, hipStream_t st);
 }  // namespace attn
 
 #include "fwd_params.h"
 #include "bwd_params.h"
+#include "dec_params.h"
 
 using namespace attn;
 
@@ -364,4 +367,89 @@ attn_status attn_bwd_fp8(const attn_bwd_args* a, void* stream) {
   if (a->prof_event_end != nullptr) e = hipEventRecord((hipEvent_t)a->prof_event_end, st);
   return hip_status(e);
 }
+
+// ---- decode-shaped forward ----
+static attn_status validate_decode(const attn_decode_args* a, int pf) {
+  if (a == nullptr) return ATTN_ERR_INVALID_ARGUMENT;
+  if (a->B < 0 || a->Hq <= 0 || a->Hkv <= 0 || a->nq < 1 || a->Nk < 0) return ATTN_ERR_INVALID_ARGUMENT;
+  if (a->D != 64 && a->D != 128) return ATTN_ERR_INVALID_ARGUMENT;
+  if (a->Hq % a->Hkv != 0) return ATTN_ERR_INVALID_ARGUMENT;
+  if (!(a->softmax_scale > 0.0f) || a->softmax_scale != a->softmax_scale) return ATTN_ERR_INVALID_ARGUMENT;
+  if (a->v.format != ATTN_V_FP8_E4M3 && a->v.format != ATTN_V_MXFP4) return ATTN_ERR_INVALID_ARGUMENT;
+  if (pf == 1 && a->v.format != ATTN_V_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
+  if (a->o_dtype != ATTN_OUT_BF16 && a->o_dtype != ATTN_OUT_F32) return ATTN_ERR_INVALID_ARGUMENT;
+  const int64_t cols = (int64_t)a->B * roundup(a->Nk, 128);
+  if ((int64_t)a->D * cols >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
+  if (a->seqlens_k != nullptr && !aligned(a->seqlens_k, 4)) return ATTN_ERR_INVALID_ARGUMENT;
+  const int64_t nq = (int64_t)a->B * a->nq, nk = (int64_t)a->B * a->Nk;
+  const attn_nvfp4_tensor* t[2] = {&a->q, &a->k};
+  const int64_t n[2] = {nq, nk};
+  for (int i = 0; i < 2; ++i) {
+    if (t[i]->tensor_scale == nullptr || !aligned(t[i]->tensor_scale, 4)) return ATTN_ERR_INVALID_ARGUMENT;
+    if (n[i] > 0 && (t[i]->codes == nullptr || t[i]->scales == nullptr || !aligned(t[i]->codes, 16) ||
+                     !aligned(t[i]->scales, 4)))
+      return ATTN_ERR_INVALID_ARGUMENT;
+  }
+  if (nk > 0 && (a->v.codes == nullptr || !aligned(a->v.codes, 16))) return ATTN_ERR_INVALID_ARGUMENT;
+  if (nk > 0 && a->v.format == ATTN_V_MXFP4 && (a->v.scales == nullptr || !aligned(a->v.scales, 4)))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (a->v.format == ATTN_V_FP8_E4M3 && (a->v.tensor_scale == nullptr || !aligned(a->v.tensor_scale, 4)))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (nq > 0 && (a->o == nullptr || !aligned(a->o, 16))) return ATTN_ERR_INVALID_ARGUMENT;
+  if (a->lse != nullptr && !aligned(a->lse, 4)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (a->dbg_p_codes != nullptr) {
+    if (a->dbg_b < 0 || a->dbg_b >= a->B || a->dbg_h < 0 || a->dbg_h >= a->Hq || !aligned(a->dbg_p_codes, 16))
+      return ATTN_ERR_INVALID_ARGUMENT;
+    if (pf == 0 && a->dbg_p_scales == nullptr) return ATTN_ERR_INVALID_ARGUMENT;
+  }
+  return ATTN_OK;
+}
+
+static attn_status run_decode(const attn_decode_args* a, void* stream, int pf) {
+  attn_status s = validate_decode(a, pf);
+  if (s != ATTN_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  DecParams p;
+  memset(&p, 0, sizeof(p));
+  p.q_codes = a->q.codes;
+  p.q_scales = a->q.scales;
+  p.k_codes = a->k.codes;
+  p.k_scales = a->k.scales;
+  p.v_codes = a->v.codes;
+  p.v_scales = a->v.scales;
+  p.gq = a->q.tensor_scale;
+  p.gk = a->k.tensor_scale;
+  p.sv = a->v.tensor_scale;
+  p.seqlens = a->seqlens_k;
+  p.o = a->o;
+  p.o_f32 = a->o_dtype == ATTN_OUT_F32;
+  p.lse = a->lse;
+  p.B = a->B;
+  p.Hq = a->Hq;
+  p.Hkv = a->Hkv;
+  p.nq = a->nq;
+  p.Nk = a->Nk;
+  p.QG = (int)(((int64_t)(a->Hq / a->Hkv) * a->nq + 31) / 32);
+  p.nk_pad = roundup(a->Nk, 128);
+  p.cols = (int64_t)a->B * p.nk_pad;
+  p.sigma = a->softmax_scale;
+  p.dbg_codes = a->dbg_p_codes;
+  p.dbg_scales = a->dbg_p_scales;
+  p.dbg_b = a->dbg_b;
+  p.dbg_h = a->dbg_h;
+  p.dbg_ld = p.nk_pad;
+  hipError_t e;
+  if (a->prof_event_begin != nullptr) {
+    e = hipEventRecord((hipEvent_t)a->prof_event_begin, st);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  e = launch_decode(p, a->D, pf, a->v.format == ATTN_V_MXFP4 ? 1 : 0, a->causal != 0, a->dbg_p_codes != nullptr, st);
+  if (e != hipSuccess) return hip_status(e);
+  if (a->prof_event_end != nullptr) e = hipEventRecord((hipEvent_t)a->prof_event_end, st);
+  return hip_status(e);
+}
+
+attn_status attn_decode_directp(const attn_decode_args* a, void* stream) { return run_decode(a, stream, 0); }
+attn_status attn_decode_fp8pv(const attn_decode_args* a, void* stream) { return run_decode(a, stream, 1); }
+
 }  // extern "C"

@@ -16,6 +16,9 @@ Gaussian tensors of the same shapes stand in for them):
   varlen16  16 sequences, N_i ~ U{1024..65536}, packed with cu_seqlens,
             H=32, D=128, noncausal; 1% of token rows of Q and (independently)
             of K scaled x16; MXFP4 P, FP8 V
+  llama8b_decode  a decode step of the Llama-3.1-style model: B=64
+            sequences, Hq=32, Hkv=8, D=128, nq=1 new token per sequence
+            against a KV cache of N=8192 keys; MXFP4 P, FP8 V (generate_decode)
 
 Draw order for a seed: sequence lengths (varlen only), then Q, K, V as
 float32 standard normals cast to bfloat16, then the outlier choice.
@@ -56,6 +59,8 @@ WORKLOADS = {
     4: Workload("llama8b", 4, 32, 8, 8192, 128, True, "fp8", "fp8", None, None, 4),
     5: Workload("varlen16", 16, 32, 32, 0, 128, False, "mxfp4", "fp8",
                 ("tokens", 0.01, 16.0), (16, 1024, 65536), 5),
+    6: Workload("llama8b_decode", 64, 32, 8, 8192, 128, True, "mxfp4", "fp8", None, None, 6,
+                {"nq": 1}),
 }
 
 
@@ -114,6 +119,64 @@ def generate(wl: Workload, device="cpu") -> Inputs:
         else:
             raise ValueError(kind)
     return Inputs(wl, q, k, v, seqlens, cu, chans)
+
+
+@dataclass
+class DecodeInputs:
+    wl: Workload
+    q: torch.Tensor            # bf16 [B, nq, Hq, D], the new tokens
+    k: torch.Tensor            # bf16 [B, Hkv, N, D], head-major K cache
+    v: torch.Tensor            # bf16 [B, N, Hkv, D], V cache
+    seqlens: torch.Tensor      # int32 CPU [B], valid cache entries per sequence
+
+    @property
+    def sigma(self):
+        return 1.0 / float(self.wl.D) ** 0.5
+
+
+def generate_decode(wl: Workload, device="cpu") -> DecodeInputs:
+    """Inputs of a decode step: ``wl.N`` is the cache capacity, ``extra["nq"]``
+    the new tokens per sequence and ``extra["ragged"]`` (optional) draws the
+    valid lengths from U{1..N} instead of taking N for every sequence.
+    Draw order: lengths (ragged only), then Q, K, V as float32 standard
+    normals cast to bfloat16."""
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed)
+    nq = int(wl.extra.get("nq", 1))
+    if wl.extra.get("ragged"):
+        seqlens = torch.randint(1, wl.N + 1, (wl.B,), generator=gen, device=dev).to("cpu", torch.int32)
+    else:
+        seqlens = torch.full((wl.B,), wl.N, dtype=torch.int32)
+
+    def draw(shape):
+        return torch.randn(shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+    q = draw((wl.B, nq, wl.Hq, wl.D))
+    k = draw((wl.B, wl.Hkv, wl.N, wl.D))
+    v = draw((wl.B, wl.N, wl.Hkv, wl.D))
+    return DecodeInputs(wl, q, k, v, seqlens)
+
+
+def decode_bytes(wl: Workload, seqlens) -> float:
+    """Bytes a decode step must move at least: every valid cache entry once
+    (NVFP4 K: D/2 + D/16 bytes per key and KV head; V: D bytes (FP8) or
+    D/2 + D/32 (MXFP4)), the NVFP4 Q and the float32 O and LSE."""
+    D = wl.D
+    per_key = D / 2 + D / 16 + (D if wl.v_format == "fp8" else D / 2 + D / 32)
+    keys = float(sum(int(n) for n in seqlens))
+    nq = int(wl.extra.get("nq", 1))
+    q = wl.B * nq * wl.Hq * (D / 2 + D / 16)
+    o = wl.B * nq * wl.Hq * (4 * D + 4)
+    return keys * wl.Hkv * per_key + q + o
+
+
+def decode_flops(wl: Workload, seqlens) -> float:
+    """4 * Hq * nq * D per valid key (the two products), halved-free: with
+    nq new tokens at the end of the cache the causal mask removes only the
+    nq (nq - 1) / 2 pairs among them, which are counted as computed."""
+    nq = int(wl.extra.get("nq", 1))
+    return 4.0 * wl.Hq * nq * wl.D * float(sum(int(n) for n in seqlens))
 
 
 def flops(wl: Workload, seqlens=None) -> float:

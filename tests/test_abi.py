@@ -59,7 +59,8 @@ def _c_offsets(struct, fields):
     return [int(x) for x in out]
 
 
-@pytest.mark.parametrize("cls,cname", [(B.FwdArgs, "attn_fwd_args"), (B.BwdArgs, "attn_bwd_args")])
+@pytest.mark.parametrize("cls,cname", [(B.FwdArgs, "attn_fwd_args"), (B.BwdArgs, "attn_bwd_args"),
+                                       (B.DecodeArgs, "attn_decode_args")])
 def test_ctypes_struct_matches_c_layout(cls, cname):
     fields = [f for f, _ in cls._fields_]
     got = _c_offsets(cname, fields)
@@ -167,3 +168,43 @@ def test_fwd_validation(lib):
     # bf16 baseline argument checks
     assert lib.attn_fwd_bf16(None, None, None, None, None, 1, 4, 3, 16, 16, 128, 0.1, 0, None) == 1
     assert lib.attn_fwd_bf16(None, None, None, None, None, 1, 4, 4, 16, 16, 80, 0.1, 0, None) == 1
+
+
+def _dec_args(**kw):
+    a = B.DecodeArgs()
+    a.B, a.Hq, a.Hkv, a.nq, a.Nk, a.D = 2, 8, 2, 1, 1000, 128
+    a.softmax_scale = 0.125
+    p = 1 << 24
+    a.q = B._NvTensor(p, p, p)
+    a.k = B._NvTensor(p, p, p)
+    a.v = B._VTensor(0, p, p, p)
+    a.o = p
+    a.o_dtype = 1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_decode_validation(lib):
+    # every case below fails on the host, so the fake pointers are never used
+    d = lambda **kw: lib.attn_decode_directp(ctypes.byref(_dec_args(**kw)), None)
+    assert d(D=96) == 1
+    assert d(Hkv=3) == 1
+    assert d(nq=0) == 1
+    assert d(Nk=-1) == 1
+    assert d(softmax_scale=0.0) == 1
+    assert d(softmax_scale=float("nan")) == 1
+    assert d(o=None) == 1
+    assert d(o_dtype=5) == 1
+    assert d(v=B._VTensor(7, 1 << 24, 1 << 24, 1 << 24)) == 1
+    assert d(v=B._VTensor(1, 1 << 24, None, 1 << 24)) == 1          # MXFP4 V needs its scales
+    assert d(k=B._NvTensor(1 << 24, None, 1 << 24)) == 1
+    assert d(q=B._NvTensor((1 << 24) + 4, 1 << 24, 1 << 24)) == 1  # misaligned codes
+    assert d(seqlens_k=(1 << 24) + 2) == 1
+    assert d(dbg_p_codes=1 << 24, dbg_b=2) == 1
+    assert d(dbg_p_codes=1 << 24) == 1                             # Direct-P dump needs the scale buffer
+    # lane offsets of the V cache must stay below 2^31
+    assert d(B=64, Nk=1 << 18) == 2
+    # FP8-P/V takes FP8 V only
+    assert lib.attn_decode_fp8pv(ctypes.byref(_dec_args(v=B._VTensor(1, 1 << 24, 1 << 24, 1 << 24))), None) == 2
+    assert lib.attn_decode_directp(None, None) == 1 and lib.attn_decode_fp8pv(None, None) == 1

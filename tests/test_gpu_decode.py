@@ -1,0 +1,155 @@
+"""GPU decode-shaped forward (attn_decode_directp / attn_decode_fp8pv) vs the
+oracle on the same seeded inputs.
+
+A decode step runs the oracle's tiled forward for the nq new tokens of each
+(sequence, head) against that sequence's valid cache entries: K quantized
+over the whole cache tensor (its amax), V quantized over the whole cache
+(MXFP4 V blocks of 32 keys from key 0 of the sequence, as stored), new token
+i at position L - nq + i for the causal mask.
+
+Bar (as for the prefill forward): every probability code or block exponent
+in which the kernel's dump differs from the oracle must be a float32
+rounding near-tie, at most 1e-4 of the live codes; O within relative L2
+1e-3 and max abs 5e-3, LSE within 1e-4 relative, against the oracle run on
+the kernel's codes where a tie went the other way.  The dump build must
+reproduce the production outputs bit for bit.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import (assert_close_outputs, check_code_choices, f32, gpu_codes, oracle_v_head, p_mismatch,
+                     P_MISMATCH_MAX)
+from oracle import attention as OA
+from oracle import quant as OQ
+from precision_attention_forward_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _amax(x, chunk=1 << 26):
+    flat = x.reshape(-1)
+    return max(float(flat[i:i + chunk].to("cpu").abs().max()) for i in range(0, flat.numel(), chunk))
+
+
+class _Prepared:
+    """Quantized operands of a decode step (the cache quantized once, as a
+    prefill would have stored it)."""
+
+    def __init__(self, gpu, inp):
+        wl = inp.wl
+        self.q = gpu.quant_nvfp4(inp.q.cuda())
+        self.k = gpu.quant_nvfp4(inp.k.cuda())
+        self.vf = gpu.V_FP8 if wl.v_format == "fp8" else gpu.V_MXFP4
+        vq = gpu.quant_v(inp.v.cuda(), self.vf)
+        self.v = (self.vf, vq[0], vq[1], vq[2])
+        self.seqlens = inp.seqlens.cuda()
+
+
+def _run(gpu, inp, prep, debug=None):
+    wl = inp.wl
+    fn = gpu.decode_directp if wl.p_format == "mxfp4" else gpu.decode_fp8pv
+    o, lse, dbg = fn(prep.q, prep.k, prep.v, B=wl.B, Hq=wl.Hq, Hkv=wl.Hkv, nq=inp.q.shape[1], Nk=wl.N, D=wl.D,
+                     softmax_scale=inp.sigma, causal=wl.causal, seqlens_k=prep.seqlens, debug=debug)
+    torch.cuda.synchronize()
+    return o, lse, dbg
+
+
+def _check(gpu, inp, pairs=None):
+    """Compare every (sequence, head) in ``pairs`` (default: all) with the oracle."""
+    wl = inp.wl
+    prep = _Prepared(gpu, inp)
+    o, lse, _ = _run(gpu, inp, prep)
+    nq = inp.q.shape[1]
+    G = wl.Hq // wl.Hkv
+    amax_q, amax_k, amax_v = _amax(inp.q), _amax(inp.k), _amax(inp.v)
+    if pairs is None:
+        pairs = [(b, h) for b in range(wl.B) for h in range(wl.Hq)]
+    worst = [0.0, 0.0, 0.0]
+    n_mis = n_tot = n_e = n_c = 0
+    vcache = {}
+    for (b, h) in pairs:
+        L = int(inp.seqlens[b])
+        hk = h // G
+        q_index = (L - nq + np.arange(nq)) if wl.causal else None
+        qc, qs, gq = OQ.quant_nvfp4(f32(inp.q[b, :, h]), amax=amax_q)
+        kc, ks, gk = OQ.quant_nvfp4(f32(inp.k[b, hk, :L]), amax=amax_k)
+        if (b, hk) not in vcache:
+            vcache[(b, hk)] = oracle_v_head(f32(inp.v[b, :, hk]), wl.v_format, amax_v)[:L]
+        args = (OQ.dequant_nvfp4_raw(qc, qs), OQ.dequant_nvfp4_raw(kc, ks), gq, gk, vcache[(b, hk)], inp.sigma,
+                wl.p_format, wl.causal)
+        od, ld, (dc, ds) = _run(gpu, inp, prep, debug=(b, h))
+        assert torch.equal(od, o) and torch.equal(ld, lse), "the dump build computes other outputs"
+        res = OA.attn_lowp_head(*args, q_index=q_index, return_pre=True)
+        if L > 0:
+            dcn = dc.cpu().numpy()
+            dsn = None if ds is None else ds.cpu().numpy()
+            gc, ge = gpu_codes(dcn, dsn, wl.p_format, L)
+            live = (np.arange(L)[None, :] <= q_index[:, None]) if wl.causal else np.ones((nq, L), bool)
+            e1, c1 = check_code_choices(gc, ge, res[2], res[3], res[4], res[5], wl.p_format, "exact", live)
+            mis, tot = p_mismatch(dcn, dsn, res[2], res[3], wl.p_format, L, live)
+            n_mis, n_tot, n_e, n_c = n_mis + mis, n_tot + tot, n_e + e1, n_c + c1
+            if e1 or c1:
+                res = OA.attn_lowp_head(*args, q_index=q_index, p_given=(gc, ge))
+        r, m, le = assert_close_outputs(f32(o[b, :, h]), f32(lse[b, h]), res[0], res[1], f"seq {b} head {h}")
+        worst = [max(worst[0], r), max(worst[1], m), max(worst[2], le)]
+    assert n_mis <= P_MISMATCH_MAX * max(n_tot, 1), f"P codes: {n_mis} of {n_tot} differ"
+    print(f"  P codes: {n_mis} of {n_tot} live codes differ; near-ties taken the other way: {n_e} exponents, "
+          f"{n_c} codes; worst O rel L2 {worst[0]:.2e}, max abs {worst[1]:.2e}, LSE rel {worst[2]:.2e}", flush=True)
+    return o, lse
+
+
+W = synth.WORKLOADS[6]
+SMALL = [
+    # Direct-P, FP8 V, one new token, ragged cache lengths, GQA 4
+    ("directp_fp8v_nq1", W.with_(B=3, Hq=8, Hkv=2, N=1000, seed=61, extra={"nq": 1, "ragged": True})),
+    # four new tokens with the causal mask among them (16 query rows per KV head)
+    ("directp_nq4_causal", W.with_(B=2, Hq=8, Hkv=2, N=700, seed=62, extra={"nq": 4, "ragged": True})),
+    # FP8 P/V, D = 64, no GQA, three causal tokens
+    ("fp8pv_d64_nq3", W.with_(B=2, Hq=4, Hkv=4, N=515, D=64, p_format="fp8", seed=63,
+                              extra={"nq": 3, "ragged": True})),
+    # Direct-P with MXFP4 V, noncausal (every new token sees the whole cache)
+    ("directp_mxfp4v_noncausal", W.with_(B=2, Hq=4, Hkv=1, N=900, causal=False, v_format="mxfp4", seed=64,
+                                         extra={"nq": 2, "ragged": True})),
+    # 48 query rows per KV head: two workgroups (query groups) per KV head
+    ("directp_two_query_groups", W.with_(B=1, Hq=16, Hkv=1, N=300, seed=65, extra={"nq": 3})),
+    # MXFP4 V with D = 64
+    ("directp_mxfp4v_d64", W.with_(B=2, Hq=2, Hkv=2, N=333, D=64, v_format="mxfp4", seed=66,
+                                   extra={"nq": 1, "ragged": True})),
+]
+
+
+@pytest.mark.parametrize("name,wl", SMALL, ids=[s[0] for s in SMALL])
+def test_decode_small_all_heads(gpu, name, wl):
+    _say(f"decode {name}")
+    _check(gpu, synth.generate_decode(wl))
+
+
+def test_decode_length_edges(gpu):
+    # valid lengths at and around the chunk (64) and tile (128) edges, an
+    # empty cache, and caches shorter than the new tokens (causal rows with no
+    # visible key: O = 0, LSE = -inf)
+    wl = W.with_(B=10, Hq=4, Hkv=2, N=260, seed=67, extra={"nq": 2})
+    inp = synth.generate_decode(wl)
+    inp.seqlens = torch.tensor([0, 1, 2, 63, 64, 65, 128, 129, 257, 260], dtype=torch.int32)
+    _say("decode length edges")
+    o, lse = _check(gpu, inp)
+    assert float(o[0].abs().max()) == 0.0 and bool(torch.isinf(lse[0]).all())
+    assert bool(torch.isinf(lse[1, :, 0]).all())          # L = 1, token 0 sits at position -1
+
+
+def test_decode_full_size_sampled(gpu):
+    # the benchmark's workload and launch configuration: B = 64, Hq = 32,
+    # Hkv = 8, 8192 cached keys, one new token; sampled (sequence, head) pairs
+    wl = synth.WORKLOADS[6]
+    _say(f"decode full-size {wl.name}")
+    inp = synth.generate_decode(wl)
+    pairs = [(0, 0), (0, 31), (17, 5), (63, 0), (63, 30)]
+    o, lse = _check(gpu, inp, pairs=pairs)
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    torch.cuda.empty_cache()
