@@ -8,6 +8,8 @@ Wan2.1-14B-shaped video self-attention (B=1, H=40, N=32760, D=128,
 noncausal, MXFP4 P and V).  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload 1..5]
+  python bench.py --backward      causal-training backward (Llama-3.1-8B shape)
+  python bench.py --decode        decode step against a resident KV cache
 """
 
 import argparse
@@ -38,10 +40,14 @@ def parse():
                     help="quantize Q and K with the Four Over Six adaptive block scale (attn_quant_nvfp4_46)")
     ap.add_argument("--backward", action="store_true",
                     help="time the causal-training backward (attn_bwd_fp8) instead of the forward; its own JSON line")
+    ap.add_argument("--decode", action="store_true",
+                    help="time a decode step (workload 6: new tokens against a resident NVFP4/FP8 KV cache); "
+                         "its own JSON line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=16384, help="query rows of the oracle sample")
     ap.add_argument("--cpu-rows-bwd", type=int, default=8192, help="rows of the backward oracle sample")
+    ap.add_argument("--cpu-seqs-dec", type=int, default=8, help="sequences of the decode oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (HBM counter calibration) and exit")
     return ap.parse_args()
@@ -51,26 +57,29 @@ def parse():
 # measured by hardware counters is reported only while they are unchanged.
 KERNEL_SOURCES = ["fwd_lowp.hip", "common.h", "pipeline.h", "fwd_params.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_lowp_kernel_hbm_traffic.md")
+DEC_KERNEL_SOURCES = ["decode.hip", "common.h", "dec_params.h", "fwd_params.h"]
+DEC_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_llama8b_decode.md")
+HBM_PEAK_GBS = 8000.0
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=None):
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, "precision_attention_forward_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, path=TRAFFIC_FILE, sources=None):
     """HBM bytes per launch of the attention kernel for `workload`, from the
     counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by the factor a plain
     copy of known size reads for the same counter), or None when there is no
     figure for this workload or the kernel sources changed since it was taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
-    src = kernel_source_hash()
-    for line in open(TRAFFIC_FILE):
+    src = kernel_source_hash(sources)
+    for line in open(path):
         m = re.match(r"\s*traffic:\s+workload=(\d+)\s+source=([0-9a-f]+)\s+bytes_per_launch=([0-9.eE+]+)", line)
         if m and int(m.group(1)) == workload and m.group(2) == src:
             return float(m.group(3))
@@ -311,6 +320,136 @@ def backward_main(args, torch, paf, synth):
     print(json.dumps(out), flush=True)
 
 
+def cpu_baseline_dec(inp, seqs):
+    """The oracle (as it stands) on a bounded sample of a decode step: every
+    head of the first ``seqs`` sequences, including the quantization of their
+    cache.  Value in GB/s of cache entries processed (the metric's unit)."""
+    import numpy as np
+    from oracle import attention as OA, quant as OQ
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = os.cpu_count() or 1
+    wl = inp.wl
+    nq = inp.q.shape[1]
+    G = wl.Hq // wl.Hkv
+    S = min(seqs, wl.B)
+    amax_q = float(inp.q.abs().max())
+    amax_k = float(inp.k.abs().max())
+    amax_v = float(inp.v.abs().max())
+    qf = inp.q[:S].float().cpu().numpy()
+    kf = inp.k[:S].float().cpu().numpy()
+    vf = inp.v[:S].float().cpu().numpy()
+    keys = 0
+    t = time.perf_counter()
+    for b in range(S):
+        L = int(inp.seqlens[b])
+        keys += L
+        q_index = (L - nq + np.arange(nq)) if wl.causal else None
+        for hk in range(wl.Hkv):
+            kc, ks, gk = OQ.quant_nvfp4(kf[b, hk, :L], amax=amax_k)
+            vcodes, s_v = OQ.quant_v_fp8(vf[b, :, hk], amax=amax_v)
+            vhat = OQ.dequant_v_fp8(vcodes, s_v)[:L]
+            kraw = OQ.dequant_nvfp4_raw(kc, ks)
+            for h in range(hk * G, hk * G + G):
+                qc, qs, gq = OQ.quant_nvfp4(qf[b, :, h], amax=amax_q)
+                OA.attn_lowp_head(OQ.dequant_nvfp4_raw(qc, qs), kraw, gq, gk, vhat, inp.sigma, wl.p_format,
+                                  wl.causal, q_index=q_index)
+    dt = time.perf_counter() - t
+    sub = wl.with_(B=S)
+    by = synth_decode_bytes(sub, inp.seqlens[:S])
+    return {"value": by / dt / 1e9, "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"all {wl.Hq} heads of the first {S} sequences of workload {wl.name} ({keys} cached keys "
+                      f"per head; quantization of their cache included), {dt:.1f} s; numpy float64, "
+                      f"BLAS threads = cores"}
+
+
+def synth_decode_bytes(wl, seqlens):
+    from precision_attention_forward_amd import synth
+    return synth.decode_bytes(wl, seqlens)
+
+
+def decode_main(args, torch, paf, synth):
+    """One step = NVFP4 quantization of the new tokens' Q and the decode
+    kernel against the resident quantized KV cache (written once, as a
+    prefill leaves it).  The metric is bandwidth: the bytes a decode step must
+    move at least (every valid cache entry once, Q, O, LSE) per second."""
+    wl = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = synth.generate_decode(wl, dev)
+    nq = inp.q.shape[1]
+    k = paf.quant_nvfp4(inp.k)
+    vf = paf.V_FP8 if wl.v_format == "fp8" else paf.V_MXFP4
+    vq = paf.quant_v(inp.v, vf)
+    v = (vf, vq[0], vq[1], vq[2])
+    seqlens = inp.seqlens.to(dev)
+    fn = paf.decode_directp if wl.p_format == "mxfp4" else paf.decode_fp8pv
+    kw = dict(B=wl.B, Hq=wl.Hq, Hkv=wl.Hkv, nq=nq, Nk=wl.N, D=wl.D, softmax_scale=inp.sigma, causal=wl.causal,
+              seqlens_k=seqlens)
+    q = paf.quant_nvfp4(inp.q)
+    out = fn(q, k, v, **kw)[:2]
+    kev = HipEvents(args.steps)
+
+    def step(i=None):
+        qq = paf.quant_nvfp4(inp.q)
+        return fn(qq, k, v, out=out, events=None if i is None else kev.handles(i), **kw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    a.record()
+    for i in range(args.steps):
+        step(i)
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = a.elapsed_time(b) / args.steps
+    # the kernel alone: back-to-back launches between two events (the
+    # per-call events above also hold the gap before each launch, which is a
+    # few percent of a 0.2 ms kernel)
+    q = paf.quant_nvfp4(inp.q)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(args.steps):
+        fn(q, k, v, out=out, **kw)
+    b.record()
+    torch.cuda.synchronize()
+    kern_ms = a.elapsed_time(b) / args.steps
+    call_ms = kev.mean_ms()
+    by = synth.decode_bytes(wl, inp.seqlens)
+    fl = synth.decode_flops(wl, inp.seqlens)
+    value = by / (ms * 1e-3) / 1e9
+    kern_gbs = by / (kern_ms * 1e-3) / 1e9
+    traffic = measured_traffic(args.workload, DEC_TRAFFIC_FILE, DEC_KERNEL_SOURCES)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_dec(inp, args.cpu_seqs_dec)
+    pf = "MXFP4 P (Direct-P)" if wl.p_format == "mxfp4" else "FP8 E4M3 P"
+    vfn = "FP8 E4M3 V" if wl.v_format == "fp8" else "MXFP4 V"
+    out_line = {
+        "metric": "Direct-P decode attention bandwidth (KV cache + Q + O bytes per second) on 1 MI355X",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp4+fp8", "data": "synthetic (seeded Gaussian Q, K cache and V cache)",
+        "config": {"workload": f"{wl.name}: B={wl.B} sequences x {nq} new token(s), Hq={wl.Hq} Hkv={wl.Hkv} "
+                               f"D={wl.D}, {wl.N} cached keys each; NVFP4 Q/K, {pf}, {vfn}",
+                   "B": wl.B, "nq": nq, "Hq": wl.Hq, "Hkv": wl.Hkv, "cached_keys": wl.N, "D": wl.D,
+                   "bytes_per_step": by, "flops_per_step": fl, "parallelism": "single GPU"},
+        "kernel_tflops": round(fl / (kern_ms * 1e-3) / 1e12, 2),
+        "kernel_call_ms": round(call_ms, 4),
+        "q_quant_ms": round(ms - call_ms, 4),
+        "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "decode_kernel", "kernel_ms": round(kern_ms, 4)},
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(out_line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -325,7 +464,16 @@ def main():
 
     paf.load_library()
     if args.workload is None:
-        args.workload = 4 if args.backward else 2
+        args.workload = 6 if args.decode else (4 if args.backward else 2)
+    if args.decode:
+        if "nq" not in synth.WORKLOADS[args.workload].extra:
+            print("--decode takes a decode workload (6)", file=sys.stderr)
+            sys.exit(2)
+        decode_main(args, torch, paf, synth)
+        return
+    if "nq" in synth.WORKLOADS[args.workload].extra:
+        print(f"workload {args.workload} is a decode step: use --decode", file=sys.stderr)
+        sys.exit(2)
     if args.backward:
         backward_main(args, torch, paf, synth)
         return

@@ -290,15 +290,19 @@ attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, 
  *           [B, Nk, Hkv, D] tensor (cols = B * roundup(Nk, 128))
  *   seqlens_k : nullable device int32 [B], the number of valid cache
  *           entries of each sequence (values are clamped to [0, Nk]); NULL
- *           means Nk for every sequence
+ *           means Nk for every sequence.  The kernel reads whole 128-key
+ *           tiles: cache entries past a sequence's valid length up to the
+ *           next multiple of 128 are read and masked, so they must hold
+ *           finite codes (zeros, or stale entries written by the quantizers)
  *   causal: new token i (0-based) of a sequence with L valid keys sits at
  *           position L - nq + i and sees keys 0 .. L - nq + i (the new
  *           tokens are the last nq entries of the cache); otherwise every
  *           new token sees all L keys.  With nq == 1 both are the same.
  *   o     : [B, nq, Hq, D] (o_dtype); lse: nullable float [B, Hq, nq]
  * A row with no visible key gets O = 0 and LSE = -inf.
- * Limits: D in {64, 128}; Hq % Hkv == 0; 1 <= nq; D * B * roundup(Nk, 128)
- * below 2^31.  attn_decode_fp8pv requires FP8 V.  Optional probability dump
+ * Limits: D in {64, 128}; Hq % Hkv == 0; 1 <= nq; the cache capacity Nk a
+ * multiple of 128 (ATTN_ERR_INVALID_ARGUMENT otherwise); D * B * Nk below
+ * 2^31 (ATTN_ERR_UNSUPPORTED otherwise).  attn_decode_fp8pv requires FP8 V.  Optional probability dump
  * of (dbg_b, dbg_h): codes [nq, roundup(Nk,128)/2] (MXFP4 P) or
  * [nq, roundup(Nk,128)] (FP8 P), E8M0 bytes [nq, roundup(Nk,128)/32].
  * prof_event_begin/end (hipEvent_t, nullable) are recorded around the kernel.

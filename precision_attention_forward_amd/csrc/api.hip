@@ -373,6 +373,7 @@ static attn_status validate_decode(const attn_decode_args* a, int pf) {
   if (a == nullptr) return ATTN_ERR_INVALID_ARGUMENT;
   if (a->B < 0 || a->Hq <= 0 || a->Hkv <= 0 || a->nq < 1 || a->Nk < 0) return ATTN_ERR_INVALID_ARGUMENT;
   if (a->D != 64 && a->D != 128) return ATTN_ERR_INVALID_ARGUMENT;
+  if (a->Nk % 128 != 0) return ATTN_ERR_INVALID_ARGUMENT;   // cache capacity in whole 128-key tiles
   if (a->Hq % a->Hkv != 0) return ATTN_ERR_INVALID_ARGUMENT;
   if (!(a->softmax_scale > 0.0f) || a->softmax_scale != a->softmax_scale) return ATTN_ERR_INVALID_ARGUMENT;
   if (a->v.format != ATTN_V_FP8_E4M3 && a->v.format != ATTN_V_MXFP4) return ATTN_ERR_INVALID_ARGUMENT;
@@ -429,7 +430,7 @@ static attn_status run_decode(const attn_decode_args* a, void* stream, int pf) {
   p.Hkv = a->Hkv;
   p.nq = a->nq;
   p.Nk = a->Nk;
-  p.QG = (int)(((int64_t)(a->Hq / a->Hkv) * a->nq + 31) / 32);
+  p.QG = (int)(((int64_t)(a->Hq / a->Hkv) * a->nq + 15) / 16);   // 16 query rows per workgroup
   p.nk_pad = roundup(a->Nk, 128);
   p.cols = (int64_t)a->B * p.nk_pad;
   p.sigma = a->softmax_scale;
@@ -443,7 +444,9 @@ static attn_status run_decode(const attn_decode_args* a, void* stream, int pf) {
     e = hipEventRecord((hipEvent_t)a->prof_event_begin, st);
     if (e != hipSuccess) return hip_status(e);
   }
-  e = launch_decode(p, a->D, pf, a->v.format == ATTN_V_MXFP4 ? 1 : 0, a->causal != 0, a->dbg_p_codes != nullptr, st);
+  // with one new token the causal mask hides nothing (the token is the last key)
+  const bool causal = a->causal != 0 && a->nq > 1;
+  e = launch_decode(p, a->D, pf, a->v.format == ATTN_V_MXFP4 ? 1 : 0, causal, a->dbg_p_codes != nullptr, st);
   if (e != hipSuccess) return hip_status(e);
   if (a->prof_event_end != nullptr) e = hipEventRecord((hipEvent_t)a->prof_event_end, st);
   return hip_status(e);

@@ -20,23 +20,25 @@
 //    packed FP16 multiply by the block scale: E2M1 x E4M3 has at most 6
 //    significant bits), where the prefill path expands K in HBM once and
 //    re-reads it for every query block.
-//  * One workgroup of four waves per (sequence, KV head, 32 query rows): the
+//  * One workgroup of four waves per (sequence, KV head, 16 query rows): the
 //    G * nq query rows of a KV head are the columns of S^T = K Q^T, so the
-//    cache is read once for the whole GQA group.  Waves take interleaved
-//    64-key chunks (step s: wave w takes chunk 4s + w, i.e. two 128-key tiles
-//    per step), keep their own O / l partials, and exchange per-chunk row
-//    maxima through LDS once per step, so that every wave encodes with the
-//    running max m' of its own tile: the codes of one sequential pass, which
-//    splitting the keys over independent workgroups would not give.
-//  * Each wave loads its chunks from HBM straight into registers two steps
+//    cache is read once for the whole GQA group.  With so few rows the 16x16
+//    matrix instructions waste least: S^T on v_mfma_f32_16x16x32_f16, P.V and
+//    the row sum l on v_mfma_scale_f32_16x16x128_f8f6f4 (l against a constant
+//    0/1 operand, so it sums exactly the rounded probabilities).  The key rows
+//    of each 16-key S^T sub-tile are permuted so that every group of 16 lanes
+//    ends up holding, for its query, the 32 keys its probability operand
+//    needs: one E8M0 block for MXFP4 P, whose block max, exponent and codes
+//    are then lane-local.
+//  * Waves take interleaved 128-key tiles (step s: wave w takes tile 4s + w),
+//    keep their own O / l partials, and exchange per-tile row maxima through
+//    LDS once per step, so that every wave encodes with the running max m' of
+//    its own tile: the codes of one sequential pass, which splitting the keys
+//    over independent workgroups would not give.
+//  * Each wave loads its tiles from HBM straight into registers two steps
 //    ahead (no LDS staging: no other wave reads them).
 //  * At the end the four partials are rescaled to the final max and summed
 //    through LDS.
-//  * S^T, P.V and l use the operand layouts of the prefill kernel: S^T on
-//    v_mfma_f32_32x32x16_f16 with one query per lane, each lane holding the 32
-//    keys of one P block (MXFP4) or the 32 keys the FP8 operand wants; P.V on
-//    v_mfma_scale_f32_32x32x64_f8f6f4; l on one 16x16x128 scaled MFMA per chunk
-//    against a constant 0/1 operand.
 #include "common.h"
 #include "dec_params.h"
 #include "fwd_params.h"
@@ -44,46 +46,46 @@
 namespace attn {
 
 constexpr int DEC_WAVES = 4;
-constexpr int DEC_CHUNK = 64;
+constexpr int DEC_Q = 16;          // query rows per workgroup (columns of S^T)
 
-// Key (0..63) of a 64-key chunk held by S^T sub-tile s2 (0, 1), accumulator
-// register v (0..15), lane half hh.  MXFP4 P: lane half hh holds the 32 keys
-// of one P block; FP8 P: the k order of the FP8 operand of the 32x32x64 MFMA
-// (k-block 0 = bytes 0-15 of both lane halves).
+// Key (0..127) of a 128-key tile at S^T sub-tile st (0..7), output row r
+// (0..15) of the 16x16 MFMA: lane group g = r / 4 ends up holding, over the
+// eight sub-tiles, exactly the 32 keys its probability operand needs in the
+// 16x16x128 scaled MFMA -- MXFP4: keys 32 g + [0, 32) (one P block); FP8:
+// keys 16 g + [0, 16) and 64 + 16 g + [0, 16) (the FP8 operand order) --
+// with element 4 st + (r % 4) in operand order.
 template <int PF>
-__host__ __device__ inline int dec_key(int s2, int v, int hh) {
-  return PF == PF_MXFP4 ? 32 * hh + 16 * s2 + v : 32 * s2 + 16 * hh + v;
+__host__ __device__ inline int dec_key(int st, int r) {
+  const int g = r >> 2, i = r & 3;
+  if (PF == PF_MXFP4) return 32 * g + 4 * st + i;
+  return st < 4 ? 16 * g + 4 * st + i : 64 + 16 * g + 4 * (st - 4) + i;
 }
 
-// Operands of one 64-key chunk, as one lane holds them.
+// Operands of one 128-key tile, as one lane holds them.
 template <int D, int VF>
 struct DecBuf {
-  u32x4 kc[2][D / 64];                       // K codes of the lane's key, its D/2 channels, per sub-tile
-  uint32_t ks[2];                            // their E4M3 block scales (D/32 bytes)
-  u32x4 va[D / 32][VF == VF_FP8 ? 2 : 1];    // V^T operand per 32 channels
-  uint32_t vs[VF == VF_MXFP4 ? D / 32 : 1];  // MXFP4 V: E8M0 bytes of the tile's 4 blocks
+  u32x4 kc[8];                               // K codes of the lane's key in sub-tile st, channels of its group
+  uint32_t ks[8];                            // their E4M3 block scales (D/64 bytes)
+  u32x4 va[D / 16][VF == VF_FP8 ? 2 : 1];    // V^T operand per 16 channels
+  uint32_t vs[VF == VF_MXFP4 ? D / 16 : 1];  // MXFP4 V: E8M0 bytes of the tile's four blocks
 };
 
 template <int D, int PF, int VF, bool CAUSAL, bool DEBUG>
 __global__ void __launch_bounds__(256, 1) decode_kernel(DecParams p) {
-  constexpr int KS = D / 16;     // k-steps of the S MFMA
-  constexpr int DT = D / 32;     // 32-row tiles of O^T
+  constexpr int KS = D / 32;     // k-steps (32 channels) of the S MFMA
+  constexpr int DT = D / 16;     // 16-row tiles of O^T
   constexpr int HALF = D / 2;    // code bytes per row
-  constexpr int LB = D / 4;      // code bytes of one lane half (D/2 channels)
-  constexpr int LS = D / 32;     // scale bytes of one lane half
+  constexpr int GC = D / 4;      // channels of one lane group
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  float* sM = reinterpret_cast<float*>(smem);                       // [2][DEC_WAVES][32] chunk maxima
-  float* sO = sM + 2 * DEC_WAVES * 32;                              // [DEC_WAVES][DT][16][64] partial O
-  float* sL = sO + DEC_WAVES * DT * 16 * 64;                        // [DEC_WAVES][64] partial l
+  float* sM = reinterpret_cast<float*>(smem);                       // [2][DEC_WAVES][16] tile maxima
+  float* sO = sM + 2 * DEC_WAVES * DEC_Q;                           // [DEC_WAVES][DT][4][64] partial O
+  float* sL = sO + DEC_WAVES * DT * 4 * 64;                         // [DEC_WAVES][64] partial l
 
   // ---- workgroup -> (sequence, KV head, query group)
-  int lin = blockIdx.x;
-  int qg = lin % p.QG;
-  int hk = (lin / p.QG) % p.Hkv;
-  int b = lin / (p.QG * p.Hkv);
-  qg = __builtin_amdgcn_readfirstlane(qg);
-  hk = __builtin_amdgcn_readfirstlane(hk);
-  b = __builtin_amdgcn_readfirstlane(b);
+  const int lin = blockIdx.x;
+  const int qg = __builtin_amdgcn_readfirstlane(lin % p.QG);
+  const int hk = __builtin_amdgcn_readfirstlane((lin / p.QG) % p.Hkv);
+  const int b = __builtin_amdgcn_readfirstlane(lin / (p.QG * p.Hkv));
   int len_k = p.seqlens != nullptr ? p.seqlens[b] : p.Nk;
   len_k = len_k < 0 ? 0 : (len_k > p.Nk ? p.Nk : len_k);          // reads stay inside the cache
   len_k = __builtin_amdgcn_readfirstlane(len_k);
@@ -92,27 +94,27 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(DecParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hh = lane >> 5, ql = lane & 31;
-  // query row of this lane's S^T column: row r = token i * G + head g
-  const int my_r = 32 * qg + ql;
+  const int n = lane & 15, g = lane >> 4;
+  // query row of this lane's S^T column: row r = token i * G + head
+  const int my_r = DEC_Q * qg + n;
   const bool row_ok = my_r < R;
   const int my_i = row_ok ? my_r / G : 0;
   const int my_h = hk * G + (row_ok ? my_r % G : 0);
   const int my_pos = len_k - p.nq + my_i;                            // absolute position (causal)
 
-  const int n_chunks = (len_k + DEC_CHUNK - 1) / DEC_CHUNK;
-  const int n_steps = (n_chunks + DEC_WAVES - 1) / DEC_WAVES;
+  const int n_tiles = (len_k + KEY_TILE - 1) / KEY_TILE;
+  const int n_steps = (n_tiles + DEC_WAVES - 1) / DEC_WAVES;
 
   const float cc = (float)((double)p.sigma * 1.4426950408889634 * (double)(*p.gq) * (double)(*p.gk));
   const float vscale = VF == VF_FP8 ? *p.sv : 1.0f;
 
-  // ---- Q operand (B of S^T): lane holds query row my_r, channels
-  // [hh D/2, hh D/2 + D/2), decoded from NVFP4 (exact in FP16)
+  // ---- Q operand (B of S^T, 16x16x32): lane (n, g) holds query row my_r,
+  // channels GC g + 8 ks + [0, 8) in k-step ks, decoded from NVFP4 (exact in FP16)
   f16x8 qf[KS];
   {
     const int64_t row = row_ok ? ((int64_t)b * p.nq + my_i) * p.Hq + my_h : 0;
-    const uint8_t* qc = p.q_codes + row * HALF + hh * LB;
-    const uint8_t* qs = p.q_scales + row * (D / 16) + hh * LS;
+    const uint8_t* qc = p.q_codes + row * HALF + g * (GC / 2);
+    const uint8_t* qs = p.q_scales + row * (D / 16) + g * (GC / 16);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const uint32_t cw = row_ok ? *reinterpret_cast<const uint32_t*>(qc + 4 * ks) : 0u;
@@ -123,137 +125,133 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(DecParams p) {
   }
 
   // ---- per-lane load offsets (bytes, below 2^31; the host checks D * cols)
-  // A operand of S^T: lane (r, hh) reads the key of accumulator row r of
-  // sub-tile s2 (rows of the 32x32 output: r = 8 (v / 4) + 4 hh' + v % 4),
-  // channels [hh D/2, hh D/2 + D/2).
-  const int rr = lane & 31;
-  const int kl0 = dec_key<PF>(0, 4 * (rr >> 3) + (rr & 3), (rr >> 2) & 1);
-  const int kl1 = dec_key<PF>(1, 4 * (rr >> 3) + (rr & 3), (rr >> 2) & 1);
+  const int rr = lane & 15;
   const uint8_t* khead = p.k_codes + ((int64_t)b * p.Hkv + hk) * p.Nk * HALF;
   const uint8_t* shead = p.k_scales + ((int64_t)b * p.Hkv + hk) * p.Nk * (D / 16);
   const int64_t col0 = (int64_t)b * p.nk_pad;
   const uint8_t* vhead = VF == VF_MXFP4 ? p.v_codes + (int64_t)hk * D * (p.cols / 2) + col0 / 2
                                         : p.v_codes + (int64_t)hk * D * p.cols + col0;
   const uint8_t* vshead = VF == VF_MXFP4 ? p.v_scales + (int64_t)hk * D * (p.cols / 32) + col0 / 32 : nullptr;
+  const uint32_t vrow = (uint32_t)rr * (uint32_t)(VF == VF_MXFP4 ? p.cols / 2 : p.cols);   // V^T row rr of a 16-row tile
+  const uint32_t vdt = 16u * (uint32_t)(VF == VF_MXFP4 ? p.cols / 2 : p.cols);             // next 16 rows
+
+  // K rows of the lane in each sub-tile (loop invariant).  Keys past the
+  // sequence but inside its cache (the capacity is whole 128-key tiles) are
+  // read and masked later, so no per-lane clamping is needed.
+  uint32_t koff[8], soff[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    const int kl = dec_key<PF>(st, rr);
+    koff[st] = (uint32_t)(kl * HALF + g * (GC / 2));
+    soff[st] = (uint32_t)(kl * (D / 16) + g * (GC / 16));
+  }
+  const uint32_t voff = vrow + 16u * (uint32_t)g;
+  const uint32_t vsoff = (uint32_t)rr * (uint32_t)(p.cols / 32);
 
   auto load = [&](DecBuf<D, VF>& bf, int s) {
     int jc = s * DEC_WAVES + wave;
-    jc = jc < n_chunks ? jc : n_chunks - 1;      // past the end: the last chunk again (a cache hit)
-    const int key0 = jc * DEC_CHUNK;
+    jc = jc < n_tiles ? jc : n_tiles - 1;        // past the end: the last tile again (a cache hit)
+    const int key0 = jc * KEY_TILE;
     const uint8_t* kb = khead + (int64_t)key0 * HALF;
     const uint8_t* sb = shead + (int64_t)key0 * (D / 16);
-    const int last = len_k - 1 - key0;           // keys past the sequence read its last key instead
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const int kl = s2 == 0 ? kl0 : kl1;
-      const int kr = kl <= last ? kl : last;
-      const uint32_t ko = (uint32_t)(kr * HALF + hh * LB);
-      const uint32_t so = (uint32_t)(kr * (D / 16) + hh * LS);
-#pragma unroll
-      for (int c = 0; c < D / 64; ++c) bf.kc[s2][c] = *reinterpret_cast<const u32x4*>(kb + ko + 16 * c);
-      if (D == 128) bf.ks[s2] = *reinterpret_cast<const uint32_t*>(sb + so);
-      else bf.ks[s2] = *reinterpret_cast<const uint16_t*>(sb + so);
+    for (int st = 0; st < 8; ++st) {
+      if (D == 128) {
+        bf.kc[st] = *reinterpret_cast<const u32x4*>(kb + koff[st]);
+        bf.ks[st] = *reinterpret_cast<const uint16_t*>(sb + soff[st]);
+      } else {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(kb + koff[st]);
+        bf.kc[st] = u32x4{w[0], w[1], 0u, 0u};
+        bf.ks[st] = sb[soff[st]];
+      }
     }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const uint32_t d = (uint32_t)(32 * dt + ql);
       if (VF == VF_FP8) {
-        const uint8_t* vb = vhead + key0;
-        bf.va[dt][0] = *reinterpret_cast<const u32x4*>(vb + d * (uint32_t)p.cols + 16 * hh);
-        bf.va[dt][VF == VF_FP8 ? 1 : 0] = *reinterpret_cast<const u32x4*>(vb + d * (uint32_t)p.cols + 16 * hh + 32);
+        const uint8_t* vb = vhead + key0 + (int64_t)dt * vdt;
+        bf.va[dt][0] = *reinterpret_cast<const u32x4*>(vb + voff);
+        bf.va[dt][VF == VF_FP8 ? 1 : 0] = *reinterpret_cast<const u32x4*>(vb + voff + 64);
       } else {
-        const uint8_t* vb = vhead + key0 / 2;
-        bf.va[dt][0] = *reinterpret_cast<const u32x4*>(vb + d * (uint32_t)(p.cols / 2) + 16 * hh);
-        const uint8_t* vsb = vshead + (key0 / 128) * 4;
-        bf.vs[VF == VF_MXFP4 ? dt : 0] = *reinterpret_cast<const uint32_t*>(vsb + d * (uint32_t)(p.cols / 32));
+        const uint8_t* vb = vhead + key0 / 2 + (int64_t)dt * vdt;
+        bf.va[dt][0] = *reinterpret_cast<const u32x4*>(vb + voff);
+        const uint8_t* vsb = vshead + key0 / 32 + (int64_t)dt * 16 * (p.cols / 32);
+        bf.vs[VF == VF_MXFP4 ? dt : 0] = *reinterpret_cast<const uint32_t*>(vsb + vsoff);
       }
     }
   };
 
   // constant 0/1 operand of the row-sum MFMA (16x16x128, FP4 1.0 = code 2):
-  // lane l of the accumulator ends up with the sum of query l % 32
+  // rows 0, 4, 8, 12 sum all 128 keys, so register 0 of every lane holds l of its query
   i32x8 ones = {0, 0, 0, 0, 0, 0, 0, 0};
-  {
-    const int row = lane & 15, g = lane >> 4;
-    const bool r0 = (row == 0 || row == 8), r1 = (row == 4 || row == 12);
-    if (PF == PF_MXFP4) {
-      // rows 0/8 sum k-blocks {0,2}, rows 4/12 k-blocks {1,3}; lane holds k = 32g + [0,32)
-      const bool on = (r0 && (g == 0 || g == 2)) || (r1 && (g == 1 || g == 3));
-      if (on) { ones[0] = ones[1] = ones[2] = ones[3] = 0x22222222; }
-    } else {
-      // FP8 P: rows 0/8 sum k with k%32 < 16, rows 4/12 k%32 >= 16
-      if (r0) { ones[0] = ones[1] = 0x22222222; }
-      if (r1) { ones[2] = ones[3] = 0x22222222; }
-    }
-  }
+  if ((rr & 3) == 0) { ones[0] = ones[1] = ones[2] = ones[3] = 0x22222222; }
 
-  f32x16 oacc[DT];
+  f32x4 oacc[DT];
 #pragma unroll
-  for (int i = 0; i < DT; ++i) oacc[i] = f32x16{};
+  for (int i = 0; i < DT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
   float m_run = -__builtin_inff();   // running max after the last tile (same in every wave)
   float m_w = -__builtin_inff();     // max the wave's partial O / l refer to
 
-  // ---- one step: chunk j = 4 s + wave
+  // ---- one step: tile j = 4 s + wave
   auto body = [&](int s, const DecBuf<D, VF>& bf) {
     const int j = s * DEC_WAVES + wave;
-    const bool live = j < n_chunks;            // wave-uniform
-    f32x16 sacc[2];
+    const bool live = j < n_tiles;             // wave-uniform
+    f32x4 sacc[8];
     float bm = -__builtin_inff();
     if (live) {
-      // S^T = K Q^T for the chunk's two 32-key sub-tiles
+      // S^T = K Q^T, eight 16-key sub-tiles
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const f16x2 sc01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bf.ks[s2], 1.0f, false);
-        const f16x2 sc23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bf.ks[s2], 1.0f, true);
+      for (int st = 0; st < 8; ++st) {
+        const f16x2 scp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bf.ks[st], 1.0f, false);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const uint32_t w = bf.kc[s2][ks >> 2][ks & 3];
-          const int blk = ks >> 1;               // block of 16 channels within the lane's half
-          const _Float16 sc = blk == 0 ? sc01[0] : blk == 1 ? sc01[1] : blk == 2 ? sc23[0] : sc23[1];
+          const uint32_t w = bf.kc[st][ks];
+          const _Float16 sc = (ks >> 1) == 0 ? scp[0] : scp[1];   // block of 16 channels
           const f16x2 s2v = {sc, sc};
           const f16x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2v;
           const f16x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2v;
           const f16x2 e2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2v;
           const f16x2 e3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2v;
           const f16x8 a = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
-          sacc[s2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ks], ks == 0 ? f32x16{} : sacc[s2], 0, 0, 0);
+          sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[st],
+                                                            0, 0, 0);
         }
       }
       // mask keys past the sequence and (causal) past each row's position
-      const int key0 = j * DEC_CHUNK;
-      if (key0 + DEC_CHUNK > len_k || (CAUSAL && key0 + DEC_CHUNK - 1 > len_k - p.nq)) {
+      const int key0 = j * KEY_TILE;
+      if (key0 + KEY_TILE > len_k || (CAUSAL && key0 + KEY_TILE - 1 > len_k - p.nq)) {
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
+        for (int st = 0; st < 8; ++st)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = key0 + dec_key<PF>(s2, v, hh);
+          for (int i = 0; i < 4; ++i) {
+            const int key = key0 + dec_key<PF>(st, 4 * g + i);
             const bool dead = key >= len_k || (CAUSAL && key > my_pos);
-            if (dead) sacc[s2][v] = -__builtin_inff();
+            if (dead) sacc[st][i] = -__builtin_inff();
           }
       }
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) bm = __builtin_fmaxf(bm, sacc[s2][v]);
+      for (int st = 0; st < 8; ++st)
+        bm = __builtin_fmaxf(bm, __builtin_fmaxf(__builtin_fmaxf(sacc[st][0], sacc[st][1]),
+                                                 __builtin_fmaxf(sacc[st][2], sacc[st][3])));
     }
-    // chunk max of the lane's query (both lane halves), through LDS to every wave
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
-    const float cmax = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    float* slot = sM + (s & 1) * DEC_WAVES * 32;
-    if (hh == 0) slot[wave * 32 + ql] = cmax;
+    // tile max of the lane's query (its four lane groups), through LDS to every wave
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+    float tm = __builtin_fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(tm), __float_as_uint(tm), false, false);
+    tm = __builtin_fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+    float* slot = sM + (s & 1) * DEC_WAVES * DEC_Q;
+    if (g == 0) slot[wave * DEC_Q + n] = tm;
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    // running max after each of the step's two tiles; this wave's tile is wave / 2
+    // running max after each of the step's four tiles; this wave's tile is the wave-th
     float m_tile = m_run;
 #pragma unroll
-    for (int t = 0; t < DEC_WAVES / 2; ++t) {
-      const float tmax = __builtin_fmaxf(slot[(2 * t) * 32 + ql], slot[(2 * t + 1) * 32 + ql]) * cc;
-      m_run = __builtin_fmaxf(m_run, tmax);
-      if (t == (wave >> 1)) m_tile = m_run;
+    for (int t = 0; t < DEC_WAVES; ++t) {
+      m_run = __builtin_fmaxf(m_run, slot[t * DEC_Q + n] * cc);
+      if (t == wave) m_tile = m_run;
     }
     if (!live) return;
 
-    // ---- encode the chunk with m' of its tile
+    // ---- encode the tile with m' (its running max)
     const bool row_dead = m_tile == -__builtin_inff();
     int psc;
     float me;
@@ -269,14 +267,14 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(DecParams p) {
     }
     i32x8 pw = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
+    for (int st = 0; st < 8; ++st)
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int v = 2 * k;
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[s2][v], cc, -me));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[s2][v + 1], cc, -me));
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[st][2 * h2], cc, -me));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[st][2 * h2 + 1], cc, -me));
         if (PF == PF_MXFP4) {
-          const int word = 2 * s2 + (k >> 2), byte = k & 3;   // key 16 s2 + v of the lane's block
+          // element 4 st + 2 h2 (+1): word st / 2, byte 2 (st % 2) + h2
+          const int word = st >> 1, byte = 2 * (st & 1) + h2;
           uint32_t w = (uint32_t)pw[word];
           if (byte == 0) w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p0, p1, 1.0f, 0);
           else if (byte == 1) w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p0, p1, 1.0f, 1);
@@ -284,24 +282,23 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(DecParams p) {
           else w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p0, p1, 1.0f, 3);
           pw[word] = (int)w;
         } else {
-          const int word = 4 * s2 + (k >> 1);
-          if (k & 1) pw[word] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pw[word], true);
-          else pw[word] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pw[word], false);
+          // element 4 st + 2 h2 (+1): word st, bytes 2 h2, 2 h2 + 1
+          if (h2) pw[st] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pw[st], true);
+          else pw[st] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pw[st], false);
         }
       }
     if (DEBUG && b == p.dbg_b && my_h == p.dbg_h && row_ok) {
       const int64_t row = (int64_t)my_i * p.dbg_ld;
-      const int key0 = j * DEC_CHUNK;
+      const int key0 = j * KEY_TILE;
       if (PF == PF_MXFP4) {
-        const int key = key0 + 32 * hh;
+        const int key = key0 + 32 * g;
         *reinterpret_cast<u32x4*>(p.dbg_codes + (row + key) / 2) =
             u32x4{(uint32_t)pw[0], (uint32_t)pw[1], (uint32_t)pw[2], (uint32_t)pw[3]};
         p.dbg_scales[(row + key) / 32] = (uint8_t)psc;
       } else {
-        const int key = key0 + 16 * hh;
-        *reinterpret_cast<u32x4*>(p.dbg_codes + row + key) =
+        *reinterpret_cast<u32x4*>(p.dbg_codes + row + key0 + 16 * g) =
             u32x4{(uint32_t)pw[0], (uint32_t)pw[1], (uint32_t)pw[2], (uint32_t)pw[3]};
-        *reinterpret_cast<u32x4*>(p.dbg_codes + row + key + 32) =
+        *reinterpret_cast<u32x4*>(p.dbg_codes + row + key0 + 64 + 16 * g) =
             u32x4{(uint32_t)pw[4], (uint32_t)pw[5], (uint32_t)pw[6], (uint32_t)pw[7]};
       }
     }
@@ -312,7 +309,7 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(DecParams p) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+        for (int i = 0; i < 4; ++i) oacc[dt][i] *= alpha;
       lacc[0] *= alpha;
     }
     m_w = m_tile;
@@ -321,20 +318,16 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(DecParams p) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       if (VF == VF_MXFP4) {
-        const i32x8 a = {(int)bf.va[dt][0][0], (int)bf.va[dt][0][1], (int)bf.va[dt][0][2], (int)bf.va[dt][0][3],
-                         0, 0, 0, 0};
-        const int vsc = (int)(bf.vs[VF == VF_MXFP4 ? dt : 0] >> (8 * hh));   // byte 2c: block (c, hh)
-        if (wave & 1)
-          oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pw, oacc[dt], 4, PF == PF_MXFP4 ? 4 : 0, 2,
-                                                                     vsc, 0, psc);
-        else
-          oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pw, oacc[dt], 4, PF == PF_MXFP4 ? 4 : 0, 0,
-                                                                     vsc, 0, psc);
+        const u32x4 x = bf.va[dt][0];
+        const i32x8 a = {(int)x[0], (int)x[1], (int)x[2], (int)x[3], 0, 0, 0, 0};
+        const int vsc = (int)(bf.vs[VF == VF_MXFP4 ? dt : 0] >> (8 * g));   // block g of the tile
+        oacc[dt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, pw, oacc[dt], 4, PF == PF_MXFP4 ? 4 : 0, 0,
+                                                                    vsc, 0, psc);
       } else {
         const u32x4 x = bf.va[dt][0], y = bf.va[dt][VF == VF_FP8 ? 1 : 0];
         const i32x8 a = {(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
-        oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pw, oacc[dt], 0, PF == PF_MXFP4 ? 4 : 0, 0, 127,
-                                                                   0, psc);
+        oacc[dt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, pw, oacc[dt], 0, PF == PF_MXFP4 ? 4 : 0, 0, 127,
+                                                                    0, psc);
       }
     }
   };
@@ -362,43 +355,39 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(DecParams p) {
   const float f = m_w == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_w - m_run);
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) sO[((wave * DT + dt) * 16 + v) * 64 + lane] = oacc[dt][v] * f;
+    *reinterpret_cast<f32x4*>(sO + ((wave * DT + dt) * 64 + lane) * 4) =
+        f32x4{oacc[dt][0] * f, oacc[dt][1] * f, oacc[dt][2] * f, oacc[dt][3] * f};
   sL[wave * 64 + lane] = lacc[0] * f;
   __syncthreads();
-  if (wave >= DT || !row_ok) return;
+  if (!row_ok) return;
   float l = 0.0f;
 #pragma unroll
   for (int w = 0; w < DEC_WAVES; ++w) l += sL[w * 64 + lane];
   const bool empty = !(l > 0.0f);
   const float inv = empty ? 0.0f : vscale / l;
-  const int dt = wave;
   const int64_t orow = (((int64_t)b * p.nq + my_i) * p.Hq + my_h) * (int64_t)D;
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const int d = 32 * dt + 8 * jj + 4 * hh;
-    float o4[4];
+  for (int k = 0; k < DT / DEC_WAVES; ++k) {
+    const int dt = wave * (DT / DEC_WAVES) + k;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int w = 0; w < DEC_WAVES; ++w) acc += sO[((w * DT + dt) * 16 + 4 * jj + k) * 64 + lane];
-      o4[k] = acc * inv;
-    }
+    for (int w = 0; w < DEC_WAVES; ++w) acc += *reinterpret_cast<const f32x4*>(sO + ((w * DT + dt) * 64 + lane) * 4);
+    const f32x4 o4 = acc * inv;
+    const int d = 16 * dt + 4 * g;
     if (p.o_f32) {
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o) + orow + d) = f32x4{o4[0], o4[1], o4[2], o4[3]};
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o) + orow + d) = o4;
     } else {
       uint32_t u[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t x = __float_as_uint(o4[k]);
-        u[k] = (x + 0x7FFFu + ((x >> 16) & 1u)) >> 16;   // round to nearest even
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t x = __float_as_uint(o4[q]);
+        u[q] = (x + 0x7FFFu + ((x >> 16) & 1u)) >> 16;   // round to nearest even
       }
       *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.o) + orow + d) =
           u32x2{u[0] | (u[1] << 16), u[2] | (u[3] << 16)};
     }
   }
-  if (p.lse != nullptr && dt == 0 && hh == 0) {
+  if (p.lse != nullptr && wave == 0 && g == 0) {
     const float lse = empty ? -__builtin_inff() : 0.6931471805599453f * (m_run + __builtin_log2f(l));
     p.lse[((int64_t)b * p.Hq + my_h) * p.nq + my_i] = lse;
   }
@@ -406,7 +395,7 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(DecParams p) {
 
 template <int D, int VF>
 constexpr int dec_lds_bytes() {
-  return (2 * DEC_WAVES * 32 + DEC_WAVES * (D / 32) * 16 * 64 + DEC_WAVES * 64) * 4;
+  return (2 * DEC_WAVES * DEC_Q + DEC_WAVES * (D / 16) * 4 * 64 + DEC_WAVES * 64) * 4;
 }
 
 template <int D, int PF, int VF, bool CAUSAL, bool DEBUG>

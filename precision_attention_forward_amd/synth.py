@@ -135,7 +135,8 @@ class DecodeInputs:
 
 
 def generate_decode(wl: Workload, device="cpu") -> DecodeInputs:
-    """Inputs of a decode step: ``wl.N`` is the cache capacity, ``extra["nq"]``
+    """Inputs of a decode step: ``wl.N`` is the cache capacity (whole
+    128-key tiles), ``extra["nq"]``
     the new tokens per sequence and ``extra["ragged"]`` (optional) draws the
     valid lengths from U{1..N} instead of taking N for every sequence.
     Draw order: lengths (ragged only), then Q, K, V as float32 standard

@@ -172,7 +172,7 @@ def test_fwd_validation(lib):
 
 def _dec_args(**kw):
     a = B.DecodeArgs()
-    a.B, a.Hq, a.Hkv, a.nq, a.Nk, a.D = 2, 8, 2, 1, 1000, 128
+    a.B, a.Hq, a.Hkv, a.nq, a.Nk, a.D = 2, 8, 2, 1, 1024, 128
     a.softmax_scale = 0.125
     p = 1 << 24
     a.q = B._NvTensor(p, p, p)
@@ -192,6 +192,7 @@ def test_decode_validation(lib):
     assert d(Hkv=3) == 1
     assert d(nq=0) == 1
     assert d(Nk=-1) == 1
+    assert d(Nk=1000) == 1                                         # capacity in whole 128-key tiles
     assert d(softmax_scale=0.0) == 1
     assert d(softmax_scale=float("nan")) == 1
     assert d(o=None) == 1

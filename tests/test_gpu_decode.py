@@ -107,19 +107,19 @@ def _check(gpu, inp, pairs=None):
 W = synth.WORKLOADS[6]
 SMALL = [
     # Direct-P, FP8 V, one new token, ragged cache lengths, GQA 4
-    ("directp_fp8v_nq1", W.with_(B=3, Hq=8, Hkv=2, N=1000, seed=61, extra={"nq": 1, "ragged": True})),
+    ("directp_fp8v_nq1", W.with_(B=3, Hq=8, Hkv=2, N=1024, seed=61, extra={"nq": 1, "ragged": True})),
     # four new tokens with the causal mask among them (16 query rows per KV head)
-    ("directp_nq4_causal", W.with_(B=2, Hq=8, Hkv=2, N=700, seed=62, extra={"nq": 4, "ragged": True})),
+    ("directp_nq4_causal", W.with_(B=2, Hq=8, Hkv=2, N=768, seed=62, extra={"nq": 4, "ragged": True})),
     # FP8 P/V, D = 64, no GQA, three causal tokens
-    ("fp8pv_d64_nq3", W.with_(B=2, Hq=4, Hkv=4, N=515, D=64, p_format="fp8", seed=63,
+    ("fp8pv_d64_nq3", W.with_(B=2, Hq=4, Hkv=4, N=640, D=64, p_format="fp8", seed=63,
                               extra={"nq": 3, "ragged": True})),
     # Direct-P with MXFP4 V, noncausal (every new token sees the whole cache)
-    ("directp_mxfp4v_noncausal", W.with_(B=2, Hq=4, Hkv=1, N=900, causal=False, v_format="mxfp4", seed=64,
+    ("directp_mxfp4v_noncausal", W.with_(B=2, Hq=4, Hkv=1, N=896, causal=False, v_format="mxfp4", seed=64,
                                          extra={"nq": 2, "ragged": True})),
     # 48 query rows per KV head: two workgroups (query groups) per KV head
-    ("directp_two_query_groups", W.with_(B=1, Hq=16, Hkv=1, N=300, seed=65, extra={"nq": 3})),
+    ("directp_two_query_groups", W.with_(B=1, Hq=16, Hkv=1, N=384, seed=65, extra={"nq": 3})),
     # MXFP4 V with D = 64
-    ("directp_mxfp4v_d64", W.with_(B=2, Hq=2, Hkv=2, N=333, D=64, v_format="mxfp4", seed=66,
+    ("directp_mxfp4v_d64", W.with_(B=2, Hq=2, Hkv=2, N=384, D=64, v_format="mxfp4", seed=66,
                                    extra={"nq": 1, "ragged": True})),
 ]
 
@@ -131,12 +131,12 @@ def test_decode_small_all_heads(gpu, name, wl):
 
 
 def test_decode_length_edges(gpu):
-    # valid lengths at and around the chunk (64) and tile (128) edges, an
-    # empty cache, and caches shorter than the new tokens (causal rows with no
-    # visible key: O = 0, LSE = -inf)
-    wl = W.with_(B=10, Hq=4, Hkv=2, N=260, seed=67, extra={"nq": 2})
+    # valid lengths at and around the block (32) and tile (128) edges, a full
+    # cache, an empty one, and caches shorter than the new tokens (causal rows
+    # with no visible key: O = 0, LSE = -inf)
+    wl = W.with_(B=10, Hq=4, Hkv=2, N=384, seed=67, extra={"nq": 2})
     inp = synth.generate_decode(wl)
-    inp.seqlens = torch.tensor([0, 1, 2, 63, 64, 65, 128, 129, 257, 260], dtype=torch.int32)
+    inp.seqlens = torch.tensor([0, 1, 2, 63, 64, 65, 128, 129, 257, 384], dtype=torch.int32)
     _say("decode length edges")
     o, lse = _check(gpu, inp)
     assert float(o[0].abs().max()) == 0.0 and bool(torch.isinf(lse[0]).all())
