@@ -31,6 +31,8 @@
 //    lane as in the forward; K^ / V rows are read so that a lane half holds
 //    32 consecutive keys, which makes the MX blocks of dS~ lane-local; dQ^T
 //    accumulates on the bf16 MFMA against K^^T.
+#include <type_traits>
+
 #include "common.h"
 #include "bwd_params.h"
 
@@ -64,11 +66,32 @@ __device__ inline int mx_e4m3_exponent(float a) {
   return e < -127 ? -127 : e;
 }
 
-// x 2^-e, clamped to the E4M3 range (the MX rule saturates block maxima with
-// a significand of 1.75 + 1/16 or more), then two of them to E4M3 codes.
-__device__ inline float mx_scaled(float x, int e) {
-  const float y = __builtin_ldexpf(x, -e);
-  return __builtin_fminf(__builtin_fmaxf(y, -448.0f), 448.0f);
+// The float32 whose exponent field is the E8M0 byte e + 127 (2^e; for
+// e = -127 the field is 0).  gfx950's scaled conversions take only the
+// exponent field of their scale operand.
+__device__ inline float e8m0_scale(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
+// Two values of an MX E4M3 block with exponent e to codes (bytes 0, 1 of the
+// result): E4M3 of x 2^-e, rounded to nearest even, saturated at +-448 (the
+// MX rule saturates block maxima with a significand of 1.75 + 1/16 or
+// more).  v_cvt_scalef32_pk_fp8_f32 divides by the scale and rounds but does
+// not saturate, so x is first clamped to +-448 2^e (exact).
+__device__ inline uint32_t mx_e4m3_pair(float x0, float x1, int e) {
+  const float lim = __builtin_ldexpf(448.0f, e);
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  const s16x2 w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2{0, 0}, __builtin_amdgcn_fmed3f(x0, -lim, lim),
+                                                           __builtin_amdgcn_fmed3f(x1, -lim, lim), e8m0_scale(e),
+                                                           false);
+  return (uint32_t)__builtin_bit_cast(uint32_t, w) & 0xFFFFu;
+}
+
+// The two block values E4M3(code) 2^e of such a pair, as bf16 (exact: four
+// significant bits).
+__device__ inline void mx_e4m3_pair_bf16(uint32_t codes, int e, __bf16& y0, __bf16& y1) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, e8m0_scale(e), false);
+  y0 = v[0];
+  y1 = v[1];
 }
 
 }  // namespace
@@ -346,26 +369,33 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
           dp[s2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, vreg[kk], dp[s2], 1, 0, 0, 127, 0, 127);
         }
       }
-      // P and dS of (query 32 s2 + 16 hh + r, this lane's key)
+      // P and dS of (query 32 s2 + 16 hh + r, this lane's key).  Padded query
+      // rows have L = +inf (P = 0); keys past the sequence and (causal) keys
+      // after the query are masked, which only the wave's boundary chunks need.
       float pv[2][16], dsv[2][16];
       float amp[2], ams[2];
+      const int wkey_last = kb * BWD_ROWS + wave * 32 + 31;
+      const bool all_live = wkey_last < p.N && (!CAUSAL || wkey_last <= c * BWD_CHUNK);
+      auto elements = [&](auto masked) {
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        amp[s2] = 0.0f;
-        ams[s2] = 0.0f;
+        for (int s2 = 0; s2 < 2; ++s2) {
+          amp[s2] = 0.0f;
+          ams[s2] = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ql = 32 * s2 + 16 * hh + r, qi = c * BWD_CHUNK + ql;
-          const bool live = key < p.N && (!CAUSAL || key <= qi);
-          const float t = s[s2][r] * cc;
-          const float pr = live ? __builtin_amdgcn_exp2f(t - sL[buf][ql]) : 0.0f;
-          const float ds = pr * (dp[s2][r] * sdv - sD[buf][ql]);
-          pv[s2][r] = pr;
-          dsv[s2][r] = ds;
-          amp[s2] = __builtin_fmaxf(amp[s2], pr);
-          ams[s2] = __builtin_fmaxf(ams[s2], __builtin_fabsf(ds));
+          for (int r = 0; r < 16; ++r) {
+            const int ql = 32 * s2 + 16 * hh + r, qi = c * BWD_CHUNK + ql;
+            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[s2][r], cc, -sL[buf][ql]));
+            if (decltype(masked)::value) pr = (key < p.N && (!CAUSAL || key <= qi)) ? pr : 0.0f;
+            const float ds = pr * __builtin_fmaf(dp[s2][r], sdv, -sD[buf][ql]);
+            pv[s2][r] = pr;
+            dsv[s2][r] = ds;
+            amp[s2] = __builtin_fmaxf(amp[s2], pr);
+            ams[s2] = __builtin_fmaxf(ams[s2], __builtin_fabsf(ds));
+          }
         }
-      }
+      };
+      if (all_live) elements(std::false_type{});
+      else elements(std::true_type{});
       // block maxima over the 32 queries of each sub-tile: this lane's 16 and lane^32's 16
       int ep[2], es[2];
 #pragma unroll
@@ -381,10 +411,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         const int s2 = w >> 2, r = 4 * (w & 3);
-        int word = 0;
-        word = __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(pv[s2][r], ep[s2]), mx_scaled(pv[s2][r + 1], ep[s2]), word, false);
-        word = __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(pv[s2][r + 2], ep[s2]), mx_scaled(pv[s2][r + 3], ep[s2]), word, true);
-        pa[w] = word;
+        pa[w] = (int)(mx_e4m3_pair(pv[s2][r], pv[s2][r + 1], ep[s2]) |
+                      (mx_e4m3_pair(pv[s2][r + 2], pv[s2][r + 3], ep[s2]) << 16));
       }
       const int scale_p = (hh ? ep[1] : ep[0]) + 127;
       const bool dump = DEBUG && b == p.dbg_b && h == p.dbg_h;
@@ -418,10 +446,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const int wq = __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(dsv[s2][r], es[s2]), mx_scaled(dsv[s2][r + 1], es[s2]), 0, false);
-          const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(wq, false);
-          dsq[s2][r] = (__bf16)__builtin_ldexpf(f[0], es[s2]);
-          dsq[s2][r + 1] = (__bf16)__builtin_ldexpf(f[1], es[s2]);
+          const uint32_t wq = mx_e4m3_pair(dsv[s2][r], dsv[s2][r + 1], es[s2]);
+          mx_e4m3_pair_bf16(wq, es[s2], dsq[s2][r], dsq[s2][r + 1]);
           if (dump) {
             const int qi = c * BWD_CHUNK + 32 * s2 + 16 * hh + r;
             p.dbg_dsk[(int64_t)qi * npad + key] = (uint8_t)wq;
@@ -566,19 +592,27 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdParams p) {
       }
     }
     // dS of (this lane's query, key 32 hh + 16 s2 + r): one MX block per lane half
+    // (keys past the sequence and, causal, after the wave's first query are
+    // masked; only the last chunks need it)
     float dsv[2][16];
     float am = 0.0f;
+    const int wq_first = qb * BWD_ROWS + wave * 32;
+    const bool all_live = c * BWD_CHUNK + BWD_CHUNK <= p.N && (!CAUSAL || c * BWD_CHUNK + BWD_CHUNK - 1 <= wq_first);
+    auto elements = [&](auto masked) {
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
+      for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kj = c * BWD_CHUNK + 32 * hh + 16 * s2 + r;
-        const bool live = kj < p.N && (!CAUSAL || kj <= q);
-        const float pr = live ? __builtin_amdgcn_exp2f(s[s2][r] * cc - lq) : 0.0f;
-        const float ds = pr * (dp[s2][r] * sdv - dq_d);
-        dsv[s2][r] = ds;
-        am = __builtin_fmaxf(am, __builtin_fabsf(ds));
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int kj = c * BWD_CHUNK + 32 * hh + 16 * s2 + r;
+          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[s2][r], cc, -lq));
+          if (decltype(masked)::value) pr = (kj < p.N && (!CAUSAL || kj <= q)) ? pr : 0.0f;
+          const float ds = pr * __builtin_fmaf(dp[s2][r], sdv, -dq_d);
+          dsv[s2][r] = ds;
+          am = __builtin_fmaxf(am, __builtin_fabsf(ds));
+        }
+    };
+    if (all_live) elements(std::false_type{});
+    else elements(std::true_type{});
     const int e = mx_e4m3_exponent(am);
     const bool dump = DEBUG && b == p.dbg_b && h == p.dbg_h;
     if (dump) p.dbg_dsq_e[(int64_t)q * (npad / 32) + 2 * c + hh] = (uint8_t)(e + 127);
@@ -587,10 +621,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdParams p) {
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const int wq = __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(dsv[s2][r], e), mx_scaled(dsv[s2][r + 1], e), 0, false);
-        const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(wq, false);
-        dsq[s2][r] = (__bf16)__builtin_ldexpf(f[0], e);
-        dsq[s2][r + 1] = (__bf16)__builtin_ldexpf(f[1], e);
+        const uint32_t wq = mx_e4m3_pair(dsv[s2][r], dsv[s2][r + 1], e);
+        mx_e4m3_pair_bf16(wq, e, dsq[s2][r], dsq[s2][r + 1]);
         if (dump) {
           const int kj = c * BWD_CHUNK + 32 * hh + 16 * s2 + r;
           p.dbg_dsq[(int64_t)q * npad + kj] = (uint8_t)wq;
