@@ -352,7 +352,8 @@ attn_status attn_decode_fp8pv(const attn_decode_args* a, void* stream);
  * query heads of a group into dK and dV.  Causal: key j is visible to query
  * i iff j <= i.
  *
- * Dense batches only (Nq == Nk == N).  D in {64, 128}; Hq % Hkv == 0.
+ * Dense batches only (Nq == Nk == N).  D in {64, 128}; Hq % Hkv == 0;
+ * 2 * D * roundup(N, 128) below 2^31 (N up to 8 388 480 at D = 128).
  *   q, k   : the forward's NVFP4 operands (attn_quant_nvfp4 output)
  *   v      : the forward's FP8 V (attn_quant_v, ATTN_V_FP8_E4M3; MXFP4 V is
  *            ATTN_ERR_UNSUPPORTED)

@@ -261,8 +261,9 @@ struct BwdLayout {
 };
 
 static bool bwd_shapes_ok(const attn_bwd_args* a) {
+  // the kernels address one head's transposed operands with 32-bit offsets: 2 D NPAD < 2^31
   return a != nullptr && a->B >= 0 && a->N >= 0 && a->Hq > 0 && a->Hkv > 0 && a->Hq % a->Hkv == 0 &&
-         (a->D == 64 || a->D == 128);
+         (a->D == 64 || a->D == 128) && 2 * (int64_t)a->D * roundup(a->N, 128) < ((int64_t)1 << 31);
 }
 
 static BwdLayout bwd_layout(const attn_bwd_args* a) {

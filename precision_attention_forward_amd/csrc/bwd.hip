@@ -66,6 +66,12 @@ __device__ inline int mx_e4m3_exponent(float a) {
   return e < -127 ? -127 : e;
 }
 
+// 16 bytes at base + off: base wave-uniform, off a per-lane byte offset below
+// 4 GiB (a scalar base plus a 32-bit vector offset in the load).
+__device__ inline u32x4 load16(const void* base, uint32_t off) {
+  return *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(base) + off);
+}
+
 // The float32 whose exponent field is the E8M0 byte e + 127 (2^e; for
 // e = -127 the field is 0).  gfx950's scaled conversions take only the
 // exponent field of their scale operand.
@@ -286,30 +292,45 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
   constexpr int NDO = BWD_CHUNK * D / 16 / 256, NDOT = D * (BWD_CHUNK / 16) / 256;
   u32x4 pq[NQ], pqt[NQT], pdo[NDO], pdot[NDOT];
   float pl = 0.0f, pd = 0.0f;
+  // per-lane byte offsets of the chunk copies (loop invariant; the chunk and
+  // head go into the wave-uniform base of each load)
+  uint32_t oq[NQ], oqt[NQT], odo[NDO], odot[NDOT];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int it = tid + 256 * i, row = it / (D / 8), g8 = it % (D / 8);
+    oq[i] = (uint32_t)(row * D + 8 * g8) * 2u;
+  }
+#pragma unroll
+  for (int i = 0; i < NQT; ++i) {
+    const int it = tid + 256 * i, d = it / (BWD_CHUNK / 8), r8 = it % (BWD_CHUNK / 8);
+    oqt[i] = ((uint32_t)d * (uint32_t)npad + 8u * r8) * 2u;
+  }
+#pragma unroll
+  for (int i = 0; i < NDO; ++i) {
+    const int it = tid + 256 * i, row = it / (D / 16), g16 = it % (D / 16);
+    odo[i] = (uint32_t)(row * D + 16 * g16);
+  }
+#pragma unroll
+  for (int i = 0; i < NDOT; ++i) {
+    const int it = tid + 256 * i, d = it / (BWD_CHUNK / 16), r16 = it % (BWD_CHUNK / 16);
+    odot[i] = (uint32_t)d * (uint32_t)npad + 16u * r16;
+  }
   auto fetch = [&](int step) {
     const int g = step / nch, c = c0 + step % nch;
     const int64_t qhead = (int64_t)b * p.Hq + hk * G + g;
     const int64_t q0 = qhead * npad + (int64_t)c * BWD_CHUNK;
+    const __bf16* qb0 = p.qrm + q0 * D;
+    const __bf16* qtb0 = p.qt + qhead * D * npad + (int64_t)c * BWD_CHUNK;
+    const uint8_t* db0 = p.dorm + q0 * D;
+    const uint8_t* dtb0 = p.dot + qhead * D * npad + (int64_t)c * BWD_CHUNK;
 #pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-      const int it = tid + 256 * i, row = it / (D / 8), g8 = it % (D / 8);
-      pq[i] = *reinterpret_cast<const u32x4*>(p.qrm + (q0 + row) * D + 8 * g8);
-    }
+    for (int i = 0; i < NQ; ++i) pq[i] = load16(qb0, oq[i]);
 #pragma unroll
-    for (int i = 0; i < NQT; ++i) {
-      const int it = tid + 256 * i, d = it / (BWD_CHUNK / 8), r8 = it % (BWD_CHUNK / 8);
-      pqt[i] = *reinterpret_cast<const u32x4*>(p.qt + (qhead * D + d) * npad + (int64_t)c * BWD_CHUNK + 8 * r8);
-    }
+    for (int i = 0; i < NQT; ++i) pqt[i] = load16(qtb0, oqt[i]);
 #pragma unroll
-    for (int i = 0; i < NDO; ++i) {
-      const int it = tid + 256 * i, row = it / (D / 16), g16 = it % (D / 16);
-      pdo[i] = *reinterpret_cast<const u32x4*>(p.dorm + (q0 + row) * D + 16 * g16);
-    }
+    for (int i = 0; i < NDO; ++i) pdo[i] = load16(db0, odo[i]);
 #pragma unroll
-    for (int i = 0; i < NDOT; ++i) {
-      const int it = tid + 256 * i, d = it / (BWD_CHUNK / 16), r16 = it % (BWD_CHUNK / 16);
-      pdot[i] = *reinterpret_cast<const u32x4*>(p.dot + (qhead * D + d) * npad + (int64_t)c * BWD_CHUNK + 16 * r16);
-    }
+    for (int i = 0; i < NDOT; ++i) pdot[i] = load16(dtb0, odot[i]);
     if (tid < BWD_CHUNK) {
       pl = p.lv[q0 + tid];
       pd = p.dv[q0 + tid];
@@ -529,23 +550,33 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdParams p) {
   // chunk copies double-buffered through registers, as in the dK/dV kernel
   constexpr int NK = BWD_CHUNK * D / 8 / 256, NKT = D * (BWD_CHUNK / 8) / 256, NV = BWD_CHUNK * D / 16 / 256;
   u32x4 pk[NK], pkt[NKT], pv4[NV];
+  uint32_t ok[NK], okt[NKT], ov[NV];               // per-lane byte offsets (loop invariant)
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    const int it = tid + 256 * i, row = it / (D / 8), g8 = it % (D / 8);
+    ok[i] = (uint32_t)(row * D + 8 * g8) * 2u;
+  }
+#pragma unroll
+  for (int i = 0; i < NKT; ++i) {
+    const int it = tid + 256 * i, d = it / (BWD_CHUNK / 8), r8 = it % (BWD_CHUNK / 8);
+    okt[i] = ((uint32_t)d * (uint32_t)npad + 8u * r8) * 2u;
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int it = tid + 256 * i, row = it / (D / 16), g16 = it % (D / 16);
+    ov[i] = (uint32_t)(row * D + 16 * g16);
+  }
   auto fetch = [&](int c) {
     const int64_t k0 = khead * npad + (int64_t)c * BWD_CHUNK;
+    const __bf16* kb0 = p.krm + k0 * D;
+    const __bf16* ktb0 = p.kt + khead * D * npad + (int64_t)c * BWD_CHUNK;
+    const uint8_t* vb0 = p.vrm + k0 * D;
 #pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int it = tid + 256 * i, row = it / (D / 8), g8 = it % (D / 8);
-      pk[i] = *reinterpret_cast<const u32x4*>(p.krm + (k0 + row) * D + 8 * g8);
-    }
+    for (int i = 0; i < NK; ++i) pk[i] = load16(kb0, ok[i]);
 #pragma unroll
-    for (int i = 0; i < NKT; ++i) {
-      const int it = tid + 256 * i, d = it / (BWD_CHUNK / 8), r8 = it % (BWD_CHUNK / 8);
-      pkt[i] = *reinterpret_cast<const u32x4*>(p.kt + (khead * D + d) * npad + (int64_t)c * BWD_CHUNK + 8 * r8);
-    }
+    for (int i = 0; i < NKT; ++i) pkt[i] = load16(ktb0, okt[i]);
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int it = tid + 256 * i, row = it / (D / 16), g16 = it % (D / 16);
-      pv4[i] = *reinterpret_cast<const u32x4*>(p.vrm + (k0 + row) * D + 16 * g16);
-    }
+    for (int i = 0; i < NV; ++i) pv4[i] = load16(vb0, ov[i]);
   };
   auto store = [&](int buf) {
 #pragma unroll
