@@ -153,3 +153,21 @@ def test_decode_full_size_sampled(gpu):
     o, lse = _check(gpu, inp, pairs=pairs)
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
     torch.cuda.empty_cache()
+
+
+def test_decode_bf16_output(gpu):
+    # the bf16 output is the float32 output rounded to nearest even, element
+    # for element; LSE is the same; without an LSE buffer O is unchanged
+    wl = W.with_(B=2, Hq=8, Hkv=2, N=512, seed=68, extra={"nq": 2, "ragged": True})
+    inp = synth.generate_decode(wl)
+    prep = _Prepared(gpu, inp)
+    kw = dict(B=wl.B, Hq=wl.Hq, Hkv=wl.Hkv, nq=2, Nk=wl.N, D=wl.D, softmax_scale=inp.sigma, causal=True,
+              seqlens_k=prep.seqlens)
+    _say("decode bf16 output")
+    o32, l32, _ = gpu.decode_directp(prep.q, prep.k, prep.v, **kw)
+    o16, l16, _ = gpu.decode_directp(prep.q, prep.k, prep.v, out_dtype=torch.bfloat16, **kw)
+    o_nolse, none, _ = gpu.decode_directp(prep.q, prep.k, prep.v, want_lse=False, **kw)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+    assert torch.equal(l16, l32) and torch.equal(o_nolse, o32)
