@@ -173,9 +173,10 @@ def decode_bytes(wl: Workload, seqlens) -> float:
 
 
 def decode_flops(wl: Workload, seqlens) -> float:
-    """4 * Hq * nq * D per valid key (the two products), halved-free: with
-    nq new tokens at the end of the cache the causal mask removes only the
-    nq (nq - 1) / 2 pairs among them, which are counted as computed."""
+    """4 * Hq * nq * D flops per valid cached key (2 D for Q.K and 2 D for
+    P.V per query row).  The causal mask among the nq new tokens removes
+    only nq (nq - 1) / 2 pairs per head; the kernel computes them anyway, so
+    they are counted."""
     nq = int(wl.extra.get("nq", 1))
     return 4.0 * wl.Hq * nq * wl.D * float(sum(int(n) for n in seqlens))
 
