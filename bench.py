@@ -200,14 +200,23 @@ class HipEvents:
                 self.cuda_event = h.value
         return (_E(self.pairs[i][0]), _E(self.pairs[i][1]))
 
-    def mean_ms(self):
+    def times_ms(self):
         ms = self.ct.c_float()
-        tot = 0.0
+        out = []
         for a, b in self.pairs:
             assert self.hip.hipEventSynchronize(b) == 0
             assert self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b) == 0
-            tot += ms.value
-        return tot / len(self.pairs)
+            out.append(ms.value)
+        return out
+
+    def mean_ms(self):
+        t = self.times_ms()
+        return sum(t) / len(t)
+
+    def median_ms(self):
+        t = sorted(self.times_ms())
+        n = len(t)
+        return t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2])
 
 
 def cpu_baseline_bwd(inp, dout, o, lse, rows):
@@ -292,6 +301,7 @@ def backward_main(args, torch, paf, synth):
     wall = time.perf_counter() - wall0
     ms = a.elapsed_time(b) / args.steps
     kern_ms = kev.mean_ms()
+    kern_median_ms = kev.median_ms()
     value = flops / (ms * 1e-3) / 1e12
     kern_tflops = flops / (kern_ms * 1e-3) / 1e12
     # three of the five products run on the bf16 MFMA (S, dK, dQ: NVFP4 values need 6 bits), two on FP8 (dP, dV)
@@ -307,6 +317,7 @@ def backward_main(args, torch, paf, synth):
                    "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "D": D, "causal": wl.causal, "flops_per_step": flops,
                    "parallelism": "single GPU"},
         "bwd_kernels_tflops": round(kern_tflops, 2),
+        "bwd_kernels_ms": {"mean": round(kern_ms, 4), "median": round(kern_median_ms, 4)},
         "prep_ms": round(ms - kern_ms, 4),
         "precision": "NVFP4 Q/K (exact values on the bf16 MFMA), E5M2 dO, FP8 E4M3 V, MX E4M3 P~ and dS~, "
                      "FP32 accumulation",
@@ -533,6 +544,7 @@ def main():
     qkv = quantize()
     fwd_ms = timed(lambda i: fwd(*qkv, workspace=ws, events=kev.handles(i), **kw), args.steps)
     kern_ms = kev.mean_ms()
+    kern_median_ms = kev.median_ms()
     fwd_tflops = flops / (fwd_ms * 1e-3) / 1e12
     kern_tflops = flops / (kern_ms * 1e-3) / 1e12
     o_out, lse_out, _ = fwd(*qkv, workspace=ws, **kw)
@@ -587,6 +599,7 @@ def main():
         "dtype": "fp4", "data": "synthetic (seeded Gaussian, the workload's outlier recipe)", "config": cfg,
         "fwd_call_tflops": round(fwd_tflops, 2),
         "fwd_kernel_tflops": round(kern_tflops, 2),
+        "fwd_kernel_ms": {"mean": round(kern_ms, 4), "median": round(kern_median_ms, 4)},
         "quantize_ms": round(ms_step - fwd_ms, 4),
         "pct_mxfp4_peak": round(100 * value / MXFP4_PEAK_TFLOPS, 2),
         "pct_mxfp4_peak_fwd_call": round(100 * fwd_tflops / MXFP4_PEAK_TFLOPS, 2),
