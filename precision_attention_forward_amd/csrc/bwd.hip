@@ -77,27 +77,24 @@ __device__ inline u32x4 load16(const void* base, uint32_t off) {
 // exponent field of their scale operand.
 __device__ inline float e8m0_scale(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
 
-// Two values of an MX E4M3 block with exponent e to codes (bytes 0, 1 of the
-// result): E4M3 of x 2^-e, rounded to nearest even, saturated at +-448 (the
-// MX rule saturates block maxima with a significand of 1.75 + 1/16 or
-// more).  v_cvt_scalef32_pk_fp8_f32 divides by the scale and rounds but does
-// not saturate, so x is first clamped to +-448 2^e (exact).
-__device__ inline uint32_t mx_e4m3_pair(float x0, float x1, int e) {
-  const float lim = __builtin_ldexpf(448.0f, e);
-  typedef short s16x2 __attribute__((ext_vector_type(2)));
-  const s16x2 w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2{0, 0}, __builtin_amdgcn_fmed3f(x0, -lim, lim),
-                                                           __builtin_amdgcn_fmed3f(x1, -lim, lim), e8m0_scale(e),
-                                                           false);
-  return (uint32_t)__builtin_bit_cast(uint32_t, w) & 0xFFFFu;
+// Two values of an MX E4M3 block to codes, written into half HI of w (the
+// other half is kept): E4M3 of x 2^-e, rounded to nearest even, saturated at
+// +-448 (the MX rule saturates block maxima with a significand of 1.75 +
+// 1/16 or more).  v_cvt_scalef32_pk_fp8_f32 divides by the scale and rounds
+// but does not saturate, so x is first clamped to +-448 2^e (exact); lim and
+// scale are 448 2^e and e8m0_scale(e).
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+template <bool HI>
+__device__ inline s16x2 mx_e4m3_pair(s16x2 w, float x0, float x1, float lim, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, __builtin_amdgcn_fmed3f(x0, -lim, lim),
+                                                  __builtin_amdgcn_fmed3f(x1, -lim, lim), scale, HI);
 }
 
-// The two block values E4M3(code) 2^e of such a pair, as bf16 (exact: four
-// significant bits).
-__device__ inline void mx_e4m3_pair_bf16(uint32_t codes, int e, __bf16& y0, __bf16& y1) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const bf16x2_t v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, e8m0_scale(e), false);
-  y0 = v[0];
-  y1 = v[1];
+// The two block values E4M3(code) 2^e of the low pair of w, as two bf16 in
+// one word (exact: four significant bits).
+__device__ inline uint32_t mx_e4m3_pair_bf16(s16x2 w, float scale) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(__builtin_bit_cast(uint32_t, w),
+                                                                                scale, false));
 }
 
 }  // namespace
@@ -429,11 +426,21 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
       // P~^T as the A operand of dV: bytes 0..15 sub-tile 0, bytes 16..31 sub-tile 1 (the
       // k-blocks of the FP8 operand); lane half hh supplies the exponent of block hh
       i32x8 pa;
+      float limp[2], scp[2], lims[2], scs[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        limp[s2] = __builtin_ldexpf(448.0f, ep[s2]);
+        scp[s2] = e8m0_scale(ep[s2]);
+        lims[s2] = __builtin_ldexpf(448.0f, es[s2]);
+        scs[s2] = e8m0_scale(es[s2]);
+      }
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         const int s2 = w >> 2, r = 4 * (w & 3);
-        pa[w] = (int)(mx_e4m3_pair(pv[s2][r], pv[s2][r + 1], ep[s2]) |
-                      (mx_e4m3_pair(pv[s2][r + 2], pv[s2][r + 3], ep[s2]) << 16));
+        s16x2 t = {0, 0};
+        t = mx_e4m3_pair<false>(t, pv[s2][r], pv[s2][r + 1], limp[s2], scp[s2]);
+        t = mx_e4m3_pair<true>(t, pv[s2][r + 2], pv[s2][r + 3], limp[s2], scp[s2]);
+        pa[w] = __builtin_bit_cast(int, t);
       }
       const int scale_p = (hh ? ep[1] : ep[0]) + 127;
       const bool dump = DEBUG && b == p.dbg_b && h == p.dbg_h;
@@ -462,14 +469,15 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
         dv[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pa, bb, dv[dt], 0, 1, 0, scale_p, 0, 127);
       }
       // dS~: E4M3 of dS 2^-e (same blocks), back to float, times 2^e: exact in bf16
-      __bf16 dsq[2][16];
+      uint32_t dsq[2][8];                       // bf16 pairs
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const uint32_t wq = mx_e4m3_pair(dsv[s2][r], dsv[s2][r + 1], es[s2]);
-          mx_e4m3_pair_bf16(wq, es[s2], dsq[s2][r], dsq[s2][r + 1]);
+          const s16x2 q2 = mx_e4m3_pair<false>(s16x2{0, 0}, dsv[s2][r], dsv[s2][r + 1], lims[s2], scs[s2]);
+          dsq[s2][r / 2] = mx_e4m3_pair_bf16(q2, scs[s2]);
           if (dump) {
+            const uint32_t wq = __builtin_bit_cast(uint32_t, q2);
             const int qi = c * BWD_CHUNK + 32 * s2 + 16 * hh + r;
             p.dbg_dsk[(int64_t)qi * npad + key] = (uint8_t)wq;
             p.dbg_dsk[(int64_t)(qi + 1) * npad + key] = (uint8_t)(wq >> 8);
@@ -479,9 +487,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int s2 = j >> 1, r0 = 8 * (j & 1);
-        bf16x8 a;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) a[i] = dsq[s2][r0 + i];
+        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{dsq[s2][r0 / 2], dsq[s2][r0 / 2 + 1],
+                                                          dsq[s2][r0 / 2 + 2], dsq[s2][r0 / 2 + 3]});
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const int d = 32 * dt + ln;
@@ -645,15 +652,17 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdParams p) {
     if (all_live) elements(std::false_type{});
     else elements(std::true_type{});
     const int e = mx_e4m3_exponent(am);
+    const float lim = __builtin_ldexpf(448.0f, e), sc = e8m0_scale(e);
     const bool dump = DEBUG && b == p.dbg_b && h == p.dbg_h;
     if (dump) p.dbg_dsq_e[(int64_t)q * (npad / 32) + 2 * c + hh] = (uint8_t)(e + 127);
-    __bf16 dsq[2][16];
+    uint32_t dsq[2][8];                         // bf16 pairs
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const uint32_t wq = mx_e4m3_pair(dsv[s2][r], dsv[s2][r + 1], e);
-        mx_e4m3_pair_bf16(wq, e, dsq[s2][r], dsq[s2][r + 1]);
+        const s16x2 q2 = mx_e4m3_pair<false>(s16x2{0, 0}, dsv[s2][r], dsv[s2][r + 1], lim, sc);
+        dsq[s2][r / 2] = mx_e4m3_pair_bf16(q2, sc);
+        const uint32_t wq = __builtin_bit_cast(uint32_t, q2);
         if (dump) {
           const int kj = c * BWD_CHUNK + 32 * hh + 16 * s2 + r;
           p.dbg_dsq[(int64_t)q * npad + kj] = (uint8_t)wq;
@@ -664,9 +673,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int s2 = j >> 1, r0 = 8 * (j & 1);
-      bf16x8 bv;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) bv[i] = dsq[s2][r0 + i];
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, u32x4{dsq[s2][r0 / 2], dsq[s2][r0 / 2 + 1],
+                                                         dsq[s2][r0 / 2 + 2], dsq[s2][r0 / 2 + 3]});
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int d = 32 * dt + ln;
