@@ -368,17 +368,12 @@ def cpu_baseline_dec(inp, seqs):
                 OA.attn_lowp_head(OQ.dequant_nvfp4_raw(qc, qs), kraw, gq, gk, vhat, inp.sigma, wl.p_format,
                                   wl.causal, q_index=q_index)
     dt = time.perf_counter() - t
-    sub = wl.with_(B=S)
-    by = synth_decode_bytes(sub, inp.seqlens[:S])
+    from precision_attention_forward_amd import synth
+    by = synth.decode_bytes(wl.with_(B=S), inp.seqlens[:S])
     return {"value": by / dt / 1e9, "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
             "sample": f"all {wl.Hq} heads of the first {S} sequences of workload {wl.name} ({keys} cached keys "
                       f"per head; quantization of their cache included), {dt:.1f} s; numpy float64, "
                       f"BLAS threads = cores"}
-
-
-def synth_decode_bytes(wl, seqlens):
-    from precision_attention_forward_amd import synth
-    return synth.decode_bytes(wl, seqlens)
 
 
 def decode_main(args, torch, paf, synth):

@@ -393,7 +393,7 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(DecParams p) {
   }
 }
 
-template <int D, int VF>
+template <int D>
 constexpr int dec_lds_bytes() {
   return (2 * DEC_WAVES * DEC_Q + DEC_WAVES * (D / 16) * 4 * 64 + DEC_WAVES * 64) * 4;
 }
@@ -401,7 +401,7 @@ constexpr int dec_lds_bytes() {
 template <int D, int PF, int VF, bool CAUSAL, bool DEBUG>
 static hipError_t launch_dec_t(const DecParams& p, int nwg, hipStream_t st) {
   auto kern = decode_kernel<D, PF, VF, CAUSAL, DEBUG>;
-  const int lds = dec_lds_bytes<D, VF>();
+  const int lds = dec_lds_bytes<D>();
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(nwg), dim3(64 * DEC_WAVES), lds, st, p);
