@@ -209,3 +209,35 @@ def dequant_v_mxfp4(codes, e8m0):
     Nk = codes.shape[0]
     s = np.repeat(e8m0_decode(e8m0), MX_BLOCK, axis=0)[:Nk]
     return e2m1_decode(codes) * s
+
+
+def quant_mxfp4(x):
+    """MXFP4 quantization along the last axis (D, a multiple of 32): the
+    MX-native Q/K format, an opt-in alternative to NVFP4 whose blocks the
+    gfx950 scaled matrix instruction can apply directly.
+
+    The pages keep Q and K in NVFP4 ("Hardware-Aware FP4 FlashAttention-4",
+    summary page, "What the paper found") and use MXFP4 -- E2M1 elements with
+    one E8M0 exponent per 32 -- for P and V; this applies that same OCP MX
+    rule to Q/K rows: per 32 consecutive elements along D,
+    e = clamp(floor(log2 amax) - 2, -127, 127) (-127 for an all-zero block)
+    and code = E2M1(x * 2**-e).  No tensor scale.
+
+    Returns (codes uint8 [..., D/2], element 2k in the low nibble of byte k;
+    e8m0 uint8 [..., D/32]).
+    """
+    x = np.asarray(x, dtype=F32)
+    D = x.shape[-1]
+    assert D % MX_BLOCK == 0
+    xb = x.reshape(x.shape[:-1] + (D // MX_BLOCK, MX_BLOCK)).astype(np.float64)
+    e = mx_block_exponent(np.max(np.abs(xb), axis=-1))              # [..., D/32]
+    codes = e2m1_encode(xb * np.ldexp(1.0, -e)[..., None])          # exact scaling by 2**-e
+    codes = codes.reshape(x.shape).astype(np.uint8)
+    return pack_nibbles(codes), (e + 127).astype(np.uint8)
+
+
+def dequant_mxfp4(codes_packed, e8m0):
+    """E2M1(code) * 2**e per 32-element block along the last axis, float64."""
+    c = unpack_nibbles(codes_packed)
+    s = np.repeat(e8m0_decode(e8m0), MX_BLOCK, axis=-1)
+    return e2m1_decode(c) * s
