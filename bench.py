@@ -38,6 +38,9 @@ def parse():
                     help="probability encoder: exact (RNE of 2^y) or the exp-free log-linear cast")
     ap.add_argument("--four-six", action="store_true",
                     help="quantize Q and K with the Four Over Six adaptive block scale (attn_quant_nvfp4_46)")
+    ap.add_argument("--qk", choices=("nvfp4", "mxfp4"), default="nvfp4",
+                    help="Q/K format: nvfp4 (the method's; Q.K^T on the FP16 MFMA, exact) or the opt-in "
+                         "MX-native mxfp4 (E8M0 per 32 along D; Q.K^T on the scaled FP4 MFMA, attn_fwd_directp_mxqk)")
     ap.add_argument("--backward", action="store_true",
                     help="time the causal-training backward (attn_bwd_fp8) instead of the forward; its own JSON line")
     ap.add_argument("--decode", action="store_true",
@@ -99,7 +102,7 @@ def copy_calibration(mib):
                       "launches": 3}), flush=True)
 
 
-def cpu_baseline(inp, rows, encoder="exact", four_six=False):
+def cpu_baseline(inp, rows, encoder="exact", four_six=False, qk="nvfp4"):
     """Time the CPU oracle (as it stands) on a bounded sample: one (batch,
     head), `rows` query rows against all keys, including the sample's
     quantization.  Returns a dict for the JSON line."""
@@ -124,22 +127,27 @@ def cpu_baseline(inp, rows, encoder="exact", four_six=False):
     kf = kh.float().cpu().numpy()
     vf = vh.float().cpu().numpy()
     t = time.perf_counter()
-    qfn = OQ.quant_nvfp4_46 if four_six else OQ.quant_nvfp4
-    qc, qs, gq = qfn(qf)
-    kc, ks, gk = qfn(kf)
+    if qk == "mxfp4":
+        qc, qe = OQ.quant_mxfp4(qf)
+        kc, ke = OQ.quant_mxfp4(kf)
+        q_raw, k_raw, gq, gk = OQ.dequant_mxfp4(qc, qe), OQ.dequant_mxfp4(kc, ke), 1.0, 1.0
+    else:
+        qfn = OQ.quant_nvfp4_46 if four_six else OQ.quant_nvfp4
+        qc, qs, gq = qfn(qf)
+        kc, ks, gk = qfn(kf)
+        q_raw, k_raw = OQ.dequant_nvfp4_raw(qc, qs), OQ.dequant_nvfp4_raw(kc, ks)
     if wl.v_format == "fp8":
         vcodes, s_v = OQ.quant_v_fp8(vf)
         vhat = OQ.dequant_v_fp8(vcodes, s_v)
     else:
         vcodes, ve = OQ.quant_v_mxfp4(vf[:, None, :])
         vhat = OQ.dequant_v_mxfp4(vcodes, ve)[:, 0, :]
-    OA.attn_lowp_head(OQ.dequant_nvfp4_raw(qc, qs), OQ.dequant_nvfp4_raw(kc, ks), gq, gk, vhat, inp.sigma,
-                      wl.p_format, wl.causal, q_index=idx, encoder=encoder)
+    OA.attn_lowp_head(q_raw, k_raw, gq, gk, vhat, inp.sigma, wl.p_format, wl.causal, q_index=idx, encoder=encoder)
     dt = time.perf_counter() - t
     live = sum(min(int(i) + 1, Nk) for i in idx) if wl.causal else R * Nk
     flops = 4.0 * live * wl.D
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"1 head, {R} query rows x {Nk} keys of workload {wl.name} (NVFP4/V quantization of the "
+            "sample": f"1 head, {R} query rows x {Nk} keys of workload {wl.name} ({qk.upper()}/V quantization of the "
                       f"sample included), {dt:.1f} s; numpy float64, BLAS threads = cores"}
 
 
@@ -484,6 +492,10 @@ def main():
         backward_main(args, torch, paf, synth)
         return
     wl = synth.WORKLOADS[args.workload]
+    mxqk = args.qk == "mxfp4"
+    if mxqk and (wl.p_format != "mxfp4" or args.encoder != "exact" or args.four_six):
+        print("--qk mxfp4 is a Direct-P mode (MXFP4 P workloads, exact encoder, no Four Over Six)", file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = synth.generate(wl, dev)
@@ -492,6 +504,8 @@ def main():
     fwd = {("mxfp4", "exact"): paf.fwd_directp, ("fp8", "exact"): paf.fwd_fp8pv,
            ("mxfp4", "loglin"): paf.fwd_directp_efq, ("fp8", "loglin"): paf.fwd_fp8pv_cast}[(wl.p_format,
                                                                                           args.encoder)]
+    if mxqk:
+        fwd = paf.fwd_directp_mxqk
     kw = dict(Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D, softmax_scale=inp.sigma, causal=wl.causal, out_dtype=torch.bfloat16)
     if varlen:
         cu = inp.cu_seqlens.to(dev)
@@ -504,8 +518,11 @@ def main():
     kev = HipEvents(args.steps)
 
     def quantize():
-        q = paf.quant_nvfp4(inp.q, four_six=args.four_six)
-        k = paf.quant_nvfp4(inp.k, four_six=args.four_six)
+        if mxqk:
+            q, k = paf.quant_mxfp4(inp.q), paf.quant_mxfp4(inp.k)
+        else:
+            q = paf.quant_nvfp4(inp.q, four_six=args.four_six)
+            k = paf.quant_nvfp4(inp.k, four_six=args.four_six)
         if varlen:
             vc, vs, vt, _ = paf.quant_v(inp.v, vfmt, cu_seqlens=kw["cu_seqlens_k"], max_seqlen=kw["max_seqlen_k"])
         else:
@@ -564,26 +581,29 @@ def main():
 
     # dominant kernel roofline: the attention kernel is MFMA bound
     pv_peak = MXFP4_PEAK_TFLOPS if wl.v_format == "mxfp4" else FP8_PEAK_TFLOPS
-    # mixed ceiling: QK^T runs on the FP16 MFMA (exact NVFP4), P.V at the P/V format rate
-    qk_rate, pv_rate = BF16_PEAK_TFLOPS, (pv_peak if wl.p_format == "mxfp4" else FP8_PEAK_TFLOPS)
+    # mixed ceiling: QK^T runs on the FP16 MFMA (exact NVFP4) or, MX-native, on the FP4 rate; P.V at the P/V
+    # format rate
+    qk_rate = MXFP4_PEAK_TFLOPS if mxqk else BF16_PEAK_TFLOPS
+    pv_rate = pv_peak if wl.p_format == "mxfp4" else FP8_PEAK_TFLOPS
     ceiling = 1.0 / (0.5 / qk_rate + 0.5 / pv_rate)
     roofline = {"bound": "mfma", "achieved": round(kern_tflops, 2), "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(kern_tflops / MXFP4_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic(args.workload) if args.encoder == "exact" else None,
+                "traffic": measured_traffic(args.workload) if args.encoder == "exact" and not mxqk else None,
                 "kernel": "fwd_lowp_kernel", "kernel_ms": round(kern_ms, 4),
                 "mixed_ceiling_tflops": round(ceiling, 1), "frac_of_mixed_ceiling": round(kern_tflops / ceiling, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, args.cpu_rows, args.encoder, args.four_six)
+        cpu = cpu_baseline(inp, args.cpu_rows, args.encoder, args.four_six, args.qk)
 
     cfg = {"workload": f"{wl.name}: " + (f"{wl.varlen[0]} packed sequences" if varlen else
                                          f"B={wl.B} N={wl.N}") +
            f" Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D} {'causal' if wl.causal else 'noncausal'}, "
            f"P={wl.p_format.upper()} V={wl.v_format.upper()}" +
            ("" if args.encoder == "exact" else ", exp-free log-linear P encoder") +
-           (", Four Over Six Q/K block scales" if args.four_six else ""),
-           "encoder": args.encoder, "four_six": args.four_six,
+           (", Four Over Six Q/K block scales" if args.four_six else "") +
+           (", MX-native MXFP4 Q/K (opt-in)" if mxqk else ""),
+           "encoder": args.encoder, "four_six": args.four_six, "qk": args.qk,
            "B": wl.B if not varlen else int(len(inp.seqlens)), "Hq": wl.Hq, "Hkv": wl.Hkv,
            "N": wl.N if not varlen else int(inp.seqlens.max()), "D": wl.D, "causal": wl.causal,
            "flops_per_step": flops, "parallelism": "single GPU"}
@@ -602,7 +622,8 @@ def main():
         "x_bf16": None if bf16 is None else round(fwd_tflops / bf16["tflops"], 3),
         "x_bf16_incl_quantize": None if bf16 is None else round(value / bf16["tflops"], 3),
         "bf16_tflops": None if bf16 is None else round(bf16["tflops"], 2),
-        "precision": "NVFP4 Q/K (exact, contracted on the FP16 MFMA), " +
+        "precision": ("MX-native MXFP4 Q/K (E8M0 per 32 along D; contracted on the scaled FP4 MFMA), " if mxqk else
+                      "NVFP4 Q/K (exact, contracted on the FP16 MFMA), ") +
                      ("MXFP4 E2M1 P (Direct-P)" if wl.p_format == "mxfp4" else "FP8 E4M3 P") +
                      ("" if args.encoder == "exact" else " by the exp-free log-linear cast") +
                      f", {wl.v_format.upper()} V, FP32 accumulation",

@@ -116,6 +116,26 @@ attn_status attn_quant_nvfp4_46(const void* x_bf16, int64_t rows, int32_t D,
                                 void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * MXFP4 quantization of Q or K for the opt-in MX-native Q/K forward
+ * (attn_fwd_directp_mxqk).  The pages keep Q and K in NVFP4 and use MXFP4 --
+ * E2M1 elements with one E8M0 exponent per 32 -- for P and V (summary page,
+ * "What the paper found"); this applies the same OCP MX rule along D so that
+ * Q.K^T can run on gfx950's block-scaled FP4 matrix instruction, whose scales
+ * are E8M0 per 32 elements (NVFP4's E4M3 scale per 16 is not one of them).
+ *   per 32 consecutive elements along D: e = clamp(floor(log2 amax) - 2,
+ *   -127, 127) (-127 when the block max is 0 or subnormal), code =
+ *   E2M1_sat(x * 2^-e) rounded to nearest even (sign kept), byte = e + 127
+ * x_bf16: [rows, D] bf16, D a multiple of 32 (the forward takes 64 and 128),
+ * 16-byte aligned.  Outputs: codes [rows, D/2] (element 2k in the low nibble
+ * of byte k, 16-byte aligned), scales [rows, D/32] E8M0 bytes.  No tensor
+ * scale and no workspace.  rows == 0 is valid and writes nothing.
+ * Errors: ATTN_ERR_INVALID_ARGUMENT (bad size, null or misaligned pointer),
+ * ATTN_ERR_HIP.
+ */
+attn_status attn_quant_mxfp4(const void* x_bf16, int64_t rows, int32_t D,
+                             uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
  * Number of key columns of the transposed V layout used by attn_quant_v and
  * the forward.  Sequence s starts at column
  *     dense : s * roundup(Nk, 128)
@@ -253,6 +273,23 @@ attn_status attn_fwd_fp8pv(const attn_fwd_args* a, void* stream);
  */
 attn_status attn_fwd_directp_efq(const attn_fwd_args* a, void* stream);
 attn_status attn_fwd_fp8pv_cast(const attn_fwd_args* a, void* stream);
+
+/*
+ * Direct-P forward with MX-native Q/K (opt-in; not the pages' format).  The
+ * arithmetic is that of attn_fwd_directp -- running max per 128-key tile,
+ * E8M0 exponent and E2M1 codes per 32 keys, denominator from the same codes,
+ * O = o / l, LSE = ln2 (m + log2 l) -- except that Q^ and K^ are the MXFP4
+ * values E2M1(code) * 2^e written by attn_quant_mxfp4, so that
+ * t = sigma * log2(e) * (Q^ . K^) and Q.K^T runs as a block-scaled FP4
+ * contraction.  Arguments as for attn_fwd_directp, with:
+ *   q, k: codes [rows, D/2] (16-byte aligned) and scales [rows, D/32] E8M0
+ *         bytes (aligned to D/32 bytes); tensor_scale is ignored (may be NULL)
+ *   ws  : at least attn_fwd_ws_bytes(args) bytes (this entry point uses
+ *         64 D + 512 bytes per 128-key tile and KV head of it)
+ * Noncausal (ATTN_ERR_UNSUPPORTED otherwise); D in {64, 128}; V FP8 or
+ * MXFP4.  Errors as for attn_fwd_directp.
+ */
+attn_status attn_fwd_directp_mxqk(const attn_fwd_args* a, void* stream);
 
 /*
  * BF16 fused attention forward, the baseline the pages compare against

@@ -94,6 +94,8 @@ EXPORTS = {
     "attn_quant_nvfp4_46": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                         ctypes.c_void_p]),
+    "attn_quant_mxfp4": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p]),
     "attn_v_cols": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]),
     "attn_quant_v": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
@@ -103,6 +105,7 @@ EXPORTS = {
     "attn_fwd_fp8pv": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "attn_fwd_directp_efq": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "attn_fwd_fp8pv_cast": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
+    "attn_fwd_directp_mxqk": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "attn_decode_directp": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]),
     "attn_decode_fp8pv": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]),
     "attn_bwd_ws_bytes": (ctypes.c_size_t, [ctypes.POINTER(BwdArgs)]),
@@ -174,6 +177,23 @@ def quant_nvfp4(x, four_six=False):
     return codes, scales, ts
 
 
+def quant_mxfp4(x):
+    """MXFP4-quantize a bf16 tensor along its last axis (D, a multiple of 32),
+    the MX-native Q/K format of fwd_directp_mxqk.  Returns (codes uint8
+    [..., D/2], E8M0 scales uint8 [..., D/32], None) -- the None stands where
+    the NVFP4 tuples carry their tensor scale."""
+    lib = load_library()
+    _need_cuda(x)
+    if x.dtype != torch.bfloat16:
+        raise AttnError("quant_mxfp4 expects bfloat16")
+    D = x.shape[-1]
+    rows = x.numel() // D if D else 0
+    codes = torch.empty(x.shape[:-1] + (D // 2,), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(x.shape[:-1] + (D // 32,), dtype=torch.uint8, device=x.device)
+    _check(lib.attn_quant_mxfp4(_ptr(x), rows, D, _ptr(codes), _ptr(scales), _stream()))
+    return codes, scales, None
+
+
 def v_cols(B, Nk, total_k=0, varlen=False):
     return load_library().attn_v_cols(B, Nk, total_k, 1 if varlen else 0)
 
@@ -234,8 +254,8 @@ def make_fwd_args(q, k, v, *, B, Hq, Hkv, Nq, Nk, D, softmax_scale, causal=False
     a.total_q, a.total_k = total_q, total_k
     a.softmax_scale = softmax_scale
     a.causal = 1 if causal else 0
-    a.q = _NvTensor(q[0].data_ptr(), q[1].data_ptr(), q[2].data_ptr())
-    a.k = _NvTensor(k[0].data_ptr(), k[1].data_ptr(), k[2].data_ptr())
+    a.q = _NvTensor(q[0].data_ptr(), q[1].data_ptr(), None if q[2] is None else q[2].data_ptr())
+    a.k = _NvTensor(k[0].data_ptr(), k[1].data_ptr(), None if k[2] is None else k[2].data_ptr())
     a.v = _VTensor(v[0], v[1].data_ptr(), None if v[2] is None else v[2].data_ptr(),
                    None if v[3] is None else v[3].data_ptr())
     a.o = None if o is None else o.data_ptr()
@@ -278,7 +298,7 @@ def _fwd_lowp(entry, q, k, v, *, Hq, Hkv, D, softmax_scale, causal=False, B=None
         dbg_b, dbg_h = debug
         nq_dbg = Nq
         nk_pad = (Nk + 127) // 128 * 128
-        if entry in ("attn_fwd_directp", "attn_fwd_directp_efq"):
+        if entry in ("attn_fwd_directp", "attn_fwd_directp_efq", "attn_fwd_directp_mxqk"):
             dbg_codes = torch.zeros((nq_dbg, nk_pad // 2), dtype=torch.uint8, device=dev)
             dbg_scales = torch.zeros((nq_dbg, nk_pad // 32), dtype=torch.uint8, device=dev)
         else:
@@ -317,6 +337,12 @@ def fwd_fp8pv_cast(q, k, v, **kw):
     return _fwd_lowp("attn_fwd_fp8pv_cast", q, k, v, **kw)
 
 
+def fwd_directp_mxqk(q, k, v, **kw):
+    """Direct-P with MX-native Q/K (opt-in): q/k from quant_mxfp4, Q.K^T on
+    the block-scaled FP4 matrix instruction (noncausal)."""
+    return _fwd_lowp("attn_fwd_directp_mxqk", q, k, v, **kw)
+
+
 def _decode(entry, q, k, v, *, B, Hq, Hkv, nq, Nk, D, softmax_scale, causal=False, seqlens_k=None,
             out_dtype=torch.float32, want_lse=True, debug=None, events=None, out=None):
     """Shared driver of the decode entry points.  q: NVFP4 (codes, scales,
@@ -338,8 +364,8 @@ def _decode(entry, q, k, v, *, B, Hq, Hkv, nq, Nk, D, softmax_scale, causal=Fals
     a.seqlens_k = None if seqlens_k is None else seqlens_k.data_ptr()
     a.softmax_scale = softmax_scale
     a.causal = 1 if causal else 0
-    a.q = _NvTensor(q[0].data_ptr(), q[1].data_ptr(), q[2].data_ptr())
-    a.k = _NvTensor(k[0].data_ptr(), k[1].data_ptr(), k[2].data_ptr())
+    a.q = _NvTensor(q[0].data_ptr(), q[1].data_ptr(), None if q[2] is None else q[2].data_ptr())
+    a.k = _NvTensor(k[0].data_ptr(), k[1].data_ptr(), None if k[2] is None else k[2].data_ptr())
     a.v = _VTensor(v[0], v[1].data_ptr(), None if v[2] is None else v[2].data_ptr(),
                    None if v[3] is None else v[3].data_ptr())
     a.o = o.data_ptr()
@@ -395,8 +421,8 @@ def bwd_fp8(q, k, v, o, lse, dout, *, softmax_scale, causal=True, workspace=None
     a.B, a.Hq, a.Hkv, a.N, a.D = B, Hq, Hkv, N, D
     a.softmax_scale = softmax_scale
     a.causal = 1 if causal else 0
-    a.q = _NvTensor(q[0].data_ptr(), q[1].data_ptr(), q[2].data_ptr())
-    a.k = _NvTensor(k[0].data_ptr(), k[1].data_ptr(), k[2].data_ptr())
+    a.q = _NvTensor(q[0].data_ptr(), q[1].data_ptr(), None if q[2] is None else q[2].data_ptr())
+    a.k = _NvTensor(k[0].data_ptr(), k[1].data_ptr(), None if k[2] is None else k[2].data_ptr())
     a.v = _VTensor(v[0], v[1].data_ptr(), None if v[2] is None else v[2].data_ptr(),
                    None if v[3] is None else v[3].data_ptr())
     a.o, a.lse, a.dout = o.data_ptr(), lse.data_ptr(), dout.data_ptr()

@@ -19,7 +19,11 @@ hipError_t launch_quant_v(const void* v, int B, int Nk, int Hkv, int D, const in
 hipError_t launch_expand_k(const uint8_t* codes, const uint8_t* scales, int H, int B, int N, int max_len,
                            const int32_t* cu, int64_t n_pad, int64_t cols, int D, int pf, _Float16* out,
                            hipStream_t st);
+hipError_t launch_quant_mxfp4(const void* x, int64_t rows, int D, uint8_t* codes, uint8_t* scales, hipStream_t st);
+hipError_t launch_pack_k_mx(const uint8_t* codes, const uint8_t* scales, int H, int B, int N, int max_len,
+                            const int32_t* cu, int64_t n_pad, int64_t cols, int D, uint8_t* out, hipStream_t st);
 struct FwdParams;
+hipError_t launch_fwd_mx(const FwdParams& p, int D, int vf, bool debug, hipStream_t st);
 hipError_t launch_fwd_lowp(const FwdParams& p, int D, int pf, int vf, bool causal, bool debug, int enc,
                            hipStream_t st);
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
@@ -95,6 +99,15 @@ attn_status attn_quant_nvfp4_46(const void* x_bf16, int64_t rows, int32_t D, uin
   return run_quant_nvfp4(x_bf16, rows, D, codes, scales, tensor_scale, ws, ws_bytes, stream, true);
 }
 
+attn_status attn_quant_mxfp4(const void* x_bf16, int64_t rows, int32_t D, uint8_t* codes, uint8_t* scales,
+                             void* stream) {
+  if (rows < 0 || D <= 0 || D % 32 != 0) return ATTN_ERR_INVALID_ARGUMENT;
+  if (rows > 0 && (x_bf16 == nullptr || codes == nullptr || scales == nullptr || !aligned(x_bf16, 16) ||
+                   !aligned(codes, 16)))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_quant_mxfp4(x_bf16, rows, D, codes, scales, (hipStream_t)stream));
+}
+
 int64_t attn_v_cols(int32_t B, int32_t Nk, int64_t total_k, int32_t varlen) {
   if (B < 0 || Nk < 0 || total_k < 0) return -1;
   if (varlen) return 128 * ((total_k + 127) / 128 + B);
@@ -141,7 +154,7 @@ size_t attn_fwd_ws_bytes(const attn_fwd_args* a) {
   return (size_t)(2 * a->D) * (size_t)(a->Hkv * fwd_kcols(a)) + 256;
 }
 
-static attn_status validate_fwd(const attn_fwd_args* a, bool allow_causal, int pf) {
+static attn_status validate_fwd(const attn_fwd_args* a, bool allow_causal, int pf, bool mx = false) {
   if (a == nullptr) return ATTN_ERR_INVALID_ARGUMENT;
   if (a->B < 0 || a->Hq <= 0 || a->Hkv <= 0 || a->Nq < 0 || a->Nk < 0) return ATTN_ERR_INVALID_ARGUMENT;
   if (a->D != 64 && a->D != 128) return ATTN_ERR_INVALID_ARGUMENT;
@@ -161,9 +174,10 @@ static attn_status validate_fwd(const attn_fwd_args* a, bool allow_causal, int p
   const attn_nvfp4_tensor* t[2] = {&a->q, &a->k};
   const int64_t n[2] = {nq, nk};
   for (int i = 0; i < 2; ++i) {
-    if (t[i]->tensor_scale == nullptr || !aligned(t[i]->tensor_scale, 4)) return ATTN_ERR_INVALID_ARGUMENT;
-    if (n[i] > 0 && (t[i]->codes == nullptr || t[i]->scales == nullptr || !aligned(t[i]->codes, 8)))
+    if (!mx && (t[i]->tensor_scale == nullptr || !aligned(t[i]->tensor_scale, 4))) return ATTN_ERR_INVALID_ARGUMENT;
+    if (n[i] > 0 && (t[i]->codes == nullptr || t[i]->scales == nullptr || !aligned(t[i]->codes, mx ? 16 : 8)))
       return ATTN_ERR_INVALID_ARGUMENT;
+    if (mx && n[i] > 0 && !aligned(t[i]->scales, a->D == 128 ? 4 : 2)) return ATTN_ERR_INVALID_ARGUMENT;
   }
   if (nk > 0 && (a->v.codes == nullptr || !aligned(a->v.codes, 16))) return ATTN_ERR_INVALID_ARGUMENT;
   if (nk > 0 && a->v.format == ATTN_V_MXFP4 && (a->v.scales == nullptr || !aligned(a->v.scales, 4)))
@@ -182,16 +196,21 @@ static attn_status validate_fwd(const attn_fwd_args* a, bool allow_causal, int p
   return ATTN_OK;
 }
 
-static attn_status run_fwd_lowp(const attn_fwd_args* a, void* stream, int pf, int enc) {
-  attn_status s = validate_fwd(a, pf == 1, pf);
+// mx: the MX-native Q/K mode (MXFP4 Q/K codes with E8M0 bytes, no tensor
+// scales; Direct-P only), whose K pre-pass packs FP4 operand tiles instead of
+// expanding K to FP16.
+static attn_status run_fwd_lowp(const attn_fwd_args* a, void* stream, int pf, int enc, bool mx = false) {
+  attn_status s = validate_fwd(a, pf == 1, pf, mx);
   if (s != ATTN_OK) return s;
   hipStream_t st = (hipStream_t)stream;
   const bool varlen = a->cu_seqlens_q != nullptr;
   const int64_t kcols = fwd_kcols(a);
   _Float16* khat = (_Float16*)a->ws;
   const int64_t nk_pad = roundup(a->Nk, 128);
-  hipError_t e = launch_expand_k(a->k.codes, a->k.scales, a->Hkv, a->B, a->Nk, a->Nk, a->cu_seqlens_k, nk_pad, kcols,
-                                 a->D, pf, khat, st);
+  hipError_t e = mx ? launch_pack_k_mx(a->k.codes, a->k.scales, a->Hkv, a->B, a->Nk, a->Nk, a->cu_seqlens_k, nk_pad,
+                                       kcols, a->D, (uint8_t*)a->ws, st)
+                    : launch_expand_k(a->k.codes, a->k.scales, a->Hkv, a->B, a->Nk, a->Nk, a->cu_seqlens_k, nk_pad,
+                                      kcols, a->D, pf, khat, st);
   if (e != hipSuccess) return hip_status(e);
   FwdParams p;
   memset(&p, 0, sizeof(p));
@@ -227,8 +246,9 @@ static attn_status run_fwd_lowp(const attn_fwd_args* a, void* stream, int pf, in
     e = hipEventRecord((hipEvent_t)a->prof_event_begin, st);
     if (e != hipSuccess) return hip_status(e);
   }
-  e = launch_fwd_lowp(p, a->D, pf, a->v.format == ATTN_V_MXFP4 ? 1 : 0, a->causal != 0, a->dbg_p_codes != nullptr,
-                      enc, st);
+  e = mx ? launch_fwd_mx(p, a->D, a->v.format == ATTN_V_MXFP4 ? 1 : 0, a->dbg_p_codes != nullptr, st)
+         : launch_fwd_lowp(p, a->D, pf, a->v.format == ATTN_V_MXFP4 ? 1 : 0, a->causal != 0,
+                           a->dbg_p_codes != nullptr, enc, st);
   if (e != hipSuccess) return hip_status(e);
   if (a->prof_event_end != nullptr) e = hipEventRecord((hipEvent_t)a->prof_event_end, st);
   return hip_status(e);
@@ -238,6 +258,9 @@ attn_status attn_fwd_directp(const attn_fwd_args* a, void* stream) { return run_
 attn_status attn_fwd_fp8pv(const attn_fwd_args* a, void* stream) { return run_fwd_lowp(a, stream, 1, 0); }
 attn_status attn_fwd_directp_efq(const attn_fwd_args* a, void* stream) { return run_fwd_lowp(a, stream, 0, 1); }
 attn_status attn_fwd_fp8pv_cast(const attn_fwd_args* a, void* stream) { return run_fwd_lowp(a, stream, 1, 1); }
+attn_status attn_fwd_directp_mxqk(const attn_fwd_args* a, void* stream) {
+  return run_fwd_lowp(a, stream, 0, 0, true);
+}
 
 attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Hq,
                           int32_t Hkv, int32_t Nq, int32_t Nk, int32_t D, float softmax_scale, int32_t causal,

@@ -90,6 +90,48 @@ __global__ void __launch_bounds__(256) expand_k_kernel(const uint8_t* __restrict
   }
 }
 
+// Pre-pass of the MX Q/K mode: MXFP4 K codes rearranged into 128-key operand
+// tiles of the scaled FP4 S MFMA (no decoding).  Tile layout (K_BYTES =
+// 64 D + 512 bytes): 16-byte unit (st, ks, kh, r) at ((st*KS + ks)*2 + kh)*32 + r
+// holds the codes of d in 64 ks + 32 kh + [0, 32) of key s_key(st, v(r), hh(r))
+// (KS = D/64), then one dword per (st, r) at 64 D + 4 (32 st + r) holding
+// that key's D/32 E8M0 bytes (byte b = block b).  Keys past the end of the
+// sequence get zero codes and zero bytes.
+template <int D, int PF>
+__global__ void __launch_bounds__(256) pack_k_mx_kernel(const uint8_t* __restrict__ codes,
+                                                        const uint8_t* __restrict__ scales, int H, int N,
+                                                        const int32_t* __restrict__ cu, int64_t n_pad, int64_t cols,
+                                                        uint8_t* __restrict__ out) {
+  const int tile = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const bool varlen = cu != nullptr;
+  const int64_t tok0 = varlen ? cu[s] : (int64_t)s * N;
+  const int len = varlen ? cu[s + 1] - cu[s] : N;
+  if (tile * KEY_TILE >= len) return;
+  constexpr int KS = D / 64, KC = KEY_TILE * D / 2, UNITS = KC / 16;
+  uint8_t* tb = out + ((int64_t)h * (cols / KEY_TILE) + kcol_offset(varlen, s, tok0, n_pad) / KEY_TILE + tile) *
+                          (int64_t)(KC + 512);
+  for (int u = threadIdx.x; u < UNITS + 128; u += 256) {
+    const bool is_code = u < UNITS;
+    const int w = is_code ? u : u - UNITS;
+    const int r = w & 31;
+    const int kh = (w >> 5) & 1, ks = (w >> 6) % KS, st = is_code ? (w >> 6) / KS : w >> 5;
+    const int hh = (r >> 2) & 1, v = 4 * (r >> 3) + (r & 3);   // inverse of out_row
+    const int idx = tile * KEY_TILE + s_key<PF>(st, v, hh);
+    const int64_t row = (tok0 + idx) * H + h;
+    if (is_code) {
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (idx < len) val = *reinterpret_cast<const u32x4*>(codes + row * (D / 2) + 32 * ks + 16 * kh);
+      *reinterpret_cast<u32x4*>(tb + u * 16) = val;
+    } else {
+      uint32_t val = 0u;
+      if (idx < len)
+        val = D == 128 ? *reinterpret_cast<const uint32_t*>(scales + row * 4)
+                       : (uint32_t)*reinterpret_cast<const uint16_t*>(scales + row * 2);
+      *reinterpret_cast<uint32_t*>(tb + KC + w * 4) = val;
+    }
+  }
+}
+
 // First vector unit of slot i of the key loop: slots [0, NPV) carry units
 // [3, 13) (statistics and the encode of sub-tile 0); then each group of KS
 // slots carries 8 units (encode of the next sub-tile; in the last group the
@@ -111,9 +153,12 @@ __host__ __device__ constexpr int slot_unit_begin(int i) {
 #define ATTN_PRIO_END (NPV - 1)
 #endif
 
-template <int D, int VF>
+// K tile: FP16 operand tile (QK = 0), or (QK = 1) the MXFP4 codes in
+// operand order followed by one E8M0 dword per (sub-tile, A-operand row).
+template <int D, int VF, int QK = 0>
 struct LdsLayout {
-  static constexpr int K_BYTES = KEY_TILE * D * 2;                         // fp16 K tile
+  static constexpr int KC_BYTES = QK ? KEY_TILE * D / 2 : KEY_TILE * D * 2;
+  static constexpr int K_BYTES = KC_BYTES + (QK ? 4 * 32 * 4 : 0);
   static constexpr int V_BYTES = VF == VF_MXFP4 ? KEY_TILE * D / 2 : KEY_TILE * D;
   static constexpr int VS_BYTES = VF == VF_MXFP4 ? D * 4 : 0;              // E8M0 V scales
   static constexpr int V_SLOT = V_BYTES + VS_BYTES;
@@ -135,12 +180,18 @@ struct LdsLayout {
 // P is double-buffered (P(t-2) is read while P(t-1) is written).  The
 // 8 waves share K(t) / V(t-2) tiles in LDS; tiles for iteration t+1 are
 // copied during iteration t and one barrier per iteration separates them.
-template <int D, int PF, int VF, bool CAUSAL, bool DEBUG, int ENC>
+//
+// QK = 1 is the opt-in MX-native Q/K mode: Q and K carry MXFP4 codes with one
+// E8M0 exponent per 32 elements along D, and each S sub-tile is D/64 scaled
+// FP4 MFMAs (v_mfma_scale_f32_32x32x64_f8f6f4, both operands E2M1, the block
+// exponents as scale_a / scale_b) instead of D/16 FP16 ones.  The S^T layout,
+// and with it everything from the row max on, is unchanged.
+template <int D, int PF, int VF, bool CAUSAL, bool DEBUG, int ENC, int QK>
 __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
-  constexpr int KS = D / 16;           // k-steps of the S MFMA
+  constexpr int KS = QK ? D / 64 : D / 16;   // k-steps of the S MFMA per sub-tile
   constexpr int DT = D / 32;           // 32-row tiles of O^T
   constexpr int HALF = D / 2;
-  using L = LdsLayout<D, VF>;
+  using L = LdsLayout<D, VF, QK>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   // ---- workgroup -> (batch, head, query block).
@@ -192,7 +243,9 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   }
 
   // ---- scalars: c = sigma * log2(e) * gq * gk
-  const float cc = (float)((double)p.sigma * 1.4426950408889634 * (double)(*p.gq) * (double)(*p.gk));
+  // (MX Q/K: no tensor scales, the E8M0 block exponents are applied by the MFMA)
+  const float cc = QK ? (float)((double)p.sigma * 1.4426950408889634)
+                      : (float)((double)p.sigma * 1.4426950408889634 * (double)(*p.gq) * (double)(*p.gk));
   const float vscale = VF == VF_FP8 ? *p.sv : 1.0f;
   // exp-free cast: 2^M, and 2^M * b, of the code format (E2M1: M = 1, b = 1;
   // E4M3: M = 3, b = 7); ccl = 2^M c is exact
@@ -203,8 +256,26 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   // ---- Q operand (B of S^T): lane holds query ql, d in [hh*D/2, hh*D/2 + D/2),
   // decoded here from the NVFP4 codes (E2M1 * E4M3 is exact in FP16); once per
   // workgroup, so a separate expansion pass for Q is not needed
-  f16x8 qf[KS];
-  {
+  f16x8 qf[QK ? 1 : KS];
+  // MX Q/K: lane (ql, hh) holds the FP4 codes of d in 64 ks + 32 hh + [0, 32)
+  // for each k-step, and the row's E8M0 bytes shifted so that byte 2 ks is
+  // block (ks, hh) -- the B operand of the scaled MFMA and its scale_b
+  u32x4 qm[QK ? KS : 1];
+  uint32_t qsc = 0u;
+  if constexpr (QK) {
+    const bool live = wave_active && my_q < len_q;
+    const int64_t row = live ? (tq0 + my_q) * p.Hq + h : 0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qm[ks] = live ? *reinterpret_cast<const u32x4*>(p.q_codes + row * HALF + 32 * ks + 16 * hh) : u32x4{0u, 0u, 0u, 0u};
+    uint32_t sw = 0u;
+    if (live) sw = D == 128 ? *reinterpret_cast<const uint32_t*>(p.q_scales + row * 4)
+                            : (uint32_t)*reinterpret_cast<const uint16_t*>(p.q_scales + row * 2);
+    qsc = sw >> (8 * hh);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qm[ks]));
+    asm volatile("" : "+v"(qsc));
+  } else {
     const bool live = wave_active && my_q < len_q;
     const int64_t row = live ? (tq0 + my_q) * p.Hq + h : 0;
     const uint8_t* qc = p.q_codes + row * HALF + hh * (HALF / 2);
@@ -225,26 +296,38 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   // ---- LDS: K slots 0/1 then V slots 0/1 (codes + scales).  Iteration t reads
   // K(t) from K slot t%2 and V(t-2) from V slot t%2.
   const int64_t kcol0 = kcol_offset(varlen, b, tk0, p.nk_pad);
-  const uint8_t* ksrc = reinterpret_cast<const uint8_t*>(p.khat + ((int64_t)hk * p.kcols + kcol0) * D);
+  // K tiles of this head in the workspace, L::K_BYTES each (kcols and kcol0
+  // are multiples of the tile)
+  const uint8_t* ksrc = reinterpret_cast<const uint8_t*>(p.khat) +
+                        ((int64_t)hk * (p.kcols / KEY_TILE) + kcol0 / KEY_TILE) * L::K_BYTES;
   const uint32_t lds0 = lds_address(smem);
   // per-head bases (per-lane offsets below stay under 4 GiB)
   const uint8_t* vhead = p.v_codes + (VF == VF_MXFP4 ? (int64_t)hk * D * p.kcols / 2 : (int64_t)hk * D * p.kcols);
   const uint8_t* shead = VF == VF_MXFP4 ? p.v_scales + (int64_t)hk * D * (p.kcols / 32) : nullptr;
-  constexpr int K_UNITS = L::K_BYTES / 16;
+  constexpr int K_UNITS = L::KC_BYTES / 16;
   constexpr int V_UNITS = L::V_BYTES / 16;
-  static_assert(K_UNITS % 512 == 0, "K tile must split evenly over the workgroup");
+  static_assert(QK || K_UNITS % 512 == 0, "K tile must split evenly over the workgroup");
+  static_assert(!QK || K_UNITS % 256 == 0, "MX K codes must split over whole waves");
   // Copies are split into parts of one instruction per wave (1 KB of K or V,
   // or the V block exponents) so that the key loop can spread them over its
   // slots: a burst of copies at one point would fill the address queue and
   // stall the issuing waves' matrix work behind it.
-  constexpr int NK_DMA = K_UNITS / 512;
+  // (MX K: the codes, then one part for the 512 bytes of block exponents)
+  constexpr int NK_DMA = QK ? (K_UNITS + 511) / 512 + 1 : K_UNITS / 512;
   constexpr int NV_DMA = (V_UNITS + 511) / 512 + (VF == VF_MXFP4 ? 1 : 0);
   // part i of K(src) -> K ring slot rs
   // (tile and part offsets go into the scalar base, so that the per-lane
   // offsets are loop invariant)
   auto copy_k_part = [&](int rs, int src, int i) {
     const uint32_t slot = lds0 + (uint32_t)(rs * L::K_BYTES);
-    const int u0 = i * 512 + wave * 64;
+    if (QK && i == NK_DMA - 1) {               // E8M0 dwords: two waves' worth, the others repeat them
+      const int w = wave & 1;
+      dma4(ksrc + (int64_t)src * L::K_BYTES + L::KC_BYTES + w * 256, (uint32_t)(lane * 4),
+           slot + L::KC_BYTES + w * 256);
+      return;
+    }
+    // (MX K at D=64: 256 units, so waves 4-7 repeat the copies of waves 0-3)
+    const int u0 = QK ? (i * 512 + wave * 64) % K_UNITS : i * 512 + wave * 64;
     dma16(ksrc + (int64_t)src * L::K_BYTES + u0 * 16, (uint32_t)(lane * 16), slot + u0 * 16);
   };
   // part i of V(src) -> V ring slot rs
@@ -314,7 +397,30 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
 
   // ---- pipeline pieces --------------------------------------------------
   // S^T sub-tiles st0, st0+1 of K(t) Q^T (K in slot ks_)
+  // MX Q/K: one scaled FP4 MFMA of S^T sub-tile st, k-step ks; ka holds the
+  // lane's 32 K codes (A operand row ql, k-half hh), ksw the key row's E8M0
+  // bytes shifted so that byte 2 ks is block (ks, hh)
+  auto mx_mfma = [&](int st, int ks, const u32x4& ka, uint32_t ksw) {
+    const i32x8 a = {(int)ka[0], (int)ka[1], (int)ka[2], (int)ka[3], 0, 0, 0, 0};
+    const i32x8 bq = {(int)qm[ks][0], (int)qm[ks][1], (int)qm[ks][2], (int)qm[ks][3], 0, 0, 0, 0};
+    if (ks == 0)
+      s[st] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bq, f32x16{}, 4, 4, 0, (int)ksw, 0, (int)qsc);
+    else
+      s[st] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bq, s[st], 4, 4, 2, (int)ksw, 2, (int)qsc);
+  };
   auto qk2 = [&](int kslot, int st0) {
+    if constexpr (QK) {
+      const uint8_t* kbm = smem + kslot * L::K_BYTES + lane * 16;
+      const uint32_t* kw = reinterpret_cast<const uint32_t*>(smem + kslot * L::K_BYTES + L::KC_BYTES);
+#pragma unroll
+      for (int st = st0; st < st0 + 2; ++st) {
+        const uint32_t ksw = kw[st * 32 + ql] >> (8 * hh);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          mx_mfma(st, ks, *reinterpret_cast<const u32x4*>(kbm + (st * KS + ks) * 64 * 16), ksw);
+      }
+      return;
+    }
     const uint8_t* kb = smem + kslot * L::K_BYTES + (hh * KS * 32 + ql) * 16;
     f16x8 a0 = *reinterpret_cast<const f16x8*>(kb + (st0 * 2 * KS) * 32 * 16);
     f16x8 a1 = *reinterpret_cast<const f16x8*>(kb + ((st0 + 1) * 2 * KS) * 32 * 16);
@@ -391,6 +497,7 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   constexpr int NS = NPV + 4 * KS;
   u32x4 opa[3], opb[3];
   uint32_t vsc[DT];
+  uint32_t ksc[4];                     // MX K: E8M0 words of K(t), one per S sub-tile
   auto load_op = [&](int i, const uint8_t* sV, const uint8_t* kb) {
     const int bs = i % 3;
     if (i < NPV) {
@@ -404,7 +511,8 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
       }
     } else {
       const int q = i - NPV, st = q / KS, ks = q % KS;
-      opa[bs] = *reinterpret_cast<const u32x4*>(kb + (st * 2 * KS + ks) * 32 * 16);
+      if (QK) opa[bs] = *reinterpret_cast<const u32x4*>(kb + (st * KS + ks) * 64 * 16);
+      else opa[bs] = *reinterpret_cast<const u32x4*>(kb + (st * 2 * KS + ks) * 32 * 16);
     }
   };
   auto mfma_slot = [&](int i) {
@@ -431,8 +539,12 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
       }
     } else {
       const int q = i - NPV, st = q / KS, ks = q % KS;
-      const f16x8 a = __builtin_bit_cast(f16x8, opa[bs]);
-      s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ks], ks == 0 ? f32x16{} : s[st], 0, 0, 0);
+      if constexpr (QK) {
+        mx_mfma(st, ks, opa[bs], ksc[st]);
+      } else {
+        const f16x8 a = __builtin_bit_cast(f16x8, opa[bs]);
+        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ks], ks == 0 ? f32x16{} : s[st], 0, 0, 0);
+      }
     }
   };
   auto vunit = [&](int u) {
@@ -580,7 +692,12 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
       bmp[1] = tile_max(2);
     }
     const uint8_t* sV = smem + L::V_BASE + rk1 * L::V_SLOT;                   // V(t-2): (t-2) mod 3 = (t+1) mod 3
-    const uint8_t* kb = smem + rk * L::K_BYTES + (hh * KS * 32 + ql) * 16;   // K(t)
+    const uint8_t* kb = smem + rk * L::K_BYTES + (QK ? lane : hh * KS * 32 + ql) * 16;   // K(t)
+    if constexpr (QK) {
+      const uint32_t* kw = reinterpret_cast<const uint32_t*>(smem + rk * L::K_BYTES + L::KC_BYTES);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) ksc[st] = kw[st * 32 + ql] >> (8 * hh);
+    }
     if (VF == VF_MXFP4) {
       const uint32_t* sVS = reinterpret_cast<const uint32_t*>(sV + L::V_BYTES);
 #pragma unroll
@@ -672,10 +789,10 @@ hipError_t launch_expand_k(const uint8_t* codes, const uint8_t* scales, int H, i
   return hipGetLastError();
 }
 
-template <int D, int PF, int VF, bool CAUSAL, bool DEBUG, int ENC>
+template <int D, int PF, int VF, bool CAUSAL, bool DEBUG, int ENC, int QK = 0>
 static hipError_t launch_fwd_t(const FwdParams& p, int nwg, hipStream_t st) {
-  auto kern = fwd_lowp_kernel<D, PF, VF, CAUSAL, DEBUG, ENC>;
-  const int lds = LdsLayout<D, VF>::TOTAL;
+  auto kern = fwd_lowp_kernel<D, PF, VF, CAUSAL, DEBUG, ENC, QK>;
+  const int lds = LdsLayout<D, VF, QK>::TOTAL;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(nwg), dim3(512), lds, st, p);
@@ -711,6 +828,29 @@ hipError_t launch_fwd_lowp(const FwdParams& p, int D, int pf, int vf, bool causa
   if (nwg == 0) return hipSuccess;
   return enc ? launch_fwd_e<1>(p, nwg, D, pf, vf, causal, debug, st)
              : launch_fwd_e<0>(p, nwg, D, pf, vf, causal, debug, st);
+}
+
+// MX Q/K mode: Direct-P (MXFP4 P), noncausal, exact encode; V FP8 or MXFP4.
+hipError_t launch_pack_k_mx(const uint8_t* codes, const uint8_t* scales, int H, int B, int N, int max_len,
+                            const int32_t* cu, int64_t n_pad, int64_t cols, int D, uint8_t* out, hipStream_t st) {
+  dim3 grid((unsigned)((max_len + KEY_TILE - 1) / KEY_TILE), (unsigned)H, (unsigned)B);
+  if (grid.x == 0 || B == 0) return hipSuccess;
+  if (D == 64)
+    hipLaunchKernelGGL((pack_k_mx_kernel<64, 0>), grid, dim3(256), 0, st, codes, scales, H, N, cu, n_pad, cols, out);
+  else
+    hipLaunchKernelGGL((pack_k_mx_kernel<128, 0>), grid, dim3(256), 0, st, codes, scales, H, N, cu, n_pad, cols, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_mx(const FwdParams& p, int D, int vf, bool debug, hipStream_t st) {
+  const int nwg = p.B * p.Hq * p.QB;
+  if (nwg == 0) return hipSuccess;
+#define MXL(DD, VV)                                                              \
+  (debug ? launch_fwd_t<DD, PF_MXFP4, VV, false, true, 0, 1>(p, nwg, st)          \
+         : launch_fwd_t<DD, PF_MXFP4, VV, false, false, 0, 1>(p, nwg, st))
+  if (vf == VF_MXFP4) return D == 64 ? MXL(64, VF_MXFP4) : MXL(128, VF_MXFP4);
+  return D == 64 ? MXL(64, VF_FP8) : MXL(128, VF_FP8);
+#undef MXL
 }
 
 }  // namespace attn

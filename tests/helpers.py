@@ -52,13 +52,22 @@ def oracle_v_head(v_head_f32, v_format, amax_all=None):
 
 
 def oracle_head(q_rows, k_rows, v_rows, *, amax_q, amax_k, amax_v, sigma, p_format, v_format, causal,
-                q_index=None, return_p=False, encoder="exact", p_given=None, return_pre=False, four_six=False):
+                q_index=None, return_p=False, encoder="exact", p_given=None, return_pre=False, four_six=False,
+                qk="nvfp4"):
     """Oracle forward for a set of query rows of one head, given the bf16
-    inputs (as float32 numpy) and the whole-tensor amax values."""
+    inputs (as float32 numpy) and the whole-tensor amax values.  ``qk="mxfp4"``
+    quantizes Q and K with the MX-native rule (E8M0 per 32 along D, no tensor
+    scales) instead of NVFP4."""
+    vh = oracle_v_head(v_rows, v_format, amax_v)
+    if qk == "mxfp4":
+        qc, qe = OQ.quant_mxfp4(q_rows)
+        kc, ke = OQ.quant_mxfp4(k_rows)
+        return OA.attn_lowp_head(OQ.dequant_mxfp4(qc, qe), OQ.dequant_mxfp4(kc, ke), 1.0, 1.0, vh, sigma,
+                                 p_format, causal, q_index=q_index, return_p=return_p, encoder=encoder,
+                                 p_given=p_given, return_pre=return_pre)
     qfn = OQ.quant_nvfp4_46 if four_six else OQ.quant_nvfp4
     qc, qs, gq = qfn(q_rows, amax=amax_q)
     kc, ks, gk = qfn(k_rows, amax=amax_k)
-    vh = oracle_v_head(v_rows, v_format, amax_v)
     return OA.attn_lowp_head(OQ.dequant_nvfp4_raw(qc, qs), OQ.dequant_nvfp4_raw(kc, ks), gq, gk, vh, sigma,
                              p_format, causal, q_index=q_index, return_p=return_p, encoder=encoder,
                              p_given=p_given, return_pre=return_pre)

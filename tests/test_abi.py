@@ -209,3 +209,23 @@ def test_decode_validation(lib):
     # FP8-P/V takes FP8 V only
     assert lib.attn_decode_fp8pv(ctypes.byref(_dec_args(v=B._VTensor(1, 1 << 24, 1 << 24, 1 << 24))), None) == 2
     assert lib.attn_decode_directp(None, None) == 1 and lib.attn_decode_fp8pv(None, None) == 1
+
+
+def test_mx_qk_entry_points_reject_bad_arguments(lib):
+    fake = ctypes.c_void_p(1 << 20)
+    # D must be a multiple of 32; non-empty tensors need their pointers; codes 16-byte aligned
+    assert lib.attn_quant_mxfp4(fake, 4, 48, fake, fake, None) == 1
+    assert lib.attn_quant_mxfp4(None, 4, 64, fake, fake, None) == 1
+    assert lib.attn_quant_mxfp4(fake, 4, 64, ctypes.c_void_p((1 << 20) + 8), fake, None) == 1
+    assert lib.attn_quant_mxfp4(None, 0, 64, None, None, None) == 0      # empty: nothing to do
+    a = _args()
+    need = lib.attn_fwd_ws_bytes(ctypes.byref(a))
+    # tensor scales are not used: NULL is accepted past validation only with everything else valid,
+    # so check the rejections that come first
+    noscale = dict(q=B._NvTensor(1 << 24, 1 << 24, None), k=B._NvTensor(1 << 24, 1 << 24, None))
+    assert lib.attn_fwd_directp_mxqk(ctypes.byref(_args(causal=1, ws=1 << 24, ws_bytes=need, **noscale)), None) == 2
+    assert lib.attn_fwd_directp_mxqk(ctypes.byref(_args(D=96, ws=1 << 24, ws_bytes=need, **noscale)), None) == 1
+    assert lib.attn_fwd_directp_mxqk(ctypes.byref(_args(ws=1 << 24, ws_bytes=need - 1, **noscale)), None) == 3
+    misaligned = dict(q=B._NvTensor((1 << 24) + 8, 1 << 24, None), k=B._NvTensor(1 << 24, 1 << 24, None))
+    assert lib.attn_fwd_directp_mxqk(ctypes.byref(_args(ws=1 << 24, ws_bytes=need, **misaligned)), None) == 1
+    assert lib.attn_fwd_directp_mxqk(None, None) == 1

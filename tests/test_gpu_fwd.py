@@ -29,10 +29,13 @@ ENTRY = {("mxfp4", "exact"): "fwd_directp", ("fp8", "exact"): "fwd_fp8pv",
          ("mxfp4", "loglin"): "fwd_directp_efq", ("fp8", "loglin"): "fwd_fp8pv_cast"}
 
 
-def _gpu_run(gpu, inp, debug=None, out_dtype=torch.float32, encoder="exact", four_six=False):
+def _gpu_run(gpu, inp, debug=None, out_dtype=torch.float32, encoder="exact", four_six=False, qk="nvfp4"):
     wl = inp.wl
-    q = gpu.quant_nvfp4(inp.q, four_six=four_six)
-    k = gpu.quant_nvfp4(inp.k, four_six=four_six)
+    if qk == "mxfp4":
+        q, k = gpu.quant_mxfp4(inp.q), gpu.quant_mxfp4(inp.k)
+    else:
+        q = gpu.quant_nvfp4(inp.q, four_six=four_six)
+        k = gpu.quant_nvfp4(inp.k, four_six=four_six)
     vf = gpu.V_FP8 if wl.v_format == "fp8" else gpu.V_MXFP4
     kw = dict(Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D, softmax_scale=inp.sigma, causal=wl.causal, out_dtype=out_dtype,
               debug=debug)
@@ -45,7 +48,7 @@ def _gpu_run(gpu, inp, debug=None, out_dtype=torch.float32, encoder="exact", fou
         vq = gpu.quant_v(inp.v, vf, cu_seqlens=cu, max_seqlen=mx)
         kw.update(cu_seqlens_q=cu, cu_seqlens_k=cu, max_seqlen_q=mx, max_seqlen_k=mx)
     v = (vf, vq[0], vq[1], vq[2])
-    fn = getattr(gpu, ENTRY[(wl.p_format, encoder)])
+    fn = getattr(gpu, "fwd_directp_mxqk" if qk == "mxfp4" else ENTRY[(wl.p_format, encoder)])
     o, lse, dbg = fn(q, k, v, **kw)
     torch.cuda.synchronize()
     return o, lse, dbg
@@ -64,7 +67,8 @@ def _seq_slices(inp):
     return [(s, int(cu[s]), int(cu[s + 1] - cu[s])) for s in range(len(cu) - 1)]
 
 
-def _check(gpu, inp, heads=None, seqs=None, rows=None, dumps=True, max_rows=None, encoder="exact", four_six=False):
+def _check(gpu, inp, heads=None, seqs=None, rows=None, dumps=True, max_rows=None, encoder="exact", four_six=False,
+           qk="nvfp4"):
     """Run the production kernel once and compare the selected (sequence,
     head, rows) with the oracle.
 
@@ -76,7 +80,7 @@ def _check(gpu, inp, heads=None, seqs=None, rows=None, dumps=True, max_rows=None
     are then compared with the oracle run on the kernel's codes, so that a
     tie decided the other way is not counted as an output error."""
     wl = inp.wl
-    o, lse, _ = _gpu_run(gpu, inp, encoder=encoder, four_six=four_six)
+    o, lse, _ = _gpu_run(gpu, inp, encoder=encoder, four_six=four_six, qk=qk)
     amax_q, amax_k, amax_v = _amax(inp.q), _amax(inp.k), _amax(inp.v)
     varlen = inp.cu_seqlens is not None
     group = wl.Hq // wl.Hkv
@@ -104,12 +108,13 @@ def _check(gpu, inp, heads=None, seqs=None, rows=None, dumps=True, max_rows=None
                 r = r[np.linspace(0, len(r) - 1, max_rows).astype(int)]
             ridx = torch.as_tensor(r, device=o.device)
             kw = dict(amax_q=amax_q, amax_k=amax_k, amax_v=amax_v, sigma=inp.sigma, p_format=wl.p_format,
-                      v_format=wl.v_format, causal=wl.causal, q_index=r, encoder=encoder, four_six=four_six)
+                      v_format=wl.v_format, causal=wl.causal, q_index=r, encoder=encoder, four_six=four_six,
+                      qk=qk)
             q_rows, k_all, v_all = f32(qh[torch.as_tensor(r, device=qh.device)]), f32(kh), f32(vh)
             if not dumps:
                 res = oracle_head(q_rows, k_all, v_all, **kw)
             else:
-                od, ld, (dc, ds) = _gpu_run(gpu, inp, debug=(s, h), encoder=encoder, four_six=four_six)
+                od, ld, (dc, ds) = _gpu_run(gpu, inp, debug=(s, h), encoder=encoder, four_six=four_six, qk=qk)
                 assert torch.equal(od, o) and torch.equal(ld, lse), "the dump build computes other outputs"
                 res = oracle_head(q_rows, k_all, v_all, return_pre=True, **kw)
                 gc, ge = gpu_codes(dc[ridx].cpu().numpy(), None if ds is None else ds[ridx].cpu().numpy(),

@@ -1,0 +1,131 @@
+"""GPU MX-native Q/K mode (opt-in; attn_quant_mxfp4 + attn_fwd_directp_mxqk)
+against the oracle on the same seeded inputs.
+
+Bar: MXFP4 Q/K codes and E8M0 bytes bit-exact; the forward to the bar of the
+NVFP4 Direct-P path (probability codes differ from the oracle's in at most
+1e-4 of the live elements, and only at rounding near-ties; O within relative
+L2 1e-3 and max abs 5e-3; LSE within 1e-4 relative), with the oracle's Q^/K^
+from its own MXFP4 quantizer.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import quant as OQ
+from precision_attention_forward_amd import synth
+from test_gpu_fwd import _check, _gpu_run
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _quant_inputs():
+    g = torch.Generator().manual_seed(71)
+    out = []
+    for rows, D in [(1, 32), (37, 64), (300, 128)]:
+        x = torch.randn(rows, D, generator=g) * torch.exp2(torch.randint(-20, 20, (rows, 1), generator=g).float())
+        x = x.to(torch.bfloat16)
+        out.append((f"rand_{rows}x{D}", x))
+    x = torch.randn(64, 128, generator=g)
+    x[0] = 0.0                                   # all-zero row
+    x[1, :32] = -0.0                             # negative zeros
+    x[2, 5] = 3.0e38                             # near the bf16 maximum
+    x[3, :] = 1e-39                              # subnormal block maxima
+    x[4, 7] = -1e-40
+    x[5, :] = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25] * 16)   # E2M1 ties at e = 0 ...
+    x[5, 0] = 6.0                                # ... (block max 6 keeps e = 0)
+    x[6, ::3] *= 64.0                            # mixed block ranges
+    out.append(("edges", x.to(torch.bfloat16)))
+    return out
+
+
+@pytest.mark.parametrize("name,x", _quant_inputs(), ids=[c[0] for c in _quant_inputs()])
+def test_quant_mxfp4_bit_exact(gpu, name, x):
+    _say(f"quant_mxfp4 {name}")
+    codes, scales, none = gpu.quant_mxfp4(x.cuda())
+    torch.cuda.synchronize()
+    assert none is None
+    rc, re_ = OQ.quant_mxfp4(x.float().numpy())
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(scales.cpu().numpy(), re_)
+
+
+def test_quant_mxfp4_full_size_sampled(gpu):
+    wl = synth.WORKLOADS[2]
+    _say("quant_mxfp4 full-size Wan Q")
+    inp = synth.generate(wl, "cuda")
+    codes, scales, _ = gpu.quant_mxfp4(inp.q)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(2).integers(0, wl.N, 512)
+    for t in (inp.q, ):
+        sel = torch.as_tensor(rows, device=t.device)
+        x = t[0, sel].float().cpu().numpy()                     # [rows, H, D]
+        rc, re_ = OQ.quant_mxfp4(x)
+        assert np.array_equal(codes[0, sel].cpu().numpy(), rc)
+        assert np.array_equal(scales[0, sel].cpu().numpy(), re_)
+    del inp
+    torch.cuda.empty_cache()
+
+
+SMALL = [
+    ("tiny", synth.WORKLOADS[1]),
+    ("wan_recipe_small_mxfp4v", synth.WORKLOADS[2].with_(Hq=2, Hkv=2, N=1000, seed=21)),
+    ("wan_d64_small_fp8v", synth.WORKLOADS[3].with_(Hq=3, Hkv=3, N=700, seed=31)),
+    ("d64_mxfp4v", synth.WORKLOADS[3].with_(Hq=2, Hkv=2, N=520, v_format="mxfp4", seed=33)),
+    ("d128_fp8v_gqa", synth.WORKLOADS[2].with_(Hq=4, Hkv=1, N=384, v_format="fp8", seed=22)),
+    ("varlen_small", synth.WORKLOADS[5].with_(Hq=2, Hkv=2, varlen=(5, 1, 700), seed=51)),
+    ("two_batches_ragged", synth.WORKLOADS[2].with_(B=2, Hq=2, Hkv=1, N=300, seed=23)),
+]
+
+
+@pytest.mark.parametrize("name,wl", SMALL, ids=[s[0] for s in SMALL])
+def test_mxqk_small_shapes_all_outputs(gpu, name, wl):
+    _say(f"fwd MX Q/K small {name}")
+    inp = synth.generate(wl, "cpu")
+    inp.q, inp.k, inp.v = inp.q.cuda(), inp.k.cuda(), inp.v.cuda()
+    o, lse, stats = _check(gpu, inp, qk="mxfp4")
+    assert stats, "probability dump not compared"
+
+
+def test_mxqk_short_sequences(gpu):
+    for n in (1, 2, 31, 33, 127, 129):
+        _say(f"fwd MX Q/K N={n}")
+        wl = synth.WORKLOADS[1].with_(N=n, seed=100 + n)
+        inp = synth.generate(wl, "cpu")
+        inp.q, inp.k, inp.v = inp.q.cuda(), inp.k.cuda(), inp.v.cuda()
+        _check(gpu, inp, qk="mxfp4")
+
+
+def test_mxqk_determinism(gpu):
+    wl = synth.WORKLOADS[2].with_(Hq=2, Hkv=2, N=700, seed=24)
+    inp = synth.generate(wl, "cpu")
+    inp.q, inp.k, inp.v = inp.q.cuda(), inp.k.cuda(), inp.v.cuda()
+    a = _gpu_run(gpu, inp, qk="mxfp4")
+    b = _gpu_run(gpu, inp, qk="mxfp4")
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+FULL = [(2, [0, 39], 32), (3, [0, 79], 32), (5, [0, 31], 24)]
+
+
+@pytest.mark.parametrize("k,heads,nrows", FULL, ids=[f"workload{f[0]}" for f in FULL])
+def test_mxqk_full_size_sampled(gpu, k, heads, nrows):
+    wl = synth.WORKLOADS[k]
+    _say(f"fwd MX Q/K full-size {wl.name}")
+    inp = synth.generate(wl, "cuda")
+    if inp.cu_seqlens is None:
+        L = wl.N
+        seqs = [0, wl.B - 1]
+    else:
+        seqs = [int(np.argmin(inp.seqlens)), int(np.argmax(inp.seqlens))]
+        L = int(inp.seqlens.max())
+    rng = np.random.default_rng(100 + k)
+    rows = np.unique(np.concatenate([rng.integers(0, L, nrows), [0, 1, 255, 256, L - 1]]))
+    o, lse, stats = _check(gpu, inp, heads=heads, seqs=seqs, rows=rows, qk="mxfp4")
+    assert stats
+    del inp
+    torch.cuda.empty_cache()
