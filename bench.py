@@ -74,18 +74,20 @@ def kernel_source_hash(sources=None):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, path=TRAFFIC_FILE, sources=None):
-    """HBM bytes per launch of the attention kernel for `workload`, from the
-    counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by the factor a plain
-    copy of known size reads for the same counter), or None when there is no
-    figure for this workload or the kernel sources changed since it was taken."""
+def measured_traffic(workload, path=TRAFFIC_FILE, sources=None, qk="nvfp4"):
+    """HBM bytes per launch of the attention kernel for `workload` (and Q/K
+    mode `qk`), from the counter summary (FETCH_SIZE + WRITE_SIZE, each scaled
+    by the factor a plain copy of known size reads for the same counter), or
+    None when there is no figure for this workload or the kernel sources
+    changed since it was taken."""
     if not os.path.exists(path):
         return None
     src = kernel_source_hash(sources)
     for line in open(path):
-        m = re.match(r"\s*traffic:\s+workload=(\d+)\s+source=([0-9a-f]+)\s+bytes_per_launch=([0-9.eE+]+)", line)
-        if m and int(m.group(1)) == workload and m.group(2) == src:
-            return float(m.group(3))
+        m = re.match(r"\s*traffic:\s+workload=(\d+)(?:\s+qk=(\w+))?\s+source=([0-9a-f]+)\s+bytes_per_launch=([0-9.eE+]+)",
+                     line)
+        if m and int(m.group(1)) == workload and (m.group(2) or "nvfp4") == qk and m.group(3) == src:
+            return float(m.group(4))
     return None
 
 
@@ -588,7 +590,7 @@ def main():
     ceiling = 1.0 / (0.5 / qk_rate + 0.5 / pv_rate)
     roofline = {"bound": "mfma", "achieved": round(kern_tflops, 2), "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(kern_tflops / MXFP4_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic(args.workload) if args.encoder == "exact" and not mxqk else None,
+                "traffic": measured_traffic(args.workload, qk=args.qk) if args.encoder == "exact" else None,
                 "kernel": "fwd_lowp_kernel", "kernel_ms": round(kern_ms, 4),
                 "mixed_ceiling_tflops": round(ceiling, 1), "frac_of_mixed_ceiling": round(kern_tflops / ceiling, 4)}
 
