@@ -40,7 +40,8 @@ def parse():
                     help="quantize Q and K with the Four Over Six adaptive block scale (attn_quant_nvfp4_46)")
     ap.add_argument("--qk", choices=("nvfp4", "mxfp4"), default="nvfp4",
                     help="Q/K format: nvfp4 (the method's; Q.K^T on the FP16 MFMA, exact) or the opt-in "
-                         "MX-native mxfp4 (E8M0 per 32 along D; Q.K^T on the scaled FP4 MFMA, attn_fwd_directp_mxqk)")
+                         "MX-native mxfp4 (E8M0 per 32 along D; Q.K^T on the scaled FP4 MFMA, "
+                         "attn_fwd_directp_mxqk / attn_fwd_fp8pv_mxqk)")
     ap.add_argument("--backward", action="store_true",
                     help="time the causal-training backward (attn_bwd_fp8) instead of the forward; its own JSON line")
     ap.add_argument("--decode", action="store_true",
@@ -495,8 +496,8 @@ def main():
         return
     wl = synth.WORKLOADS[args.workload]
     mxqk = args.qk == "mxfp4"
-    if mxqk and (wl.p_format != "mxfp4" or args.encoder != "exact" or args.four_six):
-        print("--qk mxfp4 is a Direct-P mode (MXFP4 P workloads, exact encoder, no Four Over Six)", file=sys.stderr)
+    if mxqk and (args.encoder != "exact" or args.four_six):
+        print("--qk mxfp4 takes the exact encoder and no Four Over Six", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -507,7 +508,7 @@ def main():
            ("mxfp4", "loglin"): paf.fwd_directp_efq, ("fp8", "loglin"): paf.fwd_fp8pv_cast}[(wl.p_format,
                                                                                           args.encoder)]
     if mxqk:
-        fwd = paf.fwd_directp_mxqk
+        fwd = paf.fwd_directp_mxqk if wl.p_format == "mxfp4" else paf.fwd_fp8pv_mxqk
     kw = dict(Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D, softmax_scale=inp.sigma, causal=wl.causal, out_dtype=torch.bfloat16)
     if varlen:
         cu = inp.cu_seqlens.to(dev)

@@ -288,8 +288,12 @@ attn_status attn_fwd_fp8pv_cast(const attn_fwd_args* a, void* stream);
  *         64 D + 512 bytes per 128-key tile and KV head of it)
  * Noncausal (ATTN_ERR_UNSUPPORTED otherwise); D in {64, 128}; V FP8 or
  * MXFP4.  Errors as for attn_fwd_directp.
+ *
+ * attn_fwd_fp8pv_mxqk: the same MX-native Q/K with the FP8-P/V arithmetic of
+ * attn_fwd_fp8pv (E4M3(2^(t - m')) with unit scale, FP8 V, causal or not).
  */
 attn_status attn_fwd_directp_mxqk(const attn_fwd_args* a, void* stream);
+attn_status attn_fwd_fp8pv_mxqk(const attn_fwd_args* a, void* stream);
 
 /*
  * BF16 fused attention forward, the baseline the pages compare against

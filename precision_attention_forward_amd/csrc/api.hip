@@ -21,9 +21,10 @@ hipError_t launch_expand_k(const uint8_t* codes, const uint8_t* scales, int H, i
                            hipStream_t st);
 hipError_t launch_quant_mxfp4(const void* x, int64_t rows, int D, uint8_t* codes, uint8_t* scales, hipStream_t st);
 hipError_t launch_pack_k_mx(const uint8_t* codes, const uint8_t* scales, int H, int B, int N, int max_len,
-                            const int32_t* cu, int64_t n_pad, int64_t cols, int D, uint8_t* out, hipStream_t st);
+                            const int32_t* cu, int64_t n_pad, int64_t cols, int D, int pf, uint8_t* out,
+                            hipStream_t st);
 struct FwdParams;
-hipError_t launch_fwd_mx(const FwdParams& p, int D, int vf, bool debug, hipStream_t st);
+hipError_t launch_fwd_mx(const FwdParams& p, int D, int pf, int vf, bool causal, bool debug, hipStream_t st);
 hipError_t launch_fwd_lowp(const FwdParams& p, int D, int pf, int vf, bool causal, bool debug, int enc,
                            hipStream_t st);
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
@@ -197,8 +198,8 @@ static attn_status validate_fwd(const attn_fwd_args* a, bool allow_causal, int p
 }
 
 // mx: the MX-native Q/K mode (MXFP4 Q/K codes with E8M0 bytes, no tensor
-// scales; Direct-P only), whose K pre-pass packs FP4 operand tiles instead of
-// expanding K to FP16.
+// scales; exact encoders), whose K pre-pass packs FP4 operand tiles instead
+// of expanding K to FP16.
 static attn_status run_fwd_lowp(const attn_fwd_args* a, void* stream, int pf, int enc, bool mx = false) {
   attn_status s = validate_fwd(a, pf == 1, pf, mx);
   if (s != ATTN_OK) return s;
@@ -208,7 +209,7 @@ static attn_status run_fwd_lowp(const attn_fwd_args* a, void* stream, int pf, in
   _Float16* khat = (_Float16*)a->ws;
   const int64_t nk_pad = roundup(a->Nk, 128);
   hipError_t e = mx ? launch_pack_k_mx(a->k.codes, a->k.scales, a->Hkv, a->B, a->Nk, a->Nk, a->cu_seqlens_k, nk_pad,
-                                       kcols, a->D, (uint8_t*)a->ws, st)
+                                       kcols, a->D, pf, (uint8_t*)a->ws, st)
                     : launch_expand_k(a->k.codes, a->k.scales, a->Hkv, a->B, a->Nk, a->Nk, a->cu_seqlens_k, nk_pad,
                                       kcols, a->D, pf, khat, st);
   if (e != hipSuccess) return hip_status(e);
@@ -246,7 +247,8 @@ static attn_status run_fwd_lowp(const attn_fwd_args* a, void* stream, int pf, in
     e = hipEventRecord((hipEvent_t)a->prof_event_begin, st);
     if (e != hipSuccess) return hip_status(e);
   }
-  e = mx ? launch_fwd_mx(p, a->D, a->v.format == ATTN_V_MXFP4 ? 1 : 0, a->dbg_p_codes != nullptr, st)
+  e = mx ? launch_fwd_mx(p, a->D, pf, a->v.format == ATTN_V_MXFP4 ? 1 : 0, a->causal != 0, a->dbg_p_codes != nullptr,
+                         st)
          : launch_fwd_lowp(p, a->D, pf, a->v.format == ATTN_V_MXFP4 ? 1 : 0, a->causal != 0,
                            a->dbg_p_codes != nullptr, enc, st);
   if (e != hipSuccess) return hip_status(e);
@@ -261,6 +263,7 @@ attn_status attn_fwd_fp8pv_cast(const attn_fwd_args* a, void* stream) { return r
 attn_status attn_fwd_directp_mxqk(const attn_fwd_args* a, void* stream) {
   return run_fwd_lowp(a, stream, 0, 0, true);
 }
+attn_status attn_fwd_fp8pv_mxqk(const attn_fwd_args* a, void* stream) { return run_fwd_lowp(a, stream, 1, 0, true); }
 
 attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Hq,
                           int32_t Hkv, int32_t Nq, int32_t Nk, int32_t D, float softmax_scale, int32_t causal,

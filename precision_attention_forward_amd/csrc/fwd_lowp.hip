@@ -830,26 +830,36 @@ hipError_t launch_fwd_lowp(const FwdParams& p, int D, int pf, int vf, bool causa
              : launch_fwd_e<0>(p, nwg, D, pf, vf, causal, debug, st);
 }
 
-// MX Q/K mode: Direct-P (MXFP4 P), noncausal, exact encode; V FP8 or MXFP4.
+// MX Q/K mode, exact encode: Direct-P (MXFP4 P; V FP8 or MXFP4; noncausal) or
+// FP8-P/V (causal or not).  The K tiles follow the P format's key order.
 hipError_t launch_pack_k_mx(const uint8_t* codes, const uint8_t* scales, int H, int B, int N, int max_len,
-                            const int32_t* cu, int64_t n_pad, int64_t cols, int D, uint8_t* out, hipStream_t st) {
+                            const int32_t* cu, int64_t n_pad, int64_t cols, int D, int pf, uint8_t* out,
+                            hipStream_t st) {
   dim3 grid((unsigned)((max_len + KEY_TILE - 1) / KEY_TILE), (unsigned)H, (unsigned)B);
   if (grid.x == 0 || B == 0) return hipSuccess;
-  if (D == 64)
-    hipLaunchKernelGGL((pack_k_mx_kernel<64, 0>), grid, dim3(256), 0, st, codes, scales, H, N, cu, n_pad, cols, out);
-  else
-    hipLaunchKernelGGL((pack_k_mx_kernel<128, 0>), grid, dim3(256), 0, st, codes, scales, H, N, cu, n_pad, cols, out);
+#define PK(DD, P) \
+  hipLaunchKernelGGL((pack_k_mx_kernel<DD, P>), grid, dim3(256), 0, st, codes, scales, H, N, cu, n_pad, cols, out)
+  if (pf == PF_MXFP4) {
+    if (D == 64) PK(64, PF_MXFP4); else PK(128, PF_MXFP4);
+  } else {
+    if (D == 64) PK(64, PF_FP8); else PK(128, PF_FP8);
+  }
+#undef PK
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_mx(const FwdParams& p, int D, int vf, bool debug, hipStream_t st) {
+hipError_t launch_fwd_mx(const FwdParams& p, int D, int pf, int vf, bool causal, bool debug, hipStream_t st) {
   const int nwg = p.B * p.Hq * p.QB;
   if (nwg == 0) return hipSuccess;
-#define MXL(DD, VV)                                                              \
-  (debug ? launch_fwd_t<DD, PF_MXFP4, VV, false, true, 0, 1>(p, nwg, st)          \
-         : launch_fwd_t<DD, PF_MXFP4, VV, false, false, 0, 1>(p, nwg, st))
-  if (vf == VF_MXFP4) return D == 64 ? MXL(64, VF_MXFP4) : MXL(128, VF_MXFP4);
-  return D == 64 ? MXL(64, VF_FP8) : MXL(128, VF_FP8);
+#define MXL(DD, PP, VV, CC)                                                     \
+  (debug ? launch_fwd_t<DD, PP, VV, CC, true, 0, 1>(p, nwg, st)                  \
+         : launch_fwd_t<DD, PP, VV, CC, false, 0, 1>(p, nwg, st))
+  if (pf == PF_FP8) {
+    if (causal) return D == 64 ? MXL(64, PF_FP8, VF_FP8, true) : MXL(128, PF_FP8, VF_FP8, true);
+    return D == 64 ? MXL(64, PF_FP8, VF_FP8, false) : MXL(128, PF_FP8, VF_FP8, false);
+  }
+  if (vf == VF_MXFP4) return D == 64 ? MXL(64, PF_MXFP4, VF_MXFP4, false) : MXL(128, PF_MXFP4, VF_MXFP4, false);
+  return D == 64 ? MXL(64, PF_MXFP4, VF_FP8, false) : MXL(128, PF_MXFP4, VF_FP8, false);
 #undef MXL
 }
 

@@ -264,46 +264,42 @@ __global__ void __launch_bounds__(256) quant_v_kernel(const uint16_t* __restrict
 }
 
 // MXFP4 Q/K (opt-in MX-native format; the OCP MX rule the V quantizer
-// applies along keys, here along D): one thread per 32-element block of a
-// row.  e = floor(log2 amax) - 2 (-127 for a zero or subnormal block max,
-// below the E8M0 range), codes E2M1(x * 2^-e) by the hardware RNE conversion
-// (x * 2^-e is exact), element 2k in the low nibble of byte k.  No tensor
-// scale and no amax pass: a single read of the input.
+// applies along keys, here along D).  Four consecutive lanes share one
+// 32-element block, eight elements (16 bytes) each, so a wave reads 1 KB of
+// contiguous input per load; the block max is combined with two lane
+// exchanges inside the group of four.  e = floor(log2 amax) - 2 (-127 for a
+// zero or subnormal block max, below the E8M0 range), codes E2M1(x * 2^-e)
+// by the hardware RNE conversion (x * 2^-e is exact), element 2k in the low
+// nibble of byte k.  No tensor scale and no amax pass: one read of the input.
 __global__ void __launch_bounds__(256) quant_mxfp4_kernel(const uint16_t* __restrict__ x, int64_t nblocks,
                                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int64_t nparts = nblocks * 4;            // 8-element parts; a block's four parts share a lane group
   const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x; i < nblocks; i += stride) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(x + i * 32);
-    u32x4 w[4];
+  // (stride and the start are multiples of 4, so a lane group is entirely in or out of range)
+  for (int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x; i < nparts; i += stride) {
+    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x) + i);
+    float f[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) w[k] = __builtin_nontemporal_load(&src[k]);
-    float f[32];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f[8 * k + 2 * j] = bf16_bits_to_f32(w[k][j] & 0xFFFFu);
-        f[8 * k + 2 * j + 1] = bf16_bits_to_f32(w[k][j] >> 16);
-      }
+    for (int j = 0; j < 4; ++j) {
+      f[2 * j] = bf16_bits_to_f32(w[j] & 0xFFFFu);
+      f[2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
+    }
     float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[j]));
+    for (int j = 0; j < 8; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[j]));
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2, 64));
     const uint32_t ab = __float_as_uint(amax);
     int e = (ab >> 23) == 0 ? -127 : (int)(ab >> 23) - 127 - 2;
     e = e < -127 ? -127 : e;
     const float mul = __builtin_amdgcn_ldexpf(1.0f, -e);
-    u32x4 o;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint32_t c = 0u;
-      c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, f[8 * k + 0] * mul, f[8 * k + 1] * mul, 1.0f, 0);
-      c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, f[8 * k + 2] * mul, f[8 * k + 3] * mul, 1.0f, 1);
-      c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, f[8 * k + 4] * mul, f[8 * k + 5] * mul, 1.0f, 2);
-      c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, f[8 * k + 6] * mul, f[8 * k + 7] * mul, 1.0f, 3);
-      o[k] = c;
-    }
-    *reinterpret_cast<u32x4*>(codes + i * 16) = o;
-    scales[i] = (uint8_t)(e + 127);
+    uint32_t c = 0u;
+    c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, f[0] * mul, f[1] * mul, 1.0f, 0);
+    c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, f[2] * mul, f[3] * mul, 1.0f, 1);
+    c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, f[4] * mul, f[5] * mul, 1.0f, 2);
+    c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, f[6] * mul, f[7] * mul, 1.0f, 3);
+    reinterpret_cast<uint32_t*>(codes)[i] = c;
+    if ((i & 3) == 0) scales[i >> 2] = (uint8_t)(e + 127);
   }
 }
 
@@ -350,8 +346,8 @@ hipError_t launch_quant_v(const void* v, int B, int Nk, int Hkv, int D, const in
 hipError_t launch_quant_mxfp4(const void* x, int64_t rows, int D, uint8_t* codes, uint8_t* scales, hipStream_t st) {
   const int64_t nblocks = rows * (D / 32);
   if (nblocks == 0) return hipSuccess;
-  const int64_t want = (nblocks + 255) / 256;
-  const int grid = (int)(want > 8192 ? 8192 : want);
+  const int64_t want = (nblocks * 4 + 255) / 256;
+  const int grid = (int)(want > 16384 ? 16384 : want);
   hipLaunchKernelGGL(quant_mxfp4_kernel, dim3(grid), dim3(256), 0, st, (const uint16_t*)x, nblocks, codes, scales);
   return hipGetLastError();
 }

@@ -229,3 +229,9 @@ def test_mx_qk_entry_points_reject_bad_arguments(lib):
     misaligned = dict(q=B._NvTensor((1 << 24) + 8, 1 << 24, None), k=B._NvTensor(1 << 24, 1 << 24, None))
     assert lib.attn_fwd_directp_mxqk(ctypes.byref(_args(ws=1 << 24, ws_bytes=need, **misaligned)), None) == 1
     assert lib.attn_fwd_directp_mxqk(None, None) == 1
+    # the FP8-P/V variant takes causal inputs but needs FP8 V
+    assert lib.attn_fwd_fp8pv_mxqk(ctypes.byref(_args(causal=1, Nk=128, ws=1 << 24, ws_bytes=need, **noscale)),
+                                   None) == 1
+    assert lib.attn_fwd_fp8pv_mxqk(ctypes.byref(_args(v=B._VTensor(1, 1 << 24, 1 << 24, 1 << 24), ws=1 << 24,
+                                                      ws_bytes=need, **noscale)), None) == 2
+    assert lib.attn_fwd_fp8pv_mxqk(None, None) == 1

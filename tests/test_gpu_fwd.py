@@ -48,7 +48,7 @@ def _gpu_run(gpu, inp, debug=None, out_dtype=torch.float32, encoder="exact", fou
         vq = gpu.quant_v(inp.v, vf, cu_seqlens=cu, max_seqlen=mx)
         kw.update(cu_seqlens_q=cu, cu_seqlens_k=cu, max_seqlen_q=mx, max_seqlen_k=mx)
     v = (vf, vq[0], vq[1], vq[2])
-    fn = getattr(gpu, "fwd_directp_mxqk" if qk == "mxfp4" else ENTRY[(wl.p_format, encoder)])
+    fn = getattr(gpu, ENTRY[(wl.p_format, encoder)] + ("_mxqk" if qk == "mxfp4" else ""))
     o, lse, dbg = fn(q, k, v, **kw)
     torch.cuda.synchronize()
     return o, lse, dbg

@@ -91,6 +91,33 @@ def test_mxqk_small_shapes_all_outputs(gpu, name, wl):
     assert stats, "probability dump not compared"
 
 
+FP8PV = [
+    ("llama_causal_small", synth.WORKLOADS[4].with_(B=2, Hq=4, Hkv=2, N=600, seed=41)),
+    ("llama_causal_d64", synth.WORKLOADS[4].with_(B=1, Hq=2, Hkv=1, N=450, D=64, seed=43)),
+    ("llama_noncausal_d64", synth.WORKLOADS[4].with_(B=1, Hq=4, Hkv=1, N=333, D=64, causal=False, seed=42)),
+    ("varlen_causal_fp8", synth.WORKLOADS[4].with_(B=0, Hq=2, Hkv=1, varlen=(4, 1, 400), seed=52)),
+]
+
+
+@pytest.mark.parametrize("name,wl", FP8PV, ids=[s[0] for s in FP8PV])
+def test_mxqk_fp8pv_small_shapes_all_outputs(gpu, name, wl):
+    _say(f"fwd FP8-P/V MX Q/K small {name}")
+    inp = synth.generate(wl, "cpu")
+    inp.q, inp.k, inp.v = inp.q.cuda(), inp.k.cuda(), inp.v.cuda()
+    o, lse, stats = _check(gpu, inp, qk="mxfp4")
+    assert stats, "probability dump not compared"
+
+
+def test_mxqk_bf16_output(gpu):
+    # bf16 O is the float32 O rounded to nearest even; LSE is the same
+    wl = synth.WORKLOADS[2].with_(Hq=2, Hkv=2, N=300, seed=25)
+    inp = synth.generate(wl, "cpu")
+    inp.q, inp.k, inp.v = inp.q.cuda(), inp.k.cuda(), inp.v.cuda()
+    o32, l32, _ = _gpu_run(gpu, inp, qk="mxfp4")
+    o16, l16, _ = _gpu_run(gpu, inp, qk="mxfp4", out_dtype=torch.bfloat16)
+    assert torch.equal(o32.to(torch.bfloat16), o16) and torch.equal(l32, l16)
+
+
 def test_mxqk_short_sequences(gpu):
     for n in (1, 2, 31, 33, 127, 129):
         _say(f"fwd MX Q/K N={n}")
@@ -109,7 +136,7 @@ def test_mxqk_determinism(gpu):
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-FULL = [(2, [0, 39], 32), (3, [0, 79], 32), (5, [0, 31], 24)]
+FULL = [(2, [0, 39], 32), (3, [0, 79], 32), (4, [0, 31], 32), (5, [0, 31], 24)]
 
 
 @pytest.mark.parametrize("k,heads,nrows", FULL, ids=[f"workload{f[0]}" for f in FULL])
