@@ -255,7 +255,18 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t sDO[2][BWD_CHUNK * DS];
   __shared__ __attribute__((aligned(16))) uint8_t sDOT[2][D * DTS];
   __shared__ float sL[2][BWD_CHUNK], sD[2][BWD_CHUNK];
-  const int kb = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  int kb = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  if (CAUSAL) {
+    // Causal: a key block's work falls with kb.  Dispatch (which follows the
+    // linear block index) takes the longest blocks of every head first, kb
+    // major; the (batch, KV head) index varies fastest, so with 8 KV heads
+    // each XCD (dispatch is round-robin over 8) keeps one KV head.
+    const int nh = gridDim.y * gridDim.z;
+    const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    kb = lin / nh;
+    hk = (lin % nh) % gridDim.y;
+    b = (lin % nh) / gridDim.y;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, ln = lane & 31;
   const int key = kb * BWD_ROWS + wave * 32 + ln;
   const int G = p.Hq / p.Hkv;
@@ -528,7 +539,20 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 sK[2][BWD_CHUNK * KSR];
   __shared__ __attribute__((aligned(16))) __bf16 sKT[2][D * KTS];
   __shared__ __attribute__((aligned(16))) uint8_t sV[2][BWD_CHUNK * VS];
-  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  if (CAUSAL) {
+    // Causal: a query block's work grows with qb.  Dispatch takes the longest
+    // blocks first, qb major from the last; within one qb the linear index r
+    // = g (B Hkv) + b Hkv + hk puts the query heads g of one KV head's group
+    // at the same residue mod 8, i.e. on one XCD, where they share its K / V.
+    const int nh = gridDim.y * gridDim.z, G = p.Hq / p.Hkv;
+    const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    qb = (int)gridDim.x - 1 - lin / nh;
+    const int r = lin % nh, per_g = (int)gridDim.z * p.Hkv;
+    const int g = r / per_g;
+    b = (r % per_g) / p.Hkv;
+    h = ((r % per_g) % p.Hkv) * G + g;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, ln = lane & 31;
   const int q = qb * BWD_ROWS + wave * 32 + ln;
   const int hk = h / (p.Hq / p.Hkv);
