@@ -141,6 +141,10 @@ __host__ __device__ constexpr int slot_unit_begin(int i) {
   return i < NPV ? 3 + (i * 10) / NPV : 13 + 8 * ((i - NPV) / KS) + (((i - NPV) % KS) * 8) / KS;
 }
 
+// Query blocks of one (sequence, head) dispatched to one XCD in a row in
+// packed variable-length launches (see the kernel's workgroup order).
+constexpr int VARLEN_QGROUP = 16;
+
 // Slot after which the second wave group of a workgroup takes its barrier
 // (the first group takes it after the last slot); see the key loop.
 #ifndef ATTN_G1_BARRIER
@@ -201,15 +205,30 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   // Packed variable-length batches: sequences differ in length, so grouping
   // them by XCD would leave XCDs unevenly loaded; there the order is query
   // block major, from the last block down (only long sequences have high
-  // blocks, and their workgroups are the longest-running), and consecutive
-  // workgroups spread over all XCDs.
+  // blocks, and their workgroups are the longest-running).  Within that
+  // order, VARLEN_QGROUP consecutive query blocks of one (sequence, head) go
+  // to the same XCD one after another, so the workgroups running together
+  // there stream the same K / V tiles through its L2; the (sequence, head)
+  // pairs are dealt to XCDs by pair index mod 8, which gives every XCD the
+  // same share of every sequence.  The grid is padded to whole groups
+  // (workgroups with qb < 0 exit).
   const int nwg = gridDim.x;
   int lin = blockIdx.x;
   int qb, h, b;
   if (p.cu_q != nullptr) {
-    qb = p.QB - 1 - lin / (p.B * p.Hq);
-    h = lin % p.Hq;
-    b = (lin / p.Hq) % p.B;
+    const int npairs = p.B * p.Hq;
+    if ((npairs & 7) == 0) {
+      const int j = lin >> 3, np8 = npairs >> 3;
+      const int t = j / VARLEN_QGROUP;
+      const int pair = (t % np8) * 8 + (lin & 7);
+      qb = p.QB - 1 - ((t / np8) * VARLEN_QGROUP + j % VARLEN_QGROUP);
+      h = pair % p.Hq;
+      b = pair / p.Hq;
+    } else {
+      qb = p.QB - 1 - lin / npairs;
+      h = lin % p.Hq;
+      b = (lin / p.Hq) % p.B;
+    }
   } else {
     if ((nwg & 7) == 0) lin = (lin & 7) * (nwg >> 3) + (lin >> 3);
     qb = lin % p.QB;
@@ -226,7 +245,7 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   const int64_t tk0 = varlen ? p.cu_k[b] : (int64_t)b * p.Nk;
   const int len_q = varlen ? p.cu_q[b + 1] - p.cu_q[b] : p.Nq;
   const int len_k = varlen ? p.cu_k[b + 1] - p.cu_k[b] : p.Nk;
-  if (qb * WG_Q >= len_q) return;
+  if (qb < 0 || qb * WG_Q >= len_q) return;
   const int hk = h / (p.Hq / p.Hkv);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -789,6 +808,13 @@ hipError_t launch_expand_k(const uint8_t* codes, const uint8_t* scales, int H, i
   return hipGetLastError();
 }
 
+// Workgroups of a forward launch (packed batches: padded to whole query-block
+// groups, see the kernel's workgroup order).
+static int fwd_grid(const FwdParams& p) {
+  const int qb = p.cu_q != nullptr ? (p.QB + VARLEN_QGROUP - 1) / VARLEN_QGROUP * VARLEN_QGROUP : p.QB;
+  return p.B * p.Hq * qb;
+}
+
 template <int D, int PF, int VF, bool CAUSAL, bool DEBUG, int ENC, int QK = 0>
 static hipError_t launch_fwd_t(const FwdParams& p, int nwg, hipStream_t st) {
   auto kern = fwd_lowp_kernel<D, PF, VF, CAUSAL, DEBUG, ENC, QK>;
@@ -824,7 +850,7 @@ static hipError_t launch_fwd_e(const FwdParams& p, int nwg, int D, int pf, int v
 
 hipError_t launch_fwd_lowp(const FwdParams& p, int D, int pf, int vf, bool causal, bool debug, int enc,
                            hipStream_t st) {
-  const int nwg = p.B * p.Hq * p.QB;
+  const int nwg = fwd_grid(p);
   if (nwg == 0) return hipSuccess;
   return enc ? launch_fwd_e<1>(p, nwg, D, pf, vf, causal, debug, st)
              : launch_fwd_e<0>(p, nwg, D, pf, vf, causal, debug, st);
@@ -849,7 +875,7 @@ hipError_t launch_pack_k_mx(const uint8_t* codes, const uint8_t* scales, int H, 
 }
 
 hipError_t launch_fwd_mx(const FwdParams& p, int D, int pf, int vf, bool causal, bool debug, hipStream_t st) {
-  const int nwg = p.B * p.Hq * p.QB;
+  const int nwg = fwd_grid(p);
   if (nwg == 0) return hipSuccess;
 #define MXL(DD, PP, VV, CC)                                                     \
   (debug ? launch_fwd_t<DD, PP, VV, CC, true, 0, 1>(p, nwg, st)                  \
