@@ -211,7 +211,33 @@ def dequant_v_mxfp4(codes, e8m0):
     return e2m1_decode(codes) * s
 
 
-def quant_mxfp4(x):
+def hadamard32(x):
+    """Unnormalized 32-point Walsh-Hadamard transform of each block of 32
+    consecutive elements along the last axis, in float32: the block rotation
+    read from "Bridging the Gap Between Promise and Performance for
+    Microscaling FP4 Quantization" (listed beside the arXiv entry of the
+    pages' paper; abstract only: rotations within microscaling blocks before
+    FP4 quantization).  H is the Sylvester matrix (entries +-1, H H^T = 32 I),
+    so rotating both Q and K multiplies every Q.K by exactly 32.
+
+    Fixed float32 order: stages of stride 1, 2, 4, 8, 16; in each, the pair
+    (i, i + s) with bit s of i clear becomes (x_i + x_{i+s}, x_i - x_{i+s}).
+    """
+    x = np.asarray(x, dtype=F32)
+    D = x.shape[-1]
+    assert D % MX_BLOCK == 0
+    y = x.reshape(x.shape[:-1] + (D // MX_BLOCK, MX_BLOCK)).copy()
+    s = 1
+    while s < MX_BLOCK:
+        idx = np.array([i for i in range(MX_BLOCK) if not i & s])
+        a, b = y[..., idx], y[..., idx + s]
+        y[..., idx] = a + b                     # float32 + float32 -> float32, RNE
+        y[..., idx + s] = a - b
+        s *= 2
+    return y.reshape(x.shape)
+
+
+def quant_mxfp4(x, hadamard=False):
     """MXFP4 quantization along the last axis (D, a multiple of 32): the
     MX-native Q/K format, an opt-in alternative to NVFP4 whose blocks the
     gfx950 scaled matrix instruction can apply directly.
@@ -223,10 +249,16 @@ def quant_mxfp4(x):
     e = clamp(floor(log2 amax) - 2, -127, 127) (-127 for an all-zero block)
     and code = E2M1(x * 2**-e).  No tensor scale.
 
+    With ``hadamard``, each 32-element block is first rotated by
+    :func:`hadamard32` (float32), and the quantized values are those of the
+    rotated rows.
+
     Returns (codes uint8 [..., D/2], element 2k in the low nibble of byte k;
     e8m0 uint8 [..., D/32]).
     """
     x = np.asarray(x, dtype=F32)
+    if hadamard:
+        x = hadamard32(x)
     D = x.shape[-1]
     assert D % MX_BLOCK == 0
     xb = x.reshape(x.shape[:-1] + (D // MX_BLOCK, MX_BLOCK)).astype(np.float64)

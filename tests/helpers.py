@@ -57,11 +57,16 @@ def oracle_head(q_rows, k_rows, v_rows, *, amax_q, amax_k, amax_v, sigma, p_form
     """Oracle forward for a set of query rows of one head, given the bf16
     inputs (as float32 numpy) and the whole-tensor amax values.  ``qk="mxfp4"``
     quantizes Q and K with the MX-native rule (E8M0 per 32 along D, no tensor
-    scales) instead of NVFP4."""
+    scales) instead of NVFP4; ``qk="mxfp4_had"`` rotates each 32-element block
+    by the Hadamard matrix first."""
     vh = oracle_v_head(v_rows, v_format, amax_v)
-    if qk == "mxfp4":
-        qc, qe = OQ.quant_mxfp4(q_rows)
-        kc, ke = OQ.quant_mxfp4(k_rows)
+    if qk in ("mxfp4", "mxfp4_had"):
+        # with the block Hadamard rotation of Q and K, every Q.K is 32 times the
+        # original, so the forward runs with sigma / 32
+        had = qk == "mxfp4_had"
+        qc, qe = OQ.quant_mxfp4(q_rows, hadamard=had)
+        kc, ke = OQ.quant_mxfp4(k_rows, hadamard=had)
+        sigma = sigma / 32.0 if had else sigma
         return OA.attn_lowp_head(OQ.dequant_mxfp4(qc, qe), OQ.dequant_mxfp4(kc, ke), 1.0, 1.0, vh, sigma,
                                  p_format, causal, q_index=q_index, return_p=return_p, encoder=encoder,
                                  p_given=p_given, return_pre=return_pre)

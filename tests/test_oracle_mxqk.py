@@ -106,3 +106,46 @@ def test_mxfp4_degenerate_blocks():
     assert e8[2].tolist() == [0, 127]
     assert cu[2, 40] == 15 and cu[2].sum() == 15
     assert Q.dequant_mxfp4(codes, e8)[2, 40] == -6.0
+
+
+def _sylvester(n):
+    h = np.array([[1.0]])
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def test_hadamard32_is_the_sylvester_matrix():
+    # small integers: every float32 sum is exact, so the butterfly must equal
+    # the matrix product with the Sylvester Hadamard matrix built by Kronecker
+    # products, block by block
+    rng = np.random.default_rng(3)
+    x = rng.integers(-50, 50, (5, 64)).astype(np.float32)
+    H = _sylvester(32)
+    want = np.concatenate([x[:, :32].astype(np.float64) @ H.T, x[:, 32:].astype(np.float64) @ H.T], axis=1)
+    assert np.array_equal(Q.hadamard32(x).astype(np.float64), want)
+    assert np.array_equal(H @ H.T, 32 * np.eye(32))
+
+
+def test_hadamard32_orthogonality_and_dot_products():
+    rng = np.random.default_rng(4)
+    q = rng.integers(-20, 20, (3, 128)).astype(np.float32)
+    k = rng.integers(-20, 20, (4, 128)).astype(np.float32)
+    # applying it twice gives 32 x; rotated dot products are 32 times the originals (exact here)
+    assert np.array_equal(Q.hadamard32(Q.hadamard32(q)), 32 * q)
+    assert np.array_equal(Q.hadamard32(q).astype(np.float64) @ Q.hadamard32(k).astype(np.float64).T,
+                          32 * (q.astype(np.float64) @ k.astype(np.float64).T))
+
+
+def test_hadamard32_spreads_an_outlier_channel():
+    # a lone channel of 8 becomes +-8 in every element of its block (row j of H),
+    # and the MX exponent of the rotated block follows
+    x = np.zeros((1, 64), np.float32)
+    x[0, 37] = 8.0
+    y = Q.hadamard32(x)
+    H = _sylvester(32)
+    assert np.array_equal(y[0, :32], np.zeros(32, np.float32))
+    assert np.array_equal(y[0, 32:], (8.0 * H[:, 5]).astype(np.float32))
+    codes, e8 = Q.quant_mxfp4(x, hadamard=True)
+    assert e8.tolist() == [[0, 128]]         # block 1: amax 8 -> e = 3 - 2 = 1
+    assert np.array_equal(Q.dequant_mxfp4(codes, e8)[0, 32:], y[0, 32:].astype(np.float64))
