@@ -38,10 +38,11 @@ def parse():
                     help="probability encoder: exact (RNE of 2^y) or the exp-free log-linear cast")
     ap.add_argument("--four-six", action="store_true",
                     help="quantize Q and K with the Four Over Six adaptive block scale (attn_quant_nvfp4_46)")
-    ap.add_argument("--qk", choices=("nvfp4", "mxfp4"), default="nvfp4",
+    ap.add_argument("--qk", choices=("nvfp4", "mxfp4", "mxfp4_had"), default="nvfp4",
                     help="Q/K format: nvfp4 (the method's; Q.K^T on the FP16 MFMA, exact) or the opt-in "
                          "MX-native mxfp4 (E8M0 per 32 along D; Q.K^T on the scaled FP4 MFMA, "
-                         "attn_fwd_directp_mxqk / attn_fwd_fp8pv_mxqk)")
+                         "attn_fwd_directp_mxqk / attn_fwd_fp8pv_mxqk); mxfp4_had rotates each 32-element block "
+                         "of Q and K by the Hadamard matrix first (attn_quant_mxfp4_had, softmax scale / 32)")
     ap.add_argument("--backward", action="store_true",
                     help="time the causal-training backward (attn_bwd_fp8) instead of the forward; its own JSON line")
     ap.add_argument("--decode", action="store_true",
@@ -130,10 +131,13 @@ def cpu_baseline(inp, rows, encoder="exact", four_six=False, qk="nvfp4"):
     kf = kh.float().cpu().numpy()
     vf = vh.float().cpu().numpy()
     t = time.perf_counter()
-    if qk == "mxfp4":
-        qc, qe = OQ.quant_mxfp4(qf)
-        kc, ke = OQ.quant_mxfp4(kf)
+    sigma = inp.sigma
+    if qk in ("mxfp4", "mxfp4_had"):
+        had = qk == "mxfp4_had"
+        qc, qe = OQ.quant_mxfp4(qf, hadamard=had)
+        kc, ke = OQ.quant_mxfp4(kf, hadamard=had)
         q_raw, k_raw, gq, gk = OQ.dequant_mxfp4(qc, qe), OQ.dequant_mxfp4(kc, ke), 1.0, 1.0
+        sigma = sigma / 32.0 if had else sigma
     else:
         qfn = OQ.quant_nvfp4_46 if four_six else OQ.quant_nvfp4
         qc, qs, gq = qfn(qf)
@@ -145,7 +149,7 @@ def cpu_baseline(inp, rows, encoder="exact", four_six=False, qk="nvfp4"):
     else:
         vcodes, ve = OQ.quant_v_mxfp4(vf[:, None, :])
         vhat = OQ.dequant_v_mxfp4(vcodes, ve)[:, 0, :]
-    OA.attn_lowp_head(q_raw, k_raw, gq, gk, vhat, inp.sigma, wl.p_format, wl.causal, q_index=idx, encoder=encoder)
+    OA.attn_lowp_head(q_raw, k_raw, gq, gk, vhat, sigma, wl.p_format, wl.causal, q_index=idx, encoder=encoder)
     dt = time.perf_counter() - t
     live = sum(min(int(i) + 1, Nk) for i in idx) if wl.causal else R * Nk
     flops = 4.0 * live * wl.D
@@ -495,7 +499,8 @@ def main():
         backward_main(args, torch, paf, synth)
         return
     wl = synth.WORKLOADS[args.workload]
-    mxqk = args.qk == "mxfp4"
+    mxqk = args.qk in ("mxfp4", "mxfp4_had")
+    had = args.qk == "mxfp4_had"
     if mxqk and (args.encoder != "exact" or args.four_six):
         print("--qk mxfp4 takes the exact encoder and no Four Over Six", file=sys.stderr)
         sys.exit(2)
@@ -509,7 +514,9 @@ def main():
                                                                                           args.encoder)]
     if mxqk:
         fwd = paf.fwd_directp_mxqk if wl.p_format == "mxfp4" else paf.fwd_fp8pv_mxqk
-    kw = dict(Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D, softmax_scale=inp.sigma, causal=wl.causal, out_dtype=torch.bfloat16)
+    # (Q and K rotated alike by the 32-point Hadamard matrix: every Q.K is 32 times the original)
+    kw = dict(Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D, softmax_scale=inp.sigma / 32.0 if had else inp.sigma, causal=wl.causal,
+              out_dtype=torch.bfloat16)
     if varlen:
         cu = inp.cu_seqlens.to(dev)
         mx = int(inp.seqlens.max())
@@ -522,7 +529,7 @@ def main():
 
     def quantize():
         if mxqk:
-            q, k = paf.quant_mxfp4(inp.q), paf.quant_mxfp4(inp.k)
+            q, k = paf.quant_mxfp4(inp.q, hadamard=had), paf.quant_mxfp4(inp.k, hadamard=had)
         else:
             q = paf.quant_nvfp4(inp.q, four_six=args.four_six)
             k = paf.quant_nvfp4(inp.k, four_six=args.four_six)
@@ -605,7 +612,8 @@ def main():
            f"P={wl.p_format.upper()} V={wl.v_format.upper()}" +
            ("" if args.encoder == "exact" else ", exp-free log-linear P encoder") +
            (", Four Over Six Q/K block scales" if args.four_six else "") +
-           (", MX-native MXFP4 Q/K (opt-in)" if mxqk else ""),
+           (", MX-native MXFP4 Q/K (opt-in)" if mxqk else "") +
+           (" after a 32-point block Hadamard rotation" if had else ""),
            "encoder": args.encoder, "four_six": args.four_six, "qk": args.qk,
            "B": wl.B if not varlen else int(len(inp.seqlens)), "Hq": wl.Hq, "Hkv": wl.Hkv,
            "N": wl.N if not varlen else int(inp.seqlens.max()), "D": wl.D, "causal": wl.causal,
@@ -625,7 +633,9 @@ def main():
         "x_bf16": None if bf16 is None else round(fwd_tflops / bf16["tflops"], 3),
         "x_bf16_incl_quantize": None if bf16 is None else round(value / bf16["tflops"], 3),
         "bf16_tflops": None if bf16 is None else round(bf16["tflops"], 2),
-        "precision": ("MX-native MXFP4 Q/K (E8M0 per 32 along D; contracted on the scaled FP4 MFMA), " if mxqk else
+        "precision": (("MX-native MXFP4 Q/K (E8M0 per 32 along D" +
+                       ("; 32-point block Hadamard rotation first" if had else "") +
+                       "; contracted on the scaled FP4 MFMA), ") if mxqk else
                       "NVFP4 Q/K (exact, contracted on the FP16 MFMA), ") +
                      ("MXFP4 E2M1 P (Direct-P)" if wl.p_format == "mxfp4" else "FP8 E4M3 P") +
                      ("" if args.encoder == "exact" else " by the exp-free log-linear cast") +

@@ -136,6 +136,23 @@ attn_status attn_quant_mxfp4(const void* x_bf16, int64_t rows, int32_t D,
                              uint8_t* codes, uint8_t* scales, void* stream);
 
 /*
+ * attn_quant_mxfp4 after a block rotation: each 32-element block of a row is
+ * multiplied by the unnormalized 32-point Hadamard (Sylvester) matrix H
+ * (entries +-1, H H^T = 32 I) before the MX rule above.  This is the
+ * micro-rotation of "Bridging the Gap Between Promise and Performance for
+ * Microscaling FP4 Quantization" (listed beside the pages' arXiv entry,
+ * 2609.04105v1): it spreads an outlier channel over its block.  Every step
+ * is a float32 operation in a fixed order: butterfly stages of stride 1, 2,
+ * 4, 8, 16, where the pair (i, i + s) becomes (x_i + x_{i+s}, x_i - x_{i+s}).
+ * Rotating Q and K alike multiplies every Q.K by 32, so the forward on the
+ * result takes softmax_scale = sigma / 32.  Arguments, output format and
+ * errors as for attn_quant_mxfp4.  Inputs whose rotated values overflow
+ * float32 (|x| above about 1e37) give undefined codes.
+ */
+attn_status attn_quant_mxfp4_had(const void* x_bf16, int64_t rows, int32_t D,
+                                 uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
  * Number of key columns of the transposed V layout used by attn_quant_v and
  * the forward.  Sequence s starts at column
  *     dense : s * roundup(Nk, 128)

@@ -96,6 +96,8 @@ EXPORTS = {
                                         ctypes.c_void_p]),
     "attn_quant_mxfp4": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_void_p]),
+    "attn_quant_mxfp4_had": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p]),
     "attn_v_cols": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]),
     "attn_quant_v": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
@@ -178,11 +180,13 @@ def quant_nvfp4(x, four_six=False):
     return codes, scales, ts
 
 
-def quant_mxfp4(x):
+def quant_mxfp4(x, hadamard=False):
     """MXFP4-quantize a bf16 tensor along its last axis (D, a multiple of 32),
     the MX-native Q/K format of fwd_directp_mxqk.  Returns (codes uint8
     [..., D/2], E8M0 scales uint8 [..., D/32], None) -- the None stands where
-    the NVFP4 tuples carry their tensor scale."""
+    the NVFP4 tuples carry their tensor scale.  ``hadamard`` rotates each
+    32-element block by the 32-point Hadamard matrix first
+    (attn_quant_mxfp4_had); Q and K rotated alike need softmax_scale / 32."""
     lib = load_library()
     _need_cuda(x)
     if x.dtype != torch.bfloat16:
@@ -191,7 +195,8 @@ def quant_mxfp4(x):
     rows = x.numel() // D if D else 0
     codes = torch.empty(x.shape[:-1] + (D // 2,), dtype=torch.uint8, device=x.device)
     scales = torch.empty(x.shape[:-1] + (D // 32,), dtype=torch.uint8, device=x.device)
-    _check(lib.attn_quant_mxfp4(_ptr(x), rows, D, _ptr(codes), _ptr(scales), _stream()))
+    fn = lib.attn_quant_mxfp4_had if hadamard else lib.attn_quant_mxfp4
+    _check(fn(_ptr(x), rows, D, _ptr(codes), _ptr(scales), _stream()))
     return codes, scales, None
 
 

@@ -19,7 +19,8 @@ hipError_t launch_quant_v(const void* v, int B, int Nk, int Hkv, int D, const in
 hipError_t launch_expand_k(const uint8_t* codes, const uint8_t* scales, int H, int B, int N, int max_len,
                            const int32_t* cu, int64_t n_pad, int64_t cols, int D, int pf, _Float16* out,
                            hipStream_t st);
-hipError_t launch_quant_mxfp4(const void* x, int64_t rows, int D, uint8_t* codes, uint8_t* scales, hipStream_t st);
+hipError_t launch_quant_mxfp4(const void* x, int64_t rows, int D, uint8_t* codes, uint8_t* scales, bool hadamard,
+                              hipStream_t st);
 hipError_t launch_pack_k_mx(const uint8_t* codes, const uint8_t* scales, int H, int B, int N, int max_len,
                             const int32_t* cu, int64_t n_pad, int64_t cols, int D, int pf, uint8_t* out,
                             hipStream_t st);
@@ -100,13 +101,23 @@ attn_status attn_quant_nvfp4_46(const void* x_bf16, int64_t rows, int32_t D, uin
   return run_quant_nvfp4(x_bf16, rows, D, codes, scales, tensor_scale, ws, ws_bytes, stream, true);
 }
 
-attn_status attn_quant_mxfp4(const void* x_bf16, int64_t rows, int32_t D, uint8_t* codes, uint8_t* scales,
-                             void* stream) {
+static attn_status run_quant_mxfp4(const void* x_bf16, int64_t rows, int32_t D, uint8_t* codes, uint8_t* scales,
+                                   bool hadamard, void* stream) {
   if (rows < 0 || D <= 0 || D % 32 != 0) return ATTN_ERR_INVALID_ARGUMENT;
   if (rows > 0 && (x_bf16 == nullptr || codes == nullptr || scales == nullptr || !aligned(x_bf16, 16) ||
                    !aligned(codes, 16)))
     return ATTN_ERR_INVALID_ARGUMENT;
-  return hip_status(launch_quant_mxfp4(x_bf16, rows, D, codes, scales, (hipStream_t)stream));
+  return hip_status(launch_quant_mxfp4(x_bf16, rows, D, codes, scales, hadamard, (hipStream_t)stream));
+}
+
+attn_status attn_quant_mxfp4(const void* x_bf16, int64_t rows, int32_t D, uint8_t* codes, uint8_t* scales,
+                             void* stream) {
+  return run_quant_mxfp4(x_bf16, rows, D, codes, scales, false, stream);
+}
+
+attn_status attn_quant_mxfp4_had(const void* x_bf16, int64_t rows, int32_t D, uint8_t* codes, uint8_t* scales,
+                                 void* stream) {
+  return run_quant_mxfp4(x_bf16, rows, D, codes, scales, true, stream);
 }
 
 int64_t attn_v_cols(int32_t B, int32_t Nk, int64_t total_k, int32_t varlen) {

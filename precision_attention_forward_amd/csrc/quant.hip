@@ -271,6 +271,15 @@ __global__ void __launch_bounds__(256) quant_v_kernel(const uint16_t* __restrict
 // zero or subnormal block max, below the E8M0 range), codes E2M1(x * 2^-e)
 // by the hardware RNE conversion (x * 2^-e is exact), element 2k in the low
 // nibble of byte k.  No tensor scale and no amax pass: one read of the input.
+//
+// HAD: each block is first rotated by the unnormalized 32-point Hadamard
+// (Sylvester) matrix, the micro-rotation of "Bridging the Gap Between Promise
+// and Performance for Microscaling FP4 Quantization" (listed beside the
+// pages' arXiv entry), in float32 butterfly stages of stride 1, 2, 4 (inside
+// a lane's eight elements) and 8, 16 (with lanes ^1, ^2): the pair (i, i + s)
+// becomes (x_i + x_{i+s}, x_i - x_{i+s}).  Rotating Q and K alike multiplies
+// every Q.K by 32.
+template <bool HAD>
 __global__ void __launch_bounds__(256) quant_mxfp4_kernel(const uint16_t* __restrict__ x, int64_t nblocks,
                                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
   const int64_t nparts = nblocks * 4;            // 8-element parts; a block's four parts share a lane group
@@ -283,6 +292,26 @@ __global__ void __launch_bounds__(256) quant_mxfp4_kernel(const uint16_t* __rest
     for (int j = 0; j < 4; ++j) {
       f[2 * j] = bf16_bits_to_f32(w[j] & 0xFFFFu);
       f[2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
+    }
+    if (HAD) {
+#pragma unroll
+      for (int st = 1; st < 8; st *= 2)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (!(j & st)) {
+            const float a = f[j], c = f[j + st];
+            f[j] = a + c;
+            f[j + st] = a - c;
+          }
+#pragma unroll
+      for (int lm = 1; lm < 4; lm *= 2) {          // strides 8 and 16: lanes lm apart in the group
+        const bool upper = (i & lm) != 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float other = __shfl_xor(f[j], lm, 64);
+          f[j] = upper ? other - f[j] : f[j] + other;
+        }
+      }
     }
     float amax = 0.0f;
 #pragma unroll
@@ -343,12 +372,18 @@ hipError_t launch_quant_v(const void* v, int B, int Nk, int Hkv, int D, const in
   return hipGetLastError();
 }
 
-hipError_t launch_quant_mxfp4(const void* x, int64_t rows, int D, uint8_t* codes, uint8_t* scales, hipStream_t st) {
+hipError_t launch_quant_mxfp4(const void* x, int64_t rows, int D, uint8_t* codes, uint8_t* scales, bool hadamard,
+                              hipStream_t st) {
   const int64_t nblocks = rows * (D / 32);
   if (nblocks == 0) return hipSuccess;
   const int64_t want = (nblocks * 4 + 255) / 256;
   const int grid = (int)(want > 16384 ? 16384 : want);
-  hipLaunchKernelGGL(quant_mxfp4_kernel, dim3(grid), dim3(256), 0, st, (const uint16_t*)x, nblocks, codes, scales);
+  if (hadamard)
+    hipLaunchKernelGGL(quant_mxfp4_kernel<true>, dim3(grid), dim3(256), 0, st, (const uint16_t*)x, nblocks, codes,
+                       scales);
+  else
+    hipLaunchKernelGGL(quant_mxfp4_kernel<false>, dim3(grid), dim3(256), 0, st, (const uint16_t*)x, nblocks, codes,
+                       scales);
   return hipGetLastError();
 }
 

@@ -31,13 +31,16 @@ ENTRY = {("mxfp4", "exact"): "fwd_directp", ("fp8", "exact"): "fwd_fp8pv",
 
 def _gpu_run(gpu, inp, debug=None, out_dtype=torch.float32, encoder="exact", four_six=False, qk="nvfp4"):
     wl = inp.wl
-    if qk == "mxfp4":
-        q, k = gpu.quant_mxfp4(inp.q), gpu.quant_mxfp4(inp.k)
+    sigma = inp.sigma
+    if qk in ("mxfp4", "mxfp4_had"):
+        had = qk == "mxfp4_had"
+        q, k = gpu.quant_mxfp4(inp.q, hadamard=had), gpu.quant_mxfp4(inp.k, hadamard=had)
+        sigma = sigma / 32.0 if had else sigma      # rotated Q.K is 32 times the original
     else:
         q = gpu.quant_nvfp4(inp.q, four_six=four_six)
         k = gpu.quant_nvfp4(inp.k, four_six=four_six)
     vf = gpu.V_FP8 if wl.v_format == "fp8" else gpu.V_MXFP4
-    kw = dict(Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D, softmax_scale=inp.sigma, causal=wl.causal, out_dtype=out_dtype,
+    kw = dict(Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D, softmax_scale=sigma, causal=wl.causal, out_dtype=out_dtype,
               debug=debug)
     if inp.cu_seqlens is None:
         vq = gpu.quant_v(inp.v, vf)
@@ -48,7 +51,7 @@ def _gpu_run(gpu, inp, debug=None, out_dtype=torch.float32, encoder="exact", fou
         vq = gpu.quant_v(inp.v, vf, cu_seqlens=cu, max_seqlen=mx)
         kw.update(cu_seqlens_q=cu, cu_seqlens_k=cu, max_seqlen_q=mx, max_seqlen_k=mx)
     v = (vf, vq[0], vq[1], vq[2])
-    fn = getattr(gpu, ENTRY[(wl.p_format, encoder)] + ("_mxqk" if qk == "mxfp4" else ""))
+    fn = getattr(gpu, ENTRY[(wl.p_format, encoder)] + ("_mxqk" if qk.startswith("mxfp4") else ""))
     o, lse, dbg = fn(q, k, v, **kw)
     torch.cuda.synchronize()
     return o, lse, dbg

@@ -1,5 +1,6 @@
-"""GPU MX-native Q/K mode (opt-in; attn_quant_mxfp4 + attn_fwd_directp_mxqk)
-against the oracle on the same seeded inputs.
+"""GPU MX-native Q/K mode (opt-in; attn_quant_mxfp4[_had] + attn_fwd_directp_mxqk
+/ attn_fwd_fp8pv_mxqk) against the oracle on the same seeded inputs, without
+and with the block Hadamard rotation of Q and K.
 
 Bar: MXFP4 Q/K codes and E8M0 bytes bit-exact; the forward to the bar of the
 NVFP4 Direct-P path (probability codes differ from the oracle's in at most
@@ -54,17 +55,27 @@ def test_quant_mxfp4_bit_exact(gpu, name, x):
     assert np.array_equal(scales.cpu().numpy(), re_)
 
 
+@pytest.mark.parametrize("name,x", _quant_inputs(), ids=[c[0] for c in _quant_inputs()])
+def test_quant_mxfp4_hadamard_bit_exact(gpu, name, x):
+    _say(f"quant_mxfp4 hadamard {name}")
+    codes, scales, _ = gpu.quant_mxfp4(x.cuda(), hadamard=True)
+    torch.cuda.synchronize()
+    rc, re_ = OQ.quant_mxfp4(x.float().numpy(), hadamard=True)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(scales.cpu().numpy(), re_)
+
+
 def test_quant_mxfp4_full_size_sampled(gpu):
     wl = synth.WORKLOADS[2]
     _say("quant_mxfp4 full-size Wan Q")
     inp = synth.generate(wl, "cuda")
-    codes, scales, _ = gpu.quant_mxfp4(inp.q)
-    torch.cuda.synchronize()
     rows = np.random.default_rng(2).integers(0, wl.N, 512)
-    for t in (inp.q, ):
-        sel = torch.as_tensor(rows, device=t.device)
-        x = t[0, sel].float().cpu().numpy()                     # [rows, H, D]
-        rc, re_ = OQ.quant_mxfp4(x)
+    for had in (False, True):
+        codes, scales, _ = gpu.quant_mxfp4(inp.q, hadamard=had)
+        torch.cuda.synchronize()
+        sel = torch.as_tensor(rows, device=inp.q.device)
+        x = inp.q[0, sel].float().cpu().numpy()                 # [rows, H, D]
+        rc, re_ = OQ.quant_mxfp4(x, hadamard=had)
         assert np.array_equal(codes[0, sel].cpu().numpy(), rc)
         assert np.array_equal(scales[0, sel].cpu().numpy(), re_)
     del inp
@@ -108,6 +119,23 @@ def test_mxqk_fp8pv_small_shapes_all_outputs(gpu, name, wl):
     assert stats, "probability dump not compared"
 
 
+HAD = [
+    ("wan_recipe_small_mxfp4v", synth.WORKLOADS[2].with_(Hq=2, Hkv=2, N=1000, seed=21)),
+    ("wan_d64_small_fp8v", synth.WORKLOADS[3].with_(Hq=3, Hkv=3, N=700, seed=31)),
+    ("llama_causal_small", synth.WORKLOADS[4].with_(B=2, Hq=4, Hkv=2, N=600, seed=41)),
+    ("varlen_small", synth.WORKLOADS[5].with_(Hq=2, Hkv=2, varlen=(5, 1, 700), seed=51)),
+]
+
+
+@pytest.mark.parametrize("name,wl", HAD, ids=[s[0] for s in HAD])
+def test_mxqk_hadamard_small_shapes_all_outputs(gpu, name, wl):
+    _say(f"fwd MX Q/K with block Hadamard, small {name}")
+    inp = synth.generate(wl, "cpu")
+    inp.q, inp.k, inp.v = inp.q.cuda(), inp.k.cuda(), inp.v.cuda()
+    o, lse, stats = _check(gpu, inp, qk="mxfp4_had")
+    assert stats, "probability dump not compared"
+
+
 def test_mxqk_bf16_output(gpu):
     # bf16 O is the float32 O rounded to nearest even; LSE is the same
     wl = synth.WORKLOADS[2].with_(Hq=2, Hkv=2, N=300, seed=25)
@@ -136,13 +164,14 @@ def test_mxqk_determinism(gpu):
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-FULL = [(2, [0, 39], 32), (3, [0, 79], 32), (4, [0, 31], 32), (5, [0, 31], 24)]
+FULL = [(2, [0, 39], 32, "mxfp4"), (3, [0, 79], 32, "mxfp4"), (4, [0, 31], 32, "mxfp4"), (5, [0, 31], 24, "mxfp4"),
+        (2, [0, 39], 24, "mxfp4_had"), (4, [0, 31], 24, "mxfp4_had")]
 
 
-@pytest.mark.parametrize("k,heads,nrows", FULL, ids=[f"workload{f[0]}" for f in FULL])
-def test_mxqk_full_size_sampled(gpu, k, heads, nrows):
+@pytest.mark.parametrize("k,heads,nrows,qk", FULL, ids=[f"workload{f[0]}_{f[3]}" for f in FULL])
+def test_mxqk_full_size_sampled(gpu, k, heads, nrows, qk):
     wl = synth.WORKLOADS[k]
-    _say(f"fwd MX Q/K full-size {wl.name}")
+    _say(f"fwd MX Q/K ({qk}) full-size {wl.name}")
     inp = synth.generate(wl, "cuda")
     if inp.cu_seqlens is None:
         L = wl.N
@@ -152,7 +181,7 @@ def test_mxqk_full_size_sampled(gpu, k, heads, nrows):
         L = int(inp.seqlens.max())
     rng = np.random.default_rng(100 + k)
     rows = np.unique(np.concatenate([rng.integers(0, L, nrows), [0, 1, 255, 256, L - 1]]))
-    o, lse, stats = _check(gpu, inp, heads=heads, seqs=seqs, rows=rows, qk="mxfp4")
+    o, lse, stats = _check(gpu, inp, heads=heads, seqs=seqs, rows=rows, qk=qk)
     assert stats
     del inp
     torch.cuda.empty_cache()
