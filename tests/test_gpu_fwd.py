@@ -180,9 +180,12 @@ def test_edge_single_key_and_short(gpu):
             assert torch.equal(o[0, :1].expand_as(o[0]), o[0])
 
 
-def test_varlen_with_empty_sequences(gpu):
+@pytest.mark.parametrize("qk", ["nvfp4", "mxfp4", "mxfp4_had"])
+def test_varlen_with_empty_sequences(gpu, qk):
     # packed batch whose second and fourth sequences are empty: their
     # workgroups must write nothing and the neighbours must be unaffected
+    # (4 sequences x 2 heads: the launch order that groups query blocks of
+    # one (sequence, head) per XCD, with its padding workgroups)
     wl = synth.WORKLOADS[5].with_(Hq=2, Hkv=1, varlen=(4, 0, 300), seed=53)
     lens = torch.tensor([257, 0, 130, 0], dtype=torch.int32)
     T = int(lens.sum())
@@ -193,21 +196,22 @@ def test_varlen_with_empty_sequences(gpu):
     cu = torch.zeros(5, dtype=torch.int32)
     cu[1:] = torch.cumsum(lens, 0)
     inp = synth.Inputs(wl, q, k, v, lens, cu, None)
-    _say("varlen lengths [257, 0, 130, 0]")
-    _check(gpu, inp)
+    _say(f"varlen lengths [257, 0, 130, 0], Q/K {qk}")
+    _check(gpu, inp, qk=qk)
 
 
-def test_edge_zero_queries_closed_form(gpu):
+@pytest.mark.parametrize("qk", ["nvfp4", "mxfp4", "mxfp4_had"])
+def test_edge_zero_queries_closed_form(gpu, qk):
     # Q = 0: every probability code is 4.0 with e = -2 (p = 1), so O is the mean
     # of the dequantized V rows and LSE = ln(Nk).
-    _say("fwd Q=0 closed form")
+    _say(f"fwd Q=0 closed form, Q/K {qk}")
     wl = synth.WORKLOADS[1].with_(N=300, seed=7)
     inp = synth.generate(wl, "cpu")
     inp.q = torch.zeros_like(inp.q)
     inp.q, inp.k, inp.v = inp.q.cuda(), inp.k.cuda(), inp.v.cuda()
-    o, lse, _ = _gpu_run(gpu, inp)
+    o, lse, _ = _gpu_run(gpu, inp, qk=qk)
     np.testing.assert_allclose(f32(lse), math.log(300), rtol=1e-6)
-    o, lse, _ = _check(gpu, inp, dumps=False)
+    o, lse, _ = _check(gpu, inp, dumps=False, qk=qk)
 
 
 def test_bf16_output_mode(gpu):
