@@ -254,7 +254,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 sQT[2][D * QTS];
   __shared__ __attribute__((aligned(16))) uint8_t sDO[2][BWD_CHUNK * DS];
   __shared__ __attribute__((aligned(16))) uint8_t sDOT[2][D * DTS];
-  __shared__ float sL[2][BWD_CHUNK], sD[2][BWD_CHUNK];
+  __shared__ __attribute__((aligned(16))) float sL[2][BWD_CHUNK];   // read as 16-byte vectors
+  __shared__ __attribute__((aligned(16))) float sD[2][BWD_CHUNK];
   int kb = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   if (CAUSAL) {
     // Causal: a key block's work falls with kb.  Dispatch (which follows the
@@ -379,23 +380,45 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
     fetch(step + 1 < total ? step + 1 : step);
     {
       f32x16 s[2], dp[2];
+      // S of both 32-query sub-tiles: the two accumulation chains alternate,
+      // and each A operand is read from LDS two matrix instructions ahead
+      // (fenced), so that no read's latency is waited out right before its
+      // use; each chain still sums its k-steps in order
+      {
+        const __bf16* qa = &sQ[buf][(16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3)) * QS + 8 * hh];
+        auto lda = [&](int i) {    // operand i: k-step i / 2 of sub-tile i % 2
+          return *reinterpret_cast<const bf16x8*>(qa + 32 * (i & 1) * QS + 16 * (i >> 1));
+        };
+        bf16x8 op[3];
+        op[0] = lda(0);
+        op[1] = lda(1);
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int qrow = 32 * s2 + 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
-        s[s2] = f32x16{};
-#pragma unroll
-        for (int st = 0; st < KS; ++st) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sQ[buf][qrow * QS + 16 * st + 8 * hh]);
-          s[s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kreg[st], s[s2], 0, 0, 0);
+        for (int i = 0; i < 2 * KS; ++i) {
+          if (i + 2 < 2 * KS) op[(i + 2) % 3] = lda(i + 2);
+          const int st = i >> 1, s2 = i & 1;
+          s[s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], kreg[st], st == 0 ? f32x16{} : s[s2], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        dp[s2] = f32x16{};
+      }
+      // dP likewise: the two sub-tiles' chains alternate, operands one ahead
+      {
+        const uint8_t* da = &sDO[buf][(16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3)) * DS + 16 * hh];
+        auto ldd = [&](int i) {    // operand i: k-step i / 2 of sub-tile i % 2 (two 16-byte halves)
+          const uint8_t* r = da + 32 * (i & 1) * DS + 64 * (i >> 1);
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(r);
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(r + 32);
+          return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        };
+        i32x8 op[2];
+        op[0] = ldd(0);
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const u32x4 lo = *reinterpret_cast<const u32x4*>(&sDO[buf][qrow * DS + 64 * kk + 16 * hh]);
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(&sDO[buf][qrow * DS + 64 * kk + 32 + 16 * hh]);
-          const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        for (int i = 0; i < 2 * KK; ++i) {
+          if (i + 1 < 2 * KK) op[(i + 1) & 1] = ldd(i + 1);
+          const int kk = i >> 1, s2 = i & 1;
           // A: dO^ codes (E5M2, format 1), B: V codes (E4M3, format 0), unit scales
-          dp[s2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, vreg[kk], dp[s2], 1, 0, 0, 127, 0, 127);
+          dp[s2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op[i & 1], vreg[kk], kk == 0 ? f32x16{} : dp[s2], 1,
+                                                                  0, 0, 127, 0, 127);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       // P and dS of (query 32 s2 + 16 hh + r, this lane's key).  Padded query
@@ -410,12 +433,19 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
         for (int s2 = 0; s2 < 2; ++s2) {
           amp[s2] = 0.0f;
           ams[s2] = 0.0f;
+          // the 16 rows' L and D as four 16-byte reads each, issued together
+          f32x4 lr[4], dr[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            lr[v] = *reinterpret_cast<const f32x4*>(&sL[buf][32 * s2 + 16 * hh + 4 * v]);
+            dr[v] = *reinterpret_cast<const f32x4*>(&sD[buf][32 * s2 + 16 * hh + 4 * v]);
+          }
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int ql = 32 * s2 + 16 * hh + r, qi = c * BWD_CHUNK + ql;
-            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[s2][r], cc, -sL[buf][ql]));
+            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[s2][r], cc, -lr[r >> 2][r & 3]));
             if (decltype(masked)::value) pr = (key < p.N && (!CAUSAL || key <= qi)) ? pr : 0.0f;
-            const float ds = pr * __builtin_fmaf(dp[s2][r], sdv, -sD[buf][ql]);
+            const float ds = pr * __builtin_fmaf(dp[s2][r], sdv, -dr[r >> 2][r & 3]);
             pv[s2][r] = pr;
             dsv[s2][r] = ds;
             amp[s2] = __builtin_fmaxf(amp[s2], pr);
