@@ -664,23 +664,42 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdParams p) {
     fetch(c + 1 < nchunks ? c + 1 : c);
 
     f32x16 s[2], dp[2];
+    // S^T and dP^T of both 16-key sub-tiles, as in the dK/dV kernel: the two
+    // accumulation chains alternate and each A operand is read from LDS ahead
+    // of its matrix instruction (fenced); each chain sums its k-steps in order
+    {
+      const int kr0 = 32 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
+      const __bf16* ka = &sK[buf][kr0 * KSR + 8 * hh];
+      auto lda = [&](int i) {      // operand i: k-step i / 2 of sub-tile i % 2
+        return *reinterpret_cast<const bf16x8*>(ka + 16 * (i & 1) * KSR + 16 * (i >> 1));
+      };
+      bf16x8 op[3];
+      op[0] = lda(0);
+      op[1] = lda(1);
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const int krow = 32 * ((m >> 2) & 1) + 16 * s2 + 4 * (m >> 3) + (m & 3);
-      s[s2] = f32x16{};
-#pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sK[buf][krow * KSR + 16 * st + 8 * hh]);
-        s[s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[st], s[s2], 0, 0, 0);
+      for (int i = 0; i < 2 * KS; ++i) {
+        if (i + 2 < 2 * KS) op[(i + 2) % 3] = lda(i + 2);
+        const int st = i >> 1, s2 = i & 1;
+        s[s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], qreg[st], st == 0 ? f32x16{} : s[s2], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      dp[s2] = f32x16{};
+      const uint8_t* va = &sV[buf][kr0 * VS + 16 * hh];
+      auto ldv = [&](int i) {      // operand i: k-step i / 2 of sub-tile i % 2 (two 16-byte halves)
+        const uint8_t* r = va + 16 * (i & 1) * VS + 64 * (i >> 1);
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(r);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(r + 32);
+        return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      };
+      i32x8 ov[2];
+      ov[0] = ldv(0);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(&sV[buf][krow * VS + 64 * kk + 16 * hh]);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(&sV[buf][krow * VS + 64 * kk + 32 + 16 * hh]);
-        const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      for (int i = 0; i < 2 * KK; ++i) {
+        if (i + 1 < 2 * KK) ov[(i + 1) & 1] = ldv(i + 1);
+        const int kk = i >> 1, s2 = i & 1;
         // A: V codes (E4M3, format 0), B: dO^ codes (E5M2, format 1), unit scales
-        dp[s2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, doreg[kk], dp[s2], 0, 1, 0, 127, 0, 127);
+        dp[s2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ov[i & 1], doreg[kk], kk == 0 ? f32x16{} : dp[s2], 0,
+                                                                1, 0, 127, 0, 127);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // dS of (this lane's query, key 32 hh + 16 s2 + r): one MX block per lane half
