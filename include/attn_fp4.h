@@ -308,9 +308,14 @@ attn_status attn_fwd_fp8pv_cast(const attn_fwd_args* a, void* stream);
  *
  * attn_fwd_fp8pv_mxqk: the same MX-native Q/K with the FP8-P/V arithmetic of
  * attn_fwd_fp8pv (E4M3(2^(t - m')) with unit scale, FP8 V, causal or not).
+ *
+ * attn_fwd_directp_efq_mxqk: MX-native Q/K with the exp-free E2M1 cast of
+ * attn_fwd_directp_efq (code = min(RNE(2 (t - m' - e) + 2), 7)) in place of
+ * RNE(2^(t - m' - e)); noncausal.
  */
 attn_status attn_fwd_directp_mxqk(const attn_fwd_args* a, void* stream);
 attn_status attn_fwd_fp8pv_mxqk(const attn_fwd_args* a, void* stream);
+attn_status attn_fwd_directp_efq_mxqk(const attn_fwd_args* a, void* stream);
 
 /*
  * BF16 fused attention forward, the baseline the pages compare against

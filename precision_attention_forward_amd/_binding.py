@@ -109,6 +109,7 @@ EXPORTS = {
     "attn_fwd_fp8pv_cast": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "attn_fwd_directp_mxqk": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "attn_fwd_fp8pv_mxqk": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
+    "attn_fwd_directp_efq_mxqk": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "attn_decode_directp": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]),
     "attn_decode_fp8pv": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]),
     "attn_bwd_ws_bytes": (ctypes.c_size_t, [ctypes.POINTER(BwdArgs)]),
@@ -304,7 +305,7 @@ def _fwd_lowp(entry, q, k, v, *, Hq, Hkv, D, softmax_scale, causal=False, B=None
         dbg_b, dbg_h = debug
         nq_dbg = Nq
         nk_pad = (Nk + 127) // 128 * 128
-        if entry in ("attn_fwd_directp", "attn_fwd_directp_efq", "attn_fwd_directp_mxqk"):
+        if entry in ("attn_fwd_directp", "attn_fwd_directp_efq", "attn_fwd_directp_mxqk", "attn_fwd_directp_efq_mxqk"):
             dbg_codes = torch.zeros((nq_dbg, nk_pad // 2), dtype=torch.uint8, device=dev)
             dbg_scales = torch.zeros((nq_dbg, nk_pad // 32), dtype=torch.uint8, device=dev)
         else:
@@ -352,6 +353,11 @@ def fwd_directp_mxqk(q, k, v, **kw):
 def fwd_fp8pv_mxqk(q, k, v, **kw):
     """FP8-P/V with MX-native Q/K (opt-in; causal allowed)."""
     return _fwd_lowp("attn_fwd_fp8pv_mxqk", q, k, v, **kw)
+
+
+def fwd_directp_efq_mxqk(q, k, v, **kw):
+    """Exp-free Direct-P with MX-native Q/K (opt-in; noncausal)."""
+    return _fwd_lowp("attn_fwd_directp_efq_mxqk", q, k, v, **kw)
 
 
 def _decode(entry, q, k, v, *, B, Hq, Hkv, nq, Nk, D, softmax_scale, causal=False, seqlens_k=None,

@@ -25,7 +25,8 @@ hipError_t launch_pack_k_mx(const uint8_t* codes, const uint8_t* scales, int H, 
                             const int32_t* cu, int64_t n_pad, int64_t cols, int D, int pf, uint8_t* out,
                             hipStream_t st);
 struct FwdParams;
-hipError_t launch_fwd_mx(const FwdParams& p, int D, int pf, int vf, bool causal, bool debug, hipStream_t st);
+hipError_t launch_fwd_mx(const FwdParams& p, int D, int pf, int vf, bool causal, bool debug, int enc,
+                         hipStream_t st);
 hipError_t launch_fwd_lowp(const FwdParams& p, int D, int pf, int vf, bool causal, bool debug, int enc,
                            hipStream_t st);
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
@@ -259,7 +260,7 @@ static attn_status run_fwd_lowp(const attn_fwd_args* a, void* stream, int pf, in
     if (e != hipSuccess) return hip_status(e);
   }
   e = mx ? launch_fwd_mx(p, a->D, pf, a->v.format == ATTN_V_MXFP4 ? 1 : 0, a->causal != 0, a->dbg_p_codes != nullptr,
-                         st)
+                         enc, st)
          : launch_fwd_lowp(p, a->D, pf, a->v.format == ATTN_V_MXFP4 ? 1 : 0, a->causal != 0,
                            a->dbg_p_codes != nullptr, enc, st);
   if (e != hipSuccess) return hip_status(e);
@@ -275,6 +276,9 @@ attn_status attn_fwd_directp_mxqk(const attn_fwd_args* a, void* stream) {
   return run_fwd_lowp(a, stream, 0, 0, true);
 }
 attn_status attn_fwd_fp8pv_mxqk(const attn_fwd_args* a, void* stream) { return run_fwd_lowp(a, stream, 1, 0, true); }
+attn_status attn_fwd_directp_efq_mxqk(const attn_fwd_args* a, void* stream) {
+  return run_fwd_lowp(a, stream, 0, 1, true);
+}
 
 attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Hq,
                           int32_t Hkv, int32_t Nq, int32_t Nk, int32_t D, float softmax_scale, int32_t causal,

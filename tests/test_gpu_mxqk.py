@@ -136,6 +136,34 @@ def test_mxqk_hadamard_small_shapes_all_outputs(gpu, name, wl):
     assert stats, "probability dump not compared"
 
 
+EFQ = [
+    ("tiny", synth.WORKLOADS[1], "mxfp4"),
+    ("wan_recipe_small_mxfp4v", synth.WORKLOADS[2].with_(Hq=2, Hkv=2, N=1000, seed=21), "mxfp4_had"),
+    ("varlen_small", synth.WORKLOADS[5].with_(Hq=2, Hkv=2, varlen=(5, 1, 700), seed=51), "mxfp4_had"),
+]
+
+
+@pytest.mark.parametrize("name,wl,qk", EFQ, ids=[s[0] for s in EFQ])
+def test_mxqk_expfree_small_shapes_all_outputs(gpu, name, wl, qk):
+    # exp-free E2M1 cast with MX-native Q/K (attn_fwd_directp_efq_mxqk)
+    _say(f"fwd exp-free MX Q/K ({qk}) small {name}")
+    inp = synth.generate(wl, "cpu")
+    inp.q, inp.k, inp.v = inp.q.cuda(), inp.k.cuda(), inp.v.cuda()
+    o, lse, stats = _check(gpu, inp, qk=qk, encoder="loglin")
+    assert stats, "probability dump not compared"
+
+
+def test_mxqk_expfree_full_size_sampled(gpu):
+    wl = synth.WORKLOADS[2]
+    _say("fwd exp-free MX Q/K (mxfp4_had) full-size wan14b")
+    inp = synth.generate(wl, "cuda")
+    rows = np.unique(np.concatenate([np.random.default_rng(7).integers(0, wl.N, 24), [0, 1, 255, 256, wl.N - 1]]))
+    o, lse, stats = _check(gpu, inp, heads=[0, 39], seqs=[0], rows=rows, qk="mxfp4_had", encoder="loglin")
+    assert stats
+    del inp
+    torch.cuda.empty_cache()
+
+
 def test_mxqk_bf16_output(gpu):
     # bf16 O is the float32 O rounded to nearest even; LSE is the same
     wl = synth.WORKLOADS[2].with_(Hq=2, Hkv=2, N=300, seed=25)
