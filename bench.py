@@ -501,9 +501,8 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     mxqk = args.qk in ("mxfp4", "mxfp4_had")
     had = args.qk == "mxfp4_had"
-    if mxqk and (args.four_six or (args.encoder != "exact" and wl.p_format != "mxfp4")):
-        print("--qk mxfp4 takes no Four Over Six, and the exp-free encoder only with Direct-P (MXFP4 P)",
-              file=sys.stderr)
+    if mxqk and args.four_six:
+        print("--qk mxfp4 takes no Four Over Six", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -515,7 +514,8 @@ def main():
                                                                                           args.encoder)]
     if mxqk:
         fwd = {("mxfp4", "exact"): paf.fwd_directp_mxqk, ("fp8", "exact"): paf.fwd_fp8pv_mxqk,
-               ("mxfp4", "loglin"): paf.fwd_directp_efq_mxqk}[(wl.p_format, args.encoder)]
+               ("mxfp4", "loglin"): paf.fwd_directp_efq_mxqk,
+               ("fp8", "loglin"): paf.fwd_fp8pv_cast_mxqk}[(wl.p_format, args.encoder)]
     # (Q and K rotated alike by the 32-point Hadamard matrix: every Q.K is 32 times the original)
     kw = dict(Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D, softmax_scale=inp.sigma / 32.0 if had else inp.sigma, causal=wl.causal,
               out_dtype=torch.bfloat16)

@@ -312,10 +312,15 @@ attn_status attn_fwd_fp8pv_cast(const attn_fwd_args* a, void* stream);
  * attn_fwd_directp_efq_mxqk: MX-native Q/K with the exp-free E2M1 cast of
  * attn_fwd_directp_efq (code = min(RNE(2 (t - m' - e) + 2), 7)) in place of
  * RNE(2^(t - m' - e)); noncausal.
+ *
+ * attn_fwd_fp8pv_cast_mxqk: MX-native Q/K with the exp-free E4M3 cast of
+ * attn_fwd_fp8pv_cast (code = max(RNE(8 (t - m') + 56), 0)); FP8 V, causal
+ * or not.
  */
 attn_status attn_fwd_directp_mxqk(const attn_fwd_args* a, void* stream);
 attn_status attn_fwd_fp8pv_mxqk(const attn_fwd_args* a, void* stream);
 attn_status attn_fwd_directp_efq_mxqk(const attn_fwd_args* a, void* stream);
+attn_status attn_fwd_fp8pv_cast_mxqk(const attn_fwd_args* a, void* stream);
 
 /*
  * BF16 fused attention forward, the baseline the pages compare against

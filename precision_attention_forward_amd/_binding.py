@@ -110,6 +110,7 @@ EXPORTS = {
     "attn_fwd_directp_mxqk": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "attn_fwd_fp8pv_mxqk": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "attn_fwd_directp_efq_mxqk": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
+    "attn_fwd_fp8pv_cast_mxqk": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "attn_decode_directp": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]),
     "attn_decode_fp8pv": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]),
     "attn_bwd_ws_bytes": (ctypes.c_size_t, [ctypes.POINTER(BwdArgs)]),
@@ -358,6 +359,11 @@ def fwd_fp8pv_mxqk(q, k, v, **kw):
 def fwd_directp_efq_mxqk(q, k, v, **kw):
     """Exp-free Direct-P with MX-native Q/K (opt-in; noncausal)."""
     return _fwd_lowp("attn_fwd_directp_efq_mxqk", q, k, v, **kw)
+
+
+def fwd_fp8pv_cast_mxqk(q, k, v, **kw):
+    """Exp-free FP8-P/V with MX-native Q/K (opt-in; causal allowed)."""
+    return _fwd_lowp("attn_fwd_fp8pv_cast_mxqk", q, k, v, **kw)
 
 
 def _decode(entry, q, k, v, *, B, Hq, Hkv, nq, Nk, D, softmax_scale, causal=False, seqlens_k=None,

@@ -279,6 +279,9 @@ attn_status attn_fwd_fp8pv_mxqk(const attn_fwd_args* a, void* stream) { return r
 attn_status attn_fwd_directp_efq_mxqk(const attn_fwd_args* a, void* stream) {
   return run_fwd_lowp(a, stream, 0, 1, true);
 }
+attn_status attn_fwd_fp8pv_cast_mxqk(const attn_fwd_args* a, void* stream) {
+  return run_fwd_lowp(a, stream, 1, 1, true);
+}
 
 attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Hq,
                           int32_t Hkv, int32_t Nq, int32_t Nk, int32_t D, float softmax_scale, int32_t causal,

@@ -856,9 +856,9 @@ hipError_t launch_fwd_lowp(const FwdParams& p, int D, int pf, int vf, bool causa
              : launch_fwd_e<0>(p, nwg, D, pf, vf, causal, debug, st);
 }
 
-// MX Q/K mode: Direct-P (MXFP4 P; V FP8 or MXFP4; noncausal; exact encode or,
-// enc = 1, the exp-free cast) or FP8-P/V (exact encode; causal or not).  The
-// K tiles follow the P format's key order.
+// MX Q/K mode: Direct-P (MXFP4 P; V FP8 or MXFP4; noncausal) or FP8-P/V
+// (causal or not), each with the exact encode or (enc = 1) the exp-free cast.
+// The K tiles follow the P format's key order.
 hipError_t launch_pack_k_mx(const uint8_t* codes, const uint8_t* scales, int H, int B, int N, int max_len,
                             const int32_t* cu, int64_t n_pad, int64_t cols, int D, int pf, uint8_t* out,
                             hipStream_t st) {
@@ -882,13 +882,17 @@ hipError_t launch_fwd_mx(const FwdParams& p, int D, int pf, int vf, bool causal,
 #define MXL(DD, PP, VV, CC)                                                     \
   (debug ? launch_fwd_t<DD, PP, VV, CC, true, 0, 1>(p, nwg, st)                  \
          : launch_fwd_t<DD, PP, VV, CC, false, 0, 1>(p, nwg, st))
-#define MXE(DD, VV)                                                             \
-  (debug ? launch_fwd_t<DD, PF_MXFP4, VV, false, true, 1, 1>(p, nwg, st)         \
-         : launch_fwd_t<DD, PF_MXFP4, VV, false, false, 1, 1>(p, nwg, st))
+#define MXE(DD, PP, VV, CC)                                                     \
+  (debug ? launch_fwd_t<DD, PP, VV, CC, true, 1, 1>(p, nwg, st)                  \
+         : launch_fwd_t<DD, PP, VV, CC, false, 1, 1>(p, nwg, st))
   if (enc) {
-    if (pf != PF_MXFP4 || causal) return hipErrorInvalidValue;
-    if (vf == VF_MXFP4) return D == 64 ? MXE(64, VF_MXFP4) : MXE(128, VF_MXFP4);
-    return D == 64 ? MXE(64, VF_FP8) : MXE(128, VF_FP8);
+    if (pf == PF_FP8) {
+      if (causal) return D == 64 ? MXE(64, PF_FP8, VF_FP8, true) : MXE(128, PF_FP8, VF_FP8, true);
+      return D == 64 ? MXE(64, PF_FP8, VF_FP8, false) : MXE(128, PF_FP8, VF_FP8, false);
+    }
+    if (causal) return hipErrorInvalidValue;
+    if (vf == VF_MXFP4) return D == 64 ? MXE(64, PF_MXFP4, VF_MXFP4, false) : MXE(128, PF_MXFP4, VF_MXFP4, false);
+    return D == 64 ? MXE(64, PF_MXFP4, VF_FP8, false) : MXE(128, PF_MXFP4, VF_FP8, false);
   }
 #undef MXE
   if (pf == PF_FP8) {

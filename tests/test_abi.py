@@ -238,3 +238,6 @@ def test_mx_qk_entry_points_reject_bad_arguments(lib):
     # the exp-free MX entry point is Direct-P only: noncausal
     assert lib.attn_fwd_directp_efq_mxqk(ctypes.byref(_args(causal=1, ws=1 << 24, ws_bytes=need, **noscale)), None) == 2
     assert lib.attn_fwd_directp_efq_mxqk(None, None) == 1
+    assert lib.attn_fwd_fp8pv_cast_mxqk(ctypes.byref(_args(v=B._VTensor(1, 1 << 24, 1 << 24, 1 << 24), ws=1 << 24,
+                                                           ws_bytes=need, **noscale)), None) == 2
+    assert lib.attn_fwd_fp8pv_cast_mxqk(None, None) == 1

@@ -138,6 +138,8 @@ def test_mxqk_hadamard_small_shapes_all_outputs(gpu, name, wl):
 
 EFQ = [
     ("tiny", synth.WORKLOADS[1], "mxfp4"),
+    ("llama_causal_small_fp8_cast", synth.WORKLOADS[4].with_(B=2, Hq=4, Hkv=2, N=600, seed=41), "mxfp4"),
+    ("llama_causal_d64_fp8_cast_had", synth.WORKLOADS[4].with_(B=1, Hq=2, Hkv=1, N=450, D=64, seed=43), "mxfp4_had"),
     ("wan_recipe_small_mxfp4v", synth.WORKLOADS[2].with_(Hq=2, Hkv=2, N=1000, seed=21), "mxfp4_had"),
     ("varlen_small", synth.WORKLOADS[5].with_(Hq=2, Hkv=2, varlen=(5, 1, 700), seed=51), "mxfp4_had"),
 ]
@@ -145,7 +147,7 @@ EFQ = [
 
 @pytest.mark.parametrize("name,wl,qk", EFQ, ids=[s[0] for s in EFQ])
 def test_mxqk_expfree_small_shapes_all_outputs(gpu, name, wl, qk):
-    # exp-free E2M1 cast with MX-native Q/K (attn_fwd_directp_efq_mxqk)
+    # exp-free casts with MX-native Q/K (attn_fwd_directp_efq_mxqk: E2M1; attn_fwd_fp8pv_cast_mxqk: E4M3)
     _say(f"fwd exp-free MX Q/K ({qk}) small {name}")
     inp = synth.generate(wl, "cpu")
     inp.q, inp.k, inp.v = inp.q.cuda(), inp.k.cuda(), inp.v.cuda()
@@ -153,12 +155,14 @@ def test_mxqk_expfree_small_shapes_all_outputs(gpu, name, wl, qk):
     assert stats, "probability dump not compared"
 
 
-def test_mxqk_expfree_full_size_sampled(gpu):
-    wl = synth.WORKLOADS[2]
-    _say("fwd exp-free MX Q/K (mxfp4_had) full-size wan14b")
+@pytest.mark.parametrize("k,heads", [(2, [0, 39]), (4, [0, 31])], ids=["workload2", "workload4"])
+def test_mxqk_expfree_full_size_sampled(gpu, k, heads):
+    wl = synth.WORKLOADS[k]
+    _say(f"fwd exp-free MX Q/K (mxfp4_had) full-size {wl.name}")
     inp = synth.generate(wl, "cuda")
     rows = np.unique(np.concatenate([np.random.default_rng(7).integers(0, wl.N, 24), [0, 1, 255, 256, wl.N - 1]]))
-    o, lse, stats = _check(gpu, inp, heads=[0, 39], seqs=[0], rows=rows, qk="mxfp4_had", encoder="loglin")
+    seqs = [0] if wl.B == 1 else [0, wl.B - 1]
+    o, lse, stats = _check(gpu, inp, heads=heads, seqs=seqs, rows=rows, qk="mxfp4_had", encoder="loglin")
     assert stats
     del inp
     torch.cuda.empty_cache()
