@@ -15,7 +15,7 @@ import pytest
 import torch
 
 from helpers import (assert_close_outputs, check_code_choices, f32, gpu_codes, oracle_head, p_mismatch,
-                     P_MISMATCH_MAX)
+                     score_row_slack, P_MISMATCH_MAX)
 from precision_attention_forward_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -71,7 +71,7 @@ def _seq_slices(inp):
 
 
 def _check(gpu, inp, heads=None, seqs=None, rows=None, dumps=True, max_rows=None, encoder="exact", four_six=False,
-           qk="nvfp4"):
+           qk="nvfp4", wide=False):
     """Run the production kernel once and compare the selected (sequence,
     head, rows) with the oracle.
 
@@ -81,7 +81,9 @@ def _check(gpu, inp, heads=None, seqs=None, rows=None, dumps=True, max_rows=None
     it differs from the oracle must be a rounding near-tie (helpers.
     check_code_choices), at most P_MISMATCH_MAX of the live codes; and O/LSE
     are then compared with the oracle run on the kernel's codes, so that a
-    tie decided the other way is not counted as an output error."""
+    tie decided the other way is not counted as an output error.  With
+    ``wide`` (scores far from zero), the near-tie window of every row also
+    takes the float32 error bound of its scores (helpers.score_row_slack)."""
     wl = inp.wl
     o, lse, _ = _gpu_run(gpu, inp, encoder=encoder, four_six=four_six, qk=qk)
     amax_q, amax_k, amax_v = _amax(inp.q), _amax(inp.k), _amax(inp.v)
@@ -123,7 +125,12 @@ def _check(gpu, inp, heads=None, seqs=None, rows=None, dumps=True, max_rows=None
                 gc, ge = gpu_codes(dc[ridx].cpu().numpy(), None if ds is None else ds[ridx].cpu().numpy(),
                                    wl.p_format, L)
                 live = np.arange(L)[None, :] <= r[:, None] if wl.causal else np.ones((len(r), L), bool)
-                n_e, n_c = check_code_choices(gc, ge, res[2], res[3], res[4], res[5], wl.p_format, encoder, live)
+                slack = None
+                if wide:
+                    slack = score_row_slack(q_rows, k_all, amax_q=amax_q, amax_k=amax_k, sigma=inp.sigma, qk=qk,
+                                            four_six=four_six, q_index=r, causal=wl.causal)
+                n_e, n_c = check_code_choices(gc, ge, res[2], res[3], res[4], res[5], wl.p_format, encoder, live,
+                                              row_slack=slack)
                 mis, tot = p_mismatch(dc[ridx].cpu().numpy(), None if ds is None else ds[ridx].cpu().numpy(),
                                       res[2], res[3], wl.p_format, L, live)
                 stats.append((mis, tot))
@@ -212,6 +219,37 @@ def test_edge_zero_queries_closed_form(gpu, qk):
     o, lse, _ = _gpu_run(gpu, inp, qk=qk)
     np.testing.assert_allclose(f32(lse), math.log(300), rtol=1e-6)
     o, lse, _ = _check(gpu, inp, dumps=False, qk=qk)
+
+
+WIDE = [
+    ("wan_recipe_wide", synth.WORKLOADS[2].with_(Hq=2, Hkv=2, N=700, seed=81), "nvfp4"),
+    ("llama_causal_gqa_wide", synth.WORKLOADS[4].with_(B=1, Hq=4, Hkv=2, N=520, seed=82), "nvfp4"),
+    ("wan_recipe_wide_mxqk_had", synth.WORKLOADS[2].with_(Hq=2, Hkv=2, N=700, seed=83), "mxfp4_had"),
+    ("llama_causal_wide_mxqk", synth.WORKLOADS[4].with_(B=1, Hq=2, Hkv=1, N=400, seed=84), "mxfp4"),
+]
+
+
+@pytest.mark.parametrize("name,wl,qk", WIDE, ids=[w[0] for w in WIDE])
+def test_wide_score_range(gpu, name, wl, qk):
+    # Q rows scaled by powers of two 2^-3 .. 2^6 (per batch, row and head):
+    # rows whose scaled scores span hundreds of binades sit beside near-flat
+    # ones, so whole 32-key blocks underflow (block exponent at its floor, all
+    # codes 0) and the running max jumps far enough to take alpha to 0
+    _say(f"fwd wide score range {name}, Q/K {qk}")
+    inp = synth.generate(wl, "cpu")
+    g = torch.Generator().manual_seed(wl.seed + 1000)
+    f = torch.exp2(torch.randint(-3, 7, tuple(inp.q.shape[:-1]), generator=g).float())
+    inp.q = (inp.q.float() * f[..., None]).to(torch.bfloat16)
+    # the inputs are what the case claims: some row of (batch 0, head 0)
+    # spans more than 200 binades between its largest and smallest live score
+    x = (inp.q[0, :, 0].float() @ inp.k[0, :, 0].float().T) * inp.sigma * math.log2(math.e)
+    live = torch.ones_like(x, dtype=torch.bool)
+    if wl.causal:
+        live = live.tril()
+    span = x.masked_fill(~live, -math.inf).amax(1) - x.masked_fill(~live, math.inf).amin(1)
+    assert float(span.max()) > 200.0
+    inp.q, inp.k, inp.v = inp.q.cuda(), inp.k.cuda(), inp.v.cuda()
+    _check(gpu, inp, qk=qk, wide=True)
 
 
 def test_bf16_output_mode(gpu):
