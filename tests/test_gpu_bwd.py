@@ -2,8 +2,9 @@
 
 The backward takes the forward's quantized Q/K/V, its output O and LSE, and
 dO.  O and LSE are inputs here: they are computed as textbook float32
-attention on the bf16 inputs with torch operations (never with this
-library's kernels), and both sides receive the same values.
+attention on the bf16 inputs (on the oracle's dequantized Q^ and K^ for the
+wide score-range case) with torch operations, never with this library's
+kernels, and both sides receive the same values.
 
 Bar: every E4M3 code of P~ / dS~ equals the oracle's except at float32
 near-ties (checked element by element on the dump of the kernel's codes);
@@ -71,7 +72,26 @@ def _check_close(got, ref, what):
     return rel
 
 
-def _run(gpu, wl, q_rows=None, k_rows=None, heads=None, batches=None, seed_do=0):
+def _wide_rows(q, seed):
+    """Q with each (batch, row, head) scaled by a power of two 2^-3 .. 2^6."""
+    g = torch.Generator().manual_seed(seed + 1000)
+    f = torch.exp2(torch.randint(-3, 7, tuple(q.shape[:-1]), generator=g).float()).to(q.device)
+    return (q.float() * f[..., None]).to(torch.bfloat16)
+
+
+def _dequant_nvfp4_all(x, amax):
+    """The oracle's NVFP4 quantization and dequantization of every (batch,
+    head) of x [B, N, H, D], as float32 on the CPU."""
+    B, N, H, D = x.shape
+    out = torch.empty((B, N, H, D), dtype=torch.float32)
+    for b in range(B):
+        for h in range(H):
+            c, s, g = OQ.quant_nvfp4(f32(x[b, :, h]), amax=amax)
+            out[b, :, h] = torch.from_numpy(OQ.dequant_nvfp4_raw(c, s) * float(np.float32(g)))
+    return out
+
+
+def _run(gpu, wl, q_rows=None, k_rows=None, heads=None, batches=None, seed_do=0, wide=False):
     """Generate inputs, run the production backward once, then per compared
     (batch, query head) the build with the E4M3 operand dump, which must
     reproduce the production outputs bit for bit.  Every dumped code that
@@ -79,12 +99,22 @@ def _run(gpu, wl, q_rows=None, k_rows=None, heads=None, batches=None, seed_do=0)
     (helpers.check_bwd_codes); dQ / dK / dV are then compared with the oracle
     run on the kernel's codes."""
     inp = synth.generate(wl, "cuda")
+    if wide:
+        inp.q = _wide_rows(inp.q, wl.seed)
     B, N, Hq, D = inp.q.shape
     Hkv = inp.k.shape[2]
     G = Hq // Hkv
     gen = torch.Generator().manual_seed(seed_do + wl.seed)
     dout = torch.randn((B, N, Hq, D), generator=gen).to(torch.bfloat16).cuda()
-    o, lse = _attention_o_lse(inp.q, inp.k, inp.v, inp.sigma, wl.causal, "cuda")
+    if wide:
+        # scores far from zero: the quantization error of Q^.K^ is then many
+        # units, so O and LSE come from textbook attention on the oracle's
+        # dequantized Q^ and K^, as after a low-precision forward (P = 2^(t - L)
+        # stays at most about 1)
+        o, lse = _attention_o_lse(_dequant_nvfp4_all(inp.q, _amax(inp.q)), _dequant_nvfp4_all(inp.k, _amax(inp.k)),
+                                  inp.v, inp.sigma, wl.causal, "cuda")
+    else:
+        o, lse = _attention_o_lse(inp.q, inp.k, inp.v, inp.sigma, wl.causal, "cuda")
     qq = gpu.quant_nvfp4(inp.q)
     kq = gpu.quant_nvfp4(inp.k)
     vc, vs, vt, _ = gpu.quant_v(inp.v, gpu.V_FP8)
@@ -127,10 +157,12 @@ def _run(gpu, wl, q_rows=None, k_rows=None, heads=None, batches=None, seed_do=0)
                 eps_kp = _bwd_rel_err(pk["abs_qk"], pk["lse2"][:, None])
                 eps_kd = _bwd_rel_err(pk["abs_qk"], pk["lse2"][:, None], pk["ds"], pk["p"], pk["abs_dpv"],
                                       pk["abs_D"][:, None])
-                n_ties += check_bwd_codes(*g_dsq, pq["ds"], pq["codes"], pq["exps"], eps_q, 1, live_q, f"dS~Q {b},{h}")
-                n_ties += check_bwd_codes(*g_pt, pk["p"], pk["codes_p"], pk["exps_p"], eps_kp, 0, live_k, f"P~ {b},{h}")
+                n_ties += check_bwd_codes(*g_dsq, pq["ds"], pq["codes"], pq["exps"], eps_q, 1, live_q, f"dS~Q {b},{h}",
+                                          p=pq["p"])
+                n_ties += check_bwd_codes(*g_pt, pk["p"], pk["codes_p"], pk["exps_p"], eps_kp, 0, live_k, f"P~ {b},{h}",
+                                          p=pk["p"])
                 n_ties += check_bwd_codes(*g_dsk, pk["ds"], pk["codes_ds"], pk["exps_ds"], eps_kd, 0, live_k,
-                                          f"dS~K {b},{h}")
+                                          f"dS~K {b},{h}", p=pk["p"])
                 n_live += int(live_q.sum()) + 2 * int(live_k.sum())
                 rq, rk, rv = OB.attn_bwd_head(*bargs, q_rows=qr, k_rows=kr,
                                               given={"ds_q": g_dsq, "p_t": g_pt, "ds_k": g_dsk})
@@ -163,6 +195,18 @@ def test_bwd_edges(gpu):
     for N in (1, 2, 64, 65):
         _say(f"bwd edge N={N}")
         _run(gpu, synth.WORKLOADS[4].with_(B=1, Hq=2, Hkv=1, N=N, seed=90 + N))
+
+
+@pytest.mark.parametrize("name,wl", [
+    ("causal_gqa", synth.WORKLOADS[4].with_(B=1, Hq=2, Hkv=1, N=200, seed=85)),
+    ("noncausal", synth.WORKLOADS[4].with_(B=1, Hq=1, Hkv=1, N=160, causal=False, seed=86)),
+], ids=["causal_gqa", "noncausal"])
+def test_bwd_wide_score_range(gpu, name, wl):
+    # Q rows scaled by powers of two 2^-3 .. 2^6: near one-hot rows, whose
+    # probabilities underflow E4M3 outside a few keys and whose dP - D cancels,
+    # beside near-flat ones; the code tolerance already scales with |Q||K|
+    _say(f"bwd wide score range {name}")
+    _run(gpu, wl, wide=True)
 
 
 def test_bwd_full_size_sampled(gpu):

@@ -131,3 +131,58 @@ def test_tie_check_block_exponent():
     xmax[0, b] = np.rint(xmax[0, b]) - 0.3
     with pytest.raises(AssertionError):
         check_code_choices(gc, ge, oc, oe, pre, xmax, "mxfp4", "exact", live)
+
+
+def test_tie_check_row_slack():
+    # a code rounded the other way 1e-3 (relative) from its boundary: beyond
+    # the plain window, inside a row slack of 2e-3 log2 units (1.4e-3 relative)
+    gc, ge, oc, oe, pre, xmax = _case("mxfp4", "exact", seed=7)
+    live = np.isfinite(pre)
+    i, j = np.argwhere(live & (oc > 1) & (oc < 6))[0]
+    c = int(oc[i, j])
+    pre[i, j] = 0.5 * (F.e2m1_decode(c) + F.e2m1_decode(c + 1)) * (1 - 1e-3)
+    oc = oc.copy()
+    oc[i, j] = c
+    gc = gc.copy()
+    gc[i, j] = c + 1
+    with pytest.raises(AssertionError):
+        check_code_choices(gc, ge, oc, oe, pre, xmax, "mxfp4", "exact", live)
+    slack = np.zeros(gc.shape[0])
+    slack[i] = 2e-3
+    assert check_code_choices(gc, ge, oc, oe, pre, xmax, "mxfp4", "exact", live, row_slack=slack) == (0, 1)
+    slack[i] = 1e-3                               # 0.7e-3 relative: too narrow
+    with pytest.raises(AssertionError):
+        check_code_choices(gc, ge, oc, oe, pre, xmax, "mxfp4", "exact", live, row_slack=slack)
+    with pytest.raises(ValueError):
+        check_code_choices(gc, ge, oc, oe, pre, xmax, "mxfp4", "loglin", live, row_slack=slack)
+
+
+def test_bwd_check_zero_below_float32_normal_range():
+    from helpers import check_bwd_codes
+    from oracle import backward as OB
+    # one block of 32 values along axis 1 whose block exponent sits at its
+    # floor of -127: the value 2^-128 * 5 codes to E4M3(2.5) = 0x42 (biased
+    # exponent 8, mantissa 010), but the
+    # float32 probability behind it is below the normal range
+    x = np.zeros((1, 32))
+    x[0, :4] = [2.0 ** -120, 2.0 ** -128 * 5.0, 2.0 ** -124, -(2.0 ** -122)]
+    _, oc, oe = OB.mx_e4m3(x, axis=1)
+    assert int(oe[0, 0]) == -127 and int(oc[0, 1]) == 0x42
+    eps = np.full(x.shape, 1e-6)
+    live = np.ones(x.shape, bool)
+    gc = oc.copy()
+    gc[0, 1] = 0
+    ge = oe + 127
+    p = np.ones(x.shape)
+    p[0, 1] = 2.0 ** -130
+    assert check_bwd_codes(gc, ge, x, oc, ge, eps, 1, live, p=p) == 0
+    # a zero code where the value and its probability are normal floats is a mismatch
+    gc2 = oc.copy()
+    gc2[0, 0] = 0
+    with pytest.raises(AssertionError):
+        check_bwd_codes(gc2, ge, x, oc, ge, eps, 1, live, p=np.ones(x.shape))
+    # and a nonzero wrong code below the normal range is still rejected
+    gc3 = oc.copy()
+    gc3[0, 1] = 0x30
+    with pytest.raises(AssertionError):
+        check_bwd_codes(gc3, ge, x, oc, ge, eps, 1, live, p=p)
