@@ -20,7 +20,7 @@ import pytest
 import torch
 
 from helpers import (assert_close_outputs, check_code_choices, f32, gpu_codes, oracle_v_head, p_mismatch,
-                     P_MISMATCH_MAX)
+                     score_row_slack, P_MISMATCH_MAX)
 from oracle import attention as OA
 from oracle import quant as OQ
 from precision_attention_forward_amd import synth
@@ -60,8 +60,10 @@ def _run(gpu, inp, prep, debug=None):
     return o, lse, dbg
 
 
-def _check(gpu, inp, pairs=None):
-    """Compare every (sequence, head) in ``pairs`` (default: all) with the oracle."""
+def _check(gpu, inp, pairs=None, wide=False):
+    """Compare every (sequence, head) in ``pairs`` (default: all) with the
+    oracle; with ``wide``, the near-tie window of every row also takes the
+    float32 error bound of its scores (helpers.score_row_slack)."""
     wl = inp.wl
     prep = _Prepared(gpu, inp)
     o, lse, _ = _run(gpu, inp, prep)
@@ -91,7 +93,12 @@ def _check(gpu, inp, pairs=None):
             dsn = None if ds is None else ds.cpu().numpy()
             gc, ge = gpu_codes(dcn, dsn, wl.p_format, L)
             live = (np.arange(L)[None, :] <= q_index[:, None]) if wl.causal else np.ones((nq, L), bool)
-            e1, c1 = check_code_choices(gc, ge, res[2], res[3], res[4], res[5], wl.p_format, "exact", live)
+            slack = None
+            if wide:
+                slack = score_row_slack(f32(inp.q[b, :, h]), f32(inp.k[b, hk, :L]), amax_q=amax_q, amax_k=amax_k,
+                                        sigma=inp.sigma, q_index=q_index, causal=wl.causal)
+            e1, c1 = check_code_choices(gc, ge, res[2], res[3], res[4], res[5], wl.p_format, "exact", live,
+                                        row_slack=slack)
             mis, tot = p_mismatch(dcn, dsn, res[2], res[3], wl.p_format, L, live)
             n_mis, n_tot, n_e, n_c = n_mis + mis, n_tot + tot, n_e + e1, n_c + c1
             if e1 or c1:
@@ -128,6 +135,18 @@ SMALL = [
 def test_decode_small_all_heads(gpu, name, wl):
     _say(f"decode {name}")
     _check(gpu, synth.generate_decode(wl))
+
+
+@pytest.mark.parametrize("name,wl", [SMALL[1], SMALL[2]], ids=[SMALL[1][0], SMALL[2][0]])
+def test_decode_wide_score_range(gpu, name, wl):
+    # new-token rows scaled by powers of two 2^-3 .. 2^6 (per sequence, row and
+    # head): blocks of the cache underflow to the E8M0 floor beside flat rows
+    _say(f"decode wide score range {name}")
+    inp = synth.generate_decode(wl)
+    g = torch.Generator().manual_seed(wl.seed + 1000)
+    f = torch.exp2(torch.randint(-3, 7, tuple(inp.q.shape[:-1]), generator=g).float())
+    inp.q = (inp.q.float() * f[..., None]).to(torch.bfloat16)
+    _check(gpu, inp, wide=True)
 
 
 def test_decode_length_edges(gpu):
