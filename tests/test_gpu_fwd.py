@@ -207,6 +207,29 @@ def test_varlen_with_empty_sequences(gpu, qk):
     _check(gpu, inp, qk=qk)
 
 
+@pytest.mark.parametrize("nseq,H,Hkv,causal", [(24, 2, 1, False), (24, 2, 2, True), (7, 1, 1, False)],
+                         ids=["48pairs_gqa", "48pairs_causal", "7pairs"])
+def test_varlen_many_short_sequences(gpu, nseq, H, Hkv, causal):
+    # many short sequences (0 .. 300 keys, with 128 and 129 among them): most
+    # query-block slots of the packed launch are empty or padding.  48 (batch,
+    # head) pairs take the launch order that groups query blocks per XCD, 7
+    # pairs the plain order
+    g = torch.Generator().manual_seed(900 + nseq + H + int(causal))
+    lens = torch.randint(0, 301, (nseq,), generator=g, dtype=torch.int32)
+    lens[0], lens[1], lens[2] = 128, 0, 129
+    T = int(lens.sum())
+    wl = synth.WORKLOADS[5].with_(Hq=H, Hkv=Hkv, causal=causal, p_format="fp8" if causal else "mxfp4",
+                                  varlen=(nseq, 0, 300), seed=900 + nseq)
+    q = torch.randn(T, H, 128, generator=g).to(torch.bfloat16).cuda()
+    k = torch.randn(T, Hkv, 128, generator=g).to(torch.bfloat16).cuda()
+    v = torch.randn(T, Hkv, 128, generator=g).to(torch.bfloat16).cuda()
+    cu = torch.zeros(nseq + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(lens, 0)
+    inp = synth.Inputs(wl, q, k, v, lens, cu, None)
+    _say(f"varlen {nseq} short sequences, {H} heads / {Hkv} KV heads, causal {causal}, total {T} tokens")
+    _check(gpu, inp)
+
+
 @pytest.mark.parametrize("qk", ["nvfp4", "mxfp4", "mxfp4_had"])
 def test_edge_zero_queries_closed_form(gpu, qk):
     # Q = 0: every probability code is 4.0 with e = -2 (p = 1), so O is the mean
