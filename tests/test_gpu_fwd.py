@@ -245,20 +245,23 @@ def test_edge_zero_queries_closed_form(gpu, qk):
 
 
 WIDE = [
-    ("wan_recipe_wide", synth.WORKLOADS[2].with_(Hq=2, Hkv=2, N=700, seed=81), "nvfp4"),
-    ("llama_causal_gqa_wide", synth.WORKLOADS[4].with_(B=1, Hq=4, Hkv=2, N=520, seed=82), "nvfp4"),
-    ("wan_recipe_wide_mxqk_had", synth.WORKLOADS[2].with_(Hq=2, Hkv=2, N=700, seed=83), "mxfp4_had"),
-    ("llama_causal_wide_mxqk", synth.WORKLOADS[4].with_(B=1, Hq=2, Hkv=1, N=400, seed=84), "mxfp4"),
+    ("wan_recipe_wide", synth.WORKLOADS[2].with_(Hq=2, Hkv=2, N=700, seed=81), "nvfp4", "exact"),
+    ("llama_causal_gqa_wide", synth.WORKLOADS[4].with_(B=1, Hq=4, Hkv=2, N=520, seed=82), "nvfp4", "exact"),
+    ("wan_recipe_wide_mxqk_had", synth.WORKLOADS[2].with_(Hq=2, Hkv=2, N=700, seed=83), "mxfp4_had", "exact"),
+    ("llama_causal_wide_mxqk", synth.WORKLOADS[4].with_(B=1, Hq=2, Hkv=1, N=400, seed=84), "mxfp4", "exact"),
+    ("wan_recipe_wide_cast", synth.WORKLOADS[2].with_(Hq=2, Hkv=2, N=700, seed=85), "nvfp4", "loglin"),
+    ("llama_causal_wide_cast_mxqk", synth.WORKLOADS[4].with_(B=1, Hq=2, Hkv=1, N=400, seed=86), "mxfp4_had",
+     "loglin"),
 ]
 
 
-@pytest.mark.parametrize("name,wl,qk", WIDE, ids=[w[0] for w in WIDE])
-def test_wide_score_range(gpu, name, wl, qk):
+@pytest.mark.parametrize("name,wl,qk,encoder", WIDE, ids=[w[0] for w in WIDE])
+def test_wide_score_range(gpu, name, wl, qk, encoder):
     # Q rows scaled by powers of two 2^-3 .. 2^6 (per batch, row and head):
     # rows whose scaled scores span hundreds of binades sit beside near-flat
     # ones, so whole 32-key blocks underflow (block exponent at its floor, all
     # codes 0) and the running max jumps far enough to take alpha to 0
-    _say(f"fwd wide score range {name}, Q/K {qk}")
+    _say(f"fwd wide score range {name}, Q/K {qk}, encoder {encoder}")
     inp = synth.generate(wl, "cpu")
     g = torch.Generator().manual_seed(wl.seed + 1000)
     f = torch.exp2(torch.randint(-3, 7, tuple(inp.q.shape[:-1]), generator=g).float())
@@ -272,7 +275,7 @@ def test_wide_score_range(gpu, name, wl, qk):
     span = x.masked_fill(~live, -math.inf).amax(1) - x.masked_fill(~live, math.inf).amin(1)
     assert float(span.max()) > 200.0
     inp.q, inp.k, inp.v = inp.q.cuda(), inp.k.cuda(), inp.v.cuda()
-    _check(gpu, inp, qk=qk, wide=True)
+    _check(gpu, inp, qk=qk, wide=True, encoder=encoder)
 
 
 def test_bf16_output_mode(gpu):

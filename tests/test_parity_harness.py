@@ -153,7 +153,27 @@ def test_tie_check_row_slack():
     slack[i] = 1e-3                               # 0.7e-3 relative: too narrow
     with pytest.raises(AssertionError):
         check_code_choices(gc, ge, oc, oe, pre, xmax, "mxfp4", "exact", live, row_slack=slack)
-    with pytest.raises(ValueError):
+
+
+def test_tie_check_row_slack_cast():
+    # the E2M1 cast: a position 0.01 code units from its boundary (2^M = 2 code
+    # units per log2 unit) needs a row slack of at least 0.005 - NEAR_TIE_POS / 2
+    gc, ge, oc, oe, pre, xmax = _case("mxfp4", "loglin", seed=8)
+    live = np.isfinite(pre)
+    i, j = np.argwhere(live & (oc > 1) & (oc < 6))[0]
+    c = int(oc[i, j])
+    pre[i, j] = c + 0.5 - 0.01
+    oc = oc.copy()
+    oc[i, j] = c
+    gc = gc.copy()
+    gc[i, j] = c + 1
+    with pytest.raises(AssertionError):
+        check_code_choices(gc, ge, oc, oe, pre, xmax, "mxfp4", "loglin", live)
+    slack = np.zeros(gc.shape[0])
+    slack[i] = 0.005
+    assert check_code_choices(gc, ge, oc, oe, pre, xmax, "mxfp4", "loglin", live, row_slack=slack) == (0, 1)
+    slack[i] = 0.004
+    with pytest.raises(AssertionError):
         check_code_choices(gc, ge, oc, oe, pre, xmax, "mxfp4", "loglin", live, row_slack=slack)
 
 
