@@ -9,6 +9,7 @@ noncausal, MXFP4 P and V).  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload 1..5]
   python bench.py --backward      causal-training backward (Llama-3.1-8B shape)
+  python bench.py --backward --noncausal   the same shape without the causal mask
   python bench.py --decode        decode step against a resident KV cache
 """
 
@@ -45,6 +46,8 @@ def parse():
                          "of Q and K by the Hadamard matrix first (attn_quant_mxfp4_had, softmax scale / 32)")
     ap.add_argument("--backward", action="store_true",
                     help="time the causal-training backward (attn_bwd_fp8) instead of the forward; its own JSON line")
+    ap.add_argument("--noncausal", action="store_true",
+                    help="with --backward: the same shape without the causal mask")
     ap.add_argument("--decode", action="store_true",
                     help="time a decode step (workload 6: new tokens against a resident NVFP4/FP8 KV cache); "
                          "its own JSON line")
@@ -277,6 +280,8 @@ def backward_main(args, torch, paf, synth):
     O, LSE) and dO.  Flops: 5 matrix products of 2 N^2 D per (batch, head),
     halved for causal (the usual backward count, 2.5x the forward's)."""
     wl = synth.WORKLOADS[args.workload]
+    if args.noncausal:
+        wl = wl.with_(causal=False)
     if wl.varlen is not None:
         print("the backward takes dense batches only", file=sys.stderr)
         sys.exit(2)

@@ -168,8 +168,11 @@ int64_t attn_v_cols(int32_t B, int32_t Nk, int64_t total_k, int32_t varlen);
  * contiguous, which is the operand order the P.V product reads.
  *   v_bf16 : [B, Nk, Hkv, D] (dense) or [total_k, Hkv, D] (varlen)
  *   cu_seqlens_k : device int32 [B+1] for varlen, NULL for dense
- *   FP8  : enc = 448 / amax_v (1 if amax_v == 0), *tensor_scale = 1 / enc,
- *          code = E4M3_sat(v * enc)
+ *   FP8  : enc = fl(448 / amax_v) (1 if amax_v == 0), *tensor_scale =
+ *          s_v = fl(1 / enc), code = E4M3_sat(fl(v * enc)), all float32 with
+ *          round-to-nearest-even (the NVFP4 tensor scale's pattern; s_v is
+ *          not fl(amax_v / 448): for amax_v = 49/32 that would be 7/2048,
+ *          while fl(1 / fl(448 / amax_v)) is one ulp below it)
  *   MXFP4: per (head, channel, 32 keys from the start of the sequence):
  *          e = clamp(floor(log2 amax) - 2, -127, 127) (-127 if all zero),
  *          code = E2M1_sat(v * 2^-e), scale byte = e + 127

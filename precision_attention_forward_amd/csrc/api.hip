@@ -204,6 +204,15 @@ static attn_status validate_fwd(const attn_fwd_args* a, bool allow_causal, int p
       return ATTN_ERR_INVALID_ARGUMENT;
     if (pf == 0 && a->dbg_p_scales == nullptr) return ATTN_ERR_INVALID_ARGUMENT;
   }
+  // The kernels address one KV head's V^T rows with 32-bit per-lane byte
+  // offsets d * cols (FP8: one byte per key; MXFP4: half a byte), and index
+  // workgroups with 32-bit integers.
+  const int64_t kcols = fwd_kcols(a);
+  const int64_t vrow_bytes = a->v.format == ATTN_V_MXFP4 ? (int64_t)a->D * kcols / 2 : (int64_t)a->D * kcols;
+  if (vrow_bytes >= ((int64_t)1 << 32)) return ATTN_ERR_UNSUPPORTED;
+  // (query blocks of 256 rows; packed batches pad them to whole groups of 16)
+  const int64_t qb = ((int64_t)a->Nq + WG_Q - 1) / WG_Q + 16;
+  if ((int64_t)a->B * a->Hq * qb >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
   const size_t need = attn_fwd_ws_bytes(a);
   if (a->ws == nullptr || a->ws_bytes < need || !aligned(a->ws, 256)) return ATTN_ERR_WORKSPACE;
   return ATTN_OK;
@@ -294,6 +303,9 @@ attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, 
   if (nq > 0 && (q == nullptr || o == nullptr || !aligned(q, 16) || !aligned(o, 16))) return ATTN_ERR_INVALID_ARGUMENT;
   if (nk > 0 && (k == nullptr || v == nullptr || !aligned(k, 16) || !aligned(v, 16))) return ATTN_ERR_INVALID_ARGUMENT;
   if (lse != nullptr && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARGUMENT;
+  // K and V rows are addressed with 32-bit byte offsets from each batch entry's base
+  if ((int64_t)Nk * Hkv * D * 2 >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hq * ((Nq + WG_Q - 1) / WG_Q) >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
   return hip_status(launch_fwd_bf16(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, D, softmax_scale, causal != 0,
                                     (hipStream_t)stream));
 }

@@ -260,6 +260,29 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
     const int last_q = min(qb * WG_Q + WG_Q, len_q) - 1;
     n_tiles = min(n_tiles, last_q / KEY_TILE + 1);
   }
+  // No key at all (Nk = 0, or an empty key sequence of a packed batch): every
+  // row has an empty softmax, O = 0 and LSE = -inf, and nothing of K or V
+  // may be read (their buffers can be empty).  Uniform per workgroup, before
+  // any barrier.
+  if (n_tiles == 0) {
+    if (wave_active && my_q < len_q) {
+      const int64_t orow = ((tq0 + my_q) * p.Hq + h) * (int64_t)D + hh * HALF;
+      if (p.o_f32) {
+#pragma unroll
+        for (int d = 0; d < HALF; d += 4)
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o) + orow + d) = f32x4{0.f, 0.f, 0.f, 0.f};
+      } else {
+#pragma unroll
+        for (int d = 0; d < HALF; d += 8)
+          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.o) + orow + d) = u32x4{0u, 0u, 0u, 0u};
+      }
+      if (p.lse != nullptr && hh == 0) {
+        if (varlen) p.lse[(int64_t)h * (p.cu_q[p.B]) + tq0 + my_q] = -__builtin_inff();
+        else p.lse[((int64_t)b * p.Hq + h) * p.Nq + my_q] = -__builtin_inff();
+      }
+    }
+    return;
+  }
 
   // ---- scalars: c = sigma * log2(e) * gq * gk
   // (MX Q/K: no tensor scales, the E8M0 block exponents are applied by the MFMA)

@@ -170,6 +170,32 @@ def test_fwd_validation(lib):
     assert lib.attn_fwd_bf16(None, None, None, None, None, 1, 4, 4, 16, 16, 80, 0.1, 0, None) == 1
 
 
+def test_fwd_offset_limits(lib):
+    # The forward reads one KV head's V^T rows with 32-bit per-lane byte
+    # offsets d * cols: FP8 V needs D * cols < 2^32, MXFP4 V D * cols / 2 <
+    # 2^32.  Past the limit the call returns UNSUPPORTED before any launch (the
+    # fake pointers are never touched); just below it, validation goes on to
+    # the next check (here: no workspace).
+    D = 128
+    fp8_over = (1 << 32) // D                  # cols = 2^25: D * cols = 2^32
+    fp8_under = fp8_over - 128
+    big = dict(B=1, Hq=1, Hkv=1, Nq=256)
+    v_fp8, v_mx = B._VTensor(0, 1 << 24, None, 1 << 24), B._VTensor(1, 1 << 24, 1 << 24, None)
+    for fn in (lib.attn_fwd_directp, lib.attn_fwd_fp8pv, lib.attn_fwd_directp_efq, lib.attn_fwd_fp8pv_mxqk):
+        assert fn(ctypes.byref(_args(Nk=fp8_over, v=v_fp8, **big)), None) == 2
+        assert fn(ctypes.byref(_args(Nk=fp8_under, v=v_fp8, **big)), None) == 3
+    # MXFP4 V: half a byte per key
+    assert lib.attn_fwd_directp(ctypes.byref(_args(Nk=2 * fp8_over, v=v_mx, **big)), None) == 2
+    assert lib.attn_fwd_directp(ctypes.byref(_args(Nk=2 * fp8_over - 128, v=v_mx, **big)), None) == 3
+    # one packed sequence past the limit (FP8 V): cols = 128 * (ceil(total_k / 128) + B)
+    pk = _args(Nk=fp8_over, v=v_fp8, cu_seqlens_q=1 << 24, cu_seqlens_k=1 << 24, total_q=256, total_k=fp8_over,
+               **big)
+    assert lib.attn_fwd_fp8pv(ctypes.byref(pk), None) == 2
+    # BF16 baseline: K/V rows addressed with 32-bit byte offsets per batch entry
+    fake = ctypes.c_void_p(1 << 24)
+    assert lib.attn_fwd_bf16(fake, fake, fake, fake, None, 1, 8, 8, 16, 1 << 20, 128, 0.1, 0, None) == 2
+
+
 def _dec_args(**kw):
     a = B.DecodeArgs()
     a.B, a.Hq, a.Hkv, a.nq, a.Nk, a.D = 2, 8, 2, 1, 1024, 128

@@ -380,3 +380,52 @@ def test_four_six_quantized_forward(gpu, name, wl, _):
     inp.q, inp.k, inp.v = inp.q.cuda(), inp.k.cuda(), inp.v.cuda()
     o, lse, stats = _check(gpu, inp, four_six=True)
     assert stats
+
+
+@pytest.mark.parametrize("entry", ["fwd_directp", "fwd_fp8pv"])
+def test_no_keys_gives_empty_softmax(gpu, entry):
+    # Rows that see no key have an empty softmax: O = 0 and LSE = -inf (the
+    # oracle's value), and the kernel must read nothing of K or V, whose
+    # buffers are then empty.  Dense Nk = 0, then a packed batch whose second
+    # sequence has queries but no keys, beside sequences that have both.
+    _say(f"{entry}: Nk = 0 and an empty key sequence")
+    vf = gpu.V_FP8
+    D, Hq, Hkv = 128, 4, 2
+    g = torch.Generator().manual_seed(77)
+    q = torch.randn(1, 300, Hq, D, generator=g).to(torch.bfloat16).cuda()
+    k = torch.empty(1, 0, Hkv, D, dtype=torch.bfloat16, device="cuda")
+    qq, kq = gpu.quant_nvfp4(q), gpu.quant_nvfp4(k)
+    vq = gpu.quant_v(torch.empty(1, 0, Hkv, D, dtype=torch.bfloat16, device="cuda"), vf)
+    fn = getattr(gpu, entry)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        o, lse, _ = fn(qq, kq, (vf, vq[0], vq[1], vq[2]), B=1, Nq=300, Nk=0, Hq=Hq, Hkv=Hkv, D=D,
+                       softmax_scale=D ** -0.5, out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        assert not o.float().any()
+        assert bool(torch.isneginf(lse).all())
+    # packed: query lengths [200, 130, 70], key lengths [180, 0, 300]
+    lq, lk = [200, 130, 70], [180, 0, 300]
+    cu_q = torch.tensor([0] + np.cumsum(lq).tolist(), dtype=torch.int32)
+    cu_k = torch.tensor([0] + np.cumsum(lk).tolist(), dtype=torch.int32)
+    qp = torch.randn(sum(lq), Hq, D, generator=g).to(torch.bfloat16)
+    kp = torch.randn(sum(lk), Hkv, D, generator=g).to(torch.bfloat16)
+    vp = torch.randn(sum(lk), Hkv, D, generator=g).to(torch.bfloat16)
+    qq, kq = gpu.quant_nvfp4(qp.cuda()), gpu.quant_nvfp4(kp.cuda())
+    vq = gpu.quant_v(vp.cuda(), vf, cu_seqlens=cu_k.cuda(), max_seqlen=max(lk))
+    o, lse, _ = fn(qq, kq, (vf, vq[0], vq[1], vq[2]), Hq=Hq, Hkv=Hkv, D=D, softmax_scale=D ** -0.5,
+                   cu_seqlens_q=cu_q.cuda(), cu_seqlens_k=cu_k.cuda(), max_seqlen_q=max(lq), max_seqlen_k=max(lk))
+    torch.cuda.synchronize()
+    o, lse = f32(o), f32(lse)
+    qf, kf, vf32 = qp.float().numpy(), kp.float().numpy(), vp.float().numpy()
+    amax = [float(np.abs(x).max()) for x in (qf, kf, vf32)]
+    p_format = "mxfp4" if entry == "fwd_directp" else "fp8"
+    for s in range(3):
+        q0, q1, k0, k1 = int(cu_q[s]), int(cu_q[s + 1]), int(cu_k[s]), int(cu_k[s + 1])
+        for h in range(Hq):
+            O, L = oracle_head(qf[q0:q1, h], kf[k0:k1, h // 2], vf32[k0:k1, h // 2], amax_q=amax[0], amax_k=amax[1],
+                               amax_v=amax[2], sigma=D ** -0.5, p_format=p_format, v_format="fp8", causal=False)
+            if k1 == k0:
+                assert not o[q0:q1, h].any() and bool(np.isneginf(lse[h, q0:q1]).all())
+                assert not O.any() and bool(np.isneginf(L).all())
+            else:
+                assert_close_outputs(o[q0:q1, h], lse[h, q0:q1], O, L, f"seq {s} head {h}")

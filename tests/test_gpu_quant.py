@@ -204,6 +204,26 @@ def test_v_varlen_small(gpu, fmt):
     _compare_v(codes, scales, ts, ora, fmt, lens, starts)
 
 
+def test_v_fp8_scale_non_power_of_two_amax(gpu):
+    # the hand-derived FP8 V fixture of the oracle's pins (amax = 49/32): the
+    # kernel's stored scale and codes must equal the literals bit for bit
+    from test_oracle_quant import FP8V_AMAX_PIN
+    _say("quant_v fp8, amax 49/32 fixture")
+    vals = torch.tensor(FP8V_AMAX_PIN["values"], dtype=torch.float32)
+    n = vals.numel()
+    v = torch.zeros((1, n, 1, 64), dtype=torch.float32)
+    v[0, :, 0, 0] = vals
+    v[0, :, 0, 5] = vals.flip(0) * 0.5
+    vb = v.to(torch.bfloat16)
+    assert torch.equal(vb.float(), v), "fixture values must be bf16-representable"
+    codes, scales, ts, cols = gpu.quant_v(vb.cuda(), gpu.V_FP8)
+    torch.cuda.synchronize()
+    assert ts.cpu().view(torch.int32).item() == FP8V_AMAX_PIN["s_v_bits"]
+    assert codes[0, 0, :n].cpu().tolist() == FP8V_AMAX_PIN["codes"]
+    vf = vb.float().numpy()
+    _compare_v(codes, scales, ts, _oracle_v(vf, "fp8", amax=np.abs(vf).max()), "fp8", [n], [0])
+
+
 @pytest.mark.parametrize("k", [2, 3, 5])
 def test_v_full_size_sampled(gpu, k):
     wl = synth.WORKLOADS[k]

@@ -136,3 +136,33 @@ def test_fp8_v_round_trip():
         np.testing.assert_array_equal(Q.dequant_v_fp8(codes, s_v), v.astype(np.float64))
     codes, s_v = Q.quant_v_fp8(np.zeros((3, 1, 4), np.float32))
     assert s_v == 1.0 and not codes.any()
+
+
+# FP8 V with a non-power-of-two amax.  The rule: enc = fl(448 / amax),
+# stored scale s_v = fl(1 / enc), code = E4M3(fl(v * enc)) -- the NVFP4 tensor
+# scale's pattern.  Hand-derived with exact rational arithmetic and
+# round-to-nearest-even to float32 / E4M3, for amax = 1.53125 = 49/32:
+#   448 / amax = 292.571428...; its float32 rounding enc = 0x43924925 (292.57144165).
+#   1 / enc = 0.00341796851...; float32 s_v = 0x3B5FFFFF, one ulp below
+#   amax / 448 = 7/2048 = 0x3B600000 (which the rule s_v = fl(amax / 448)
+#   would store).
+#   v = 91 * 2^-21: v * enc = 0.0126953134 > 13 * 2^-10, the midpoint of the
+#   E4M3 subnormals 6 * 2^-9 and 7 * 2^-9, so the code is 7; dividing by
+#   7/2048 instead would land exactly on the midpoint and tie to the even 6.
+#   1.0 -> 292.571 -> nearest 288 (1.125 * 2^8, code 0x79); -0.5 -> 146.29 ->
+#   144 (0xF1); 0.75 -> 219.43 -> 224 (1.75 * 2^7, 0x76); 2^-10 -> 0.2857 ->
+#   0.28125 (1.125 * 2^-2, 0x29); +-amax -> 448.00003 saturates to 448 (0x7E).
+FP8V_AMAX_PIN = {
+    "values": [49 / 32, -49 / 32, 1.0, -0.5, 91 * 2.0 ** -21, -91 * 2.0 ** -21, 0.0, 0.75, 2.0 ** -10],
+    "codes": [0x7E, 0xFE, 0x79, 0xF1, 0x07, 0x87, 0x00, 0x76, 0x29],
+    "s_v_bits": 0x3B5FFFFF,
+}
+
+
+def test_fp8_v_scale_non_power_of_two_amax():
+    v = np.array(FP8V_AMAX_PIN["values"], np.float32).reshape(3, 1, 3)
+    codes, s_v = Q.quant_v_fp8(v)
+    assert np.float32(s_v).view(np.uint32) == FP8V_AMAX_PIN["s_v_bits"]
+    assert codes.reshape(-1).tolist() == FP8V_AMAX_PIN["codes"]
+    # the stored scale is not amax / 448 rounded once (that would be 0x3B600000)
+    assert np.float32(np.float32(49 / 32) / np.float32(448)).view(np.uint32) == 0x3B600000
