@@ -261,6 +261,28 @@ size_t attn_fwd_ws_bytes(const attn_fwd_args* a);
 attn_status attn_fwd_directp(const attn_fwd_args* a, void* stream);
 
 /*
+ * attn_fwd_directp for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, kernels, results and errors as attn_fwd_directp, except
+ * that a->ws and a->ws_bytes are ignored: the float16 K operand tiles that
+ * attn_fwd_directp keeps in the caller's workspace go to a fixed device
+ * array inside the library, ATTN_NOALLOC_SCRATCH_BYTES per GPU, which every
+ * GPU the library runs on holds until the process ends.  The call itself
+ * allocates nothing (no hipMalloc, no hipFree, no allocating library call).
+ * Limit: attn_fwd_ws_bytes(a) <= ATTN_NOALLOC_SCRATCH_BYTES, i.e. Hkv * kcols
+ * <= 262159 at D = 128 (2 x 262159 at D = 64), e.g. 8 KV heads x 4 x 8192
+ * keys; beyond it the call returns ATTN_ERR_WORKSPACE and launches nothing.
+ * The array's address on a device is looked up once, on the first call on
+ * that device (the device of `stream`).  All calls on one GPU share its
+ * array, which keeps the last call's contents (each call writes every tile
+ * it reads before reading it, so nothing needs clearing): calls that overlap
+ * on one GPU -- on different streams, or from different host threads without
+ * ordering -- race and give undefined results.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (((size_t)64 << 20) + 4096)
+attn_status attn_fwd_directp_noalloc(const attn_fwd_args* a, void* stream);
+
+/*
  * FP8-P/V forward (the variant the pages keep for stable causal training;
  * summary page, "What the paper found"): identical to attn_fwd_directp
  * except that each probability is E4M3(2^(t - m')) with unit scale and V is

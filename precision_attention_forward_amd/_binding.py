@@ -104,6 +104,7 @@ EXPORTS = {
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "attn_fwd_ws_bytes": (ctypes.c_size_t, [ctypes.POINTER(FwdArgs)]),
     "attn_fwd_directp": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
+    "attn_fwd_directp_noalloc": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "attn_fwd_fp8pv": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "attn_fwd_directp_efq": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "attn_fwd_fp8pv_cast": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
@@ -306,7 +307,8 @@ def _fwd_lowp(entry, q, k, v, *, Hq, Hkv, D, softmax_scale, causal=False, B=None
         dbg_b, dbg_h = debug
         nq_dbg = Nq
         nk_pad = (Nk + 127) // 128 * 128
-        if entry in ("attn_fwd_directp", "attn_fwd_directp_efq", "attn_fwd_directp_mxqk", "attn_fwd_directp_efq_mxqk"):
+        if entry in ("attn_fwd_directp", "attn_fwd_directp_noalloc", "attn_fwd_directp_efq", "attn_fwd_directp_mxqk",
+                     "attn_fwd_directp_efq_mxqk"):
             dbg_codes = torch.zeros((nq_dbg, nk_pad // 2), dtype=torch.uint8, device=dev)
             dbg_scales = torch.zeros((nq_dbg, nk_pad // 32), dtype=torch.uint8, device=dev)
         else:
@@ -315,9 +317,10 @@ def _fwd_lowp(entry, q, k, v, *, Hq, Hkv, D, softmax_scale, causal=False, B=None
                       cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k, total_q=total_q, total_k=total_k, o=o,
                       o_dtype=OUT_F32 if out_dtype == torch.float32 else OUT_BF16, lse=lse,
                       dbg_codes=dbg_codes, dbg_scales=dbg_scales, dbg_b=dbg_b, dbg_h=dbg_h)
-    need = lib.attn_fwd_ws_bytes(ctypes.byref(a))
-    ws = (workspace or _default_ws).get(need, dev)
-    a.ws, a.ws_bytes = ws.data_ptr(), ws.numel()
+    if entry != "attn_fwd_directp_noalloc":      # (that one keeps its K tiles in the library's own array)
+        need = lib.attn_fwd_ws_bytes(ctypes.byref(a))
+        ws = (workspace or _default_ws).get(need, dev)
+        a.ws, a.ws_bytes = ws.data_ptr(), ws.numel()
     if events is not None:
         a.prof_event_begin = events[0].cuda_event
         a.prof_event_end = events[1].cuda_event
@@ -328,6 +331,13 @@ def _fwd_lowp(entry, q, k, v, *, Hq, Hkv, D, softmax_scale, causal=False, B=None
 def fwd_directp(q, k, v, **kw):
     """Direct-P forward: MXFP4 P, V FP8 or MXFP4 (noncausal)."""
     return _fwd_lowp("attn_fwd_directp", q, k, v, **kw)
+
+
+def fwd_directp_noalloc(q, k, v, **kw):
+    """attn_fwd_directp without a caller workspace: the library keeps the K
+    operand tiles in a fixed device array (ATTN_NOALLOC_SCRATCH_BYTES per GPU)
+    and the call allocates nothing.  Calls that overlap on one GPU race."""
+    return _fwd_lowp("attn_fwd_directp_noalloc", q, k, v, **kw)
 
 
 def fwd_fp8pv(q, k, v, **kw):

@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/attn_fp4.h"
 #include "common.h"
 
@@ -167,7 +169,8 @@ size_t attn_fwd_ws_bytes(const attn_fwd_args* a) {
   return (size_t)(2 * a->D) * (size_t)(a->Hkv * fwd_kcols(a)) + 256;
 }
 
-static attn_status validate_fwd(const attn_fwd_args* a, bool allow_causal, int pf, bool mx = false) {
+static attn_status validate_fwd(const attn_fwd_args* a, bool allow_causal, int pf, bool mx = false,
+                                bool own_ws = false) {
   if (a == nullptr) return ATTN_ERR_INVALID_ARGUMENT;
   if (a->B < 0 || a->Hq <= 0 || a->Hkv <= 0 || a->Nq < 0 || a->Nk < 0) return ATTN_ERR_INVALID_ARGUMENT;
   if (a->D != 64 && a->D != 128) return ATTN_ERR_INVALID_ARGUMENT;
@@ -214,23 +217,61 @@ static attn_status validate_fwd(const attn_fwd_args* a, bool allow_causal, int p
   const int64_t qb = ((int64_t)a->Nq + WG_Q - 1) / WG_Q + 16;
   if ((int64_t)a->B * a->Hq * qb >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
   const size_t need = attn_fwd_ws_bytes(a);
+  if (own_ws) return need <= ATTN_NOALLOC_SCRATCH_BYTES ? ATTN_OK : ATTN_ERR_WORKSPACE;
   if (a->ws == nullptr || a->ws_bytes < need || !aligned(a->ws, 256)) return ATTN_ERR_WORKSPACE;
+  return ATTN_OK;
+}
+
+// Scratch of attn_fwd_directp_noalloc: a fixed device array in place of the
+// caller's workspace for the float16 K operand tiles.  In host code `scratch`
+// names a host-side stand-in, not device memory: its device address is looked
+// up once per device (hipGetSymbolAddress, with that device current) and only
+// that address is passed to the kernels.
+static __device__ __align__(256) uint8_t scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+constexpr int SCRATCH_MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[SCRATCH_MAX_DEVICES];
+
+static attn_status scratch_address(hipStream_t st, void** out) {
+  int dev = 0, cur = 0;
+  hipError_t e = hipStreamGetDevice(st, &dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return ATTN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_status(e);
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e);
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return hip_status(e);
+    if (ptr == nullptr) return hip_status(hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
   return ATTN_OK;
 }
 
 // mx: the MX-native Q/K mode (MXFP4 Q/K codes with E8M0 bytes, no tensor
 // scales; exact encoders), whose K pre-pass packs FP4 operand tiles instead
 // of expanding K to FP16.
-static attn_status run_fwd_lowp(const attn_fwd_args* a, void* stream, int pf, int enc, bool mx = false) {
-  attn_status s = validate_fwd(a, pf == 1, pf, mx);
+static attn_status run_fwd_lowp(const attn_fwd_args* a, void* stream, int pf, int enc, bool mx = false,
+                                bool own_ws = false) {
+  attn_status s = validate_fwd(a, pf == 1, pf, mx, own_ws);
   if (s != ATTN_OK) return s;
   hipStream_t st = (hipStream_t)stream;
   const bool varlen = a->cu_seqlens_q != nullptr;
   const int64_t kcols = fwd_kcols(a);
-  _Float16* khat = (_Float16*)a->ws;
+  void* ws = a->ws;
+  if (own_ws && (s = scratch_address(st, &ws)) != ATTN_OK) return s;
+  _Float16* khat = (_Float16*)ws;
   const int64_t nk_pad = roundup(a->Nk, 128);
   hipError_t e = mx ? launch_pack_k_mx(a->k.codes, a->k.scales, a->Hkv, a->B, a->Nk, a->Nk, a->cu_seqlens_k, nk_pad,
-                                       kcols, a->D, pf, (uint8_t*)a->ws, st)
+                                       kcols, a->D, pf, (uint8_t*)ws, st)
                     : launch_expand_k(a->k.codes, a->k.scales, a->Hkv, a->B, a->Nk, a->Nk, a->cu_seqlens_k, nk_pad,
                                       kcols, a->D, pf, khat, st);
   if (e != hipSuccess) return hip_status(e);
@@ -278,6 +319,9 @@ static attn_status run_fwd_lowp(const attn_fwd_args* a, void* stream, int pf, in
 }
 
 attn_status attn_fwd_directp(const attn_fwd_args* a, void* stream) { return run_fwd_lowp(a, stream, 0, 0); }
+attn_status attn_fwd_directp_noalloc(const attn_fwd_args* a, void* stream) {
+  return run_fwd_lowp(a, stream, 0, 0, false, true);
+}
 attn_status attn_fwd_fp8pv(const attn_fwd_args* a, void* stream) { return run_fwd_lowp(a, stream, 1, 0); }
 attn_status attn_fwd_directp_efq(const attn_fwd_args* a, void* stream) { return run_fwd_lowp(a, stream, 0, 1); }
 attn_status attn_fwd_fp8pv_cast(const attn_fwd_args* a, void* stream) { return run_fwd_lowp(a, stream, 1, 1); }

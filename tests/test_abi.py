@@ -267,3 +267,20 @@ def test_mx_qk_entry_points_reject_bad_arguments(lib):
     assert lib.attn_fwd_fp8pv_cast_mxqk(ctypes.byref(_args(v=B._VTensor(1, 1 << 24, 1 << 24, 1 << 24), ws=1 << 24,
                                                            ws_bytes=need, **noscale)), None) == 2
     assert lib.attn_fwd_fp8pv_cast_mxqk(None, None) == 1
+
+
+def test_noalloc_validation(lib):
+    # The forward without a caller workspace keeps the K operand tiles in a
+    # fixed device array of ATTN_NOALLOC_SCRATCH_BYTES: past it the call
+    # returns ATTN_ERR_WORKSPACE; its other checks are attn_fwd_directp's.  All
+    # of these fail on the host before the array or the GPU is touched.
+    cap = (64 << 20) + 4096
+    fn = lambda **kw: lib.attn_fwd_directp_noalloc(ctypes.byref(_args(**kw)), None)
+    over = _args(B=4, Hq=32, Hkv=8, Nq=8192, Nk=8192 + 128)
+    assert lib.attn_fwd_ws_bytes(ctypes.byref(over)) > cap
+    assert lib.attn_fwd_directp_noalloc(ctypes.byref(over), None) == 3
+    assert lib.attn_fwd_ws_bytes(ctypes.byref(_args(B=4, Hq=32, Hkv=8, Nq=8192, Nk=8192))) <= cap
+    assert fn(causal=1) == 2
+    assert fn(D=96) == 1
+    assert fn(o=None) == 1
+    assert lib.attn_fwd_directp_noalloc(None, None) == 1
