@@ -44,7 +44,7 @@ LN2 = math.log(2.0)
 
 def attn_lowp_head(q_raw, k_raw, gq, gk, v_hat, sigma, p_format="mxfp4",
                    causal=False, q_index=None, return_p=False, encoder="exact",
-                   p_given=None, return_pre=False):
+                   p_given=None, return_pre=False, return_tiles=False):
     """One (batch, head): tiled Direct-P (``p_format="mxfp4"``) or FP8-P
     (``p_format="fp8"``) forward.
 
@@ -69,6 +69,10 @@ def attn_lowp_head(q_raw, k_raw, gq, gk, v_hat, sigma, p_format="mxfp4",
                 the exact encoders, the position 2**M (y + b) for the cast,
                 -inf where masked), and the block maxima xmax of t - m',
                 [nq, ceil(Nk/32)] (-inf for blocks with no live key)
+    return_tiles  append a dict of the scales the accumulation ran at:
+                "m_tile" [nq, ceil(Nk/128)] the running max m' each tile's
+                probabilities are relative to (-inf for a tile with no live
+                key), and the final "m" and "l" [nq]
     """
     if encoder not in ("exact", "loglin"):
         raise ValueError(encoder)
@@ -90,6 +94,7 @@ def attn_lowp_head(q_raw, k_raw, gq, gk, v_hat, sigma, p_format="mxfp4",
     p_e8m0 = np.zeros((nq, nblk), np.uint8) if (return_p and p_format == "mxfp4") else None
     pre_all = np.full((nq, Nk), -np.inf) if return_pre else None
     xmax_all = np.full((nq, nblk), -np.inf) if return_pre else None
+    m_tile = np.full((nq, (Nk + TILE - 1) // TILE), -np.inf) if return_tiles else None
     for t0 in range(0, Nk, TILE):
         t1 = min(t0 + TILE, Nk)
         keys = np.arange(t0, t1)
@@ -150,14 +155,17 @@ def attn_lowp_head(q_raw, k_raw, gq, gk, v_hat, sigma, p_format="mxfp4",
         l = alpha * l + p_hat.sum(axis=1)
         o = alpha[:, None] * o + p_hat @ v_hat[t0:t1]
         m = m_new
+        if return_tiles:
+            m_tile[:, t0 // TILE] = np.where(any_live, m_new, -np.inf)
     with np.errstate(divide="ignore", invalid="ignore"):
         O = np.where(l[:, None] > 0, o / np.where(l > 0, l, 1.0)[:, None], 0.0)
         lse = np.where(l > 0, LN2 * (m + np.log2(np.where(l > 0, l, 1.0))), -np.inf)
+    tiles = ({"m_tile": m_tile, "m": m, "l": l},) if return_tiles else ()
     if return_pre:
-        return O, lse, p_codes, p_e8m0, pre_all, xmax_all
+        return (O, lse, p_codes, p_e8m0, pre_all, xmax_all) + tiles
     if return_p:
-        return O, lse, p_codes, p_e8m0
-    return O, lse
+        return (O, lse, p_codes, p_e8m0) + tiles
+    return (O, lse) + tiles
 
 
 def attn_exact_head(q, k, v, sigma, causal=False, q_index=None):

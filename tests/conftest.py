@@ -23,3 +23,10 @@ def gpu():
     import precision_attention_forward_amd as paf
     paf.load_library()          # raises if the shared library is missing
     return paf
+
+
+def pytest_sessionfinish(session, exitstatus):
+    # stop the oracle's worker processes, if a parity check started them
+    mod = sys.modules.get("oracle_pool")
+    if mod is not None:
+        mod.shutdown()

@@ -133,50 +133,6 @@ def test_tie_check_block_exponent():
         check_code_choices(gc, ge, oc, oe, pre, xmax, "mxfp4", "exact", live)
 
 
-def test_tie_check_row_slack():
-    # a code rounded the other way 1e-3 (relative) from its boundary: beyond
-    # the plain window, inside a row slack of 2e-3 log2 units (1.4e-3 relative)
-    gc, ge, oc, oe, pre, xmax = _case("mxfp4", "exact", seed=7)
-    live = np.isfinite(pre)
-    i, j = np.argwhere(live & (oc > 1) & (oc < 6))[0]
-    c = int(oc[i, j])
-    pre[i, j] = 0.5 * (F.e2m1_decode(c) + F.e2m1_decode(c + 1)) * (1 - 1e-3)
-    oc = oc.copy()
-    oc[i, j] = c
-    gc = gc.copy()
-    gc[i, j] = c + 1
-    with pytest.raises(AssertionError):
-        check_code_choices(gc, ge, oc, oe, pre, xmax, "mxfp4", "exact", live)
-    slack = np.zeros(gc.shape[0])
-    slack[i] = 2e-3
-    assert check_code_choices(gc, ge, oc, oe, pre, xmax, "mxfp4", "exact", live, row_slack=slack) == (0, 1)
-    slack[i] = 1e-3                               # 0.7e-3 relative: too narrow
-    with pytest.raises(AssertionError):
-        check_code_choices(gc, ge, oc, oe, pre, xmax, "mxfp4", "exact", live, row_slack=slack)
-
-
-def test_tie_check_row_slack_cast():
-    # the E2M1 cast: a position 0.01 code units from its boundary (2^M = 2 code
-    # units per log2 unit) needs a row slack of at least 0.005 - NEAR_TIE_POS / 2
-    gc, ge, oc, oe, pre, xmax = _case("mxfp4", "loglin", seed=8)
-    live = np.isfinite(pre)
-    i, j = np.argwhere(live & (oc > 1) & (oc < 6))[0]
-    c = int(oc[i, j])
-    pre[i, j] = c + 0.5 - 0.01
-    oc = oc.copy()
-    oc[i, j] = c
-    gc = gc.copy()
-    gc[i, j] = c + 1
-    with pytest.raises(AssertionError):
-        check_code_choices(gc, ge, oc, oe, pre, xmax, "mxfp4", "loglin", live)
-    slack = np.zeros(gc.shape[0])
-    slack[i] = 0.005
-    assert check_code_choices(gc, ge, oc, oe, pre, xmax, "mxfp4", "loglin", live, row_slack=slack) == (0, 1)
-    slack[i] = 0.004
-    with pytest.raises(AssertionError):
-        check_code_choices(gc, ge, oc, oe, pre, xmax, "mxfp4", "loglin", live, row_slack=slack)
-
-
 def test_bwd_check_zero_below_float32_normal_range():
     from helpers import check_bwd_codes
     from oracle import backward as OB
@@ -206,3 +162,129 @@ def test_bwd_check_zero_below_float32_normal_range():
     gc3[0, 1] = 0x30
     with pytest.raises(AssertionError):
         check_bwd_codes(gc3, ge, x, oc, ge, eps, 1, live, p=p)
+
+
+# ---- the oracle-only bounds that widen the pure-oracle comparison ---------
+
+def _perturbed_codes(pf, enc, pre, xmax, oe, live, rng, tol_rel, tol_pos, tol_int):
+    """Codes a float32 implementation could produce: every unrounded value
+    moved by up to 0.9 of its near-tie window, every block max by up to 0.9
+    of NEAR_INT, then rounded again."""
+    fmt = "e2m1" if pf == "mxfp4" else "e4m3"
+    nq, nk = pre.shape
+    ge = None
+    shift = np.zeros((nq, nk))
+    if pf == "mxfp4":
+        # (a block whose max is the running max has xmax = 0 exactly on both sides)
+        xm = np.where(xmax == 0.0, 0.0, xmax + rng.uniform(-0.9, 0.9, xmax.shape) * tol_int)
+        e_new = np.where(np.isfinite(xmax), np.maximum(np.floor(np.where(np.isfinite(xm), xm, 0.0)) - 2, -127),
+                         oe.astype(np.int64) - 127)
+        ge = (e_new + 127).astype(np.uint8)
+        shift = np.repeat(oe.astype(np.int64) - 127 - e_new, 32, axis=1)[:, :nk]
+    fin = np.isfinite(pre)
+    u = rng.uniform(-0.9, 0.9, pre.shape)
+    if enc == "exact":
+        x = np.where(fin, pre * np.exp2(shift) * (1 + u * tol_rel), 0.0)
+        gc = F.e2m1_encode(x) if fmt == "e2m1" else F.e4m3_encode(x)
+    else:
+        x = np.where(fin, pre + (2.0 if fmt == "e2m1" else 8.0) * shift + u * tol_pos, -1.0)
+        gc = loglin_round(x, fmt)
+    return np.where(live, gc, 0).astype(np.uint8), ge
+
+
+@pytest.mark.parametrize("pf,enc", [("mxfp4", "exact"), ("mxfp4", "loglin"), ("fp8", "exact"), ("fp8", "loglin")])
+def test_tie_bound_covers_every_near_tie_rounding(monkeypatch, pf, enc):
+    import helpers
+    tol_rel, tol_pos, tol_int = 0.02, 0.05, 0.05      # wide windows: many candidates per row
+    monkeypatch.setattr(helpers, "NEAR_TIE_REL", tol_rel)
+    monkeypatch.setattr(helpers, "NEAR_TIE_POS", tol_pos)
+    monkeypatch.setattr(helpers, "NEAR_INT", tol_int)
+    rng = np.random.default_rng(11)
+    q, k, v = _head(rng, nq=10, nk=333, d=16)
+    qi = np.arange(10) * 33 + 20
+    for causal in (False, True):
+        res = A.attn_lowp_head(q, k, 1.0, 1.0, v, 0.7, pf, causal=causal, q_index=qi, encoder=enc,
+                               return_pre=True, return_tiles=True)
+        O, L, oc, oe, pre, xmax, tiles = res
+        live = np.isfinite(pre)
+        ob, lb, frac = helpers.tie_flip_bound(pre, oc, oe, xmax, tiles, O, v, pf, enc, live)
+        assert (ob > 0).any() and (frac < 0.5).all()
+        moved = 0.0
+        for trial in range(12):
+            gc, ge = _perturbed_codes(pf, enc, pre, xmax, oe, live, rng, tol_rel, tol_pos, tol_int)
+            O2, L2 = A.attn_lowp_head(q, k, 1.0, 1.0, v, 0.7, pf, causal=causal, q_index=qi, encoder=enc,
+                                      p_given=(gc, ge))
+            assert (np.abs(O2 - O) <= ob + 1e-12).all()
+            assert (np.abs(L2 - L) <= lb + 1e-12).all()
+            moved = max(moved, float(np.abs(O2 - O).max()))
+        assert moved > 0, "no perturbed rounding changed any code: the test is vacuous"
+
+
+def test_tie_bound_zero_without_candidates():
+    import helpers
+    rng = np.random.default_rng(12)
+    q, k, v = _head(rng, nq=4, nk=200, d=16)
+    res = A.attn_lowp_head(q, k, 1.0, 1.0, v, 0.7, "mxfp4", return_pre=True, return_tiles=True)
+    O, L, oc, oe, pre, xmax, tiles = res
+    # no unrounded value lies within the (tiny) default windows of a boundary here
+    ob, lb, frac = helpers.tie_flip_bound(pre, oc, oe, xmax, tiles, O, v, "mxfp4", "exact", np.isfinite(pre))
+    assert not ob.any() and not lb.any()
+
+
+def test_pure_compare_bars():
+    from helpers import PureCompare, O_MAX_ABS
+    O = np.ones((3, 4))
+    L = np.array([1.0, 2.0, -np.inf])
+    pc = PureCompare("t")
+    pc.add(O + 0.5 * O_MAX_ABS, L, O, L)
+    with pytest.raises(AssertionError):
+        PureCompare("t").add(O + 2 * O_MAX_ABS, L, O, L)
+    # the widened bound admits the same error on a row with candidates
+    ob = np.zeros_like(O)
+    ob[1] = 2 * O_MAX_ABS
+    pc2 = PureCompare("t")
+    pc2.add(O + np.array([[0.0], [2.5 * O_MAX_ABS], [0.0]]), L, O, L, ob, np.zeros(3))
+    assert pc2.rows_widened == 1
+    with pytest.raises(AssertionError):
+        PureCompare("t").add(O, L + np.array([0.0, 1e-3, 0.0]), O, L)
+
+
+def test_bwd_flip_bound_covers_perturbed_operands():
+    from helpers import BWD_TIE_FACTOR, bwd_flip_delta
+    from oracle import backward as OB
+    rng = np.random.default_rng(13)
+    N, D = 70, 16
+    q = rng.standard_normal((N, D))
+    k = rng.standard_normal((N, D))
+    v = rng.standard_normal((N, D))
+    o = rng.standard_normal((N, D)) * 0.3
+    do = rng.standard_normal((N, D))
+    lse = np.log(np.exp(0.5 * q @ k.T * np.tril(np.ones((N, N)))).sum(1))
+    args = (q, k, 1.0, 1.0, v, o, do, lse, 0.5, True)
+    dq, dk, dv, pre = OB.attn_bwd_head(*args, return_pre=True)
+    eps = 3e-3                                            # a wide error bound: many candidates
+    pq, pk = pre["q"], pre["k"]
+    live_q, live_k = pq["p"] > 0, pk["p"] > 0
+    e_q = np.full(pq["ds"].shape, eps)
+    e_k = np.full(pk["p"].shape, eps)
+    d_dsq = bwd_flip_delta(pq["codes"], pq["exps"], pq["ds"], e_q, 1, live_q)
+    d_pt = bwd_flip_delta(pk["codes_p"], pk["exps_p"], pk["p"], e_k, 0, live_k)
+    d_dsk = bwd_flip_delta(pk["codes_ds"], pk["exps_ds"], pk["ds"], e_k, 0, live_k)
+    b_dq = 0.5 * d_dsq @ np.abs(k)
+    b_dv = d_pt.T @ np.abs(do)
+    b_dk = 0.5 * d_dsk.T @ np.abs(q)
+    moved = 0.0
+    for trial in range(10):
+        # operands a float32 implementation could round: each exact value moved
+        # by up to 0.9 of BWD_TIE_FACTOR times its error bound, then MX-quantized
+        pert = lambda x: x * (1 + rng.uniform(-0.9, 0.9, x.shape) * BWD_TIE_FACTOR * eps)
+        _, cq, eq = OB.mx_e4m3(pert(pq["ds"]), axis=1)
+        _, cp, ep = OB.mx_e4m3(pert(pk["p"]), axis=0)
+        _, ck, ek = OB.mx_e4m3(pert(pk["ds"]), axis=0)
+        g = {"ds_q": (cq, eq + 127), "p_t": (cp, ep + 127), "ds_k": (ck, ek + 127)}
+        dq2, dk2, dv2 = OB.attn_bwd_head(*args, given=g)
+        assert (np.abs(dq2 - dq) <= b_dq + 1e-12).all()
+        assert (np.abs(dv2 - dv) <= b_dv + 1e-12).all()
+        assert (np.abs(dk2 - dk) <= b_dk + 1e-12).all()
+        moved = max(moved, float(np.abs(dv2 - dv).max()))
+    assert moved > 0
