@@ -82,6 +82,14 @@ __device__ inline float e2m1_decode(uint32_t c) {
   return (c & 8u) ? -mag : mag;
 }
 
+// IEEE-2019 maximum of two / three floats (v_maximum3_f32 on gfx950): the
+// larger operand, NaN if either is NaN.  Unlike fmax, its operands need no
+// canonicalizing, which matters for matrix-instruction results.
+__device__ inline float fmax2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ inline float fmax3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
 // Wave-wide max (DPP/permute based; 64 lanes).
 __device__ inline float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));

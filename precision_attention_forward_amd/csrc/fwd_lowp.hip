@@ -478,14 +478,16 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
       if (ks + 1 < KS) { a0 = n0; a1 = n1; }
     }
   };
-  // max of the 16 scores of S sub-tile st, as a shallow tree (short dependency chains)
+  // max of the 16 scores of S sub-tile st, as a shallow tree (short dependency
+  // chains).  IEEE-2019 maximum (v_maximum3_f32): the scores hold no NaN, and
+  // unlike fmax it needs no canonicalizing copies of the matrix results.
   auto tile_max = [&](int st) {
-    const float a = __builtin_fmaxf(__builtin_fmaxf(s[st][0], s[st][1]), s[st][2]);
-    const float b = __builtin_fmaxf(__builtin_fmaxf(s[st][3], s[st][4]), s[st][5]);
-    const float c = __builtin_fmaxf(__builtin_fmaxf(s[st][6], s[st][7]), s[st][8]);
-    const float d = __builtin_fmaxf(__builtin_fmaxf(s[st][9], s[st][10]), s[st][11]);
-    const float e = __builtin_fmaxf(__builtin_fmaxf(s[st][12], s[st][13]), s[st][14]);
-    return __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(a, b), c), __builtin_fmaxf(__builtin_fmaxf(d, e), s[st][15]));
+    const float a = fmax3(s[st][0], s[st][1], s[st][2]);
+    const float b = fmax3(s[st][3], s[st][4], s[st][5]);
+    const float c = fmax3(s[st][6], s[st][7], s[st][8]);
+    const float d = fmax3(s[st][9], s[st][10], s[st][11]);
+    const float e = fmax3(s[st][12], s[st][13], s[st][14]);
+    return fmax3(fmax3(a, b, c), fmax3(d, e, s[st][15]), -__builtin_inff());
   };
   // masking of S (tail of the sequence, causal diagonal) for tile j
   auto mask = [&](int j) {
@@ -593,16 +595,18 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
     if (u < 4) {                                 // block maxima of S(t-1): sub-tile 3 joins the
       if (u == 3) {                              // maxima of sub-tiles 0..2 taken a tile earlier
         bm[0] = bmp[0];
-        bm[1] = __builtin_fmaxf(bmp[1], tile_max(3));
+        bm[1] = fmax2(bmp[1], tile_max(3));
       }
     } else if (u == 4) {                         // row statistics
-      float rmax = __builtin_fmaxf(bm[0], bm[1]);
+      float rmax = fmax2(bm[0], bm[1]);
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax), __float_as_uint(rmax), false, false);
-      rmax = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));   // max with lane ^ 32
+      rmax = fmax2(__uint_as_float(sw[0]), __uint_as_float(sw[1]));   // max with lane ^ 32
       const float tmax = rmax * cc;              // max of fl(S*c) (c > 0)
-      const float m_new = __builtin_fmaxf(m_run, tmax);
-      const bool row_dead = m_new == -__builtin_inff();
-      alpha_pend = row_dead ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      // Every row sees a live key in its first tile (the key-less case exits
+      // before the loop; causal rows always see key 0), so m' is finite from
+      // the first tile on, and alpha = 2^(m - m') is 0 there (m = -inf).
+      const float m_new = fmax2(m_run, tmax);
+      alpha_pend = __builtin_amdgcn_exp2f(m_run - m_new);
       // alpha is exactly 1 wherever the running max did not move; the rescale
       // is skipped when that holds for the whole wave
       rescale_any = __builtin_amdgcn_ballot_w64(alpha_pend != 1.0f) != 0;
@@ -611,13 +615,14 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
       for (int c = 0; c < 2; ++c) {
         if (PF == PF_MXFP4) {
           const float xmax = bm[c] * cc - m_new;   // fl(fl(S*c) - m'), no contraction
-          const float fl = __builtin_floorf(xmax);
-          const int e = fl < -125.0f ? -127 : (int)fl - 2;   // also -inf (no live key)
-          psw[c] = e + 127;
-          me[c] = row_dead ? 0.0f : m_new + (float)e;
+          // e = max(floor(xmax) - 2, -127); a block without a live key has
+          // xmax = -inf and gets -127
+          const float ef = fmax2(__builtin_floorf(xmax), -125.0f) - 2.0f;
+          psw[c] = (int)ef + 127;
+          me[c] = m_new + ef;
         } else {
           psw[c] = 127;
-          me[c] = row_dead ? 0.0f : m_new;
+          me[c] = m_new;
         }
         if (ENC) mb[c] = CAST_BIAS - CAST_MUL * me[c];   // 2^M me is exact
       }
@@ -667,7 +672,7 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
       }
     } else if (u >= 45) {                        // maxima of S(t) sub-tiles 0..2 for the next tile
       if (u == 45) bmn[0] = tile_max(0);
-      else if (u == 46) bmn[0] = __builtin_fmaxf(bmn[0], tile_max(1));
+      else if (u == 46) bmn[0] = fmax2(bmn[0], tile_max(1));
       else bmn[1] = tile_max(2);
     } else {                                     // rescale slice
       const int r = u - 37;
@@ -707,7 +712,7 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   if (n_tiles > 1) copy_k(1);
   qk2(0, 0);
   qk2(0, 2);
-  bmp[0] = __builtin_fmaxf(tile_max(0), tile_max(1));
+  bmp[0] = fmax2(tile_max(0), tile_max(1));
   bmp[1] = tile_max(2);
   dma_wait();
   phase_barrier();
@@ -730,7 +735,7 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
     const int j = t - 1;                       // tile being encoded
     if (j * KEY_TILE + KEY_TILE > len_k || (CAUSAL && j * KEY_TILE + KEY_TILE - 1 > q0)) {
       mask(j);
-      bmp[0] = __builtin_fmaxf(tile_max(0), tile_max(1));   // maxima taken before the mask
+      bmp[0] = fmax2(tile_max(0), tile_max(1));   // maxima taken before the mask
       bmp[1] = tile_max(2);
     }
     const uint8_t* sV = smem + L::V_BASE + rk1 * L::V_SLOT;                   // V(t-2): (t-2) mod 3 = (t+1) mod 3
