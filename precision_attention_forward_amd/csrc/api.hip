@@ -347,8 +347,8 @@ attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, 
   if (nq > 0 && (q == nullptr || o == nullptr || !aligned(q, 16) || !aligned(o, 16))) return ATTN_ERR_INVALID_ARGUMENT;
   if (nk > 0 && (k == nullptr || v == nullptr || !aligned(k, 16) || !aligned(v, 16))) return ATTN_ERR_INVALID_ARGUMENT;
   if (lse != nullptr && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARGUMENT;
-  // K and V rows are addressed with 32-bit byte offsets from each batch entry's base
-  if ((int64_t)Nk * Hkv * D * 2 >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
+  // the rows of one 128-key tile are addressed with 32-bit byte offsets from the tile's base
+  if ((int64_t)KEY_TILE * Hkv * D * 2 >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
   if ((int64_t)B * Hq * ((Nq + WG_Q - 1) / WG_Q) >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
   return hip_status(launch_fwd_bf16(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, D, softmax_scale, causal != 0,
                                     (hipStream_t)stream));

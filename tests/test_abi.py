@@ -191,9 +191,10 @@ def test_fwd_offset_limits(lib):
     pk = _args(Nk=fp8_over, v=v_fp8, cu_seqlens_q=1 << 24, cu_seqlens_k=1 << 24, total_q=256, total_k=fp8_over,
                **big)
     assert lib.attn_fwd_fp8pv(ctypes.byref(pk), None) == 2
-    # BF16 baseline: K/V rows addressed with 32-bit byte offsets per batch entry
+    # BF16 baseline: the rows of a 128-key tile are addressed with 32-bit byte
+    # offsets (128 * Hkv * D * 2 < 2^31)
     fake = ctypes.c_void_p(1 << 24)
-    assert lib.attn_fwd_bf16(fake, fake, fake, fake, None, 1, 8, 8, 16, 1 << 20, 128, 0.1, 0, None) == 2
+    assert lib.attn_fwd_bf16(fake, fake, fake, fake, None, 1, 1 << 16, 1 << 16, 16, 16, 128, 0.1, 0, None) == 2
 
 
 def _dec_args(**kw):

@@ -44,3 +44,26 @@ def test_bf16_forward(gpu, idx):
             rel = np.linalg.norm(o[b, :, h] - oe) / np.linalg.norm(oe)
             assert rel < 1e-2, (b, h, rel)
             assert np.max(np.abs(lse[b, h] - le)) < 1e-4
+
+
+def test_bf16_forward_full_size_sampled(gpu):
+    # the Wan2.1-14B shape the benchmark times (B=1, H=40, N=32760, D=128):
+    # 48 sampled query rows of the first and the last head, all keys
+    print("[case] bf16 full-size wan14b", flush=True)
+    wl = synth.WORKLOADS[2]
+    inp = synth.generate(wl, "cuda")
+    o, lse = gpu.fwd_bf16(inp.q, inp.k, inp.v, inp.sigma, causal=False)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.random.default_rng(5).integers(0, wl.N, 44), [0, 255, 256, wl.N - 1]]))
+    ridx = torch.as_tensor(rows, device="cuda")
+    for h in (0, wl.Hq - 1):
+        q = inp.q[0, ridx, h].double().cpu().numpy()
+        k = inp.k[0, :, h].double().cpu().numpy()
+        v = inp.v[0, :, h].double().cpu().numpy()
+        oe, le = OA.attn_exact_head(q, k, v, inp.sigma, q_index=rows)
+        og = o[0, ridx, h].float().cpu().numpy()
+        rel = np.linalg.norm(og - oe) / np.linalg.norm(oe)
+        assert rel < 1e-2, (h, rel)
+        assert np.max(np.abs(lse[0, h, ridx].cpu().numpy() - le)) < 1e-4
+    del inp, o, lse
+    torch.cuda.empty_cache()
