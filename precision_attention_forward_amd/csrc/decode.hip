@@ -35,13 +35,20 @@
 //    LDS once per step, so that every wave encodes with the running max m' of
 //    its own tile: the codes of one sequential pass, which splitting the keys
 //    over independent workgroups would not give.
-//  * Each wave loads its tiles from HBM straight into registers two steps
-//    ahead (no LDS staging: no other wave reads them).
+//  * Each wave streams its own tiles.  K codes and scales go by direct
+//    global->LDS copies into two buffers of the wave, two steps ahead; the
+//    16-byte chunks of each code row are XOR-swizzled so that the 16 rows of
+//    one operand read fall on distinct banks.  V goes straight into registers
+//    one step ahead (issued as soon as the step's P.V has read the previous
+//    tile).  At most 256 registers and ~75 KB of LDS per workgroup let two
+//    workgroups share a CU, i.e. two waves per SIMD, so that one wave's
+//    matrix products overlap the other's K decode and softmax.
 //  * At the end the four partials are rescaled to the final max and summed
 //    through LDS.
 #include "common.h"
 #include "dec_params.h"
 #include "fwd_params.h"
+#include "pipeline.h"
 
 namespace attn {
 
@@ -61,25 +68,46 @@ __host__ __device__ inline int dec_key(int st, int r) {
   return st < 4 ? 16 * g + 4 * st + i : 64 + 16 * g + 4 * (st - 4) + i;
 }
 
-// Operands of one 128-key tile, as one lane holds them.
-template <int D, int VF>
-struct DecBuf {
-  u32x4 kc[8];                               // K codes of the lane's key in sub-tile st, channels of its group
-  uint32_t ks[8];                            // their E4M3 block scales (D/64 bytes)
-  u32x4 va[D / 16][VF == VF_FP8 ? 2 : 1];    // V^T operand per 16 channels
-  uint32_t vs[VF == VF_MXFP4 ? D / 16 : 1];  // MXFP4 V: E8M0 bytes of the tile's four blocks
-};
+// LDS bytes of one K tile: 128 rows of D/2 code bytes, then 128 rows of D/16
+// E4M3 block-scale bytes.
+template <int D>
+constexpr int dec_ktile_bytes() {
+  return KEY_TILE * (D / 2 + D / 16);
+}
+// Copy instructions per K tile (1 KB of codes each; the scales in one 1 KB
+// copy at D = 128, two 256-byte copies at D = 64) and load instructions per V
+// tile (per 16 rows of V^T: two 16-byte loads for FP8, one 16-byte code load
+// and one 4-byte scale load for MXFP4).
+template <int D>
+constexpr int dec_k_copies() {
+  return D / 16 + (D == 128 ? 1 : 2);
+}
+template <int D>
+constexpr int dec_v_loads() {
+  return 2 * (D / 16);
+}
+// Position of 16-byte chunk c of K code row k (D = 128: four chunks per row)
+// in LDS: c ^ kswz(k).  The 16 lanes of one operand read take keys
+// 4 st + i + 32 j (MXFP4 P) or 16 j + 4 st + i (FP8 P), i, j in 0..3; the
+// swizzle sends the four values of j to four different chunks, so the 16
+// reads hit 16 different 16-byte bank groups of a 256-byte window.
+__host__ __device__ constexpr int dec_kswz(int k) { return ((k >> 4) ^ (k >> 5)) & 3; }
 
 template <int D, int PF, int VF, bool CAUSAL, bool DEBUG>
-__global__ void __launch_bounds__(256, 1) decode_kernel(DecParams p) {
+__global__ void __launch_bounds__(256, 2) decode_kernel(DecParams p) {
   constexpr int KS = D / 32;     // k-steps (32 channels) of the S MFMA
   constexpr int DT = D / 16;     // 16-row tiles of O^T
   constexpr int HALF = D / 2;    // code bytes per row
   constexpr int GC = D / 4;      // channels of one lane group
+  constexpr int KT = dec_ktile_bytes<D>();
+  constexpr int KSC = KEY_TILE * HALF;                              // scale rows within a K tile
+  constexpr int NK = dec_k_copies<D>(), NV = dec_v_loads<D>();
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   float* sM = reinterpret_cast<float*>(smem);                       // [2][DEC_WAVES][16] tile maxima
-  float* sO = sM + 2 * DEC_WAVES * DEC_Q;                           // [DEC_WAVES][DT][4][64] partial O
-  float* sL = sO + DEC_WAVES * DT * 4 * 64;                         // [DEC_WAVES][64] partial l
+  float* sL = sM + 2 * DEC_WAVES * DEC_Q;                           // [DEC_WAVES][64] partial l
+  uint8_t* sKall = smem + (2 * DEC_WAVES * DEC_Q + DEC_WAVES * 64) * 4;   // [DEC_WAVES][2][KT] K tiles
+  float* sO = reinterpret_cast<float*>(sKall);                      // [DEC_WAVES][DT][4][64] partial O, after the loop
+  static_assert(DEC_WAVES * DT * 4 * 64 * 4 <= DEC_WAVES * 2 * KT, "the partial O fits the K tiles");
 
   // ---- workgroup -> (sequence, KV head, query group)
   const int lin = blockIdx.x;
@@ -129,53 +157,69 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(DecParams p) {
   const uint8_t* khead = p.k_codes + ((int64_t)b * p.Hkv + hk) * p.Nk * HALF;
   const uint8_t* shead = p.k_scales + ((int64_t)b * p.Hkv + hk) * p.Nk * (D / 16);
   const int64_t col0 = (int64_t)b * p.nk_pad;
-  const uint8_t* vhead = VF == VF_MXFP4 ? p.v_codes + (int64_t)hk * D * (p.cols / 2) + col0 / 2
-                                        : p.v_codes + (int64_t)hk * D * p.cols + col0;
+  const int64_t vcols = VF == VF_MXFP4 ? p.cols / 2 : p.cols;           // bytes of a V^T row of the cache
+  const uint8_t* vhead = VF == VF_MXFP4 ? p.v_codes + (int64_t)hk * D * vcols + col0 / 2
+                                        : p.v_codes + (int64_t)hk * D * vcols + col0;
   const uint8_t* vshead = VF == VF_MXFP4 ? p.v_scales + (int64_t)hk * D * (p.cols / 32) + col0 / 32 : nullptr;
-  const uint32_t vrow = (uint32_t)rr * (uint32_t)(VF == VF_MXFP4 ? p.cols / 2 : p.cols);   // V^T row rr of a 16-row tile
-  const uint32_t vdt = 16u * (uint32_t)(VF == VF_MXFP4 ? p.cols / 2 : p.cols);             // next 16 rows
 
-  // K rows of the lane in each sub-tile (loop invariant).  Keys past the
-  // sequence but inside its cache (the capacity is whole 128-key tiles) are
-  // read and masked later, so no per-lane clamping is needed.
-  uint32_t koff[8], soff[8];
+  auto tile_of = [&](int s) {
+    const int jc = s * DEC_WAVES + wave;
+    return jc < n_tiles ? jc : n_tiles - 1;   // past the end: the last tile again (a cache hit)
+  };
+
+  // K tiles: copied into two LDS buffers of this wave, two steps ahead.
+  // Keys past the sequence but inside its cache (the capacity is whole
+  // 128-key tiles) are read and masked later.
+  uint8_t* sK = sKall + wave * 2 * KT;
+  const uint32_t sK_lds = lds_address(sK);
+  uint32_t kcp_off[4];                  // D = 128: lane's source offset in a copy, per swizzle value
+#pragma unroll
+  for (int f = 0; f < 4; ++f) kcp_off[f] = (uint32_t)((lane >> 2) * HALF + 16 * ((lane & 3) ^ f));
+  auto copy_k = [&](int s, int buf) {
+    const int key0 = tile_of(s) * KEY_TILE;
+    const uint8_t* kb = khead + (int64_t)key0 * HALF;
+    const uint8_t* sb = shead + (int64_t)key0 * (D / 16);
+    const uint32_t dst = sK_lds + buf * KT;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      // copy i: 1 KB of code rows (16 keys at D = 128, 32 at D = 64)
+      const uint32_t off = D == 128 ? kcp_off[dec_kswz(16 * i)] : (uint32_t)(16 * lane);
+      dma16(kb + 1024 * i, off, dst + 1024 * i);
+    }
+    if (D == 128) {
+      dma16(sb, (uint32_t)(16 * lane), dst + KSC);
+    } else {
+      dma4(sb, (uint32_t)(4 * lane), dst + KSC);
+      dma4(sb + 256, (uint32_t)(4 * lane), dst + KSC + 256);
+    }
+  };
+  // the lane's operand reads of sub-tile st within a K tile (loop invariant)
+  uint32_t kr_off[8], sr_off[8];
 #pragma unroll
   for (int st = 0; st < 8; ++st) {
     const int kl = dec_key<PF>(st, rr);
-    koff[st] = (uint32_t)(kl * HALF + g * (GC / 2));
-    soff[st] = (uint32_t)(kl * (D / 16) + g * (GC / 16));
+    kr_off[st] = D == 128 ? (uint32_t)(kl * HALF + 16 * (g ^ dec_kswz(kl))) : (uint32_t)(kl * HALF + 8 * g);
+    sr_off[st] = (uint32_t)(KSC + kl * (D / 16) + g * (GC / 16));
   }
-  const uint32_t voff = vrow + 16u * (uint32_t)g;
-  const uint32_t vsoff = (uint32_t)rr * (uint32_t)(p.cols / 32);
 
-  auto load = [&](DecBuf<D, VF>& bf, int s) {
-    int jc = s * DEC_WAVES + wave;
-    jc = jc < n_tiles ? jc : n_tiles - 1;        // past the end: the last tile again (a cache hit)
-    const int key0 = jc * KEY_TILE;
-    const uint8_t* kb = khead + (int64_t)key0 * HALF;
-    const uint8_t* sb = shead + (int64_t)key0 * (D / 16);
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      if (D == 128) {
-        bf.kc[st] = *reinterpret_cast<const u32x4*>(kb + koff[st]);
-        bf.ks[st] = *reinterpret_cast<const uint16_t*>(sb + soff[st]);
-      } else {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(kb + koff[st]);
-        bf.kc[st] = u32x4{w[0], w[1], 0u, 0u};
-        bf.ks[st] = sb[soff[st]];
-      }
-    }
+  // V tile: straight into registers, one step ahead
+  u32x4 va[DT][VF == VF_FP8 ? 2 : 1];    // V^T operand per 16 channels
+  uint32_t vs[VF == VF_MXFP4 ? DT : 1];  // MXFP4 V: E8M0 bytes of the tile's four blocks
+  const uint32_t voff = (uint32_t)rr * (uint32_t)vcols + 16u * (uint32_t)g;   // V^T row rr of a 16-row tile
+  const uint32_t vsoff = (uint32_t)rr * (uint32_t)(p.cols / 32);
+  auto load_v = [&](int s) {
+    const int key0 = tile_of(s) * KEY_TILE;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       if (VF == VF_FP8) {
-        const uint8_t* vb = vhead + key0 + (int64_t)dt * vdt;
-        bf.va[dt][0] = *reinterpret_cast<const u32x4*>(vb + voff);
-        bf.va[dt][VF == VF_FP8 ? 1 : 0] = *reinterpret_cast<const u32x4*>(vb + voff + 64);
+        const uint8_t* vb = vhead + key0 + (int64_t)(16 * dt) * vcols;
+        va[dt][0] = *reinterpret_cast<const u32x4*>(vb + voff);
+        va[dt][VF == VF_FP8 ? 1 : 0] = *reinterpret_cast<const u32x4*>(vb + voff + 64);
       } else {
-        const uint8_t* vb = vhead + key0 / 2 + (int64_t)dt * vdt;
-        bf.va[dt][0] = *reinterpret_cast<const u32x4*>(vb + voff);
-        const uint8_t* vsb = vshead + key0 / 32 + (int64_t)dt * 16 * (p.cols / 32);
-        bf.vs[VF == VF_MXFP4 ? dt : 0] = *reinterpret_cast<const uint32_t*>(vsb + vsoff);
+        const uint8_t* vb = vhead + key0 / 2 + (int64_t)(16 * dt) * vcols;
+        va[dt][0] = *reinterpret_cast<const u32x4*>(vb + voff);
+        const uint8_t* vsb = vshead + key0 / 32 + (int64_t)(16 * dt) * (p.cols / 32);
+        vs[VF == VF_MXFP4 ? dt : 0] = *reinterpret_cast<const uint32_t*>(vsb + vsoff);
       }
     }
   };
@@ -193,19 +237,36 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(DecParams p) {
   float m_w = -__builtin_inff();     // max the wave's partial O / l refer to
 
   // ---- one step: tile j = 4 s + wave
-  auto body = [&](int s, const DecBuf<D, VF>& bf) {
+  auto body = [&](int s) {
     const int j = s * DEC_WAVES + wave;
     const bool live = j < n_tiles;             // wave-uniform
     f32x4 sacc[8];
     float bm = -__builtin_inff();
     if (live) {
-      // S^T = K Q^T, eight 16-key sub-tiles
+      // S^T = K Q^T, eight 16-key sub-tiles, K from this wave's LDS tile
+      const uint8_t* kt = sK + (s & 1) * KT;
+      u32x4 kc_next;
+      uint32_t ksc_next;
+      auto read_k = [&](int st) {   // operands of sub-tile st, read one sub-tile ahead
+        if (D == 128) {
+          kc_next = *reinterpret_cast<const u32x4*>(kt + kr_off[st]);
+          ksc_next = *reinterpret_cast<const uint16_t*>(kt + sr_off[st]);
+        } else {
+          const u32x2 w = *reinterpret_cast<const u32x2*>(kt + kr_off[st]);
+          kc_next = u32x4{w[0], w[1], 0u, 0u};
+          ksc_next = kt[sr_off[st]];
+        }
+      };
+      read_k(0);
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
-        const f16x2 scp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bf.ks[st], 1.0f, false);
+        const u32x4 kc = kc_next;
+        const uint32_t ksc = ksc_next;
+        if (st < 7) read_k(st + 1);
+        const f16x2 scp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ksc, 1.0f, false);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const uint32_t w = bf.kc[st][ks];
+          const uint32_t w = kc[ks];
           const _Float16 sc = (ks >> 1) == 0 ? scp[0] : scp[1];   // block of 16 channels
           const f16x2 s2v = {sc, sc};
           const f16x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2v;
@@ -220,14 +281,13 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(DecParams p) {
       // mask keys past the sequence and (causal) past each row's position
       const int key0 = j * KEY_TILE;
       if (key0 + KEY_TILE > len_k || (CAUSAL && key0 + KEY_TILE - 1 > len_k - p.nq)) {
+        // live keys of the lane's row: key < lim (one compare per score)
+        const int lim = (CAUSAL ? min(len_k, my_pos + 1) : len_k) - key0;
 #pragma unroll
         for (int st = 0; st < 8; ++st)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = key0 + dec_key<PF>(st, 4 * g + i);
-            const bool dead = key >= len_k || (CAUSAL && key > my_pos);
-            if (dead) sacc[st][i] = -__builtin_inff();
-          }
+          for (int i = 0; i < 4; ++i)
+            sacc[st][i] = dec_key<PF>(st, 4 * g + i) < lim ? sacc[st][i] : -__builtin_inff();
       }
 #pragma unroll
       for (int st = 0; st < 8; ++st)
@@ -318,13 +378,13 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(DecParams p) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       if (VF == VF_MXFP4) {
-        const u32x4 x = bf.va[dt][0];
+        const u32x4 x = va[dt][0];
         const i32x8 a = {(int)x[0], (int)x[1], (int)x[2], (int)x[3], 0, 0, 0, 0};
-        const int vsc = (int)(bf.vs[VF == VF_MXFP4 ? dt : 0] >> (8 * g));   // block g of the tile
+        const int vsc = (int)(vs[VF == VF_MXFP4 ? dt : 0] >> (8 * g));   // block g of the tile
         oacc[dt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, pw, oacc[dt], 4, PF == PF_MXFP4 ? 4 : 0, 0,
                                                                     vsc, 0, psc);
       } else {
-        const u32x4 x = bf.va[dt][0], y = bf.va[dt][VF == VF_FP8 ? 1 : 0];
+        const u32x4 x = va[dt][0], y = va[dt][VF == VF_FP8 ? 1 : 0];
         const i32x8 a = {(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
         oacc[dt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, pw, oacc[dt], 0, PF == PF_MXFP4 ? 4 : 0, 0, 127,
                                                                     0, psc);
@@ -332,24 +392,28 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(DecParams p) {
     }
   };
 
-  // ---- the key loop: three register buffers, loads two steps ahead
+  // ---- the key loop.  Per step the wave issues, in this order, the V loads
+  // of the next step (into the registers the step's P.V has just read) and
+  // the K copies of the step after (into the LDS buffer the step's S has
+  // read).  Memory operations complete in order, so at the top of step s the
+  // K tile of s has landed once no more than NV + NK loads are outstanding
+  // (those of V(s) and K(s + 1)); the compiler waits for V(s) itself before
+  // the P.V products.
   if (n_steps > 0) {
-    DecBuf<D, VF> b0, b1, b2;
-    load(b0, 0);
-    load(b1, 1);
-    int s = 0;
-    for (;;) {
-      load(b2, s + 2);
-      body(s, b0);
-      if (++s == n_steps) break;
-      load(b0, s + 2);
-      body(s, b1);
-      if (++s == n_steps) break;
-      load(b1, s + 2);
-      body(s, b2);
-      if (++s == n_steps) break;
+    copy_k(0, 0);
+    load_v(0);
+    copy_k(1, 1);
+    for (int s = 0; s < n_steps; ++s) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NV + NK) : "memory");
+      body(s);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the step's LDS reads are done
+      load_v(s + 1);
+      copy_k(s + 2, s & 1);
     }
   }
+  // no copy may still be writing the K tiles, which the partial O reuses
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
   // ---- combine the four partials at the final max, O = o / l, LSE
   const float f = m_w == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_w - m_run);
@@ -395,7 +459,7 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(DecParams p) {
 
 template <int D>
 constexpr int dec_lds_bytes() {
-  return (2 * DEC_WAVES * DEC_Q + DEC_WAVES * (D / 16) * 4 * 64 + DEC_WAVES * 64) * 4;
+  return (2 * DEC_WAVES * DEC_Q + DEC_WAVES * 64) * 4 + DEC_WAVES * 2 * dec_ktile_bytes<D>();
 }
 
 template <int D, int PF, int VF, bool CAUSAL, bool DEBUG>
