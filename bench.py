@@ -408,7 +408,7 @@ def decode_main(args, torch, paf, synth):
     nq = inp.q.shape[1]
     k = paf.quant_nvfp4(inp.k)
     vf = paf.V_FP8 if wl.v_format == "fp8" else paf.V_MXFP4
-    vq = paf.quant_v(inp.v, vf)
+    vq = paf.quant_v_cache(inp.v, vf)
     v = (vf, vq[0], vq[1], vq[2])
     seqlens = inp.seqlens.to(dev)
     fn = paf.decode_directp if wl.p_format == "mxfp4" else paf.decode_fp8pv

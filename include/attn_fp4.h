@@ -188,6 +188,29 @@ attn_status attn_quant_v(const void* v_bf16, int32_t B, int32_t Nk, int32_t Hkv,
                          uint8_t* codes, uint8_t* scales, float* tensor_scale,
                          void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Quantize a decode step's V cache: the same codes, E8M0 bytes and FP8
+ * tensor scale as attn_quant_v of the same dense tensor (summary page, "What
+ * the paper found": FP4 or FP8 V), stored as the decode kernels read it
+ * (the cached keys and values of the Colfax Research feed's post on
+ * FlashAttention-4 decode): one block of D key-contiguous rows per
+ * (sequence, KV head, 128-key tile), the tiles of one (sequence, head) in
+ * order, so that every tile is one contiguous read.
+ *   v_bf16 : dense [B, Nk, Hkv, D]; Nk is the cache capacity, a multiple of
+ *            128 (ATTN_ERR_INVALID_ARGUMENT otherwise)
+ * Outputs, with t = (b * Hkv + h) * (Nk / 128) + key / 128 and j = key % 128:
+ *   FP8  : codes [B, Hkv, Nk/128, D, 128]: code of (b, key, h, d) at byte
+ *          (t * D + d) * 128 + j; tensor_scale as attn_quant_v
+ *   MXFP4: codes [B, Hkv, Nk/128, D, 64]: byte (t * D + d) * 64 + j / 2, key
+ *          j even in the low nibble; scales [B, Hkv, Nk/128, D, 4]: E8M0 of
+ *          keys 32 i .. 32 i + 31 of the tile at byte (t * D + d) * 4 + i
+ * ws as attn_quant_v (attn_quant_ws_bytes()).  Nothing is read past the
+ * input and nothing written past these sizes.
+ */
+attn_status attn_quant_v_cache(const void* v_bf16, int32_t B, int32_t Nk, int32_t Hkv, int32_t D,
+                               int32_t format, uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                               void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Forward
  * --------------------------------------------------------------------- */
@@ -379,8 +402,9 @@ attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, 
  *           (attn_quant_nvfp4 of a bf16 [B, nq, Hq, D] tensor)
  *   k     : NVFP4 K cache, head-major: rows ordered [B, Hkv, Nk]
  *           (attn_quant_nvfp4 of a bf16 [B, Hkv, Nk, D] tensor)
- *   v     : V cache as attn_quant_v writes it for a dense bf16
- *           [B, Nk, Hkv, D] tensor (cols = B * roundup(Nk, 128))
+ *   v     : V cache as attn_quant_v_cache writes it for a dense bf16
+ *           [B, Nk, Hkv, D] tensor (one contiguous block per sequence, KV
+ *           head and 128-key tile)
  *   seqlens_k : nullable device int32 [B], the number of valid cache
  *           entries of each sequence (values are clamped to [0, Nk]); NULL
  *           means Nk for every sequence.  The kernel reads whole 128-key
@@ -394,8 +418,9 @@ attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, 
  *   o     : [B, nq, Hq, D] (o_dtype); lse: nullable float [B, Hq, nq]
  * A row with no visible key gets O = 0 and LSE = -inf.
  * Limits: D in {64, 128}; Hq % Hkv == 0; 1 <= nq; the cache capacity Nk a
- * multiple of 128 (ATTN_ERR_INVALID_ARGUMENT otherwise); D * B * Nk below
- * 2^31 (ATTN_ERR_UNSUPPORTED otherwise).  attn_decode_fp8pv requires FP8 V.  Optional probability dump
+ * multiple of 128 (ATTN_ERR_INVALID_ARGUMENT otherwise); B * Hkv *
+ * ceil(Hq / Hkv * nq / 16) below 2^31 (ATTN_ERR_UNSUPPORTED otherwise).
+ * attn_decode_fp8pv requires FP8 V.  Optional probability dump
  * of (dbg_b, dbg_h): codes [nq, roundup(Nk,128)/2] (MXFP4 P) or
  * [nq, roundup(Nk,128)] (FP8 P), E8M0 bytes [nq, roundup(Nk,128)/32].
  * prof_event_begin/end (hipEvent_t, nullable) are recorded around the kernel.

@@ -102,6 +102,9 @@ EXPORTS = {
     "attn_quant_v": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "attn_quant_v_cache": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "attn_fwd_ws_bytes": (ctypes.c_size_t, [ctypes.POINTER(FwdArgs)]),
     "attn_fwd_directp": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "attn_fwd_directp_noalloc": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
@@ -235,6 +238,32 @@ def quant_v(v, fmt, cu_seqlens=None, max_seqlen=None):
     _check(lib.attn_quant_v(_ptr(v), B, Nk, Hkv, D, _ptr(cu_seqlens), total, fmt, _ptr(codes), _ptr(scales),
                             _ptr(ts), _ptr(ws), ws.numel(), _stream()))
     return codes, scales, ts, cols
+
+
+def quant_v_cache(v, fmt):
+    """Quantize a decode step's V cache (bf16 [B, Nk, Hkv, D], Nk a multiple
+    of 128) to FP8 E4M3 or MXFP4 with the values of quant_v, stored as the
+    decode kernels read it: one block of D key-contiguous rows per (sequence,
+    KV head, 128-key tile).  Returns (codes [B, Hkv, Nk/128, D, 128 or 64],
+    scales [B, Hkv, Nk/128, D, 4]|None, tensor_scale|None)."""
+    lib = load_library()
+    _need_cuda(v)
+    if v.dtype != torch.bfloat16:
+        raise AttnError("quant_v_cache expects bfloat16")
+    B, Nk, Hkv, D = v.shape
+    nt = Nk // 128
+    if fmt == V_FP8:
+        codes = torch.empty((B, Hkv, nt, D, 128), dtype=torch.uint8, device=v.device)
+        scales = None
+        ts = torch.empty(1, dtype=torch.float32, device=v.device)
+    else:
+        codes = torch.empty((B, Hkv, nt, D, 64), dtype=torch.uint8, device=v.device)
+        scales = torch.empty((B, Hkv, nt, D, 4), dtype=torch.uint8, device=v.device)
+        ts = None
+    ws = torch.empty(lib.attn_quant_ws_bytes(), dtype=torch.uint8, device=v.device)
+    _check(lib.attn_quant_v_cache(_ptr(v), B, Nk, Hkv, D, fmt, _ptr(codes), _ptr(scales), _ptr(ts), _ptr(ws),
+                                  ws.numel(), _stream()))
+    return codes, scales, ts
 
 
 class Workspace:
@@ -381,7 +410,7 @@ def _decode(entry, q, k, v, *, B, Hq, Hkv, nq, Nk, D, softmax_scale, causal=Fals
     """Shared driver of the decode entry points.  q: NVFP4 (codes, scales,
     tensor_scale) of a [B, nq, Hq, D] tensor; k: the same of the head-major
     K cache [B, Hkv, Nk, D]; v: (format, codes, scales|None,
-    tensor_scale|None) from quant_v of the [B, Nk, Hkv, D] V cache;
+    tensor_scale|None) from quant_v_cache of the [B, Nk, Hkv, D] V cache;
     seqlens_k: optional device int32 [B].  Returns (O [B, nq, Hq, D],
     LSE [B, Hq, nq], (dump codes, dump scales))."""
     lib = load_library()

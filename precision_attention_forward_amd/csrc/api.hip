@@ -17,7 +17,7 @@ hipError_t launch_quant_nvfp4(const void* x, int64_t rows, int D, const float* p
                               uint8_t* scales, float* tensor_scale, bool four_six, hipStream_t st);
 hipError_t launch_quant_v(const void* v, int B, int Nk, int Hkv, int D, const int32_t* cu_k, int max_len, int64_t cols,
                           int fmt, const float* partials, int np, uint8_t* codes, uint8_t* scales, float* tensor_scale,
-                          hipStream_t st);
+                          bool cache_layout, hipStream_t st);
 hipError_t launch_expand_k(const uint8_t* codes, const uint8_t* scales, int H, int B, int N, int max_len,
                            const int32_t* cu, int64_t n_pad, int64_t cols, int D, int pf, _Float16* out,
                            hipStream_t st);
@@ -155,7 +155,33 @@ attn_status attn_quant_v(const void* v_bf16, int32_t B, int32_t Nk, int32_t Hkv,
   }
   if (B == 0) return ATTN_OK;
   return hip_status(launch_quant_v(v_bf16, B, Nk, Hkv, D, cu_seqlens_k, Nk, cols, format, partials, np, codes, scales,
-                                   tensor_scale, st));
+                                   tensor_scale, false, st));
+}
+
+attn_status attn_quant_v_cache(const void* v_bf16, int32_t B, int32_t Nk, int32_t Hkv, int32_t D, int32_t format,
+                               uint8_t* codes, uint8_t* scales, float* tensor_scale, void* ws, size_t ws_bytes,
+                               void* stream) {
+  if (B < 0 || Nk < 0 || Nk % 128 != 0 || Hkv <= 0 || (D != 64 && D != 128)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (format != ATTN_V_FP8_E4M3 && format != ATTN_V_MXFP4) return ATTN_ERR_INVALID_ARGUMENT;
+  const int64_t tokens = (int64_t)B * Nk;
+  if (format == ATTN_V_FP8_E4M3 && (tensor_scale == nullptr || !aligned(tensor_scale, 4)))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (tokens > 0 && (v_bf16 == nullptr || codes == nullptr || !aligned(v_bf16, 16) || !aligned(codes, 16)))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (tokens > 0 && format == ATTN_V_MXFP4 && (scales == nullptr || !aligned(scales, 4)))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (ws == nullptr || ws_bytes < QUANT_WS || !aligned(ws, 16)) return ATTN_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  float* partials = (float*)ws;
+  int np = 0;
+  hipError_t e;
+  if (format == ATTN_V_FP8_E4M3) {
+    e = launch_amax(v_bf16, tokens * Hkv * (int64_t)D, partials, &np, st);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (B == 0) return ATTN_OK;
+  return hip_status(launch_quant_v(v_bf16, B, Nk, Hkv, D, nullptr, Nk, (int64_t)B * Nk, format, partials, np, codes,
+                                   scales, tensor_scale, true, st));
 }
 
 // Workspace of the forward: the K fp16 operand tiles, kcols columns per KV head.
@@ -480,8 +506,9 @@ static attn_status validate_decode(const attn_decode_args* a, int pf) {
   if (a->v.format != ATTN_V_FP8_E4M3 && a->v.format != ATTN_V_MXFP4) return ATTN_ERR_INVALID_ARGUMENT;
   if (pf == 1 && a->v.format != ATTN_V_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
   if (a->o_dtype != ATTN_OUT_BF16 && a->o_dtype != ATTN_OUT_F32) return ATTN_ERR_INVALID_ARGUMENT;
-  const int64_t cols = (int64_t)a->B * roundup(a->Nk, 128);
-  if ((int64_t)a->D * cols >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
+  // one workgroup per (sequence, KV head, 16 query rows): the grid's x size
+  const int64_t qg = ((int64_t)(a->Hq / a->Hkv) * a->nq + 15) / 16;
+  if ((int64_t)a->B * a->Hkv * qg >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
   if (a->seqlens_k != nullptr && !aligned(a->seqlens_k, 4)) return ATTN_ERR_INVALID_ARGUMENT;
   const int64_t nq = (int64_t)a->B * a->nq, nk = (int64_t)a->B * a->Nk;
   const attn_nvfp4_tensor* t[2] = {&a->q, &a->k};
@@ -533,7 +560,6 @@ static attn_status run_decode(const attn_decode_args* a, void* stream, int pf) {
   p.Nk = a->Nk;
   p.QG = (int)(((int64_t)(a->Hq / a->Hkv) * a->nq + 15) / 16);   // 16 query rows per workgroup
   p.nk_pad = roundup(a->Nk, 128);
-  p.cols = (int64_t)a->B * p.nk_pad;
   p.sigma = a->softmax_scale;
   p.dbg_codes = a->dbg_p_codes;
   p.dbg_scales = a->dbg_p_scales;

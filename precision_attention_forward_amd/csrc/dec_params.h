@@ -10,8 +10,8 @@ struct DecParams {
   const uint8_t* q_scales;
   const uint8_t* k_codes;   // NVFP4 K cache, head-major: [B][Hkv][Nk][D/2], scales [B][Hkv][Nk][D/16]
   const uint8_t* k_scales;
-  const uint8_t* v_codes;   // V cache in the transposed layout of the V quantizer ([Hkv][D][cols], keys
-  const uint8_t* v_scales;  // contiguous; sequence b starts at column b * nk_pad)
+  const uint8_t* v_codes;   // V cache: [B][Hkv][Nk/128] blocks of D key-contiguous rows (FP8 128 bytes,
+  const uint8_t* v_scales;  // MXFP4 64 bytes per row; MXFP4 scales [B][Hkv][Nk/128][D][4])
   const float* gq;
   const float* gk;
   const float* sv;
@@ -21,7 +21,6 @@ struct DecParams {
   float* lse;               // [B][Hq][nq] or null
   int B, Hq, Hkv, nq, Nk, QG;
   int64_t nk_pad;
-  int64_t cols;
   float sigma;
   uint8_t* dbg_codes;       // probability dump of (dbg_b, dbg_h): [nq][dbg_ld] codes, [nq][dbg_ld/32] E8M0
   uint8_t* dbg_scales;

@@ -40,7 +40,11 @@
 //    16-byte chunks of each code row are XOR-swizzled so that the 16 rows of
 //    one operand read fall on distinct banks.  V goes straight into registers
 //    one step ahead (issued as soon as the step's P.V has read the previous
-//    tile).  At most 256 registers and ~75 KB of LDS per workgroup let two
+//    tile), from the decode cache layout in which each (sequence, KV head,
+//    128-key tile) is one contiguous block: the V^T rows of a tile in the
+//    forward's layout lie a whole cache row apart, and reading such 128-byte
+//    pieces streams far below the rate of contiguous blocks.  The K copies
+//    carry the non-temporal hint (the cache is read once per step).  At most 256 registers and ~75 KB of LDS per workgroup let two
 //    workgroups share a CU, i.e. two waves per SIMD, so that one wave's
 //    matrix products overlap the other's K decode and softmax.
 //  * At the end the four partials are rescaled to the final max and summed
@@ -152,16 +156,13 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecParams p) {
     }
   }
 
-  // ---- per-lane load offsets (bytes, below 2^31; the host checks D * cols)
+  // ---- tile bases (64-bit) and per-lane offsets within a tile
   const int rr = lane & 15;
   const uint8_t* khead = p.k_codes + ((int64_t)b * p.Hkv + hk) * p.Nk * HALF;
   const uint8_t* shead = p.k_scales + ((int64_t)b * p.Hkv + hk) * p.Nk * (D / 16);
-  const int64_t col0 = (int64_t)b * p.nk_pad;
-  const int64_t vcols = VF == VF_MXFP4 ? p.cols / 2 : p.cols;           // bytes of a V^T row of the cache
-  const uint8_t* vhead = VF == VF_MXFP4 ? p.v_codes + (int64_t)hk * D * vcols + col0 / 2
-                                        : p.v_codes + (int64_t)hk * D * vcols + col0;
-  const uint8_t* vshead = VF == VF_MXFP4 ? p.v_scales + (int64_t)hk * D * (p.cols / 32) + col0 / 32 : nullptr;
-
+  // V cache: one block of D key-contiguous rows (V^T) per (sequence, KV head, 128-key tile)
+  constexpr int VROWB = VF == VF_MXFP4 ? KEY_TILE / 2 : KEY_TILE;       // code bytes of a block row
+  const int64_t vtile0 = ((int64_t)b * p.Hkv + hk) * (p.Nk / KEY_TILE);
   auto tile_of = [&](int s) {
     const int jc = s * DEC_WAVES + wave;
     return jc < n_tiles ? jc : n_tiles - 1;   // past the end: the last tile again (a cache hit)
@@ -184,13 +185,13 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecParams p) {
     for (int i = 0; i < D / 16; ++i) {
       // copy i: 1 KB of code rows (16 keys at D = 128, 32 at D = 64)
       const uint32_t off = D == 128 ? kcp_off[dec_kswz(16 * i)] : (uint32_t)(16 * lane);
-      dma16(kb + 1024 * i, off, dst + 1024 * i);
+      dma16_nt(kb + 1024 * i, off, dst + 1024 * i);
     }
     if (D == 128) {
-      dma16(sb, (uint32_t)(16 * lane), dst + KSC);
+      dma16_nt(sb, (uint32_t)(16 * lane), dst + KSC);
     } else {
-      dma4(sb, (uint32_t)(4 * lane), dst + KSC);
-      dma4(sb + 256, (uint32_t)(4 * lane), dst + KSC + 256);
+      dma4_nt(sb, (uint32_t)(4 * lane), dst + KSC);
+      dma4_nt(sb + 256, (uint32_t)(4 * lane), dst + KSC + 256);
     }
   };
   // the lane's operand reads of sub-tile st within a K tile (loop invariant)
@@ -205,22 +206,17 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecParams p) {
   // V tile: straight into registers, one step ahead
   u32x4 va[DT][VF == VF_FP8 ? 2 : 1];    // V^T operand per 16 channels
   uint32_t vs[VF == VF_MXFP4 ? DT : 1];  // MXFP4 V: E8M0 bytes of the tile's four blocks
-  const uint32_t voff = (uint32_t)rr * (uint32_t)vcols + 16u * (uint32_t)g;   // V^T row rr of a 16-row tile
-  const uint32_t vsoff = (uint32_t)rr * (uint32_t)(p.cols / 32);
+  const uint32_t voff = (uint32_t)(rr * VROWB + 16 * g);   // row rr of a 16-row group, the lane's 16 bytes
   auto load_v = [&](int s) {
-    const int key0 = tile_of(s) * KEY_TILE;
+    const int64_t t = vtile0 + tile_of(s);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      if (VF == VF_FP8) {
-        const uint8_t* vb = vhead + key0 + (int64_t)(16 * dt) * vcols;
-        va[dt][0] = *reinterpret_cast<const u32x4*>(vb + voff);
+      const uint8_t* vb = p.v_codes + t * (D * VROWB) + 16 * dt * VROWB;
+      va[dt][0] = *reinterpret_cast<const u32x4*>(vb + voff);
+      if (VF == VF_FP8)
         va[dt][VF == VF_FP8 ? 1 : 0] = *reinterpret_cast<const u32x4*>(vb + voff + 64);
-      } else {
-        const uint8_t* vb = vhead + key0 / 2 + (int64_t)(16 * dt) * vcols;
-        va[dt][0] = *reinterpret_cast<const u32x4*>(vb + voff);
-        const uint8_t* vsb = vshead + key0 / 32 + (int64_t)(16 * dt) * (p.cols / 32);
-        vs[VF == VF_MXFP4 ? dt : 0] = *reinterpret_cast<const uint32_t*>(vsb + vsoff);
-      }
+      else
+        vs[VF == VF_MXFP4 ? dt : 0] = *reinterpret_cast<const uint32_t*>(p.v_scales + (t * D + 16 * dt + rr) * 4);
     }
   };
 

@@ -38,6 +38,20 @@ __device__ inline void dma4(const void* base, uint32_t off, uint32_t lds) {
                : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(base)
                : "memory");
 }
+// The same two copies with the non-temporal hint (nt): for data that is read
+// exactly once, such as a decode step's KV cache.
+__device__ inline void dma16_nt(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(base)
+               : "memory");
+}
+__device__ inline void dma4_nt(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2 nt"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(base)
+               : "memory");
+}
 // Wait until every global load (and LDS copy) this wave issued has landed.
 __device__ inline void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

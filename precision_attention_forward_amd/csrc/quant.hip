@@ -186,7 +186,11 @@ __global__ void __launch_bounds__(256) quant_nvfp4_kernel(const uint16_t* __rest
 // Pass 2 (V): one workgroup per (128-key tile, kv head, sequence).  The tile
 // is staged in LDS, then each thread encodes one (channel, 32-key block) and
 // writes it key-contiguous.  FMT 0 = FP8 E4M3 (per-tensor scale), 1 = MXFP4.
-template <int FMT, int D>
+// LAYOUT 0: the transposed layout [Hkv][D][cols] of the forward; LAYOUT 1:
+// the decode cache, one block of D key-contiguous rows per (sequence, KV
+// head, 128-key tile), tiles of a (sequence, head) consecutive (dense input,
+// nk_pad = Nk).
+template <int FMT, int D, int LAYOUT>
 __global__ void __launch_bounds__(256) quant_v_kernel(const uint16_t* __restrict__ v, int Nk, int Hkv,
                                                       const int32_t* __restrict__ cu_k, int64_t nk_pad, int64_t cols,
                                                       const float* __restrict__ partials, int np,
@@ -223,6 +227,17 @@ __global__ void __launch_bounds__(256) quant_v_kernel(const uint16_t* __restrict
 #pragma unroll
     for (int j = 0; j < 32; ++j) x[j] = bf16_bits_to_f32(tileb[(blk * 32 + j) * D + d]);
     const int64_t row = (int64_t)h * D + d;
+    // destinations of this (channel, block): 32 FP8 codes / 16 MXFP4 code bytes and one scale byte
+    uint8_t* cdst;
+    uint8_t* sdst = nullptr;
+    if (LAYOUT == 0) {
+      cdst = FMT == 0 ? codes + row * cols + col0 + blk * 32 : codes + (row * cols + col0 + blk * 32) / 2;
+      if (FMT == 1) sdst = scales + row * (cols / 32) + (col0 + blk * 32) / 32;
+    } else {
+      const int64_t t = ((int64_t)s * Hkv + h) * (nk_pad / KEY_TILE) + tile;
+      cdst = FMT == 0 ? codes + (t * D + d) * 128 + blk * 32 : codes + (t * D + d) * 64 + blk * 16;
+      if (FMT == 1) sdst = scales + (t * D + d) * 4 + blk;
+    }
     float mul = enc;
     if (FMT == 1) {
       float amax = 0.0f;
@@ -233,7 +248,7 @@ __global__ void __launch_bounds__(256) quant_v_kernel(const uint16_t* __restrict
       int e = (ab >> 23) == 0 ? -127 : E - 2;           // zero/subnormal block max -> -127
       e = e < -127 ? -127 : e;
       mul = __builtin_amdgcn_ldexpf(1.0f, -e);          // exact: x * 2^-e
-      scales[row * (cols / 32) + (col0 + blk * 32) / 32] = (uint8_t)(e + 127);
+      *sdst = (uint8_t)(e + 127);
     }
 #pragma unroll
     for (int j = 0; j < 32; ++j) x[j] *= mul;
@@ -244,7 +259,7 @@ __global__ void __launch_bounds__(256) quant_v_kernel(const uint16_t* __restrict
         const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * k], x[4 * k + 1], 0, false);
         o[k >> 2][k & 3] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x[4 * k + 2], x[4 * k + 3], lo, true);
       }
-      u32x4* dst = reinterpret_cast<u32x4*>(codes + row * cols + col0 + blk * 32);
+      u32x4* dst = reinterpret_cast<u32x4*>(cdst);
       dst[0] = o[0];
       dst[1] = o[1];
     } else {
@@ -258,7 +273,7 @@ __global__ void __launch_bounds__(256) quant_v_kernel(const uint16_t* __restrict
         w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[8 * k + 6], x[8 * k + 7], 1.0f, 3);
         o[k] = w;
       }
-      *reinterpret_cast<u32x4*>(codes + (row * cols + col0 + blk * 32) / 2) = o;
+      *reinterpret_cast<u32x4*>(cdst) = o;
     }
   }
 }
@@ -355,20 +370,27 @@ hipError_t launch_quant_nvfp4(const void* x, int64_t rows, int D, const float* p
   return hipGetLastError();
 }
 
+template <int F, int DD>
+static void launch_quant_v_t(dim3 grid, hipStream_t st, const void* v, int Nk, int Hkv, const int32_t* cu_k,
+                             int64_t nk_pad, int64_t cols, const float* partials, int np, uint8_t* codes,
+                             uint8_t* scales, float* tensor_scale, bool cache_layout) {
+  if (cache_layout)
+    hipLaunchKernelGGL((quant_v_kernel<F, DD, 1>), grid, dim3(256), 0, st, (const uint16_t*)v, Nk, Hkv, cu_k, nk_pad,
+                       cols, partials, np, codes, scales, tensor_scale);
+  else
+    hipLaunchKernelGGL((quant_v_kernel<F, DD, 0>), grid, dim3(256), 0, st, (const uint16_t*)v, Nk, Hkv, cu_k, nk_pad,
+                       cols, partials, np, codes, scales, tensor_scale);
+}
+
 hipError_t launch_quant_v(const void* v, int B, int Nk, int Hkv, int D, const int32_t* cu_k, int max_len, int64_t cols,
                           int fmt, const float* partials, int np, uint8_t* codes, uint8_t* scales, float* tensor_scale,
-                          hipStream_t st) {
+                          bool cache_layout, hipStream_t st) {
   const int64_t nk_pad = roundup(Nk, KEY_TILE);
   dim3 grid((unsigned)((max_len + KEY_TILE - 1) / KEY_TILE), (unsigned)Hkv, (unsigned)B);
   if (grid.x == 0) grid.x = 1;
-#define QV(F, DD)                                                                                           \
-  hipLaunchKernelGGL((quant_v_kernel<F, DD>), grid, dim3(256), 0, st, (const uint16_t*)v, Nk, Hkv, cu_k, nk_pad, \
-                     cols, partials, np, codes, scales, tensor_scale)
-  if (fmt == 0 && D == 64) QV(0, 64);
-  else if (fmt == 0 && D == 128) QV(0, 128);
-  else if (fmt == 1 && D == 64) QV(1, 64);
-  else QV(1, 128);
-#undef QV
+  auto go = fmt == 0 ? (D == 64 ? launch_quant_v_t<0, 64> : launch_quant_v_t<0, 128>)
+                     : (D == 64 ? launch_quant_v_t<1, 64> : launch_quant_v_t<1, 128>);
+  go(grid, st, v, Nk, Hkv, cu_k, nk_pad, cols, partials, np, codes, scales, tensor_scale, cache_layout);
   return hipGetLastError();
 }
 

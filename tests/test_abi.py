@@ -107,6 +107,15 @@ def test_quant_rejects_bad_arguments_without_launching(lib):
     # V: unsupported head dim, bad format
     assert lib.attn_quant_v(fake, 1, 8, 1, 96, None, 0, 0, fake, None, ctypes.byref(ts), ws, 4096, None) == 1
     assert lib.attn_quant_v(fake, 1, 8, 1, 64, None, 0, 7, fake, None, ctypes.byref(ts), ws, 4096, None) == 1
+    # decode V cache: capacity in whole 128-key tiles, head dim, format, MXFP4 scales, workspace
+    qc = lib.attn_quant_v_cache
+    assert qc(fake, 1, 200, 1, 64, 0, fake, None, ctypes.byref(ts), ws, 4096, None) == 1
+    assert qc(fake, 1, 128, 1, 96, 0, fake, None, ctypes.byref(ts), ws, 4096, None) == 1
+    assert qc(fake, 1, 128, 1, 64, 7, fake, None, ctypes.byref(ts), ws, 4096, None) == 1
+    assert qc(fake, 1, 128, 1, 64, 0, fake, None, None, ws, 4096, None) == 1             # FP8 needs its scale slot
+    assert qc(fake, 1, 128, 1, 64, 1, fake, None, None, ws, 4096, None) == 1             # MXFP4 needs scales
+    assert qc(None, 1, 128, 1, 64, 0, fake, None, ctypes.byref(ts), ws, 4096, None) == 1
+    assert qc(fake, 1, 128, 1, 64, 0, fake, None, ctypes.byref(ts), ws, 16, None) == 3
 
 
 def _args(**kw):
@@ -231,8 +240,8 @@ def test_decode_validation(lib):
     assert d(seqlens_k=(1 << 24) + 2) == 1
     assert d(dbg_p_codes=1 << 24, dbg_b=2) == 1
     assert d(dbg_p_codes=1 << 24) == 1                             # Direct-P dump needs the scale buffer
-    # lane offsets of the V cache must stay below 2^31
-    assert d(B=64, Nk=1 << 18) == 2
+    # the grid (one workgroup per sequence, KV head and 16 query rows) stays below 2^31
+    assert d(B=1 << 30) == 2
     # FP8-P/V takes FP8 V only
     assert lib.attn_decode_fp8pv(ctypes.byref(_dec_args(v=B._VTensor(1, 1 << 24, 1 << 24, 1 << 24))), None) == 2
     assert lib.attn_decode_directp(None, None) == 1 and lib.attn_decode_fp8pv(None, None) == 1

@@ -48,7 +48,7 @@ class _Prepared:
         self.q = gpu.quant_nvfp4(inp.q.cuda())
         self.k = gpu.quant_nvfp4(inp.k.cuda())
         self.vf = gpu.V_FP8 if wl.v_format == "fp8" else gpu.V_MXFP4
-        vq = gpu.quant_v(inp.v.cuda(), self.vf)
+        vq = gpu.quant_v_cache(inp.v.cuda(), self.vf)
         self.v = (self.vf, vq[0], vq[1], vq[2])
         self.seqlens = inp.seqlens.cuda()
 

@@ -266,3 +266,62 @@ def test_v_full_size_sampled(gpu, k):
     _compare_v(sub_codes, sub_scales, ts, ora_sel, wl.v_format, lens, starts)
     del inp
     torch.cuda.empty_cache()
+
+
+def _compare_v_cache(codes, scales, ts, ora, fmt, seqs, heads, chans):
+    """Decode-cache V (blocks [B, Hkv, Nk/128, D, row]) against the oracle's
+    codes of the listed sequences (ora[i] covers sequence seqs[i], heads and
+    channels indexed as given)."""
+    codes = codes.cpu().numpy()
+    scales = None if scales is None else scales.cpu().numpy()
+    for i, b in enumerate(seqs):
+        oc = ora[i][0]
+        N = oc.shape[0]
+        for hi, h in enumerate(heads):
+            for ci, d in enumerate(chans):
+                if fmt == "fp8":
+                    got = codes[b, h, :, d, :].reshape(-1)
+                else:
+                    got = OF.unpack_nibbles(codes[b, h, :, d, :].reshape(-1))
+                    np.testing.assert_array_equal(scales[b, h, :, d, :].reshape(-1), ora[i][1][:, hi, ci],
+                                                  err_msg=f"scales seq {b} h {h} d {d}")
+                np.testing.assert_array_equal(got[:N], oc[:, hi, ci], err_msg=f"codes seq {b} h {h} d {d}")
+        if fmt == "fp8":
+            assert ts.item() == float(ora[i][1])
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_v_cache_small(gpu, fmt, D):
+    # the decode cache layout holds the oracle's V codes of every key, head and channel
+    _say(f"quant_v_cache fmt={fmt} D={D}")
+    g = torch.Generator().manual_seed(10 + D)
+    B, Nk, H = 2, 256, 3
+    v = (torch.randn((B, Nk, H, D), generator=g) * 3).to(torch.bfloat16)
+    v[1, 130:162, 2, 9] = 0       # an all-zero MX block
+    f = gpu.V_FP8 if fmt == "fp8" else gpu.V_MXFP4
+    codes, scales, ts = gpu.quant_v_cache(v.cuda(), f)
+    torch.cuda.synchronize()
+    vf = v.float().numpy()
+    ora = _oracle_v(vf, fmt, amax=np.abs(vf).max())
+    _compare_v_cache(codes, scales, ts, ora, fmt, list(range(B)), list(range(H)), list(range(D)))
+
+
+def test_v_cache_full_size_sampled(gpu):
+    # the decode workload's cache (64 sequences x 8192 keys x 8 KV heads, FP8):
+    # first and last sequence, first and last head, three channels
+    wl = synth.WORKLOADS[6]
+    _say(f"quant_v_cache full-size workload {wl.name} fmt={wl.v_format}")
+    inp = synth.generate_decode(wl, "cuda")
+    f = gpu.V_FP8 if wl.v_format == "fp8" else gpu.V_MXFP4
+    amax = _amax_cpu(inp.v)
+    codes, scales, ts = gpu.quant_v_cache(inp.v, f)
+    torch.cuda.synchronize()
+    seqs, heads, chans = [0, wl.B - 1], [0, wl.Hkv - 1], [0, 5, wl.D - 1]
+    ora = []
+    for b in seqs:
+        vf = inp.v[b][:, heads][:, :, chans].to("cpu").float().numpy()
+        ora.append(OQ.quant_v_fp8(vf, amax=amax) if wl.v_format == "fp8" else OQ.quant_v_mxfp4(vf))
+    _compare_v_cache(codes, scales, ts, ora, wl.v_format, seqs, heads, chans)
+    del inp
+    torch.cuda.empty_cache()
