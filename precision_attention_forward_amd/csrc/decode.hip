@@ -90,12 +90,16 @@ template <int D>
 constexpr int dec_v_loads() {
   return 2 * (D / 16);
 }
-// Position of 16-byte chunk c of K code row k (D = 128: four chunks per row)
-// in LDS: c ^ kswz(k).  The 16 lanes of one operand read take keys
-// 4 st + i + 32 j (MXFP4 P) or 16 j + 4 st + i (FP8 P), i, j in 0..3; the
-// swizzle sends the four values of j to four different chunks, so the 16
-// reads hit 16 different 16-byte bank groups of a 256-byte window.
-__host__ __device__ constexpr int dec_kswz(int k) { return ((k >> 4) ^ (k >> 5)) & 3; }
+// Position of 16-byte chunk c of K code row k (D = 128: four 64-byte rows
+// per 256 bytes) in LDS: c ^ kswz(k).  The 16 lanes of one operand read take
+// keys 32 j + 4 st + i (MXFP4 P) or 16 j + 4 st + i (FP8 P), i, j in 0..3,
+// lane 4 j + i.  With kswz = (j ^ (i & 2)) & 3, the 16 lanes fall on 16
+// different 16-byte bank groups of a 256-byte window, and lanes 0..7 and
+// 8..15 each on 8 different ones of a 128-byte window.
+template <int PF>
+__host__ __device__ constexpr int dec_kswz(int k) {
+  return ((PF == PF_MXFP4 ? k >> 5 : k >> 4) ^ (k & 2)) & 3;
+}
 
 template <int D, int PF, int VF, bool CAUSAL, bool DEBUG>
 __global__ void __launch_bounds__(256, 2) decode_kernel(DecParams p) {
@@ -163,19 +167,20 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecParams p) {
   // V cache: one block of D key-contiguous rows (V^T) per (sequence, KV head, 128-key tile)
   constexpr int VROWB = VF == VF_MXFP4 ? KEY_TILE / 2 : KEY_TILE;       // code bytes of a block row
   const int64_t vtile0 = ((int64_t)b * p.Hkv + hk) * (p.Nk / KEY_TILE);
-  auto tile_of = [&](int s) {
-    const int jc = s * DEC_WAVES + wave;
-    return jc < n_tiles ? jc : n_tiles - 1;   // past the end: the last tile again (a cache hit)
-  };
+  auto tile_of = [&](int s) { return s * DEC_WAVES + wave; };   // loaded only while below n_tiles
 
   // K tiles: copied into two LDS buffers of this wave, two steps ahead.
   // Keys past the sequence but inside its cache (the capacity is whole
   // 128-key tiles) are read and masked later.
   uint8_t* sK = sKall + wave * 2 * KT;
   const uint32_t sK_lds = lds_address(sK);
-  uint32_t kcp_off[4];                  // D = 128: lane's source offset in a copy, per swizzle value
+  // D = 128: lane l of copy i writes key 16 i + l / 4, LDS chunk l % 4, which
+  // holds its chunk (l % 4) ^ kswz(key); kswz(16 i + r) depends on i through
+  // f = kswz(16 i) and on r = l / 4 through r & 2 only.
+  uint32_t kcp_off[4];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) kcp_off[f] = (uint32_t)((lane >> 2) * HALF + 16 * ((lane & 3) ^ f));
+  for (int f = 0; f < 4; ++f)
+    kcp_off[f] = (uint32_t)((lane >> 2) * HALF + 16 * ((lane & 3) ^ ((f ^ ((lane >> 2) & 2)) & 3)));
   auto copy_k = [&](int s, int buf) {
     const int key0 = tile_of(s) * KEY_TILE;
     const uint8_t* kb = khead + (int64_t)key0 * HALF;
@@ -184,7 +189,7 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecParams p) {
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) {
       // copy i: 1 KB of code rows (16 keys at D = 128, 32 at D = 64)
-      const uint32_t off = D == 128 ? kcp_off[dec_kswz(16 * i)] : (uint32_t)(16 * lane);
+      const uint32_t off = D == 128 ? kcp_off[dec_kswz<PF>(16 * i)] : (uint32_t)(16 * lane);
       dma16_nt(kb + 1024 * i, off, dst + 1024 * i);
     }
     if (D == 128) {
@@ -199,7 +204,7 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecParams p) {
 #pragma unroll
   for (int st = 0; st < 8; ++st) {
     const int kl = dec_key<PF>(st, rr);
-    kr_off[st] = D == 128 ? (uint32_t)(kl * HALF + 16 * (g ^ dec_kswz(kl))) : (uint32_t)(kl * HALF + 8 * g);
+    kr_off[st] = D == 128 ? (uint32_t)(kl * HALF + 16 * (g ^ dec_kswz<PF>(kl))) : (uint32_t)(kl * HALF + 8 * g);
     sr_off[st] = (uint32_t)(KSC + kl * (D / 16) + g * (GC / 16));
   }
 
@@ -395,16 +400,25 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecParams p) {
   // K tile of s has landed once no more than NV + NK loads are outstanding
   // (those of V(s) and K(s + 1)); the compiler waits for V(s) itself before
   // the P.V products.
+  // Only tiles the wave takes are loaded (live(s): tile 4 s + wave exists;
+  // live(s + 1) implies live(s)), so the count also drops NK when the
+  // next K tile is not loaded.
+  auto live_step = [&](int s) { return s * DEC_WAVES + wave < n_tiles; };
   if (n_steps > 0) {
-    copy_k(0, 0);
-    load_v(0);
-    copy_k(1, 1);
+    if (live_step(0)) {
+      copy_k(0, 0);
+      load_v(0);
+    }
+    if (live_step(1)) copy_k(1, 1);
     for (int s = 0; s < n_steps; ++s) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NV + NK) : "memory");
+      if (live_step(s + 1))
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NV + NK) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NV) : "memory");
       body(s);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the step's LDS reads are done
-      load_v(s + 1);
-      copy_k(s + 2, s & 1);
+      if (live_step(s + 1)) load_v(s + 1);
+      if (live_step(s + 2)) copy_k(s + 2, s & 1);
     }
   }
   // no copy may still be writing the K tiles, which the partial O reuses
