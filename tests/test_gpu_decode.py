@@ -202,3 +202,43 @@ def test_decode_bf16_output(gpu):
     assert none is None
     assert torch.equal(o16, o32.to(torch.bfloat16))
     assert torch.equal(l16, l32) and torch.equal(o_nolse, o32)
+
+
+def test_decode_step_graph_replays(gpu):
+    # a decode step (Q quantization + decode kernel) captured as a HIP graph:
+    # every replay, with eager library work and synchronizations between the
+    # replays, reproduces the eager step's outputs bit for bit
+    wl = W.with_(B=4, Hq=8, Hkv=2, N=512, seed=69, extra={"nq": 1, "ragged": True})
+    inp = synth.generate_decode(wl)
+    prep = _Prepared(gpu, inp)
+    qb = inp.q.cuda()
+    kw = dict(B=wl.B, Hq=wl.Hq, Hkv=wl.Hkv, nq=1, Nk=wl.N, D=wl.D, softmax_scale=inp.sigma, causal=True,
+              seqlens_k=prep.seqlens)
+    _say("decode step as a replayed graph")
+    out = gpu.decode_directp(gpu.quant_nvfp4(qb), prep.k, prep.v, **kw)[:2]
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in out]
+
+    def step():
+        gpu.decode_directp(gpu.quant_nvfp4(qb), prep.k, prep.v, out=out, **kw)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    other = (qb.float() * 2).to(torch.bfloat16)
+    for r in range(4):
+        for t in out:
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for x, y in zip(out, ref):
+            assert torch.equal(x, y), f"replay {r}"
+        # eager work between replays: another step on other inputs and outputs
+        o2 = gpu.decode_directp(gpu.quant_nvfp4(other), prep.k, prep.v, **kw)[0]
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(o2).all())
