@@ -65,7 +65,7 @@ def parse():
 # measured by hardware counters is reported only while they are unchanged.
 KERNEL_SOURCES = ["fwd_lowp.hip", "common.h", "pipeline.h", "fwd_params.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_lowp_kernel_hbm_traffic.md")
-DEC_KERNEL_SOURCES = ["decode.hip", "common.h", "dec_params.h", "fwd_params.h"]
+DEC_KERNEL_SOURCES = ["decode.hip", "common.h", "dec_params.h", "fwd_params.h", "pipeline.h"]
 DEC_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_llama8b_decode.md")
 HBM_PEAK_GBS = 8000.0
 

@@ -92,14 +92,12 @@ constexpr int dec_v_loads() {
 }
 // Position of 16-byte chunk c of K code row k (D = 128: four 64-byte rows
 // per 256 bytes) in LDS: c ^ kswz(k).  The 16 lanes of one operand read take
-// keys 32 j + 4 st + i (MXFP4 P) or 16 j + 4 st + i (FP8 P), i, j in 0..3,
-// lane 4 j + i.  With kswz = (j ^ (i & 2)) & 3, the 16 lanes fall on 16
-// different 16-byte bank groups of a 256-byte window, and lanes 0..7 and
-// 8..15 each on 8 different ones of a 128-byte window.
-template <int PF>
-__host__ __device__ constexpr int dec_kswz(int k) {
-  return ((PF == PF_MXFP4 ? k >> 5 : k >> 4) ^ (k & 2)) & 3;
-}
+// keys 32 j + 4 st + i (MXFP4 P) or 16 j + 4 st + i (FP8 P), i, j in 0..3;
+// kswz sends the four values of j to four different chunks, so the 16 reads
+// hit 16 different 16-byte bank groups of a 256-byte window.  (A variant that
+// also separated them within 128-byte windows counted more bank conflicts on
+// gfx950 and ran no faster.)
+__host__ __device__ constexpr int dec_kswz(int k) { return ((k >> 4) ^ (k >> 5)) & 3; }
 
 template <int D, int PF, int VF, bool CAUSAL, bool DEBUG>
 __global__ void __launch_bounds__(256, 2) decode_kernel(DecParams p) {
@@ -175,12 +173,10 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecParams p) {
   uint8_t* sK = sKall + wave * 2 * KT;
   const uint32_t sK_lds = lds_address(sK);
   // D = 128: lane l of copy i writes key 16 i + l / 4, LDS chunk l % 4, which
-  // holds its chunk (l % 4) ^ kswz(key); kswz(16 i + r) depends on i through
-  // f = kswz(16 i) and on r = l / 4 through r & 2 only.
+  // holds its chunk (l % 4) ^ kswz(key); kswz(16 i + r) = kswz(16 i) for r < 16.
   uint32_t kcp_off[4];
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
-    kcp_off[f] = (uint32_t)((lane >> 2) * HALF + 16 * ((lane & 3) ^ ((f ^ ((lane >> 2) & 2)) & 3)));
+  for (int f = 0; f < 4; ++f) kcp_off[f] = (uint32_t)((lane >> 2) * HALF + 16 * ((lane & 3) ^ f));
   auto copy_k = [&](int s, int buf) {
     const int key0 = tile_of(s) * KEY_TILE;
     const uint8_t* kb = khead + (int64_t)key0 * HALF;
@@ -189,7 +185,7 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecParams p) {
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) {
       // copy i: 1 KB of code rows (16 keys at D = 128, 32 at D = 64)
-      const uint32_t off = D == 128 ? kcp_off[dec_kswz<PF>(16 * i)] : (uint32_t)(16 * lane);
+      const uint32_t off = D == 128 ? kcp_off[dec_kswz(16 * i)] : (uint32_t)(16 * lane);
       dma16_nt(kb + 1024 * i, off, dst + 1024 * i);
     }
     if (D == 128) {
@@ -204,7 +200,7 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecParams p) {
 #pragma unroll
   for (int st = 0; st < 8; ++st) {
     const int kl = dec_key<PF>(st, rr);
-    kr_off[st] = D == 128 ? (uint32_t)(kl * HALF + 16 * (g ^ dec_kswz<PF>(kl))) : (uint32_t)(kl * HALF + 8 * g);
+    kr_off[st] = D == 128 ? (uint32_t)(kl * HALF + 16 * (g ^ dec_kswz(kl))) : (uint32_t)(kl * HALF + 8 * g);
     sr_off[st] = (uint32_t)(KSC + kl * (D / 16) + g * (GC / 16));
   }
 
