@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--cpu-seqs-dec", type=int, default=8, help="sequences of the decode oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (HBM counter calibration) and exit")
+    ap.add_argument("--gemm-reference", action="store_true",
+                    help="only time torch's bf16 and fp16 matrix products (n = 8192, 16384) on this GPU, the "
+                         "vendor-library reference for the BF16 attention's matrix rate, and exit")
     return ap.parse_args()
 
 
@@ -107,6 +110,33 @@ def copy_calibration(mib):
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
                       "launches": 3}), flush=True)
+
+
+def gemm_reference():
+    """Square bf16 / fp16 products through torch (the vendor BLAS): the
+    matrix rate a plain library GEMM reaches on this GPU, printed as one JSON
+    line per (dtype, n)."""
+    import torch
+    torch.manual_seed(0)
+    for dt in (torch.bfloat16, torch.float16):
+        for n in (8192, 16384):
+            a = torch.randn(n, n, device="cuda:0", dtype=dt)
+            b = torch.randn(n, n, device="cuda:0", dtype=dt)
+            for _ in range(3):
+                c = a @ b
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            reps = 10 if n == 8192 else 4
+            e0.record()
+            for _ in range(reps):
+                c = a @ b
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            print(json.dumps({"gemm": str(dt).replace("torch.", ""), "n": n, "ms": round(ms, 3),
+                              "tflops": round(2 * n ** 3 / ms / 1e9, 1)}), flush=True)
+            del a, b, c
 
 
 def cpu_baseline(inp, rows, encoder="exact", four_six=False, qk="nvfp4"):
@@ -483,6 +513,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.gemm_reference:
+        gemm_reference()
         return
     import torch
     import precision_attention_forward_amd as paf
