@@ -239,23 +239,85 @@ __global__ void __launch_bounds__(256) bwd_v_kernel(const uint8_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV.  Workgroup: 4 waves, keys kb*128 + 32*wave + (lane & 31) of KV
-// head hk.  S sub-tile s2 of a 64-query chunk: accumulator (lane half hh,
-// register r) holds query 32*s2 + 16*hh + r of the chunk; A row m of the S /
-// dP products is therefore query 32*s2 + 16*((m>>2)&1) + 4*(m>>3) + (m&3).
+// LDS chunk tiles of the main kernels: 64 rows of the other side (queries for
+// dK/dV, keys for dQ) row-major, and their transposes (one row per channel d),
+// copied straight from global memory by 1 KB global->LDS copies.  The 16-byte
+// chunks of each row are XOR-swizzled instead of padding the rows (a copy
+// fills 1 KB of LDS contiguously): chunk c of row R sits at c ^ f(R), with f
+// a linear map of the row bits chosen so that every operand read of the
+// kernels (16 lanes at a time over 256 bytes, 8 at a time over 128 bytes)
+// touches distinct 16-byte bank groups.
+//
+// dK/dV: A-operand rows R = query perm(m) + 32 s2 of the chunk, with
+// perm(m) = 16 ((m>>2)&1) + 4 (m>>3) + (m&3) (bits 0-4 of R vary across a read).
+template <int RB>                      // row bytes: 256 (16 chunks), 128 (8), 64 (4)
+__device__ __host__ inline int swz_qrows(int R) {
+  if (RB == 256) return (R & 3) | (((R >> 4) & 1) << 2) | (((R >> 2) & 1) << 3);
+  if (RB == 128) return ((R >> 1) & 1) | (((R >> 4) & 1) << 1) | (((R ^ (R >> 2)) & 1) << 2);
+  return ((R >> 4) & 1) | ((((R >> 1) ^ (R >> 2)) & 1) << 1);
+}
+// transposed tiles: row d = 32 dt + ln read by lanes ln = 0..31 (bits 0-3 vary
+// across 16 lanes); 128-byte rows (bf16 x 64) and 64-byte rows (8-bit x 64)
+__device__ __host__ inline int swz_drows128(int d) {
+  return ((d >> 1) & 1) | (((d >> 2) & 1) << 1) | ((((d >> 3) ^ d) & 1) << 2);
+}
+__device__ __host__ inline int swz_drows64(int d) { return ((d >> 2) & 1) | ((((d >> 3) ^ (d >> 1)) & 1) << 1); }
+
+// Copy 16 bytes per lane from global memory straight into LDS (lane i writes
+// LDS bytes [lds + 16 i, lds + 16 i + 16)); `base` and `lds` wave-uniform,
+// `off` a per-lane byte offset below 4 GiB.  Inline assembly, so that the
+// compiler inserts no wait for it before unrelated LDS reads; completion is
+// awaited with an explicit vmcnt wait.
+__device__ inline void bwd_dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(base)
+               : "memory");
+}
+__device__ inline void bwd_dma4(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(base)
+               : "memory");
+}
+__device__ inline uint32_t bwd_lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV.  Workgroup: 8 waves for 128 keys kb*128 + 32*kw + (lane & 31) of KV
+// head hk, two waves per 32-key block kw, on one SIMD (waves kw and kw + 4):
+//   S side (waves 0-3):  S = Q^ K^T, P = 2^(t - L), P~ and dV += P~^T dO^
+//   dP side (waves 4-7): dP = dO^ V^T, dS = P (dP - D), dS~ and dK += dS~^T Q^
+// The dP side runs one 64-query chunk behind: in step s the S side takes
+// chunk s and the dP side chunk s - 1, whose P the S side left in LDS as
+// float32 (the dP side's lane l needs exactly the 32 values lane l of its
+// partner computed).  One barrier per step, so one wave's matrix products
+// overlap its partner's vector work; each wave holds one accumulator and one
+// resident operand (K^ or V), so the two fit on one SIMD.
+//   LDS: the Q^ chunk row-major in a ring of three (chunk x in slot x % 3:
+//   the S side's chunk, the dP side's chunk and the next), read straight for
+//   S and through transposing reads (ds_read_b64_tr_b16) as the Q^T operand of
+//   dK; dO^ row-major and dO^T, L and D, and P, two buffers each.
+// S / dP sub-tile s2 of a chunk: accumulator (lane half hh, register r) holds
+// query 32*s2 + 16*hh + r of the chunk; A row m of the S / dP products is
+// therefore query 32*s2 + 16*((m>>2)&1) + 4*(m>>3) + (m&3).
+typedef short s16x4 __attribute__((__vector_size__(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
 template <int D, bool CAUSAL, bool DEBUG>
-__global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
+__global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
   constexpr int KS = D / 16, DT = D / 32, KK = D / 64;
-  // LDS rows padded by 16 bytes (row strides of 256k + 16 bytes spread the
-  // permuted-row operand reads over all banks)
-  constexpr int QS = D + 8, QTS = BWD_CHUNK + 8;          // bf16 elements
-  constexpr int DS = D + 16, DTS = BWD_CHUNK + 16;        // bytes
-  __shared__ __attribute__((aligned(16))) __bf16 sQ[2][BWD_CHUNK * QS];
-  __shared__ __attribute__((aligned(16))) __bf16 sQT[2][D * QTS];
-  __shared__ __attribute__((aligned(16))) uint8_t sDO[2][BWD_CHUNK * DS];
-  __shared__ __attribute__((aligned(16))) uint8_t sDOT[2][D * DTS];
+  constexpr int NW = 8;                                     // waves per workgroup
+  // bytes of one buffer of each chunk tile
+  constexpr int QB = BWD_CHUNK * D * 2, DOB = BWD_CHUNK * D, DOTB = D * BWD_CHUNK;
+  constexpr int NQC = QB / 1024, NDOC = DOB / 1024, NDOTC = DOTB / 1024;
+  __shared__ __attribute__((aligned(1024))) uint8_t sQ[3][QB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sDO[2][DOB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sDOT[2][DOTB];
   __shared__ __attribute__((aligned(16))) float sL[2][BWD_CHUNK];   // read as 16-byte vectors
   __shared__ __attribute__((aligned(16))) float sD[2][BWD_CHUNK];
+  __shared__ __attribute__((aligned(16))) f32x4 sP[2][4][2][4][64];  // [buffer][key block][s2][r / 4][lane]
   int kb = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   if (CAUSAL) {
     // Causal: a key block's work falls with kb.  Dispatch (which follows the
@@ -268,145 +330,285 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
     hk = (lin % nh) % gridDim.y;
     b = (lin % nh) / gridDim.y;
   }
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, ln = lane & 31;
-  const int key = kb * BWD_ROWS + wave * 32 + ln;
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, ln = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool s_side = wave < 4;                 // uniform
+  const int kw = wave & 3;
+  const int key = kb * BWD_ROWS + kw * 32 + ln;
   const int G = p.Hq / p.Hkv;
   const int64_t npad = p.npad;
   const int64_t krow = ((int64_t)b * p.Hkv + hk) * npad + key;
-  bf16x8 kreg[KS];
+  // resident operand, in one register array for both sides (a wave keeps
+  // one side for the whole kernel, but the compiler cannot know that): K^ as
+  // KS bf16x8 (S side, B operand of S) or V as KK i32x8 (dP side, B operand of dP)
+  u32x4 res[KS];
+  if (s_side) {
 #pragma unroll
-  for (int s = 0; s < KS; ++s) kreg[s] = *reinterpret_cast<const bf16x8*>(p.krm + krow * D + 16 * s + 8 * hh);
-  i32x8 vreg[KK];
+    for (int s = 0; s < KS; ++s) res[s] = *reinterpret_cast<const u32x4*>(p.krm + krow * D + 16 * s + 8 * hh);
+  } else {
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(p.vrm + krow * D + 64 * kk + 16 * hh);
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(p.vrm + krow * D + 64 * kk + 32 + 16 * hh);
-    vreg[kk] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    for (int kk = 0; kk < KK; ++kk) {
+      res[2 * kk] = *reinterpret_cast<const u32x4*>(p.vrm + krow * D + 64 * kk + 16 * hh);
+      res[2 * kk + 1] = *reinterpret_cast<const u32x4*>(p.vrm + krow * D + 64 * kk + 32 + 16 * hh);
+    }
   }
-  f32x16 dv[DT], dk[DT];
+  auto kop = [&](int st) { return __builtin_bit_cast(bf16x8, res[st]); };
+  auto vop = [&](int kk) {
+    const u32x4 lo = res[2 * kk], hi = res[2 * kk + 1];
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+  f32x16 acc[DT];                               // dV (S side) or dK (dP side)
 #pragma unroll
-  for (int i = 0; i < DT; ++i) { dv[i] = f32x16{}; dk[i] = f32x16{}; }
+  for (int i = 0; i < DT; ++i) acc[i] = f32x16{};
   const float cc = (float)((double)p.sigma * 1.4426950408889634 * (double)(*p.gq) * (double)(*p.gk));
   const float sdo = *p.sdo;
   const float sdv = sdo * *p.sv;
   const int nchunks = (int)(npad / BWD_CHUNK);
   const int c0 = CAUSAL ? (kb * BWD_ROWS) / BWD_CHUNK : 0;
   const int nch = nchunks - c0;                 // >= 2: the key block's own chunks
-  const int total = G * nch;                    // (query head, query chunk) steps
+  const int total = G * nch;                    // (query head, query chunk) steps of each side
   const int m = ln;
-  // Chunk copies are double-buffered through registers: the global loads of
-  // step it + 1 are issued before the matrix work of step it and stored to
-  // the other LDS buffer after it (one barrier per step).
-  constexpr int NQ = BWD_CHUNK * D / 8 / 256, NQT = D * (BWD_CHUNK / 8) / 256;
-  constexpr int NDO = BWD_CHUNK * D / 16 / 256, NDOT = D * (BWD_CHUNK / 16) / 256;
-  u32x4 pq[NQ], pqt[NQT], pdo[NDO], pdot[NDOT];
-  float pl = 0.0f, pd = 0.0f;
-  // per-lane byte offsets of the chunk copies (loop invariant; the chunk and
-  // head go into the wave-uniform base of each load)
-  uint32_t oq[NQ], oqt[NQT], odo[NDO], odot[NDOT];
+
+  // ---- chunk copies.  Wave w issues copies j = w + 8 t of each tile; the
+  // per-lane source offsets within a tile are loop invariant.
+  constexpr int NQW = (NQC + NW - 1) / NW, NDOW = (NDOC + NW - 1) / NW, NDOTW = (NDOTC + NW - 1) / NW;
+  uint32_t oqc[NQW], odc[NDOW], otc[NDOTW];
 #pragma unroll
-  for (int i = 0; i < NQ; ++i) {
-    const int it = tid + 256 * i, row = it / (D / 8), g8 = it % (D / 8);
-    oq[i] = (uint32_t)(row * D + 8 * g8) * 2u;
+  for (int t = 0; t < NQW; ++t) {                          // Q rows: 2D bytes, 1024 / 2D rows per copy
+    const int j = wave + NW * t;
+    const int r = j * (1024 / (2 * D)) + (16 * lane) / (2 * D), c = ((16 * lane) % (2 * D)) / 16;
+    oqc[t] = (uint32_t)(r * 2 * D + 16 * (c ^ swz_qrows<2 * D>(r)));
   }
 #pragma unroll
-  for (int i = 0; i < NQT; ++i) {
-    const int it = tid + 256 * i, d = it / (BWD_CHUNK / 8), r8 = it % (BWD_CHUNK / 8);
-    oqt[i] = ((uint32_t)d * (uint32_t)npad + 8u * r8) * 2u;
+  for (int t = 0; t < NDOW; ++t) {                         // dO rows: D bytes
+    const int j = wave + NW * t;
+    const int r = j * (1024 / D) + (16 * lane) / D, c = ((16 * lane) % D) / 16;
+    odc[t] = (uint32_t)(r * D + 16 * (c ^ swz_qrows<D>(r)));
   }
 #pragma unroll
-  for (int i = 0; i < NDO; ++i) {
-    const int it = tid + 256 * i, row = it / (D / 16), g16 = it % (D / 16);
-    odo[i] = (uint32_t)(row * D + 16 * g16);
+  for (int t = 0; t < NDOTW; ++t) {                        // dO^T rows: 64 bytes, 16 rows per copy
+    const int j = wave + NW * t;
+    const int d = 16 * j + (lane >> 2), c = lane & 3;
+    otc[t] = (uint32_t)d * (uint32_t)npad + 16u * (uint32_t)(c ^ swz_drows64(d));
   }
-#pragma unroll
-  for (int i = 0; i < NDOT; ++i) {
-    const int it = tid + 256 * i, d = it / (BWD_CHUNK / 16), r16 = it % (BWD_CHUNK / 16);
-    odot[i] = (uint32_t)d * (uint32_t)npad + 16u * r16;
-  }
-  auto fetch = [&](int step) {
-    const int g = step / nch, c = c0 + step % nch;
+  auto chunk_row = [&](int g, int c) { return ((int64_t)b * p.Hq + hk * G + g) * npad + (int64_t)c * BWD_CHUNK; };
+  // the S side's tiles of chunk (g, c): Q^ -> ring slot, dO^T and L -> buffer
+  auto copy_s = [&](int g, int c, int slot, int buf) {
+    const int64_t q0 = chunk_row(g, c);
     const int64_t qhead = (int64_t)b * p.Hq + hk * G + g;
-    const int64_t q0 = qhead * npad + (int64_t)c * BWD_CHUNK;
-    const __bf16* qb0 = p.qrm + q0 * D;
-    const __bf16* qtb0 = p.qt + qhead * D * npad + (int64_t)c * BWD_CHUNK;
-    const uint8_t* db0 = p.dorm + q0 * D;
+    const uint8_t* qb0 = reinterpret_cast<const uint8_t*>(p.qrm + q0 * D);
     const uint8_t* dtb0 = p.dot + qhead * D * npad + (int64_t)c * BWD_CHUNK;
 #pragma unroll
-    for (int i = 0; i < NQ; ++i) pq[i] = load16(qb0, oq[i]);
-#pragma unroll
-    for (int i = 0; i < NQT; ++i) pqt[i] = load16(qtb0, oqt[i]);
-#pragma unroll
-    for (int i = 0; i < NDO; ++i) pdo[i] = load16(db0, odo[i]);
-#pragma unroll
-    for (int i = 0; i < NDOT; ++i) pdot[i] = load16(dtb0, odot[i]);
-    if (tid < BWD_CHUNK) {
-      pl = p.lv[q0 + tid];
-      pd = p.dv[q0 + tid];
+    for (int t = 0; t < NQW; ++t) {
+      const int j = wave + NW * t;
+      if (j < NQC) bwd_dma16(qb0, oqc[t], bwd_lds_address(&sQ[slot][0]) + 1024 * j);
     }
+#pragma unroll
+    for (int t = 0; t < NDOTW; ++t) {
+      const int j = wave + NW * t;
+      if (j < NDOTC) bwd_dma16(dtb0, otc[t], bwd_lds_address(&sDOT[buf][0]) + 1024 * j);
+    }
+    if (wave == 0) bwd_dma4(p.lv + q0, (uint32_t)(4 * lane), bwd_lds_address(&sL[buf][0]));
   };
-  auto store = [&](int buf) {
+  // the dP side's tiles of chunk (g, c): dO^ and D -> buffer
+  auto copy_d = [&](int g, int c, int buf) {
+    const int64_t q0 = chunk_row(g, c);
+    const uint8_t* db0 = p.dorm + q0 * D;
 #pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-      const int it = tid + 256 * i, row = it / (D / 8), g8 = it % (D / 8);
-      *reinterpret_cast<u32x4*>(&sQ[buf][row * QS + 8 * g8]) = pq[i];
+    for (int t = 0; t < NDOW; ++t) {
+      const int j = wave + NW * t;
+      if (j < NDOC) bwd_dma16(db0, odc[t], bwd_lds_address(&sDO[buf][0]) + 1024 * j);
     }
-#pragma unroll
-    for (int i = 0; i < NQT; ++i) {
-      const int it = tid + 256 * i, d = it / (BWD_CHUNK / 8), r8 = it % (BWD_CHUNK / 8);
-      *reinterpret_cast<u32x4*>(&sQT[buf][d * QTS + 8 * r8]) = pqt[i];
-    }
-#pragma unroll
-    for (int i = 0; i < NDO; ++i) {
-      const int it = tid + 256 * i, row = it / (D / 16), g16 = it % (D / 16);
-      *reinterpret_cast<u32x4*>(&sDO[buf][row * DS + 16 * g16]) = pdo[i];
-    }
-#pragma unroll
-    for (int i = 0; i < NDOT; ++i) {
-      const int it = tid + 256 * i, d = it / (BWD_CHUNK / 16), r16 = it % (BWD_CHUNK / 16);
-      *reinterpret_cast<u32x4*>(&sDOT[buf][d * DTS + 16 * r16]) = pdot[i];
-    }
-    if (tid < BWD_CHUNK) {
-      sL[buf][tid] = pl;
-      sD[buf][tid] = pd;
-    }
+    if (wave == 1) bwd_dma4(p.dv + q0, (uint32_t)(4 * lane), bwd_lds_address(&sD[buf][0]));
   };
-  fetch(0);
-  store(0);
+  // per-lane operand read offsets (bytes within a buffer), one array for both
+  // sides: S side Q rows per k-step, then the dO^T halves; dP side dO rows
+  // per (k-step, half), then the transposing Q reads per (dt, half)
+  const int R0 = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);   // A row of the S / dP products
+  constexpr int NOFS = KS + 2 > 2 * KK + 2 * DT ? KS + 2 : 2 * KK + 2 * DT;
+  uint32_t ofs[NOFS];
+  if (s_side) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ofs[ks] = (uint32_t)(R0 * 2 * D + 16 * ((2 * ks + hh) ^ swz_qrows<2 * D>(R0)));
+#pragma unroll
+    for (int lh = 0; lh < 2; ++lh) ofs[KS + lh] = (uint32_t)(ln * 64 + 16 * ((hh + 2 * lh) ^ swz_drows64(ln)));
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int lh = 0; lh < 2; ++lh)
+        ofs[2 * kk + lh] = (uint32_t)(R0 * D + 16 * ((4 * kk + hh + 2 * lh) ^ swz_qrows<D>(R0)));
+    // transposing reads of Q^ for the dK B operand: lane (g, c) of a 16-lane
+    // group reads 4 bf16 of row 16 (g >> 1) + 4 half + (c >> 2) (+ 32 s2 + r0,
+    // which leave the swizzle unchanged) at channel 32 dt + 16 (g & 1) + 4 (c & 3);
+    // the transpose hands it channel 32 dt + 16 (g & 1) + c of 4 rows
+    const int g4 = lane >> 4, c16 = lane & 15;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int R = 16 * (g4 >> 1) + 4 * half + (c16 >> 2);
+        const int byte = 2 * (32 * dt + 16 * (g4 & 1) + 4 * (c16 & 3));
+        ofs[2 * KK + 2 * dt + half] = (uint32_t)(R * 2 * D + 16 * ((byte / 16) ^ swz_qrows<2 * D>(R)) + (byte % 16));
+      }
+  }
+
+  const int wkey_last = kb * BWD_ROWS + kw * 32 + 31;
+  // prologue: the S side's tiles of chunk 0
+  copy_s(0, c0, 0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int step = 0; step < total; ++step) {
-    const int g = step / nch, c = c0 + step % nch, buf = step & 1;
-    const int h = hk * G + g;
-    fetch(step + 1 < total ? step + 1 : step);
-    {
-      f32x16 s[2], dp[2];
-      // S of both 32-query sub-tiles: the two accumulation chains alternate,
-      // and each A operand is read from LDS two matrix instructions ahead
-      // (fenced), so that no read's latency is waited out right before its
-      // use; each chain still sums its k-steps in order
-      {
-        const __bf16* qa = &sQ[buf][(16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3)) * QS + 8 * hh];
-        auto lda = [&](int i) {    // operand i: k-step i / 2 of sub-tile i % 2
-          return *reinterpret_cast<const bf16x8*>(qa + 32 * (i & 1) * QS + 16 * (i >> 1));
-        };
-        bf16x8 op[3];
-        op[0] = lda(0);
-        op[1] = lda(1);
+  // Each side runs its own copy of the step loop (one side per wave for the
+  // whole kernel; separate loops keep each side's accumulator in place).
+  // Both loops take the same number of barriers.  Per step: the copies for
+  // step + 1 (the S side's chunk step + 1, the dP side's chunk step), this
+  // side's work, then a barrier once this wave's copies have landed and its
+  // LDS writes are done.
+  // (g, c): the S side's chunk of step s; (gp, cp): the dP side's (s - 1)
+  int g = 0, c = c0, gp = 0, cp = c0;
+  auto step_begin = [&](int step, int& gn, int& cn) {
+    gn = g;
+    cn = c + 1;
+    if (cn == nchunks) { cn = c0; ++gn; }
+    if (step + 1 < total) copy_s(gn, cn, (step + 1) % 3, (step + 1) & 1);
+    if (step < total) copy_d(g, c, step & 1);
+  };
+  auto step_end = [&](int gn, int cn) {
+    // the copies for step + 1 (this wave's) have landed and this wave's LDS
+    // writes are done; after the barrier every wave's are, and the tiles of
+    // step - 1 may be overwritten
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    gp = g;
+    cp = c;
+    g = gn;
+    c = cn;
+  };
+  if (s_side) {
+    for (int step = 0; step <= total; ++step) {
+      int gn, cn;
+      step_begin(step, gn, cn);
+      if (step < total) {
+
+        const int buf = step & 1, slot = step % 3;
+        const int h = hk * G + g;
+        const bool dump = DEBUG && b == p.dbg_b && h == p.dbg_h;
+        float pv[2][16];
+        float amx[2];
+        {
+          f32x16 s[2];
+          // S of both 32-query sub-tiles: the two accumulation chains
+          // alternate, each A operand read from LDS two matrix instructions
+          // ahead (fenced); each chain sums its k-steps in order
+          const uint8_t* qa = sQ[slot];
+          auto lda = [&](int i) {    // operand i: k-step i / 2 of sub-tile i % 2
+            return *reinterpret_cast<const bf16x8*>(qa + ofs[i >> 1] + 32 * 2 * D * (i & 1));
+          };
+          bf16x8 op[3];
+          op[0] = lda(0);
+          op[1] = lda(1);
 #pragma unroll
-        for (int i = 0; i < 2 * KS; ++i) {
-          if (i + 2 < 2 * KS) op[(i + 2) % 3] = lda(i + 2);
-          const int st = i >> 1, s2 = i & 1;
-          s[s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], kreg[st], st == 0 ? f32x16{} : s[s2], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
+          for (int i = 0; i < 2 * KS; ++i) {
+            if (i + 2 < 2 * KS) op[(i + 2) % 3] = lda(i + 2);
+            const int st = i >> 1, s2 = i & 1;
+            s[s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], kop(st), st == 0 ? f32x16{} : s[s2], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          // P of (query 32 s2 + 16 hh + r, this lane's key).  Padded query rows
+          // have L = +inf (P = 0); keys past the sequence and (causal) keys after
+          // the query are masked, which only the block's boundary chunks need.
+          const bool all_live = wkey_last < p.N && (!CAUSAL || wkey_last <= c * BWD_CHUNK);
+          auto elements = [&](auto masked) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+              amx[s2] = 0.0f;
+              f32x4 lr[4];           // the 16 rows' L as four 16-byte reads, issued together
+#pragma unroll
+              for (int v = 0; v < 4; ++v) lr[v] = *reinterpret_cast<const f32x4*>(&sL[buf][32 * s2 + 16 * hh + 4 * v]);
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int qi = c * BWD_CHUNK + 32 * s2 + 16 * hh + r;
+                float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[s2][r], cc, -lr[r >> 2][r & 3]));
+                if (decltype(masked)::value) pr = (key < p.N && (!CAUSAL || key <= qi)) ? pr : 0.0f;
+                pv[s2][r] = pr;
+                amx[s2] = __builtin_fmaxf(amx[s2], pr);
+              }
+            }
+          };
+          if (all_live) elements(std::false_type{});
+          else elements(std::true_type{});
+        }
+        // P for the dP side (next step)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            sP[buf][kw][s2][v][lane] = f32x4{pv[s2][4 * v], pv[s2][4 * v + 1], pv[s2][4 * v + 2], pv[s2][4 * v + 3]};
+        // P~^T as the A operand of dV: bytes 0..15 sub-tile 0, bytes 16..31
+        // sub-tile 1 (the k-blocks of the FP8 operand); block maxima over the 32
+        // queries of each sub-tile (this lane's 16 and lane^32's 16); lane half
+        // hh supplies the exponent of block hh
+        int ep[2];
+        float limp[2], scp[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const auto wp = __builtin_amdgcn_permlane32_swap(__float_as_uint(amx[s2]), __float_as_uint(amx[s2]), false, false);
+          ep[s2] = mx_e4m3_exponent(__builtin_fmaxf(__uint_as_float(wp[0]), __uint_as_float(wp[1])));
+          limp[s2] = __builtin_ldexpf(448.0f, ep[s2]);
+          scp[s2] = e8m0_scale(ep[s2]);
+        }
+        i32x8 pa;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const int s2 = w >> 2, r = 4 * (w & 3);
+          s16x2 t = {0, 0};
+          t = mx_e4m3_pair<false>(t, pv[s2][r], pv[s2][r + 1], limp[s2], scp[s2]);
+          t = mx_e4m3_pair<true>(t, pv[s2][r + 2], pv[s2][r + 3], limp[s2], scp[s2]);
+          pa[w] = __builtin_bit_cast(int, t);
+        }
+        const int scale_p = (hh ? ep[1] : ep[0]) + 127;
+        if (dump) {
+#pragma unroll
+          for (int w = 0; w < 8; ++w)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int qi = c * BWD_CHUNK + 32 * (w >> 2) + 16 * hh + 4 * (w & 3) + j;
+              p.dbg_pt[(int64_t)qi * npad + key] = (uint8_t)((uint32_t)pa[w] >> (8 * j));
+            }
+          if (hh == 0)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) p.dbg_pt_e[(int64_t)(2 * c + s2) * npad + key] = (uint8_t)(ep[s2] + 127);
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(&sDOT[buf][ofs[KS] + 32 * 64 * dt]);
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(&sDOT[buf][ofs[KS + 1] + 32 * 64 * dt]);
+          const i32x8 bb = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          // A: P~ (E4M3, format 0) with its block exponents, B: dO^ codes (E5M2, format 1)
+          acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pa, bb, acc[dt], 0, 1, 0, scale_p, 0, 127);
         }
       }
-      // dP likewise: the two sub-tiles' chains alternate, operands one ahead
+      step_end(gn, cn);
+    }
+  } else {
+    for (int step = 0; step <= total; ++step) {
+      int gn, cn;
+      step_begin(step, gn, cn);
+      if (step > 0) {
+
+      // the dP side: chunk (gp, cp) of step - 1
+      const int buf = (step - 1) & 1, slot = (step - 1) % 3;
+      const int h = hk * G + gp;
+      const bool dump = DEBUG && b == p.dbg_b && h == p.dbg_h;
+      float pv[2][16];
+      float amx[2];
       {
-        const uint8_t* da = &sDO[buf][(16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3)) * DS + 16 * hh];
+        f32x16 dp[2];
+        // dP of both sub-tiles: the two chains alternate, operands one ahead
+        const uint8_t* da = sDO[buf];
         auto ldd = [&](int i) {    // operand i: k-step i / 2 of sub-tile i % 2 (two 16-byte halves)
-          const uint8_t* r = da + 32 * (i & 1) * DS + 64 * (i >> 1);
-          const u32x4 lo = *reinterpret_cast<const u32x4*>(r);
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(r + 32);
+          const int kk = i >> 1, s2 = i & 1;
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(da + ofs[2 * kk] + 32 * D * s2);
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(da + ofs[2 * kk + 1] + 32 * D * s2);
           return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         };
         i32x8 op[2];
@@ -416,115 +618,59 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
           if (i + 1 < 2 * KK) op[(i + 1) & 1] = ldd(i + 1);
           const int kk = i >> 1, s2 = i & 1;
           // A: dO^ codes (E5M2, format 1), B: V codes (E4M3, format 0), unit scales
-          dp[s2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op[i & 1], vreg[kk], kk == 0 ? f32x16{} : dp[s2], 1,
+          dp[s2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op[i & 1], vop(kk), kk == 0 ? f32x16{} : dp[s2], 1,
                                                                   0, 0, 127, 0, 127);
           __builtin_amdgcn_sched_barrier(0);
         }
-      }
-      // P and dS of (query 32 s2 + 16 hh + r, this lane's key).  Padded query
-      // rows have L = +inf (P = 0); keys past the sequence and (causal) keys
-      // after the query are masked, which only the wave's boundary chunks need.
-      float pv[2][16], dsv[2][16];
-      float amp[2], ams[2];
-      const int wkey_last = kb * BWD_ROWS + wave * 32 + 31;
-      const bool all_live = wkey_last < p.N && (!CAUSAL || wkey_last <= c * BWD_CHUNK);
-      auto elements = [&](auto masked) {
+        // dS = P (dP s - D) of (query 32 s2 + 16 hh + r, this lane's key)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          amp[s2] = 0.0f;
-          ams[s2] = 0.0f;
-          // the 16 rows' L and D as four 16-byte reads each, issued together
-          f32x4 lr[4], dr[4];
+          amx[s2] = 0.0f;
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            lr[v] = *reinterpret_cast<const f32x4*>(&sL[buf][32 * s2 + 16 * hh + 4 * v]);
-            dr[v] = *reinterpret_cast<const f32x4*>(&sD[buf][32 * s2 + 16 * hh + 4 * v]);
-          }
+            const f32x4 dr = *reinterpret_cast<const f32x4*>(&sD[buf][32 * s2 + 16 * hh + 4 * v]);
+            const f32x4 pp = sP[buf][kw][s2][v][lane];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int ql = 32 * s2 + 16 * hh + r, qi = c * BWD_CHUNK + ql;
-            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[s2][r], cc, -lr[r >> 2][r & 3]));
-            if (decltype(masked)::value) pr = (key < p.N && (!CAUSAL || key <= qi)) ? pr : 0.0f;
-            const float ds = pr * __builtin_fmaf(dp[s2][r], sdv, -dr[r >> 2][r & 3]);
-            pv[s2][r] = pr;
-            dsv[s2][r] = ds;
-            amp[s2] = __builtin_fmaxf(amp[s2], pr);
-            ams[s2] = __builtin_fmaxf(ams[s2], __builtin_fabsf(ds));
+            for (int j = 0; j < 4; ++j) {
+              const float ds = pp[j] * __builtin_fmaf(dp[s2][4 * v + j], sdv, -dr[j]);
+              pv[s2][4 * v + j] = ds;
+              amx[s2] = __builtin_fmaxf(amx[s2], __builtin_fabsf(ds));
+            }
           }
         }
-      };
-      if (all_live) elements(std::false_type{});
-      else elements(std::true_type{});
-      // block maxima over the 32 queries of each sub-tile: this lane's 16 and lane^32's 16
-      int ep[2], es[2];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const auto wp = __builtin_amdgcn_permlane32_swap(__float_as_uint(amp[s2]), __float_as_uint(amp[s2]), false, false);
-        const auto ws = __builtin_amdgcn_permlane32_swap(__float_as_uint(ams[s2]), __float_as_uint(ams[s2]), false, false);
-        ep[s2] = mx_e4m3_exponent(__builtin_fmaxf(__uint_as_float(wp[0]), __uint_as_float(wp[1])));
-        es[s2] = mx_e4m3_exponent(__builtin_fmaxf(__uint_as_float(ws[0]), __uint_as_float(ws[1])));
       }
-      // P~^T as the A operand of dV: bytes 0..15 sub-tile 0, bytes 16..31 sub-tile 1 (the
-      // k-blocks of the FP8 operand); lane half hh supplies the exponent of block hh
-      i32x8 pa;
-      float limp[2], scp[2], lims[2], scs[2];
+      // dS~: E4M3 of dS 2^-e (blocks of 32 queries, as for P~), back to
+      // float, times 2^e: exact in bf16
+      int es[2];
+      float lims[2], scs[2];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        limp[s2] = __builtin_ldexpf(448.0f, ep[s2]);
-        scp[s2] = e8m0_scale(ep[s2]);
+        const auto ws = __builtin_amdgcn_permlane32_swap(__float_as_uint(amx[s2]), __float_as_uint(amx[s2]), false, false);
+        es[s2] = mx_e4m3_exponent(__builtin_fmaxf(__uint_as_float(ws[0]), __uint_as_float(ws[1])));
         lims[s2] = __builtin_ldexpf(448.0f, es[s2]);
         scs[s2] = e8m0_scale(es[s2]);
       }
+      if (dump && hh == 0)
 #pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const int s2 = w >> 2, r = 4 * (w & 3);
-        s16x2 t = {0, 0};
-        t = mx_e4m3_pair<false>(t, pv[s2][r], pv[s2][r + 1], limp[s2], scp[s2]);
-        t = mx_e4m3_pair<true>(t, pv[s2][r + 2], pv[s2][r + 3], limp[s2], scp[s2]);
-        pa[w] = __builtin_bit_cast(int, t);
-      }
-      const int scale_p = (hh ? ep[1] : ep[0]) + 127;
-      const bool dump = DEBUG && b == p.dbg_b && h == p.dbg_h;
-      if (dump) {
-#pragma unroll
-        for (int w = 0; w < 8; ++w)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int qi = c * BWD_CHUNK + 32 * (w >> 2) + 16 * hh + 4 * (w & 3) + j;
-            p.dbg_pt[(int64_t)qi * npad + key] = (uint8_t)((uint32_t)pa[w] >> (8 * j));
-          }
-        if (hh == 0)
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            p.dbg_pt_e[(int64_t)(2 * c + s2) * npad + key] = (uint8_t)(ep[s2] + 127);
-            p.dbg_dsk_e[(int64_t)(2 * c + s2) * npad + key] = (uint8_t)(es[s2] + 127);
-          }
-      }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d = 32 * dt + ln;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(&sDOT[buf][d * DTS + 16 * hh]);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(&sDOT[buf][d * DTS + 32 + 16 * hh]);
-        const i32x8 bb = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        // A: P~ (E4M3, format 0) with its block exponents, B: dO^ codes (E5M2, format 1)
-        dv[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pa, bb, dv[dt], 0, 1, 0, scale_p, 0, 127);
-      }
-      // dS~: E4M3 of dS 2^-e (same blocks), back to float, times 2^e: exact in bf16
+        for (int s2 = 0; s2 < 2; ++s2) p.dbg_dsk_e[(int64_t)(2 * cp + s2) * npad + key] = (uint8_t)(es[s2] + 127);
       uint32_t dsq[2][8];                       // bf16 pairs
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const s16x2 q2 = mx_e4m3_pair<false>(s16x2{0, 0}, dsv[s2][r], dsv[s2][r + 1], lims[s2], scs[s2]);
+          const s16x2 q2 = mx_e4m3_pair<false>(s16x2{0, 0}, pv[s2][r], pv[s2][r + 1], lims[s2], scs[s2]);
           dsq[s2][r / 2] = mx_e4m3_pair_bf16(q2, scs[s2]);
           if (dump) {
             const uint32_t wq = __builtin_bit_cast(uint32_t, q2);
-            const int qi = c * BWD_CHUNK + 32 * s2 + 16 * hh + r;
+            const int qi = cp * BWD_CHUNK + 32 * s2 + 16 * hh + r;
             p.dbg_dsk[(int64_t)qi * npad + key] = (uint8_t)wq;
             p.dbg_dsk[(int64_t)(qi + 1) * npad + key] = (uint8_t)(wq >> 8);
           }
         }
-      // dK: k-step j takes queries 32 (j/2) + 16 hh + 8 (j%2) + [0, 8) in both operands
+      // dK: k-step j takes queries 32 (j/2) + 16 hh + 8 (j%2) + [0, 8) in both
+      // operands; the Q^T operand comes from the row-major Q^ tile by two
+      // transposing reads of 4 queries each
+      const uint8_t* qt = sQ[slot];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int s2 = j >> 1, r0 = 8 * (j & 1);
@@ -532,27 +678,29 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
                                                           dsq[s2][r0 / 2 + 2], dsq[s2][r0 / 2 + 3]});
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const int d = 32 * dt + ln;
-          const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&sQT[buf][d * QTS + 32 * s2 + 16 * hh + r0]);
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, dk[dt], 0, 0, 0);
+          const int rowoff = (32 * s2 + r0) * 2 * D;
+          const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)(__attribute__((address_space(3))) const void*)(qt + ofs[2 * KK + 2 * dt] + rowoff));
+          const s16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)(__attribute__((address_space(3))) const void*)(qt + ofs[2 * KK + 2 * dt + 1] + rowoff));
+          const u32x2 w1 = __builtin_bit_cast(u32x2, r1), w2 = __builtin_bit_cast(u32x2, r2);
+          const bf16x8 bq = __builtin_bit_cast(bf16x8, u32x4{w1[0], w1[1], w2[0], w2[1]});
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, acc[dt], 0, 0, 0);
         }
       }
+      }
+      step_end(gn, cn);
     }
-    store(buf ^ 1);
-    __syncthreads();
   }
   // C[key row][d]: lane holds d = 32 dt + ln, register r holds key row out_row(r, hh)
-  const float fk = p.sigma * *p.gq;
+  const float f = s_side ? sdo : p.sigma * *p.gq;
+  float* out = s_side ? p.dv_out : p.dk_out;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int kr = kb * BWD_ROWS + wave * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (kr < p.N) {
-        const int64_t o = (((int64_t)b * p.N + kr) * p.Hkv + hk) * D + 32 * dt + ln;
-        p.dv_out[o] = dv[dt][r] * sdo;
-        p.dk_out[o] = dk[dt][r] * fk;
-      }
+      const int kr = kb * BWD_ROWS + kw * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      if (kr < p.N) out[(((int64_t)b * p.N + kr) * p.Hkv + hk) * D + 32 * dt + ln] = acc[dt][r] * f;
     }
 }
 
@@ -798,7 +946,7 @@ hipError_t launch_bwd_main(const BwdParams& p, int D, bool causal, bool debug, h
   const dim3 gq((unsigned)(p.npad / BWD_ROWS), (unsigned)p.Hq, (unsigned)p.B);
 #define BWD_LAUNCH(DD, C, G)                                                         \
   do {                                                                               \
-    hipLaunchKernelGGL((bwd_dkdv_kernel<DD, C, G>), gkv, dim3(256), 0, st, p);       \
+    hipLaunchKernelGGL((bwd_dkdv_kernel<DD, C, G>), gkv, dim3(512), 0, st, p);       \
     hipLaunchKernelGGL((bwd_dq_kernel<DD, C, G>), gq, dim3(256), 0, st, p);          \
   } while (0)
   if (debug) {
