@@ -298,7 +298,7 @@ __device__ inline uint32_t bwd_lds_address(const void* p) {
 //   LDS: the Q^ chunk row-major in a ring of three (chunk x in slot x % 3:
 //   the S side's chunk, the dP side's chunk and the next), read straight for
 //   S and through transposing reads (ds_read_b64_tr_b16) as the Q^T operand of
-//   dK; dO^ row-major and dO^T, L and D, and P, two buffers each.
+//   dK; dO^ row-major, dO^T, L and P in two buffers each, D in a ring of three.
 // S / dP sub-tile s2 of a chunk: accumulator (lane half hh, register r) holds
 // query 32*s2 + 16*hh + r of the chunk; A row m of the S / dP products is
 // therefore query 32*s2 + 16*((m>>2)&1) + 4*(m>>3) + (m&3).
@@ -316,7 +316,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t sDO[2][DOB];
   __shared__ __attribute__((aligned(1024))) uint8_t sDOT[2][DOTB];
   __shared__ __attribute__((aligned(16))) float sL[2][BWD_CHUNK];   // read as 16-byte vectors
-  __shared__ __attribute__((aligned(16))) float sD[2][BWD_CHUNK];
+  __shared__ __attribute__((aligned(16))) float sD[3][BWD_CHUNK];   // chunk x in slot x % 3
   __shared__ __attribute__((aligned(16))) f32x4 sP[2][4][2][4][64];  // [buffer][key block][s2][r / 4][lane]
   int kb = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   if (CAUSAL) {
@@ -410,8 +410,8 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
     }
     if (wave == 0) bwd_dma4(p.lv + q0, (uint32_t)(4 * lane), bwd_lds_address(&sL[buf][0]));
   };
-  // the dP side's tiles of chunk (g, c): dO^ and D -> buffer
-  auto copy_d = [&](int g, int c, int buf) {
+  // the dP side's tiles of chunk (g, c): dO^ -> buffer, D -> ring slot
+  auto copy_d = [&](int g, int c, int buf, int slot) {
     const int64_t q0 = chunk_row(g, c);
     const uint8_t* db0 = p.dorm + q0 * D;
 #pragma unroll
@@ -419,7 +419,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
       const int j = wave + NW * t;
       if (j < NDOC) bwd_dma16(db0, odc[t], bwd_lds_address(&sDO[buf][0]) + 1024 * j);
     }
-    if (wave == 1) bwd_dma4(p.dv + q0, (uint32_t)(4 * lane), bwd_lds_address(&sD[buf][0]));
+    if (wave == 1) bwd_dma4(p.dv + q0, (uint32_t)(4 * lane), bwd_lds_address(&sD[slot][0]));
   };
   // per-lane operand read offsets (bytes within a buffer), one array for both
   // sides: S side Q rows per k-step, then the dO^T halves; dP side dO rows
@@ -454,24 +454,26 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
   }
 
   const int wkey_last = kb * BWD_ROWS + kw * 32 + 31;
-  // prologue: the S side's tiles of chunk 0
+  // prologue: the tiles of chunk 0
   copy_s(0, c0, 0, 0);
+  copy_d(0, c0, 0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   // Each side runs its own copy of the step loop (one side per wave for the
   // whole kernel; separate loops keep each side's accumulator in place).
-  // Both loops take the same number of barriers.  Per step: the copies for
-  // step + 1 (the S side's chunk step + 1, the dP side's chunk step), this
-  // side's work, then a barrier once this wave's copies have landed and its
-  // LDS writes are done.
+  // Both loops take the same number of barriers.  Per step: the copies of
+  // chunk step + 1, this side's work, then a barrier once this wave's copies
+  // have landed and its LDS writes are done.
   // (g, c): the S side's chunk of step s; (gp, cp): the dP side's (s - 1)
   int g = 0, c = c0, gp = 0, cp = c0;
   auto step_begin = [&](int step, int& gn, int& cn) {
     gn = g;
     cn = c + 1;
     if (cn == nchunks) { cn = c0; ++gn; }
-    if (step + 1 < total) copy_s(gn, cn, (step + 1) % 3, (step + 1) & 1);
-    if (step < total) copy_d(g, c, step & 1);
+    if (step + 1 < total) {
+      copy_s(gn, cn, (step + 1) % 3, (step + 1) & 1);
+      copy_d(gn, cn, (step + 1) & 1, (step + 1) % 3);
+    }
   };
   auto step_end = [&](int gn, int cn) {
     // the copies for step + 1 (this wave's) have landed and this wave's LDS
@@ -590,21 +592,90 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
       step_end(gn, cn);
     }
   } else {
+    // The dP side orders its step vector work first, matrix work last, so that
+    // it runs opposite its partner (S products first, then P): step s takes
+    // dS, dS~ and dK of chunk s - 1 (with the dP of that chunk, made at the
+    // end of step s - 1 and kept in registers), then dP of chunk s.
+    f32x16 dp[2];
     for (int step = 0; step <= total; ++step) {
       int gn, cn;
       step_begin(step, gn, cn);
       if (step > 0) {
-
-      // the dP side: chunk (gp, cp) of step - 1
-      const int buf = (step - 1) & 1, slot = (step - 1) % 3;
-      const int h = hk * G + gp;
-      const bool dump = DEBUG && b == p.dbg_b && h == p.dbg_h;
-      float pv[2][16];
-      float amx[2];
-      {
-        f32x16 dp[2];
-        // dP of both sub-tiles: the two chains alternate, operands one ahead
-        const uint8_t* da = sDO[buf];
+        // chunk (gp, cp) of step - 1
+        const int buf = (step - 1) & 1, slot = (step - 1) % 3;
+        const int h = hk * G + gp;
+        const bool dump = DEBUG && b == p.dbg_b && h == p.dbg_h;
+        float pv[2][16];
+        float amx[2];
+        // dS = P (dP s - D) of (query 32 s2 + 16 hh + r, this lane's key)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          amx[s2] = 0.0f;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const f32x4 dr = *reinterpret_cast<const f32x4*>(&sD[slot][32 * s2 + 16 * hh + 4 * v]);
+            const f32x4 pp = sP[buf][kw][s2][v][lane];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float ds = pp[j] * __builtin_fmaf(dp[s2][4 * v + j], sdv, -dr[j]);
+              pv[s2][4 * v + j] = ds;
+              amx[s2] = __builtin_fmaxf(amx[s2], __builtin_fabsf(ds));
+            }
+          }
+        }
+        // dS~: E4M3 of dS 2^-e (blocks of 32 queries, as for P~), back to
+        // float, times 2^e: exact in bf16
+        int es[2];
+        float lims[2], scs[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const auto ws = __builtin_amdgcn_permlane32_swap(__float_as_uint(amx[s2]), __float_as_uint(amx[s2]), false, false);
+          es[s2] = mx_e4m3_exponent(__builtin_fmaxf(__uint_as_float(ws[0]), __uint_as_float(ws[1])));
+          lims[s2] = __builtin_ldexpf(448.0f, es[s2]);
+          scs[s2] = e8m0_scale(es[s2]);
+        }
+        if (dump && hh == 0)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) p.dbg_dsk_e[(int64_t)(2 * cp + s2) * npad + key] = (uint8_t)(es[s2] + 127);
+        uint32_t dsq[2][8];                       // bf16 pairs
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const s16x2 q2 = mx_e4m3_pair<false>(s16x2{0, 0}, pv[s2][r], pv[s2][r + 1], lims[s2], scs[s2]);
+            dsq[s2][r / 2] = mx_e4m3_pair_bf16(q2, scs[s2]);
+            if (dump) {
+              const uint32_t wq = __builtin_bit_cast(uint32_t, q2);
+              const int qi = cp * BWD_CHUNK + 32 * s2 + 16 * hh + r;
+              p.dbg_dsk[(int64_t)qi * npad + key] = (uint8_t)wq;
+              p.dbg_dsk[(int64_t)(qi + 1) * npad + key] = (uint8_t)(wq >> 8);
+            }
+          }
+        // dK: k-step j takes queries 32 (j/2) + 16 hh + 8 (j%2) + [0, 8) in both
+        // operands; the Q^T operand comes from the row-major Q^ tile by two
+        // transposing reads of 4 queries each
+        const uint8_t* qt = sQ[slot];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int s2 = j >> 1, r0 = 8 * (j & 1);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{dsq[s2][r0 / 2], dsq[s2][r0 / 2 + 1],
+                                                            dsq[s2][r0 / 2 + 2], dsq[s2][r0 / 2 + 3]});
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const int rowoff = (32 * s2 + r0) * 2 * D;
+            const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(__attribute__((address_space(3))) const void*)(qt + ofs[2 * KK + 2 * dt] + rowoff));
+            const s16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(__attribute__((address_space(3))) const void*)(qt + ofs[2 * KK + 2 * dt + 1] + rowoff));
+            const u32x2 w1 = __builtin_bit_cast(u32x2, r1), w2 = __builtin_bit_cast(u32x2, r2);
+            const bf16x8 bq = __builtin_bit_cast(bf16x8, u32x4{w1[0], w1[1], w2[0], w2[1]});
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, acc[dt], 0, 0, 0);
+          }
+        }
+      }
+      if (step < total) {
+        // dP of chunk (g, c), both sub-tiles: the two chains alternate, operands one ahead
+        const uint8_t* da = sDO[step & 1];
         auto ldd = [&](int i) {    // operand i: k-step i / 2 of sub-tile i % 2 (two 16-byte halves)
           const int kk = i >> 1, s2 = i & 1;
           const u32x4 lo = *reinterpret_cast<const u32x4*>(da + ofs[2 * kk] + 32 * D * s2);
@@ -622,72 +693,6 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
                                                                   0, 0, 127, 0, 127);
           __builtin_amdgcn_sched_barrier(0);
         }
-        // dS = P (dP s - D) of (query 32 s2 + 16 hh + r, this lane's key)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          amx[s2] = 0.0f;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const f32x4 dr = *reinterpret_cast<const f32x4*>(&sD[buf][32 * s2 + 16 * hh + 4 * v]);
-            const f32x4 pp = sP[buf][kw][s2][v][lane];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float ds = pp[j] * __builtin_fmaf(dp[s2][4 * v + j], sdv, -dr[j]);
-              pv[s2][4 * v + j] = ds;
-              amx[s2] = __builtin_fmaxf(amx[s2], __builtin_fabsf(ds));
-            }
-          }
-        }
-      }
-      // dS~: E4M3 of dS 2^-e (blocks of 32 queries, as for P~), back to
-      // float, times 2^e: exact in bf16
-      int es[2];
-      float lims[2], scs[2];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const auto ws = __builtin_amdgcn_permlane32_swap(__float_as_uint(amx[s2]), __float_as_uint(amx[s2]), false, false);
-        es[s2] = mx_e4m3_exponent(__builtin_fmaxf(__uint_as_float(ws[0]), __uint_as_float(ws[1])));
-        lims[s2] = __builtin_ldexpf(448.0f, es[s2]);
-        scs[s2] = e8m0_scale(es[s2]);
-      }
-      if (dump && hh == 0)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) p.dbg_dsk_e[(int64_t)(2 * cp + s2) * npad + key] = (uint8_t)(es[s2] + 127);
-      uint32_t dsq[2][8];                       // bf16 pairs
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const s16x2 q2 = mx_e4m3_pair<false>(s16x2{0, 0}, pv[s2][r], pv[s2][r + 1], lims[s2], scs[s2]);
-          dsq[s2][r / 2] = mx_e4m3_pair_bf16(q2, scs[s2]);
-          if (dump) {
-            const uint32_t wq = __builtin_bit_cast(uint32_t, q2);
-            const int qi = cp * BWD_CHUNK + 32 * s2 + 16 * hh + r;
-            p.dbg_dsk[(int64_t)qi * npad + key] = (uint8_t)wq;
-            p.dbg_dsk[(int64_t)(qi + 1) * npad + key] = (uint8_t)(wq >> 8);
-          }
-        }
-      // dK: k-step j takes queries 32 (j/2) + 16 hh + 8 (j%2) + [0, 8) in both
-      // operands; the Q^T operand comes from the row-major Q^ tile by two
-      // transposing reads of 4 queries each
-      const uint8_t* qt = sQ[slot];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int s2 = j >> 1, r0 = 8 * (j & 1);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{dsq[s2][r0 / 2], dsq[s2][r0 / 2 + 1],
-                                                          dsq[s2][r0 / 2 + 2], dsq[s2][r0 / 2 + 3]});
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int rowoff = (32 * s2 + r0) * 2 * D;
-          const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(__attribute__((address_space(3))) const void*)(qt + ofs[2 * KK + 2 * dt] + rowoff));
-          const s16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(__attribute__((address_space(3))) const void*)(qt + ofs[2 * KK + 2 * dt + 1] + rowoff));
-          const u32x2 w1 = __builtin_bit_cast(u32x2, r1), w2 = __builtin_bit_cast(u32x2, r2);
-          const bf16x8 bq = __builtin_bit_cast(bf16x8, u32x4{w1[0], w1[1], w2[0], w2[1]});
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, acc[dt], 0, 0, 0);
-        }
-      }
       }
       step_end(gn, cn);
     }
