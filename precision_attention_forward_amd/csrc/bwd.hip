@@ -256,6 +256,14 @@ __device__ __host__ inline int swz_qrows(int R) {
   if (RB == 128) return ((R >> 1) & 1) | (((R >> 4) & 1) << 1) | (((R ^ (R >> 2)) & 1) << 2);
   return ((R >> 4) & 1) | ((((R >> 1) ^ (R >> 2)) & 1) << 1);
 }
+// The Q^ tile of the dK/dV kernel (rows of 2D bytes) is also read through
+// transposing reads (4 consecutive rows x 32 bytes per 16 lanes), which this
+// swizzle spreads over the banks as well.
+template <int D>
+__device__ __host__ inline int swz_qtile(int R) {
+  if (D == 128) return (R & 3) | ((((R >> 2) ^ R) & 1) << 2) | ((((R >> 4) ^ (R >> 1)) & 1) << 3);
+  return ((R >> 1) & 1) | (((R >> 2) & 1) << 1) | ((((R >> 4) ^ (R >> 1)) & 1) << 2);
+}
 // transposed tiles: row d = 32 dt + ln read by lanes ln = 0..31 (bits 0-3 vary
 // across 16 lanes); 128-byte rows (bf16 x 64) and 64-byte rows (8-bit x 64)
 __device__ __host__ inline int swz_drows128(int d) {
@@ -377,7 +385,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
   for (int t = 0; t < NQW; ++t) {                          // Q rows: 2D bytes, 1024 / 2D rows per copy
     const int j = wave + NW * t;
     const int r = j * (1024 / (2 * D)) + (16 * lane) / (2 * D), c = ((16 * lane) % (2 * D)) / 16;
-    oqc[t] = (uint32_t)(r * 2 * D + 16 * (c ^ swz_qrows<2 * D>(r)));
+    oqc[t] = (uint32_t)(r * 2 * D + 16 * (c ^ swz_qtile<D>(r)));
   }
 #pragma unroll
   for (int t = 0; t < NDOW; ++t) {                         // dO rows: D bytes
@@ -429,7 +437,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
   uint32_t ofs[NOFS];
   if (s_side) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) ofs[ks] = (uint32_t)(R0 * 2 * D + 16 * ((2 * ks + hh) ^ swz_qrows<2 * D>(R0)));
+    for (int ks = 0; ks < KS; ++ks) ofs[ks] = (uint32_t)(R0 * 2 * D + 16 * ((2 * ks + hh) ^ swz_qtile<D>(R0)));
 #pragma unroll
     for (int lh = 0; lh < 2; ++lh) ofs[KS + lh] = (uint32_t)(ln * 64 + 16 * ((hh + 2 * lh) ^ swz_drows64(ln)));
   } else {
@@ -449,7 +457,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
       for (int half = 0; half < 2; ++half) {
         const int R = 16 * (g4 >> 1) + 4 * half + (c16 >> 2);
         const int byte = 2 * (32 * dt + 16 * (g4 & 1) + 4 * (c16 & 3));
-        ofs[2 * KK + 2 * dt + half] = (uint32_t)(R * 2 * D + 16 * ((byte / 16) ^ swz_qrows<2 * D>(R)) + (byte % 16));
+        ofs[2 * KK + 2 * dt + half] = (uint32_t)(R * 2 * D + 16 * ((byte / 16) ^ swz_qtile<D>(R)) + (byte % 16));
       }
   }
 
