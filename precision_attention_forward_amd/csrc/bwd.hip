@@ -718,18 +718,42 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ.  Workgroup: 4 waves, queries qb*128 + 32*wave + (lane & 31) of head h.
-// S^T sub-tile s2 of a 64-key chunk: accumulator (lane half hh, register r)
-// holds key 32*hh + 16*s2 + r of the chunk; A row m of the S^T / dP^T
-// products is therefore key 32*((m>>2)&1) + 16*s2 + 4*(m>>3) + (m&3).
+// dQ tiles: the K^ chunk (rows = keys, 2D bytes) is read straight as the A
+// operand of S^T and through transposing reads as the K^T operand of dQ; the V
+// chunk (rows = keys, D bytes) straight as the A operand of dP^T.  A rows are
+// keys kr0(m) + 16 s2 with kr0(m) = 32 ((m>>2)&1) + 4 (m>>3) + (m&3).
+template <int D>
+__device__ __host__ inline int swz_ktile(int R) {
+  if (D == 128) return (R & 3) | ((((R >> 2) ^ R) & 1) << 2) | ((((R >> 5) ^ (R >> 1)) & 1) << 3);
+  return ((R >> 1) & 1) | (((R >> 2) & 1) << 1) | ((((R >> 5) ^ (R >> 1)) & 1) << 2);
+}
+template <int D>
+__device__ __host__ inline int swz_vtile(int R) {
+  if (D == 128) return ((R >> 1) & 1) | (((R >> 2) & 1) << 1) | (((R >> 5) & 1) << 2);
+  return ((R >> 2) & 1) | (((R >> 5) & 1) << 1);
+}
+
+// dQ.  Workgroup: 8 waves for 128 queries qb*128 + 32*qw + (lane & 31) of
+// head h, two waves per 32-query block qw on one SIMD (waves qw and qw + 4):
+//   S side (waves 0-3):  S^T = K^ Q^T, P = 2^(t - L)
+//   dP side (waves 4-7): dP^T = V dO^T, dS = P (dP - D), dS~ and dQ^T += K^T dS~^T
+// as in the dK/dV kernel: P goes to the dP side through LDS as float32; the
+// dP side takes dS, dS~ and dQ of chunk s - 1 first and dP of chunk s last.
+// LDS: K^ in a ring of three (the S side's chunk, the dP side's and the
+// next), V and P in two buffers.  S^T sub-tile s2 of a 64-key chunk:
+// accumulator (lane half hh, register r) holds key 32*hh + 16*s2 + r of the
+// chunk; A row m of the S^T / dP^T products is therefore key
+// 32*((m>>2)&1) + 16*s2 + 4*(m>>3) + (m&3).
 template <int D, bool CAUSAL, bool DEBUG>
-__global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdParams p) {
+__global__ void __launch_bounds__(512, 1) bwd_dq_kernel(BwdParams p) {
   constexpr int KS = D / 16, DT = D / 32, KK = D / 64;
-  constexpr int KSR = D + 8, KTS = BWD_CHUNK + 8;         // padded row strides (bf16 elements)
-  constexpr int VS = D + 16;                              // bytes
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2][BWD_CHUNK * KSR];
-  __shared__ __attribute__((aligned(16))) __bf16 sKT[2][D * KTS];
-  __shared__ __attribute__((aligned(16))) uint8_t sV[2][BWD_CHUNK * VS];
+  constexpr int NW = 8;
+  constexpr int KB = BWD_CHUNK * D * 2, VB = BWD_CHUNK * D;        // bytes of one K^ / V chunk
+  constexpr int NKC = KB / 1024, NVC = VB / 1024;
+  constexpr int NKW = (NKC + NW - 1) / NW, NVW = (NVC + NW - 1) / NW;
+  __shared__ __attribute__((aligned(1024))) uint8_t sK[3][KB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV[2][VB];
+  __shared__ __attribute__((aligned(16))) f32x4 sP[2][4][2][4][64];  // [buffer][query block][s2][r / 4][lane]
   int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   if (CAUSAL) {
     // Causal: a query block's work grows with qb.  Dispatch takes the longest
@@ -744,189 +768,250 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdParams p) {
     b = (r % per_g) / p.Hkv;
     h = ((r % per_g) % p.Hkv) * G + g;
   }
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, ln = lane & 31;
-  const int q = qb * BWD_ROWS + wave * 32 + ln;
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, ln = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool s_side = wave < 4;                 // uniform
+  const int qw = wave & 3;
+  const int q = qb * BWD_ROWS + qw * 32 + ln;
   const int hk = h / (p.Hq / p.Hkv);
   const int64_t npad = p.npad;
   const int64_t qrow = ((int64_t)b * p.Hq + h) * npad + q;
-  bf16x8 qreg[KS];
+  // resident operand (one array for both sides): Q^ as KS bf16x8 (S side, B
+  // operand of S^T) or dO^ as KK i32x8 (dP side, B operand of dP^T)
+  u32x4 res[KS];
+  if (s_side) {
 #pragma unroll
-  for (int s = 0; s < KS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(p.qrm + qrow * D + 16 * s + 8 * hh);
-  i32x8 doreg[KK];
+    for (int s = 0; s < KS; ++s) res[s] = *reinterpret_cast<const u32x4*>(p.qrm + qrow * D + 16 * s + 8 * hh);
+  } else {
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(p.dorm + qrow * D + 64 * kk + 16 * hh);
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(p.dorm + qrow * D + 64 * kk + 32 + 16 * hh);
-    doreg[kk] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    for (int kk = 0; kk < KK; ++kk) {
+      res[2 * kk] = *reinterpret_cast<const u32x4*>(p.dorm + qrow * D + 64 * kk + 16 * hh);
+      res[2 * kk + 1] = *reinterpret_cast<const u32x4*>(p.dorm + qrow * D + 64 * kk + 32 + 16 * hh);
+    }
   }
-  const float lq = p.lv[qrow], dq_d = p.dv[qrow];
-  f32x16 acc[DT];
-#pragma unroll
-  for (int i = 0; i < DT; ++i) acc[i] = f32x16{};
+  auto qop = [&](int st) { return __builtin_bit_cast(bf16x8, res[st]); };
+  auto dop = [&](int kk) {
+    const u32x4 lo = res[2 * kk], hi = res[2 * kk + 1];
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+  const float lrow = s_side ? p.lv[qrow] : p.dv[qrow];   // L log2 e (S side) or D (dP side) of the lane's query
   const float cc = (float)((double)p.sigma * 1.4426950408889634 * (double)(*p.gq) * (double)(*p.gk));
   const float sdv = *p.sdo * *p.sv;
   const int64_t khead = (int64_t)b * p.Hkv + hk;
   int nchunks = (int)(npad / BWD_CHUNK);
   if (CAUSAL) nchunks = min(nchunks, (qb * BWD_ROWS + BWD_ROWS) / BWD_CHUNK);
   const int m = ln;
-  // chunk copies double-buffered through registers, as in the dK/dV kernel
-  constexpr int NK = BWD_CHUNK * D / 8 / 256, NKT = D * (BWD_CHUNK / 8) / 256, NV = BWD_CHUNK * D / 16 / 256;
-  u32x4 pk[NK], pkt[NKT], pv4[NV];
-  uint32_t ok[NK], okt[NKT], ov[NV];               // per-lane byte offsets (loop invariant)
+  const int wq_first = qb * BWD_ROWS + qw * 32;
+
+  // ---- chunk copies (all 8 waves): K^ and V rows, wave w takes copies w + 8 t
+  uint32_t okc[NKW], ovc[NVW];
 #pragma unroll
-  for (int i = 0; i < NK; ++i) {
-    const int it = tid + 256 * i, row = it / (D / 8), g8 = it % (D / 8);
-    ok[i] = (uint32_t)(row * D + 8 * g8) * 2u;
+  for (int t = 0; t < NKW; ++t) {
+    const int j = wave + NW * t;
+    const int r = j * (1024 / (2 * D)) + (16 * lane) / (2 * D), c = ((16 * lane) % (2 * D)) / 16;
+    okc[t] = (uint32_t)(r * 2 * D + 16 * (c ^ swz_ktile<D>(r)));
   }
 #pragma unroll
-  for (int i = 0; i < NKT; ++i) {
-    const int it = tid + 256 * i, d = it / (BWD_CHUNK / 8), r8 = it % (BWD_CHUNK / 8);
-    okt[i] = ((uint32_t)d * (uint32_t)npad + 8u * r8) * 2u;
+  for (int t = 0; t < NVW; ++t) {
+    const int j = wave + NW * t;
+    const int r = j * (1024 / D) + (16 * lane) / D, c = ((16 * lane) % D) / 16;
+    ovc[t] = (uint32_t)(r * D + 16 * (c ^ swz_vtile<D>(r)));
   }
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int it = tid + 256 * i, row = it / (D / 16), g16 = it % (D / 16);
-    ov[i] = (uint32_t)(row * D + 16 * g16);
-  }
-  auto fetch = [&](int c) {
+  auto copy_chunk = [&](int c, int slot, int buf) {
     const int64_t k0 = khead * npad + (int64_t)c * BWD_CHUNK;
-    const __bf16* kb0 = p.krm + k0 * D;
-    const __bf16* ktb0 = p.kt + khead * D * npad + (int64_t)c * BWD_CHUNK;
+    const uint8_t* kb0 = reinterpret_cast<const uint8_t*>(p.krm + k0 * D);
     const uint8_t* vb0 = p.vrm + k0 * D;
 #pragma unroll
-    for (int i = 0; i < NK; ++i) pk[i] = load16(kb0, ok[i]);
-#pragma unroll
-    for (int i = 0; i < NKT; ++i) pkt[i] = load16(ktb0, okt[i]);
-#pragma unroll
-    for (int i = 0; i < NV; ++i) pv4[i] = load16(vb0, ov[i]);
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int it = tid + 256 * i, row = it / (D / 8), g8 = it % (D / 8);
-      *reinterpret_cast<u32x4*>(&sK[buf][row * KSR + 8 * g8]) = pk[i];
+    for (int t = 0; t < NKW; ++t) {
+      const int j = wave + NW * t;
+      if (j < NKC) bwd_dma16(kb0, okc[t], bwd_lds_address(&sK[slot][0]) + 1024 * j);
     }
 #pragma unroll
-    for (int i = 0; i < NKT; ++i) {
-      const int it = tid + 256 * i, d = it / (BWD_CHUNK / 8), r8 = it % (BWD_CHUNK / 8);
-      *reinterpret_cast<u32x4*>(&sKT[buf][d * KTS + 8 * r8]) = pkt[i];
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int it = tid + 256 * i, row = it / (D / 16), g16 = it % (D / 16);
-      *reinterpret_cast<u32x4*>(&sV[buf][row * VS + 16 * g16]) = pv4[i];
+    for (int t = 0; t < NVW; ++t) {
+      const int j = wave + NW * t;
+      if (j < NVC) bwd_dma16(vb0, ovc[t], bwd_lds_address(&sV[buf][0]) + 1024 * j);
     }
   };
-  fetch(0);
-  store(0);
-  __syncthreads();
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
-    fetch(c + 1 < nchunks ? c + 1 : c);
-
-    f32x16 s[2], dp[2];
-    // S^T and dP^T of both 16-key sub-tiles, as in the dK/dV kernel: the two
-    // accumulation chains alternate and each A operand is read from LDS ahead
-    // of its matrix instruction (fenced); each chain sums its k-steps in order
-    {
-      const int kr0 = 32 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
-      const __bf16* ka = &sK[buf][kr0 * KSR + 8 * hh];
-      auto lda = [&](int i) {      // operand i: k-step i / 2 of sub-tile i % 2
-        return *reinterpret_cast<const bf16x8*>(ka + 16 * (i & 1) * KSR + 16 * (i >> 1));
-      };
-      bf16x8 op[3];
-      op[0] = lda(0);
-      op[1] = lda(1);
+  // per-lane operand read offsets: S side K^ rows per k-step; dP side V rows
+  // per (k-step, half), then the transposing K^ reads per (dt, half)
+  const int R0 = 32 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);   // A row of the S^T / dP^T products
+  constexpr int NOFS = KS > 2 * KK + 2 * DT ? KS : 2 * KK + 2 * DT;
+  uint32_t ofs[NOFS];
+  if (s_side) {
 #pragma unroll
-      for (int i = 0; i < 2 * KS; ++i) {
-        if (i + 2 < 2 * KS) op[(i + 2) % 3] = lda(i + 2);
-        const int st = i >> 1, s2 = i & 1;
-        s[s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], qreg[st], st == 0 ? f32x16{} : s[s2], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      const uint8_t* va = &sV[buf][kr0 * VS + 16 * hh];
-      auto ldv = [&](int i) {      // operand i: k-step i / 2 of sub-tile i % 2 (two 16-byte halves)
-        const uint8_t* r = va + 16 * (i & 1) * VS + 64 * (i >> 1);
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(r);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(r + 32);
-        return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      };
-      i32x8 ov[2];
-      ov[0] = ldv(0);
+    for (int ks = 0; ks < KS; ++ks) ofs[ks] = (uint32_t)(R0 * 2 * D + 16 * ((2 * ks + hh) ^ swz_ktile<D>(R0)));
+  } else {
 #pragma unroll
-      for (int i = 0; i < 2 * KK; ++i) {
-        if (i + 1 < 2 * KK) ov[(i + 1) & 1] = ldv(i + 1);
-        const int kk = i >> 1, s2 = i & 1;
-        // A: V codes (E4M3, format 0), B: dO^ codes (E5M2, format 1), unit scales
-        dp[s2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ov[i & 1], doreg[kk], kk == 0 ? f32x16{} : dp[s2], 0,
-                                                                1, 0, 127, 0, 127);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // dS of (this lane's query, key 32 hh + 16 s2 + r): one MX block per lane half
-    // (keys past the sequence and, causal, after the wave's first query are
-    // masked; only the last chunks need it)
-    float dsv[2][16];
-    float am = 0.0f;
-    const int wq_first = qb * BWD_ROWS + wave * 32;
-    const bool all_live = c * BWD_CHUNK + BWD_CHUNK <= p.N && (!CAUSAL || c * BWD_CHUNK + BWD_CHUNK - 1 <= wq_first);
-    auto elements = [&](auto masked) {
+    for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kj = c * BWD_CHUNK + 32 * hh + 16 * s2 + r;
-          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[s2][r], cc, -lq));
-          if (decltype(masked)::value) pr = (kj < p.N && (!CAUSAL || kj <= q)) ? pr : 0.0f;
-          const float ds = pr * __builtin_fmaf(dp[s2][r], sdv, -dq_d);
-          dsv[s2][r] = ds;
-          am = __builtin_fmaxf(am, __builtin_fabsf(ds));
-        }
-    };
-    if (all_live) elements(std::false_type{});
-    else elements(std::true_type{});
-    const int e = mx_e4m3_exponent(am);
-    const float lim = __builtin_ldexpf(448.0f, e), sc = e8m0_scale(e);
-    const bool dump = DEBUG && b == p.dbg_b && h == p.dbg_h;
-    if (dump) p.dbg_dsq_e[(int64_t)q * (npad / 32) + 2 * c + hh] = (uint8_t)(e + 127);
-    uint32_t dsq[2][8];                         // bf16 pairs
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const s16x2 q2 = mx_e4m3_pair<false>(s16x2{0, 0}, dsv[s2][r], dsv[s2][r + 1], lim, sc);
-        dsq[s2][r / 2] = mx_e4m3_pair_bf16(q2, sc);
-        const uint32_t wq = __builtin_bit_cast(uint32_t, q2);
-        if (dump) {
-          const int kj = c * BWD_CHUNK + 32 * hh + 16 * s2 + r;
-          p.dbg_dsq[(int64_t)q * npad + kj] = (uint8_t)wq;
-          p.dbg_dsq[(int64_t)q * npad + kj + 1] = (uint8_t)(wq >> 8);
-        }
-      }
-    // dQ^T: k-step j takes keys 32 hh + 16 (j/2) + 8 (j%2) + [0, 8) in both operands
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int s2 = j >> 1, r0 = 8 * (j & 1);
-      const bf16x8 bv = __builtin_bit_cast(bf16x8, u32x4{dsq[s2][r0 / 2], dsq[s2][r0 / 2 + 1],
-                                                         dsq[s2][r0 / 2 + 2], dsq[s2][r0 / 2 + 3]});
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d = 32 * dt + ln;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sKT[buf][d * KTS + 32 * hh + 16 * s2 + r0]);
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv, acc[dt], 0, 0, 0);
-      }
-    }
-    store(buf ^ 1);
-    __syncthreads();
-  }
-  // C[d row][query]: lane holds the query, register r holds d = 32 dt + out_row(r, hh)
-  if (q < p.N) {
-    const float fq = p.sigma * *p.gk;
-    float* out = p.dq_out + (((int64_t)b * p.N + q) * p.Hq + h) * D;
+      for (int lh = 0; lh < 2; ++lh)
+        ofs[2 * kk + lh] = (uint32_t)(R0 * D + 16 * ((4 * kk + hh + 2 * lh) ^ swz_vtile<D>(R0)));
+    // transposing reads of K^ for the dQ A operand: lane (g, c) of a 16-lane
+    // group reads 4 bf16 of key row 32 (g >> 1) + 4 half + (c >> 2) (+ 16 s2 +
+    // r0, which leave the swizzle unchanged) at channel 32 dt + 16 (g & 1) +
+    // 4 (c & 3); the transpose hands it channel 32 dt + 16 (g & 1) + c of 4 keys
+    const int g4 = lane >> 4, c16 = lane & 15;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) out[32 * dt + 8 * (r >> 2) + 4 * hh + (r & 3)] = acc[dt][r] * fq;
+      for (int half = 0; half < 2; ++half) {
+        const int R = 32 * (g4 >> 1) + 4 * half + (c16 >> 2);
+        const int byte = 2 * (32 * dt + 16 * (g4 & 1) + 4 * (c16 & 3));
+        ofs[2 * KK + 2 * dt + half] = (uint32_t)(R * 2 * D + 16 * ((byte / 16) ^ swz_ktile<D>(R)) + (byte % 16));
+      }
+  }
+
+  copy_chunk(0, 0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  auto step_end = [&]() {
+    // this wave's copies for the next step have landed and its LDS writes are
+    // done; after the barrier every wave's are, and the tiles of step - 1 may
+    // be overwritten
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  f32x16 acc[DT];                               // dQ^T (dP side)
+  if (s_side) {
+    for (int c = 0; c <= nchunks; ++c) {
+      if (c + 1 < nchunks) copy_chunk(c + 1, (c + 1) % 3, (c + 1) & 1);
+      if (c < nchunks) {
+        // S^T of both 16-key sub-tiles: the two chains alternate, operands two ahead
+        f32x16 s[2];
+        const uint8_t* ka = sK[c % 3];
+        auto lda = [&](int i) {    // operand i: k-step i / 2 of sub-tile i % 2
+          return *reinterpret_cast<const bf16x8*>(ka + ofs[i >> 1] + 16 * 2 * D * (i & 1));
+        };
+        bf16x8 op[3];
+        op[0] = lda(0);
+        op[1] = lda(1);
+#pragma unroll
+        for (int i = 0; i < 2 * KS; ++i) {
+          if (i + 2 < 2 * KS) op[(i + 2) % 3] = lda(i + 2);
+          const int st = i >> 1, s2 = i & 1;
+          s[s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], qop(st), st == 0 ? f32x16{} : s[s2], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // P of (this lane's query, key 32 hh + 16 s2 + r) to LDS; keys past the
+        // sequence and (causal) after the query are masked, which only the
+        // last chunks need
+        const bool all_live = c * BWD_CHUNK + BWD_CHUNK <= p.N && (!CAUSAL || c * BWD_CHUNK + BWD_CHUNK - 1 <= wq_first);
+        float pv[2][16];
+        auto elements = [&](auto masked) {
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int kj = c * BWD_CHUNK + 32 * hh + 16 * s2 + r;
+              float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[s2][r], cc, -lrow));
+              if (decltype(masked)::value) pr = (kj < p.N && (!CAUSAL || kj <= q)) ? pr : 0.0f;
+              pv[s2][r] = pr;
+            }
+        };
+        if (all_live) elements(std::false_type{});
+        else elements(std::true_type{});
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            sP[c & 1][qw][s2][v][lane] = f32x4{pv[s2][4 * v], pv[s2][4 * v + 1], pv[s2][4 * v + 2], pv[s2][4 * v + 3]};
+      }
+      step_end();
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < DT; ++i) acc[i] = f32x16{};
+    f32x16 dp[2];
+    for (int c = 0; c <= nchunks; ++c) {
+      if (c + 1 < nchunks) copy_chunk(c + 1, (c + 1) % 3, (c + 1) & 1);
+      if (c > 0) {
+        // chunk c - 1: dS of (this lane's query, key 32 hh + 16 s2 + r), one MX
+        // block per lane half
+        const int cp = c - 1;
+        float dsv[2][16];
+        float am = 0.0f;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const f32x4 pp = sP[cp & 1][qw][s2][v][lane];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float ds = pp[j] * __builtin_fmaf(dp[s2][4 * v + j], sdv, -lrow);
+              dsv[s2][4 * v + j] = ds;
+              am = __builtin_fmaxf(am, __builtin_fabsf(ds));
+            }
+          }
+        const int e = mx_e4m3_exponent(am);
+        const float lim = __builtin_ldexpf(448.0f, e), sc = e8m0_scale(e);
+        const bool dump = DEBUG && b == p.dbg_b && h == p.dbg_h;
+        if (dump) p.dbg_dsq_e[(int64_t)q * (npad / 32) + 2 * cp + hh] = (uint8_t)(e + 127);
+        uint32_t dsq[2][8];                     // bf16 pairs
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const s16x2 q2 = mx_e4m3_pair<false>(s16x2{0, 0}, dsv[s2][r], dsv[s2][r + 1], lim, sc);
+            dsq[s2][r / 2] = mx_e4m3_pair_bf16(q2, sc);
+            if (dump) {
+              const uint32_t wq = __builtin_bit_cast(uint32_t, q2);
+              const int kj = cp * BWD_CHUNK + 32 * hh + 16 * s2 + r;
+              p.dbg_dsq[(int64_t)q * npad + kj] = (uint8_t)wq;
+              p.dbg_dsq[(int64_t)q * npad + kj + 1] = (uint8_t)(wq >> 8);
+            }
+          }
+        // dQ^T: k-step j takes keys 32 hh + 16 (j/2) + 8 (j%2) + [0, 8) in both
+        // operands; K^T from the row-major K^ tile by two transposing reads of 4 keys
+        const uint8_t* kt = sK[cp % 3];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int s2 = j >> 1, r0 = 8 * (j & 1);
+          const bf16x8 bv = __builtin_bit_cast(bf16x8, u32x4{dsq[s2][r0 / 2], dsq[s2][r0 / 2 + 1],
+                                                             dsq[s2][r0 / 2 + 2], dsq[s2][r0 / 2 + 3]});
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const int rowoff = (16 * s2 + r0) * 2 * D;
+            const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(__attribute__((address_space(3))) const void*)(kt + ofs[2 * KK + 2 * dt] + rowoff));
+            const s16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(__attribute__((address_space(3))) const void*)(kt + ofs[2 * KK + 2 * dt + 1] + rowoff));
+            const u32x2 w1 = __builtin_bit_cast(u32x2, r1), w2 = __builtin_bit_cast(u32x2, r2);
+            const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{w1[0], w1[1], w2[0], w2[1]});
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv, acc[dt], 0, 0, 0);
+          }
+        }
+      }
+      if (c < nchunks) {
+        // dP^T of chunk c, both sub-tiles: the two chains alternate, operands one ahead
+        const uint8_t* va = sV[c & 1];
+        auto ldv = [&](int i) {    // operand i: k-step i / 2 of sub-tile i % 2 (two 16-byte halves)
+          const int kk = i >> 1, s2 = i & 1;
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(va + ofs[2 * kk] + 16 * D * s2);
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(va + ofs[2 * kk + 1] + 16 * D * s2);
+          return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        };
+        i32x8 ov[2];
+        ov[0] = ldv(0);
+#pragma unroll
+        for (int i = 0; i < 2 * KK; ++i) {
+          if (i + 1 < 2 * KK) ov[(i + 1) & 1] = ldv(i + 1);
+          const int kk = i >> 1, s2 = i & 1;
+          // A: V codes (E4M3, format 0), B: dO^ codes (E5M2, format 1), unit scales
+          dp[s2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ov[i & 1], dop(kk), kk == 0 ? f32x16{} : dp[s2], 0,
+                                                                  1, 0, 127, 0, 127);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      step_end();
+    }
+    // C[d row][query]: lane holds the query, register r holds d = 32 dt + out_row(r, hh)
+    if (q < p.N) {
+      const float fq = p.sigma * *p.gk;
+      float* out = p.dq_out + (((int64_t)b * p.N + q) * p.Hq + h) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) out[32 * dt + 8 * (r >> 2) + 4 * hh + (r & 3)] = acc[dt][r] * fq;
+    }
   }
 }
 
@@ -960,7 +1045,7 @@ hipError_t launch_bwd_main(const BwdParams& p, int D, bool causal, bool debug, h
 #define BWD_LAUNCH(DD, C, G)                                                         \
   do {                                                                               \
     hipLaunchKernelGGL((bwd_dkdv_kernel<DD, C, G>), gkv, dim3(512), 0, st, p);       \
-    hipLaunchKernelGGL((bwd_dq_kernel<DD, C, G>), gq, dim3(256), 0, st, p);          \
+    hipLaunchKernelGGL((bwd_dq_kernel<DD, C, G>), gq, dim3(512), 0, st, p);          \
   } while (0)
   if (debug) {
     if (D == 64) {
