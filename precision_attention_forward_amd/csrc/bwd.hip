@@ -291,6 +291,16 @@ __device__ inline void bwd_dma4(const void* base, uint32_t off, uint32_t lds) {
 __device__ inline uint32_t bwd_lds_address(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
+// Makes the compiler wait, once, for registers loaded before a step loop.
+// The loops' chunk copies are asm, invisible to the compiler's wait counting:
+// left pending at the loop header, a pre-loop load would get a vmcnt wait in
+// every iteration, which also waits for the copies of the next chunk that the
+// iteration has just issued.
+template <int N>
+__device__ inline void bwd_settle(const u32x4 (&r)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(r[i]));
+}
 
 // ---------------------------------------------------------------------------
 // dK / dV.  Workgroup: 8 waves for 128 keys kb*128 + 32*kw + (lane & 31) of KV
@@ -463,6 +473,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
 
   const int wkey_last = kb * BWD_ROWS + kw * 32 + 31;
   // prologue: the tiles of chunk 0
+  bwd_settle(res);
   copy_s(0, c0, 0, 0);
   copy_d(0, c0, 0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -861,6 +872,8 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_kernel(BwdParams p) {
       }
   }
 
+  bwd_settle(res);
+  asm volatile("" ::"v"(lrow));
   copy_chunk(0, 0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
