@@ -301,6 +301,10 @@ __device__ inline void bwd_settle(const u32x4 (&r)[N]) {
 #pragma unroll
   for (int i = 0; i < N; ++i) asm volatile("" ::"v"(r[i]));
 }
+// 16 bytes, and (transposing read) 4 bf16, at an LDS byte address
+__device__ inline u32x4 bwd_lds16(uint32_t a) {
+  return *(__attribute__((address_space(3))) const u32x4*)(uintptr_t)a;
+}
 
 // ---------------------------------------------------------------------------
 // dK / dV.  Workgroup: 8 waves for 128 keys kb*128 + 32*kw + (lane & 31) of KV
@@ -322,6 +326,9 @@ __device__ inline void bwd_settle(const u32x4 (&r)[N]) {
 // therefore query 32*s2 + 16*((m>>2)&1) + 4*(m>>3) + (m&3).
 typedef short s16x4 __attribute__((__vector_size__(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ inline s16x4 bwd_lds_tr8(uint32_t a) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)a);
+}
 
 template <int D, bool CAUSAL, bool DEBUG>
 __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
@@ -744,17 +751,25 @@ __device__ __host__ inline int swz_vtile(int R) {
   return ((R >> 2) & 1) | (((R >> 5) & 1) << 1);
 }
 
-// dQ.  Workgroup: 8 waves for 128 queries qb*128 + 32*qw + (lane & 31) of
-// head h, two waves per 32-query block qw on one SIMD (waves qw and qw + 4):
-//   S side (waves 0-3):  S^T = K^ Q^T, P = 2^(t - L)
-//   dP side (waves 4-7): dP^T = V dO^T, dS = P (dP - D), dS~ and dQ^T += K^T dS~^T
-// as in the dK/dV kernel: P goes to the dP side through LDS as float32; the
-// dP side takes dS, dS~ and dQ of chunk s - 1 first and dP of chunk s last.
-// LDS: K^ in a ring of three (the S side's chunk, the dP side's and the
-// next), V and P in two buffers.  S^T sub-tile s2 of a 64-key chunk:
-// accumulator (lane half hh, register r) holds key 32*hh + 16*s2 + r of the
-// chunk; A row m of the S^T / dP^T products is therefore key
+// dQ.  Workgroup: 8 waves for 256 queries qb*256 + 32*w + (lane & 31) of head
+// h.  Every wave takes, for its 32 queries and each 64-key chunk,
+//   S^T = K^ Q^T, P = 2^(t - L), dP^T = V dO^T, dS = P (dP - D), dS~ and
+//   dQ^T += K^T dS~^T,
+// with P and dS in its own registers (a lane holds one query and 32 keys of
+// it per lane half, so the MX blocks of dS~ are lane-local).  The two waves
+// of a SIMD (w and w + 4) run half a step apart: waves 0-3 take the S^T / dP^T
+// products of chunk s first, then its vector work and dQ products; waves 4-7
+// take the vector work and dQ products of chunk s - 1 first, then the S^T /
+// dP^T products of chunk s.  So the vector phase of one wave runs beside the
+// matrix phase of the other, with one barrier per step.
+// LDS: K^ in a ring of three (chunks s - 1, s and the copy of s + 1), read
+// straight (A operand of S^T) and through transposing reads (the K^T operand
+// of dQ); V in two buffers.  S^T sub-tile s2 of a 64-key chunk: accumulator
+// (lane half hh, register r) holds key 32*hh + 16*s2 + r of the chunk; A row m
+// of the S^T / dP^T products is therefore key
 // 32*((m>>2)&1) + 16*s2 + 4*(m>>3) + (m&3).
+constexpr int BWD_QROWS = 256;     // queries per dQ workgroup
+
 template <int D, bool CAUSAL, bool DEBUG>
 __global__ void __launch_bounds__(512, 1) bwd_dq_kernel(BwdParams p) {
   constexpr int KS = D / 16, DT = D / 32, KK = D / 64;
@@ -764,7 +779,6 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_kernel(BwdParams p) {
   constexpr int NKW = (NKC + NW - 1) / NW, NVW = (NVC + NW - 1) / NW;
   __shared__ __attribute__((aligned(1024))) uint8_t sK[3][KB];
   __shared__ __attribute__((aligned(1024))) uint8_t sV[2][VB];
-  __shared__ __attribute__((aligned(16))) f32x4 sP[2][4][2][4][64];  // [buffer][query block][s2][r / 4][lane]
   int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   if (CAUSAL) {
     // Causal: a query block's work grows with qb.  Dispatch takes the longest
@@ -781,38 +795,47 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_kernel(BwdParams p) {
   }
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, ln = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool s_side = wave < 4;                 // uniform
-  const int qw = wave & 3;
-  const int q = qb * BWD_ROWS + qw * 32 + ln;
-  const int hk = h / (p.Hq / p.Hkv);
+  const bool lead = wave < 4;                   // uniform: matrix products of a chunk first
   const int64_t npad = p.npad;
-  const int64_t qrow = ((int64_t)b * p.Hq + h) * npad + q;
-  // resident operand (one array for both sides): Q^ as KS bf16x8 (S side, B
-  // operand of S^T) or dO^ as KK i32x8 (dP side, B operand of dP^T)
-  u32x4 res[KS];
-  if (s_side) {
+  const int wq_first = qb * BWD_QROWS + wave * 32;
+  const bool wave_live = wq_first < npad;       // the last block may reach past the padded rows
+  const int q = wq_first + ln;
+  const int hk = h / (p.Hq / p.Hkv);
+  const int64_t qrow = ((int64_t)b * p.Hq + h) * npad + (wave_live ? q : 0);
+  // resident operands: Q^ as KS bf16x8 (B operand of S^T), dO^ as KK i32x8
+  // (B operand of dP^T); L log2 e and D of the lane's query
+  u32x4 qres[KS], dres[2 * KK];
+  float lrow = 0.0f, drow = 0.0f;
+  if (wave_live) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) res[s] = *reinterpret_cast<const u32x4*>(p.qrm + qrow * D + 16 * s + 8 * hh);
-  } else {
+    for (int s = 0; s < KS; ++s) qres[s] = *reinterpret_cast<const u32x4*>(p.qrm + qrow * D + 16 * s + 8 * hh);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      res[2 * kk] = *reinterpret_cast<const u32x4*>(p.dorm + qrow * D + 64 * kk + 16 * hh);
-      res[2 * kk + 1] = *reinterpret_cast<const u32x4*>(p.dorm + qrow * D + 64 * kk + 32 + 16 * hh);
+      dres[2 * kk] = *reinterpret_cast<const u32x4*>(p.dorm + qrow * D + 64 * kk + 16 * hh);
+      dres[2 * kk + 1] = *reinterpret_cast<const u32x4*>(p.dorm + qrow * D + 64 * kk + 32 + 16 * hh);
     }
+    lrow = p.lv[qrow];
+    drow = p.dv[qrow];
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qres[s] = u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < 2 * KK; ++s) dres[s] = u32x4{0, 0, 0, 0};
   }
-  auto qop = [&](int st) { return __builtin_bit_cast(bf16x8, res[st]); };
+  auto qop = [&](int st) { return __builtin_bit_cast(bf16x8, qres[st]); };
   auto dop = [&](int kk) {
-    const u32x4 lo = res[2 * kk], hi = res[2 * kk + 1];
+    const u32x4 lo = dres[2 * kk], hi = dres[2 * kk + 1];
     return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
-  const float lrow = s_side ? p.lv[qrow] : p.dv[qrow];   // L log2 e (S side) or D (dP side) of the lane's query
   const float cc = (float)((double)p.sigma * 1.4426950408889634 * (double)(*p.gq) * (double)(*p.gk));
   const float sdv = *p.sdo * *p.sv;
   const int64_t khead = (int64_t)b * p.Hkv + hk;
   int nchunks = (int)(npad / BWD_CHUNK);
-  if (CAUSAL) nchunks = min(nchunks, (qb * BWD_ROWS + BWD_ROWS) / BWD_CHUNK);
+  if (CAUSAL) nchunks = min(nchunks, (qb * BWD_QROWS + BWD_QROWS) / BWD_CHUNK);
+  // chunks this wave contributes to (causal: keys up to its last query)
+  int wchunks = wave_live ? nchunks : 0;
+  if (CAUSAL && wave_live) wchunks = min(nchunks, (wq_first + 31) / BWD_CHUNK + 1);
   const int m = ln;
-  const int wq_first = qb * BWD_ROWS + qw * 32;
 
   // ---- chunk copies (all 8 waves): K^ and V rows, wave w takes copies w + 8 t
   uint32_t okc[NKW], ovc[NVW];
@@ -843,188 +866,170 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_kernel(BwdParams p) {
       if (j < NVC) bwd_dma16(vb0, ovc[t], bwd_lds_address(&sV[buf][0]) + 1024 * j);
     }
   };
-  // per-lane operand read offsets: S side K^ rows per k-step; dP side V rows
-  // per (k-step, half), then the transposing K^ reads per (dt, half)
+  // per-lane operand read offsets within a tile.  The 16-byte chunk index of
+  // a read is the swizzle XOR a sum of disjoint bit fields, so each offset is
+  // one per-lane base XOR a constant (the tiles are 1024-byte aligned, so the
+  // XOR may be applied to the LDS address):
+  //   K^ row R0, k-step ks:  kofs ^ 32 ks  (chunk 2 ks + hh)
+  //   V row R0, (kk, lh):    vofs ^ (64 kk + 32 lh)  (chunk 4 kk + 2 lh + hh)
+  //   transposing K^ read (dt, half): lane (g, c) of a 16-lane group reads 4
+  //   bf16 of key row 32 (g >> 1) + 4 half + (c >> 2) (+ 16 s2 + r0, which
+  //   leave the swizzle unchanged) at channel 32 dt + 16 (g & 1) + 4 (c & 3),
+  //   and the transpose hands it channel 32 dt + 16 (g & 1) + c of 4 keys:
+  //   (tofs + 8 D half) ^ (64 dt) ^ (half ? swizzle bit of row bit 2 : 0)
   const int R0 = 32 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);   // A row of the S^T / dP^T products
-  constexpr int NOFS = KS > 2 * KK + 2 * DT ? KS : 2 * KK + 2 * DT;
-  uint32_t ofs[NOFS];
-  if (s_side) {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) ofs[ks] = (uint32_t)(R0 * 2 * D + 16 * ((2 * ks + hh) ^ swz_ktile<D>(R0)));
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-      for (int lh = 0; lh < 2; ++lh)
-        ofs[2 * kk + lh] = (uint32_t)(R0 * D + 16 * ((4 * kk + hh + 2 * lh) ^ swz_vtile<D>(R0)));
-    // transposing reads of K^ for the dQ A operand: lane (g, c) of a 16-lane
-    // group reads 4 bf16 of key row 32 (g >> 1) + 4 half + (c >> 2) (+ 16 s2 +
-    // r0, which leave the swizzle unchanged) at channel 32 dt + 16 (g & 1) +
-    // 4 (c & 3); the transpose hands it channel 32 dt + 16 (g & 1) + c of 4 keys
+  const uint32_t kofs = (uint32_t)(R0 * 2 * D + 16 * (hh ^ swz_ktile<D>(R0)));
+  const uint32_t vofs = (uint32_t)(R0 * D + 16 * (hh ^ swz_vtile<D>(R0)));
+  uint32_t tofs;
+  {
     const int g4 = lane >> 4, c16 = lane & 15;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int R = 32 * (g4 >> 1) + 4 * half + (c16 >> 2);
-        const int byte = 2 * (32 * dt + 16 * (g4 & 1) + 4 * (c16 & 3));
-        ofs[2 * KK + 2 * dt + half] = (uint32_t)(R * 2 * D + 16 * ((byte / 16) ^ swz_ktile<D>(R)) + (byte % 16));
-      }
+    const int R = 32 * (g4 >> 1) + (c16 >> 2);
+    const int byte = 2 * (16 * (g4 & 1) + 4 * (c16 & 3));
+    tofs = (uint32_t)(R * 2 * D + 16 * ((byte / 16) ^ swz_ktile<D>(R)) + (byte % 16));
   }
+  constexpr uint32_t TR_HALF_X = D == 128 ? 64 : 32;   // 16 x (the swizzle bit that row bit 2 flips)
 
-  bwd_settle(res);
-  asm volatile("" ::"v"(lrow));
+  // S^T and dP^T of chunk c, both 16-key sub-tiles each: the chains of a
+  // product alternate, operands read ahead
+  f32x16 s[2], dp[2];
+  auto products = [&](int c) {
+    const uint32_t ka = bwd_lds_address(&sK[c % 3][0]) + kofs;
+    auto lda = [&](int i) {    // operand i: k-step i / 2 of sub-tile i % 2
+      return __builtin_bit_cast(bf16x8, bwd_lds16((ka ^ (32u * (uint32_t)(i >> 1))) + 16 * 2 * D * (i & 1)));
+    };
+    bf16x8 op[3];
+    op[0] = lda(0);
+    op[1] = lda(1);
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) {
+      if (i + 2 < 2 * KS) op[(i + 2) % 3] = lda(i + 2);
+      const int st = i >> 1, s2 = i & 1;
+      s[s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], qop(st), st == 0 ? f32x16{} : s[s2], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const uint32_t va = bwd_lds_address(&sV[c & 1][0]) + vofs;
+    auto ldv = [&](int i) {    // operand i: k-step i / 2 of sub-tile i % 2 (two 16-byte halves)
+      const int kk = i >> 1, s2 = i & 1;
+      const u32x4 lo = bwd_lds16((va ^ (64u * kk)) + 16 * D * s2);
+      const u32x4 hi = bwd_lds16((va ^ (64u * kk + 32u)) + 16 * D * s2);
+      return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    };
+    i32x8 ov[2];
+    ov[0] = ldv(0);
+#pragma unroll
+    for (int i = 0; i < 2 * KK; ++i) {
+      if (i + 1 < 2 * KK) ov[(i + 1) & 1] = ldv(i + 1);
+      const int kk = i >> 1, s2 = i & 1;
+      // A: V codes (E4M3, format 0), B: dO^ codes (E5M2, format 1), unit scales
+      dp[s2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ov[i & 1], dop(kk), kk == 0 ? f32x16{} : dp[s2], 0, 1,
+                                                              0, 127, 0, 127);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // P, dS, dS~ of chunk c and dQ^T += K^T dS~^T
+  f32x16 acc[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) acc[i] = f32x16{};
+  auto update = [&](int c) {
+    // dS of (this lane's query, key 32 hh + 16 s2 + r); keys past the sequence
+    // and (causal) after the query have P = 0, which only the last chunks need
+    const bool all_live = c * BWD_CHUNK + BWD_CHUNK <= p.N && (!CAUSAL || c * BWD_CHUNK + BWD_CHUNK - 1 <= wq_first);
+    // (dS overwrites dP in place); key 32 hh + 16 s2 + r of the chunk is live
+    // when 16 s2 + r < lim
+    float am = 0.0f;
+    auto elements = [&](auto masked) {
+      const int lim = (CAUSAL ? min(p.N, q + 1) : p.N) - (c * BWD_CHUNK + 32 * hh);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[s2][r], cc, -lrow));
+          if (decltype(masked)::value) pr = 16 * s2 + r < lim ? pr : 0.0f;
+          const float ds = pr * __builtin_fmaf(dp[s2][r], sdv, -drow);
+          dp[s2][r] = ds;
+          am = __builtin_fmaxf(am, __builtin_fabsf(ds));
+        }
+    };
+    if (all_live) elements(std::false_type{});
+    else elements(std::true_type{});
+    // dS~: one MX block per lane half
+    const int e = mx_e4m3_exponent(am);
+    const float lim = __builtin_ldexpf(448.0f, e), sc = e8m0_scale(e);
+    const bool dump = DEBUG && b == p.dbg_b && h == p.dbg_h;
+    if (dump) p.dbg_dsq_e[(int64_t)q * (npad / 32) + 2 * c + hh] = (uint8_t)(e + 127);
+    uint32_t dsq[2][8];                         // bf16 pairs
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const s16x2 q2 = mx_e4m3_pair<false>(s16x2{0, 0}, dp[s2][r], dp[s2][r + 1], lim, sc);
+        dsq[s2][r / 2] = mx_e4m3_pair_bf16(q2, sc);
+        if (dump) {
+          const uint32_t wq = __builtin_bit_cast(uint32_t, q2);
+          const int kj = c * BWD_CHUNK + 32 * hh + 16 * s2 + r;
+          p.dbg_dsq[(int64_t)q * npad + kj] = (uint8_t)wq;
+          p.dbg_dsq[(int64_t)q * npad + kj + 1] = (uint8_t)(wq >> 8);
+        }
+      }
+    // dQ^T: k-step j takes keys 32 hh + 16 (j/2) + 8 (j%2) + [0, 8) in both
+    // operands; K^T from the row-major K^ tile by two transposing reads of 4 keys
+    const uint32_t kt = bwd_lds_address(&sK[c % 3][0]) + tofs;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s2 = j >> 1, r0 = 8 * (j & 1);
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, u32x4{dsq[s2][r0 / 2], dsq[s2][r0 / 2 + 1],
+                                                         dsq[s2][r0 / 2 + 2], dsq[s2][r0 / 2 + 3]});
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint32_t rowoff = (16 * s2 + r0) * 2 * D;
+        const s16x4 r1 = bwd_lds_tr8((kt ^ (64u * dt)) + rowoff);
+        const s16x4 r2 = bwd_lds_tr8(((kt + 8 * D) ^ ((64u * dt) ^ TR_HALF_X)) + rowoff);
+        const u32x2 w1 = __builtin_bit_cast(u32x2, r1), w2 = __builtin_bit_cast(u32x2, r2);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{w1[0], w1[1], w2[0], w2[1]});
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv, acc[dt], 0, 0, 0);
+      }
+    }
+  };
+
+  bwd_settle(qres);
+  bwd_settle(dres);
+  asm volatile("" ::"v"(lrow), "v"(drow));
   copy_chunk(0, 0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   auto step_end = [&]() {
     // this wave's copies for the next step have landed and its LDS writes are
-    // done; after the barrier every wave's are, and the tiles of step - 1 may
+    // done; after the barrier every wave's are, and the tiles of step - 2 may
     // be overwritten
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
-  f32x16 acc[DT];                               // dQ^T (dP side)
-  if (s_side) {
+  // Each group runs its own copy of the step loop (separate loops keep the
+  // accumulators in place); both take nchunks + 1 barriers.
+  if (lead) {
     for (int c = 0; c <= nchunks; ++c) {
       if (c + 1 < nchunks) copy_chunk(c + 1, (c + 1) % 3, (c + 1) & 1);
-      if (c < nchunks) {
-        // S^T of both 16-key sub-tiles: the two chains alternate, operands two ahead
-        f32x16 s[2];
-        const uint8_t* ka = sK[c % 3];
-        auto lda = [&](int i) {    // operand i: k-step i / 2 of sub-tile i % 2
-          return *reinterpret_cast<const bf16x8*>(ka + ofs[i >> 1] + 16 * 2 * D * (i & 1));
-        };
-        bf16x8 op[3];
-        op[0] = lda(0);
-        op[1] = lda(1);
-#pragma unroll
-        for (int i = 0; i < 2 * KS; ++i) {
-          if (i + 2 < 2 * KS) op[(i + 2) % 3] = lda(i + 2);
-          const int st = i >> 1, s2 = i & 1;
-          s[s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], qop(st), st == 0 ? f32x16{} : s[s2], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // P of (this lane's query, key 32 hh + 16 s2 + r) to LDS; keys past the
-        // sequence and (causal) after the query are masked, which only the
-        // last chunks need
-        const bool all_live = c * BWD_CHUNK + BWD_CHUNK <= p.N && (!CAUSAL || c * BWD_CHUNK + BWD_CHUNK - 1 <= wq_first);
-        float pv[2][16];
-        auto elements = [&](auto masked) {
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int kj = c * BWD_CHUNK + 32 * hh + 16 * s2 + r;
-              float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[s2][r], cc, -lrow));
-              if (decltype(masked)::value) pr = (kj < p.N && (!CAUSAL || kj <= q)) ? pr : 0.0f;
-              pv[s2][r] = pr;
-            }
-        };
-        if (all_live) elements(std::false_type{});
-        else elements(std::true_type{});
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            sP[c & 1][qw][s2][v][lane] = f32x4{pv[s2][4 * v], pv[s2][4 * v + 1], pv[s2][4 * v + 2], pv[s2][4 * v + 3]};
+      if (c < wchunks) {
+        products(c);
+        update(c);
       }
       step_end();
     }
   } else {
-#pragma unroll
-    for (int i = 0; i < DT; ++i) acc[i] = f32x16{};
-    f32x16 dp[2];
     for (int c = 0; c <= nchunks; ++c) {
       if (c + 1 < nchunks) copy_chunk(c + 1, (c + 1) % 3, (c + 1) & 1);
-      if (c > 0) {
-        // chunk c - 1: dS of (this lane's query, key 32 hh + 16 s2 + r), one MX
-        // block per lane half
-        const int cp = c - 1;
-        float dsv[2][16];
-        float am = 0.0f;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const f32x4 pp = sP[cp & 1][qw][s2][v][lane];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float ds = pp[j] * __builtin_fmaf(dp[s2][4 * v + j], sdv, -lrow);
-              dsv[s2][4 * v + j] = ds;
-              am = __builtin_fmaxf(am, __builtin_fabsf(ds));
-            }
-          }
-        const int e = mx_e4m3_exponent(am);
-        const float lim = __builtin_ldexpf(448.0f, e), sc = e8m0_scale(e);
-        const bool dump = DEBUG && b == p.dbg_b && h == p.dbg_h;
-        if (dump) p.dbg_dsq_e[(int64_t)q * (npad / 32) + 2 * cp + hh] = (uint8_t)(e + 127);
-        uint32_t dsq[2][8];                     // bf16 pairs
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            const s16x2 q2 = mx_e4m3_pair<false>(s16x2{0, 0}, dsv[s2][r], dsv[s2][r + 1], lim, sc);
-            dsq[s2][r / 2] = mx_e4m3_pair_bf16(q2, sc);
-            if (dump) {
-              const uint32_t wq = __builtin_bit_cast(uint32_t, q2);
-              const int kj = cp * BWD_CHUNK + 32 * hh + 16 * s2 + r;
-              p.dbg_dsq[(int64_t)q * npad + kj] = (uint8_t)wq;
-              p.dbg_dsq[(int64_t)q * npad + kj + 1] = (uint8_t)(wq >> 8);
-            }
-          }
-        // dQ^T: k-step j takes keys 32 hh + 16 (j/2) + 8 (j%2) + [0, 8) in both
-        // operands; K^T from the row-major K^ tile by two transposing reads of 4 keys
-        const uint8_t* kt = sK[cp % 3];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int s2 = j >> 1, r0 = 8 * (j & 1);
-          const bf16x8 bv = __builtin_bit_cast(bf16x8, u32x4{dsq[s2][r0 / 2], dsq[s2][r0 / 2 + 1],
-                                                             dsq[s2][r0 / 2 + 2], dsq[s2][r0 / 2 + 3]});
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const int rowoff = (16 * s2 + r0) * 2 * D;
-            const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(__attribute__((address_space(3))) const void*)(kt + ofs[2 * KK + 2 * dt] + rowoff));
-            const s16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(__attribute__((address_space(3))) const void*)(kt + ofs[2 * KK + 2 * dt + 1] + rowoff));
-            const u32x2 w1 = __builtin_bit_cast(u32x2, r1), w2 = __builtin_bit_cast(u32x2, r2);
-            const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{w1[0], w1[1], w2[0], w2[1]});
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv, acc[dt], 0, 0, 0);
-          }
-        }
-      }
-      if (c < nchunks) {
-        // dP^T of chunk c, both sub-tiles: the two chains alternate, operands one ahead
-        const uint8_t* va = sV[c & 1];
-        auto ldv = [&](int i) {    // operand i: k-step i / 2 of sub-tile i % 2 (two 16-byte halves)
-          const int kk = i >> 1, s2 = i & 1;
-          const u32x4 lo = *reinterpret_cast<const u32x4*>(va + ofs[2 * kk] + 16 * D * s2);
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(va + ofs[2 * kk + 1] + 16 * D * s2);
-          return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        };
-        i32x8 ov[2];
-        ov[0] = ldv(0);
-#pragma unroll
-        for (int i = 0; i < 2 * KK; ++i) {
-          if (i + 1 < 2 * KK) ov[(i + 1) & 1] = ldv(i + 1);
-          const int kk = i >> 1, s2 = i & 1;
-          // A: V codes (E4M3, format 0), B: dO^ codes (E5M2, format 1), unit scales
-          dp[s2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ov[i & 1], dop(kk), kk == 0 ? f32x16{} : dp[s2], 0,
-                                                                  1, 0, 127, 0, 127);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+      if (c > 0 && c - 1 < wchunks) update(c - 1);
+      if (c < wchunks) products(c);
       step_end();
     }
-    // C[d row][query]: lane holds the query, register r holds d = 32 dt + out_row(r, hh)
-    if (q < p.N) {
-      const float fq = p.sigma * *p.gk;
-      float* out = p.dq_out + (((int64_t)b * p.N + q) * p.Hq + h) * D;
+  }
+  // C[d row][query]: lane holds the query, register r holds d = 32 dt + out_row(r, hh)
+  if (wave_live && q < p.N) {
+    const float fq = p.sigma * *p.gk;
+    float* out = p.dq_out + (((int64_t)b * p.N + q) * p.Hq + h) * D;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) out[32 * dt + 8 * (r >> 2) + 4 * hh + (r & 3)] = acc[dt][r] * fq;
-    }
+      for (int r = 0; r < 16; ++r) out[32 * dt + 8 * (r >> 2) + 4 * hh + (r & 3)] = acc[dt][r] * fq;
   }
 }
 
@@ -1054,7 +1059,7 @@ hipError_t launch_bwd_prep(const uint8_t* q_codes, const uint8_t* q_scales, cons
 
 hipError_t launch_bwd_main(const BwdParams& p, int D, bool causal, bool debug, hipStream_t st) {
   const dim3 gkv((unsigned)(p.npad / BWD_ROWS), (unsigned)p.Hkv, (unsigned)p.B);
-  const dim3 gq((unsigned)(p.npad / BWD_ROWS), (unsigned)p.Hq, (unsigned)p.B);
+  const dim3 gq((unsigned)((p.npad + BWD_QROWS - 1) / BWD_QROWS), (unsigned)p.Hq, (unsigned)p.B);
 #define BWD_LAUNCH(DD, C, G)                                                         \
   do {                                                                               \
     hipLaunchKernelGGL((bwd_dkdv_kernel<DD, C, G>), gkv, dim3(512), 0, st, p);       \
