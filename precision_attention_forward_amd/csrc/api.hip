@@ -36,7 +36,7 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
 hipError_t launch_bwd_prep(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
                            const uint8_t* k_scales, const uint8_t* v_codes, int64_t v_cols, const void* dout,
                            const void* o, const float* lse, const float* partials, int np, int B, int Hq, int Hkv,
-                           int N, int D, int64_t npad, __bf16* qrm, __bf16* qt, __bf16* krm, __bf16* kt,
+                           int N, int D, int64_t npad, __bf16* qrm, __bf16* krm,
                            uint8_t* vrm, uint8_t* drm, uint8_t* dtr, float* dvec, float* lvec, float* sdo,
                            hipStream_t st);
 struct BwdParams;
@@ -383,7 +383,7 @@ attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, 
 
 // ---- backward -------------------------------------------------------------
 struct BwdLayout {
-  int64_t npad, qrm, qt, krm, kt, vrm, drm, dtr, dvec, lvec, sdo, partials, total;
+  int64_t npad, qrm, krm, vrm, drm, dtr, dvec, lvec, sdo, partials, total;
 };
 
 static bool bwd_shapes_ok(const attn_bwd_args* a) {
@@ -399,9 +399,7 @@ static BwdLayout bwd_layout(const attn_bwd_args* a) {
   const int64_t nq = (int64_t)a->B * a->Hq * L.npad * a->D, nk = (int64_t)a->B * a->Hkv * L.npad * a->D;
   int64_t off = 0;
   L.qrm = off; off += al(2 * nq);
-  L.qt = off; off += al(2 * nq);
   L.krm = off; off += al(2 * nk);
-  L.kt = off; off += al(2 * nk);
   L.vrm = off; off += al(nk);
   L.drm = off; off += al(nq);
   L.dtr = off; off += al(nq);
@@ -450,15 +448,13 @@ attn_status attn_bwd_fp8(const attn_bwd_args* a, void* stream) {
   float* sdo = (float*)(w + L.sdo);
   e = launch_bwd_prep(a->q.codes, a->q.scales, a->k.codes, a->k.scales, a->v.codes, (int64_t)a->B * L.npad, a->dout,
                       a->o, a->lse, partials, np, a->B, a->Hq, a->Hkv, a->N, a->D, L.npad, (__bf16*)(w + L.qrm),
-                      (__bf16*)(w + L.qt), (__bf16*)(w + L.krm), (__bf16*)(w + L.kt), w + L.vrm, w + L.drm,
+                      (__bf16*)(w + L.krm), w + L.vrm, w + L.drm,
                       w + L.dtr, (float*)(w + L.dvec), (float*)(w + L.lvec), sdo, st);
   if (e != hipSuccess) return hip_status(e);
   BwdParams p;
   memset(&p, 0, sizeof(p));
   p.qrm = (const __bf16*)(w + L.qrm);
-  p.qt = (const __bf16*)(w + L.qt);
   p.krm = (const __bf16*)(w + L.krm);
-  p.kt = (const __bf16*)(w + L.kt);
   p.vrm = w + L.vrm;
   p.dorm = w + L.drm;
   p.dot = w + L.dtr;

@@ -15,22 +15,27 @@
 //
 // gfx950 mapping:
 //  * Preparation kernels write the exact NVFP4 values of Q and K as bf16 (at
-//    most 6 significant bits: exact) row-major and transposed, dO^ as E5M2
-//    codes row-major and transposed, V as key-major E4M3 codes, and the per
-//    row D and LSE log2 e.
-//  * dK/dV: one workgroup of 4 waves per 128 keys of a KV head, one key per
-//    lane (32 keys per wave); it walks the query heads of its group and the
-//    query chunks of 64.  S = Q^ K^T runs on v_mfma_f32_32x32x16_bf16 and
-//    dP = dO^ V^T on the scaled FP8 MFMA (E5M2 x E4M3), with the query rows
-//    of Q^ / dO^ read in the order that makes each S sub-tile one 32-query MX
-//    block split 16/16 between a lane and lane^32 -- the k-blocks of the
-//    FP8 32x32x64 operand.  P~^T is then directly the A operand of the dV
-//    MFMA with its E8M0 exponents as scale_a; dS~ (rounded to E4M3 and
-//    rescaled, exact in bf16) feeds dK on the bf16 MFMA against Q^^T.
-//  * dQ: one workgroup of 4 waves per 128 queries of a head, one query per
-//    lane as in the forward; K^ / V rows are read so that a lane half holds
-//    32 consecutive keys, which makes the MX blocks of dS~ lane-local; dQ^T
-//    accumulates on the bf16 MFMA against K^^T.
+//    most 6 significant bits: exact) row-major, dO^ as E5M2 codes row-major
+//    and transposed, V as key-major E4M3 codes, and the per row D and
+//    LSE log2 e.
+//  * dK/dV: one workgroup of 8 waves per 128 keys of a KV head, one key per
+//    lane (32 keys per pair of waves on one SIMD); it walks the query heads
+//    of its group and the query chunks of 64.  One wave of a pair computes
+//    S = Q^ K^T (v_mfma_f32_32x32x16_bf16), P, P~ and dV, its partner dP =
+//    dO^ V^T (scaled FP8 MFMA, E5M2 x E4M3), dS, dS~ and dK one chunk
+//    behind, with P passed through LDS.  The query rows of Q^ / dO^ are read
+//    in the order that makes each S sub-tile one 32-query MX block split
+//    16/16 between a lane and lane^32 -- the k-blocks of the FP8 32x32x64
+//    operand -- so P~^T is directly the A operand of the dV MFMA with its
+//    E8M0 exponents as scale_a; dS~ (rounded to E4M3 and rescaled, exact in
+//    bf16) feeds dK on the bf16 MFMA against Q^^T, read from the row-major
+//    Q^ tile by transposing LDS reads.
+//  * dQ: one workgroup of 8 waves per 256 queries of a head, one query per
+//    lane as in the forward; every wave computes S^T, P, dP^T, dS, dS~ and
+//    dQ^T for its 32 queries.  K^ / V rows are read so that a lane half
+//    holds 32 consecutive keys, which makes the MX blocks of dS~ lane-local;
+//    dQ^T accumulates on the bf16 MFMA against K^^T (transposing reads of the
+//    row-major K^ tile).
 #include <type_traits>
 
 #include "common.h"
@@ -101,14 +106,12 @@ __device__ inline uint32_t mx_e4m3_pair_bf16(s16x2 w, float scale) {
 
 // ---------------------------------------------------------------------------
 // Preparation 1: exact bf16 values of NVFP4 rows (without the tensor scale),
-// row-major and transposed.  One workgroup per (64 rows, head, batch).
+// row-major.  One workgroup per (64 rows, head, batch).
 template <int D>
 __global__ void __launch_bounds__(256) bwd_expand_kernel(const uint8_t* __restrict__ codes,
                                                          const uint8_t* __restrict__ scales, int H, int N,
-                                                         int64_t npad, __bf16* __restrict__ rm,
-                                                         __bf16* __restrict__ tr) {
+                                                         int64_t npad, __bf16* __restrict__ rm) {
   constexpr int G8 = D / 8;
-  __shared__ __bf16 tile[64][D + 8];
   const int r0 = blockIdx.x * 64, h = blockIdx.y, b = blockIdx.z;
   const int64_t head = (int64_t)b * H + h;
   for (int it = threadIdx.x; it < 64 * G8; it += 256) {
@@ -125,16 +128,6 @@ __global__ void __launch_bounds__(256) bwd_expand_kernel(const uint8_t* __restri
       for (int j = 0; j < 8; ++j) val[j] = (__bf16)0.0f;
     }
     *reinterpret_cast<bf16x8*>(rm + (head * npad + n) * D + 8 * g) = val;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) tile[row][8 * g + j] = val[j];
-  }
-  __syncthreads();
-  for (int it = threadIdx.x; it < D * 8; it += 256) {
-    const int d = it / 8, rg = it % 8;
-    bf16x8 val;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) val[j] = tile[8 * rg + j][d];
-    *reinterpret_cast<bf16x8*>(tr + (head * D + d) * npad + r0 + 8 * rg) = val;
   }
 }
 
@@ -1037,19 +1030,19 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_kernel(BwdParams p) {
 hipError_t launch_bwd_prep(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
                            const uint8_t* k_scales, const uint8_t* v_codes, int64_t v_cols, const void* dout,
                            const void* o, const float* lse, const float* partials, int np, int B, int Hq, int Hkv,
-                           int N, int D, int64_t npad, __bf16* qrm, __bf16* qt, __bf16* krm, __bf16* kt,
+                           int N, int D, int64_t npad, __bf16* qrm, __bf16* krm,
                            uint8_t* vrm, uint8_t* drm, uint8_t* dtr, float* dvec, float* lvec, float* sdo,
                            hipStream_t st) {
   const dim3 gq((unsigned)(npad / 64), (unsigned)Hq, (unsigned)B), gk((unsigned)(npad / 64), (unsigned)Hkv, (unsigned)B);
   if (D == 64) {
-    hipLaunchKernelGGL(bwd_expand_kernel<64>, gq, dim3(256), 0, st, q_codes, q_scales, Hq, N, npad, qrm, qt);
-    hipLaunchKernelGGL(bwd_expand_kernel<64>, gk, dim3(256), 0, st, k_codes, k_scales, Hkv, N, npad, krm, kt);
+    hipLaunchKernelGGL(bwd_expand_kernel<64>, gq, dim3(256), 0, st, q_codes, q_scales, Hq, N, npad, qrm);
+    hipLaunchKernelGGL(bwd_expand_kernel<64>, gk, dim3(256), 0, st, k_codes, k_scales, Hkv, N, npad, krm);
     hipLaunchKernelGGL(bwd_v_kernel<64>, gk, dim3(256), 0, st, v_codes, Hkv, v_cols, npad, vrm);
     hipLaunchKernelGGL(bwd_do_kernel<64>, gq, dim3(256), 0, st, (const uint16_t*)dout, (const uint16_t*)o, lse,
                        partials, np, Hq, N, npad, drm, dtr, dvec, lvec, sdo);
   } else {
-    hipLaunchKernelGGL(bwd_expand_kernel<128>, gq, dim3(256), 0, st, q_codes, q_scales, Hq, N, npad, qrm, qt);
-    hipLaunchKernelGGL(bwd_expand_kernel<128>, gk, dim3(256), 0, st, k_codes, k_scales, Hkv, N, npad, krm, kt);
+    hipLaunchKernelGGL(bwd_expand_kernel<128>, gq, dim3(256), 0, st, q_codes, q_scales, Hq, N, npad, qrm);
+    hipLaunchKernelGGL(bwd_expand_kernel<128>, gk, dim3(256), 0, st, k_codes, k_scales, Hkv, N, npad, krm);
     hipLaunchKernelGGL(bwd_v_kernel<128>, gk, dim3(256), 0, st, v_codes, Hkv, v_cols, npad, vrm);
     hipLaunchKernelGGL(bwd_do_kernel<128>, gq, dim3(256), 0, st, (const uint16_t*)dout, (const uint16_t*)o, lse,
                        partials, np, Hq, N, npad, drm, dtr, dvec, lvec, sdo);

@@ -9,9 +9,7 @@ namespace attn {
 
 struct BwdParams {
   const __bf16* qrm;      // [B][Hq][NPAD][D]   exact NVFP4 Q values without tensor scale (bf16)
-  const __bf16* qt;       // [B][Hq][D][NPAD]   the same, transposed
   const __bf16* krm;      // [B][Hkv][NPAD][D]
-  const __bf16* kt;       // [B][Hkv][D][NPAD]
   const uint8_t* vrm;     // [B][Hkv][NPAD][D]  FP8 E4M3 V codes, key-major
   const uint8_t* dorm;    // [B][Hq][NPAD][D]   E5M2 dO codes
   const uint8_t* dot;     // [B][Hq][D][NPAD]
