@@ -302,14 +302,16 @@ __device__ inline u32x4 bwd_lds16(uint32_t a) {
 // ---------------------------------------------------------------------------
 // dK / dV.  Workgroup: 8 waves for 128 keys kb*128 + 32*kw + (lane & 31) of KV
 // head hk, two waves per 32-key block kw, on one SIMD (waves kw and kw + 4):
-//   S side (waves 0-3):  S = Q^ K^T, P = 2^(t - L), P~ and dV += P~^T dO^
-//   dP side (waves 4-7): dP = dO^ V^T, dS = P (dP - D), dS~ and dK += dS~^T Q^
+//   dP side (waves 0-3): dP = dO^ V^T, dS = P (dP - D), dS~ and dK += dS~^T Q^
+//   S side (waves 4-7):  S = Q^ K^T, P = 2^(t - L), P~ and dV += P~^T dO^
 // The dP side runs one 64-query chunk behind: in step s the S side takes
 // chunk s and the dP side chunk s - 1, whose P the S side left in LDS as
 // float32 (the dP side's lane l needs exactly the 32 values lane l of its
 // partner computed).  One barrier per step, so one wave's matrix products
 // overlap its partner's vector work; each wave holds one accumulator and one
-// resident operand (K^ or V), so the two fit on one SIMD.
+// resident operand (K^ or V), so the two fit on one SIMD.  The dP side, the
+// longer of the two, takes the older waves, which win the SIMD's issue
+// arbitration.
 //   LDS: the Q^ chunk row-major in a ring of three (chunk x in slot x % 3:
 //   the S side's chunk, the dP side's chunk and the next), read straight for
 //   S and through transposing reads (ds_read_b64_tr_b16) as the Q^T operand of
@@ -350,7 +352,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
   }
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, ln = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool s_side = wave < 4;                 // uniform
+  const bool s_side = wave >= 4;                // uniform
   const int kw = wave & 3;
   const int key = kb * BWD_ROWS + kw * 32 + ln;
   const int G = p.Hq / p.Hkv;
@@ -750,11 +752,13 @@ __device__ __host__ inline int swz_vtile(int R) {
 //   dQ^T += K^T dS~^T,
 // with P and dS in its own registers (a lane holds one query and 32 keys of
 // it per lane half, so the MX blocks of dS~ are lane-local).  The two waves
-// of a SIMD (w and w + 4) run half a step apart: waves 0-3 take the S^T / dP^T
-// products of chunk s first, then its vector work and dQ products; waves 4-7
+// of a SIMD (w and w + 4) run half a step apart: waves 4-7 take the S^T / dP^T
+// products of chunk s first, then its vector work and dQ products; waves 0-3
 // take the vector work and dQ products of chunk s - 1 first, then the S^T /
 // dP^T products of chunk s.  So the vector phase of one wave runs beside the
-// matrix phase of the other, with one barrier per step.
+// matrix phase of the other, with one barrier per step; the waves that start
+// with vector work are the older ones, which win the SIMD's issue
+// arbitration (about 7 % faster than the other assignment).
 // LDS: K^ in a ring of three (chunks s - 1, s and the copy of s + 1), read
 // straight (A operand of S^T) and through transposing reads (the K^T operand
 // of dQ); V in two buffers.  S^T sub-tile s2 of a 64-key chunk: accumulator
@@ -788,7 +792,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_kernel(BwdParams p) {
   }
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, ln = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool lead = wave < 4;                   // uniform: matrix products of a chunk first
+  const bool lead = wave >= 4;                  // uniform: matrix products of a chunk first
   const int64_t npad = p.npad;
   const int wq_first = qb * BWD_QROWS + wave * 32;
   const bool wave_live = wq_first < npad;       // the last block may reach past the padded rows
