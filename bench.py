@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--cpu-seqs-dec", type=int, default=8, help="sequences of the decode oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (HBM counter calibration) and exit")
+    ap.add_argument("--issue-rates", action="store_true",
+                    help="print the per-instruction costs measured by the library's issue-rate micro-kernels")
     ap.add_argument("--gemm-reference", action="store_true",
                     help="only time torch's bf16 and fp16 matrix products (n = 8192, 16384) on this GPU, the "
                          "vendor-library reference for the BF16 attention's matrix rate, and exit")
@@ -137,6 +139,36 @@ def gemm_reference():
             print(json.dumps({"gemm": str(dt).replace("torch.", ""), "n": n, "ms": round(ms, 3),
                               "tflops": round(2 * n ** 3 / ms / 1e9, 1)}), flush=True)
             del a, b, c
+
+
+PROBE_NAMES = ("v_fma_f32", "v_exp_f32", "v_med3_f32", "v_cvt_scalef32_pk_fp8_f32 (two values)", "v_max3_f32",
+               "v_mfma_f32_32x32x16_bf16", "v_mfma_scale_f32_32x32x64_f8f6f4 FP8", "v_mfma_scale_f32_32x32x64_f8f6f4 FP4",
+               "bf16 MFMA wave + v_fma_f32 wave", "bf16 MFMA wave + v_exp_f32 wave",
+               "2 v_fma_f32 per MFMA, two waves", "4 v_fma_f32 per MFMA, two waves", "8 v_fma_f32 per MFMA, two waves",
+               "ds_read_b128", "ds_read_b64", "ds_read_b64_tr_b16", "ds_write_b128", "ds_write_b32")
+
+
+def issue_rates():
+    """The library's issue-rate micro-kernels (attn_probe_issue_rates): one
+    JSON line per kind with cycles per instruction per SIMD, or bytes per
+    clock per CU for the LDS kinds; for the MFMA + vector kinds, the time
+    relative to the MFMA issue alone (32 cycles per bf16 32x32x16)."""
+    import torch  # noqa: F401
+    import precision_attention_forward_amd as paf
+    n = paf.load_library().attn_probe_kinds()
+    assert n == len(PROBE_NAMES), (n, len(PROBE_NAMES))
+    for kind in range(n):
+        paf.probe_issue_rates(kind)                      # warm-up (clocks, code load)
+        cyc, units, grid = paf.probe_issue_rates(kind)
+        line = {"probe": kind, "what": PROBE_NAMES[kind], "cycles_per_workgroup": round(cyc)}
+        if kind >= 13:
+            line["bytes_per_clock_per_cu"] = round(units / cyc, 1)
+        elif 8 <= kind <= 12:
+            line["mfma_per_simd"] = units
+            line["time_over_mfma_alone"] = round(cyc / (32.0 * units), 3)
+        else:
+            line["cycles_per_instruction_per_simd"] = round(cyc / units, 2)
+        print(json.dumps(line), flush=True)
 
 
 def cpu_baseline(inp, rows, encoder="exact", four_six=False, qk="nvfp4"):
@@ -513,6 +545,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.issue_rates:
+        issue_rates()
         return
     if args.gemm_reference:
         gemm_reference()

@@ -520,6 +520,34 @@ typedef struct attn_bwd_args {
 size_t attn_bwd_ws_bytes(const attn_bwd_args* a);
 attn_status attn_bwd_fp8(const attn_bwd_args* a, void* stream);
 
+/* ---- diagnostics ---------------------------------------------------------
+ * For the measurement script that derives the per-instruction costs behind
+ * the kernels' roofline notes; not part of the attention path.
+ *
+ * attn_probe_kinds: the number of issue-rate micro-kernels.
+ * attn_probe_issue_rates launches micro-kernel `kind` (0 .. attn_probe_kinds()
+ * - 1) on `stream` as 256 workgroups of 96 KB LDS (one per CU).  Each
+ * workgroup writes its cycle count (s_memtime, from a barrier before its
+ * waves start to a barrier after all finish) to cycles[workgroup].
+ * `cycles` is a device buffer of 512 int64, 8-byte aligned, owned by the
+ * caller: entries 256 .. 511 belong to a store that keeps the kernels'
+ * results live and that no launch takes in practice.  *units receives the work of one launch: instructions per SIMD
+ * (vector and matrix kinds) or bytes per CU (LDS kinds); *grid receives 256.
+ * Kinds: 0 v_fma_f32, 1 v_exp_f32, 2 v_med3_f32, 3 v_cvt_scalef32_pk_fp8_f32,
+ * 4 v_max3_f32 (two waves per SIMD, eight independent chains each);
+ * 5 v_mfma_f32_32x32x16_bf16, 6 the scaled 32x32x64 MFMA on FP8, 7 on FP4
+ * (one wave per SIMD, four accumulators); 8 and 9: one MFMA wave (bf16) and
+ * one v_fma_f32 (8) or v_exp_f32 (9) wave per SIMD, units = MFMA per SIMD;
+ * 10, 11, 12: two waves per SIMD, each issuing 2, 4 or 8 v_fma_f32 per MFMA,
+ * units = MFMA per SIMD; 13 ds_read_b128, 14 ds_read_b64, 15
+ * ds_read_b64_tr_b16, 16 ds_write_b128, 17 ds_write_b32 (eight waves,
+ * lane-contiguous, conflict-free; units = bytes per CU).
+ * Errors: ATTN_ERR_INVALID_ARGUMENT (kind out of range, null or misaligned
+ * pointer), ATTN_ERR_HIP.
+ */
+int attn_probe_kinds(void);
+attn_status attn_probe_issue_rates(int kind, long long* cycles, long long* units, int* grid, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -123,6 +123,9 @@ EXPORTS = {
                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
                                      ctypes.c_void_p]),
+    "attn_probe_kinds": (ctypes.c_int, []),
+    "attn_probe_issue_rates": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(ctypes.c_longlong),
+                                              ctypes.POINTER(ctypes.c_int), ctypes.c_void_p]),
 }
 
 
@@ -525,3 +528,17 @@ def fwd_bf16(q, k, v, softmax_scale, causal=False, want_lse=True):
     _check(lib.attn_fwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, D, softmax_scale,
                              1 if causal else 0, _stream()))
     return o, lse
+
+
+def probe_issue_rates(kind):
+    """Diagnostics: one launch of issue-rate micro-kernel ``kind`` on the
+    current stream (see attn_probe_issue_rates in include/attn_fp4.h).
+    Returns (mean cycles per workgroup, units of work per launch, grid)."""
+    lib = load_library()
+    cycles = torch.zeros(512, dtype=torch.int64, device="cuda")
+    units = ctypes.c_longlong(0)
+    grid = ctypes.c_int(0)
+    _check(lib.attn_probe_issue_rates(int(kind), cycles.data_ptr(), ctypes.byref(units), ctypes.byref(grid),
+                                      _stream()))
+    torch.cuda.synchronize()
+    return float(cycles[:grid.value].double().mean()), int(units.value), int(grid.value)

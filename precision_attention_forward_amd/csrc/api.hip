@@ -43,6 +43,8 @@ struct BwdParams;
 hipError_t launch_bwd_main(const BwdParams& p, int D, bool causal, bool debug, hipStream_t st);
 struct DecParams;
 hipError_t launch_decode(const DecParams& p, int D, int pf, int vf, bool causal, bool debug, hipStream_t st);
+hipError_t launch_probe_kind(int kind, long long* cycles, int64_t* units, int* grid, hipStream_t st);
+int probe_kind_count();
 }  // namespace attn
 
 #include "fwd_params.h"
@@ -577,5 +579,20 @@ static attn_status run_decode(const attn_decode_args* a, void* stream, int pf) {
 
 attn_status attn_decode_directp(const attn_decode_args* a, void* stream) { return run_decode(a, stream, 0); }
 attn_status attn_decode_fp8pv(const attn_decode_args* a, void* stream) { return run_decode(a, stream, 1); }
+
+// ---- diagnostics ------------------------------------------------------------
+int attn_probe_kinds(void) { return probe_kind_count(); }
+
+attn_status attn_probe_issue_rates(int kind, long long* cycles, long long* units, int* grid, void* stream) {
+  if (kind < 0 || kind >= probe_kind_count() || cycles == nullptr || units == nullptr || grid == nullptr ||
+      !aligned(cycles, 8))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  int64_t u = 0;
+  int g = 0;
+  const hipError_t e = launch_probe_kind(kind, cycles, &u, &g, (hipStream_t)stream);
+  *units = (long long)u;
+  *grid = g;
+  return hip_status(e);
+}
 
 }  // extern "C"

@@ -1,0 +1,199 @@
+// Issue-rate micro-kernels of gfx950: the per-instruction costs that the
+// kernels' roofline notes rest on (vector ALU, transcendental, the MX
+// conversions, the matrix instructions, LDS reads and writes, and how much
+// vector issue fits beside the matrix pipe).  Not part of the attention
+// path: a diagnostics entry point for the measurement script.
+//
+// Each launch is 256 workgroups with 96 KB of LDS each (one per CU).  Every
+// wave of a workgroup starts after a barrier and the span ends after a second
+// barrier, so the cycle count (s_memtime) covers every wave's work.
+#include "common.h"
+
+namespace attn {
+namespace {
+
+constexpr int PROBE_GRID = 256;
+constexpr int PROBE_ITERS = 4096;
+constexpr int PROBE_LDS = 96 * 1024;
+
+typedef short p16x4 __attribute__((__vector_size__(8)));
+typedef __attribute__((address_space(3))) p16x4 lds_p16x4;
+
+enum ProbeKind {
+  P_FMA = 0, P_EXP, P_MED3, P_CVT_FP8, P_MAX3,          // 8 waves per CU, 8 independent chains each
+  P_MFMA_BF16, P_MFMA_FP8, P_MFMA_FP4,                  // 4 waves per CU (one per SIMD), 4 chains
+  P_MFMA_AND_FMA, P_MFMA_AND_EXP,                       // waves 0-3 MFMA, waves 4-7 vector
+  P_MIX2, P_MIX4, P_MIX8,                               // 8 waves: k FMA per MFMA in each wave
+  P_LDS_R128, P_LDS_R64, P_LDS_TR64, P_LDS_W128, P_LDS_W32,
+  P_COUNT
+};
+
+template <int KIND>
+__global__ void __launch_bounds__(512) probe_kernel(long long* cycles) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[PROBE_LDS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = 0.001f * (float)(tid + i);
+  const float a = 1.0001f, b = 0.5f, one = 1.0f;
+  f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+  bf16x8 opb;
+  i32x8 op8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    opb[i] = (__bf16)(0.01f * (float)(tid + i));
+    op8[i] = 0x3a3a3a3a + tid + i;
+  }
+  for (int i = tid; i < PROBE_LDS / 16; i += blockDim.x)
+    reinterpret_cast<u32x4*>(lds)[i] = u32x4{(uint32_t)i, 1u, 2u, 3u};
+  u32x4 lacc = {0, 0, 0, 0};
+  __syncthreads();
+  const long long t0 = __builtin_readcyclecounter();
+  if (KIND <= P_MAX3) {
+    for (int it = 0; it < PROBE_ITERS; ++it) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (KIND == P_FMA) asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(x[i]) : "v"(a), "v"(b));
+        if (KIND == P_EXP) asm volatile("v_exp_f32 %0, %0" : "+v"(x[i]));
+        if (KIND == P_MED3) asm volatile("v_med3_f32 %0, %0, %1, %2" : "+v"(x[i]) : "v"(a), "v"(b));
+        if (KIND == P_MAX3) asm volatile("v_max3_f32 %0, %0, |%1|, |%2|" : "+v"(x[i]) : "v"(a), "v"(b));
+        if (KIND == P_CVT_FP8)
+          asm volatile("v_cvt_scalef32_pk_fp8_f32 %0, %1, %1, %2" : "+v"(x[i]) : "v"(x[(i + 1) & 7]), "v"(one));
+      }
+    }
+  } else if (KIND <= P_MFMA_FP4) {
+    for (int it = 0; it < PROBE_ITERS; ++it) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (KIND == P_MFMA_BF16) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opb, opb, acc[c], 0, 0, 0);
+        if (KIND == P_MFMA_FP8)
+          acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op8, op8, acc[c], 0, 0, 0, 127, 0, 127);
+        if (KIND == P_MFMA_FP4)
+          acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op8, op8, acc[c], 4, 4, 0, 127, 0, 127);
+      }
+    }
+  } else if (KIND <= P_MFMA_AND_EXP) {
+    if (wave < 4) {
+      for (int it = 0; it < PROBE_ITERS; ++it) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opb, opb, acc[c & 1], 0, 0, 0);
+      }
+    } else {
+      for (int it = 0; it < PROBE_ITERS; ++it) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (KIND == P_MFMA_AND_FMA) asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(x[i]) : "v"(a), "v"(b));
+          else asm volatile("v_exp_f32 %0, %0" : "+v"(x[i]));
+        }
+      }
+    }
+  } else if (KIND <= P_MIX8) {
+    constexpr int K = KIND == P_MIX2 ? 2 : KIND == P_MIX4 ? 4 : 8;
+    for (int it = 0; it < PROBE_ITERS; ++it) {
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opb, opb, acc[0], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < K; ++i) asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(x[i & 7]) : "v"(a), "v"(b));
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opb, opb, acc[1], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < K; ++i) asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(x[(i + 4) & 7]) : "v"(a), "v"(b));
+    }
+  } else {
+    // LDS: each wave streams 8 accesses per iteration over a 64 KB window,
+    // lane-contiguous (no bank conflicts); 16, 8 or 4 bytes per lane
+    constexpr int BPL = (KIND == P_LDS_R128 || KIND == P_LDS_W128) ? 16 : (KIND == P_LDS_W32 ? 4 : 8);
+    const uint32_t lb = (uint32_t)lane * BPL;
+    for (int it = 0; it < PROBE_ITERS; ++it) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t ad = (lb + (uint32_t)((it * 8 + j + wave * 8) * 64 * BPL)) & 65535u;
+        uint8_t* pa = lds + ad;
+        if (KIND == P_LDS_R128) lacc ^= *reinterpret_cast<const u32x4*>(pa);
+        if (KIND == P_LDS_R64) {
+          const u32x2 v = *reinterpret_cast<const u32x2*>(pa);
+          lacc[0] ^= v[0];
+          lacc[1] ^= v[1];
+        }
+        if (KIND == P_LDS_TR64) {
+          const p16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_p16x4*)(__attribute__((address_space(3))) void*)pa);
+          lacc[0] ^= (uint32_t)(uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16);
+          lacc[1] ^= (uint32_t)(uint16_t)r[2] | ((uint32_t)(uint16_t)r[3] << 16);
+        }
+        if (KIND == P_LDS_W128) *reinterpret_cast<u32x4*>(pa) = u32x4{(uint32_t)it, (uint32_t)j, 0u, 0u};
+        if (KIND == P_LDS_W32) *reinterpret_cast<uint32_t*>(pa) = (uint32_t)(it + j);
+      }
+    }
+  }
+  __syncthreads();
+  const long long t1 = __builtin_readcyclecounter();
+  // keep every result live: a store that no input can trigger
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += x[i];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += acc[c][i];
+  lacc[0] ^= reinterpret_cast<const uint32_t*>(lds)[tid];
+  // a hash of every result against a value the compiler cannot know (it
+  // depends on the clock): the store, in bounds, almost never happens
+  const uint32_t hsh = __float_as_uint(s) ^ lacc[0] ^ lacc[1] ^ lacc[2] ^ lacc[3];
+  if (hsh == 0x5a5a0000u + (uint32_t)(t1 & 0xffff)) cycles[PROBE_GRID + blockIdx.x] = hsh;
+  if (tid == 0) cycles[blockIdx.x] = t1 - t0;
+}
+
+// threads per workgroup and the work one launch puts on a SIMD (instructions)
+// or, for the LDS kinds, on a CU (bytes)
+void probe_shape(int kind, int* threads, int64_t* units) {
+  const int64_t it = PROBE_ITERS;
+  switch (kind) {
+    case P_FMA: case P_EXP: case P_MED3: case P_MAX3: *threads = 512; *units = 2 * it * 8; break;
+    case P_CVT_FP8: *threads = 512; *units = 2 * it * 8; break;
+    case P_MFMA_BF16: case P_MFMA_FP8: case P_MFMA_FP4: *threads = 256; *units = it * 4; break;
+    case P_MFMA_AND_FMA: case P_MFMA_AND_EXP: *threads = 512; *units = it * 4; break;   // MFMA per SIMD
+    case P_MIX2: case P_MIX4: case P_MIX8: *threads = 512; *units = 2 * it * 2; break;   // MFMA per SIMD
+    case P_LDS_R128: case P_LDS_W128: *threads = 512; *units = 8 * it * 8 * 64 * 16; break;
+    case P_LDS_R64: case P_LDS_TR64: *threads = 512; *units = 8 * it * 8 * 64 * 8; break;
+    default: *threads = 512; *units = 8 * it * 8 * 64 * 4; break;
+  }
+}
+
+template <int KIND>
+hipError_t launch_probe(int threads, long long* cycles, hipStream_t st) {
+  hipLaunchKernelGGL(probe_kernel<KIND>, dim3(PROBE_GRID), dim3(threads), 0, st, cycles);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_probe_kind(int kind, long long* cycles, int64_t* units, int* grid, hipStream_t st) {
+  int threads;
+  probe_shape(kind, &threads, units);
+  *grid = PROBE_GRID;
+  switch (kind) {
+    case P_FMA: return launch_probe<P_FMA>(threads, cycles, st);
+    case P_EXP: return launch_probe<P_EXP>(threads, cycles, st);
+    case P_MED3: return launch_probe<P_MED3>(threads, cycles, st);
+    case P_CVT_FP8: return launch_probe<P_CVT_FP8>(threads, cycles, st);
+    case P_MAX3: return launch_probe<P_MAX3>(threads, cycles, st);
+    case P_MFMA_BF16: return launch_probe<P_MFMA_BF16>(threads, cycles, st);
+    case P_MFMA_FP8: return launch_probe<P_MFMA_FP8>(threads, cycles, st);
+    case P_MFMA_FP4: return launch_probe<P_MFMA_FP4>(threads, cycles, st);
+    case P_MFMA_AND_FMA: return launch_probe<P_MFMA_AND_FMA>(threads, cycles, st);
+    case P_MFMA_AND_EXP: return launch_probe<P_MFMA_AND_EXP>(threads, cycles, st);
+    case P_MIX2: return launch_probe<P_MIX2>(threads, cycles, st);
+    case P_MIX4: return launch_probe<P_MIX4>(threads, cycles, st);
+    case P_MIX8: return launch_probe<P_MIX8>(threads, cycles, st);
+    case P_LDS_R128: return launch_probe<P_LDS_R128>(threads, cycles, st);
+    case P_LDS_R64: return launch_probe<P_LDS_R64>(threads, cycles, st);
+    case P_LDS_TR64: return launch_probe<P_LDS_TR64>(threads, cycles, st);
+    case P_LDS_W128: return launch_probe<P_LDS_W128>(threads, cycles, st);
+    case P_LDS_W32: return launch_probe<P_LDS_W32>(threads, cycles, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int probe_kind_count() { return P_COUNT; }
+
+}  // namespace attn
