@@ -441,37 +441,33 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
     }
     if (wave == 1) bwd_dma4(p.dv + q0, (uint32_t)(4 * lane), bwd_lds_address(&sD[slot][0]));
   };
-  // per-lane operand read offsets (bytes within a buffer), one array for both
-  // sides: S side Q rows per k-step, then the dO^T halves; dP side dO rows
-  // per (k-step, half), then the transposing Q reads per (dt, half)
+  // per-lane operand read offsets within a tile, as one per-lane base per
+  // operand XOR a constant (the chunk index of a read is the swizzle XOR a
+  // sum of disjoint bit fields; the tiles are 1024-byte aligned, so the XOR
+  // may be applied to the LDS address).  Two bases per side, sharing two
+  // registers:
+  //   S side  b0: Q row R0, k-step ks: b0 ^ 32 ks (chunk 2 ks + hh)
+  //           b1: dO^T row ln (+ 32 dt), half lh: b1 ^ 32 lh (chunk 2 lh + hh)
+  //   dP side b0: dO row R0, (kk, lh): b0 ^ (64 kk + 32 lh) (chunk 4 kk + 2 lh + hh)
+  //           b1: transposing Q read (dt, half): lane (g, c) of a 16-lane
+  //           group reads 4 bf16 of row 16 (g >> 1) + 4 half + (c >> 2) (+ 32
+  //           s2 + r0, which leave the swizzle unchanged) at channel 32 dt + 16
+  //           (g & 1) + 4 (c & 3), and the transpose hands it channel 32 dt + 16
+  //           (g & 1) + c of 4 rows: (b1 + 8 D half) ^ (64 dt) ^ (half ?
+  //           swizzle bit of row bit 2 : 0)
   const int R0 = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);   // A row of the S / dP products
-  constexpr int NOFS = KS + 2 > 2 * KK + 2 * DT ? KS + 2 : 2 * KK + 2 * DT;
-  uint32_t ofs[NOFS];
+  uint32_t b0, b1;
   if (s_side) {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) ofs[ks] = (uint32_t)(R0 * 2 * D + 16 * ((2 * ks + hh) ^ swz_qtile<D>(R0)));
-#pragma unroll
-    for (int lh = 0; lh < 2; ++lh) ofs[KS + lh] = (uint32_t)(ln * 64 + 16 * ((hh + 2 * lh) ^ swz_drows64(ln)));
+    b0 = (uint32_t)(R0 * 2 * D + 16 * (hh ^ swz_qtile<D>(R0)));
+    b1 = (uint32_t)(ln * 64 + 16 * (hh ^ swz_drows64(ln)));
   } else {
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-      for (int lh = 0; lh < 2; ++lh)
-        ofs[2 * kk + lh] = (uint32_t)(R0 * D + 16 * ((4 * kk + hh + 2 * lh) ^ swz_qrows<D>(R0)));
-    // transposing reads of Q^ for the dK B operand: lane (g, c) of a 16-lane
-    // group reads 4 bf16 of row 16 (g >> 1) + 4 half + (c >> 2) (+ 32 s2 + r0,
-    // which leave the swizzle unchanged) at channel 32 dt + 16 (g & 1) + 4 (c & 3);
-    // the transpose hands it channel 32 dt + 16 (g & 1) + c of 4 rows
+    b0 = (uint32_t)(R0 * D + 16 * (hh ^ swz_qrows<D>(R0)));
     const int g4 = lane >> 4, c16 = lane & 15;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int R = 16 * (g4 >> 1) + 4 * half + (c16 >> 2);
-        const int byte = 2 * (32 * dt + 16 * (g4 & 1) + 4 * (c16 & 3));
-        ofs[2 * KK + 2 * dt + half] = (uint32_t)(R * 2 * D + 16 * ((byte / 16) ^ swz_qtile<D>(R)) + (byte % 16));
-      }
+    const int R = 16 * (g4 >> 1) + (c16 >> 2);
+    const int byte = 2 * (16 * (g4 & 1) + 4 * (c16 & 3));
+    b1 = (uint32_t)(R * 2 * D + 16 * ((byte / 16) ^ swz_qtile<D>(R)) + (byte % 16));
   }
+  constexpr uint32_t TR_HALF_X = D == 128 ? 64 : 32;   // 16 x (the swizzle bit that row bit 2 flips)
 
   const int wkey_last = kb * BWD_ROWS + kw * 32 + 31;
   // prologue: the tiles of chunk 0
@@ -522,9 +518,9 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
           // S of both 32-query sub-tiles: the two accumulation chains
           // alternate, each A operand read from LDS two matrix instructions
           // ahead (fenced); each chain sums its k-steps in order
-          const uint8_t* qa = sQ[slot];
+          const uint32_t qa = bwd_lds_address(&sQ[slot][0]) + b0;
           auto lda = [&](int i) {    // operand i: k-step i / 2 of sub-tile i % 2
-            return *reinterpret_cast<const bf16x8*>(qa + ofs[i >> 1] + 32 * 2 * D * (i & 1));
+            return __builtin_bit_cast(bf16x8, bwd_lds16((qa ^ (32u * (uint32_t)(i >> 1))) + 32 * 2 * D * (i & 1)));
           };
           bf16x8 op[3];
           op[0] = lda(0);
@@ -601,10 +597,11 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) p.dbg_pt_e[(int64_t)(2 * c + s2) * npad + key] = (uint8_t)(ep[s2] + 127);
         }
+        const uint32_t ta = bwd_lds_address(&sDOT[buf][0]) + b1;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const u32x4 lo = *reinterpret_cast<const u32x4*>(&sDOT[buf][ofs[KS] + 32 * 64 * dt]);
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(&sDOT[buf][ofs[KS + 1] + 32 * 64 * dt]);
+          const u32x4 lo = bwd_lds16(ta + 32 * 64 * dt);
+          const u32x4 hi = bwd_lds16((ta ^ 32u) + 32 * 64 * dt);
           const i32x8 bb = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
           // A: P~ (E4M3, format 0) with its block exponents, B: dO^ codes (E5M2, format 1)
           acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pa, bb, acc[dt], 0, 1, 0, scale_p, 0, 127);
@@ -675,7 +672,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
         // dK: k-step j takes queries 32 (j/2) + 16 hh + 8 (j%2) + [0, 8) in both
         // operands; the Q^T operand comes from the row-major Q^ tile by two
         // transposing reads of 4 queries each
-        const uint8_t* qt = sQ[slot];
+        const uint32_t xa = bwd_lds_address(&sQ[slot][0]) + b1;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int s2 = j >> 1, r0 = 8 * (j & 1);
@@ -683,11 +680,9 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
                                                             dsq[s2][r0 / 2 + 2], dsq[s2][r0 / 2 + 3]});
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const int rowoff = (32 * s2 + r0) * 2 * D;
-            const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(__attribute__((address_space(3))) const void*)(qt + ofs[2 * KK + 2 * dt] + rowoff));
-            const s16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(__attribute__((address_space(3))) const void*)(qt + ofs[2 * KK + 2 * dt + 1] + rowoff));
+            const uint32_t rowoff = (32 * s2 + r0) * 2 * D;
+            const s16x4 r1 = bwd_lds_tr8((xa ^ (64u * dt)) + rowoff);
+            const s16x4 r2 = bwd_lds_tr8(((xa + 8 * D) ^ ((64u * dt) ^ TR_HALF_X)) + rowoff);
             const u32x2 w1 = __builtin_bit_cast(u32x2, r1), w2 = __builtin_bit_cast(u32x2, r2);
             const bf16x8 bq = __builtin_bit_cast(bf16x8, u32x4{w1[0], w1[1], w2[0], w2[1]});
             acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, acc[dt], 0, 0, 0);
@@ -696,11 +691,11 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
       }
       if (step < total) {
         // dP of chunk (g, c), both sub-tiles: the two chains alternate, operands one ahead
-        const uint8_t* da = sDO[step & 1];
+        const uint32_t da = bwd_lds_address(&sDO[step & 1][0]) + b0;
         auto ldd = [&](int i) {    // operand i: k-step i / 2 of sub-tile i % 2 (two 16-byte halves)
           const int kk = i >> 1, s2 = i & 1;
-          const u32x4 lo = *reinterpret_cast<const u32x4*>(da + ofs[2 * kk] + 32 * D * s2);
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(da + ofs[2 * kk + 1] + 32 * D * s2);
+          const u32x4 lo = bwd_lds16((da ^ (64u * kk)) + 32 * D * s2);
+          const u32x4 hi = bwd_lds16((da ^ (64u * kk + 32u)) + 32 * D * s2);
           return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         };
         i32x8 op[2];
