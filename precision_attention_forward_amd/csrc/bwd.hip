@@ -540,14 +540,15 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
               amx[s2] = 0.0f;
+              // query 32 s2 + 16 hh + r is live for this key when r >= thr
+              const int thr = key >= p.N ? 16 : (CAUSAL ? key - (c * BWD_CHUNK + 32 * s2 + 16 * hh) : 0);
               f32x4 lr[4];           // the 16 rows' L as four 16-byte reads, issued together
 #pragma unroll
               for (int v = 0; v < 4; ++v) lr[v] = *reinterpret_cast<const f32x4*>(&sL[buf][32 * s2 + 16 * hh + 4 * v]);
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
-                const int qi = c * BWD_CHUNK + 32 * s2 + 16 * hh + r;
                 float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[s2][r], cc, -lr[r >> 2][r & 3]));
-                if (decltype(masked)::value) pr = (key < p.N && (!CAUSAL || key <= qi)) ? pr : 0.0f;
+                if (decltype(masked)::value) pr = r >= thr ? pr : 0.0f;
                 pv[s2][r] = pr;
                 amx[s2] = __builtin_fmaxf(amx[s2], pr);
               }
