@@ -94,6 +94,13 @@ __device__ inline s16x2 mx_e4m3_pair(s16x2 w, float x0, float x1, float lim, flo
   return __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, __builtin_amdgcn_fmed3f(x0, -lim, lim),
                                                   __builtin_amdgcn_fmed3f(x1, -lim, lim), scale, HI);
 }
+// The same into the low half of a new word whose high half is left as
+// whatever the register held (the clamped x0: a dead value, so no copy).
+__device__ inline s16x2 mx_e4m3_pair_lo(float x0, float x1, float lim, float scale) {
+  const float c0 = __builtin_amdgcn_fmed3f(x0, -lim, lim);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(s16x2, c0), c0,
+                                                  __builtin_amdgcn_fmed3f(x1, -lim, lim), scale, false);
+}
 
 // The two block values E4M3(code) 2^e of the low pair of w, as two bf16 in
 // one word (exact: four significant bits).
@@ -580,8 +587,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
           const int s2 = w >> 2, r = 4 * (w & 3);
-          s16x2 t = {0, 0};
-          t = mx_e4m3_pair<false>(t, pv[s2][r], pv[s2][r + 1], limp[s2], scp[s2]);
+          s16x2 t = mx_e4m3_pair_lo(pv[s2][r], pv[s2][r + 1], limp[s2], scp[s2]);
           t = mx_e4m3_pair<true>(t, pv[s2][r + 2], pv[s2][r + 3], limp[s2], scp[s2]);
           pa[w] = __builtin_bit_cast(int, t);
         }
@@ -661,7 +667,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
           for (int r = 0; r < 16; r += 2) {
-            const s16x2 q2 = mx_e4m3_pair<false>(s16x2{0, 0}, pv[s2][r], pv[s2][r + 1], lims[s2], scs[s2]);
+            const s16x2 q2 = mx_e4m3_pair_lo(pv[s2][r], pv[s2][r + 1], lims[s2], scs[s2]);
             dsq[s2][r / 2] = mx_e4m3_pair_bf16(q2, scs[s2]);
             if (dump) {
               const uint32_t wq = __builtin_bit_cast(uint32_t, q2);
@@ -955,7 +961,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_kernel(BwdParams p) {
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const s16x2 q2 = mx_e4m3_pair<false>(s16x2{0, 0}, dp[s2][r], dp[s2][r + 1], lim, sc);
+        const s16x2 q2 = mx_e4m3_pair_lo(dp[s2][r], dp[s2][r + 1], lim, sc);
         dsq[s2][r / 2] = mx_e4m3_pair_bf16(q2, sc);
         if (dump) {
           const uint32_t wq = __builtin_bit_cast(uint32_t, q2);
