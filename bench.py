@@ -145,14 +145,20 @@ PROBE_NAMES = ("v_fma_f32", "v_exp_f32", "v_med3_f32", "v_cvt_scalef32_pk_fp8_f3
                "v_mfma_f32_32x32x16_bf16", "v_mfma_scale_f32_32x32x64_f8f6f4 FP8", "v_mfma_scale_f32_32x32x64_f8f6f4 FP4",
                "bf16 MFMA wave + v_fma_f32 wave", "bf16 MFMA wave + v_exp_f32 wave",
                "2 v_fma_f32 per MFMA, two waves", "4 v_fma_f32 per MFMA, two waves", "8 v_fma_f32 per MFMA, two waves",
-               "ds_read_b128", "ds_read_b64", "ds_read_b64_tr_b16", "ds_write_b128", "ds_write_b32")
+               "ds_read_b128", "ds_read_b64", "ds_read_b64_tr_b16", "ds_write_b128", "ds_write_b32",
+               "v_cvt_scalef32_pk_fp4_f32 (two values)",
+               "v_exp_f32 + 1 v_fma_f32", "v_exp_f32 + 3 v_fma_f32", "v_exp_f32 + 1 v_max3_f32",
+               "v_exp_f32 + 1 v_cvt_scalef32_pk_fp4_f32", "4 v_exp_f32 + 4 v_fma_f32 (per 4 steps)",
+               "v_fma_f32, four waves per SIMD", "8 v_fma_f32 per MFMA, four waves", "16 v_fma_f32 per MFMA, two waves")
 
 
 def issue_rates():
     """The library's issue-rate micro-kernels (attn_probe_issue_rates): one
     JSON line per kind with cycles per instruction per SIMD, or bytes per
     clock per CU for the LDS kinds; for the MFMA + vector kinds, the time
-    relative to the MFMA issue alone (32 cycles per bf16 32x32x16)."""
+    relative to the MFMA issue alone (32 cycles per bf16 32x32x16); for the
+    exponential + other kinds, cycles per step (one exponential and its
+    partners) per SIMD."""
     import torch  # noqa: F401
     import precision_attention_forward_amd as paf
     n = paf.load_library().attn_probe_kinds()
@@ -161,9 +167,11 @@ def issue_rates():
         paf.probe_issue_rates(kind)                      # warm-up (clocks, code load)
         cyc, units, grid = paf.probe_issue_rates(kind)
         line = {"probe": kind, "what": PROBE_NAMES[kind], "cycles_per_workgroup": round(cyc)}
-        if kind >= 13:
+        if 13 <= kind <= 17:
             line["bytes_per_clock_per_cu"] = round(units / cyc, 1)
-        elif 8 <= kind <= 12:
+        elif 19 <= kind <= 23:
+            line["cycles_per_exp_step_per_simd"] = round(cyc / units, 2)
+        elif 8 <= kind <= 12 or kind >= 25:
             line["mfma_per_simd"] = units
             line["time_over_mfma_alone"] = round(cyc / (32.0 * units), 3)
         else:

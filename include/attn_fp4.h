@@ -541,7 +541,14 @@ attn_status attn_bwd_fp8(const attn_bwd_args* a, void* stream);
  * 10, 11, 12: two waves per SIMD, each issuing 2, 4 or 8 v_fma_f32 per MFMA,
  * units = MFMA per SIMD; 13 ds_read_b128, 14 ds_read_b64, 15
  * ds_read_b64_tr_b16, 16 ds_write_b128, 17 ds_write_b32 (eight waves,
- * lane-contiguous, conflict-free; units = bytes per CU).
+ * lane-contiguous, conflict-free; units = bytes per CU); 18
+ * v_cvt_scalef32_pk_fp4_f32 (as 0-4); 19-22: two waves per SIMD, each step
+ * one v_exp_f32 followed by independent work: 19 one v_fma_f32, 20 three
+ * v_fma_f32, 21 one v_max3_f32, 22 one v_cvt_scalef32_pk_fp4_f32, 23 as
+ * 19 in runs of four exponentials and four FMAs (units = steps per SIMD);
+ * 24 v_fma_f32 at four waves per SIMD (1024 threads); 25 as 12 at four
+ * waves per SIMD; 26 as 12 with 16 v_fma_f32 per MFMA (units = MFMA per
+ * SIMD for 25 and 26).
  * Errors: ATTN_ERR_INVALID_ARGUMENT (kind out of range, null or misaligned
  * pointer), ATTN_ERR_HIP.
  */

@@ -4,7 +4,8 @@
 // vector issue fits beside the matrix pipe).  Not part of the attention
 // path: a diagnostics entry point for the measurement script.
 //
-// Each launch is 256 workgroups with 96 KB of LDS each (one per CU).  Every
+// Each launch is 256 workgroups with 96 KB of LDS each (one per CU), of 512
+// threads (two waves per SIMD) unless a kind says otherwise.  Every
 // wave of a workgroup starts after a barrier and the span ends after a second
 // barrier, so the cycle count (s_memtime) covers every wave's work.
 #include "common.h"
@@ -25,17 +26,25 @@ enum ProbeKind {
   P_MFMA_AND_FMA, P_MFMA_AND_EXP,                       // waves 0-3 MFMA, waves 4-7 vector
   P_MIX2, P_MIX4, P_MIX8,                               // 8 waves: k FMA per MFMA in each wave
   P_LDS_R128, P_LDS_R64, P_LDS_TR64, P_LDS_W128, P_LDS_W32,
+  P_CVT_FP4,                                            // 8 waves per CU, 8 chains, like the vector kinds
+  P_EXP_FMA, P_EXP_FMA3, P_EXP_MAX3, P_EXP_CVT_FP4,     // 8 waves: v_exp_f32 chains interleaved with others
+  P_EXP_FMA_G4,                                         // as P_EXP_FMA, in runs of four of each
+  P_FMA_4W, P_MIX8_4W,                                  // 16 waves per CU (four per SIMD)
+  P_MIX16,                                              // 8 waves: 16 FMA per MFMA in each wave
   P_COUNT
 };
 
 template <int KIND>
-__global__ void __launch_bounds__(512) probe_kernel(long long* cycles) {
+__global__ void __launch_bounds__(1024) probe_kernel(long long* cycles) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[PROBE_LDS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  float x[8];
+  float x[8], y[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = 0.001f * (float)(tid + i);
+  for (int i = 0; i < 8; ++i) {
+    x[i] = 0.001f * (float)(tid + i);
+    y[i] = 0.002f * (float)(tid + i);
+  }
   const float a = 1.0001f, b = 0.5f, one = 1.0f;
   f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
   bf16x8 opb;
@@ -50,7 +59,45 @@ __global__ void __launch_bounds__(512) probe_kernel(long long* cycles) {
   u32x4 lacc = {0, 0, 0, 0};
   __syncthreads();
   const long long t0 = __builtin_readcyclecounter();
-  if (KIND <= P_MAX3) {
+  if (KIND == P_CVT_FP4) {
+    for (int it = 0; it < PROBE_ITERS; ++it) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        asm volatile("v_cvt_scalef32_pk_fp4_f32 %0, %1, %1, %2" : "+v"(x[i]) : "v"(x[(i + 1) & 7]), "v"(one));
+    }
+  } else if (KIND == P_EXP_FMA_G4) {
+    for (int it = 0; it < PROBE_ITERS; ++it) {
+#pragma unroll
+      for (int g = 0; g < 8; g += 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) asm volatile("v_exp_f32 %0, %0" : "+v"(x[g + i]));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(y[g + i]) : "v"(a), "v"(b));
+      }
+    }
+  } else if (KIND == P_FMA_4W) {
+    for (int it = 0; it < PROBE_ITERS; ++it) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(x[i]) : "v"(a), "v"(b));
+    }
+  } else if (KIND > P_CVT_FP4 && KIND <= P_EXP_CVT_FP4) {
+    // one v_exp_f32 per step on x[i], followed by independent work on y
+    for (int it = 0; it < PROBE_ITERS; ++it) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        asm volatile("v_exp_f32 %0, %0" : "+v"(x[i]));
+        if (KIND == P_EXP_FMA) asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(y[i]) : "v"(a), "v"(b));
+        if (KIND == P_EXP_FMA3) {
+          asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(y[i]) : "v"(a), "v"(b));
+          asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(y[(i + 3) & 7]) : "v"(a), "v"(b));
+          asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(y[(i + 6) & 7]) : "v"(a), "v"(b));
+        }
+        if (KIND == P_EXP_MAX3) asm volatile("v_max3_f32 %0, %0, |%1|, |%2|" : "+v"(y[i]) : "v"(a), "v"(b));
+        if (KIND == P_EXP_CVT_FP4)
+          asm volatile("v_cvt_scalef32_pk_fp4_f32 %0, %1, %1, %2" : "+v"(y[i]) : "v"(y[(i + 1) & 7]), "v"(one));
+      }
+    }
+  } else if (KIND <= P_MAX3) {
     for (int it = 0; it < PROBE_ITERS; ++it) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -88,8 +135,8 @@ __global__ void __launch_bounds__(512) probe_kernel(long long* cycles) {
         }
       }
     }
-  } else if (KIND <= P_MIX8) {
-    constexpr int K = KIND == P_MIX2 ? 2 : KIND == P_MIX4 ? 4 : 8;
+  } else if (KIND <= P_MIX8 || KIND == P_MIX8_4W || KIND == P_MIX16) {
+    constexpr int K = KIND == P_MIX2 ? 2 : KIND == P_MIX4 ? 4 : KIND == P_MIX16 ? 16 : 8;
     for (int it = 0; it < PROBE_ITERS; ++it) {
       acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opb, opb, acc[0], 0, 0, 0);
 #pragma unroll
@@ -130,7 +177,7 @@ __global__ void __launch_bounds__(512) probe_kernel(long long* cycles) {
   // keep every result live: a store that no input can trigger
   float s = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) s += x[i];
+  for (int i = 0; i < 8; ++i) s += x[i] + y[i];
 #pragma unroll
   for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -155,6 +202,12 @@ void probe_shape(int kind, int* threads, int64_t* units) {
     case P_MIX2: case P_MIX4: case P_MIX8: *threads = 512; *units = 2 * it * 2; break;   // MFMA per SIMD
     case P_LDS_R128: case P_LDS_W128: *threads = 512; *units = 8 * it * 8 * 64 * 16; break;
     case P_LDS_R64: case P_LDS_TR64: *threads = 512; *units = 8 * it * 8 * 64 * 8; break;
+    case P_CVT_FP4: *threads = 512; *units = 2 * it * 8; break;
+    case P_EXP_FMA: case P_EXP_FMA3: case P_EXP_MAX3: case P_EXP_CVT_FP4: case P_EXP_FMA_G4:
+      *threads = 512; *units = 2 * it * 8; break;                    // exponentials per SIMD
+    case P_FMA_4W: *threads = 1024; *units = 4 * it * 8; break;
+    case P_MIX8_4W: *threads = 1024; *units = 4 * it * 2; break;     // MFMA per SIMD
+    case P_MIX16: *threads = 512; *units = 2 * it * 2; break;        // MFMA per SIMD
     default: *threads = 512; *units = 8 * it * 8 * 64 * 4; break;
   }
 }
@@ -190,6 +243,15 @@ hipError_t launch_probe_kind(int kind, long long* cycles, int64_t* units, int* g
     case P_LDS_TR64: return launch_probe<P_LDS_TR64>(threads, cycles, st);
     case P_LDS_W128: return launch_probe<P_LDS_W128>(threads, cycles, st);
     case P_LDS_W32: return launch_probe<P_LDS_W32>(threads, cycles, st);
+    case P_CVT_FP4: return launch_probe<P_CVT_FP4>(threads, cycles, st);
+    case P_EXP_FMA: return launch_probe<P_EXP_FMA>(threads, cycles, st);
+    case P_EXP_FMA3: return launch_probe<P_EXP_FMA3>(threads, cycles, st);
+    case P_EXP_MAX3: return launch_probe<P_EXP_MAX3>(threads, cycles, st);
+    case P_EXP_CVT_FP4: return launch_probe<P_EXP_CVT_FP4>(threads, cycles, st);
+    case P_EXP_FMA_G4: return launch_probe<P_EXP_FMA_G4>(threads, cycles, st);
+    case P_FMA_4W: return launch_probe<P_FMA_4W>(threads, cycles, st);
+    case P_MIX8_4W: return launch_probe<P_MIX8_4W>(threads, cycles, st);
+    case P_MIX16: return launch_probe<P_MIX16>(threads, cycles, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -22,7 +22,13 @@ def test_probe_mfma_costs_and_every_kind_runs(gpu):
     for kind, expect in ((5, 32.0), (6, 64.0), (7, 32.0)):
         assert abs(costs[kind] - expect) <= 0.05 * expect, (kind, costs[kind])
     # vector instructions cost at least one cycle each; LDS kinds move at most 256 B per clock per CU
-    for kind in range(5):
+    for kind in list(range(5)) + [18, 24]:
         assert 1.0 <= costs[kind] <= 32.0, (kind, costs[kind])
-    for kind in range(13, n):
+    # an exponential step with work beside it costs at least the exponential alone
+    for kind in range(19, 24):
+        assert costs[kind] >= 0.95 * costs[1], (kind, costs[kind], costs[1])
+    # MFMA with vector work beside it takes at least the MFMA time
+    for kind in list(range(8, 13)) + [25, 26]:
+        assert costs[kind] >= 0.95 * 32.0, (kind, costs[kind])
+    for kind in range(13, 18):
         assert 1.0 / costs[kind] <= 256.0 + 1.0, (kind, 1.0 / costs[kind])
