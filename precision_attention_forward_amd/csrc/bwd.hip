@@ -335,7 +335,6 @@ __device__ inline s16x4 bwd_lds_tr8(uint32_t a) {
 template <int D, bool CAUSAL, bool DEBUG>
 __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
   constexpr int KS = D / 16, DT = D / 32, KK = D / 64;
-  constexpr int NW = 8;                                     // waves per workgroup
   // bytes of one buffer of each chunk tile
   constexpr int QB = BWD_CHUNK * D * 2, DOB = BWD_CHUNK * D, DOTB = D * BWD_CHUNK;
   constexpr int NQC = QB / 1024, NDOC = DOB / 1024, NDOTC = DOTB / 1024;
@@ -396,25 +395,30 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
   const int total = G * nch;                    // (query head, query chunk) steps of each side
   const int m = ln;
 
-  // ---- chunk copies.  Wave w issues copies j = w + 8 t of each tile; the
-  // per-lane source offsets within a tile are loop invariant.
-  constexpr int NQW = (NQC + NW - 1) / NW, NDOW = (NDOC + NW - 1) / NW, NDOTW = (NDOTC + NW - 1) / NW;
+  // ---- chunk copies, issued by the dP side only: wave w < 4 issues copies
+  // j = w + 4 t of each tile.  A wave that issues copies stalls until the
+  // vector memory path has taken them (32 KB per step and workgroup, at about
+  // 64 bytes per clock), and the S side is the longer of the two; the dP side
+  // has the slack (4 % faster than all eight waves issuing).  The per-lane
+  // source offsets within a tile are loop invariant.
+  constexpr int CW = 4;
+  constexpr int NQW = (NQC + CW - 1) / CW, NDOW = (NDOC + CW - 1) / CW, NDOTW = (NDOTC + CW - 1) / CW;
   uint32_t oqc[NQW], odc[NDOW], otc[NDOTW];
 #pragma unroll
   for (int t = 0; t < NQW; ++t) {                          // Q rows: 2D bytes, 1024 / 2D rows per copy
-    const int j = wave + NW * t;
+    const int j = kw + CW * t;
     const int r = j * (1024 / (2 * D)) + (16 * lane) / (2 * D), c = ((16 * lane) % (2 * D)) / 16;
     oqc[t] = (uint32_t)(r * 2 * D + 16 * (c ^ swz_qtile<D>(r)));
   }
 #pragma unroll
   for (int t = 0; t < NDOW; ++t) {                         // dO rows: D bytes
-    const int j = wave + NW * t;
+    const int j = kw + CW * t;
     const int r = j * (1024 / D) + (16 * lane) / D, c = ((16 * lane) % D) / 16;
     odc[t] = (uint32_t)(r * D + 16 * (c ^ swz_qrows<D>(r)));
   }
 #pragma unroll
   for (int t = 0; t < NDOTW; ++t) {                        // dO^T rows: 64 bytes, 16 rows per copy
-    const int j = wave + NW * t;
+    const int j = kw + CW * t;
     const int d = 16 * j + (lane >> 2), c = lane & 3;
     otc[t] = (uint32_t)d * (uint32_t)npad + 16u * (uint32_t)(c ^ swz_drows64(d));
   }
@@ -427,12 +431,12 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
     const uint8_t* dtb0 = p.dot + qhead * D * npad + (int64_t)c * BWD_CHUNK;
 #pragma unroll
     for (int t = 0; t < NQW; ++t) {
-      const int j = wave + NW * t;
+      const int j = kw + CW * t;
       if (j < NQC) bwd_dma16(qb0, oqc[t], bwd_lds_address(&sQ[slot][0]) + 1024 * j);
     }
 #pragma unroll
     for (int t = 0; t < NDOTW; ++t) {
-      const int j = wave + NW * t;
+      const int j = kw + CW * t;
       if (j < NDOTC) bwd_dma16(dtb0, otc[t], bwd_lds_address(&sDOT[buf][0]) + 1024 * j);
     }
     if (wave == 0) bwd_dma4(p.lv + q0, (uint32_t)(4 * lane), bwd_lds_address(&sL[buf][0]));
@@ -443,7 +447,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
     const uint8_t* db0 = p.dorm + q0 * D;
 #pragma unroll
     for (int t = 0; t < NDOW; ++t) {
-      const int j = wave + NW * t;
+      const int j = kw + CW * t;
       if (j < NDOC) bwd_dma16(db0, odc[t], bwd_lds_address(&sDO[buf][0]) + 1024 * j);
     }
     if (wave == 1) bwd_dma4(p.dv + q0, (uint32_t)(4 * lane), bwd_lds_address(&sD[slot][0]));
@@ -479,8 +483,10 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
   const int wkey_last = kb * BWD_ROWS + kw * 32 + 31;
   // prologue: the tiles of chunk 0
   bwd_settle(res);
-  copy_s(0, c0, 0, 0);
-  copy_d(0, c0, 0, 0);
+  if (!s_side) {
+    copy_s(0, c0, 0, 0);
+    copy_d(0, c0, 0, 0);
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   // Each side runs its own copy of the step loop (one side per wave for the
@@ -494,7 +500,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
     gn = g;
     cn = c + 1;
     if (cn == nchunks) { cn = c0; ++gn; }
-    if (step + 1 < total) {
+    if (!s_side && step + 1 < total) {
       copy_s(gn, cn, (step + 1) % 3, (step + 1) & 1);
       copy_d(gn, cn, (step + 1) & 1, (step + 1) % 3);
     }
