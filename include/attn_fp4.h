@@ -480,8 +480,8 @@ attn_status attn_decode_fp8pv(const attn_decode_args* a, void* stream);
  *   dout   : bf16 [B, N, Hq, D]
  *   dq     : float [B, N, Hq, D];  dk, dv : float [B, N, Hkv, D] (written)
  *   ws     : attn_bwd_ws_bytes(args) bytes, 256-byte aligned: the prepared
- *            operands (bf16 Q^/K^ row-major, E5M2 dO^ row-major and
- *            transposed, key-major V codes, D and LSE log2 e per row)
+ *            operands (bf16 Q^/K^ row-major, E5M2 dO^ row-major,
+ *            key-major V codes, D and LSE log2 e per row)
  * Argument errors are found before any launch.  prof_event_begin/end
  * (hipEvent_t, nullable) are recorded around the dK/dV and dQ kernels.
  */

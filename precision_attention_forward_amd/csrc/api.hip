@@ -37,7 +37,7 @@ hipError_t launch_bwd_prep(const uint8_t* q_codes, const uint8_t* q_scales, cons
                            const uint8_t* k_scales, const uint8_t* v_codes, int64_t v_cols, const void* dout,
                            const void* o, const float* lse, const float* partials, int np, int B, int Hq, int Hkv,
                            int N, int D, int64_t npad, __bf16* qrm, __bf16* krm,
-                           uint8_t* vrm, uint8_t* drm, uint8_t* dtr, float* dvec, float* lvec, float* sdo,
+                           uint8_t* vrm, uint8_t* drm, float* dvec, float* lvec, float* sdo,
                            hipStream_t st);
 struct BwdParams;
 hipError_t launch_bwd_main(const BwdParams& p, int D, bool causal, bool debug, hipStream_t st);
@@ -385,11 +385,11 @@ attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, 
 
 // ---- backward -------------------------------------------------------------
 struct BwdLayout {
-  int64_t npad, qrm, krm, vrm, drm, dtr, dvec, lvec, sdo, partials, total;
+  int64_t npad, qrm, krm, vrm, drm, dvec, lvec, sdo, partials, total;
 };
 
 static bool bwd_shapes_ok(const attn_bwd_args* a) {
-  // the kernels address one head's transposed operands with 32-bit offsets: 2 D NPAD < 2^31
+  // the supported range: one head's bf16 operand rows (2 D NPAD bytes) below 2^31 bytes
   return a != nullptr && a->B >= 0 && a->N >= 0 && a->Hq > 0 && a->Hkv > 0 && a->Hq % a->Hkv == 0 &&
          (a->D == 64 || a->D == 128) && 2 * (int64_t)a->D * roundup(a->N, 128) < ((int64_t)1 << 31);
 }
@@ -404,7 +404,6 @@ static BwdLayout bwd_layout(const attn_bwd_args* a) {
   L.krm = off; off += al(2 * nk);
   L.vrm = off; off += al(nk);
   L.drm = off; off += al(nq);
-  L.dtr = off; off += al(nq);
   L.dvec = off; off += al(4 * (int64_t)a->B * a->Hq * L.npad);
   L.lvec = off; off += al(4 * (int64_t)a->B * a->Hq * L.npad);
   L.sdo = off; off += 256;
@@ -450,8 +449,8 @@ attn_status attn_bwd_fp8(const attn_bwd_args* a, void* stream) {
   float* sdo = (float*)(w + L.sdo);
   e = launch_bwd_prep(a->q.codes, a->q.scales, a->k.codes, a->k.scales, a->v.codes, (int64_t)a->B * L.npad, a->dout,
                       a->o, a->lse, partials, np, a->B, a->Hq, a->Hkv, a->N, a->D, L.npad, (__bf16*)(w + L.qrm),
-                      (__bf16*)(w + L.krm), w + L.vrm, w + L.drm,
-                      w + L.dtr, (float*)(w + L.dvec), (float*)(w + L.lvec), sdo, st);
+                      (__bf16*)(w + L.krm), w + L.vrm, w + L.drm, (float*)(w + L.dvec), (float*)(w + L.lvec), sdo,
+                      st);
   if (e != hipSuccess) return hip_status(e);
   BwdParams p;
   memset(&p, 0, sizeof(p));
@@ -459,7 +458,6 @@ attn_status attn_bwd_fp8(const attn_bwd_args* a, void* stream) {
   p.krm = (const __bf16*)(w + L.krm);
   p.vrm = w + L.vrm;
   p.dorm = w + L.drm;
-  p.dot = w + L.dtr;
   p.lv = (const float*)(w + L.lvec);
   p.dv = (const float*)(w + L.dvec);
   p.gq = a->q.tensor_scale;

@@ -138,17 +138,16 @@ __global__ void __launch_bounds__(256) bwd_expand_kernel(const uint8_t* __restri
   }
 }
 
-// Preparation 2: dO^ (E5M2, one scale per tensor), row-major and transposed,
-// D = sum_d dO^ O and LSE log2 e per row.  One workgroup per (64 rows, head,
+// Preparation 2: dO^ (E5M2, one scale per tensor), row-major, D = sum_d dO^ O
+// and LSE log2 e per row.  One workgroup per (64 rows, head,
 // batch); the tensor amax comes from the shared amax pass.
 template <int D>
 __global__ void __launch_bounds__(256) bwd_do_kernel(const uint16_t* __restrict__ dout, const uint16_t* __restrict__ o,
                                                      const float* __restrict__ lse, const float* __restrict__ partials,
                                                      int np, int H, int N, int64_t npad, uint8_t* __restrict__ drm,
-                                                     uint8_t* __restrict__ dtr, float* __restrict__ dvec,
+                                                     float* __restrict__ dvec,
                                                      float* __restrict__ lvec, float* __restrict__ sdo) {
   constexpr int G8 = D / 8;
-  __shared__ uint8_t tile[64][D + 16];
   __shared__ float part[64][G8 + 1];
   const float amax = bwd_reduce_partials(partials, np);
   float enc = amax == 0.0f ? 1.0f : 57344.0f / amax;
@@ -186,11 +185,6 @@ __global__ void __launch_bounds__(256) bwd_do_kernel(const uint16_t* __restrict_
       for (int j = 0; j < 8; ++j) acc = acc + (dq[j] * s) * ox[j];
     }
     *reinterpret_cast<u32x2*>(drm + (head * npad + n) * D + 8 * g) = u32x2{w0, w1};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      tile[row][8 * g + j] = (uint8_t)(w0 >> (8 * j));
-      tile[row][8 * g + 4 + j] = (uint8_t)(w1 >> (8 * j));
-    }
     part[row][g] = acc;
   }
   __syncthreads();
@@ -200,15 +194,6 @@ __global__ void __launch_bounds__(256) bwd_do_kernel(const uint16_t* __restrict_
     for (int g = 0; g < G8; ++g) acc = acc + part[row][g];
     dvec[head * npad + n] = n < N ? acc : 0.0f;
     lvec[head * npad + n] = n < N ? lse[head * N + n] * 1.4426950408889634f : __builtin_inff();
-  }
-  for (int it = threadIdx.x; it < D * 4; it += 256) {
-    const int d = it / 4, rg = it % 4;
-    u32x4 val;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      val[j] = (uint32_t)tile[16 * rg + 4 * j][d] | ((uint32_t)tile[16 * rg + 4 * j + 1][d] << 8) |
-               ((uint32_t)tile[16 * rg + 4 * j + 2][d] << 16) | ((uint32_t)tile[16 * rg + 4 * j + 3][d] << 24);
-    *reinterpret_cast<u32x4*>(dtr + (head * D + d) * npad + r0 + 16 * rg) = val;
   }
 }
 
@@ -253,7 +238,7 @@ __global__ void __launch_bounds__(256) bwd_v_kernel(const uint8_t* __restrict__ 
 template <int RB>                      // row bytes: 256 (16 chunks), 128 (8), 64 (4)
 __device__ __host__ inline int swz_qrows(int R) {
   if (RB == 256) return (R & 3) | (((R >> 4) & 1) << 2) | (((R >> 2) & 1) << 3);
-  if (RB == 128) return ((R >> 1) & 1) | (((R >> 4) & 1) << 1) | (((R ^ (R >> 2)) & 1) << 2);
+  if (RB == 128) return ((R >> 4) & 1) | (((R >> 1) & 1) << 1) | (((R ^ (R >> 2)) & 1) << 2);
   return ((R >> 4) & 1) | ((((R >> 1) ^ (R >> 2)) & 1) << 1);
 }
 // The Q^ tile of the dK/dV kernel (rows of 2D bytes) is also read through
@@ -322,7 +307,9 @@ __device__ inline u32x4 bwd_lds16(uint32_t a) {
 //   LDS: the Q^ chunk row-major in a ring of three (chunk x in slot x % 3:
 //   the S side's chunk, the dP side's chunk and the next), read straight for
 //   S and through transposing reads (ds_read_b64_tr_b16) as the Q^T operand of
-//   dK; dO^ row-major, dO^T, L and P in two buffers each, D in a ring of three.
+//   dK; dO^ row-major in two buffers, read straight for dP and through 8-bit
+//   transposing reads (ds_read_b64_tr_b8) as the dO^ operand of dV; L and P in
+//   two buffers each, D in a ring of three.
 // S / dP sub-tile s2 of a chunk: accumulator (lane half hh, register r) holds
 // query 32*s2 + 16*hh + r of the chunk; A row m of the S / dP products is
 // therefore query 32*s2 + 16*((m>>2)&1) + 4*(m>>3) + (m&3).
@@ -331,16 +318,24 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 __device__ inline s16x4 bwd_lds_tr8(uint32_t a) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)a);
 }
+// 8-bit transposing read: a 16-lane group reads 8 rows of 16 bytes (row j from
+// the addresses of lanes 2j and 2j + 1, 8 bytes each); lane c receives byte c
+// of every row
+typedef int i32x2v __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2v lds_i32x2;
+__device__ inline u32x2 bwd_lds_tr_b8(uint32_t a) {
+  const i32x2v r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(uintptr_t)a);
+  return u32x2{(uint32_t)r[0], (uint32_t)r[1]};
+}
 
 template <int D, bool CAUSAL, bool DEBUG>
 __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
   constexpr int KS = D / 16, DT = D / 32, KK = D / 64;
   // bytes of one buffer of each chunk tile
-  constexpr int QB = BWD_CHUNK * D * 2, DOB = BWD_CHUNK * D, DOTB = D * BWD_CHUNK;
-  constexpr int NQC = QB / 1024, NDOC = DOB / 1024, NDOTC = DOTB / 1024;
+  constexpr int QB = BWD_CHUNK * D * 2, DOB = BWD_CHUNK * D;
+  constexpr int NQC = QB / 1024, NDOC = DOB / 1024;
   __shared__ __attribute__((aligned(1024))) uint8_t sQ[3][QB];
   __shared__ __attribute__((aligned(1024))) uint8_t sDO[2][DOB];
-  __shared__ __attribute__((aligned(1024))) uint8_t sDOT[2][DOTB];
   __shared__ __attribute__((aligned(16))) float sL[2][BWD_CHUNK];   // read as 16-byte vectors
   __shared__ __attribute__((aligned(16))) float sD[3][BWD_CHUNK];   // chunk x in slot x % 3
   __shared__ __attribute__((aligned(16))) f32x4 sP[2][4][2][4][64];  // [buffer][key block][s2][r / 4][lane]
@@ -402,8 +397,8 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
   // has the slack (4 % faster than all eight waves issuing).  The per-lane
   // source offsets within a tile are loop invariant.
   constexpr int CW = 4;
-  constexpr int NQW = (NQC + CW - 1) / CW, NDOW = (NDOC + CW - 1) / CW, NDOTW = (NDOTC + CW - 1) / CW;
-  uint32_t oqc[NQW], odc[NDOW], otc[NDOTW];
+  constexpr int NQW = (NQC + CW - 1) / CW, NDOW = (NDOC + CW - 1) / CW;
+  uint32_t oqc[NQW], odc[NDOW];
 #pragma unroll
   for (int t = 0; t < NQW; ++t) {                          // Q rows: 2D bytes, 1024 / 2D rows per copy
     const int j = kw + CW * t;
@@ -416,28 +411,15 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
     const int r = j * (1024 / D) + (16 * lane) / D, c = ((16 * lane) % D) / 16;
     odc[t] = (uint32_t)(r * D + 16 * (c ^ swz_qrows<D>(r)));
   }
-#pragma unroll
-  for (int t = 0; t < NDOTW; ++t) {                        // dO^T rows: 64 bytes, 16 rows per copy
-    const int j = kw + CW * t;
-    const int d = 16 * j + (lane >> 2), c = lane & 3;
-    otc[t] = (uint32_t)d * (uint32_t)npad + 16u * (uint32_t)(c ^ swz_drows64(d));
-  }
   auto chunk_row = [&](int g, int c) { return ((int64_t)b * p.Hq + hk * G + g) * npad + (int64_t)c * BWD_CHUNK; };
-  // the S side's tiles of chunk (g, c): Q^ -> ring slot, dO^T and L -> buffer
+  // the S side's tiles of chunk (g, c): Q^ -> ring slot, L -> buffer
   auto copy_s = [&](int g, int c, int slot, int buf) {
     const int64_t q0 = chunk_row(g, c);
-    const int64_t qhead = (int64_t)b * p.Hq + hk * G + g;
     const uint8_t* qb0 = reinterpret_cast<const uint8_t*>(p.qrm + q0 * D);
-    const uint8_t* dtb0 = p.dot + qhead * D * npad + (int64_t)c * BWD_CHUNK;
 #pragma unroll
     for (int t = 0; t < NQW; ++t) {
       const int j = kw + CW * t;
       if (j < NQC) bwd_dma16(qb0, oqc[t], bwd_lds_address(&sQ[slot][0]) + 1024 * j);
-    }
-#pragma unroll
-    for (int t = 0; t < NDOTW; ++t) {
-      const int j = kw + CW * t;
-      if (j < NDOTC) bwd_dma16(dtb0, otc[t], bwd_lds_address(&sDOT[buf][0]) + 1024 * j);
     }
     if (wave == 0) bwd_dma4(p.lv + q0, (uint32_t)(4 * lane), bwd_lds_address(&sL[buf][0]));
   };
@@ -458,7 +440,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
   // may be applied to the LDS address).  Two bases per side, sharing two
   // registers:
   //   S side  b0: Q row R0, k-step ks: b0 ^ 32 ks (chunk 2 ks + hh)
-  //           b1: dO^T row ln (+ 32 dt), half lh: b1 ^ 32 lh (chunk 2 lh + hh)
+  //           b1: transposing dO read (t, dt): (b1 + (8 (t & 1) + 32 (t >> 1)) D) ^ 32 dt
   //   dP side b0: dO row R0, (kk, lh): b0 ^ (64 kk + 32 lh) (chunk 4 kk + 2 lh + hh)
   //           b1: transposing Q read (dt, half): lane (g, c) of a 16-lane
   //           group reads 4 bf16 of row 16 (g >> 1) + 4 half + (c >> 2) (+ 32
@@ -470,7 +452,14 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
   uint32_t b0, b1;
   if (s_side) {
     b0 = (uint32_t)(R0 * 2 * D + 16 * (hh ^ swz_qtile<D>(R0)));
-    b1 = (uint32_t)(ln * 64 + 16 * (hh ^ swz_drows64(ln)));
+    // transposing 8-bit reads of the row-major dO^ tile: lane (g, c) of a
+    // 16-lane group gives the address of row 16 (g >> 1) + (c >> 1) (+ 8 t0 +
+    // 32 t1, which leave the swizzle unchanged), bytes 8 (c & 1) of chunk
+    // 2 dt + (g & 1); the transpose hands lane c channel 32 dt + 16 (g & 1) + c
+    // of 8 consecutive queries
+    const int g4 = lane >> 4, c16 = lane & 15;
+    const int R = 16 * (g4 >> 1) + (c16 >> 1);
+    b1 = (uint32_t)(R * D + 16 * ((g4 & 1) ^ swz_qrows<D>(R)) + 8 * (c16 & 1));
   } else {
     b0 = (uint32_t)(R0 * D + 16 * (hh ^ swz_qrows<D>(R0)));
     const int g4 = lane >> 4, c16 = lane & 15;
@@ -610,12 +599,16 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) p.dbg_pt_e[(int64_t)(2 * c + s2) * npad + key] = (uint8_t)(ep[s2] + 127);
         }
-        const uint32_t ta = bwd_lds_address(&sDOT[buf][0]) + b1;
+        const uint32_t ta = bwd_lds_address(&sDO[buf][0]) + b1;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const u32x4 lo = bwd_lds16(ta + 32 * 64 * dt);
-          const u32x4 hi = bwd_lds16((ta ^ 32u) + 32 * 64 * dt);
-          const i32x8 bb = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          // queries 16 hh + [0, 16) and 32 + 16 hh + [0, 16) of channel 32 dt + ln
+          u32x2 w[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            w[t] = bwd_lds_tr_b8((ta + (uint32_t)((8 * (t & 1) + 32 * (t >> 1)) * D)) ^ (32u * (uint32_t)dt));
+          const i32x8 bb = {(int)w[0][0], (int)w[0][1], (int)w[1][0], (int)w[1][1],
+                            (int)w[2][0], (int)w[2][1], (int)w[3][0], (int)w[3][1]};
           // A: P~ (E4M3, format 0) with its block exponents, B: dO^ codes (E5M2, format 1)
           acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pa, bb, acc[dt], 0, 1, 0, scale_p, 0, 127);
         }
@@ -1046,21 +1039,20 @@ hipError_t launch_bwd_prep(const uint8_t* q_codes, const uint8_t* q_scales, cons
                            const uint8_t* k_scales, const uint8_t* v_codes, int64_t v_cols, const void* dout,
                            const void* o, const float* lse, const float* partials, int np, int B, int Hq, int Hkv,
                            int N, int D, int64_t npad, __bf16* qrm, __bf16* krm,
-                           uint8_t* vrm, uint8_t* drm, uint8_t* dtr, float* dvec, float* lvec, float* sdo,
-                           hipStream_t st) {
+                           uint8_t* vrm, uint8_t* drm, float* dvec, float* lvec, float* sdo, hipStream_t st) {
   const dim3 gq((unsigned)(npad / 64), (unsigned)Hq, (unsigned)B), gk((unsigned)(npad / 64), (unsigned)Hkv, (unsigned)B);
   if (D == 64) {
     hipLaunchKernelGGL(bwd_expand_kernel<64>, gq, dim3(256), 0, st, q_codes, q_scales, Hq, N, npad, qrm);
     hipLaunchKernelGGL(bwd_expand_kernel<64>, gk, dim3(256), 0, st, k_codes, k_scales, Hkv, N, npad, krm);
     hipLaunchKernelGGL(bwd_v_kernel<64>, gk, dim3(256), 0, st, v_codes, Hkv, v_cols, npad, vrm);
     hipLaunchKernelGGL(bwd_do_kernel<64>, gq, dim3(256), 0, st, (const uint16_t*)dout, (const uint16_t*)o, lse,
-                       partials, np, Hq, N, npad, drm, dtr, dvec, lvec, sdo);
+                       partials, np, Hq, N, npad, drm, dvec, lvec, sdo);
   } else {
     hipLaunchKernelGGL(bwd_expand_kernel<128>, gq, dim3(256), 0, st, q_codes, q_scales, Hq, N, npad, qrm);
     hipLaunchKernelGGL(bwd_expand_kernel<128>, gk, dim3(256), 0, st, k_codes, k_scales, Hkv, N, npad, krm);
     hipLaunchKernelGGL(bwd_v_kernel<128>, gk, dim3(256), 0, st, v_codes, Hkv, v_cols, npad, vrm);
     hipLaunchKernelGGL(bwd_do_kernel<128>, gq, dim3(256), 0, st, (const uint16_t*)dout, (const uint16_t*)o, lse,
-                       partials, np, Hq, N, npad, drm, dtr, dvec, lvec, sdo);
+                       partials, np, Hq, N, npad, drm, dvec, lvec, sdo);
   }
   return hipGetLastError();
 }

@@ -12,7 +12,6 @@ struct BwdParams {
   const __bf16* krm;      // [B][Hkv][NPAD][D]
   const uint8_t* vrm;     // [B][Hkv][NPAD][D]  FP8 E4M3 V codes, key-major
   const uint8_t* dorm;    // [B][Hq][NPAD][D]   E5M2 dO codes
-  const uint8_t* dot;     // [B][Hq][D][NPAD]
   const float* lv;        // [B][Hq][NPAD]      LSE * log2 e (+inf on padded rows)
   const float* dv;        // [B][Hq][NPAD]      D = sum_d dO^ O
   const float* gq;        // device scalars: tensor scales of Q, K, V and dO

@@ -163,7 +163,7 @@ def test_fwd_validation(lib):
     need_b = lib.attn_bwd_ws_bytes(ctypes.byref(bw))
     nq_b, nk_b = 2 * 4 * 256 * 128, 2 * 2 * 256 * 128   # elements of Q / dO and of K / V
     # bf16 Q^ and K^, E4M3 V, E5M2 dO^ row-major and transposed
-    assert need_b > 2 * nq_b + 2 * nk_b + nk_b + 2 * nq_b
+    assert need_b > 2 * nq_b + 2 * nk_b + nk_b + nq_b
     bw.D = 96
     assert lib.attn_bwd_ws_bytes(ctypes.byref(bw)) == 0 and lib.attn_bwd_fp8(ctypes.byref(bw), None) == 1
     bw.D, bw.Hkv = 128, 3
