@@ -58,9 +58,11 @@ __host__ __device__ inline int out_row(int v, int hh) { return 8 * (v >> 2) + 4 
 // Pre-pass: exact FP16 expansion of NVFP4 K into the operand tile order.
 //   K tile (128 keys, D): element (st, kh, ks, r, j) at (((st*2+kh)*KS+ks)*32+r)*8+j,
 //     holding K[key = s_key(st, v(r), hh(r))][d = kh*D/2 + 8*ks + j], KS = D/16.
-// Each thread writes whole 16-byte chunks in output order (coalesced) and
-// gathers the 4 code bytes and the scale of its 8 elements.  Keys past the
-// end of the sequence are written as zeros.
+// The tile's code rows (D/2 bytes per key) and scale rows (D/16 bytes) are
+// first staged in LDS with row-contiguous loads (consecutive keys of one head
+// lie H rows apart); then each thread writes whole 16-byte chunks in output
+// order (coalesced), gathering the 4 code bytes and the scale of its 8
+// elements from LDS.  Keys past the end of the sequence are written as zeros.
 template <int D, int PF>
 __global__ void __launch_bounds__(256) expand_k_kernel(const uint8_t* __restrict__ codes,
                                                        const uint8_t* __restrict__ scales, int H, int N,
@@ -72,20 +74,34 @@ __global__ void __launch_bounds__(256) expand_k_kernel(const uint8_t* __restrict
   const int len = varlen ? cu[s + 1] - cu[s] : N;
   if (tile * KEY_TILE >= len) return;
   constexpr int KS = D / 16, HALF = D / 2, CHUNKS = KEY_TILE * D / 8;
+  constexpr int CW = HALF / 4, SB = D / 16;          // code words and scale bytes per key
+  __shared__ uint32_t scode[KEY_TILE][CW + 1];
+  __shared__ uint8_t sscale[KEY_TILE][SB];
+  for (int i = threadIdx.x; i < KEY_TILE * (CW / 2); i += 256) {   // 8-byte pieces of the code rows
+    const int key = i / (CW / 2), c = i % (CW / 2);
+    const int idx = tile * KEY_TILE + key;
+    u32x2 w = {0u, 0u};
+    if (idx < len) w = *reinterpret_cast<const u32x2*>(codes + ((tok0 + idx) * H + h) * HALF + 8 * c);
+    scode[key][2 * c] = w[0];
+    scode[key][2 * c + 1] = w[1];
+  }
+  for (int i = threadIdx.x; i < KEY_TILE * SB; i += 256) {
+    const int key = i / SB, c = i % SB;
+    const int idx = tile * KEY_TILE + key;
+    sscale[key][c] = idx < len ? scales[((tok0 + idx) * H + h) * SB + c] : (uint8_t)0;
+  }
+  __syncthreads();
   _Float16* tb = out + ((int64_t)h * cols + kcol_offset(varlen, s, tok0, n_pad) + (int64_t)tile * KEY_TILE) * D;
   for (int u = threadIdx.x; u < CHUNKS; u += 256) {
     const int r = u & 31, ks = (u >> 5) % KS, kh = ((u >> 5) / KS) & 1, st = (u >> 5) / (2 * KS);
     const int hh = (r >> 2) & 1, v = 4 * (r >> 3) + (r & 3);   // inverse of out_row
-    const int idx = tile * KEY_TILE + s_key<PF>(st, v, hh);
+    const int key = s_key<PF>(st, v, hh);
     const int d0 = kh * HALF + 8 * ks;
-    f16x8 val = {};
-    if (idx < len) {
-      const int64_t row = (tok0 + idx) * H + h;
-      const uint32_t cw = *reinterpret_cast<const uint32_t*>(codes + row * HALF + d0 / 2);
-      const float sv = e4m3_decode(scales[row * (D / 16) + d0 / 16]);
+    const uint32_t cw = scode[key][d0 / 8];
+    const float sv = e4m3_decode(sscale[key][d0 / 16]);
+    f16x8 val;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) val[j] = (_Float16)(e2m1_decode((cw >> (4 * j)) & 0xFu) * sv);
-    }
+    for (int j = 0; j < 8; ++j) val[j] = (_Float16)(e2m1_decode((cw >> (4 * j)) & 0xFu) * sv);
     *reinterpret_cast<f16x8*>(tb + u * 8) = val;
   }
 }
