@@ -229,13 +229,16 @@ def quant_v(v, fmt, cu_seqlens=None, max_seqlen=None):
         B = cu_seqlens.numel() - 1
         Nk = int(max_seqlen)
     cols = lib.attn_v_cols(B, Nk, total, 0 if cu_seqlens is None else 1)
+    # dense: the library writes every column (zeros past Nk in the last tile);
+    # packed: the columns between sequences are never written, so they are zeroed
+    alloc = torch.empty if cu_seqlens is None else torch.zeros
     if fmt == V_FP8:
-        codes = torch.zeros((Hkv, D, cols), dtype=torch.uint8, device=v.device)
+        codes = alloc((Hkv, D, cols), dtype=torch.uint8, device=v.device)
         scales = None
         ts = torch.empty(1, dtype=torch.float32, device=v.device)
     else:
-        codes = torch.zeros((Hkv, D, cols // 2), dtype=torch.uint8, device=v.device)
-        scales = torch.zeros((Hkv, D, cols // 32), dtype=torch.uint8, device=v.device)
+        codes = alloc((Hkv, D, cols // 2), dtype=torch.uint8, device=v.device)
+        scales = alloc((Hkv, D, cols // 32), dtype=torch.uint8, device=v.device)
         ts = None
     ws = torch.empty(lib.attn_quant_ws_bytes(), dtype=torch.uint8, device=v.device)
     _check(lib.attn_quant_v(_ptr(v), B, Nk, Hkv, D, _ptr(cu_seqlens), total, fmt, _ptr(codes), _ptr(scales),
