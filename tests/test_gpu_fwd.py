@@ -514,3 +514,95 @@ def test_no_keys_gives_empty_softmax(gpu, entry):
                 assert not O.any() and bool(np.isneginf(L).all())
             else:
                 assert_close_outputs(o[q0:q1, h], lse[h, q0:q1], O, L, f"seq {s} head {h}")
+
+
+# ---- cross attention: Nq != Nk (non-causal; causal needs Nq == Nk) -------------
+# Dense cases take Q from the first Nq tokens and K / V from the first Nk tokens
+# of one draw of the workload's recipe (so the Wan recipe's outlier channels
+# agree); packed cases draw the query and the key sequences from two seeds with
+# the same number of sequences.
+CROSS = [
+    ("dense_mxfp4_q_lt_k", synth.WORKLOADS[2].with_(Hq=2, Hkv=2, seed=91), 300, 700, None),
+    ("dense_mxfp4_q_gt_k_gqa", synth.WORKLOADS[2].with_(Hq=2, Hkv=1, seed=92), 650, 200, None),
+    ("dense_fp8_d64_gqa", synth.WORKLOADS[4].with_(B=2, Hq=4, Hkv=2, D=64, causal=False, seed=93), 129, 383, None),
+    ("varlen_fp8_gqa", synth.WORKLOADS[5].with_(Hq=2, Hkv=1, p_format="fp8", seed=94), 0, 0, (4, 300, 520)),
+    ("varlen_mxfp4", synth.WORKLOADS[5].with_(Hq=2, Hkv=2, v_format="mxfp4", seed=95), 0, 0, (3, 450, 140)),
+]
+
+
+def _cross_inputs(wl, nq, nk, varlen):
+    if varlen is None:
+        inp = synth.generate(wl.with_(N=max(nq, nk)), "cpu")
+        return (inp.q[:, :nq].contiguous(), inp.k[:, :nk].contiguous(), inp.v[:, :nk].contiguous(), None, None,
+                inp.sigma)
+    n, qhi, khi = varlen
+    iq = synth.generate(wl.with_(varlen=(n, 1, qhi)), "cpu")
+    ik = synth.generate(wl.with_(varlen=(n, 1, khi), seed=wl.seed + 1000), "cpu")
+    return iq.q, ik.k, ik.v, iq.cu_seqlens, ik.cu_seqlens, iq.sigma
+
+
+@pytest.mark.parametrize("name,wl,nq,nk,varlen", CROSS, ids=[c[0] for c in CROSS])
+def test_cross_attention(gpu, name, wl, nq, nk, varlen):
+    """Every output of every (sequence, head) against the oracle run on the
+    query rows and the other key sequence, with the P-code dump checks."""
+    _say(f"fwd cross {name}")
+    qb, kb, vb, cu_q, cu_k, sigma = _cross_inputs(wl, nq, nk, varlen)
+    qb, kb, vb = qb.cuda(), kb.cuda(), vb.cuda()
+    q, k = gpu.quant_nvfp4(qb), gpu.quant_nvfp4(kb)
+    vf = gpu.V_FP8 if wl.v_format == "fp8" else gpu.V_MXFP4
+    kw = dict(Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D, softmax_scale=sigma, causal=False, out_dtype=torch.float32)
+    if cu_q is None:
+        vq = gpu.quant_v(vb, vf)
+        kw.update(B=wl.B, Nq=nq, Nk=nk)
+        seqs = [(b, b * nq, nq, b * nk, nk) for b in range(wl.B)]
+    else:
+        mq, mk = int((cu_q[1:] - cu_q[:-1]).max()), int((cu_k[1:] - cu_k[:-1]).max())
+        vq = gpu.quant_v(vb, vf, cu_seqlens=cu_k.cuda(), max_seqlen=mk)
+        kw.update(cu_seqlens_q=cu_q.cuda(), cu_seqlens_k=cu_k.cuda(), max_seqlen_q=mq, max_seqlen_k=mk)
+        seqs = [(s, int(cu_q[s]), int(cu_q[s + 1] - cu_q[s]), int(cu_k[s]), int(cu_k[s + 1] - cu_k[s]))
+                for s in range(len(cu_q) - 1)]
+    v = (vf, vq[0], vq[1], vq[2])
+    fn = getattr(gpu, ENTRY[(wl.p_format, "exact")])
+    o, lse, _ = fn(q, k, v, **kw)
+    torch.cuda.synchronize()
+    group = wl.Hq // wl.Hkv
+    amax_q, amax_k, amax_v = _amax(qb), _amax(kb), _amax(vb)
+    pure = PureCompare(f"{name} vs the oracle")
+    mis_all = tot_all = 0
+    tmp = tempfile.mkdtemp(prefix="attn_cross_", dir="/dev/shm" if os.path.isdir("/dev/shm") else None)
+    try:
+        futs = []
+        for (s, q0, lq, k0, lk) in seqs:
+            if lq == 0:
+                continue
+            for h in range(wl.Hq):
+                hk = h // group
+                if cu_q is None:
+                    qh, kh, vh = qb[s, :, h], kb[s, :, hk], vb[s, :, hk]
+                    og, lg = o[s, :, h], lse[s, h]
+                else:
+                    qh, kh, vh = qb[q0:q0 + lq, h], kb[k0:k0 + lk, hk], vb[k0:k0 + lk, hk]
+                    og, lg = o[q0:q0 + lq, h], lse[h, q0:q0 + lq]
+                od, ld, (dc, ds) = fn(q, k, v, debug=(s, h), **kw)
+                assert torch.equal(od, o) and torch.equal(ld, lse), "the dump build computes other outputs"
+                path = os.path.join(tmp, f"kv_{s}_{h}.npz")
+                np.savez(path, k=f32(kh), v=f32(vh))
+                task = dict(kv_path=path, kv_params=dict(amax_k=amax_k, amax_v=amax_v, v_format=wl.v_format,
+                                                         four_six=False, qk="nvfp4"),
+                            q=f32(qh), q_params=dict(amax_q=amax_q, sigma=sigma, four_six=False, qk="nvfp4"),
+                            rows=np.arange(lq), L=lk, p_format=wl.p_format, encoder="exact", causal=False,
+                            og=f32(og).astype(np.float64), lg=f32(lg).astype(np.float64),
+                            dc=dc[:lq].cpu().numpy(), ds=None if ds is None else ds[:lq].cpu().numpy(),
+                            what=f"seq {s} head {h}")
+                futs.append((task["og"], task["lg"], oracle_pool.pool().submit(oracle_pool.fwd_chunk, task)))
+        for og, lg, f in futs:
+            out = f.result()
+            pure.add(og, lg, out["O"], out["L"], out["ob"], out["lb"])
+            mis_all += out["mis"]
+            tot_all += out["tot"]
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    rel = pure.finish()
+    assert tot_all > 0 and mis_all <= P_MISMATCH_MAX * tot_all, f"P codes: {mis_all} of {tot_all} differ"
+    print(f"  P codes: {mis_all} of {tot_all} differ; O rel L2 {rel:.2e}, max abs {pure.max_abs:.2e}, "
+          f"LSE rel {pure.lse_rel:.2e} over {pure.rows} rows", flush=True)
