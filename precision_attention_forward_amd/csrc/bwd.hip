@@ -71,12 +71,6 @@ __device__ inline int mx_e4m3_exponent(float a) {
   return e < -127 ? -127 : e;
 }
 
-// 16 bytes at base + off: base wave-uniform, off a per-lane byte offset below
-// 4 GiB (a scalar base plus a 32-bit vector offset in the load).
-__device__ inline u32x4 load16(const void* base, uint32_t off) {
-  return *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(base) + off);
-}
-
 // The float32 whose exponent field is the E8M0 byte e + 127 (2^e; for
 // e = -127 the field is 0).  gfx950's scaled conversions take only the
 // exponent field of their scale operand.
@@ -771,7 +765,6 @@ constexpr int BWD_QROWS = 256;     // queries per dQ workgroup
 template <int D, bool CAUSAL, bool DEBUG>
 __global__ void __launch_bounds__(512, 1) bwd_dq_kernel(BwdParams p) {
   constexpr int KS = D / 16, DT = D / 32, KK = D / 64;
-  constexpr int NW = 8;
   constexpr int KB = BWD_CHUNK * D * 2, VB = BWD_CHUNK * D;        // bytes of one K^ / V chunk
   constexpr int NKC = KB / 1024, NVC = VB / 1024;
   constexpr int CW = 4;
