@@ -295,9 +295,10 @@ __device__ inline u32x4 bwd_lds16(uint32_t a) {
 // float32 (the dP side's lane l needs exactly the 32 values lane l of its
 // partner computed).  One barrier per step, so one wave's matrix products
 // overlap its partner's vector work; each wave holds one accumulator and one
-// resident operand (K^ or V), so the two fit on one SIMD.  The dP side, the
-// longer of the two, takes the older waves, which win the SIMD's issue
-// arbitration.
+// resident operand (K^ or V), so the two fit on one SIMD.  The dP side takes
+// the older waves, which win the SIMD's issue arbitration (measured faster
+// than the other assignment, when the dP side also issued only its share of
+// the copies).
 //   LDS: the Q^ chunk row-major in a ring of three (chunk x in slot x % 3:
 //   the S side's chunk, the dP side's chunk and the next), read straight for
 //   S and through transposing reads (ds_read_b64_tr_b16) as the Q^T operand of
@@ -387,9 +388,10 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
   // ---- chunk copies, issued by the dP side only: wave w < 4 issues copies
   // j = w + 4 t of each tile.  A wave that issues copies stalls until the
   // vector memory path has taken them (32 KB per step and workgroup, at about
-  // 64 bytes per clock), and the S side is the longer of the two; the dP side
-  // has the slack (4 % faster than all eight waves issuing).  The per-lane
-  // source offsets within a tile are loop invariant.
+  // 64 bytes per clock); with the copies spread over all eight waves the dP
+  // side waited at the barrier for the S side every step, so it takes them
+  // all (4 % faster than all eight waves issuing).  The per-lane source
+  // offsets within a tile are loop invariant.
   constexpr int CW = 4;
   constexpr int NQW = (NQC + CW - 1) / CW, NDOW = (NDOC + CW - 1) / CW;
   uint32_t oqc[NQW], odc[NDOW];
