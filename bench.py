@@ -149,7 +149,11 @@ PROBE_NAMES = ("v_fma_f32", "v_exp_f32", "v_med3_f32", "v_cvt_scalef32_pk_fp8_f3
                "v_cvt_scalef32_pk_fp4_f32 (two values)",
                "v_exp_f32 + 1 v_fma_f32", "v_exp_f32 + 3 v_fma_f32", "v_exp_f32 + 1 v_max3_f32",
                "v_exp_f32 + 1 v_cvt_scalef32_pk_fp4_f32", "4 v_exp_f32 + 4 v_fma_f32 (per 4 steps)",
-               "v_fma_f32, four waves per SIMD", "8 v_fma_f32 per MFMA, four waves", "16 v_fma_f32 per MFMA, two waves")
+               "v_fma_f32, four waves per SIMD", "8 v_fma_f32 per MFMA, four waves", "16 v_fma_f32 per MFMA, two waves",
+               "bf16 MFMA wave + 3x v_fma_f32 wave", "bf16 MFMA wave + 4x v_fma_f32 wave",
+               "bf16 MFMA wave + 2x v_exp_f32 wave",
+               "forward tile mix, interleaved", "forward tile mix, ping-pong with barriers",
+               "forward tile mix, encode chains in one slot", "forward tile mix, encode chains over three slots")
 
 
 def issue_rates():
@@ -171,9 +175,12 @@ def issue_rates():
             line["bytes_per_clock_per_cu"] = round(units / cyc, 1)
         elif 19 <= kind <= 23:
             line["cycles_per_exp_step_per_simd"] = round(cyc / units, 2)
-        elif 8 <= kind <= 12 or kind >= 25:
+        elif 8 <= kind <= 12 or 25 <= kind <= 29:
             line["mfma_per_simd"] = units
             line["time_over_mfma_alone"] = round(cyc / (32.0 * units), 3)
+        elif kind >= 30:
+            line["cycles_per_wave_tile_per_simd"] = round(cyc / units, 1)
+            line["time_over_mfma_alone"] = round(cyc / units / (42 * 32.0), 3)
         else:
             line["cycles_per_instruction_per_simd"] = round(cyc / units, 2)
         print(json.dumps(line), flush=True)

@@ -548,7 +548,13 @@ attn_status attn_bwd_fp8(const attn_bwd_args* a, void* stream);
  * 19 in runs of four exponentials and four FMAs (units = steps per SIMD);
  * 24 v_fma_f32 at four waves per SIMD (1024 threads); 25 as 12 at four
  * waves per SIMD; 26 as 12 with 16 v_fma_f32 per MFMA (units = MFMA per
- * SIMD for 25 and 26).
+ * SIMD for 25 and 26); 27, 28: as 8 with 3 and 4 times the FMAs, 29: as 9
+ * with twice the exponentials (units = MFMA per SIMD); 30-33: the forward
+ * key loop's instruction mix per 128-key tile (42 bf16 MFMA, 64 v_exp_f32,
+ * 32 FP4 conversions, 36 v_max3_f32, the rest v_fma_f32) -- 30 interleaved
+ * one MFMA per slot, 31 as two-phase ping-pong with a barrier per phase, 32
+ * and 33 with the encode as dependent fma -> exp -> conversion chains, in
+ * one slot (32) or spread over three (33); units = wave-tiles per SIMD.
  * Errors: ATTN_ERR_INVALID_ARGUMENT (kind out of range, null or misaligned
  * pointer), ATTN_ERR_HIP.
  */

@@ -31,19 +31,37 @@ enum ProbeKind {
   P_EXP_FMA_G4,                                         // as P_EXP_FMA, in runs of four of each
   P_FMA_4W, P_MIX8_4W,                                  // 16 waves per CU (four per SIMD)
   P_MIX16,                                              // 8 waves: 16 FMA per MFMA in each wave
+  P_MFMA_FMA3, P_MFMA_FMA4, P_MFMA_EXP2,                // as P_MFMA_AND_FMA / EXP with 3x, 4x, 2x the vector work
+  P_FWD_INTER, P_FWD_PPB, P_FWD_DEP, P_FWD_SKEW,        // the forward key loop's instruction mix per 128-key tile
   P_COUNT
 };
+
+// The forward mix per wave and 128-key tile: 42 bf16 32x32x16 MFMA and 228
+// vector instructions (64 v_exp_f32, 32 FP4 conversions, 36 v_max3_f32, 96
+// v_fma_f32), all independent (FX_*), or with the encode as dependent chains.
+#define FX_MFMA(c) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc[(c) & 3]) : "v"(opb), "v"(opb))
+#define FX_EXP(i) asm volatile("v_exp_f32 %0, %0" : "+v"(x[(i) & 7]))
+#define FX_FMA(i) asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(y[(i) & 7]) : "v"(a), "v"(b))
+#define FX_MAX3(i) asm volatile("v_max3_f32 %0, %0, |%1|, |%2|" : "+v"(z[(i) & 3]) : "v"(a), "v"(b))
+#define FX_CVT(i) asm volatile("v_cvt_scalef32_pk_fp4_f32 %0, %1, %1, %2" : "+v"(w[(i) & 3]) : "v"(y[((i) + 3) & 7]), "v"(one))
+#define FX_VUNIT(u) do { const int uu = (u); \
+    if (uu % 57 < 16) FX_EXP(uu); else if (uu % 57 < 24) FX_CVT(uu); else if (uu % 57 < 33) FX_MAX3(uu); else FX_FMA(uu); } while (0)
 
 template <int KIND>
 __global__ void __launch_bounds__(1024) probe_kernel(long long* cycles) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[PROBE_LDS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  float x[8], y[8];
+  float x[8], y[8], z[4], w[4];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     x[i] = 0.001f * (float)(tid + i);
     y[i] = 0.002f * (float)(tid + i);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    z[i] = 0.1f * (float)(tid + i);
+    w[i] = 0.0f;
   }
   const float a = 1.0001f, b = 0.5f, one = 1.0f;
   f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
@@ -59,7 +77,114 @@ __global__ void __launch_bounds__(1024) probe_kernel(long long* cycles) {
   u32x4 lacc = {0, 0, 0, 0};
   __syncthreads();
   const long long t0 = __builtin_readcyclecounter();
-  if (KIND == P_CVT_FP4) {
+  if (KIND >= P_MFMA_FMA3 && KIND <= P_MFMA_EXP2) {
+    // waves 0-3: 4 MFMA per iteration; waves 4-7: N x 8 FMA or exponentials
+    constexpr int N = KIND == P_MFMA_FMA3 ? 3 : KIND == P_MFMA_FMA4 ? 4 : 2;
+    if (wave < 4) {
+      for (int it = 0; it < PROBE_ITERS; ++it) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opb, opb, acc[c & 1], 0, 0, 0);
+      }
+    } else {
+      for (int it = 0; it < PROBE_ITERS; ++it) {
+#pragma unroll
+        for (int r = 0; r < N; ++r)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            if (KIND == P_MFMA_EXP2) asm volatile("v_exp_f32 %0, %0" : "+v"(x[i]));
+            else asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(x[i]) : "v"(a), "v"(b));
+          }
+      }
+    }
+  } else if (KIND == P_FWD_INTER || KIND == P_FWD_PPB) {
+    constexpr int T = PROBE_ITERS / 32;   // tiles per wave
+    if (KIND == P_FWD_INTER) {
+      // every wave: 42 slots of one MFMA and its share of the 228 vector instructions
+      for (int t = 0; t < T; ++t) {
+#pragma unroll
+        for (int sl = 0; sl < 42; ++sl) {
+          FX_MFMA(sl);
+#pragma unroll
+          for (int u = (sl * 228) / 42; u < ((sl + 1) * 228) / 42; ++u) FX_VUNIT(u);
+        }
+      }
+    } else {
+      // ping-pong: each wave alternates the 42 MFMA and the 228 vector
+      // instructions; waves 4-7 start with a vector phase, so the two waves of a
+      // SIMD are in opposite phases, with a workgroup barrier after every phase
+      if (wave >= 4) {
+#pragma unroll
+        for (int u = 0; u < 228; ++u) FX_VUNIT(u);
+        __builtin_amdgcn_s_barrier();
+      }
+      for (int t = 0; t < T; ++t) {
+#pragma unroll
+        for (int sl = 0; sl < 42; ++sl) FX_MFMA(sl);
+        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int u = 0; u < 228; ++u) FX_VUNIT(u);
+        __builtin_amdgcn_s_barrier();
+      }
+      if (wave < 4) {
+#pragma unroll
+        for (int sl = 0; sl < 42; ++sl) FX_MFMA(sl);
+        __builtin_amdgcn_s_barrier();
+      }
+    }
+  } else if (KIND == P_FWD_DEP || KIND == P_FWD_SKEW) {
+    // the encode as dependent chains: per unit of two scores t = fma(s, c, -m),
+    // p = exp(t), codes = cvt(p0, p1); 32 units per tile, one starting in each
+    // of slots 0-31, beside 100 further vector instructions (36 max3, 64 fma);
+    // 260 vector instructions per tile.  DEP: a unit's whole chain in its slot;
+    // SKEW: its fma in slot i, its exponentials in slot i+1, its conversion in
+    // slot i+2.
+    constexpr int T = PROBE_ITERS / 32;
+    float sv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sv[i] = 0.01f * (float)(tid + i);
+    float t0[3], t1[3], p0[3], p1[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) t0[i] = t1[i] = p0[i] = p1[i] = 0.0f;
+    for (int t = 0; t < T; ++t) {
+#pragma unroll
+      for (int sl = 0; sl < 42; ++sl) {
+        FX_MFMA(sl);
+        if (KIND == P_FWD_DEP) {
+          if (sl < 32) {
+            const float a0 = sv[(2 * sl) & 7], a1 = sv[(2 * sl + 1) & 7];
+            asm volatile("v_fma_f32 %0, %1, %2, %3" : "=v"(t0[0]) : "v"(a0), "v"(a), "v"(b));
+            asm volatile("v_fma_f32 %0, %1, %2, %3" : "=v"(t1[0]) : "v"(a1), "v"(a), "v"(b));
+            asm volatile("v_exp_f32 %0, %1" : "=v"(p0[0]) : "v"(t0[0]));
+            asm volatile("v_exp_f32 %0, %1" : "=v"(p1[0]) : "v"(t1[0]));
+            asm volatile("v_cvt_scalef32_pk_fp4_f32 %0, %1, %2, %3" : "+v"(w[sl & 3]) : "v"(p0[0]), "v"(p1[0]), "v"(one));
+          }
+        } else {
+          if (sl >= 2 && sl < 34) {
+            const int k2 = (sl - 2) % 3;
+            asm volatile("v_cvt_scalef32_pk_fp4_f32 %0, %1, %2, %3" : "+v"(w[sl & 3]) : "v"(p0[k2]), "v"(p1[k2]), "v"(one));
+          }
+          if (sl >= 1 && sl < 33) {
+            const int k1 = (sl - 1) % 3;
+            asm volatile("v_exp_f32 %0, %1" : "=v"(p0[k1]) : "v"(t0[k1]));
+            asm volatile("v_exp_f32 %0, %1" : "=v"(p1[k1]) : "v"(t1[k1]));
+          }
+          if (sl < 32) {
+            const int k = sl % 3;
+            const float a0 = sv[(2 * sl) & 7], a1 = sv[(2 * sl + 1) & 7];
+            asm volatile("v_fma_f32 %0, %1, %2, %3" : "=v"(t0[k]) : "v"(a0), "v"(a), "v"(b));
+            asm volatile("v_fma_f32 %0, %1, %2, %3" : "=v"(t1[k]) : "v"(a1), "v"(a), "v"(b));
+          }
+        }
+#pragma unroll
+        for (int u = (sl * 100) / 42; u < ((sl + 1) * 100) / 42; ++u) {
+          if (u % 25 < 9) FX_MAX3(u);
+          else FX_FMA(u);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i) x[i] += t0[i] + t1[i] + p0[i] + p1[i];
+  } else if (KIND == P_CVT_FP4) {
     for (int it = 0; it < PROBE_ITERS; ++it) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
@@ -179,6 +304,8 @@ __global__ void __launch_bounds__(1024) probe_kernel(long long* cycles) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) s += x[i] + y[i];
 #pragma unroll
+  for (int i = 0; i < 4; ++i) s += z[i] + w[i];
+#pragma unroll
   for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int i = 0; i < 16; ++i) s += acc[c][i];
@@ -208,6 +335,9 @@ void probe_shape(int kind, int* threads, int64_t* units) {
     case P_FMA_4W: *threads = 1024; *units = 4 * it * 8; break;
     case P_MIX8_4W: *threads = 1024; *units = 4 * it * 2; break;     // MFMA per SIMD
     case P_MIX16: *threads = 512; *units = 2 * it * 2; break;        // MFMA per SIMD
+    case P_MFMA_FMA3: case P_MFMA_FMA4: case P_MFMA_EXP2: *threads = 512; *units = it * 4; break;   // MFMA per SIMD
+    case P_FWD_INTER: case P_FWD_PPB: case P_FWD_DEP: case P_FWD_SKEW:
+      *threads = 512; *units = 2 * (it / 32); break;                 // wave-tiles per SIMD
     default: *threads = 512; *units = 8 * it * 8 * 64 * 4; break;
   }
 }
@@ -252,6 +382,13 @@ hipError_t launch_probe_kind(int kind, long long* cycles, int64_t* units, int* g
     case P_FMA_4W: return launch_probe<P_FMA_4W>(threads, cycles, st);
     case P_MIX8_4W: return launch_probe<P_MIX8_4W>(threads, cycles, st);
     case P_MIX16: return launch_probe<P_MIX16>(threads, cycles, st);
+    case P_MFMA_FMA3: return launch_probe<P_MFMA_FMA3>(threads, cycles, st);
+    case P_MFMA_FMA4: return launch_probe<P_MFMA_FMA4>(threads, cycles, st);
+    case P_MFMA_EXP2: return launch_probe<P_MFMA_EXP2>(threads, cycles, st);
+    case P_FWD_INTER: return launch_probe<P_FWD_INTER>(threads, cycles, st);
+    case P_FWD_PPB: return launch_probe<P_FWD_PPB>(threads, cycles, st);
+    case P_FWD_DEP: return launch_probe<P_FWD_DEP>(threads, cycles, st);
+    case P_FWD_SKEW: return launch_probe<P_FWD_SKEW>(threads, cycles, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -301,10 +301,10 @@ def test_noalloc_validation(lib):
 def test_probe_entry_points_reject_bad_arguments(lib):
     # the issue-rate diagnostics: kinds are counted by the library; bad kinds
     # and null or misaligned pointers are rejected before any launch
-    assert lib.attn_probe_kinds() == 27
+    assert lib.attn_probe_kinds() == 34
     units = ctypes.c_longlong(-1)
     grid = ctypes.c_int(-1)
-    for kind in (-1, 27, 1000):
+    for kind in (-1, 34, 1000):
         assert lib.attn_probe_issue_rates(kind, 1 << 20, ctypes.byref(units), ctypes.byref(grid), None) == 1
     assert lib.attn_probe_issue_rates(0, None, ctypes.byref(units), ctypes.byref(grid), None) == 1
     assert lib.attn_probe_issue_rates(0, (1 << 20) + 4, ctypes.byref(units), ctypes.byref(grid), None) == 1

@@ -28,7 +28,10 @@ def test_probe_mfma_costs_and_every_kind_runs(gpu):
     for kind in range(19, 24):
         assert costs[kind] >= 0.95 * costs[1], (kind, costs[kind], costs[1])
     # MFMA with vector work beside it takes at least the MFMA time
-    for kind in list(range(8, 13)) + [25, 26]:
+    for kind in list(range(8, 13)) + [25, 26, 27, 28, 29]:
         assert costs[kind] >= 0.95 * 32.0, (kind, costs[kind])
+    # a 128-key tile of the forward mix takes at least its 42 MFMA
+    for kind in range(30, 34):
+        assert costs[kind] >= 0.95 * 42 * 32.0, (kind, costs[kind])
     for kind in range(13, 18):
         assert 1.0 / costs[kind] <= 256.0 + 1.0, (kind, 1.0 / costs[kind])
