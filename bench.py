@@ -60,6 +60,10 @@ def parse():
                     help="only run a plain device copy of MIB MiB three times (HBM counter calibration) and exit")
     ap.add_argument("--issue-rates", action="store_true",
                     help="print the per-instruction costs measured by the library's issue-rate micro-kernels")
+    ap.add_argument("--phase-trace", action="store_true",
+                    help="run the Wan-shape forward on the phase-trace library (libattnfp4_trace.so, built by "
+                         "`python -m precision_attention_forward_amd.build --phase-trace`) and print each wave's "
+                         "shader-clock cycles per key-loop iteration in five phases, then exit")
     ap.add_argument("--gemm-reference", action="store_true",
                     help="only time torch's bf16 and fp16 matrix products (n = 8192, 16384) on this GPU, the "
                          "vendor-library reference for the BF16 attention's matrix rate, and exit")
@@ -184,6 +188,61 @@ def issue_rates():
         else:
             line["cycles_per_instruction_per_simd"] = round(cyc / units, 2)
         print(json.dumps(line), flush=True)
+
+
+PHASE_NAMES = ("before the slots", "slots 0-9 (P.V, statistics)", "slots 10-25 (S sub-tiles 0-1)",
+               "slots 26-41 (S sub-tiles 2-3; waves 4-7's barrier)", "after the slots (waves 0-3's barrier)")
+
+
+def phase_trace(steps=5):
+    """The forward attention kernel's key-loop phases on the Wan shape
+    (workload 2, MXFP4 P / MXFP4 V, NVFP4 Q/K): the diagnostic library's
+    workgroup 0 records, per wave, the shader-clock cycles spent in each phase
+    summed over its iterations (see the phase trace in csrc/fwd_lowp.hip).
+    Prints one JSON line per wave (cycles per iteration) and a summary line
+    with the call time, which includes the stamps' own cost."""
+    import ctypes
+    import numpy as np
+    import torch
+    import precision_attention_forward_amd as paf
+    from precision_attention_forward_amd import synth
+    from precision_attention_forward_amd.build import TRACE_LIB
+    lib = paf.load_library(TRACE_LIB)
+    lib.attn_fwd_phase_trace_read.restype = ctypes.c_int
+    lib.attn_fwd_phase_trace_read.argtypes = [ctypes.c_void_p]
+    wl = synth.WORKLOADS[2]
+    inp = synth.generate(wl, "cuda")
+    q, k = paf.quant_nvfp4(inp.q), paf.quant_nvfp4(inp.k)
+    vq = paf.quant_v(inp.v, paf.V_MXFP4)
+    v = (paf.V_MXFP4, vq[0], vq[1], vq[2])
+    kw = dict(Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D, softmax_scale=inp.sigma, causal=False, out_dtype=torch.bfloat16,
+              B=1, Nq=wl.N, Nk=wl.N)
+    ws = paf.Workspace()
+    o, lse, _ = paf.fwd_directp(q, k, v, workspace=ws, **kw)
+    for _ in range(2):
+        paf.fwd_directp(q, k, v, workspace=ws, out=(o, lse), **kw)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        paf.fwd_directp(q, k, v, workspace=ws, out=(o, lse), **kw)
+    ev1.record()
+    torch.cuda.synchronize()
+    buf = np.zeros((8, 8), dtype=np.uint64)
+    st = lib.attn_fwd_phase_trace_read(buf.ctypes.data_as(ctypes.c_void_p))
+    if st != 0:
+        raise RuntimeError(f"attn_fwd_phase_trace_read failed: hip error {st}")
+    totals = []
+    for w in range(8):
+        iters = int(buf[w, 5]) + 1                   # the key loop runs n_tiles + 1 iterations
+        per = [float(buf[w, j]) / iters for j in range(5)]
+        totals.append(sum(per))
+        print(json.dumps({"wave": w, "iterations": iters,
+                          "cycles_per_iteration": {n: round(x, 1) for n, x in zip(PHASE_NAMES, per)},
+                          "total": round(sum(per), 1)}), flush=True)
+    print(json.dumps({"phase_trace": "fwd_lowp_kernel wan14b (MXFP4 P, MXFP4 V, NVFP4 Q/K)",
+                      "call_ms_with_stamps": round(ev0.elapsed_time(ev1) / steps, 4),
+                      "cycles_per_iteration_mean": round(sum(totals) / 8, 1)}), flush=True)
 
 
 def cpu_baseline(inp, rows, encoder="exact", four_six=False, qk="nvfp4"):
@@ -566,6 +625,9 @@ def main():
         return
     if args.gemm_reference:
         gemm_reference()
+        return
+    if args.phase_trace:
+        phase_trace()
         return
     import torch
     import precision_attention_forward_amd as paf

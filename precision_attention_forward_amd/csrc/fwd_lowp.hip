@@ -206,6 +206,34 @@ struct LdsLayout {
 // FP4 MFMAs (v_mfma_scale_f32_32x32x64_f8f6f4, both operands E2M1, the block
 // exponents as scale_a / scale_b) instead of D/16 FP16 ones.  The S^T layout,
 // and with it everything from the row max on, is unchanged.
+// Phase trace (a diagnostic build only: compiled with -DATTN_FWD_PHASE_TRACE
+// into its own library, libattnfp4_trace.so; the product library has none of
+// it).  Workgroup 0 of a launch writes, per wave, the shader-clock cycles
+// (s_memtime) that the wave spent in five phases of the key loop, summed over
+// its iterations, and its tile count:
+//   [0] from the previous iteration's end to the first slot (rescale, mask,
+//       scale and operand loads), [1] slots 0 .. NPV-1, [2] slots
+//       NPV .. NPV+2KS-1, [3] the remaining slots (waves 4-7 take their
+//       barrier there), [4] after the last slot (waves 0-3 take theirs there);
+//   [5] the number of key tiles.
+// Each stamp is fenced by scheduling barriers, which perturbs the schedule a
+// little.  attn_fwd_phase_trace_read copies the 8 x 8 table to the host.
+#ifdef ATTN_FWD_PHASE_TRACE
+__device__ unsigned long long g_fwd_phase_trace[8][8];
+extern "C" hipError_t attn_fwd_phase_trace_read(unsigned long long* host_dst) {
+  return hipMemcpyFromSymbol(host_dst, HIP_SYMBOL(g_fwd_phase_trace), sizeof(g_fwd_phase_trace), 0,
+                             hipMemcpyDeviceToHost);
+}
+#define FWD_PHASE_STAMP(k)                      \
+  do {                                          \
+    __builtin_amdgcn_sched_barrier(0);          \
+    tstamp[k] = __builtin_amdgcn_s_memtime();   \
+    __builtin_amdgcn_sched_barrier(0);          \
+  } while (0)
+#else
+#define FWD_PHASE_STAMP(k) do {} while (0)
+#endif
+
 template <int D, int PF, int VF, bool CAUSAL, bool DEBUG, int ENC, int QK>
 __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   constexpr int KS = QK ? D / 64 : D / 16;   // k-steps of the S MFMA per sub-tile
@@ -763,6 +791,10 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
   bmp[1] = tile_max(2);
   dma_wait();
   phase_barrier();
+#ifdef ATTN_FWD_PHASE_TRACE
+  unsigned long long tacc[5] = {0, 0, 0, 0, 0}, tstamp[5];
+  unsigned long long tprev = __builtin_amdgcn_s_memtime();
+#endif
   int rk = 1;                                  // ring slot of K(t) = t mod 3
   for (int t = 1; t <= n_tiles + 1; ++t) {
     const int rk1 = rk == 2 ? 0 : rk + 1, rk2 = rk1 == 2 ? 0 : rk1 + 1;   // (t+1), (t+2) = (t-1) mod 3
@@ -803,6 +835,7 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
     setprio_if<2>(group);
 #endif
     __builtin_amdgcn_sched_barrier(0);
+    FWD_PHASE_STAMP(0);
 #pragma clang loop unroll(full)
     for (int i = 0; i < NS; ++i) {
       // copies for the next iterations, K(t+1) and V(t-1), spread over the
@@ -827,14 +860,32 @@ __global__ void __launch_bounds__(512, 1) fwd_lowp_kernel(FwdParams p) {
       if (i == ATTN_PRIO_END) setprio_if<0>(group);
 #endif
       if (i == G1B - 1 && G1B < NS) dma_wait_barrier_if(group);
+      if (i == NPV - 1) FWD_PHASE_STAMP(1);
+      if (i == NPV + 2 * KS - 1) FWD_PHASE_STAMP(2);
+      if (i == NS - 1) FWD_PHASE_STAMP(3);
     }
 
     if (j < n_tiles) dump(j, pw, psw);
     pr[0] = pw[0]; pr[1] = pw[1]; psr[0] = psw[0]; psr[1] = psw[1];
     bmp[0] = bmn[0]; bmp[1] = bmn[1];
     dma_wait_barrier_if(G1B >= NS ? 1 : group ^ 1);
+#ifdef ATTN_FWD_PHASE_TRACE
+    FWD_PHASE_STAMP(4);
+    tacc[0] += tstamp[0] - tprev;
+#pragma unroll
+    for (int k = 1; k < 5; ++k) tacc[k] += tstamp[k] - tstamp[k - 1];
+    tprev = tstamp[4];
+#endif
     rk = rk1;
   }
+#ifdef ATTN_FWD_PHASE_TRACE
+  if (blockIdx.x == 0 && lane < 6) {
+    unsigned long long v = (unsigned long long)n_tiles;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) v = lane == k ? tacc[k] : v;
+    g_fwd_phase_trace[wave][lane] = v;
+  }
+#endif
 
   // ---- epilogue: O = o / l (x FP8 V tensor scale), LSE = ln2 * (m + log2 l)
   if (!wave_active || my_q >= len_q) return;

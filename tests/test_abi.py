@@ -35,6 +35,15 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) == set(B.EXPORTS), "binding and header disagree"
 
 
+def test_product_library_has_no_phase_trace(lib):
+    # The forward's phase-trace stamps exist only in the diagnostic build
+    # (libattnfp4_trace.so); the product library compiles them out.
+    assert not hasattr(lib, "attn_fwd_phase_trace_read")
+    from precision_attention_forward_amd.build import TRACE_LIB
+    if os.path.exists(TRACE_LIB):
+        assert hasattr(ctypes.CDLL(TRACE_LIB), "attn_fwd_phase_trace_read")
+
+
 def test_struct_layout_matches_header():
     # attn_fwd_args as laid out by the compiler for the C declaration
     assert ctypes.sizeof(B.FwdArgs) == 4 * 6 + 8 * 2 + 8 * 2 + 4 + 4 + 24 * 2 + 32 + 8 + 4 + 4 + 8 + 8 + 8 + 8 + 8 + 4 + 4 + 8 + 8
