@@ -196,7 +196,13 @@ __global__ void __launch_bounds__(256) quant_v_kernel(const uint16_t* __restrict
                                                       const float* __restrict__ partials, int np,
                                                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                       float* __restrict__ tensor_scale) {
-  const int tile = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  // Head fastest in dispatch order: a key's row holds all KV heads side by
+  // side (Hkv * D * 2 bytes), so the workgroups dispatched together read
+  // neighbouring head slices of the same keys instead of one head's slice of
+  // keys far apart.  1.06x (MXFP4) and 1.09x (FP8) against tile-fastest order
+  // on the Wan shape.
+  const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int h = lin % gridDim.y, tile = (lin / gridDim.y) % gridDim.x, s = lin / (gridDim.x * gridDim.y);
   const bool varlen = cu_k != nullptr;
   const int64_t tok0 = varlen ? cu_k[s] : (int64_t)s * Nk;
   const int len = varlen ? cu_k[s + 1] - cu_k[s] : Nk;
