@@ -207,6 +207,10 @@ def phase_trace(steps=5):
     import precision_attention_forward_amd as paf
     from precision_attention_forward_amd import synth
     from precision_attention_forward_amd.build import TRACE_LIB
+    if not os.path.exists(TRACE_LIB):
+        print(f"{TRACE_LIB} is missing: build it with `python -m precision_attention_forward_amd.build --phase-trace`",
+              file=sys.stderr)
+        sys.exit(2)
     lib = paf.load_library(TRACE_LIB)
     lib.attn_fwd_phase_trace_read.restype = ctypes.c_int
     lib.attn_fwd_phase_trace_read.argtypes = [ctypes.c_void_p]
